@@ -1,0 +1,334 @@
+"""ctypes front end of the scalar-C oracle (``mtp_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library; both sides are fed the same arrays built by
+``mtp_speculative_draft_amd.synth``.
+
+Every function takes and returns numpy arrays; the C side accumulates in
+double and stores f32 between steps.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mtp_oracle.c")
+_HDR = os.path.join(_HERE, "mtp_oracle.h")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc -O2 -std=c99 (no fast-math)."""
+    stale = (not os.path.exists(LIB_PATH) or
+             os.path.getmtime(LIB_PATH) < max(os.path.getmtime(_SRC), os.path.getmtime(_HDR)))
+    if force or stale:
+        tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class _Q4(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("n", C.c_int32), ("k", C.c_int32)]
+
+
+class _Q8(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
+
+
+class _Layer(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("vocab", C.c_int32), ("ffn_inter", C.c_int32),
+                ("rope_theta", C.c_double), ("eps", C.c_float),
+                ("gamma_e", C.c_void_p), ("gamma_h", C.c_void_p), ("gamma_attn", C.c_void_p),
+                ("gamma_post", C.c_void_p), ("gamma_final", C.c_void_p),
+                ("eh_proj", _Q4), ("wq", _Q4), ("wk", _Q4), ("wv", _Q4), ("wo", _Q4),
+                ("gate", _Q4), ("up", _Q4), ("down", _Q4), ("lm_head", _Q4)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = C.CDLL(LIB_PATH)
+        P, I = C.c_void_p, C.c_int32
+        sig = {
+            "orc_unpack4": (None, [P, I, I, P]),
+            "orc_deq4": (None, [P, P]),
+            "orc_deq8": (None, [P, P]),
+            "orc_gemv4": (None, [P, P, I, P]),
+            "orc_gemv8": (None, [P, P, I, P]),
+            "orc_gemv_f32": (None, [P, I, I, P, I, P]),
+            "orc_rmsnorm": (None, [P, P, I, I, C.c_float, P]),
+            "orc_rope": (None, [P, I, I, I, I, C.c_double]),
+            "orc_sdpa": (None, [P, P, P, I, I, I, I, I, I, P]),
+            "orc_argmax": (I, [P, I]),
+            "orc_norm_concat_proj": (None, [P, P, P, P, C.c_float, P, I, P]),
+            "orc_attention": (None, [P, P, P, P, I, I, I, P]),
+            "orc_ffn_dense": (None, [P, P, P, P, P, I, P]),
+            "orc_moe": (I, [P, P, I, I, P, P, P, P, P, P, P, I, P, P, P, P]),
+            "orc_head": (None, [P, P, C.c_float, P, I, P, P, P]),
+            "orc_draft_step": (I, [P, P, P, P, P, P, P, I, I, I, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(_lib, name)
+            f.restype = res
+            f.argtypes = args
+    return _lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+class _Keep:
+    """Holds the contiguous copies alive while a C call runs."""
+
+    def __init__(self):
+        self.refs = []
+
+    def arr(self, a, dtype):
+        a = _c(a, dtype)
+        self.refs.append(a)
+        return a
+
+
+def _q4(w, keep: _Keep) -> _Q4:
+    c = keep.arr(w.codes, np.uint32)
+    s = keep.arr(w.scales, np.float32)
+    b = keep.arr(w.biases, np.float32)
+    return _Q4(c.ctypes.data, s.ctypes.data, b.ctypes.data, w.n, w.k)
+
+
+def _q8_list(w, keep: _Keep):
+    """Array of per-expert _Q8 descriptors over an [E, n, k] stack."""
+    c = keep.arr(w.codes, np.int8)
+    s = keep.arr(w.scales, np.float32)
+    E, n, k = c.shape
+    arr = (_Q8 * E)()
+    for e in range(E):
+        arr[e] = _Q8(c.ctypes.data + e * n * k, s.ctypes.data + e * n * (k // 32) * 4, n, k)
+    keep.refs.append(arr)
+    return arr
+
+
+def _layer(L, keep: _Keep) -> _Layer:
+    f = lambda a: keep.arr(a, np.float32).ctypes.data  # noqa: E731
+    return _Layer(L.hidden, L.n_heads, L.n_kv_heads, L.head_dim, L.vocab, L.ffn_inter,
+                  float(L.rope_theta), float(L.eps),
+                  f(L.gamma_e), f(L.gamma_h), f(L.gamma_attn), f(L.gamma_post), f(L.gamma_final),
+                  _q4(L.eh_proj, keep), _q4(L.wq, keep), _q4(L.wk, keep), _q4(L.wv, keep), _q4(L.wo, keep),
+                  _q4(L.gate, keep), _q4(L.up, keep), _q4(L.down, keep), _q4(L.lm_head, keep))
+
+
+# --------------------------------------------------------------------------
+# public functions
+# --------------------------------------------------------------------------
+def unpack4(codes: np.ndarray, k: int) -> np.ndarray:
+    codes = _c(codes, np.uint32)
+    n = codes.shape[0]
+    out = np.empty((n, k), dtype=np.uint8)
+    lib().orc_unpack4(_p(codes), n, k, _p(out))
+    return out
+
+
+def deq4(w) -> np.ndarray:
+    keep = _Keep()
+    d = _q4(w, keep)
+    out = np.empty((w.n, w.k), dtype=np.float32)
+    lib().orc_deq4(C.byref(d), _p(out))
+    return out
+
+
+def deq8(w, expert: int = 0) -> np.ndarray:
+    keep = _Keep()
+    arr = _q8_list(w, keep)
+    out = np.empty((w.n, w.k), dtype=np.float32)
+    lib().orc_deq8(C.byref(arr[expert]), _p(out))
+    return out
+
+
+def gemv4(w, x: np.ndarray) -> np.ndarray:
+    keep = _Keep()
+    d = _q4(w, keep)
+    x = keep.arr(np.atleast_2d(x), np.float32)
+    y = np.empty((x.shape[0], w.n), dtype=np.float32)
+    lib().orc_gemv4(C.byref(d), _p(x), x.shape[0], _p(y))
+    return y
+
+
+def gemv8(w, x: np.ndarray, expert: int = 0) -> np.ndarray:
+    keep = _Keep()
+    arr = _q8_list(w, keep)
+    x = keep.arr(np.atleast_2d(x), np.float32)
+    y = np.empty((x.shape[0], w.n), dtype=np.float32)
+    lib().orc_gemv8(C.byref(arr[expert]), _p(x), x.shape[0], _p(y))
+    return y
+
+
+def gemv_f32(w: np.ndarray, x: np.ndarray) -> np.ndarray:
+    w = _c(w, np.float32)
+    x = _c(np.atleast_2d(x), np.float32)
+    y = np.empty((x.shape[0], w.shape[0]), dtype=np.float32)
+    lib().orc_gemv_f32(_p(w), w.shape[0], w.shape[1], _p(x), x.shape[0], _p(y))
+    return y
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    x = _c(np.atleast_2d(x), np.float32)
+    g = _c(gamma, np.float32)
+    y = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x), _p(g), x.shape[0], x.shape[1], float(eps), _p(y))
+    return y
+
+
+def rope(x: np.ndarray, n_heads: int, head_dim: int, pos0: int, theta: float) -> np.ndarray:
+    y = np.array(np.atleast_2d(x), dtype=np.float32, copy=True, order="C")
+    lib().orc_rope(_p(y), y.shape[0], n_heads, head_dim, pos0, float(theta))
+    return y
+
+
+def sdpa(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, n_heads: int, cache_len: int) -> np.ndarray:
+    q = _c(np.atleast_2d(q), np.float32)
+    kc = _c(k_cache, np.float32)
+    vc = _c(v_cache, np.float32)
+    nkv, cap, d = kc.shape
+    out = np.empty((q.shape[0], n_heads * d), dtype=np.float32)
+    lib().orc_sdpa(_p(q), _p(kc), _p(vc), q.shape[0], n_heads, nkv, d, cache_len, cap, _p(out))
+    return out
+
+
+def argmax(v: np.ndarray) -> int:
+    v = _c(v, np.float32)
+    return int(lib().orc_argmax(_p(v), v.size))
+
+
+def norm_concat_proj(e, h, gamma_e, gamma_h, eps, w) -> np.ndarray:
+    keep = _Keep()
+    d = _q4(w, keep)
+    e = keep.arr(np.atleast_2d(e), np.float32)
+    h = keep.arr(np.atleast_2d(h), np.float32)
+    ge, gh = keep.arr(gamma_e, np.float32), keep.arr(gamma_h, np.float32)
+    u = np.empty((e.shape[0], w.n), dtype=np.float32)
+    lib().orc_norm_concat_proj(_p(e), _p(h), _p(ge), _p(gh), float(eps), C.byref(d), e.shape[0], _p(u))
+    return u
+
+
+def attention(L, u, k_cache: np.ndarray, v_cache: np.ndarray, cache_len: int) -> np.ndarray:
+    """Attention block with residual; appends K/V rows into the given caches in place."""
+    assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
+    assert v_cache.flags.c_contiguous and v_cache.dtype == np.float32
+    keep = _Keep()
+    d = _layer(L, keep)
+    u = keep.arr(np.atleast_2d(u), np.float32)
+    r1 = np.empty_like(u)
+    lib().orc_attention(C.byref(d), _p(u), _p(k_cache), _p(v_cache), cache_len, k_cache.shape[1],
+                        u.shape[0], _p(r1))
+    return r1
+
+
+def ffn_dense(x, gate, up, down, residual=None) -> np.ndarray:
+    keep = _Keep()
+    g, u, dn = _q4(gate, keep), _q4(up, keep), _q4(down, keep)
+    x = keep.arr(np.atleast_2d(x), np.float32)
+    res = None if residual is None else keep.arr(np.atleast_2d(residual), np.float32)
+    y = np.empty((x.shape[0], down.n), dtype=np.float32)
+    lib().orc_ffn_dense(_p(x), C.byref(g), C.byref(u), C.byref(dn), _p(res), x.shape[0], _p(y))
+    return y
+
+
+def moe(inp, x=None, residual=None):
+    """Returns (y, expert_ids [m, top_k], gates [m, top_k], router_logits [m, E])."""
+    keep = _Keep()
+    x = keep.arr(np.atleast_2d(inp.x if x is None else x), np.float32)
+    router = keep.arr(inp.router, np.float32)
+    m, E, K = x.shape[0], inp.n_experts, inp.top_k
+    ge, ue, de = _q8_list(inp.gate_exps, keep), _q8_list(inp.up_exps, keep), _q8_list(inp.down_exps, keep)
+    if inp.sh_gate is not None:
+        sg, su, sd = (C.byref(_q8_list(inp.sh_gate, keep)[0]), C.byref(_q8_list(inp.sh_up, keep)[0]),
+                      C.byref(_q8_list(inp.sh_down, keep)[0]))
+    else:
+        sg = su = sd = None
+    res = None if residual is None else keep.arr(np.atleast_2d(residual), np.float32)
+    y = np.empty((m, inp.gate_exps.k), dtype=np.float32)
+    ids = np.empty((m, K), dtype=np.int32)
+    gates = np.empty((m, K), dtype=np.float32)
+    logits = np.empty((m, E), dtype=np.float32)
+    rc = lib().orc_moe(_p(x), _p(router), E, K, ge, ue, de, sg, su, sd, _p(res), m, _p(y), _p(ids),
+                       _p(gates), _p(logits))
+    if rc != 0:
+        raise ValueError("orc_moe rejected its arguments")
+    return y, ids, gates, logits
+
+
+def head(hidden, gamma, eps, lm):
+    """Returns (normed [m, H], logits [m, V], ids [m])."""
+    keep = _Keep()
+    d = _q4(lm, keep)
+    x = keep.arr(np.atleast_2d(hidden), np.float32)
+    g = keep.arr(gamma, np.float32)
+    m = x.shape[0]
+    normed = np.empty((m, lm.k), dtype=np.float32)
+    logits = np.empty((m, lm.n), dtype=np.float32)
+    ids = np.empty(m, dtype=np.int32)
+    lib().orc_head(_p(x), _p(g), float(eps), C.byref(d), m, _p(normed), _p(logits), _p(ids))
+    return normed, logits, ids
+
+
+def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_logits: bool = True):
+    """One draft-layer forward over m rows; appends K/V rows in place.
+
+    Returns (ids [m], hidden_out [m, H] (post-final-norm), logits [m, V] or None)."""
+    assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
+    assert v_cache.flags.c_contiguous and v_cache.dtype == np.float32
+    keep = _Keep()
+    d = _layer(L, keep)
+    h = keep.arr(np.atleast_2d(h), np.float32)
+    m = h.shape[0]
+    e = None if e is None else keep.arr(np.atleast_2d(e), np.float32)
+    tok = None if tokens is None else keep.arr(np.asarray(tokens).reshape(-1), np.int32)
+    tab = None if table is None else (table if (table.flags.c_contiguous and table.dtype == np.float32)
+                                      else keep.arr(table, np.float32))
+    ids = np.empty(m, dtype=np.int32)
+    hid = np.empty((m, L.hidden), dtype=np.float32)
+    logits = np.empty((m, L.vocab), dtype=np.float32) if want_logits else None
+    rc = lib().orc_draft_step(C.byref(d), _p(e), _p(tok), _p(tab), _p(h), _p(k_cache), _p(v_cache),
+                              cache_len, k_cache.shape[1], m, _p(ids), _p(hid), _p(logits))
+    if rc != 0:
+        raise ValueError("orc_draft_step rejected its arguments")
+    return ids, hid, logits
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    """Cosine similarity with double accumulation; NaN when a norm is zero
+    (hf2q 0.1.1 forward_mlx_shared.rs, `cosine_pairwise_f32`)."""
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    na, nb = np.sqrt((a * a).sum()), np.sqrt((b * b).sum())
+    if na == 0.0 or nb == 0.0:
+        return float("nan")
+    return float((a * b).sum() / (na * nb))
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_2 / ||ref||_2 in double."""
+    g = np.asarray(got, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    den = np.sqrt((r * r).sum())
+    num = np.sqrt(((g - r) ** 2).sum())
+    return float(num / den) if den > 0 else float(num)

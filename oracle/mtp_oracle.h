@@ -1,0 +1,99 @@
+/*
+ * mtp_oracle.h -- plain, slow, scalar-C reference of the quantized MTP draft
+ * layer forward.  TEST INFRASTRUCTURE ONLY: the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg call it; the product library never
+ * links, loads or calls anything here, and nothing here is shared with it.
+ *
+ * Sources (public web pages, cited by title and Rust item):
+ *   [mtp.rs]    hf2q 0.1.13, src/inference/models/qwen35/mtp.rs
+ *   [mimo.rs]   cortiq-engine 0.8.49, src/mimo_mtp.rs
+ *   [shared.rs] hf2q 0.1.1, src/serve/forward_mlx_shared.rs
+ *
+ * Arithmetic rules (the pages' own CPU checks accumulate in double; the
+ * pages keep activations and logits in f32):
+ *   - every sum is a double accumulator over ascending index;
+ *   - every activation passed between steps is stored as f32;
+ *   - the f32 dequantized weight is the exact affine value rounded once
+ *     (fmaf), while the products inside a GEMV use the exact value in double.
+ *
+ * Parity-unpinned parts: absolute values of a whole draft step.  The pages
+ * print no outputs for it; it is pinned only through invariants (batched
+ * equals sequential, length-1 attention returns V, gates sum to one, ...).
+ */
+#ifndef MTP_ORACLE_H
+#define MTP_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* 4-bit affine weight, group size 32 ([shared.rs] `MlxAffineExtra`):
+ * codes u32 [n][k/8], element k of a row is nibble (k%8) of word k/8, the low
+ * nibble holding the lowest k; scales and biases f32 [n][k/32]. */
+typedef struct {
+    const uint32_t* codes;
+    const float* scales;
+    const float* biases;
+    int32_t n, k;
+} orc_q4;
+
+/* 8-bit block weight, block 32: int8 codes [n][k], f32 scales [n][k/32],
+ * value = scale * code.  One matrix; expert stacks are passed as arrays. */
+typedef struct {
+    const int8_t* codes;
+    const float* scales;
+    int32_t n, k;
+} orc_q8;
+
+/* One dense MTP draft layer ([mimo.rs] module doc "The draft forward";
+ * [mtp.rs] `MtpWeights`). */
+typedef struct {
+    int32_t hidden, n_heads, n_kv_heads, head_dim, vocab, ffn_inter;
+    double rope_theta;
+    float eps;
+    const float *gamma_e, *gamma_h, *gamma_attn, *gamma_post, *gamma_final;
+    orc_q4 eh_proj, wq, wk, wv, wo, gate, up, down, lm_head;
+} orc_layer;
+
+/* ---- weight formats ---- */
+void orc_unpack4(const uint32_t* codes, int32_t n, int32_t k, uint8_t* out);
+void orc_deq4(const orc_q4* w, float* out);
+void orc_deq8(const orc_q8* w, float* out);
+
+/* ---- primitives ---- */
+void orc_gemv4(const orc_q4* w, const float* x, int32_t m, float* y);
+void orc_gemv8(const orc_q8* w, const float* x, int32_t m, float* y);
+void orc_gemv_f32(const float* w, int32_t n, int32_t k, const float* x, int32_t m, float* y);
+void orc_rmsnorm(const float* x, const float* gamma, int32_t m, int32_t h, float eps, float* y);
+void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t pos0, double theta);
+void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_t m,
+              int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t cache_len,
+              int32_t capacity, float* out);
+int32_t orc_argmax(const float* v, int32_t n);
+
+/* ---- layer steps ---- */
+void orc_norm_concat_proj(const float* e, const float* h, const float* gamma_e, const float* gamma_h,
+                          float eps, const orc_q4* eh_proj, int32_t m, float* u);
+void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_cache,
+                   int32_t cache_len, int32_t capacity, int32_t m, float* r1);
+void orc_ffn_dense(const float* x, const orc_q4* gate, const orc_q4* up, const orc_q4* down,
+                   const float* residual, int32_t m, float* y);
+int32_t orc_moe(const float* x, const float* router, int32_t n_experts, int32_t top_k,
+                const orc_q8* gate_exps, const orc_q8* up_exps, const orc_q8* down_exps,
+                const orc_q8* sh_gate, const orc_q8* sh_up, const orc_q8* sh_down,
+                const float* residual, int32_t m, float* y, int32_t* expert_ids, float* gates,
+                float* router_logits);
+void orc_head(const float* hidden, const float* gamma, float eps, const orc_q4* lm_head, int32_t m,
+              float* normed_out, float* logits_out, int32_t* ids_out);
+int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens,
+                       const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                       int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
+                       float* hidden_out, float* logits_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

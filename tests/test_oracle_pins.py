@@ -1,0 +1,439 @@
+"""Pins of the scalar-C oracle against things other than itself: hand-computed
+values (tests/golden), closed forms, exact rational brute force on tiny
+inputs, and invariants of the method.  CPU only.
+
+Each pin is chosen so that a plausible slip in the oracle (nibble order,
+group index, dropped bias, transposed weight, wrong RoPE pairing or
+frequency, an off-by-one causal mask, a missing gate renormalisation, the
+concat order) fails at least one test here.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from mtp_speculative_draft_amd import synth
+from tests.conftest import GOLDEN
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _q4_from(codes, scales, biases):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return synth.Q4(synth.pack_q4(codes), np.asarray(scales, np.float32), np.asarray(biases, np.float32))
+
+
+def _ulp32(v):
+    v = np.float32(abs(v))
+    return float(np.nextafter(v, np.float32(np.inf)) - v) if v != 0 else float(np.finfo(np.float32).tiny)
+
+
+# --------------------------------------------------------------------------
+# weight formats
+# --------------------------------------------------------------------------
+def test_unpack_and_dequant_hand_examples():
+    g = _golden("dequant_q4_hand.json")
+    c0 = g["cases"][0]
+    words = np.array([c0["words"]], dtype=np.uint32)
+    assert oracle.unpack4(words, 32)[0].tolist() == c0["codes"]
+    w = synth.Q4(words, np.array([[c0["scale"]]], np.float32), np.array([[c0["bias"]]], np.float32))
+    assert oracle.deq4(w)[0].tolist() == c0["values"]
+
+    c1 = g["cases"][1]
+    s = np.float32(c1["scale"])
+    w = synth.Q4(np.array([c1["words"]], np.uint32), np.array([[s]], np.float32),
+                 np.array([[-8 * s]], np.float32))
+    d = oracle.deq4(w)[0]
+    assert oracle.unpack4(w.codes, 32)[0].tolist() == c1["codes"]
+    assert d.tolist() == c1["values"] and not np.signbit(d).any()
+
+    c2 = g["cases"][2]
+    w = synth.Q4(np.array([c2["words"]], np.uint32), np.array([c2["group_scales"]], np.float32),
+                 np.array([c2["group_biases"]], np.float32))
+    d = oracle.deq4(w)[0]
+    assert d[:32].tolist() == c0["values"]
+    assert d[32:].tolist() == c2["values_group1"]
+
+
+def test_pack_roundtrip_low_nibble_first():
+    g = np.random.default_rng(5)
+    codes = g.integers(0, 16, size=(7, 96), dtype=np.uint8)
+    packed = synth.pack_q4(codes)
+    assert packed.shape == (7, 12)
+    assert (oracle.unpack4(packed, 96) == codes).all()
+    # word layout stated by the page: code j of a word at bits 4j..4j+3
+    j = 5
+    assert int(packed[3, 2]) >> (4 * j) & 0xF == codes[3, 2 * 8 + j]
+
+
+def test_deq4_is_the_exact_value_rounded_once():
+    g = np.random.default_rng(11)
+    w = synth.q4_weight(g, 9, 128)
+    codes = synth.unpack_q4_codes(w.codes).astype(np.int64)
+    s = np.repeat(w.scales, 32, axis=1)
+    b = np.repeat(w.biases, 32, axis=1)
+    d = oracle.deq4(w)
+    for (i, j) in [(0, 0), (3, 77), (8, 127), (5, 31), (5, 32)]:
+        exact = Fraction(float(s[i, j])) * int(codes[i, j]) + Fraction(float(b[i, j]))
+        assert float(exact) == float(s[i, j]) * codes[i, j] + float(b[i, j])  # the double sum is exact here
+        assert d[i, j] == np.float32(float(exact))
+    ref = (s.astype(np.float64) * codes + b.astype(np.float64)).astype(np.float32)
+    assert (d.view(np.uint32) == ref.view(np.uint32)).all()
+
+
+def test_deq8_hand_examples():
+    g = _golden("dequant_q8_hand.json")
+    for case in g["cases"]:
+        n_first = len(case["codes_first"])
+        codes = np.zeros((1, 1, 32), np.int8)
+        codes[0, 0, :n_first] = case["codes_first"]
+        w = synth.Q8(codes, np.full((1, 1, 1), case["scale"], np.float32))
+        d = oracle.deq8(w)[0, :n_first]
+        if "values_first" in case:
+            assert d.tolist() == case["values_first"]
+        else:
+            assert [hex(int(v)) for v in d.view(np.uint32)] == case["values_first_hex"]
+
+
+# --------------------------------------------------------------------------
+# GEMV
+# --------------------------------------------------------------------------
+def _page_fixture(fx):
+    n, k, m = fx["n"], fx["k"], fx["m"]
+    gpr = k // 32
+    q = ((np.arange(n * k) * fx["code_mul"] + fx["code_add"]) % 16).astype(np.uint8).reshape(n, k)
+    i = np.arange(n * gpr, dtype=np.float32)
+    scales = (np.float32(fx["scale0"]) + i * np.float32(fx["scale_step"])).astype(np.float32).reshape(n, gpr)
+    biases = (np.float32(fx["bias0"]) + i * np.float32(fx["bias_step"])).astype(np.float32).reshape(n, gpr)
+    t = np.arange(m * k, dtype=np.float32) * np.float32(fx["x_mul"]) + np.float32(fx["x_add"])
+    x = ((np.sin(t) if fx["x_fn"] == "sin" else np.cos(t)) * np.float32(fx["x_amp"])).astype(np.float32)
+    return _q4_from(q, scales, biases), q, scales, biases, x.reshape(m, k)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_gemv4_matches_exact_rational_sum_on_page_fixtures(idx):
+    fx = _golden("page_gemv_fixtures.json")["fixtures"][idx]
+    w, q, s, b, x = _page_fixture(fx)
+    y = oracle.gemv4(w, x)
+    m, n, k = fx["m"], fx["n"], fx["k"]
+    rows = range(m) if m * n * k <= 40000 else [0, m // 2, m - 1]
+    for r in rows:
+        xf = [Fraction(float(v)) for v in x[r]]
+        for o in range(n):
+            acc = Fraction(0)
+            for c in range(k):
+                acc += xf[c] * (Fraction(float(s[o, c // 32])) * int(q[o, c]) + Fraction(float(b[o, c // 32])))
+            ex = float(acc)
+            assert abs(float(y[r, o]) - ex) <= 0.5 * _ulp32(ex) + 1e-12, (r, o, y[r, o], ex)
+    # the page's own acceptance bound against its double-precision sum
+    ref = (x.astype(np.float64) @ (q.astype(np.float64) * np.repeat(s, 32, 1) + np.repeat(b, 32, 1)).T)
+    assert np.abs(y - ref).max() < 1e-3
+
+
+def test_gemv4_one_hot_input_selects_a_column_of_w():
+    g = np.random.default_rng(3)
+    w = synth.q4_weight(g, 40, 96)  # non-square: a transposed operand cannot pass
+    d = oracle.deq4(w)
+    for j in [0, 31, 32, 95]:
+        x = np.zeros((1, 96), np.float32)
+        x[0, j] = 1.0
+        y = oracle.gemv4(w, x)[0]
+        assert (y.view(np.uint32) == d[:, j].view(np.uint32)).all()
+
+
+def test_gemv4_midpoint_codes_give_zero():
+    g = np.random.default_rng(4)
+    s = g.uniform(0.005, 0.02, size=(6, 4)).astype(np.float32)
+    w = _q4_from(np.full((6, 128), 8, np.uint8), s, (-8 * s).astype(np.float32))
+    y = oracle.gemv4(w, synth.normal(g, (3, 128)))
+    assert (y == 0).all()
+
+
+def test_gemv8_exact_and_one_hot():
+    g = np.random.default_rng(8)
+    w = synth.q8_weight(g, 1, 5, 64)
+    x = synth.normal(g, (2, 64))
+    y = oracle.gemv8(w, x)
+    for r in range(2):
+        for o in range(5):
+            acc = sum(Fraction(float(x[r, c])) * Fraction(float(w.scales[0, o, c // 32])) * int(w.codes[0, o, c])
+                      for c in range(64))
+            assert abs(float(y[r, o]) - float(acc)) <= 0.5 * _ulp32(float(acc)) + 1e-12
+    d = oracle.deq8(w)
+    e = np.zeros((1, 64), np.float32)
+    e[0, 40] = 1.0
+    assert (oracle.gemv8(w, e)[0] == d[:, 40]).all()
+
+
+def test_gemv_f32_one_hot_and_exact():
+    g = np.random.default_rng(9)
+    w = synth.normal(g, (6, 64), 0.02)
+    e = np.zeros((1, 64), np.float32)
+    e[0, 17] = 1.0
+    assert (oracle.gemv_f32(w, e)[0] == w[:, 17]).all()
+    x = synth.normal(g, (1, 64))
+    y = oracle.gemv_f32(w, x)[0]
+    for o in range(6):
+        ex = float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[0], w[o])))
+        assert abs(float(y[o]) - ex) <= 0.5 * _ulp32(ex) + 1e-15
+
+
+# --------------------------------------------------------------------------
+# RMSNorm, RoPE, attention
+# --------------------------------------------------------------------------
+def test_rmsnorm_closed_forms():
+    for c in _golden("rmsnorm_closed_form.json")["cases"]:
+        y = oracle.rmsnorm(np.array([c["x"]], np.float32), np.array(c["gamma"], np.float32), c["eps"])[0]
+        for got, want in zip(y, c["y"]):
+            assert abs(float(got) - want) <= 0.5 * _ulp32(want), (c, y)
+
+
+def test_rmsnorm_scale_invariance():
+    g = np.random.default_rng(1)
+    x = synth.normal(g, (2, 64))
+    gam = synth.gamma(g, 64)
+    a = oracle.rmsnorm(x, gam, 0.0)
+    b = oracle.rmsnorm(x * np.float32(8.0), gam, 0.0)
+    assert (a == b).all()
+
+
+def test_rope_closed_form_half_split_pairs():
+    theta = 1.0e6
+    x = np.array([[0.3, -1.2, 0.7, 2.0]], np.float32)  # one head, head_dim 4: pairs (0,2) and (1,3)
+    p = 5
+    y = oracle.rope(x, 1, 4, p, theta)[0]
+    f0, f1 = 1.0, theta ** -0.5
+    exp = [0.3 * math.cos(p * f0) - 0.7 * math.sin(p * f0),
+           -1.2 * math.cos(p * f1) - 2.0 * math.sin(p * f1),
+           0.3 * math.sin(p * f0) + 0.7 * math.cos(p * f0),
+           -1.2 * math.sin(p * f1) + 2.0 * math.cos(p * f1)]
+    xd = [float(v) for v in x[0]]
+    exp = [xd[0] * math.cos(p * f0) - xd[2] * math.sin(p * f0),
+           xd[1] * math.cos(p * f1) - xd[3] * math.sin(p * f1),
+           xd[0] * math.sin(p * f0) + xd[2] * math.cos(p * f0),
+           xd[1] * math.sin(p * f1) + xd[3] * math.cos(p * f1)]
+    assert np.allclose(y, np.array(exp, np.float32), rtol=0, atol=2e-7)
+
+
+def test_rope_identity_norm_and_relative_position():
+    g = np.random.default_rng(2)
+    q = synth.normal(g, (1, 2 * 128))
+    k = synth.normal(g, (1, 128))
+    assert (oracle.rope(q, 2, 128, 0, 1e6) == q).all()
+    r = oracle.rope(q, 2, 128, 4099, 1e6)
+    half = 64
+    for hh in range(2):
+        a, b = q[0, hh * 128:hh * 128 + half].astype(np.float64), q[0, hh * 128 + half:(hh + 1) * 128].astype(np.float64)
+        ra, rb = r[0, hh * 128:hh * 128 + half].astype(np.float64), r[0, hh * 128 + half:(hh + 1) * 128].astype(np.float64)
+        assert np.allclose(a * a + b * b, ra * ra + rb * rb, rtol=1e-5, atol=1e-6)
+    q1 = q[:, :128]
+    d1 = float(oracle.rope(q1, 1, 128, 100, 1e6)[0].astype(np.float64) @ oracle.rope(k, 1, 128, 90, 1e6)[0])
+    d2 = float(oracle.rope(q1, 1, 128, 1010, 1e6)[0].astype(np.float64) @ oracle.rope(k, 1, 128, 1000, 1e6)[0])
+    assert abs(d1 - d2) < 1e-4 * (1 + abs(d1))
+
+
+def _caches(g, nkv, cap, d):
+    return synth.normal(g, (nkv, cap, d)), synth.normal(g, (nkv, cap, d))
+
+
+def test_sdpa_length_one_cache_returns_v():
+    g = np.random.default_rng(6)
+    kc, vc = _caches(g, 2, 4, 16)
+    q = synth.normal(g, (1, 4 * 16))
+    o = oracle.sdpa(q, kc, vc, 4, 0)
+    for hh in range(4):
+        assert (o[0, hh * 16:(hh + 1) * 16] == vc[hh // 2, 0]).all()
+
+
+def test_sdpa_equal_keys_average_values_per_kv_group():
+    g = np.random.default_rng(7)
+    nkv, cap, d, L = 2, 9, 8, 6
+    kc = np.zeros((nkv, cap, d), np.float32)
+    kc[:] = synth.normal(g, (1, 1, d))
+    vc = synth.normal(g, (nkv, cap, d))
+    q = synth.normal(g, (1, 4 * d))
+    o = oracle.sdpa(q, kc, vc, 4, L - 1)  # row 0 sees rows 0..L-1
+    for hh in range(4):
+        want = vc[hh // 2, :L].astype(np.float64).mean(axis=0)
+        assert np.allclose(o[0, hh * d:(hh + 1) * d], want, rtol=0, atol=1e-6)
+
+
+def test_sdpa_dominant_score_and_causal_rows():
+    g = np.random.default_rng(8)
+    nkv, cap, d = 1, 8, 8
+    kc = synth.normal(g, (nkv, cap, d), 0.01)
+    vc = synth.normal(g, (nkv, cap, d))
+    q = np.zeros((2, d), np.float32)
+    q[:, 0] = 50.0
+    kc[0, 3, 0] = 10.0  # score 500/sqrt(8) dominates every other key
+    o = oracle.sdpa(q, kc, vc, 1, 4)
+    assert np.allclose(o[0], vc[0, 3], atol=1e-6)
+    # causal: row 0 (length 5) must ignore row 5, which row 1 (length 6) sees
+    kc[0, 5, 0] = 20.0
+    o2 = oracle.sdpa(q, kc, vc, 1, 4)
+    assert (o2[0] == o[0]).all()
+    assert np.allclose(o2[1], vc[0, 5], atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# layer steps
+# --------------------------------------------------------------------------
+def _small_layer(seed=21, H=64, nh=4, nkv=2, d=16, inter=96, vocab=300):
+    return synth.dense_layer(np.random.default_rng(seed), hidden=H, n_heads=nh, n_kv_heads=nkv, head_dim=d,
+                             vocab=vocab, ffn_inter=inter)
+
+
+def test_norm_concat_proj_embedding_half_first():
+    g = np.random.default_rng(12)
+    H = 64
+    w = synth.q4_weight(g, 32, 2 * H)
+    w.scales[:, H // 32:] = 0.0  # weights over the hidden half are exactly zero
+    w.biases[:, H // 32:] = 0.0
+    e, h = synth.normal(g, (2, H)), synth.normal(g, (2, H))
+    ge, gh = synth.gamma(g, H), synth.gamma(g, H)
+    u = oracle.norm_concat_proj(e, h, ge, gh, 1e-6, w)
+    u2 = oracle.norm_concat_proj(e, synth.normal(g, (2, H)), ge, gh, 1e-6, w)
+    assert (u == u2).all()
+    left = synth.Q4(w.codes[:, : H // 8].copy(), w.scales[:, : H // 32].copy(), w.biases[:, : H // 32].copy())
+    assert np.array_equal(u, oracle.gemv4(left, oracle.rmsnorm(e, ge, 1e-6)))
+    u3 = oracle.norm_concat_proj(synth.normal(g, (2, H)), h, ge, gh, 1e-6, w)
+    assert not np.array_equal(u, u3)
+
+
+def test_ffn_zero_gate_returns_residual_and_closed_form():
+    g = np.random.default_rng(13)
+    H, inter = 64, 32
+    gate, up, down = synth.q4_weight(g, inter, H), synth.q4_weight(g, inter, H), synth.q4_weight(g, H, inter)
+    x, res = synth.normal(g, (2, H)), synth.normal(g, (2, H))
+    zg = synth.Q4(gate.codes, np.zeros_like(gate.scales), np.zeros_like(gate.biases))
+    assert (oracle.ffn_dense(x, zg, up, down, res) == res).all()
+    # one-hot x: a_i, b_i are single weights; y = res + sum_i Wd[n,i] * silu(a_i) * b_i
+    xo = np.zeros((1, H), np.float32)
+    xo[0, 37] = 1.0
+    dg, du, dd = oracle.deq4(gate), oracle.deq4(up), oracle.deq4(down)
+    y = oracle.ffn_dense(xo, gate, up, down, res[:1])[0]
+    a = dg[:, 37].astype(np.float64)
+    z = (a / (1.0 + np.exp(-a)) * du[:, 37].astype(np.float64)).astype(np.float32).astype(np.float64)
+    codes = synth.unpack_q4_codes(down.codes).astype(np.float64)
+    wd = codes * np.repeat(down.scales, 32, 1).astype(np.float64) + np.repeat(down.biases, 32, 1).astype(np.float64)
+    want = (res[0].astype(np.float64) + wd @ z).astype(np.float32)
+    assert np.allclose(y, want, rtol=0, atol=2e-6)
+    assert abs(dd[0, 0] - np.float32(wd[0, 0])) == 0
+
+
+def _moe_small(seed, E=6, k=2, H=64, inter=32, shared=32, m=3):
+    return synth.moe_inputs(np.random.default_rng(seed), m, hidden=H, n_experts=E, inter=inter, top_k=k,
+                            shared_inter=shared)
+
+
+def test_moe_gates_sum_to_one_and_selection_is_a_full_sort():
+    inp = _moe_small(31, E=16, k=4)
+    y, ids, gates, logits = oracle.moe(inp)
+    assert np.allclose(gates.astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
+    for r in range(ids.shape[0]):
+        order = sorted(range(16), key=lambda e: (-float(logits[r, e]), e))
+        assert ids[r].tolist() == order[:4]
+        assert (np.diff(gates[r]) <= 0).all()
+    assert np.array_equal(logits, oracle.gemv_f32(inp.router, inp.x))
+
+
+def test_moe_all_experts_selected_gives_softmax_gates():
+    inp = _moe_small(32, E=5, k=5)
+    _, ids, gates, logits = oracle.moe(inp)
+    for r in range(ids.shape[0]):
+        l = logits[r].astype(np.float64)
+        p = np.exp(l - l.max())
+        p /= p.sum()
+        assert np.allclose(gates[r], p[ids[r]], rtol=0, atol=1e-7)
+
+
+def test_moe_identical_experts_equal_one_expert_plus_shared_and_residual():
+    inp = _moe_small(33, E=6, k=3)
+    for stack in (inp.gate_exps, inp.up_exps, inp.down_exps):
+        stack.codes[:] = stack.codes[0]
+        stack.scales[:] = stack.scales[0]
+    res = synth.normal(np.random.default_rng(1), inp.x.shape)
+    y, _, _, _ = oracle.moe(inp, residual=res)
+    one = synth.MoeInputs(inp.x, inp.router[:1], synth.Q8(inp.gate_exps.codes[:1], inp.gate_exps.scales[:1]),
+                          synth.Q8(inp.up_exps.codes[:1], inp.up_exps.scales[:1]),
+                          synth.Q8(inp.down_exps.codes[:1], inp.down_exps.scales[:1]), None, None, None, 1)
+    single, _, g1, _ = oracle.moe(one)
+    assert (g1 == 1.0).all()
+    sh = synth.MoeInputs(inp.x, inp.router[:1], inp.sh_gate, inp.sh_up, inp.sh_down, None, None, None, 1)
+    shared_only, _, _, _ = oracle.moe(sh)
+    want = res.astype(np.float64) + single.astype(np.float64) + shared_only.astype(np.float64)
+    assert np.allclose(y, want, rtol=0, atol=1e-5)
+
+
+def test_head_argmax_is_the_index_of_the_max_logit_with_ties_low():
+    g = np.random.default_rng(41)
+    lm = synth.q4_weight(g, 500, 64)
+    x, gam = synth.normal(g, (3, 64)), synth.gamma(g, 64)
+    normed, logits, ids = oracle.head(x, gam, 1e-6, lm)
+    assert np.array_equal(normed, oracle.rmsnorm(x, gam, 1e-6))
+    assert np.array_equal(logits, oracle.gemv4(lm, normed))
+    assert ids.tolist() == [int(np.argmax(row)) for row in logits]
+    v = np.array([1.0, 3.0, -2.0, 3.0, np.nan, 3.0], np.float32)
+    assert oracle.argmax(v) == 1
+    assert oracle.argmax(np.array([np.nan, -1.0, -0.5], np.float32)) == 2
+
+
+def test_draft_step_batched_verify_equals_the_sequential_chain():
+    L = _small_layer()
+    g = np.random.default_rng(55)
+    cap, L0 = 40, 30
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, L0, cap, L.head_dim)
+    table = synth.normal(g, (L.vocab, L.hidden))
+    e0, h0 = synth.normal(g, (1, L.hidden)), synth.normal(g, (1, L.hidden))
+    k1, v1 = kc.copy(), vc.copy()
+    toks, hs, ids_chain, hid_chain, log_chain = [-1], [h0[0]], [], [], []
+    for step in range(3):
+        ids, hid, lg = oracle.draft_step(L, e0, np.array([toks[-1]], np.int32), table, hs[-1][None], k1, v1, L0 + step)
+        toks.append(int(ids[0]))
+        hs.append(hid[0])
+        ids_chain.append(int(ids[0]))
+        hid_chain.append(hid[0])
+        log_chain.append(lg[0])
+    k2, v2 = kc.copy(), vc.copy()
+    ids_v, hid_v, log_v = oracle.draft_step(L, np.repeat(e0, 4, 0), np.array(toks, np.int32), table,
+                                            np.stack(hs), k2, v2, L0)
+    assert ids_v[:3].tolist() == ids_chain
+    assert np.array_equal(hid_v[:3], np.stack(hid_chain))
+    assert np.array_equal(log_v[:3], np.stack(log_chain))
+    assert np.array_equal(k2[:, : L0 + 3], k1[:, : L0 + 3]) and np.array_equal(v2[:, : L0 + 3], v1[:, : L0 + 3])
+    assert np.array_equal(k2[:, :L0], kc[:, :L0])
+
+
+def test_draft_step_rejects_bad_arguments_without_writing():
+    L = _small_layer()
+    g = np.random.default_rng(56)
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, 10, 12, L.head_dim)
+    k0 = kc.copy()
+    h = synth.normal(g, (4, L.hidden))
+    with pytest.raises(ValueError):
+        oracle.draft_step(L, h, None, None, h, kc, vc, 10)  # 10 + 4 > capacity 12
+    with pytest.raises(ValueError):
+        oracle.draft_step(L, None, np.array([L.vocab], np.int32), synth.normal(g, (L.vocab, L.hidden)), h[:1], kc, vc, 0)
+    assert np.array_equal(kc, k0)
+
+
+def test_attention_on_empty_cache_reduces_to_the_value_row():
+    """With cache_len 0 and one row, attention returns v, so r1 = u + Wo v."""
+    L = _small_layer(seed=22)
+    g = np.random.default_rng(57)
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, 0, 4, L.head_dim)
+    u = synth.normal(g, (1, L.hidden))
+    r1 = oracle.attention(L, u, kc, vc, 0)
+    xa = oracle.rmsnorm(u, L.gamma_attn, L.eps)
+    v = oracle.gemv4(L.wv, xa)[0].reshape(L.n_kv_heads, L.head_dim)
+    assert np.array_equal(vc[:, 0], v)
+    o = np.concatenate([v[hh // (L.n_heads // L.n_kv_heads)] for hh in range(L.n_heads)])[None]
+    want = (u.astype(np.float64) + oracle.gemv4(L.wo, o).astype(np.float64)).astype(np.float32)
+    assert np.array_equal(r1, want)
