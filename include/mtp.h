@@ -1,0 +1,211 @@
+/*
+ * mtp.h -- C ABI of libmtp: the quantized-weight forward of one
+ * Multi-Token-Prediction (MTP / NextN) draft layer on AMD Instinct MI355X
+ * (gfx950), at m = 1 row for drafting and m = K+1 rows for a batched verify.
+ *
+ * Sources (public pages, cited by title and Rust item):
+ *   [mtp.rs]    hf2q 0.1.13, src/inference/models/qwen35/mtp.rs
+ *   [mimo.rs]   cortiq-engine 0.8.49, src/mimo_mtp.rs
+ *   [shared.rs] hf2q 0.1.1, src/serve/forward_mlx_shared.rs
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is DEVICE memory owned by the caller, unless a
+ *   comment says "host".  The library never allocates, frees or keeps device
+ *   memory; scratch space is the caller's `ws` of at least the size the
+ *   matching *_workspace_size() call returns.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work and return; outputs are valid once the stream has reached
+ *   that point.  Calls that share an output or a workspace must be ordered on
+ *   one stream.  Inputs and outputs must not alias unless stated.
+ * - Activations, logits and norm weights are f32, row-major, rows contiguous.
+ *   Row pointers (x, e, h, u, hidden, ...) must be 16-byte aligned and
+ *   quantized code arrays 16-byte aligned.
+ * - m (rows) is 1 .. MTP_MAX_ROWS.  Input features k are a multiple of 32 and
+ *   at most MTP_MAX_K.
+ * - All argument checks run on the host before anything is enqueued: a call
+ *   that returns an error has launched nothing and written nothing (the KV
+ *   cache included).  mtp_last_error() then describes the failure (a
+ *   thread-local string).  A failed HIP launch returns MTP_ERR_HIP.
+ * - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef MTP_H
+#define MTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_MAX_ROWS 8
+#define MTP_GROUP 32
+#define MTP_MAX_K 8192
+
+typedef enum {
+    MTP_OK = 0,
+    MTP_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, cache overflow */
+    MTP_ERR_UNSUPPORTED = 2, /* a shape this build does not implement */
+    MTP_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes below the required size */
+    MTP_ERR_HIP = 4          /* a HIP runtime error while enqueuing */
+} mtp_status;
+
+/* 4-bit affine weight, group 32 ([shared.rs] `MlxAffineExtra`,
+ * `MlxQWeight::from_mlx_affine_linear`): a matrix of n output rows and k
+ * input features, stored out x in.
+ *   codes  u32 [n][k/8]: element k of a row is nibble k%8 of word k/8, the
+ *          low nibble holding the lowest k;
+ *   scales f32 [n][k/32], biases f32 [n][k/32]: value = scale*code + bias. */
+typedef struct {
+    const uint32_t* codes;
+    const float* scales;
+    const float* biases;
+    int32_t n, k;
+} mtp_q4;
+
+/* 8-bit block weight, block 32, as a stack of n_experts matrices
+ * (n_experts = 1 for a single matrix):
+ *   codes  int8 [n_experts][n][k], scales f32 [n_experts][n][k/32];
+ *   value = scale * code. */
+typedef struct {
+    const int8_t* codes;
+    const float* scales;
+    int32_t n, k, n_experts;
+} mtp_q8;
+
+#define MTP_FFN_DENSE_Q4 0
+#define MTP_FFN_MOE_Q8 1
+
+/* One MTP draft layer ([mimo.rs] module doc "The draft forward"; [mtp.rs]
+ * `MtpWeights`, `MtpFullAttnWeightsGpu`, `MtpFfnWeightsGpu`).
+ * Shapes: eh_proj [hidden][2*hidden]; wq [n_heads*head_dim][hidden];
+ * wk, wv [n_kv_heads*head_dim][hidden]; wo [hidden][n_heads*head_dim];
+ * dense FFN: gate, up [ffn_inter][hidden], down [hidden][ffn_inter];
+ * MoE FFN: router f32 [n_experts][hidden], gate_exps/up_exps
+ * [n_experts][inter][hidden], down_exps [n_experts][hidden][inter], optional
+ * shared expert sh_* (n_experts = 1); lm_head [vocab][hidden].
+ * gamma_* are f32 [hidden] norm weights applied as x/rms(x)*gamma. */
+typedef struct {
+    int32_t hidden, n_heads, n_kv_heads, head_dim, vocab;
+    int32_t ffn_kind; /* MTP_FFN_DENSE_Q4 or MTP_FFN_MOE_Q8 */
+    int32_t ffn_inter;
+    int32_t top_k;
+    double rope_theta;
+    float eps;
+    const float *gamma_e, *gamma_h, *gamma_attn, *gamma_post, *gamma_final;
+    mtp_q4 eh_proj, wq, wk, wv, wo, gate, up, down, lm_head;
+    const float* router;
+    mtp_q8 gate_exps, up_exps, down_exps, sh_gate, sh_up, sh_down;
+} mtp_layer;
+
+const char* mtp_status_string(mtp_status s);
+const char* mtp_last_error(void);
+const char* mtp_version(void);
+
+/* ---------------------------------------------------------------------- */
+/* Workspace sizes (bytes; 0 when the call needs none)                     */
+/* ---------------------------------------------------------------------- */
+size_t mtp_attn_decode_workspace_size(const mtp_layer* L, int32_t cache_len, int32_t m);
+size_t mtp_ffn_dense_workspace_size(int32_t ffn_inter, int32_t m);
+size_t mtp_ffn_moe_workspace_size(int32_t hidden, int32_t n_experts, int32_t top_k, int32_t inter,
+                                  int32_t shared_inter, int32_t m);
+size_t mtp_lmhead_workspace_size(int32_t vocab, int32_t m);
+size_t mtp_draft_step_workspace_size(const mtp_layer* L, int32_t cache_len, int32_t m);
+
+/* ---------------------------------------------------------------------- */
+/* Test exports: dequantize through the same device routine the GEMVs use  */
+/* ---------------------------------------------------------------------- */
+/* out f32 [n][k] = scale*code + bias, rounded once to f32 ([shared.rs]
+ * `MlxAffineExtra`). */
+mtp_status mtp_dequant_q4(const mtp_q4* w, float* out, void* stream);
+/* out f32 [n][k] = scale*code of matrix `expert` of the stack. */
+mtp_status mtp_dequant_q8(const mtp_q8* w, int32_t expert, float* out, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Hot-path calls                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* y[m][w->n] = x[m][w->k] * W^T (+ residual[m][w->n] when not NULL): the
+ * quantized linear of [shared.rs] `dispatch_qmatmul` (affine route) and
+ * [mtp.rs] `apply_linear_projection_f32_with_ggml_type`.  y may alias
+ * residual. */
+mtp_status mtp_qgemv(const mtp_q4* w, const float* x, const float* residual, float* y, int32_t m,
+                     void* stream);
+
+/* The 8-bit counterpart of mtp_qgemv on matrix `expert` of a stack. */
+mtp_status mtp_q8gemv(const mtp_q8* w, int32_t expert, const float* x, const float* residual, float* y,
+                      int32_t m, void* stream);
+
+/* u[m][H] = eh_proj * [rms(e; gamma_e) ; rms(h; gamma_h)] with the embedding
+ * half first ([mtp.rs] `project_embedding_and_hidden`; [mimo.rs] module doc).
+ * e, h [m][H]; eh_proj n = H, k = 2H.  The concatenation is never stored. */
+mtp_status mtp_norm_concat_proj(const float* e, const float* h, const float* gamma_e, const float* gamma_h,
+                                float eps, const mtp_q4* eh_proj, float* u, int32_t m, void* stream);
+
+/* Attention block with its residual ([mtp.rs] `forward_full_attention`):
+ *   xa = rms(u; gamma_attn); q = Wq xa, k = Wk xa, v = Wv xa;
+ *   RoPE (half-split pairs, theta^(-2i/d)) on q and k at positions
+ *   cache_len + r; the m new k (post-RoPE) and v rows are written to cache
+ *   rows cache_len .. cache_len+m-1; causal GQA attention (query head h reads
+ *   KV head h / (n_heads/n_kv_heads), scale 1/sqrt(head_dim)) over rows
+ *   0 .. cache_len + r; out = u + Wo * attn.
+ * k_cache, v_cache f32 [n_kv_heads][capacity][head_dim].  Requires
+ * cache_len + m <= capacity and head_dim == 128. Uses only L's attention
+ * fields. out [m][hidden] must not alias u. */
+mtp_status mtp_attn_decode(const mtp_layer* L, const float* u, float* k_cache, float* v_cache,
+                           int32_t cache_len, int32_t capacity, int32_t m, float* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Dense SwiGLU with 4-bit weights ([mtp.rs] `forward_ffn_residual`, DenseQ):
+ *   f = gamma ? rms(x; gamma) : x;  y = [residual +] down*(silu(gate f).(up f)).
+ * x, residual, y [m][H]; y may alias residual but not x. */
+mtp_status mtp_ffn_dense_q(const float* x, const float* gamma, float eps, const mtp_q4* gate,
+                           const mtp_q4* up, const mtp_q4* down, const float* residual, float* y,
+                           int32_t m, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed mixture of 8-bit SwiGLU experts plus an optional shared expert
+ * ([mtp.rs] `MtpFfnWeightsGpu::Moe`).  Per row: f = gamma ? rms(x) : x;
+ * router logits l = router f (router f32 [n_experts][H]); p = softmax(l);
+ * the top_k experts by (p descending, index ascending); gates p_e / sum of
+ * the selected p; y = [residual] + sum_e gate_e * expert_e(f) + shared(f).
+ * expert_ids int32 [m][top_k] and gates f32 [m][top_k] (selection order) are
+ * optional outputs.  sh_gate/sh_up/sh_down are all NULL or all set. */
+mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
+                         const mtp_q8* gate_exps, const mtp_q8* up_exps, const mtp_q8* down_exps,
+                         const mtp_q8* sh_gate, const mtp_q8* sh_up, const mtp_q8* sh_down,
+                         const float* residual, float* y, int32_t* expert_ids, float* gates, int32_t m,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Shared head with a greedy pick ([mtp.rs] `forward_shared_head_greedy`):
+ *   yn = rms(hidden; gamma); logits = lm_head yn; ids[r] = argmax_v logits[r][v]
+ * (ties to the lowest index).  normed_out [m][H] and logits_out [m][V] are
+ * optional (NULL skips them); ids_out int32 [m] is required. */
+mtp_status mtp_lmhead_argmax(const float* hidden, const float* gamma, float eps, const mtp_q4* lm_head,
+                             float* normed_out, float* logits_out, int32_t* ids_out, int32_t m, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* One draft-layer forward over m rows at positions cache_len .. cache_len+m-1
+ * ([mimo.rs] "The draft forward" and `mimo_mtp_block_with_probe`; [mtp.rs]
+ * `forward_draft_body` and `forward_shared_head_greedy`):
+ *   u  = eh_proj [rms(e_r; gamma_e) ; rms(h_r; gamma_h)]
+ *   r1 = u + attention(rms(u; gamma_attn))   (appends K/V rows)
+ *   r2 = r1 + ffn(rms(r1; gamma_post))        (dense 4-bit or MoE 8-bit)
+ *   hidden_out = rms(r2; gamma_final), logits = lm_head hidden_out,
+ *   ids_out = argmax.
+ * Row r's embedding e_r is embed_table[tokens[r]] when tokens is not NULL and
+ * tokens[r] >= 0 (device int32 [m]; embed_table f32 [vocab][H]), else row r
+ * of e [m][H].  Token ids are read on the device: an id >= vocab is clamped
+ * to vocab-1.  hidden_out [m][H] is the post-final-norm row, the input of a
+ * chained next step ([mtp.rs] `forward_draft_with_hidden`); logits_out
+ * [m][vocab] is optional.  The call never advances any cursor: the caller
+ * owns cache_len and rolls back by passing a smaller one. */
+mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                          const float* h, float* k_cache, float* v_cache, int32_t cache_len,
+                          int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,
+                          float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTP_H */

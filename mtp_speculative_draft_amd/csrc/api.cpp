@@ -1,0 +1,656 @@
+// api.cpp -- the C ABI of libmtp (declared in include/mtp.h): argument checks,
+// workspace carving and the launch sequence of each call.  Every check runs
+// before the first enqueue, so a rejected call has no effect on the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mtp.h"
+#include "launch.hpp"
+
+using namespace mtp;
+
+namespace {
+
+thread_local std::string g_err;
+
+mtp_status fail(mtp_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+mtp_status hip_fail(hipError_t e, const char* what) {
+    return fail(MTP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap (sizes the argmax partials)
+
+mtp_status check_rows(int32_t m) {
+    if (m < 1 || m > MTP_MAX_ROWS) return fail(MTP_ERR_INVALID_ARG, "m=%d outside 1..%d", m, MTP_MAX_ROWS);
+    return MTP_OK;
+}
+
+mtp_status check_q4(const mtp_q4* w, const char* name) {
+    if (!w) return fail(MTP_ERR_INVALID_ARG, "%s: descriptor is NULL", name);
+    if (!w->codes || !w->scales || !w->biases) return fail(MTP_ERR_INVALID_ARG, "%s: NULL codes/scales/biases", name);
+    if (w->n < 1) return fail(MTP_ERR_INVALID_ARG, "%s: n=%d must be >= 1", name, w->n);
+    if (w->k < MTP_GROUP || w->k % MTP_GROUP) return fail(MTP_ERR_INVALID_ARG, "%s: k=%d must be a positive multiple of 32", name, w->k);
+    if (w->k > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "%s: k=%d above %d", name, w->k, MTP_MAX_K);
+    if (!a16(w->codes) || !a4(w->scales) || !a4(w->biases)) return fail(MTP_ERR_INVALID_ARG, "%s: misaligned pointer", name);
+    return MTP_OK;
+}
+
+mtp_status check_q8(const mtp_q8* w, const char* name) {
+    if (!w) return fail(MTP_ERR_INVALID_ARG, "%s: descriptor is NULL", name);
+    if (!w->codes || !w->scales) return fail(MTP_ERR_INVALID_ARG, "%s: NULL codes/scales", name);
+    if (w->n < 1 || w->n_experts < 1) return fail(MTP_ERR_INVALID_ARG, "%s: n=%d n_experts=%d", name, w->n, w->n_experts);
+    if (w->k < MTP_GROUP || w->k % MTP_GROUP) return fail(MTP_ERR_INVALID_ARG, "%s: k=%d must be a positive multiple of 32", name, w->k);
+    if (w->k > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "%s: k=%d above %d", name, w->k, MTP_MAX_K);
+    if (!a16(w->codes) || !a4(w->scales)) return fail(MTP_ERR_INVALID_ARG, "%s: misaligned pointer", name);
+    return MTP_OK;
+}
+
+mtp_status check_vec(const void* p, const char* name) {
+    if (!p) return fail(MTP_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!a16(p)) return fail(MTP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return MTP_OK;
+}
+
+QMat qmat(const mtp_q4& w) { return QMat{w.codes, w.scales, w.biases, w.n}; }
+QMat qmat8(const mtp_q8& w, int expert) {
+    const int64_t gpr = w.k / MTP_GROUP;
+    return QMat{static_cast<const int8_t*>(w.codes) + (int64_t)expert * w.n * w.k,
+                w.scales + (int64_t)expert * w.n * gpr, nullptr, w.n};
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).  With
+// base == nullptr it only measures.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    template <class T>
+    T* take(size_t count) {
+        off = (off + 255) & ~size_t(255);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+int chunks_for(int32_t cache_len, int32_t m) { return (cache_len + m + kAttnChunk - 1) / kAttnChunk; }
+
+// ---- per-call workspace layouts ----
+struct AttnWs {
+    float *qkv, *part, *o;
+};
+AttnWs carve_attn(Carve& c, const mtp_layer* L, int32_t cache_len, int32_t m) {
+    AttnWs w;
+    const int d = L->head_dim, nh = L->n_heads, nkv = L->n_kv_heads;
+    w.qkv = c.take<float>((size_t)m * (nh + 2 * nkv) * d);
+    w.part = c.take<float>((size_t)chunks_for(cache_len, m) * nkv * (nh / (nkv ? nkv : 1)) * m * (d + 2));
+    w.o = c.take<float>((size_t)m * nh * d);
+    return w;
+}
+
+struct HeadWs {
+    float* pv;
+    int* pi;
+};
+HeadWs carve_head(Carve& c, int32_t m) {
+    HeadWs w;
+    w.pv = c.take<float>((size_t)kHeadMaxBlocks * 4 * m);
+    w.pi = c.take<int>((size_t)kHeadMaxBlocks * 4 * m);
+    return w;
+}
+
+struct MoeWs {
+    float *f, *logits, *gates, *slot_gate, *z, *ypart;
+    int *ids, *slot_expert, *n_slots;
+    int max_slots;
+};
+MoeWs carve_moe(Carve& c, int H, int E, int top_k, int inter, int sh_inter, int m) {
+    MoeWs w;
+    const int routed = (m * top_k < E) ? m * top_k : E;
+    w.max_slots = routed + (sh_inter > 0 ? 1 : 0);
+    const int imax = inter > sh_inter ? inter : sh_inter;
+    w.f = c.take<float>((size_t)m * H);
+    w.logits = c.take<float>((size_t)m * E);
+    w.ids = c.take<int>((size_t)m * top_k);
+    w.gates = c.take<float>((size_t)m * top_k);
+    w.slot_expert = c.take<int>((size_t)w.max_slots);
+    w.slot_gate = c.take<float>((size_t)w.max_slots * m);
+    w.n_slots = c.take<int>(1);
+    w.z = c.take<float>((size_t)w.max_slots * m * imax);
+    w.ypart = c.take<float>((size_t)w.max_slots * m * H);
+    return w;
+}
+
+mtp_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return MTP_OK;
+    if (!ws) return fail(MTP_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (ws_bytes < need) return fail(MTP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(MTP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return MTP_OK;
+}
+
+// ---- shared launch helpers ----
+hipError_t run_gemv(int fmt, int pro, int epi, int m, GemvParams& p, int max_blocks, hipStream_t st) {
+    p.m = m;
+    p.G = p.K / MTP_GROUP;
+    p.S = (p.G + 63) / 64;
+    const GemvShape sh = gemv_shape(fmt, epi, m, p.N, p.K, max_blocks);
+    return launch_gemv(fmt, pro, epi, m, p, sh, st);
+}
+
+int default_blocks() { return 4 * device_cu_count(); }
+
+hipError_t run_head(const float* hidden, const float* gamma, float eps, const mtp_q4& lm, float* normed_out,
+                    float* logits_out, int* ids, int m, const HeadWs& w, hipStream_t st) {
+    GemvParams p{};
+    p.w[0] = qmat(lm);
+    p.nmat = 1;
+    p.N = lm.n;
+    p.K = lm.k;
+    p.x0 = hidden;
+    p.g0 = gamma;
+    p.eps = eps;
+    p.normed_out = normed_out;
+    p.logits = logits_out;
+    p.part_val = w.pv;
+    p.part_idx = w.pi;
+    p.m = m;
+    p.G = p.K / MTP_GROUP;
+    p.S = (p.G + 63) / 64;
+    int maxb = 2 * device_cu_count();
+    if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
+    const GemvShape sh = gemv_shape(FMT_Q4, EPI_ARGMAX, m, p.N, p.K, maxb);
+    hipError_t e = launch_gemv(FMT_Q4, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
+    if (e != hipSuccess) return e;
+    return launch_argmax_final(w.pv, w.pi, sh.grid * sh.Q, m, ids, st);
+}
+
+hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* vc, int cache_len, int capacity,
+                         int m, float* out, const AttnWs& w, hipStream_t st) {
+    GemvParams p{};
+    p.w[0] = qmat(L->wq);
+    p.w[1] = qmat(L->wk);
+    p.w[2] = qmat(L->wv);
+    p.nmat = 3;
+    p.N = L->wq.n + L->wk.n + L->wv.n;
+    p.K = L->hidden;
+    p.x0 = u;
+    p.g0 = L->gamma_attn;
+    p.eps = L->eps;
+    p.y = w.qkv;
+    hipError_t e = run_gemv(FMT_Q4, PRO_RMS, EPI_STORE, m, p, default_blocks(), st);
+    if (e != hipSuccess) return e;
+    AttnParams a{};
+    a.qkv = w.qkv;
+    a.k_cache = kc;
+    a.v_cache = vc;
+    a.cache_len = cache_len;
+    a.capacity = capacity;
+    a.m = m;
+    a.nh = L->n_heads;
+    a.nkv = L->n_kv_heads;
+    a.d = L->head_dim;
+    a.theta = L->rope_theta;
+    a.part = w.part;
+    a.o = w.o;
+    a.chunks = chunks_for(cache_len, m);
+    if ((e = launch_attention(a, st)) != hipSuccess) return e;
+    GemvParams o{};
+    o.w[0] = qmat(L->wo);
+    o.nmat = 1;
+    o.N = L->wo.n;
+    o.K = L->wo.k;
+    o.x0 = w.o;
+    o.residual = u;
+    o.y = out;
+    return run_gemv(FMT_Q4, PRO_PLAIN, EPI_STORE, m, o, default_blocks(), st);
+}
+
+hipError_t run_ffn_dense(const float* x, const float* gamma, float eps, const mtp_q4& gate, const mtp_q4& up,
+                         const mtp_q4& down, const float* residual, float* y, int m, float* z, hipStream_t st) {
+    GemvParams g{};
+    g.w[0] = qmat(gate);
+    g.w[1] = qmat(up);
+    g.nmat = 2;
+    g.N = gate.n;
+    g.K = gate.k;
+    g.x0 = x;
+    g.g0 = gamma;
+    g.eps = eps;
+    g.y = z;
+    hipError_t e = run_gemv(FMT_Q4, gamma ? PRO_RMS : PRO_PLAIN, EPI_SWIGLU, m, g, default_blocks(), st);
+    if (e != hipSuccess) return e;
+    GemvParams d{};
+    d.w[0] = qmat(down);
+    d.nmat = 1;
+    d.N = down.n;
+    d.K = down.k;
+    d.x0 = z;
+    d.residual = residual;
+    d.y = y;
+    return run_gemv(FMT_Q4, PRO_PLAIN, EPI_STORE, m, d, default_blocks(), st);
+}
+
+hipError_t run_moe(const float* x, const float* gamma, float eps, const float* router, int top_k, const mtp_q8& ge,
+                   const mtp_q8& ue, const mtp_q8& de, const mtp_q8* sg, const mtp_q8* su, const mtp_q8* sd,
+                   const float* residual, float* y, int* ids_out, float* gates_out, int m, const MoeWs& w,
+                   hipStream_t st) {
+    MoeParams p{};
+    p.x = x;
+    p.gamma = gamma;
+    p.eps = eps;
+    p.f = w.f;
+    p.router = router;
+    p.logits = w.logits;
+    p.E = ge.n_experts;
+    p.H = ge.k;
+    p.top_k = top_k;
+    p.m = m;
+    p.expert_ids = ids_out ? ids_out : w.ids;
+    p.gates = gates_out ? gates_out : w.gates;
+    p.slot_expert = w.slot_expert;
+    p.slot_gate = w.slot_gate;
+    p.n_slots = w.n_slots;
+    p.max_slots = w.max_slots;
+    p.ge = qmat8(ge, 0);
+    p.ue = qmat8(ue, 0);
+    p.de = qmat8(de, 0);
+    if (sg) {
+        p.sg = qmat8(*sg, 0);
+        p.su = qmat8(*su, 0);
+        p.sd = qmat8(*sd, 0);
+        p.sh_inter = sg->n;
+    }
+    p.inter = ge.n;
+    p.z = w.z;
+    p.ypart = w.ypart;
+    p.residual = residual;
+    p.y = y;
+    return launch_moe(p, st);
+}
+
+mtp_status check_layer_attn(const mtp_layer* L) {
+    if (!L) return fail(MTP_ERR_INVALID_ARG, "layer is NULL");
+    const int H = L->hidden;
+    if (H < MTP_GROUP || H % MTP_GROUP || H > MTP_MAX_K) return fail(MTP_ERR_INVALID_ARG, "hidden=%d", H);
+    if (L->head_dim != 128) return fail(MTP_ERR_UNSUPPORTED, "head_dim=%d (only 128 is built)", L->head_dim);
+    if (L->n_heads < 1 || L->n_kv_heads < 1 || L->n_heads % L->n_kv_heads)
+        return fail(MTP_ERR_INVALID_ARG, "n_heads=%d n_kv_heads=%d", L->n_heads, L->n_kv_heads);
+    if (!(L->eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
+    if (!(L->rope_theta > 0.0)) return fail(MTP_ERR_INVALID_ARG, "rope_theta must be > 0");
+    mtp_status s;
+    if ((s = check_vec(L->gamma_attn, "gamma_attn")) != MTP_OK) return s;
+    if ((s = check_q4(&L->wq, "wq")) || (s = check_q4(&L->wk, "wk")) || (s = check_q4(&L->wv, "wv")) ||
+        (s = check_q4(&L->wo, "wo")))
+        return s;
+    const int qn = L->n_heads * L->head_dim, kvn = L->n_kv_heads * L->head_dim;
+    if (L->wq.n != qn || L->wq.k != H || L->wk.n != kvn || L->wk.k != H || L->wv.n != kvn || L->wv.k != H ||
+        L->wo.n != H || L->wo.k != qn)
+        return fail(MTP_ERR_INVALID_ARG, "attention weight shapes do not match hidden/heads/head_dim");
+    if (qn > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "n_heads*head_dim=%d above %d", qn, MTP_MAX_K);
+    return MTP_OK;
+}
+
+mtp_status check_cache(const float* kc, const float* vc, int32_t cache_len, int32_t capacity, int32_t m,
+                       const mtp_layer* L) {
+    if (!kc || !vc) return fail(MTP_ERR_INVALID_ARG, "k_cache/v_cache is NULL");
+    if (!a16(kc) || !a16(vc)) return fail(MTP_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+    if (kc == vc) return fail(MTP_ERR_INVALID_ARG, "k_cache and v_cache alias");
+    if (cache_len < 0 || capacity < 1) return fail(MTP_ERR_INVALID_ARG, "cache_len=%d capacity=%d", cache_len, capacity);
+    if ((int64_t)cache_len + m > capacity)
+        return fail(MTP_ERR_INVALID_ARG, "cache overflow: cache_len %d + m %d > capacity %d", cache_len, m, capacity);
+    if ((L->n_heads / L->n_kv_heads) * m > 64)
+        return fail(MTP_ERR_UNSUPPORTED, "(n_heads/n_kv_heads)*m=%d above 64", (L->n_heads / L->n_kv_heads) * m);
+    return MTP_OK;
+}
+
+mtp_status check_moe_weights(const float* router, int top_k, const mtp_q8* ge, const mtp_q8* ue, const mtp_q8* de,
+                             const mtp_q8* sg, const mtp_q8* su, const mtp_q8* sd, int H) {
+    mtp_status s;
+    if ((s = check_q8(ge, "gate_exps")) || (s = check_q8(ue, "up_exps")) || (s = check_q8(de, "down_exps"))) return s;
+    if (!router || !a4(router)) return fail(MTP_ERR_INVALID_ARG, "router is NULL or misaligned");
+    const int E = ge->n_experts, I = ge->n;
+    if (ue->n_experts != E || de->n_experts != E) return fail(MTP_ERR_INVALID_ARG, "expert stacks differ in n_experts");
+    if (E > 1024) return fail(MTP_ERR_UNSUPPORTED, "n_experts=%d above 1024", E);
+    if (top_k < 1 || top_k > E || top_k > 64) return fail(MTP_ERR_INVALID_ARG, "top_k=%d (1..min(n_experts, 64))", top_k);
+    if (ge->k != H || ue->k != H || ue->n != I || de->n != H || de->k != I)
+        return fail(MTP_ERR_INVALID_ARG, "expert shapes: gate/up [E][I][H], down [E][H][I] expected");
+    const bool any = sg || su || sd, all = sg && su && sd;
+    if (any && !all) return fail(MTP_ERR_INVALID_ARG, "shared expert: give all of sh_gate/sh_up/sh_down or none");
+    if (all) {
+        if ((s = check_q8(sg, "sh_gate")) || (s = check_q8(su, "sh_up")) || (s = check_q8(sd, "sh_down"))) return s;
+        const int Is = sg->n;
+        if (sg->k != H || su->k != H || su->n != Is || sd->n != H || sd->k != Is)
+            return fail(MTP_ERR_INVALID_ARG, "shared expert shapes do not match");
+        if ((I + 2047) / 2048 != (Is + 2047) / 2048)
+            return fail(MTP_ERR_UNSUPPORTED, "expert and shared intermediate sizes need the same 2048-wide chunk count");
+    }
+    return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtp_status_string(mtp_status s) {
+    switch (s) {
+        case MTP_OK: return "ok";
+        case MTP_ERR_INVALID_ARG: return "invalid argument";
+        case MTP_ERR_UNSUPPORTED: return "unsupported shape";
+        case MTP_ERR_WORKSPACE: return "workspace too small";
+        case MTP_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* mtp_last_error(void) { return g_err.c_str(); }
+
+const char* mtp_version(void) { return "libmtp 0.1 gfx950"; }
+
+size_t mtp_attn_decode_workspace_size(const mtp_layer* L, int32_t cache_len, int32_t m) {
+    if (!L || m < 1 || cache_len < 0 || L->n_kv_heads < 1) return 0;
+    Carve c{nullptr};
+    carve_attn(c, L, cache_len, m);
+    return c.off;
+}
+
+size_t mtp_ffn_dense_workspace_size(int32_t ffn_inter, int32_t m) {
+    if (ffn_inter < 1 || m < 1) return 0;
+    Carve c{nullptr};
+    c.take<float>((size_t)m * ffn_inter);
+    return c.off;
+}
+
+size_t mtp_ffn_moe_workspace_size(int32_t hidden, int32_t n_experts, int32_t top_k, int32_t inter,
+                                  int32_t shared_inter, int32_t m) {
+    if (hidden < 1 || n_experts < 1 || top_k < 1 || inter < 1 || m < 1 || shared_inter < 0) return 0;
+    Carve c{nullptr};
+    carve_moe(c, hidden, n_experts, top_k, inter, shared_inter, m);
+    return c.off;
+}
+
+size_t mtp_lmhead_workspace_size(int32_t vocab, int32_t m) {
+    (void)vocab;
+    if (m < 1) return 0;
+    Carve c{nullptr};
+    carve_head(c, m);
+    return c.off;
+}
+
+size_t mtp_draft_step_workspace_size(const mtp_layer* L, int32_t cache_len, int32_t m) {
+    if (!L || m < 1 || cache_len < 0 || L->n_kv_heads < 1) return 0;
+    Carve c{nullptr};
+    c.take<float>((size_t)m * L->hidden);  // u
+    c.take<float>((size_t)m * L->hidden);  // r1
+    c.take<float>((size_t)m * L->hidden);  // r2
+    carve_attn(c, L, cache_len, m);
+    if (L->ffn_kind == MTP_FFN_MOE_Q8)
+        carve_moe(c, L->hidden, L->gate_exps.n_experts, L->top_k, L->gate_exps.n, L->sh_gate.codes ? L->sh_gate.n : 0, m);
+    else
+        c.take<float>((size_t)m * L->ffn_inter);
+    carve_head(c, m);
+    return c.off;
+}
+
+mtp_status mtp_dequant_q4(const mtp_q4* w, float* out, void* stream) {
+    mtp_status s = check_q4(w, "w");
+    if (s) return s;
+    if (!out || !a4(out)) return fail(MTP_ERR_INVALID_ARG, "out is NULL or misaligned");
+    hipError_t e = launch_dequant(FMT_Q4, qmat(*w), w->k, out, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_dequant_q4");
+}
+
+mtp_status mtp_dequant_q8(const mtp_q8* w, int32_t expert, float* out, void* stream) {
+    mtp_status s = check_q8(w, "w");
+    if (s) return s;
+    if (expert < 0 || expert >= w->n_experts) return fail(MTP_ERR_INVALID_ARG, "expert=%d outside 0..%d", expert, w->n_experts - 1);
+    if (!out || !a4(out)) return fail(MTP_ERR_INVALID_ARG, "out is NULL or misaligned");
+    hipError_t e = launch_dequant(FMT_Q8, qmat8(*w, expert), w->k, out, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_dequant_q8");
+}
+
+mtp_status mtp_qgemv(const mtp_q4* w, const float* x, const float* residual, float* y, int32_t m, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_q4(w, "w")) || (s = check_vec(x, "x"))) return s;
+    if (!y || !a4(y)) return fail(MTP_ERR_INVALID_ARG, "y is NULL or misaligned");
+    if (residual && !a4(residual)) return fail(MTP_ERR_INVALID_ARG, "residual misaligned");
+    if ((const void*)y == (const void*)x) return fail(MTP_ERR_INVALID_ARG, "y aliases x");
+    GemvParams p{};
+    p.w[0] = qmat(*w);
+    p.nmat = 1;
+    p.N = w->n;
+    p.K = w->k;
+    p.x0 = x;
+    p.residual = residual;
+    p.y = y;
+    hipError_t e = run_gemv(FMT_Q4, PRO_PLAIN, EPI_STORE, m, p, default_blocks(), (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_qgemv");
+}
+
+mtp_status mtp_q8gemv(const mtp_q8* w, int32_t expert, const float* x, const float* residual, float* y, int32_t m,
+                      void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_q8(w, "w")) || (s = check_vec(x, "x"))) return s;
+    if (expert < 0 || expert >= w->n_experts) return fail(MTP_ERR_INVALID_ARG, "expert=%d outside 0..%d", expert, w->n_experts - 1);
+    if (!y || !a4(y)) return fail(MTP_ERR_INVALID_ARG, "y is NULL or misaligned");
+    if (residual && !a4(residual)) return fail(MTP_ERR_INVALID_ARG, "residual misaligned");
+    if ((const void*)y == (const void*)x) return fail(MTP_ERR_INVALID_ARG, "y aliases x");
+    GemvParams p{};
+    p.w[0] = qmat8(*w, expert);
+    p.nmat = 1;
+    p.N = w->n;
+    p.K = w->k;
+    p.x0 = x;
+    p.residual = residual;
+    p.y = y;
+    hipError_t e = run_gemv(FMT_Q8, PRO_PLAIN, EPI_STORE, m, p, default_blocks(), (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_q8gemv");
+}
+
+mtp_status mtp_norm_concat_proj(const float* e, const float* h, const float* gamma_e, const float* gamma_h, float eps,
+                                const mtp_q4* eh_proj, float* u, int32_t m, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_q4(eh_proj, "eh_proj")) || (s = check_vec(e, "e")) ||
+        (s = check_vec(h, "h")) || (s = check_vec(gamma_e, "gamma_e")) || (s = check_vec(gamma_h, "gamma_h")))
+        return s;
+    if (eh_proj->k % 64) return fail(MTP_ERR_INVALID_ARG, "eh_proj k=%d must be 2*hidden with hidden %% 32 == 0", eh_proj->k);
+    if (!u || !a4(u)) return fail(MTP_ERR_INVALID_ARG, "u is NULL or misaligned");
+    if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
+    const int H = eh_proj->k / 2;
+    if ((const float*)u == e || (const float*)u == h) return fail(MTP_ERR_INVALID_ARG, "u aliases an input");
+    GemvParams p{};
+    p.w[0] = qmat(*eh_proj);
+    p.nmat = 1;
+    p.N = eh_proj->n;
+    p.K = 2 * H;
+    p.H = H;
+    p.x0 = e;
+    p.x1 = h;
+    p.g0 = gamma_e;
+    p.g1 = gamma_h;
+    p.eps = eps;
+    p.y = u;
+    hipError_t err = run_gemv(FMT_Q4, PRO_CONCAT, EPI_STORE, m, p, default_blocks(), (hipStream_t)stream);
+    return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_norm_concat_proj");
+}
+
+mtp_status mtp_attn_decode(const mtp_layer* L, const float* u, float* k_cache, float* v_cache, int32_t cache_len,
+                           int32_t capacity, int32_t m, float* out, void* ws, size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_layer_attn(L)) || (s = check_vec(u, "u")) ||
+        (s = check_cache(k_cache, v_cache, cache_len, capacity, m, L)))
+        return s;
+    if (!out || !a16(out)) return fail(MTP_ERR_INVALID_ARG, "out is NULL or misaligned");
+    if ((const float*)out == u) return fail(MTP_ERR_INVALID_ARG, "out aliases u");
+    Carve c{static_cast<char*>(ws)};
+    Carve probe{nullptr};
+    carve_attn(probe, L, cache_len, m);
+    if ((s = check_ws(ws, ws_bytes, probe.off))) return s;
+    const AttnWs w = carve_attn(c, L, cache_len, m);
+    hipError_t e = run_attention(L, u, k_cache, v_cache, cache_len, capacity, m, out, w, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_attn_decode");
+}
+
+mtp_status mtp_ffn_dense_q(const float* x, const float* gamma, float eps, const mtp_q4* gate, const mtp_q4* up,
+                           const mtp_q4* down, const float* residual, float* y, int32_t m, void* ws, size_t ws_bytes,
+                           void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_vec(x, "x")) || (s = check_q4(gate, "gate")) || (s = check_q4(up, "up")) ||
+        (s = check_q4(down, "down")))
+        return s;
+    if (gamma && (s = check_vec(gamma, "gamma"))) return s;
+    if (gate->n != up->n || gate->k != up->k || down->k != gate->n || down->n != gate->k)
+        return fail(MTP_ERR_INVALID_ARG, "FFN shapes: gate/up [I][H], down [H][I] expected");
+    if (!y || !a16(y)) return fail(MTP_ERR_INVALID_ARG, "y is NULL or misaligned");
+    if (residual && !a4(residual)) return fail(MTP_ERR_INVALID_ARG, "residual misaligned");
+    if ((const float*)y == x) return fail(MTP_ERR_INVALID_ARG, "y aliases x");
+    if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
+    const size_t need = mtp_ffn_dense_workspace_size(gate->n, m);
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    hipError_t e = run_ffn_dense(x, gamma, eps, *gate, *up, *down, residual, y, m, static_cast<float*>(ws),
+                                 (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_ffn_dense_q");
+}
+
+mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
+                         const mtp_q8* gate_exps, const mtp_q8* up_exps, const mtp_q8* down_exps, const mtp_q8* sh_gate,
+                         const mtp_q8* sh_up, const mtp_q8* sh_down, const float* residual, float* y,
+                         int32_t* expert_ids, float* gates, int32_t m, void* ws, size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_vec(x, "x"))) return s;
+    if (!gate_exps) return fail(MTP_ERR_INVALID_ARG, "gate_exps is NULL");
+    const int H = gate_exps->k;
+    if ((s = check_moe_weights(router, top_k, gate_exps, up_exps, down_exps, sh_gate, sh_up, sh_down, H))) return s;
+    if (gamma && (s = check_vec(gamma, "gamma"))) return s;
+    if (!y || !a4(y)) return fail(MTP_ERR_INVALID_ARG, "y is NULL or misaligned");
+    if (residual && !a4(residual)) return fail(MTP_ERR_INVALID_ARG, "residual misaligned");
+    if ((const float*)y == x) return fail(MTP_ERR_INVALID_ARG, "y aliases x");
+    if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
+    const int sh_inter = sh_gate ? sh_gate->n : 0;
+    const size_t need = mtp_ffn_moe_workspace_size(H, gate_exps->n_experts, top_k, gate_exps->n, sh_inter, m);
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    Carve c{static_cast<char*>(ws)};
+    const MoeWs w = carve_moe(c, H, gate_exps->n_experts, top_k, gate_exps->n, sh_inter, m);
+    hipError_t e = run_moe(x, gamma, eps, router, top_k, *gate_exps, *up_exps, *down_exps, sh_gate, sh_up, sh_down,
+                           residual, y, expert_ids, gates, m, w, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_ffn_moe_q");
+}
+
+mtp_status mtp_lmhead_argmax(const float* hidden, const float* gamma, float eps, const mtp_q4* lm_head,
+                             float* normed_out, float* logits_out, int32_t* ids_out, int32_t m, void* ws,
+                             size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_vec(hidden, "hidden")) || (s = check_vec(gamma, "gamma")) ||
+        (s = check_q4(lm_head, "lm_head")))
+        return s;
+    if (!ids_out || !a4(ids_out)) return fail(MTP_ERR_INVALID_ARG, "ids_out is NULL or misaligned");
+    if (normed_out && !a16(normed_out)) return fail(MTP_ERR_INVALID_ARG, "normed_out misaligned");
+    if (logits_out && !a4(logits_out)) return fail(MTP_ERR_INVALID_ARG, "logits_out misaligned");
+    if (normed_out == hidden && normed_out) return fail(MTP_ERR_INVALID_ARG, "normed_out aliases hidden");
+    if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
+    const size_t need = mtp_lmhead_workspace_size(lm_head->n, m);
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    Carve c{static_cast<char*>(ws)};
+    const HeadWs w = carve_head(c, m);
+    hipError_t e = run_head(hidden, gamma, eps, *lm_head, normed_out, logits_out, ids_out, m, w, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_lmhead_argmax");
+}
+
+mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                          const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                          int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_layer_attn(L)) || (s = check_cache(k_cache, v_cache, cache_len, capacity, m, L)))
+        return s;
+    const int H = L->hidden;
+    if ((s = check_vec(h, "h")) || (s = check_vec(L->gamma_e, "gamma_e")) || (s = check_vec(L->gamma_h, "gamma_h")) ||
+        (s = check_vec(L->gamma_post, "gamma_post")) || (s = check_vec(L->gamma_final, "gamma_final")) ||
+        (s = check_q4(&L->eh_proj, "eh_proj")) || (s = check_q4(&L->lm_head, "lm_head")))
+        return s;
+    if (L->eh_proj.n != H || L->eh_proj.k != 2 * H) return fail(MTP_ERR_INVALID_ARG, "eh_proj must be [hidden][2*hidden]");
+    if (L->lm_head.k != H || L->lm_head.n != L->vocab) return fail(MTP_ERR_INVALID_ARG, "lm_head must be [vocab][hidden]");
+    if (!tokens && !e) return fail(MTP_ERR_INVALID_ARG, "give e or tokens");
+    if (e && (s = check_vec(e, "e"))) return s;
+    if (tokens && (!a4(tokens) || !embed_table)) return fail(MTP_ERR_INVALID_ARG, "tokens needs an aligned pointer and embed_table");
+    if (embed_table && !a16(embed_table)) return fail(MTP_ERR_INVALID_ARG, "embed_table misaligned");
+    if (!ids_out || !a4(ids_out)) return fail(MTP_ERR_INVALID_ARG, "ids_out is NULL or misaligned");
+    if (!hidden_out || !a16(hidden_out)) return fail(MTP_ERR_INVALID_ARG, "hidden_out is NULL or misaligned");
+    if (logits_out && !a4(logits_out)) return fail(MTP_ERR_INVALID_ARG, "logits_out misaligned");
+    if (hidden_out == h || hidden_out == e) return fail(MTP_ERR_INVALID_ARG, "hidden_out aliases an input");
+    if (L->ffn_kind == MTP_FFN_DENSE_Q4) {
+        if ((s = check_q4(&L->gate, "gate")) || (s = check_q4(&L->up, "up")) || (s = check_q4(&L->down, "down"))) return s;
+        if (L->gate.n != L->ffn_inter || L->up.n != L->ffn_inter || L->gate.k != H || L->up.k != H ||
+            L->down.n != H || L->down.k != L->ffn_inter)
+            return fail(MTP_ERR_INVALID_ARG, "dense FFN shapes do not match hidden/ffn_inter");
+    } else if (L->ffn_kind == MTP_FFN_MOE_Q8) {
+        const bool sh = L->sh_gate.codes != nullptr;
+        if ((s = check_moe_weights(L->router, L->top_k, &L->gate_exps, &L->up_exps, &L->down_exps, sh ? &L->sh_gate : nullptr,
+                                   sh ? &L->sh_up : nullptr, sh ? &L->sh_down : nullptr, H)))
+            return s;
+    } else {
+        return fail(MTP_ERR_INVALID_ARG, "ffn_kind=%d", L->ffn_kind);
+    }
+    const size_t need = mtp_draft_step_workspace_size(L, cache_len, m);
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{static_cast<char*>(ws)};
+    float* u = c.take<float>((size_t)m * H);
+    float* r1 = c.take<float>((size_t)m * H);
+    float* r2 = c.take<float>((size_t)m * H);
+    const AttnWs aw = carve_attn(c, L, cache_len, m);
+
+    // u = eh_proj [rms(e); rms(h)]
+    GemvParams p{};
+    p.w[0] = qmat(L->eh_proj);
+    p.nmat = 1;
+    p.N = H;
+    p.K = 2 * H;
+    p.H = H;
+    p.x0 = e;
+    p.x1 = h;
+    p.tokens = tokens;
+    p.table = embed_table;
+    p.vocab = L->vocab;
+    p.g0 = L->gamma_e;
+    p.g1 = L->gamma_h;
+    p.eps = L->eps;
+    p.y = u;
+    hipError_t err = run_gemv(FMT_Q4, PRO_CONCAT, EPI_STORE, m, p, default_blocks(), st);
+    if (err != hipSuccess) return hip_fail(err, "mtp_draft_step eh_proj");
+    if ((err = run_attention(L, u, k_cache, v_cache, cache_len, capacity, m, r1, aw, st)) != hipSuccess)
+        return hip_fail(err, "mtp_draft_step attention");
+    if (L->ffn_kind == MTP_FFN_DENSE_Q4) {
+        float* z = c.take<float>((size_t)m * L->ffn_inter);
+        err = run_ffn_dense(r1, L->gamma_post, L->eps, L->gate, L->up, L->down, r1, r2, m, z, st);
+    } else {
+        const bool sh = L->sh_gate.codes != nullptr;
+        const MoeWs mw = carve_moe(c, H, L->gate_exps.n_experts, L->top_k, L->gate_exps.n, sh ? L->sh_gate.n : 0, m);
+        err = run_moe(r1, L->gamma_post, L->eps, L->router, L->top_k, L->gate_exps, L->up_exps, L->down_exps,
+                      sh ? &L->sh_gate : nullptr, sh ? &L->sh_up : nullptr, sh ? &L->sh_down : nullptr, r1, r2,
+                      nullptr, nullptr, m, mw, st);
+    }
+    if (err != hipSuccess) return hip_fail(err, "mtp_draft_step ffn");
+    const HeadWs hw = carve_head(c, m);
+    if ((err = run_head(r2, L->gamma_final, L->eps, L->lm_head, hidden_out, logits_out, ids_out, m, hw, st)) != hipSuccess)
+        return hip_fail(err, "mtp_draft_step head");
+    return MTP_OK;
+}
+
+}  // extern "C"

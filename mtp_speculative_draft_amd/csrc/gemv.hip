@@ -1,0 +1,410 @@
+// gemv.hip -- quantized GEMV kernels for m <= 8 activation rows (gfx950).
+//
+// One kernel template covers every weight-streaming op of the draft layer:
+// the plain linear, the eh_proj with its two fused RMSNorms and virtual
+// concat, the fused attention-norm + q/k/v projection, the SwiGLU gate/up
+// pair, the MoE expert slots and the lm_head with its fused final norm and
+// first argmax pass.  See device.hpp for the lane/group scheme.
+#include <climits>
+#include <cmath>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace mtp {
+
+struct View {
+    QMat w[3];
+    int N, K, G;
+    const float* x0;
+    float* y;
+    const float* rowscale;
+};
+
+__device__ __forceinline__ bool resolve_view(const GemvParams& p, View& v) {
+    v.w[0] = p.w[0];
+    v.w[1] = p.w[1];
+    v.w[2] = p.w[2];
+    v.N = p.N;
+    v.K = p.K;
+    v.G = p.G;
+    v.x0 = p.x0;
+    v.y = p.y;
+    v.rowscale = p.rowscale;
+    if (p.slot_expert) {
+        const int slot = blockIdx.y;
+        if (slot >= *p.n_slots) return false;
+        const int e = p.slot_expert[slot];
+        if (e >= 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                v.w[j].codes = static_cast<const char*>(p.w[j].codes) + p.ex_codes * e;
+                v.w[j].scales = p.w[j].scales + p.ex_scales * e;
+            }
+        } else {
+            v.w[0] = p.shw[0];
+            v.w[1] = p.shw[1];
+            v.N = p.N_sh;
+            v.K = p.K_sh;
+            v.G = p.K_sh / kGroup;
+        }
+        v.x0 = p.x0 + p.x_slot * slot;
+        v.y = p.y + p.y_slot * slot;
+        if (p.rowscale) v.rowscale = p.rowscale + p.rs_slot * slot;
+    }
+    return true;
+}
+
+// Builds the lane's activation fragments for all M rows (prologue + 16-bit
+// split).  Every thread of the block calls it; it holds block barriers when
+// several waves share one weight row (S > 1).
+template <int FMT, int M, int PRO>
+__device__ __forceinline__ void gemv_setup(const GemvParams& p, const View& v, int wid, int lane, int S,
+                                           XFrag (&xf)[M], float (&xs)[M], float (*nred)[2]) {
+    const int s = wid % S, q = wid / S;
+    const int g = s * kWave + lane;
+    const bool active = g < v.G;
+    const int kk = g * kGroup;
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+        float xv[32];
+        int seg = 0, kl = kk, nfeat = v.K;
+        const float* src;
+        const float* gam = p.g0;
+        if constexpr (PRO == PRO_CONCAT) {
+            seg = kk >= p.H ? 1 : 0;
+            kl = seg ? kk - p.H : kk;
+            nfeat = p.H;
+            if (seg) {
+                src = p.x1 + (int64_t)mi * p.H;
+                gam = p.g1;
+            } else {
+                src = v.x0 + (int64_t)mi * p.H;
+                if (p.tokens && mi < p.m) {
+                    int tok = p.tokens[mi];
+                    if (tok >= 0 || v.x0 == nullptr) {  // no e rows given: every row is a token
+                        tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
+                        src = p.table + (int64_t)tok * p.H;
+                    }
+                }
+            }
+        } else {
+            src = v.x0 + (int64_t)mi * v.K;
+        }
+        if (active && mi < p.m) {
+            load32(xv, src + kl);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
+        }
+        if constexpr (PRO != PRO_PLAIN) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) ss = fmaf(xv[i], xv[i], ss);
+            float s0 = wave_sum(seg == 0 ? ss : 0.0f);
+            float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
+            if (S > 1) {
+                __syncthreads();
+                if (lane == 0) {
+                    nred[wid][0] = s0;
+                    nred[wid][1] = s1;
+                }
+                __syncthreads();
+                s0 = 0.0f;
+                s1 = 0.0f;
+                for (int j = 0; j < S; ++j) {
+                    s0 += nred[q * S + j][0];
+                    s1 += nred[q * S + j][1];
+                }
+            }
+            const float tot = seg ? s1 : s0;
+            const float inv = rsqrtf(tot / (float)nfeat + p.eps);
+            if (active) {
+                float gv[32];
+                load32(gv, gam + kl);
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xv[i] = xv[i] * inv * gv[i];
+                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0 && q == 0 && mi < p.m)
+                    store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
+            }
+        }
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
+        am = wave_max(am);
+        const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
+        xs[mi] = am / kQMax;
+        quantize_group<FMT>(xv, inv_q, xs[mi], xf[mi]);
+    }
+}
+
+template <int FMT, int M>
+__device__ __forceinline__ void row_partials(const QMat& w, int64_t row, int G, int g, const XFrag (&xf)[M],
+                                             float* out, int stride) {
+    WFrag<FMT> f;
+    load_frag(f, w.codes, w.scales, w.biases, row, G, g);
+    if constexpr (FMT == FMT_Q4) {
+        const Nib n = unpack_nibbles(f.c);
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) out[mi * stride] = dot_q4(n, f.s, f.b, xf[mi]);
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) out[mi * stride] = dot_q8(f, xf[mi]);
+    }
+}
+
+template <int FMT, int M, int PRO, int EPI>
+__global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
+    constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int R = rows_per_iter<M, P>();
+    constexpr int V = R * M * P;
+    __shared__ float red[4][kWave * 2];
+    __shared__ float nred[4][2];
+
+    View v;
+    if (!resolve_view(p, v)) return;
+
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int S = p.S;
+    const int Q = (blockDim.x / kWave) / S;
+    const int s = wid % S, q = wid / S;
+    const int g = s * kWave + lane;
+    const int gc = g < v.G ? g : v.G - 1;
+
+    XFrag xf[M];
+    float xs[M];
+    gemv_setup<FMT, M, PRO>(p, v, wid, lane, S, xf, xs, nred);
+
+    const int pos = reduce_base<V, P>(lane) / P;  // = r * M + mi of this lane's result
+    const int r_l = pos / M, mi_l = pos % M;
+    const bool writer = reduce_writer<V, P>(lane);
+    const float xs_l = select_m<M>(xs, mi_l);
+    float best = -INFINITY;
+    int best_i = INT_MAX;
+
+    const int tile_rows = Q * R;
+    const int ntiles = (v.N + tile_rows - 1) / tile_rows;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int row0 = (t * Q + q) * R;
+        float acc[V];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int row = row0 + r;
+            row = row < v.N ? row : v.N - 1;  // tail rows are computed and dropped
+            if constexpr (EPI == EPI_SWIGLU) {
+                row_partials<FMT, M>(v.w[0], row, v.G, gc, xf, &acc[r * M * 2], 2);
+                row_partials<FMT, M>(v.w[1], row, v.G, gc, xf, &acc[r * M * 2 + 1], 2);
+            } else {
+                int lr = row, j = 0;
+                if (lr >= v.w[0].n) {
+                    lr -= v.w[0].n;
+                    j = 1;
+                    if (lr >= v.w[1].n) {
+                        lr -= v.w[1].n;
+                        j = 2;
+                    }
+                }
+                QMat w;
+                w.codes = (j == 0) ? v.w[0].codes : (j == 1 ? v.w[1].codes : v.w[2].codes);
+                w.scales = (j == 0) ? v.w[0].scales : (j == 1 ? v.w[1].scales : v.w[2].scales);
+                w.biases = (j == 0) ? v.w[0].biases : (j == 1 ? v.w[1].biases : v.w[2].biases);
+                row_partials<FMT, M>(w, lr, v.G, gc, xf, &acc[r * M], 1);
+            }
+        }
+        reduce_transpose<V, P>(acc, lane);
+        float v0 = acc[0] * xs_l;
+        float v1 = (P == 2) ? acc[P - 1] * xs_l : 0.0f;
+        if (S > 1) {
+            red[wid][2 * lane] = v0;
+            red[wid][2 * lane + 1] = v1;
+            __syncthreads();
+            if (s == 0) {
+                v0 = 0.0f;
+                v1 = 0.0f;
+                for (int j = 0; j < S; ++j) {
+                    v0 += red[q * S + j][2 * lane];
+                    v1 += red[q * S + j][2 * lane + 1];
+                }
+            }
+            __syncthreads();
+        }
+        if (s == 0) {
+            const int row = row0 + r_l;
+            if (row < v.N && mi_l < p.m) {
+                const int64_t o = (int64_t)mi_l * v.N + row;
+                if constexpr (EPI == EPI_STORE) {
+                    if (writer) v.y[o] = p.residual ? v0 + p.residual[o] : v0;
+                } else if constexpr (EPI == EPI_SWIGLU) {
+                    if (writer) {
+                        float z = silu(v0) * v1;
+                        if (v.rowscale) z *= v.rowscale[mi_l];
+                        v.y[o] = z;
+                    }
+                } else {
+                    if (p.logits && writer) p.logits[o] = v0;
+                    if (v0 > best) {  // rows only grow within a lane: ties keep the lower one
+                        best = v0;
+                        best_i = row;
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (EPI == EPI_ARGMAX) {
+        if (s == 0) {
+#pragma unroll
+            for (int mi = 0; mi < M; ++mi) {
+                float bv = (mi_l == mi) ? best : -INFINITY;
+                int bi = (mi_l == mi) ? best_i : INT_MAX;
+                wave_argmax(bv, bi);
+                if (lane == 0 && mi < p.m) {
+                    const int idx = (blockIdx.x * Q + q) * p.m + mi;
+                    p.part_val[idx] = bv;
+                    p.part_idx[idx] = bi;
+                }
+            }
+        }
+    }
+}
+
+// Second argmax pass: one block per activation row over all block partials.
+__global__ void __launch_bounds__(256) k_argmax_final(const float* pv, const int* pi, int parts, int m, int* ids) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int mi = blockIdx.x;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int j = threadIdx.x; j < parts; j += blockDim.x) argmax_merge(bv, bi, pv[(int64_t)j * m + mi], pi[(int64_t)j * m + mi]);
+    wave_argmax(bv, bi);
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    if (lane == 0) {
+        sv[wid] = bv;
+        si[wid] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) argmax_merge(bv, bi, sv[w], si[w]);
+        ids[mi] = (bi == INT_MAX) ? 0 : bi;
+    }
+}
+
+// Dequantize through the GEMV fragment path (load_frag + nibble unpack): one
+// thread per (row, group).
+template <int FMT>
+__global__ void __launch_bounds__(256) k_dequant(const QMat w, int n, int K, float* out) {
+    const int G = K / kGroup;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)n * G) return;
+    const int64_t row = gid / G;
+    const int g = (int)(gid % G);
+    float* dst = out + row * K + (int64_t)g * kGroup;
+    WFrag<FMT> f;
+    load_frag(f, w.codes, w.scales, w.biases, row, G, g);
+    if constexpr (FMT == FMT_Q4) {
+        const Nib nb = unpack_nibbles(f.c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                dst[8 * j + 2 * t] = fmaf(f.s, (float)((nb.e[j] >> (8 * t)) & 0xFF), f.b);
+                dst[8 * j + 2 * t + 1] = fmaf(f.s, (float)((nb.o[j] >> (8 * t)) & 0xFF), f.b);
+            }
+    } else {
+        const int c[8] = {(int)f.c0.x, (int)f.c0.y, (int)f.c0.z, (int)f.c0.w,
+                          (int)f.c1.x, (int)f.c1.y, (int)f.c1.z, (int)f.c1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dst[4 * j + t] = f.s * (float)(signed char)((c[j] >> (8 * t)) & 0xFF);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
+GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks) {
+    (void)fmt;
+    const int G = K / kGroup;
+    const int S = (G + kWave - 1) / kWave;
+    const int Q = (S == 1) ? 4 : (S == 2 ? 2 : 1);
+    const int Mi = inst_m(m);
+    const int P = (epi == EPI_SWIGLU) ? 2 : 1;
+    int R = 32 / (Mi * P);
+    R = R < 8 ? R : 8;
+    const int ntiles = (N + Q * R - 1) / (Q * R);
+    GemvShape sh;
+    sh.Q = Q;
+    sh.R = R;
+    sh.block = kWave * S * Q;
+    sh.grid = ntiles < max_blocks ? ntiles : max_blocks;
+    if (sh.grid < 1) sh.grid = 1;
+    return sh;
+}
+
+template <int FMT, int PRO, int EPI>
+static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int slots, hipStream_t st) {
+    dim3 grid(sh.grid, slots), block(sh.block);
+    switch (inst_m(m)) {
+        case 1: hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI>), grid, block, 0, st, p); break;
+        case 4: hipLaunchKernelGGL((k_gemv<FMT, 4, PRO, EPI>), grid, block, 0, st, p); break;
+        default: hipLaunchKernelGGL((k_gemv<FMT, 8, PRO, EPI>), grid, block, 0, st, p); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
+                       hipStream_t st) {
+    if (p.slot_expert) return hipErrorInvalidValue;  // slot launches use launch_gemv_slots
+    if (fmt == FMT_Q4) {
+        if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
+        if (pro == PRO_RMS && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_RMS, EPI_STORE>(m, p, sh, 1, st);
+        if (pro == PRO_CONCAT && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_CONCAT, EPI_STORE>(m, p, sh, 1, st);
+        if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_m<FMT_Q4, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, 1, st);
+        if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_m<FMT_Q4, PRO_RMS, EPI_SWIGLU>(m, p, sh, 1, st);
+        if (pro == PRO_RMS && epi == EPI_ARGMAX) return launch_m<FMT_Q4, PRO_RMS, EPI_ARGMAX>(m, p, sh, 1, st);
+    } else {
+        if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
+        if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, 1, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, const GemvShape& sh, int max_slots,
+                             hipStream_t st) {
+    if (fmt != FMT_Q8 || !p.slot_expert) return hipErrorInvalidValue;
+    if (epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, max_slots, st);
+    if (epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE>(m, p, sh, max_slots, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_argmax_final(const float* pv, const int* pi, int parts, int m, int* ids, hipStream_t st) {
+    hipLaunchKernelGGL(k_argmax_final, dim3(m), dim3(256), 0, st, pv, pi, parts, m, ids);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int fmt, const QMat& w, int k, float* out, hipStream_t st) {
+    const int64_t threads = (int64_t)w.n * (k / kGroup);
+    const int64_t blocks = (threads + 255) / 256;
+    if (fmt == FMT_Q4)
+        hipLaunchKernelGGL(k_dequant<FMT_Q4>, dim3((unsigned)blocks), dim3(256), 0, st, w, w.n, k, out);
+    else
+        hipLaunchKernelGGL(k_dequant<FMT_Q8>, dim3((unsigned)blocks), dim3(256), 0, st, w, w.n, k, out);
+    return hipGetLastError();
+}
+
+}  // namespace mtp

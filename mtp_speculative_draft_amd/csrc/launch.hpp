@@ -1,0 +1,125 @@
+// launch.hpp -- host-side launchers of libmtp's kernels (internal; the public
+// interface is include/mtp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+// One quantized matrix (device pointers). biases is unused for 8-bit.
+struct QMat {
+    const void* codes;
+    const float* scales;
+    const float* biases;
+    int n;
+};
+
+enum Fmt { FMT_Q4 = 0, FMT_Q8 = 1 };
+enum Pro { PRO_PLAIN = 0, PRO_RMS = 1, PRO_CONCAT = 2 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
+
+// Parameters of one quantized GEMV launch over m activation rows.
+//  weights: EPI_STORE / EPI_ARGMAX: up to three matrices with the same k,
+//           concatenated along their output rows (w[0] rows first);
+//           EPI_SWIGLU: w[0] = gate, w[1] = up, equal n.
+//  prologue (the activation x[m][K] the GEMV consumes):
+//           PRO_PLAIN  x = x0 [m][K]
+//           PRO_RMS    x = rms(x0; g0, eps) over K; normed_out [m][K] optional
+//           PRO_CONCAT x = [rms(e; g0) ; rms(x1; g1)], K = 2H, e row r is
+//                      table[tokens[r]] when tokens && tokens[r] >= 0 else x0
+//  epilogue: EPI_STORE  y[r][n] = v (+ residual[r][n])
+//            EPI_SWIGLU y[r][n] = silu(a)*b (* rowscale[r] when given)
+//            EPI_ARGMAX logits[r][n] = v when logits; per-wave-group (max,
+//                       index) partials in part_val/part_idx [blocks*Q][m]
+struct GemvParams {
+    QMat w[3];
+    int nmat;
+    int m;  // activation rows actually present (the kernel may be built for more)
+    int N, K, G, S;
+    const float* x0;
+    const float* x1;
+    const int* tokens;
+    const float* table;
+    int vocab;
+    const float* g0;
+    const float* g1;
+    float eps;
+    int H;
+    float* normed_out;
+    float* y;
+    const float* residual;
+    const float* rowscale;
+    float* logits;
+    float* part_val;
+    int* part_idx;
+    // Expert slots (MoE): when slot_expert is set, blockIdx.y is a slot; slots
+    // >= *n_slots exit at once.  Slot j uses expert e = slot_expert[j] of the
+    // stacks in w[0..1] (byte stride ex_codes, float stride ex_scales), or the
+    // shared matrices shw[0..1] (N_sh rows, K_sh features) when e < 0; x0 and y
+    // advance by x_slot / y_slot elements per slot and rowscale by rs_slot.
+    const int* slot_expert;
+    const int* n_slots;
+    int64_t ex_codes, ex_scales;
+    QMat shw[2];
+    int N_sh, K_sh;
+    int64_t x_slot, y_slot, rs_slot;
+};
+
+struct GemvShape {
+    int grid, block, Q, R;
+};
+
+// Grid/block choice for a GEMV of N rows, K features (S chunks) at m rows.
+GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks);
+hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
+                       hipStream_t stream);
+// MoE slot launch: grid.y = max_slots (blocks of unused slots exit at once).
+hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, const GemvShape& sh, int max_slots,
+                             hipStream_t stream);
+hipError_t launch_argmax_final(const float* part_val, const int* part_idx, int parts, int m, int* ids,
+                               hipStream_t stream);
+hipError_t launch_dequant(int fmt, const QMat& w, int k, float* out, hipStream_t stream);
+int device_cu_count();
+
+// Attention (head_dim 128): RoPE + append + chunked partial softmax, then the
+// log-sum-exp combine.
+struct AttnParams {
+    const float* qkv;  // [m][(nh + 2 nkv) * d] pre-RoPE q, k and v
+    float* k_cache;
+    float* v_cache;
+    int cache_len, capacity, m, nh, nkv, d;
+    double theta;
+    float* part;  // [chunks][nkv][group*m][d + 2]: p*V sums, chunk max, exp-sum
+    float* o;     // [m][nh * d]
+    int chunks;
+};
+constexpr int kAttnChunk = 32;
+hipError_t launch_attention(const AttnParams& p, hipStream_t stream);
+
+// MoE (8-bit experts).
+struct MoeParams {
+    const float* x;      // [m][H] input rows
+    const float* gamma;  // optional input norm
+    float eps;
+    float* f;            // [m][H] normalized rows (workspace)
+    const float* router;  // [E][H]
+    float* logits;        // [m][E]
+    int E, H, top_k, m;
+    int* expert_ids;      // [m][top_k] (workspace or caller)
+    float* gates;         // [m][top_k]
+    int* slot_expert;     // [max_slots]  (-1 = shared expert)
+    float* slot_gate;     // [max_slots][m]
+    int* n_slots;         // [1]
+    int max_slots;
+    QMat ge, ue, de;      // expert stacks (codes of expert 0; stride per expert below)
+    QMat sg, su, sd;      // shared expert (codes NULL when absent)
+    int inter, sh_inter;
+    float* z;             // [max_slots][m][max(inter, sh_inter)]
+    float* ypart;         // [max_slots][m][H]
+    const float* residual;
+    float* y;
+};
+hipError_t launch_moe(const MoeParams& p, hipStream_t stream);
+
+}  // namespace mtp

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mtp.h declares, and rejects bad arguments on the host before anything
+is enqueued (so these calls never reach the HIP runtime)."""
+import ctypes as C
+import re
+
+import pytest
+
+import mtp_speculative_draft_amd as mtp
+
+FAKE = 0x100000  # a 256-aligned non-null address; never dereferenced by rejected calls
+
+
+def _declared():
+    text = open(mtp.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared()
+    assert len(names) >= 17
+    lib = mtp.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in mtp._SIGS, f"binding lacks {n}"
+
+
+def test_status_strings_and_version():
+    lib = mtp.lib()
+    assert lib.mtp_status_string(0) == b"ok"
+    assert lib.mtp_status_string(3) == b"workspace too small"
+    assert b"gfx950" in lib.mtp_version()
+
+
+def _q4(n=64, k=64, codes=FAKE, scales=FAKE, biases=FAKE):
+    return mtp.MtpQ4(codes, scales, biases, n, k)
+
+
+@pytest.mark.parametrize("m", [0, -1, 9])
+def test_qgemv_rejects_row_counts(m):
+    w = _q4()
+    assert mtp.lib().mtp_qgemv(C.byref(w), FAKE, None, FAKE + 4096, m, None) == mtp.MTP_ERR_INVALID_ARG
+    assert b"m=" in mtp.lib().mtp_last_error()
+
+
+@pytest.mark.parametrize("n,k,codes,want", [
+    (64, 48, FAKE, mtp.MTP_ERR_INVALID_ARG),       # k not a multiple of 32
+    (0, 64, FAKE, mtp.MTP_ERR_INVALID_ARG),        # empty output
+    (64, 8224, FAKE, mtp.MTP_ERR_UNSUPPORTED),     # k above the maximum
+    (64, 64, FAKE + 8, mtp.MTP_ERR_INVALID_ARG),   # codes not 16-byte aligned
+    (64, 64, None, mtp.MTP_ERR_INVALID_ARG),       # NULL codes
+])
+def test_qgemv_rejects_bad_weights(n, k, codes, want):
+    w = _q4(n, k, codes=codes)
+    assert mtp.lib().mtp_qgemv(C.byref(w), FAKE, None, FAKE + 4096, 1, None) == want
+
+
+def test_qgemv_rejects_null_and_aliasing():
+    w = _q4()
+    lib = mtp.lib()
+    assert lib.mtp_qgemv(None, FAKE, None, FAKE, 1, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_qgemv(C.byref(w), None, None, FAKE, 1, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_qgemv(C.byref(w), FAKE, None, FAKE, 1, None) == mtp.MTP_ERR_INVALID_ARG  # y aliases x
+    assert lib.mtp_qgemv(C.byref(w), FAKE + 4, None, FAKE + 4096, 1, None) == mtp.MTP_ERR_INVALID_ARG
+
+
+def _layer(H=256, nh=2, nkv=1, d=128, vocab=1000, inter=512):
+    q = lambda n, k: _q4(n, k)  # noqa: E731
+    z8 = mtp.MtpQ8(None, None, 0, 0, 0)
+    return mtp.MtpLayer(H, nh, nkv, d, vocab, mtp.MTP_FFN_DENSE_Q4, inter, 0, 1e6, 1e-6,
+                        FAKE, FAKE, FAKE, FAKE, FAKE,
+                        q(H, 2 * H), q(nh * d, H), q(nkv * d, H), q(nkv * d, H), q(H, nh * d),
+                        q(inter, H), q(inter, H), q(H, inter), q(vocab, H), None, z8, z8, z8, z8, z8, z8)
+
+
+def test_workspace_sizes_are_host_arithmetic():
+    lib = mtp.lib()
+    L = _layer()
+    a1 = lib.mtp_attn_decode_workspace_size(C.byref(L), 4096, 1)
+    a4 = lib.mtp_attn_decode_workspace_size(C.byref(L), 4096, 4)
+    assert 0 < a1 < a4
+    assert lib.mtp_ffn_dense_workspace_size(6144, 4) >= 4 * 6144 * 4
+    assert lib.mtp_lmhead_workspace_size(151936, 1) > 0
+    d = lib.mtp_draft_step_workspace_size(C.byref(L), 4096, 4)
+    assert d > a4
+    assert lib.mtp_ffn_moe_workspace_size(2048, 256, 8, 512, 512, 4) >= 33 * 4 * 2048 * 4
+    assert lib.mtp_ffn_dense_workspace_size(0, 1) == 0
+
+
+def test_draft_step_rejects_cache_overflow_and_small_workspace():
+    lib = mtp.lib()
+    L = _layer()
+    need = lib.mtp_draft_step_workspace_size(C.byref(L), 10, 4)
+    args = lambda cache_len, cap, ws_bytes: (C.byref(L), FAKE, None, None, FAKE, FAKE * 2, FAKE * 3, cache_len,  # noqa: E731
+                                             cap, 4, FAKE * 4, FAKE * 5, None, FAKE * 6, ws_bytes, None)
+    assert lib.mtp_draft_step(*args(10, 13, need)) == mtp.MTP_ERR_INVALID_ARG
+    assert b"overflow" in lib.mtp_last_error()
+    assert lib.mtp_draft_step(*args(10, 14, need - 1)) == mtp.MTP_ERR_WORKSPACE
+    assert lib.mtp_draft_step(*args(-1, 14, need)) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_attention_rejects_unsupported_head_dim_and_bad_group():
+    lib = mtp.lib()
+    L = _layer(d=64)
+    assert lib.mtp_attn_decode(C.byref(L), FAKE, FAKE * 2, FAKE * 3, 0, 16, 1, FAKE * 4, FAKE * 5, 1 << 30,
+                               None) == mtp.MTP_ERR_UNSUPPORTED
+    L = _layer(nh=3, nkv=2)
+    assert lib.mtp_attn_decode(C.byref(L), FAKE, FAKE * 2, FAKE * 3, 0, 16, 1, FAKE * 4, FAKE * 5, 1 << 30,
+                               None) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_moe_rejects_bad_top_k_and_half_given_shared_expert():
+    lib = mtp.lib()
+    g = mtp.MtpQ8(FAKE, FAKE, 64, 64, 4)
+    d = mtp.MtpQ8(FAKE, FAKE, 64, 64, 4)
+    call = lambda k, sg: lib.mtp_ffn_moe_q(FAKE, None, 1e-6, FAKE, k, C.byref(g), C.byref(g), C.byref(d),  # noqa: E731
+                                           sg, None, None, None, FAKE * 2, None, None, 1, FAKE * 3, 1 << 30, None)
+    assert call(5, None) == mtp.MTP_ERR_INVALID_ARG
+    assert call(0, None) == mtp.MTP_ERR_INVALID_ARG
+    assert call(2, C.byref(g)) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_lmhead_requires_ids_and_workspace():
+    lib = mtp.lib()
+    w = _q4(1000, 256)
+    assert lib.mtp_lmhead_argmax(FAKE, FAKE, 1e-6, C.byref(w), None, None, None, 1, FAKE, 1 << 20,
+                                 None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_lmhead_argmax(FAKE, FAKE, 1e-6, C.byref(w), None, None, FAKE * 2, 1, FAKE * 3, 16,
+                                 None) == mtp.MTP_ERR_WORKSPACE

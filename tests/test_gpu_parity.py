@@ -1,0 +1,408 @@
+"""GPU parity: every libmtp call against the scalar-C oracle on the same seeded
+inputs.  Bar: bit-exact dequantized weights, token ids and expert sets (ties
+excluded by construction: planted maxima, margin gates); relative L2 <= 2e-3
+on f32 activations and logits.
+
+Shapes: several-tile sizes with ragged tails (rows not a multiple of the
+tile, K not a multiple of 2048), the pages' closed-form fixtures, and the full
+configurations (4-bit GEMV 1024x1024; eh_proj 2048x4096; lm_head
+151936x2048; MoE 256 experts; the dense draft step with a 4096-row cache).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from mtp_speculative_draft_amd import synth
+from tests import planting
+
+torch = pytest.importorskip("torch")
+import mtp_speculative_draft_amd as mtp  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _t(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a if dtype is None else a.astype(dtype)).to(DEV)
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def _close(got, ref, what, tol=TOL):
+    rl = oracle.rel_l2(got, ref)
+    cs = oracle.cosine(got, ref)
+    _say(f"  {what}: rel-L2 {rl:.3e} cosine {cs:.9f} max|d| {np.abs(got.astype(np.float64) - ref).max():.3e}")
+    assert np.isfinite(got).all(), what
+    assert rl <= tol, f"{what}: rel-L2 {rl} > {tol}"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need the MI355X"
+    mtp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# dequantization (bit-exact)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k", [(1024, 1024), (37, 96), (5, 8192), (3, 32)])
+def test_dequant_q4_bit_exact(n, k):
+    _say(f"dequant_q4 n={n} k={k}")
+    w = synth.q4_weight(synth.rng(100, n, k), n, k) if (n, k) != (1024, 1024) else synth.config0_gemv()[0]
+    got = _np(mtp.mtp_dequant_q4(mtp.DeviceQ4(w)))
+    ref = oracle.deq4(w)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_q8_bit_exact():
+    w = synth.q8_weight(synth.rng(101), 3, 40, 96)
+    dw = mtp.DeviceQ8(w)
+    for e in range(3):
+        got = _np(mtp.mtp_dequant_q8(dw, e))
+        assert np.array_equal(got.view(np.uint32), oracle.deq8(w, e).view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# GEMV
+# --------------------------------------------------------------------------
+def test_qgemv_config0_full():
+    w, x = synth.config0_gemv()
+    _say("qgemv config0 1024x1024 m=1")
+    got = _np(mtp.mtp_qgemv(mtp.DeviceQ4(w), _t(x)))
+    _close(got, oracle.gemv4(w, x), "y")
+
+
+@pytest.mark.parametrize("n,k,m,res", [(1000, 96, 3, True), (333, 4096, 4, False), (517, 6144, 2, True),
+                                       (64, 32, 8, False), (300, 8192, 5, False), (2049, 2048, 7, True),
+                                       (4099, 2048, 1, False), (129, 1024, 6, True)])
+def test_qgemv_shapes(n, k, m, res):
+    _say(f"qgemv n={n} k={k} m={m} residual={res}")
+    g = synth.rng(102, n, k, m)
+    w = synth.q4_weight(g, n, k)
+    x = synth.normal(g, (m, k))
+    r = synth.normal(g, (m, n)) if res else None
+    got = _np(mtp.mtp_qgemv(mtp.DeviceQ4(w), _t(x), residual=None if r is None else _t(r)))
+    ref = oracle.gemv4(w, x)
+    if r is not None:
+        ref = (ref.astype(np.float64) + r).astype(np.float32)
+    _close(got, ref, "y")
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_qgemv_page_fixtures(idx):
+    """The three closed-form fixtures of the affine test module (max|dy| < 1e-3 there)."""
+    from tests.test_oracle_pins import _golden, _page_fixture
+    fx = _golden("page_gemv_fixtures.json")["fixtures"][idx]
+    w, _, _, _, x = _page_fixture(fx)
+    dw = mtp.DeviceQ4(w)
+    ref = oracle.gemv4(w, x)
+    for r0 in range(0, x.shape[0], 8):
+        got = _np(mtp.mtp_qgemv(dw, _t(x[r0:r0 + 8])))
+        _close(got, ref[r0:r0 + 8], f"{fx['name']} rows {r0}..")
+        assert np.abs(got - ref[r0:r0 + 8]).max() < 1e-3
+
+
+@pytest.mark.parametrize("n,k,m,e", [(513, 512, 4, 1), (64, 2048, 1, 0), (100, 6144, 3, 2)])
+def test_q8gemv_shapes(n, k, m, e):
+    _say(f"q8gemv n={n} k={k} m={m} expert={e}")
+    g = synth.rng(103, n, k, m)
+    w = synth.q8_weight(g, 3, n, k)
+    x = synth.normal(g, (m, k))
+    got = _np(mtp.mtp_q8gemv(mtp.DeviceQ8(w), e, _t(x)))
+    _close(got, oracle.gemv8(w, x, e), "y")
+
+
+# --------------------------------------------------------------------------
+# eh_proj with fused norms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("m", [1, 4])
+def test_norm_concat_proj_config1(m):
+    e, h, ge, gh, w = synth.config1_proj()
+    _say(f"norm_concat_proj config1 m={m}")
+    got = _np(mtp.mtp_norm_concat_proj(_t(e[:m]), _t(h[:m]), _t(ge), _t(gh), 1e-6, mtp.DeviceQ4(w)))
+    _close(got, oracle.norm_concat_proj(e[:m], h[:m], ge, gh, 1e-6, w), "u")
+
+
+def test_norm_concat_proj_small_ragged():
+    g = synth.rng(104)
+    H, m = 96, 3  # K = 192: six groups, half e and half h, one partial wave
+    e, h = synth.normal(g, (m, H)), synth.normal(g, (m, H))
+    ge, gh = synth.gamma(g, H), synth.gamma(g, H)
+    w = synth.q4_weight(g, 70, 2 * H)
+    got = _np(mtp.mtp_norm_concat_proj(_t(e), _t(h), _t(ge), _t(gh), 1e-6, mtp.DeviceQ4(w)))
+    _close(got, oracle.norm_concat_proj(e, h, ge, gh, 1e-6, w), "u")
+
+
+def test_norm_concat_proj_large_hidden():
+    """H = 3072: the e/h boundary falls inside the second 2048-feature chunk."""
+    g = synth.rng(105)
+    H, m = 3072, 2
+    e, h = synth.normal(g, (m, H)), synth.normal(g, (m, H))
+    ge, gh = synth.gamma(g, H), synth.gamma(g, H)
+    w = synth.q4_weight(g, 257, 2 * H)
+    got = _np(mtp.mtp_norm_concat_proj(_t(e), _t(h), _t(ge), _t(gh), 1e-6, mtp.DeviceQ4(w)))
+    _close(got, oracle.norm_concat_proj(e, h, ge, gh, 1e-6, w), "u")
+
+
+# --------------------------------------------------------------------------
+# lm_head + argmax
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def planted_config2():
+    x, gf, lm = synth.config2_head()
+    _say("planting config2 lm_head (oracle pass over 151936 rows)")
+    planted, targets, normed, logits = planting.planted_head(x, gf, lm, 1e-6, margin=0.5, seed=2)
+    return x, gf, planted, targets, normed, logits, mtp.DeviceQ4(planted)
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_lmhead_argmax_config2_planted(m, planted_config2):
+    x, gf, planted, targets, normed, logits, dlm = planted_config2
+    _say(f"lmhead config2 m={m} targets={targets[:m].tolist()}")
+    ids_ref = targets[:m]
+    normed_out = torch.empty((m, 2048), dtype=torch.float32, device=DEV)
+    logits_out = torch.empty((m, planted.n), dtype=torch.float32, device=DEV)
+    ids = _np(mtp.mtp_lmhead_argmax(_t(x[:m]), _t(gf), 1e-6, dlm, normed_out=normed_out, logits_out=logits_out))
+    assert ids.tolist() == ids_ref.tolist()
+    _close(_np(normed_out), normed[:m], "normed")
+    _close(_np(logits_out), logits[:m], "logits")
+    # ids alone (no optional outputs) take the same path
+    ids2 = _np(mtp.mtp_lmhead_argmax(_t(x[:m]), _t(gf), 1e-6, dlm))
+    assert ids2.tolist() == ids_ref.tolist()
+
+
+def test_lmhead_argmax_small_vocab_all_rows():
+    g = synth.rng(106)
+    x, gf = synth.normal(g, (8, 96)), synth.gamma(g, 96)
+    lm = synth.q4_weight(g, 1001, 96)
+    planted, targets, normed, logits = planting.planted_head(x, gf, lm, 1e-6, margin=0.25, seed=3)
+    logits_out = torch.empty((8, 1001), dtype=torch.float32, device=DEV)
+    ids = _np(mtp.mtp_lmhead_argmax(_t(x), _t(gf), 1e-6, mtp.DeviceQ4(planted), logits_out=logits_out))
+    assert ids.tolist() == targets.tolist()
+    _close(_np(logits_out), logits, "logits")
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _small_layer(seed, H=256, nh=4, nkv=2, inter=320, vocab=1000):
+    return synth.dense_layer(synth.rng(107, seed), hidden=H, n_heads=nh, n_kv_heads=nkv, head_dim=128,
+                             vocab=vocab, ffn_inter=inter)
+
+
+@pytest.mark.parametrize("cache_len,m", [(100, 1), (100, 3), (0, 1), (31, 8), (64, 2)])
+def test_attn_decode_small(cache_len, m):
+    _say(f"attn small cache_len={cache_len} m={m}")
+    L = _small_layer(1)
+    g = synth.rng(108, cache_len, m)
+    cap = cache_len + m + 5
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, cache_len, cap, 128)
+    u = synth.normal(g, (m, L.hidden))
+    dl = mtp.DeviceLayer(L)
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(dl, _t(u), dk, dv, cache_len))
+    kr, vr = kc.copy(), vc.copy()
+    ref = oracle.attention(L, u, kr, vr, cache_len)
+    _close(got, ref, "out")
+    gk, gv = _np(dk), _np(dv)
+    assert np.array_equal(gk[:, :cache_len], kc[:, :cache_len]) and np.array_equal(gv[:, :cache_len], vc[:, :cache_len])
+    assert np.array_equal(gk[:, cache_len + m:], kc[:, cache_len + m:])
+    _close(gk[:, cache_len:cache_len + m], kr[:, cache_len:cache_len + m], "appended k")
+    _close(gv[:, cache_len:cache_len + m], vr[:, cache_len:cache_len + m], "appended v")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_attn_decode_config4_shape(m):
+    _say(f"attn config4 shape m={m}")
+    g = synth.rng(109, m)
+    L = synth.dense_layer(g, vocab=64, ffn_inter=64)  # attention weights at full size
+    kc, vc = synth.kv_cache(g, 2, 4096, 4104, 128)
+    u = synth.normal(g, (m, 2048))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(u), dk, dv, 4096))
+    ref = oracle.attention(L, u, kc, vc, 4096)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, 4096:4096 + m], kc[:, 4096:4096 + m], "appended k")
+
+
+def test_attn_decode_rejects_overflow_without_writing():
+    L = _small_layer(2)
+    g = synth.rng(110)
+    kc, vc = synth.kv_cache(g, 2, 10, 12, 128)
+    dk, dv = _t(kc), _t(vc)
+    with pytest.raises(mtp.MtpError):
+        mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(synth.normal(g, (3, L.hidden))), dk, dv, 10)
+    assert np.array_equal(_np(dk), kc) and np.array_equal(_np(dv), vc)
+
+
+# --------------------------------------------------------------------------
+# FFN
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("H,inter,m,norm,res", [(256, 320, 3, True, True), (96, 64, 1, False, False),
+                                                (2048, 6144, 1, True, True), (2048, 6144, 4, True, True)])
+def test_ffn_dense(H, inter, m, norm, res):
+    _say(f"ffn_dense H={H} I={inter} m={m}")
+    g = synth.rng(111, H, inter, m)
+    gate, up, down = synth.q4_weight(g, inter, H), synth.q4_weight(g, inter, H), synth.q4_weight(g, H, inter)
+    x = synth.normal(g, (m, H))
+    gam = synth.gamma(g, H) if norm else None
+    r = synth.normal(g, (m, H)) if res else None
+    got = _np(mtp.mtp_ffn_dense_q(_t(x), None if gam is None else _t(gam), 1e-6, mtp.DeviceQ4(gate), mtp.DeviceQ4(up),
+                                  mtp.DeviceQ4(down), residual=None if r is None else _t(r)))
+    f = x if gam is None else oracle.rmsnorm(x, gam, 1e-6)
+    _close(got, oracle.ffn_dense(f, gate, up, down, r), "y")
+
+
+# --------------------------------------------------------------------------
+# MoE
+# --------------------------------------------------------------------------
+def _moe_case(cfg_seed, m, **shape):
+    for extra in range(20):
+        inp = synth.moe_inputs(synth.rng(cfg_seed, extra), m, **shape)
+        if planting.router_margin_ok(oracle.gemv_f32(inp.router, inp.x), inp.top_k, 1e-3):
+            return inp, extra
+    raise RuntimeError("no seed passed the router margin gate")
+
+
+def _run_moe(inp, gamma=None, residual=None):
+    dg, du, dd = mtp.DeviceQ8(inp.gate_exps), mtp.DeviceQ8(inp.up_exps), mtp.DeviceQ8(inp.down_exps)
+    sh = [mtp.DeviceQ8(w) for w in (inp.sh_gate, inp.sh_up, inp.sh_down)] if inp.sh_gate is not None else [None] * 3
+    y, ids, gates = mtp.mtp_ffn_moe_q(_t(inp.x), None if gamma is None else _t(gamma), 1e-6, _t(inp.router),
+                                      inp.top_k, dg, du, dd, *sh, residual=None if residual is None else _t(residual))
+    return _np(y), _np(ids), _np(gates)
+
+
+@pytest.mark.parametrize("m,shared", [(1, True), (3, True), (4, False), (8, True)])
+def test_moe_small(m, shared):
+    _say(f"moe small m={m} shared={shared}")
+    inp, extra = _moe_case(112, m, hidden=256, n_experts=16, inter=64, top_k=4, shared_inter=64 if shared else None)
+    res = synth.normal(synth.rng(113, m), (m, 256))
+    y, ids, gates = _run_moe(inp, residual=res)
+    ry, rids, rgates, _ = oracle.moe(inp, residual=res)
+    assert ids.tolist() == rids.tolist()
+    _close(gates, rgates, "gates", tol=1e-5)
+    _close(y, ry, "y")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_moe_config3(m):
+    _say(f"moe config3 m={m}")
+    for extra in range(20):
+        inp = synth.moe_inputs(synth.rng(3, extra), m)
+        if planting.router_margin_ok(oracle.gemv_f32(inp.router, inp.x), inp.top_k, 1e-3):
+            break
+    _say(f"  seed extra {extra}")
+    y, ids, gates = _run_moe(inp)
+    ry, rids, rgates, _ = oracle.moe(inp)
+    assert ids.tolist() == rids.tolist()
+    _close(gates, rgates, "gates", tol=1e-5)
+    _close(y, ry, "y")
+
+
+def test_moe_with_input_norm():
+    inp, _ = _moe_case(114, 2, hidden=256, n_experts=8, inter=64, top_k=2, shared_inter=64)
+    gam = synth.gamma(synth.rng(115), 256)
+    f = oracle.rmsnorm(inp.x, gam, 1e-6)
+    if not planting.router_margin_ok(oracle.gemv_f32(inp.router, f), inp.top_k, 1e-3):
+        pytest.skip("router margin gate not met for the normalised input")
+    y, ids, _ = _run_moe(inp, gamma=gam)
+    ry, rids, _, _ = oracle.moe(inp, x=f)
+    assert ids.tolist() == rids.tolist()
+    _close(y, ry, "y")
+
+
+# --------------------------------------------------------------------------
+# full draft step: K=3 chain at m=1, rollback, verify at m=4
+# --------------------------------------------------------------------------
+def _chain_and_verify_oracle(S):
+    L, table = S.layer, S.table
+    kc, vc = S.k_cache.copy(), S.v_cache.copy()
+    toks, hs, out = [-1], [S.h0[0]], []
+    for step in range(3):
+        ids, hid, lg = oracle.draft_step(L, S.e0, np.array([toks[-1]], np.int32), table, hs[-1][None], kc, vc,
+                                         S.cache_len + step)
+        toks.append(int(ids[0]))
+        hs.append(hid[0])
+        out.append((int(ids[0]), hid[0], lg[0]))
+    kv = S.k_cache.copy(), S.v_cache.copy()
+    ids_v, hid_v, log_v = oracle.draft_step(L, S.e0, np.array(toks, np.int32), table, np.stack(hs), kv[0], kv[1],
+                                            S.cache_len)
+    return out, (ids_v, hid_v, log_v), toks, kv
+
+
+def _chain_and_verify_gpu(S, dl, dtable):
+    m_h = torch.empty((4, S.layer.hidden), dtype=torch.float32, device=DEV)
+    m_h[0].copy_(_t(S.h0[0]))
+    tok = torch.full((4,), -1, dtype=torch.int32, device=DEV)
+    e0 = _t(S.e0)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    V = S.layer.vocab
+    chain_logits = torch.empty((3, V), dtype=torch.float32, device=DEV)
+    for step in range(3):
+        mtp.mtp_draft_step(dl, e0, tok[step:step + 1], dtable, m_h[step:step + 1], dk, dv, S.cache_len + step,
+                           ids_out=tok[step + 1:step + 2], hidden_out=m_h[step + 1:step + 2],
+                           logits_out=chain_logits[step:step + 1])
+    chain = (_np(tok)[1:].copy(), _np(m_h)[1:].copy(), _np(chain_logits))
+    e4 = e0.repeat(4, 1).contiguous()
+    ids_v = torch.empty(4, dtype=torch.int32, device=DEV)
+    hid_v = torch.empty((4, S.layer.hidden), dtype=torch.float32, device=DEV)
+    log_v = torch.empty((4, V), dtype=torch.float32, device=DEV)
+    mtp.mtp_draft_step(dl, e4, tok, dtable, m_h, dk, dv, S.cache_len, ids_out=ids_v, hidden_out=hid_v, logits_out=log_v)
+    return chain, (_np(ids_v), _np(hid_v), _np(log_v)), (_np(dk), _np(dv))
+
+
+def _check_step(S, label, ref):
+    out, ver, toks, kv = ref
+    margins = [planting.head_margin(o[2]) for o in out] + [planting.head_margin(r) for r in ver[2]]
+    _say(f"  {label}: oracle chain {toks[1:]} verify {ver[0].tolist()} min margin {min(margins):.4f}")
+    dl = mtp.DeviceLayer(S.layer)
+    chain, v, (gk, gv) = _chain_and_verify_gpu(S, dl, _t(S.table))
+    assert chain[0].tolist() == toks[1:], "chain ids"
+    _close(chain[1], np.stack([o[1] for o in out]), "chain hidden")
+    _close(chain[2], np.stack([o[2] for o in out]), "chain logits")
+    assert v[0].tolist() == ver[0].tolist(), "verify ids"
+    _close(v[1], ver[1], "verify hidden")
+    _close(v[2], ver[2], "verify logits")
+    # batched == sequential on the device too
+    assert v[0][:3].tolist() == chain[0].tolist()
+    _close(v[1][:3], chain[1], "verify rows vs chain (gpu)")
+    L0 = S.cache_len
+    _close(gk[:, L0:L0 + 4], kv[0][:, L0:L0 + 4], "cache k rows")
+    _close(gv[:, L0:L0 + 4], kv[1][:, L0:L0 + 4], "cache v rows")
+    assert np.array_equal(gk[:, :L0], S.k_cache[:, :L0])
+    return margins
+
+
+def test_draft_step_small_chain_and_verify():
+    for extra in range(1, 30):
+        S = synth.config4_step(seed_extra=1000 + extra, cache_len=100, capacity=110, hidden=256, n_heads=4,
+                               n_kv_heads=2, head_dim=128, vocab=1000, ffn_inter=320)
+        ref = _chain_and_verify_oracle(S)
+        margins = [planting.head_margin(o[2]) for o in ref[0]] + [planting.head_margin(r) for r in ref[1][2]]
+        if min(margins) >= 1e-2:
+            break
+    _check_step(S, f"small seed {extra}", ref)
+
+
+def test_draft_step_config4():
+    for extra in range(0, 20):
+        S = synth.config4_step(seed_extra=extra)
+        ref = _chain_and_verify_oracle(S)
+        margins = [planting.head_margin(o[2]) for o in ref[0]] + [planting.head_margin(r) for r in ref[1][2]]
+        _say(f"config4 seed extra {extra}: min margin {min(margins):.4f}")
+        if min(margins) >= 1e-2:
+            break
+    _check_step(S, f"config4 seed {extra}", ref)
