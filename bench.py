@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MTP draft-layer forward on one MI355X.
+
+One step = one pass of the whole hot path over the dense draft workload:
+a K=3 draft chain at m=1 (cache 4096 -> 4099), rollback, and one verify pass
+at m=4 rows over positions 4096..4099 (hidden 2048, 16 query / 2 KV heads of
+128, SwiGLU 6144, vocab 151936, 4-bit affine g32 weights, f32 KV cache).
+
+Inputs are resident in HBM before the timed region.  To keep the 256 MB
+Infinity Cache from serving repeated weight reads, R copies of the layer
+weights and of the KV caches are rotated (step i uses copy i % R).
+
+Printed: one JSON line with the weight-stream GB/s of the whole step
+(algorithmic bytes / time), draft steps/s and verify rows/s, the roofline of
+the dominant call (lm_head + argmax, timed with HIP events on its stream) and
+the oracle's CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized weight-stream GB/s (% of HBM peak); MTP draft steps/sec at m=1"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="weight/cache copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--head-only", action="store_true",
+                    help="only the lm_head + argmax launches (m=1), for counter runs")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="only a plain device copy of 256 MiB, the reference for scaling byte counters")
+    return ap.parse_args()
+
+
+def copy_ref(torch, dev, reps=4):
+    """torch's device copy of a 256 MiB f32 tensor: reads and writes 268,435,456 bytes per launch."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_ref_bytes_per_launch": src.numel() * 4, "launches": reps}), flush=True)
+
+
+def head_only(torch, mtp, synth, dev, reps):
+    """lm_head + argmax at m=1 over 3 rotated copies of a 151936 x 2048 4-bit weight."""
+    lm = synth.config2_head()[2]
+    copies = [mtp.DeviceQ4(lm, dev) for _ in range(3)]
+    gam = torch.ones(lm.k, device=dev)
+    ws = torch.zeros(mtp.mtp_lmhead_workspace_size(lm.n, 1), dtype=torch.uint8, device=dev)
+    x = torch.randn((1, lm.k), device=dev)
+    for i in range(reps):
+        mtp.mtp_lmhead_argmax(x, gam, 1e-6, copies[i % 3], ws=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"head_launches": reps, "bytes_per_launch": copies[0].nbytes}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the draft layer runs on a single MI355X; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mtp_speculative_draft_amd as mtp
+    from mtp_speculative_draft_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mtp.lib()
+    if args.copy_ref:
+        return copy_ref(torch, dev)
+    if args.head_only:
+        return head_only(torch, mtp, synth, dev, args.steps)
+
+    t0 = time.time()
+    S = synth.config4_step()
+    L = S.layer
+    R = max(1, args.copies)
+    layers = [mtp.DeviceLayer(L, dev) for _ in range(R)]
+    caches = [(torch.from_numpy(S.k_cache).to(dev), torch.from_numpy(S.v_cache).to(dev)) for _ in range(R)]
+    table = torch.from_numpy(S.table).to(dev)
+    e0 = torch.from_numpy(S.e0).to(dev)
+    e4 = e0.repeat(4, 1).contiguous()
+    h0 = torch.from_numpy(S.h0[0]).to(dev)
+    H, V, L0 = L.hidden, L.vocab, S.cache_len
+    hbuf = torch.empty((4, H), dtype=torch.float32, device=dev)
+    tok = torch.full((4,), -1, dtype=torch.int32, device=dev)
+    ids_v = torch.empty(4, dtype=torch.int32, device=dev)
+    hid_v = torch.empty((4, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(mtp.mtp_draft_step_workspace_size(layers[0], L0 + 3, 1),
+                         mtp.mtp_draft_step_workspace_size(layers[0], L0, 4)), dtype=torch.uint8, device=dev)
+    hbuf[0].copy_(h0)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def chain(i):
+        dl = layers[i % R]
+        kc, vc = caches[i % R]
+        for k in range(3):
+            mtp.mtp_draft_step(dl, e0, tok[k:k + 1], table, hbuf[k:k + 1], kc, vc, L0 + k,
+                               ids_out=tok[k + 1:k + 2], hidden_out=hbuf[k + 1:k + 2], ws=ws)
+
+    def verify(i):
+        dl = layers[i % R]
+        kc, vc = caches[i % R]
+        mtp.mtp_draft_step(dl, e4, tok, table, hbuf, kc, vc, L0, ids_out=ids_v, hidden_out=hid_v, ws=ws)
+
+    def step(i):
+        chain(i)
+        verify(i)
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n
+
+    K, W = args.steps, args.warmup
+    sec_step = timed(step, K, W)
+    sec_chain = timed(chain, K, W)
+    sec_verify = timed(verify, K, W)
+
+    # algorithmic bytes: every weight byte once per call, the K/V rows read
+    # (positions 0..cache_len+m-1, both heads, K and V) and the new rows written,
+    # the embedding rows gathered and the f32 input/output rows
+    wbytes = layers[0].weight_nbytes
+    kvrow = L.n_kv_heads * L.head_dim * 4 * 2
+
+    def call_bytes(cache_len, m):
+        return wbytes + kvrow * (cache_len + m) + kvrow * m + m * H * 4 * 3
+
+    step_bytes = sum(call_bytes(L0 + k, 1) for k in range(3)) + call_bytes(L0, 4)
+    gbs = step_bytes / sec_step / 1e9
+
+    # dominant call: lm_head + final norm + argmax, events on its own stream
+    lm_copies = [dl.q4["lm_head"] for dl in layers]
+    gam = layers[0].gammas[4]
+    hws = torch.zeros(mtp.mtp_lmhead_workspace_size(V, 4), dtype=torch.uint8, device=dev)
+    ids1 = torch.empty(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    head_ms = {}
+    for m in (1, 4):
+        xm = torch.randn((m, H), device=dev)
+        for i in range(W):
+            mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m], ws=hws)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            evs[i][0].record(stream)
+            mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m], ws=hws)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        head_ms[m] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    lm_bytes = lm_copies[0].nbytes + 8 + H * 4  # weights + ids + gamma
+    head_bytes_m1 = lm_bytes + 1 * H * 4
+    achieved = head_bytes_m1 / (head_ms[1] * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(sec_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-dot/f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense MTP draft step: K=3 chain at m=1 (cache 4096->4099) + verify at m=4; hidden 2048, "
+                        "16 q / 2 kv heads x 128, SwiGLU 6144, vocab 151936, 4-bit affine g32 weights, f32 KV",
+            "hidden": H, "vocab": V, "cache_len": L0, "verify_rows": 4, "draft_chain": 3,
+            "weight_copies_rotated": R,
+        },
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "draft_steps_per_s": round(3.0 / sec_chain, 1),
+        "verify_rows_per_s": round(4.0 / sec_verify, 1),
+        "ms_chain3": round(sec_chain * 1e3, 4),
+        "ms_verify4": round(sec_verify * 1e3, 4),
+        "step_bytes": int(step_bytes),
+        "roofline": {
+            "kernel": "mtp_lmhead_argmax (fused final RMSNorm + 4-bit lm_head GEMV + argmax), m=1",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "ms_per_launch_m1": round(head_ms[1], 5),
+            "ms_per_launch_m4": round(head_ms[4], 5),
+            "bytes_per_launch_m1": int(head_bytes_m1),
+        },
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(S, step_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(S, step_bytes, budget_s):
+    """The scalar-C oracle (single thread, as written) on a bounded sample of
+    the same workload: whole steps (chain of 3 + verify of 4) until the budget
+    is spent, at least one."""
+    import oracle
+
+    L = S.layer
+    n = 0
+    t = time.perf_counter()
+    while True:
+        kc, vc = S.k_cache.copy(), S.v_cache.copy()
+        toks, hs = [-1], [S.h0[0]]
+        for k in range(3):
+            ids, hid, _ = oracle.draft_step(L, S.e0, np.array([toks[-1]], np.int32), S.table, hs[-1][None], kc, vc,
+                                            S.cache_len + k, want_logits=False)
+            toks.append(int(ids[0]))
+            hs.append(hid[0])
+        oracle.draft_step(L, np.repeat(S.e0, 4, 0), np.array(toks, np.int32), S.table, np.stack(hs), kc, vc,
+                          S.cache_len, want_logits=False)
+        n += 1
+        el = time.perf_counter() - t
+        if el >= budget_s or el / n * (n + 1) > 2.5 * budget_s:
+            break
+    sec = el / n
+    return {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole step(s) (3 chained m=1 drafts + one m=4 verify) of the same workload",
+            "ms_per_step": round(sec * 1e3, 1),
+            # the oracle's loops are row-independent, so each of the 7 rows costs about the same
+            "draft_steps_per_s": round(7.0 / sec, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -34,7 +34,7 @@ mtp_status hip_fail(hipError_t e, const char* what) {
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap (sizes the argmax partials)
+constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap
 
 mtp_status check_rows(int32_t m) {
     if (m < 1 || m > MTP_MAX_ROWS) return fail(MTP_ERR_INVALID_ARG, "m=%d outside 1..%d", m, MTP_MAX_ROWS);
@@ -103,14 +103,19 @@ AttnWs carve_attn(Carve& c, const mtp_layer* L, int32_t cache_len, int32_t m) {
     return w;
 }
 
+// State of the fused lm_head argmax: MTP_MAX_ROWS 64-bit keys then the
+// arrival counter, in one 256-byte piece at the start of the call's share of
+// the workspace.  It is zero between calls.
 struct HeadWs {
-    float* pv;
-    int* pi;
+    unsigned long long* keys;
+    unsigned* counter;
 };
+constexpr int kHeadStateWords = MTP_MAX_ROWS * 2 + 1;
 HeadWs carve_head(Carve& c, int32_t m) {
+    (void)m;
     HeadWs w;
-    w.pv = c.take<float>((size_t)kHeadMaxBlocks * 4 * m);
-    w.pi = c.take<int>((size_t)kHeadMaxBlocks * 4 * m);
+    w.keys = c.take<unsigned long long>(MTP_MAX_ROWS + 1);
+    w.counter = reinterpret_cast<unsigned*>(w.keys + MTP_MAX_ROWS);
     return w;
 }
 
@@ -167,17 +172,16 @@ hipError_t run_head(const float* hidden, const float* gamma, float eps, const mt
     p.eps = eps;
     p.normed_out = normed_out;
     p.logits = logits_out;
-    p.part_val = w.pv;
-    p.part_idx = w.pi;
+    p.head_keys = w.keys;
+    p.counter = w.counter;
+    p.ids = ids;
     p.m = m;
     p.G = p.K / MTP_GROUP;
     p.S = (p.G + 63) / 64;
-    int maxb = 2 * device_cu_count();
+    int maxb = kHeadBlocksPerCU * device_cu_count();
     if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
     const GemvShape sh = gemv_shape(FMT_Q4, EPI_ARGMAX, m, p.N, p.K, maxb);
-    hipError_t e = launch_gemv(FMT_Q4, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
-    if (e != hipSuccess) return e;
-    return launch_argmax_final(w.pv, w.pi, sh.grid * sh.Q, m, ids, st);
+    return launch_gemv(FMT_Q4, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
 }
 
 hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* vc, int cache_len, int capacity,
@@ -610,11 +614,21 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
     if ((s = check_ws(ws, ws_bytes, need))) return s;
 
     hipStream_t st = (hipStream_t)stream;
+    // carve in the order mtp_draft_step_workspace_size measures
     Carve c{static_cast<char*>(ws)};
     float* u = c.take<float>((size_t)m * H);
     float* r1 = c.take<float>((size_t)m * H);
     float* r2 = c.take<float>((size_t)m * H);
     const AttnWs aw = carve_attn(c, L, cache_len, m);
+    const bool moe = L->ffn_kind == MTP_FFN_MOE_Q8;
+    const bool sh = L->sh_gate.codes != nullptr;
+    float* z = nullptr;
+    MoeWs mw{};
+    if (moe)
+        mw = carve_moe(c, H, L->gate_exps.n_experts, L->top_k, L->gate_exps.n, sh ? L->sh_gate.n : 0, m);
+    else
+        z = c.take<float>((size_t)m * L->ffn_inter);
+    const HeadWs hw = carve_head(c, m);
 
     // u = eh_proj [rms(e); rms(h)]
     GemvParams p{};
@@ -632,22 +646,20 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
     p.g1 = L->gamma_h;
     p.eps = L->eps;
     p.y = u;
+    p.zero_words = reinterpret_cast<unsigned*>(hw.keys);  // the head's argmax state starts from zero
+    p.zero_n = kHeadStateWords;
     hipError_t err = run_gemv(FMT_Q4, PRO_CONCAT, EPI_STORE, m, p, default_blocks(), st);
     if (err != hipSuccess) return hip_fail(err, "mtp_draft_step eh_proj");
     if ((err = run_attention(L, u, k_cache, v_cache, cache_len, capacity, m, r1, aw, st)) != hipSuccess)
         return hip_fail(err, "mtp_draft_step attention");
-    if (L->ffn_kind == MTP_FFN_DENSE_Q4) {
-        float* z = c.take<float>((size_t)m * L->ffn_inter);
+    if (!moe) {
         err = run_ffn_dense(r1, L->gamma_post, L->eps, L->gate, L->up, L->down, r1, r2, m, z, st);
     } else {
-        const bool sh = L->sh_gate.codes != nullptr;
-        const MoeWs mw = carve_moe(c, H, L->gate_exps.n_experts, L->top_k, L->gate_exps.n, sh ? L->sh_gate.n : 0, m);
         err = run_moe(r1, L->gamma_post, L->eps, L->router, L->top_k, L->gate_exps, L->up_exps, L->down_exps,
                       sh ? &L->sh_gate : nullptr, sh ? &L->sh_up : nullptr, sh ? &L->sh_down : nullptr, r1, r2,
                       nullptr, nullptr, m, mw, st);
     }
     if (err != hipSuccess) return hip_fail(err, "mtp_draft_step ffn");
-    const HeadWs hw = carve_head(c, m);
     if ((err = run_head(r2, L->gamma_final, L->eps, L->lm_head, hidden_out, logits_out, ids_out, m, hw, st)) != hipSuccess)
         return hip_fail(err, "mtp_draft_step head");
     return MTP_OK;

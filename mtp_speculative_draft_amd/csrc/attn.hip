@@ -159,27 +159,61 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     }
 }
 
-__global__ void __launch_bounds__(128) k_attn_combine(const AttnParams p) {
-    const int g = blockIdx.x, hm = blockIdx.y, dd = threadIdx.x;
-    const int GQ = p.nh / p.nkv;
-    const int mi = hm / GQ, hq = g * GQ + hm % GQ;
-    float M = -INFINITY, L = 0.0f, acc = 0.0f;
-    for (int c = 0; c < p.chunks; ++c) {
-        const float* pr = p.part + (((int64_t)c * p.nkv + g) * (GQ * p.m) + hm) * (kD + 2);
-        const float l = pr[kD + 1];
-        if (l == 0.0f) continue;
-        const float mc = pr[kD];
-        if (mc > M) {
-            const float r = __expf(M - mc);  // M = -inf gives 0
-            acc *= r;
-            L *= r;
-            M = mc;
-        }
-        const float w = __expf(mc - M);
-        acc = fmaf(w, pr[dd], acc);
-        L = fmaf(w, l, L);
+// One block per (KV head, query row-head, half of the head dims): 8 chunk
+// lanes x 64 dims.  Each lane requests a batch of chunks' (max, exp-sum, p*V)
+// at once, merges them with the online log-sum-exp rule, and the 8 lanes are
+// merged through LDS.
+constexpr int kCombDims = 64;
+constexpr int kCombLanes = 8;
+constexpr int kCombBatch = 16;
+
+__device__ __forceinline__ void lse_merge(float& M, float& L, float& A, float m2, float l2, float a2) {
+    if (!(l2 > 0.0f)) return;
+    if (m2 > M) {
+        const float r = __expf(M - m2);  // M = -inf gives 0
+        A *= r;
+        L *= r;
+        M = m2;
     }
-    p.o[(int64_t)mi * p.nh * kD + hq * kD + dd] = L > 0.0f ? acc / L : 0.0f;
+    const float w = __expf(m2 - M);
+    A = fmaf(w, a2, A);
+    L = fmaf(w, l2, L);
+}
+
+__global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const AttnParams p) {
+    __shared__ float sm[kCombLanes][kCombDims], sl[kCombLanes][kCombDims], sa[kCombLanes][kCombDims];
+    const int g = blockIdx.x, hm = blockIdx.y;
+    const int t = threadIdx.x, dl = t % kCombDims, cs = t / kCombDims;
+    const int dd = blockIdx.z * kCombDims + dl;
+    const int GQ = p.nh / p.nkv;
+    const int HM = GQ * p.m;
+    const int mi = hm / GQ, hq = g * GQ + hm % GQ;
+    const int64_t stride = (int64_t)p.nkv * HM * (kD + 2);  // between chunks
+    const float* base = p.part + ((int64_t)g * HM + hm) * (kD + 2);
+
+    float M = -INFINITY, L = 0.0f, A = 0.0f;
+    for (int c0 = cs; c0 < p.chunks; c0 += kCombLanes * kCombBatch) {
+        float lv[kCombBatch], mv[kCombBatch], av[kCombBatch];
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+            const int c = c0 + u * kCombLanes;
+            const float* pr = base + (int64_t)(c < p.chunks ? c : 0) * stride;
+            lv[u] = pr[kD + 1];
+            mv[u] = pr[kD];
+            av[u] = pr[dd];
+            if (c >= p.chunks) lv[u] = 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) lse_merge(M, L, A, mv[u], lv[u], av[u]);
+    }
+    sm[cs][dl] = M;
+    sl[cs][dl] = L;
+    sa[cs][dl] = A;
+    __syncthreads();
+    if (cs == 0) {
+        for (int j = 1; j < kCombLanes; ++j) lse_merge(M, L, A, sm[j][dl], sl[j][dl], sa[j][dl]);
+        p.o[(int64_t)mi * p.nh * kD + hq * kD + dd] = L > 0.0f ? A / L : 0.0f;
+    }
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
@@ -187,7 +221,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int HM = (p.nh / p.nkv) * p.m;
-    hipLaunchKernelGGL(k_attn_combine, dim3(p.nkv, HM), dim3(kD), 0, st, p);
+    hipLaunchKernelGGL(k_attn_combine, dim3(p.nkv, HM, kD / kCombDims), dim3(kCombLanes * kCombDims), 0, st, p);
     return hipGetLastError();
 }
 

@@ -62,6 +62,19 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     }
 }
 
+// 64-bit argmax key: order-preserving bits of the value above the complement
+// of the index, so an unsigned max picks the larger value and, among equal
+// values, the lower index.  0 means "no candidate" (below every real key).
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+    const unsigned u = __float_as_uint(v);
+    const unsigned hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)hi << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)i);
+}
+
+__device__ __forceinline__ int argmax_key_index(unsigned long long k) {
+    return k == 0ull ? 0 : (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
+}
+
 // ---------------------------------------------------------------------------
 // Activation fragment: one row of x restricted to this lane's group of 32.
 // Q4 layout: word j of the group holds nibbles k = 8j..8j+7; the even
@@ -79,31 +92,37 @@ __device__ __forceinline__ int pack_bytes(int a, int b, int c, int d) {
     return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((unsigned)d << 24);
 }
 
+__device__ __forceinline__ void split16(float x, float inv, int& h, int& l) {
+    const int q = __float2int_rn(x * inv);  // |q| <= 32512
+    h = (q + 128) >> 8;                     // round(q / 256), in -127..127
+    l = q - h * 256;                        // in -128..127
+}
+
+// Quantizes the 32 values word by word (few live registers).
 template <int FMT>
 __device__ __forceinline__ void quantize_group(const float (&xv)[32], float inv, float xs, XFrag& f) {
-    int hv[32], lv[32];
     float sx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        sx += xv[i];
-        const int q = __float2int_rn(xv[i] * inv);  // |q| <= 32512
-        const int h = (q + 128) >> 8;                // round(q / 256), in -127..127
-        hv[i] = h;
-        lv[i] = q - h * 256;                         // in -128..127
-    }
+    for (int i = 0; i < 32; ++i) sx += xv[i];
     if constexpr (FMT == FMT_Q4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            f.hi[2 * j] = pack_bytes(hv[8 * j], hv[8 * j + 2], hv[8 * j + 4], hv[8 * j + 6]);
-            f.hi[2 * j + 1] = pack_bytes(hv[8 * j + 1], hv[8 * j + 3], hv[8 * j + 5], hv[8 * j + 7]);
-            f.lo[2 * j] = pack_bytes(lv[8 * j], lv[8 * j + 2], lv[8 * j + 4], lv[8 * j + 6]);
-            f.lo[2 * j + 1] = pack_bytes(lv[8 * j + 1], lv[8 * j + 3], lv[8 * j + 5], lv[8 * j + 7]);
+            int h[8], l[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) split16(xv[8 * j + i], inv, h[i], l[i]);
+            f.hi[2 * j] = pack_bytes(h[0], h[2], h[4], h[6]);
+            f.hi[2 * j + 1] = pack_bytes(h[1], h[3], h[5], h[7]);
+            f.lo[2 * j] = pack_bytes(l[0], l[2], l[4], l[6]);
+            f.lo[2 * j + 1] = pack_bytes(l[1], l[3], l[5], l[7]);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            f.hi[j] = pack_bytes(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
-            f.lo[j] = pack_bytes(lv[4 * j], lv[4 * j + 1], lv[4 * j + 2], lv[4 * j + 3]);
+            int h[4], l[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split16(xv[4 * j + i], inv, h[i], l[i]);
+            f.hi[j] = pack_bytes(h[0], h[1], h[2], h[3]);
+            f.lo[j] = pack_bytes(l[0], l[1], l[2], l[3]);
         }
     }
     f.sxd = xs > 0.0f ? sx / xs : 0.0f;
@@ -249,12 +268,6 @@ __device__ __forceinline__ bool reduce_writer(int lane) {
     constexpr int outs = V / FINAL;  // distinct positions across the wave
     constexpr int dup = 64 / outs;   // lanes holding each position
     return (lane & (dup - 1)) == 0;
-}
-
-// Rows per wave per iteration: R*M*P <= 32 values and R <= 8.
-template <int M, int P>
-constexpr int rows_per_iter() {
-    return (32 / (M * P)) < 8 ? (32 / (M * P)) : 8;
 }
 
 template <int M>

@@ -13,8 +13,14 @@
 
 namespace mtp {
 
+// The matrices, sizes and row pointers one block works on (scalars only, so
+// the whole view stays in registers).
 struct View {
-    QMat w[3];
+    const void *c0, *c1;
+    const float *s0, *s1;
+    const float *b0, *b1;
+    int64_t dc1, dc2, ds1, ds2, db1, db2;  // byte distances matrix 0->1 and 1->2
+    int n0, n1;
     int N, K, G;
     const float* x0;
     float* y;
@@ -22,9 +28,23 @@ struct View {
 };
 
 __device__ __forceinline__ bool resolve_view(const GemvParams& p, View& v) {
-    v.w[0] = p.w[0];
-    v.w[1] = p.w[1];
-    v.w[2] = p.w[2];
+    v.c0 = p.w[0].codes;
+    v.s0 = p.w[0].scales;
+    v.b0 = p.w[0].biases;
+    v.c1 = p.w[1].codes;
+    v.s1 = p.w[1].scales;
+    v.b1 = p.w[1].biases;
+    auto dist = [](const void* a, const void* b) -> int64_t {
+        return (int64_t)(reinterpret_cast<uintptr_t>(b) - reinterpret_cast<uintptr_t>(a));
+    };
+    v.dc1 = dist(p.w[0].codes, p.w[1].codes);
+    v.dc2 = dist(p.w[1].codes, p.w[2].codes);
+    v.ds1 = dist(p.w[0].scales, p.w[1].scales);
+    v.ds2 = dist(p.w[1].scales, p.w[2].scales);
+    v.db1 = dist(p.w[0].biases, p.w[1].biases);
+    v.db2 = dist(p.w[1].biases, p.w[2].biases);
+    v.n0 = p.w[0].n;
+    v.n1 = p.w[1].n;
     v.N = p.N;
     v.K = p.K;
     v.G = p.G;
@@ -36,14 +56,15 @@ __device__ __forceinline__ bool resolve_view(const GemvParams& p, View& v) {
         if (slot >= *p.n_slots) return false;
         const int e = p.slot_expert[slot];
         if (e >= 0) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                v.w[j].codes = static_cast<const char*>(p.w[j].codes) + p.ex_codes * e;
-                v.w[j].scales = p.w[j].scales + p.ex_scales * e;
-            }
+            v.c0 = static_cast<const char*>(p.w[0].codes) + p.ex_codes * e;
+            v.s0 = p.w[0].scales + p.ex_scales * e;
+            v.c1 = static_cast<const char*>(p.w[1].codes) + p.ex_codes * e;
+            v.s1 = p.w[1].scales + p.ex_scales * e;
         } else {
-            v.w[0] = p.shw[0];
-            v.w[1] = p.shw[1];
+            v.c0 = p.shw[0].codes;
+            v.s0 = p.shw[0].scales;
+            v.c1 = p.shw[1].codes;
+            v.s1 = p.shw[1].scales;
             v.N = p.N_sh;
             v.K = p.K_sh;
             v.G = p.K_sh / kGroup;
@@ -138,29 +159,67 @@ __device__ __forceinline__ void gemv_setup(const GemvParams& p, const View& v, i
     }
 }
 
-template <int FMT, int M>
-__device__ __forceinline__ void row_partials(const QMat& w, int64_t row, int G, int g, const XFrag (&xf)[M],
-                                             float* out, int stride) {
-    WFrag<FMT> f;
-    load_frag(f, w.codes, w.scales, w.biases, row, G, g);
-    if constexpr (FMT == FMT_Q4) {
-        const Nib n = unpack_nibbles(f.c);
+// Weight fragments of one tile (R rows x P matrices) for this lane's group.
+template <int FMT, int R, int P>
+struct TileFrags {
+    WFrag<FMT> f[R][P];
+};
+
+template <int FMT, int R, int P>
+__device__ __forceinline__ void load_tile(TileFrags<FMT, R, P>& tf, const View& v, int row0, int gc) {
 #pragma unroll
-        for (int mi = 0; mi < M; ++mi) out[mi * stride] = dot_q4(n, f.s, f.b, xf[mi]);
-    } else {
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) out[mi * stride] = dot_q8(f, xf[mi]);
+    for (int r = 0; r < R; ++r) {
+        int row = row0 + r;
+        row = row < v.N ? row : v.N - 1;  // tail rows are computed and dropped
+        if constexpr (P == 2) {
+            load_frag(tf.f[r][0], v.c0, v.s0, v.b0, row, v.G, gc);
+            load_frag(tf.f[r][1], v.c1, v.s1, v.b1, row, v.G, gc);
+        } else {
+            // rows of up to three matrices concatenated along n (row is
+            // wave-uniform); the matrix is picked with 0/1 multiples of the
+            // byte distances between the arrays, which keeps it in registers
+            const int64_t in1 = row >= v.n0, in2 = row >= v.n0 + v.n1;
+            const int lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
+            const void* codes = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2;
+            const float* scales = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 +
+                                                                 in2 * v.ds2);
+            const float* biases = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 +
+                                                                 in2 * v.db2);
+            load_frag(tf.f[r][0], codes, scales, biases, lr, v.G, gc);
+        }
     }
+}
+
+// acc[(r*M + mi)*P + pp] = partial of row r, activation row mi, matrix pp.
+template <int FMT, int M, int R, int P>
+__device__ __forceinline__ void compute_tile(const TileFrags<FMT, R, P>& tf, const XFrag (&xf)[M],
+                                             float (&acc)[R * M * P]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp) {
+            const WFrag<FMT>& f = tf.f[r][pp];
+            if constexpr (FMT == FMT_Q4) {
+                const Nib n = unpack_nibbles(f.c);
+#pragma unroll
+                for (int mi = 0; mi < M; ++mi) acc[(r * M + mi) * P + pp] = dot_q4(n, f.s, f.b, xf[mi]);
+            } else {
+#pragma unroll
+                for (int mi = 0; mi < M; ++mi) acc[(r * M + mi) * P + pp] = dot_q8(f, xf[mi]);
+            }
+        }
 }
 
 template <int FMT, int M, int PRO, int EPI>
 __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
-    constexpr int R = rows_per_iter<M, P>();
+    constexpr int R = gemv_rows(M, P);
     constexpr int V = R * M * P;
     __shared__ float red[4][kWave * 2];
     __shared__ float nred[4][2];
 
+    if (p.zero_words && blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < p.zero_n)
+        p.zero_words[threadIdx.x] = 0u;
     View v;
     if (!resolve_view(p, v)) return;
 
@@ -170,6 +229,14 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     const int s = wid % S, q = wid / S;
     const int g = s * kWave + lane;
     const int gc = g < v.G ? g : v.G - 1;
+    const int tile_rows = Q * R;
+    const int ntiles = (v.N + tile_rows - 1) / tile_rows;
+
+    // the first tile's weights are requested before the activation setup so
+    // their latency overlaps it
+    TileFrags<FMT, R, P> tf;
+    int t = blockIdx.x;
+    if (t < ntiles) load_tile<FMT, R, P>(tf, v, (t * Q + q) * R, gc);
 
     XFrag xf[M];
     float xs[M];
@@ -182,35 +249,12 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     float best = -INFINITY;
     int best_i = INT_MAX;
 
-    const int tile_rows = Q * R;
-    const int ntiles = (v.N + tile_rows - 1) / tile_rows;
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (; t < ntiles; t += gridDim.x) {
         const int row0 = (t * Q + q) * R;
         float acc[V];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            int row = row0 + r;
-            row = row < v.N ? row : v.N - 1;  // tail rows are computed and dropped
-            if constexpr (EPI == EPI_SWIGLU) {
-                row_partials<FMT, M>(v.w[0], row, v.G, gc, xf, &acc[r * M * 2], 2);
-                row_partials<FMT, M>(v.w[1], row, v.G, gc, xf, &acc[r * M * 2 + 1], 2);
-            } else {
-                int lr = row, j = 0;
-                if (lr >= v.w[0].n) {
-                    lr -= v.w[0].n;
-                    j = 1;
-                    if (lr >= v.w[1].n) {
-                        lr -= v.w[1].n;
-                        j = 2;
-                    }
-                }
-                QMat w;
-                w.codes = (j == 0) ? v.w[0].codes : (j == 1 ? v.w[1].codes : v.w[2].codes);
-                w.scales = (j == 0) ? v.w[0].scales : (j == 1 ? v.w[1].scales : v.w[2].scales);
-                w.biases = (j == 0) ? v.w[0].biases : (j == 1 ? v.w[1].biases : v.w[2].biases);
-                row_partials<FMT, M>(w, lr, v.G, gc, xf, &acc[r * M], 1);
-            }
-        }
+        compute_tile<FMT, M, R, P>(tf, xf, acc);
+        // next tile's loads fly while this one is reduced and stored
+        if (t + (int)gridDim.x < ntiles) load_tile<FMT, R, P>(tf, v, ((t + gridDim.x) * Q + q) * R, gc);
         reduce_transpose<V, P>(acc, lane);
         float v0 = acc[0] * xs_l;
         float v1 = (P == 2) ? acc[P - 1] * xs_l : 0.0f;
@@ -251,40 +295,43 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
         }
     }
     if constexpr (EPI == EPI_ARGMAX) {
+        // block best per activation row: waves -> LDS -> thread 0
+        __shared__ float bv_s[4][8];
+        __shared__ int bi_s[4][8];
         if (s == 0) {
 #pragma unroll
             for (int mi = 0; mi < M; ++mi) {
                 float bv = (mi_l == mi) ? best : -INFINITY;
                 int bi = (mi_l == mi) ? best_i : INT_MAX;
                 wave_argmax(bv, bi);
-                if (lane == 0 && mi < p.m) {
-                    const int idx = (blockIdx.x * Q + q) * p.m + mi;
-                    p.part_val[idx] = bv;
-                    p.part_idx[idx] = bi;
+                if (lane == 0) {
+                    bv_s[q][mi] = bv;
+                    bi_s[q][mi] = bi;
                 }
             }
         }
-    }
-}
-
-// Second argmax pass: one block per activation row over all block partials.
-__global__ void __launch_bounds__(256) k_argmax_final(const float* pv, const int* pi, int parts, int m, int* ids) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
-    const int mi = blockIdx.x;
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int j = threadIdx.x; j < parts; j += blockDim.x) argmax_merge(bv, bi, pv[(int64_t)j * m + mi], pi[(int64_t)j * m + mi]);
-    wave_argmax(bv, bi);
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    if (lane == 0) {
-        sv[wid] = bv;
-        si[wid] = bi;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) argmax_merge(bv, bi, sv[w], si[w]);
-        ids[mi] = (bi == INT_MAX) ? 0 : bi;
+        __syncthreads();
+        __shared__ unsigned long long sink;
+        if (threadIdx.x == 0) {
+            // returning atomics: their results are consumed below, so each
+            // update has been performed before this block is counted
+            unsigned long long olds = 0;
+            for (int mi = 0; mi < p.m; ++mi) {
+                float bv = bv_s[0][mi];
+                int bi = bi_s[0][mi];
+                for (int j = 1; j < Q; ++j) argmax_merge(bv, bi, bv_s[j][mi], bi_s[j][mi]);
+                if (bi != INT_MAX) olds ^= atomicMax(p.head_keys + mi, argmax_key(bv, bi));
+            }
+            sink = olds;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            if (atomicAdd(p.counter, 1u) == gridDim.x - 1) {
+                for (int mi = 0; mi < p.m; ++mi) {
+                    const unsigned long long k = atomicExch(p.head_keys + mi, 0ull);
+                    p.ids[mi] = argmax_key_index(k);
+                }
+                atomicExch(p.counter, 0u);
+            }
+        }
     }
 }
 
@@ -343,8 +390,7 @@ GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks) {
     const int Q = (S == 1) ? 4 : (S == 2 ? 2 : 1);
     const int Mi = inst_m(m);
     const int P = (epi == EPI_SWIGLU) ? 2 : 1;
-    int R = 32 / (Mi * P);
-    R = R < 8 ? R : 8;
+    const int R = gemv_rows(Mi, P);
     const int ntiles = (N + Q * R - 1) / (Q * R);
     GemvShape sh;
     sh.Q = Q;
@@ -390,11 +436,6 @@ hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, const
     if (epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, max_slots, st);
     if (epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE>(m, p, sh, max_slots, st);
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_argmax_final(const float* pv, const int* pi, int parts, int m, int* ids, hipStream_t st) {
-    hipLaunchKernelGGL(k_argmax_final, dim3(m), dim3(256), 0, st, pv, pi, parts, m, ids);
-    return hipGetLastError();
 }
 
 hipError_t launch_dequant(int fmt, const QMat& w, int k, float* out, hipStream_t st) {

@@ -30,8 +30,8 @@ enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 //                      table[tokens[r]] when tokens && tokens[r] >= 0 else x0
 //  epilogue: EPI_STORE  y[r][n] = v (+ residual[r][n])
 //            EPI_SWIGLU y[r][n] = silu(a)*b (* rowscale[r] when given)
-//            EPI_ARGMAX logits[r][n] = v when logits; per-wave-group (max,
-//                       index) partials in part_val/part_idx [blocks*Q][m]
+//            EPI_ARGMAX logits[r][n] = v when logits; the per-row argmax
+//                       goes to ids[m] (see head_keys/counter)
 struct GemvParams {
     QMat w[3];
     int nmat;
@@ -51,8 +51,16 @@ struct GemvParams {
     const float* residual;
     const float* rowscale;
     float* logits;
-    float* part_val;
-    int* part_idx;
+    // EPI_ARGMAX: per-row 64-bit (value, index) keys merged with atomicMax and
+    // a block arrival counter; both are zero on entry and zero again on exit
+    // (the last block to arrive turns the keys into ids[m] and clears them).
+    unsigned long long* head_keys;
+    unsigned* counter;
+    int* ids;
+    // Any epilogue: when set, block (0, 0) first stores zero into zero_n words
+    // here (stream-ordered initialisation of state a later kernel uses).
+    unsigned* zero_words;
+    int zero_n;
     // Expert slots (MoE): when slot_expert is set, blockIdx.y is a slot; slots
     // >= *n_slots exit at once.  Slot j uses expert e = slot_expert[j] of the
     // stacks in w[0..1] (byte stride ex_codes, float stride ex_scales), or the
@@ -66,6 +74,16 @@ struct GemvParams {
     int64_t x_slot, y_slot, rs_slot;
 };
 
+// Weight rows a wave handles per loop iteration: R*M*P partial sums per lane
+// (P = 2 for the SwiGLU pair), at most kGemvVals, and at most kGemvRows rows.
+constexpr int kGemvRows = 8;
+constexpr int kGemvVals = 32;
+__host__ __device__ constexpr int gemv_rows(int M, int P) {
+    return (kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows;
+}
+// lm_head grid: blocks per compute unit (grid-stride over the vocabulary).
+constexpr int kHeadBlocksPerCU = 2;
+
 struct GemvShape {
     int grid, block, Q, R;
 };
@@ -77,8 +95,6 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
 // MoE slot launch: grid.y = max_slots (blocks of unused slots exit at once).
 hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, const GemvShape& sh, int max_slots,
                              hipStream_t stream);
-hipError_t launch_argmax_final(const float* part_val, const int* part_idx, int parts, int m, int* ids,
-                               hipStream_t stream);
 hipError_t launch_dequant(int fmt, const QMat& w, int k, float* out, hipStream_t stream);
 int device_cu_count();
 
