@@ -30,6 +30,33 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized weight-stream GB/s (% of HBM peak); MTP draft steps/sec at m=1"
 HBM_PEAK_GBS = 8000.0
+HEAD_PROFILE = os.path.join(ROOT, "profiles", "lmhead_m1_vocab151936.md")
+KERNEL_SOURCES = ["device.hpp", "launch.hpp", "gemv.hip"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mtp_speculative_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per lm_head launch from the committed counter summary, or None
+    when the kernel sources changed since those counters were taken."""
+    try:
+        text = open(HEAD_PROFILE).read()
+    except OSError:
+        return None
+    want, got = None, None
+    for line in text.splitlines():
+        if line.startswith("kernel-source-sha256-16:"):
+            want = line.split(":", 1)[1].split()[0]
+        if line.startswith("traffic_bytes_per_launch:"):
+            got = int(line.split(":", 1)[1].split()[0])
+    return got if (want is not None and want == kernel_source_hash()) else None
 
 
 def parse():
@@ -209,7 +236,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
+            "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, see profiles/)",
             "ms_per_launch_m1": round(head_ms[1], 5),
             "ms_per_launch_m4": round(head_ms[4], 5),
             "bytes_per_launch_m1": int(head_bytes_m1),
