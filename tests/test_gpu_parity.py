@@ -387,9 +387,11 @@ def _check_step(S, label, ref):
     assert v[0].tolist() == ver[0].tolist(), "verify ids"
     _close(v[1], ver[1], "verify hidden")
     _close(v[2], ver[2], "verify logits")
-    # batched == sequential on the device too
+    # batched == sequential on the device, bit for bit: a row's arithmetic
+    # (fragments, reduction tree, attention chunks) does not depend on m
     assert v[0][:3].tolist() == chain[0].tolist()
-    _close(v[1][:3], chain[1], "verify rows vs chain (gpu)")
+    assert np.array_equal(v[1][:3].view(np.uint32), chain[1].view(np.uint32)), "verify rows vs chain (gpu)"
+    assert np.array_equal(v[2][:3].view(np.uint32), chain[2].view(np.uint32)), "verify logits vs chain (gpu)"
     L0 = S.cache_len
     _close(gk[:, L0:L0 + 4], kv[0][:, L0:L0 + 4], "cache k rows")
     _close(gv[:, L0:L0 + 4], kv[1][:, L0:L0 + 4], "cache v rows")
@@ -417,3 +419,60 @@ def test_draft_step_config4():
         if min(margins) >= 1e-2:
             break
     _check_step(S, f"config4 seed {extra}", ref)
+
+
+# --------------------------------------------------------------------------
+# MoE draft layer end to end (the FFN is the routed 8-bit mixture)
+# --------------------------------------------------------------------------
+def _oracle_moe_step(L, moe_inp, e_rows, h, kc, vc, cache_len):
+    """The draft forward composed from the oracle's own steps with the MoE FFN
+    (returns ids, post-final-norm rows, logits, router logits of rms(r1))."""
+    u = oracle.norm_concat_proj(e_rows, h, L.gamma_e, L.gamma_h, L.eps, L.eh_proj)
+    r1 = oracle.attention(L, u, kc, vc, cache_len)
+    f = oracle.rmsnorm(r1, L.gamma_post, L.eps)
+    r2, _, _, rl = oracle.moe(moe_inp, x=f, residual=r1)
+    normed, logits, ids = oracle.head(r2, L.gamma_final, L.eps, L.lm_head)
+    return ids, normed, logits, rl
+
+
+def _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cap):
+    S = synth.config4_step(seed_extra=3000 + extra, cache_len=cache_len, capacity=cap, hidden=H, n_heads=H // 128,
+                           n_kv_heads=2 if H >= 256 else 1, head_dim=128, vocab=vocab, ffn_inter=64)
+    moe_inp = synth.moe_inputs(synth.rng(30, extra), 1, hidden=H, n_experts=E, inter=inter, top_k=top_k,
+                               shared_inter=inter)
+    L = S.layer
+    kc, vc = S.k_cache.copy(), S.v_cache.copy()
+    toks, hs, chain, rls = [-1], [S.h0[0]], [], []
+    for step in range(3):
+        e_rows = S.e0 if toks[-1] < 0 else S.table[toks[-1]][None]
+        ids, hid, lg, rl = _oracle_moe_step(L, moe_inp, e_rows, hs[-1][None], kc, vc, S.cache_len + step)
+        toks.append(int(ids[0]))
+        hs.append(hid[0])
+        chain.append((int(ids[0]), hid[0], lg[0]))
+        rls.append(rl)
+    kv = S.k_cache.copy(), S.v_cache.copy()
+    e4 = np.stack([S.e0[0]] + [S.table[t] for t in toks[1:]])
+    ver = _oracle_moe_step(L, moe_inp, e4, np.stack(hs), kv[0], kv[1], S.cache_len)
+    rls.append(ver[3])
+    margins = [planting.head_margin(c[2]) for c in chain] + [planting.head_margin(r) for r in ver[2]]
+    ok = min(margins) >= 1e-2 and all(planting.router_margin_ok(r, top_k, 1e-3) for r in rls)
+    return S, moe_inp, toks, chain, ver, ok
+
+
+@pytest.mark.parametrize("H,E,inter,top_k,vocab", [(256, 16, 64, 4, 1000), (2048, 256, 512, 8, 151936)])
+def test_draft_step_moe_chain_and_verify(H, E, inter, top_k, vocab):
+    _say(f"moe draft step H={H} E={E} top_k={top_k}")
+    cache_len = 100 if H == 256 else 4096
+    for extra in range(30):
+        S, moe_inp, toks, chain, ver, ok = _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cache_len + 8)
+        if ok:
+            break
+    _say(f"  seed extra {extra}: chain {toks[1:]} verify {ver[0].tolist()}")
+    dl = mtp.DeviceLayer(S.layer, moe=moe_inp)
+    (g_ids, g_hid, g_log), (v_ids, v_hid, v_log), _ = _chain_and_verify_gpu(S, dl, _t(S.table))
+    assert g_ids.tolist() == toks[1:]
+    _close(g_hid, np.stack([c[1] for c in chain]), "chain hidden")
+    _close(g_log, np.stack([c[2] for c in chain]), "chain logits")
+    assert v_ids.tolist() == ver[0].tolist()
+    _close(v_hid, ver[1], "verify hidden")
+    _close(v_log, ver[2], "verify logits")
