@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -209,7 +210,7 @@ hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* v
     a.nh = L->n_heads;
     a.nkv = L->n_kv_heads;
     a.d = L->head_dim;
-    a.theta = L->rope_theta;
+    a.log2_theta = log2(L->rope_theta);
     a.part = w.part;
     a.o = w.o;
     a.chunks = chunks_for(cache_len, m);

@@ -22,38 +22,65 @@
 
 namespace mtp {
 
-constexpr int kD = 128;            // head_dim handled here
-constexpr int kC = kAttnChunk;     // positions per block
-constexpr int kKStride = kD + 4;   // padded LDS row (floats)
-constexpr int kMaxHM = 64;         // query row-heads per KV head (group * m)
+constexpr int kD = 128;           // head_dim handled here
+constexpr int kC = kAttnChunk;    // positions per block
+constexpr int kKStride = kD + 4;  // padded LDS row (floats)
+constexpr int kMaxHM = 64;        // query row-heads per KV head (group * m)
+constexpr int kSStride = kC + 4;  // score row stride (16-byte aligned)
 
+// cos/sin of pos * inv_freq: the angle and its reduction to [-pi, pi] in
+// double, the sine and cosine of the reduced angle in single precision.
+__device__ __forceinline__ void rotary(double pos, double inv_freq, float& c, float& s) {
+    const double two_pi = 6.283185307179586476925286766559;
+    const double ang = pos * inv_freq;
+    const double red = ang - two_pi * rint(ang * (1.0 / two_pi));
+    __sincosf((float)red, &s, &c);
+}
+
+// HMT: the row-head count (group * m) rounded up to 8, 16, 32 or 64; the
+// register-blocked loops below are sized by it.
+template <int HMT>
 __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     __shared__ float qs[kMaxHM][kD];
     __shared__ float ks[kC][kKStride];
     __shared__ float vs[kC][kD];
-    __shared__ float sc[kMaxHM][kC + 1];
+    __shared__ float sc[kMaxHM][kSStride];
     __shared__ float rc[8][kD / 2], rs[8][kD / 2];  // rotary cos/sin per new row
     __shared__ float stat_m[kMaxHM], stat_l[kMaxHM];
 
     const int c = blockIdx.x, g = blockIdx.y;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
     const int GQ = p.nh / p.nkv;
     const int HM = GQ * p.m;
     const int ld = (p.nh + 2 * p.nkv) * kD;  // qkv row stride
     const int p0 = c * kC;
-    const float scale = 1.0f / sqrtf((float)kD);
+    const int64_t cbase = (int64_t)g * p.capacity * kD;
+    constexpr int kQuads = kC * (kD / 4) / 256;  // float4 slots of K (and of V) per thread
 
-    // rotary table for positions cache_len + mi (double precision angles)
+    // 1. the chunk's cached K/V rows are requested first ...
+    float4 kr[kQuads], vr[kQuads];
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+        const int idx = t + 256 * u, j = idx / (kD / 4), w = idx % (kD / 4);
+        const int pos = p0 + j;
+        kr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        vr[u] = kr[u];
+        if (pos < p.cache_len) {
+            kr[u] = reinterpret_cast<const float4*>(p.k_cache + cbase + (int64_t)pos * kD)[w];
+            vr[u] = reinterpret_cast<const float4*>(p.v_cache + cbase + (int64_t)pos * kD)[w];
+        }
+    }
+    // ... and the rotary table for positions cache_len + mi is built meanwhile
     for (int idx = t; idx < p.m * (kD / 2); idx += blockDim.x) {
         const int mi = idx / (kD / 2), i = idx % (kD / 2);
-        const double inv_freq = pow(p.theta, -2.0 * (double)i / (double)kD);
-        const double ang = (double)(p.cache_len + mi) * inv_freq;
-        rc[mi][i] = (float)cos(ang);
-        rs[mi][i] = (float)sin(ang);
+        const double inv_freq = exp2(-(2.0 * (double)i / (double)kD) * p.log2_theta);
+        rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
     }
     __syncthreads();
 
-    // rotated queries of this group: hm = mi * GQ + local head
+    // 2. rotated queries of this group (hm = mi * GQ + local head), cached
+    //    rows into LDS, rows past the new ones zeroed, the new rows rotated and
+    //    appended to the cache (only by the chunk that owns them)
     for (int idx = t; idx < HM * (kD / 2); idx += blockDim.x) {
         const int hm = idx / (kD / 2), i = idx % (kD / 2);
         const int mi = hm / GQ, hq = g * GQ + hm % GQ;
@@ -63,98 +90,120 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
         qs[hm][i] = a * cs - b * sn;
         qs[hm][i + kD / 2] = a * sn + b * cs;
     }
-    // cached K/V rows of the chunk (float4); new and out-of-range rows later
-    const int64_t cbase = (int64_t)g * p.capacity * kD;
-    for (int idx = t; idx < kC * (kD / 4); idx += blockDim.x) {
-        const int j = idx / (kD / 4), u = idx % (kD / 4);
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+        const int idx = t + 256 * u, j = idx / (kD / 4), w = idx % (kD / 4);
         const int pos = p0 + j;
-        float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
-        if (pos < p.cache_len) {
-            kv4 = reinterpret_cast<const float4*>(p.k_cache + cbase + (int64_t)pos * kD)[u];
-            vv4 = reinterpret_cast<const float4*>(p.v_cache + cbase + (int64_t)pos * kD)[u];
+        if (pos < p.cache_len || pos >= p.cache_len + p.m) {
+            *reinterpret_cast<float4*>(&ks[j][4 * w]) = kr[u];
+            *reinterpret_cast<float4*>(&vs[j][4 * w]) = vr[u];
         }
-        *reinterpret_cast<float4*>(&ks[j][4 * u]) = kv4;
-        *reinterpret_cast<float4*>(&vs[j][4 * u]) = vv4;
     }
-    __syncthreads();
-    // new rows owned by this chunk: rotate k, keep in LDS, append to the cache
     for (int idx = t; idx < p.m * (kD / 2); idx += blockDim.x) {
         const int mi = idx / (kD / 2), i = idx % (kD / 2);
         const int pos = p.cache_len + mi;
         if (pos < p0 || pos >= p0 + kC) continue;
         const int j = pos - p0;
-        const float* kr = p.qkv + (int64_t)mi * ld + p.nh * kD + g * kD;
-        const float* vr = p.qkv + (int64_t)mi * ld + (p.nh + p.nkv) * kD + g * kD;
-        const float a = kr[i], b = kr[i + kD / 2];
+        const float* kn = p.qkv + (int64_t)mi * ld + p.nh * kD + g * kD;
+        const float* vn = p.qkv + (int64_t)mi * ld + (p.nh + p.nkv) * kD + g * kD;
+        const float a = kn[i], b = kn[i + kD / 2];
         const float cs = rc[mi][i], sn = rs[mi][i];
         const float k0 = a * cs - b * sn, k1 = a * sn + b * cs;
         ks[j][i] = k0;
         ks[j][i + kD / 2] = k1;
-        vs[j][i] = vr[i];
-        vs[j][i + kD / 2] = vr[i + kD / 2];
+        vs[j][i] = vn[i];
+        vs[j][i + kD / 2] = vn[i + kD / 2];
         float* kd = p.k_cache + cbase + (int64_t)pos * kD;
         float* vd = p.v_cache + cbase + (int64_t)pos * kD;
         kd[i] = k0;
         kd[i + kD / 2] = k1;
-        vd[i] = vr[i];
-        vd[i + kD / 2] = vr[i + kD / 2];
+        vd[i] = vn[i];
+        vd[i + kD / 2] = vn[i + kD / 2];
     }
     __syncthreads();
 
-    // scores (masked: query row mi sees positions <= cache_len + mi)
-    for (int idx = t; idx < HM * kC; idx += blockDim.x) {
-        const int hm = idx / kC, j = idx % kC;
-        const int mi = hm / GQ;
+    // 3. scores: thread = (position j, row-head block hb); one K row read
+    //    serves every row-head hm = hb + 8r of the thread (masked: query row
+    //    mi sees positions <= cache_len + mi)
+    {
+        const int j = t % kC, hb = t / kC;  // 8 blocks of row-heads
         const int pos = p0 + j;
-        float s = -INFINITY;
-        if (pos <= p.cache_len + mi) {
-            const float4* qa = reinterpret_cast<const float4*>(&qs[hm][0]);
-            const float4* ka = reinterpret_cast<const float4*>(&ks[j][0]);
-            float acc = 0.0f;
-#pragma unroll 8
-            for (int u = 0; u < kD / 4; ++u) {
-                const float4 a = qa[u], b = ka[u];
-                acc = fmaf(a.x, b.x, acc);
-                acc = fmaf(a.y, b.y, acc);
-                acc = fmaf(a.z, b.z, acc);
-                acc = fmaf(a.w, b.w, acc);
+        const float scale = 1.0f / sqrtf((float)kD);
+        float acc[HMT / 8];
+#pragma unroll
+        for (int r = 0; r < HMT / 8; ++r) acc[r] = 0.0f;
+        const float4* ka = reinterpret_cast<const float4*>(&ks[j][0]);
+#pragma unroll 4
+        for (int u = 0; u < kD / 4; ++u) {
+            const float4 kv = ka[u];
+#pragma unroll
+            for (int r = 0; r < HMT / 8; ++r) {
+                const int hm = hb + 8 * r;
+                if (hm < HM) {
+                    const float4 qv = reinterpret_cast<const float4*>(&qs[hm][0])[u];
+                    acc[r] = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, acc[r]))));
+                }
             }
-            s = acc * scale;
         }
-        sc[hm][j] = s;
+#pragma unroll
+        for (int r = 0; r < HMT / 8; ++r) {
+            const int hm = hb + 8 * r;
+            if (hm < HM) sc[hm][j] = (pos <= p.cache_len + hm / GQ) ? acc[r] * scale : -INFINITY;
+        }
     }
     __syncthreads();
 
-    // chunk softmax statistics, one thread per query row-head
-    for (int hm = t; hm < HM; hm += blockDim.x) {
-        float mx = -INFINITY;
-        for (int j = 0; j < kC; ++j) mx = fmaxf(mx, sc[hm][j]);
-        float l = 0.0f;
-        if (mx != -INFINITY) {
-            for (int j = 0; j < kC; ++j) {
-                const float e = __expf(sc[hm][j] - mx);
-                sc[hm][j] = e;
-                l += e;
+    // 4. chunk softmax statistics: a wave takes two row-heads at a time, one
+    //    per 32-lane half, one position per lane
+    for (int hm0 = 2 * wid; hm0 < HM; hm0 += 2 * (int)(blockDim.x / kWave)) {
+        const int hm = hm0 + (lane >> 5);
+        const bool ok = hm < HM;
+        const float sv = ok ? sc[hm][lane & 31] : -INFINITY;
+        float mx = sv;
+#pragma unroll
+        for (int d = 16; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+        const float e = (mx == -INFINITY) ? 0.0f : __expf(sv - mx);
+        float l = e;
+#pragma unroll
+        for (int d = 16; d >= 1; d >>= 1) l += __shfl_xor(l, d, kWave);
+        if (ok) {
+            sc[hm][lane & 31] = e;
+            if ((lane & 31) == 0) {
+                stat_m[hm] = mx;
+                stat_l[hm] = l;
             }
-        } else {
-            for (int j = 0; j < kC; ++j) sc[hm][j] = 0.0f;
         }
-        stat_m[hm] = mx;
-        stat_l[hm] = l;
     }
     __syncthreads();
 
-    // unnormalised p*V per (hm, dim)
+    // 5. unnormalised p*V: thread = (dim, half of the row-heads)
     float* out = p.part + ((int64_t)c * p.nkv + g) * HM * (kD + 2);
-    for (int idx = t; idx < HM * kD; idx += blockDim.x) {
-        const int hm = idx / kD, dd = idx % kD;
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int j = 0; j < kC; ++j) acc = fmaf(sc[hm][j], vs[j][dd], acc);
-        out[hm * (kD + 2) + dd] = acc;
-        if (dd == 0) {
-            out[hm * (kD + 2) + kD] = stat_m[hm];
-            out[hm * (kD + 2) + kD + 1] = stat_l[hm];
+    {
+        const int dd = t % kD, hh = t / kD;
+        float acc[HMT / 2];
+#pragma unroll
+        for (int r = 0; r < HMT / 2; ++r) acc[r] = 0.0f;
+        for (int j0 = 0; j0 < kC; j0 += 4) {
+            const float v0 = vs[j0][dd], v1 = vs[j0 + 1][dd], v2 = vs[j0 + 2][dd], v3 = vs[j0 + 3][dd];
+#pragma unroll
+            for (int r = 0; r < HMT / 2; ++r) {
+                const int hm = hh + 2 * r;
+                if (hm < HM) {
+                    const float4 pv = *reinterpret_cast<const float4*>(&sc[hm][j0]);
+                    acc[r] = fmaf(pv.x, v0, fmaf(pv.y, v1, fmaf(pv.z, v2, fmaf(pv.w, v3, acc[r]))));
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < HMT / 2; ++r) {
+            const int hm = hh + 2 * r;
+            if (hm < HM) {
+                out[hm * (kD + 2) + dd] = acc[r];
+                if (dd == 0) {
+                    out[hm * (kD + 2) + kD] = stat_m[hm];
+                    out[hm * (kD + 2) + kD + 1] = stat_l[hm];
+                }
+            }
         }
     }
 }
@@ -217,7 +266,16 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
-    hipLaunchKernelGGL(k_attn_partial, dim3(p.chunks, p.nkv), dim3(256), 0, st, p);
+    const int hm = (p.nh / p.nkv) * p.m;
+    const dim3 grid(p.chunks, p.nkv), block(256);
+    if (hm <= 8)
+        hipLaunchKernelGGL(k_attn_partial<8>, grid, block, 0, st, p);
+    else if (hm <= 16)
+        hipLaunchKernelGGL(k_attn_partial<16>, grid, block, 0, st, p);
+    else if (hm <= 32)
+        hipLaunchKernelGGL(k_attn_partial<32>, grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL(k_attn_partial<kMaxHM>, grid, block, 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int HM = (p.nh / p.nkv) * p.m;
