@@ -112,8 +112,10 @@ __device__ __forceinline__ void gemv_setup(const GemvParams& p, const View& v, i
         } else {
             src = v.x0 + (int64_t)mi * v.K;
         }
+        float gv[32];
         if (active && mi < p.m) {
             load32(xv, src + kl);
+            if constexpr (PRO != PRO_PLAIN) load32(gv, gam + kl);  // both requests in flight together
         } else {
 #pragma unroll
             for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
@@ -140,12 +142,10 @@ __device__ __forceinline__ void gemv_setup(const GemvParams& p, const View& v, i
             }
             const float tot = seg ? s1 : s0;
             const float inv = rsqrtf(tot / (float)nfeat + p.eps);
-            if (active) {
-                float gv[32];
-                load32(gv, gam + kl);
+            if (active && mi < p.m) {
 #pragma unroll
                 for (int i = 0; i < 32; ++i) xv[i] = xv[i] * inv * gv[i];
-                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0 && q == 0 && mi < p.m)
+                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0 && q == 0)
                     store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
             }
         }
@@ -218,8 +218,8 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     __shared__ float red[4][kWave * 2];
     __shared__ float nred[4][2];
 
-    if (p.zero_words && blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < p.zero_n)
-        p.zero_words[threadIdx.x] = 0u;
+    if (p.zero_words && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
     if (!resolve_view(p, v)) return;
 
@@ -232,11 +232,14 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     const int tile_rows = Q * R;
     const int ntiles = (v.N + tile_rows - 1) / tile_rows;
 
-    // the first tile's weights are requested before the activation setup so
-    // their latency overlaps it
-    TileFrags<FMT, R, P> tf;
+    // the first tiles' weights are requested before the activation setup so
+    // their latency overlaps it (two tiles where the loop double-buffers)
+    constexpr bool kDouble = (M <= 2 && P == 1);
+    const int stride = gridDim.x;
+    TileFrags<FMT, R, P> tf, tf2;
     int t = blockIdx.x;
     if (t < ntiles) load_tile<FMT, R, P>(tf, v, (t * Q + q) * R, gc);
+    if (kDouble && t + stride < ntiles) load_tile<FMT, R, P>(tf2, v, ((t + stride) * Q + q) * R, gc);
 
     XFrag xf[M];
     float xs[M];
@@ -249,12 +252,9 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     float best = -INFINITY;
     int best_i = INT_MAX;
 
-    for (; t < ntiles; t += gridDim.x) {
-        const int row0 = (t * Q + q) * R;
-        float acc[V];
-        compute_tile<FMT, M, R, P>(tf, xf, acc);
-        // next tile's loads fly while this one is reduced and stored
-        if (t + (int)gridDim.x < ntiles) load_tile<FMT, R, P>(tf, v, ((t + gridDim.x) * Q + q) * R, gc);
+    // reduce one tile's partials across the lanes (and the S chunk waves) and
+    // apply the epilogue
+    auto finish = [&](float (&acc)[V], int row0) {
         reduce_transpose<V, P>(acc, lane);
         float v0 = acc[0] * xs_l;
         float v1 = (P == 2) ? acc[P - 1] * xs_l : 0.0f;
@@ -292,6 +292,35 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
                     }
                 }
             }
+        }
+    };
+
+    if constexpr (kDouble) {
+        // double buffering where the registers allow it: a tile's weights are
+        // requested two tiles ahead of their dot products
+        for (; t < ntiles; t += 2 * stride) {
+            const int t1 = t + stride;
+            {
+                float acc[V];
+                compute_tile<FMT, M, R, P>(tf, xf, acc);
+                finish(acc, (t * Q + q) * R);
+            }
+            if (t1 >= ntiles) break;
+            if (t1 + stride < ntiles) load_tile<FMT, R, P>(tf, v, ((t1 + stride) * Q + q) * R, gc);
+            {
+                float acc[V];
+                compute_tile<FMT, M, R, P>(tf2, xf, acc);
+                finish(acc, (t1 * Q + q) * R);
+            }
+            if (t1 + 2 * stride < ntiles) load_tile<FMT, R, P>(tf2, v, ((t1 + 2 * stride) * Q + q) * R, gc);
+        }
+    } else {
+        for (; t < ntiles; t += stride) {
+            float acc[V];
+            compute_tile<FMT, M, R, P>(tf, xf, acc);
+            // next tile's loads fly while this one is reduced and stored
+            if (t + stride < ntiles) load_tile<FMT, R, P>(tf, v, ((t + stride) * Q + q) * R, gc);
+            finish(acc, (t * Q + q) * R);
         }
     }
     if constexpr (EPI == EPI_ARGMAX) {
