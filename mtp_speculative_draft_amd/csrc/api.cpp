@@ -179,9 +179,13 @@ hipError_t run_head(const float* hidden, const float* gamma, float eps, const mt
     p.m = m;
     p.G = p.K / MTP_GROUP;
     p.S = (p.G + 63) / 64;
-    int maxb = kHeadBlocksPerCU * device_cu_count();
+    // persistent: one block of 8 waves per compute unit (two of 4 for more
+    // than four rows), its waves sharing the block's rows at run time
+    p.balance = 1;
+    const int waves = head_waves(EPI_ARGMAX, inst_m(m));
+    int maxb = device_cu_count() * (kMaxWaves / waves);
     if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
-    const GemvShape sh = gemv_shape(FMT_Q4, EPI_ARGMAX, m, p.N, p.K, maxb);
+    const GemvShape sh = gemv_shape(FMT_Q4, EPI_ARGMAX, m, p.N, p.K, maxb, waves);
     return launch_gemv(FMT_Q4, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
 }
 

@@ -160,12 +160,10 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
         const bool ok = hm < HM;
         const float sv = ok ? sc[hm][lane & 31] : -INFINITY;
         float mx = sv;
-#pragma unroll
-        for (int d = 16; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+        mx = half_max(mx);
         const float e = (mx == -INFINITY) ? 0.0f : __expf(sv - mx);
         float l = e;
-#pragma unroll
-        for (int d = 16; d >= 1; d >>= 1) l += __shfl_xor(l, d, kWave);
+        l = half_sum(l);
         if (ok) {
             sc[hm][lane & 31] = e;
             if ((lane & 31) == 0) {

@@ -34,16 +34,82 @@ constexpr float kQMax = 32512.0f;       // |q| bound so that hi = round(q/256) f
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// ---------------------------------------------------------------------------
+// Cross-lane pairings by distance class D (gfx950).  D = 32 and 16 use the
+// permlane swaps (the two 32-lane halves; the two 16-lane rows of each half),
+// D = 8 and 4 the row mirrors (lane i with 15-i within 16, with 7-i within
+// 8), D = 2 and 1 quad permutations (i^2, i^1).  Pairing D always flips lane
+// bit D and keeps the bits of the larger classes, and the six together join
+// all 64 lanes, so they serve both full reductions and the transposed
+// butterfly below.  No LDS traffic.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ float dpp_partner(float x) {
+    static_assert(D == 8 || D == 4 || D == 2 || D == 1, "row-local pairing");
+    constexpr int ctrl = D == 8 ? 0x140 : (D == 4 ? 0x141 : (D == 2 ? 0x4E : 0xB1));
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), ctrl, 0xF, 0xF, false));
+}
+template <int D>
+__device__ __forceinline__ int dpp_partner(int x) {
+    return (int)__float_as_uint(dpp_partner<D>(__uint_as_float((unsigned)x)));
+}
+
+// Exchange across lane bit D for D = 32 (the wave's halves) or 16 (the two
+// 16-lane rows of each half): afterwards r0 holds a from the lanes with bit D
+// clear and b from the lanes with it set, r1 the partners' a and b in the
+// same places, so a lane-wise combine of r0 and r1 gives a's pair result
+// where bit D is clear and b's where it is set.
+template <int D>
+__device__ __forceinline__ void swap_halves(float a, float b, float& r0, float& r1) {
+    static_assert(D == 32 || D == 16, "half swap");
+    if constexpr (D == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        r0 = __uint_as_float(r[0]);
+        r1 = __uint_as_float(r[1]);
+    }
+}
+
+// One all-reduce step at class D with a commutative combine f.
+template <int D, class F>
+__device__ __forceinline__ float xor_step(float v, F f) {
+    if constexpr (D >= 16) {
+        float r0, r1;
+        swap_halves<D>(v, v, r0, r1);
+        return f(r0, r1);
+    } else {
+        return f(v, dpp_partner<D>(v));
+    }
+}
+
+template <int FROM = 32, class F>
+__device__ __forceinline__ float lanes_reduce(float v, F f) {
+    if constexpr (FROM >= 32) v = xor_step<32>(v, f);
+    if constexpr (FROM >= 16) v = xor_step<16>(v, f);
+    v = xor_step<8>(v, f);
+    v = xor_step<4>(v, f);
+    v = xor_step<2>(v, f);
+    return xor_step<1>(v, f);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
+    return lanes_reduce(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-    return v;
+    return lanes_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
+// Sum / max over each 32-lane half of the wave.
+__device__ __forceinline__ float half_sum(float v) {
+    return lanes_reduce<16>(v, [](float a, float b) { return a + b; });
+}
+
+__device__ __forceinline__ float half_max(float v) {
+    return lanes_reduce<16>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // Larger value wins; equal values go to the lower index; NaN never wins.
@@ -54,13 +120,27 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi)
     }
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        float ov = __shfl_xor(v, d, kWave);
-        int oi = __shfl_xor(i, d, kWave);
-        argmax_merge(v, i, ov, oi);
+template <int D>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+    if constexpr (D >= 16) {
+        float v0, v1, i0, i1;
+        swap_halves<D>(v, v, v0, v1);
+        swap_halves<D>(__uint_as_float((unsigned)i), __uint_as_float((unsigned)i), i0, i1);
+        v = v0;
+        i = (int)__float_as_uint(i0);
+        argmax_merge(v, i, v1, (int)__float_as_uint(i1));
+    } else {
+        argmax_merge(v, i, dpp_partner<D>(v), dpp_partner<D>(i));
     }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    argmax_step<32>(v, i);
+    argmax_step<16>(v, i);
+    argmax_step<8>(v, i);
+    argmax_step<4>(v, i);
+    argmax_step<2>(v, i);
+    argmax_step<1>(v, i);
 }
 
 // 64-bit argmax key: order-preserving bits of the value above the complement
@@ -228,9 +308,9 @@ __device__ __forceinline__ float dot_q8(const WFrag<FMT_Q8>& w, const XFrag& x) 
 // ---------------------------------------------------------------------------
 // Transposed butterfly: v[0..V) per lane -> after the call each lane holds in
 // v[0..FINAL) the 64-lane sums of positions base..base+FINAL-1, where base is
-// returned by reduce_base().  Positions are halved at xor distances 32, 16, ...
-// (the lane keeping the upper half when its bit is set); once FINAL values
-// remain the rest of the distances are plain xor sums.
+// returned by reduce_base().  Positions are halved at the pairing classes 32,
+// 16, ... (the lane keeping the upper half when its bit is set); once FINAL
+// values remain the remaining classes are plain sums.
 // ---------------------------------------------------------------------------
 template <int V, int FINAL, int STEP>
 struct Butterfly {
@@ -239,17 +319,28 @@ struct Butterfly {
             constexpr int d = 32 >> STEP;
             if constexpr (V > FINAL) {
                 constexpr int half = V / 2;
-                const bool up = (lane & d) != 0;
+                if constexpr (d >= 16) {
+                    // the swap hands each lane its own and its partner's copy
+                    // of the half it keeps
 #pragma unroll
-                for (int i = 0; i < half; ++i) {
-                    const float send = up ? v[i] : v[i + half];
-                    const float keep = up ? v[i + half] : v[i];
-                    v[i] = keep + __shfl_xor(send, d, kWave);
+                    for (int i = 0; i < half; ++i) {
+                        float r0, r1;
+                        swap_halves<d>(v[i], v[i + half], r0, r1);
+                        v[i] = r0 + r1;
+                    }
+                } else {
+                    const bool up = (lane & d) != 0;
+#pragma unroll
+                    for (int i = 0; i < half; ++i) {
+                        const float send = up ? v[i] : v[i + half];
+                        const float keep = up ? v[i + half] : v[i];
+                        v[i] = keep + dpp_partner<d>(send);
+                    }
                 }
                 Butterfly<half, FINAL, STEP + 1>::run(v, lane);
             } else {
 #pragma unroll
-                for (int i = 0; i < FINAL; ++i) v[i] += __shfl_xor(v[i], d, kWave);
+                for (int i = 0; i < FINAL; ++i) v[i] = xor_step<d>(v[i], [](float a, float b) { return a + b; });
                 Butterfly<V, FINAL, STEP + 1>::run(v, lane);
             }
         }

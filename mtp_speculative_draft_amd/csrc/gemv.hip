@@ -76,86 +76,211 @@ __device__ __forceinline__ bool resolve_view(const GemvParams& p, View& v) {
     return true;
 }
 
-// Builds the lane's activation fragments for all M rows (prologue + 16-bit
-// split).  Every thread of the block calls it; it holds block barriers when
-// several waves share one weight row (S > 1).
-template <int FMT, int M, int PRO>
-__device__ __forceinline__ void gemv_setup(const GemvParams& p, const View& v, int wid, int lane, int S,
-                                           XFrag (&xf)[M], float (&xs)[M], float (*nred)[2]) {
-    const int s = wid % S, q = wid / S;
-    const int g = s * kWave + lane;
-    const bool active = g < v.G;
-    const int kk = g * kGroup;
+// Requests the lane's 32 activation features of row mi (for PRO_CONCAT: from
+// the embedding rows, the token table or the hidden rows, by the lane's
+// half of the virtual concat) and, when want_g, the matching gamma.
+template <int PRO>
+__device__ __forceinline__ void load_x_row(const GemvParams& p, const View& v, int mi, int kk, bool active,
+                                           float (&xv)[32], float (&gv)[32], bool want_g) {
+    int seg = 0, kl = kk;
+    const float* src;
+    const float* gam = p.g0;
+    if constexpr (PRO == PRO_CONCAT) {
+        seg = kk >= p.H ? 1 : 0;
+        kl = seg ? kk - p.H : kk;
+        if (seg) {
+            src = p.x1 + (int64_t)mi * p.H;
+            gam = p.g1;
+        } else {
+            src = v.x0 + (int64_t)mi * p.H;
+            if (p.tokens && mi < p.m) {
+                int tok = p.tokens[mi];
+                if (tok >= 0 || v.x0 == nullptr) {  // no e rows given: every row is a token
+                    tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
+                    src = p.table + (int64_t)tok * p.H;
+                }
+            }
+        }
+    } else {
+        src = v.x0 + (int64_t)mi * v.K;
+    }
+    if (active && mi < p.m) {
+        load32(xv, src + kl);
+        if constexpr (PRO != PRO_PLAIN)
+            if (want_g) load32(gv, gam + kl);  // both requests in flight together
+    } else {
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-        float xv[32];
-        int seg = 0, kl = kk, nfeat = v.K;
-        const float* src;
-        const float* gam = p.g0;
-        if constexpr (PRO == PRO_CONCAT) {
-            seg = kk >= p.H ? 1 : 0;
-            kl = seg ? kk - p.H : kk;
-            nfeat = p.H;
-            if (seg) {
-                src = p.x1 + (int64_t)mi * p.H;
-                gam = p.g1;
-            } else {
-                src = v.x0 + (int64_t)mi * p.H;
-                if (p.tokens && mi < p.m) {
-                    int tok = p.tokens[mi];
-                    if (tok >= 0 || v.x0 == nullptr) {  // no e rows given: every row is a token
-                        tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
-                        src = p.table + (int64_t)tok * p.H;
+        for (int i = 0; i < 32; ++i) {
+            xv[i] = 0.0f;
+            if (PRO != PRO_PLAIN && want_g) gv[i] = 0.0f;
+        }
+    }
+}
+
+// Norm (for PRO_RMS / PRO_CONCAT) and 16-bit split of the lane's features of
+// row mi.  Every thread of the block calls it; it holds block barriers when
+// several waves share one weight row (S > 1).
+template <int FMT, int PRO>
+__device__ __forceinline__ void norm_quant_row(const GemvParams& p, const View& v, int wid, int lane, int S, int mi,
+                                               int kk, bool active, float (&xv)[32], const float (&gv)[32],
+                                               XFrag& xf, float& xs, float (*nred)[2]) {
+    const int q = wid / S;
+    if constexpr (PRO != PRO_PLAIN) {
+        const int seg = (PRO == PRO_CONCAT && kk >= p.H) ? 1 : 0;
+        const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ss = fmaf(xv[i], xv[i], ss);
+        float s0 = wave_sum(seg == 0 ? ss : 0.0f);
+        float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
+        if (S > 1) {
+            __syncthreads();
+            if (lane == 0) {
+                nred[wid][0] = s0;
+                nred[wid][1] = s1;
+            }
+            __syncthreads();
+            s0 = 0.0f;
+            s1 = 0.0f;
+            for (int j = 0; j < S; ++j) {
+                s0 += nred[q * S + j][0];
+                s1 += nred[q * S + j][1];
+            }
+        }
+        const float tot = seg ? s1 : s0;
+        const float inv = rsqrtf(tot / (float)nfeat + p.eps);
+        if (active && mi < p.m) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xv[i] = xv[i] * inv * gv[i];
+            if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0 && q == 0)
+                store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
+        }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
+    am = wave_max(am);
+    const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
+    xs = am / kQMax;
+    quantize_group<FMT>(xv, inv_q, xs, xf);
+}
+
+// Block-shared setup for two or more activation rows.  The (row, chunk)
+// fragments are computed once per block instead of once per wave: wave
+// (s, q) takes rows q, q + Q, ... of its chunk s (two rows' loads in flight
+// at a time), norms combine the chunks' sums of squares through LDS, and
+// each fragment goes to LDS, from where every wave of chunk s reads all M.
+// Rows are independent work, so M rows cost about one row's latency when
+// Q >= M.  Used for two and four rows (eight would not fit the registers
+// beside the kernel's other state).
+template <int M>
+__host__ __device__ constexpr int xq_slots() { return M == 2 ? 8 : 12; }
+constexpr int kXqWords = 18;  // hi[8], lo[8], sxd, corr
+
+template <int PRO>
+__device__ __forceinline__ const float* gamma_src(const GemvParams& p, int kk) {
+    if constexpr (PRO == PRO_CONCAT) return kk >= p.H ? p.g1 + (kk - p.H) : p.g0 + kk;
+    return p.g0 + kk;
+}
+
+template <int FMT, int M, int PRO>
+__device__ __forceinline__ void shared_rows(const GemvParams& p, const View& v, int lane, int S, int Q, int s,
+                                            int q, int kk, bool active, unsigned* xq, float* xsq, float (*nq)[2],
+                                            XFrag (&xf)[M], float (&xs)[M]) {
+    constexpr int JB = 2;
+    const int per = (M + Q - 1) / Q;  // rows per wave, the same in every wave
+    float gv[32];
+    if constexpr (PRO != PRO_PLAIN) {
+        if (active) {
+            load32(gv, gamma_src<PRO>(p, kk));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) gv[i] = 0.0f;
+        }
+    }
+    const int seg = (PRO == PRO_CONCAT && kk >= p.H) ? 1 : 0;
+    for (int j0 = 0; j0 < per; j0 += JB) {
+        float xv[JB][32];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int mi = q + Q * (j0 + jj);
+            if (mi < M) load_x_row<PRO>(p, v, mi, kk, active, xv[jj], gv, false);
+        }
+        float inv[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) inv[jj] = 1.0f;
+        if constexpr (PRO != PRO_PLAIN) {
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+                const int mi = q + Q * (j0 + jj);
+                if (mi < M) {
+                    float ss = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) ss = fmaf(xv[jj][i], xv[jj][i], ss);
+                    const float s0 = wave_sum(seg == 0 ? ss : 0.0f);
+                    const float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
+                    if (lane == 0) {
+                        nq[mi * S + s][0] = s0;
+                        nq[mi * S + s][1] = s1;
                     }
                 }
             }
-        } else {
-            src = v.x0 + (int64_t)mi * v.K;
-        }
-        float gv[32];
-        if (active && mi < p.m) {
-            load32(xv, src + kl);
-            if constexpr (PRO != PRO_PLAIN) load32(gv, gam + kl);  // both requests in flight together
-        } else {
+            __syncthreads();
+            const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
-        }
-        if constexpr (PRO != PRO_PLAIN) {
-            float ss = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) ss = fmaf(xv[i], xv[i], ss);
-            float s0 = wave_sum(seg == 0 ? ss : 0.0f);
-            float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
-            if (S > 1) {
-                __syncthreads();
-                if (lane == 0) {
-                    nred[wid][0] = s0;
-                    nred[wid][1] = s1;
-                }
-                __syncthreads();
-                s0 = 0.0f;
-                s1 = 0.0f;
-                for (int j = 0; j < S; ++j) {
-                    s0 += nred[q * S + j][0];
-                    s1 += nred[q * S + j][1];
+            for (int jj = 0; jj < JB; ++jj) {
+                const int mi = q + Q * (j0 + jj);
+                if (mi < M) {
+                    float tot = 0.0f;
+                    for (int j = 0; j < S; ++j) tot += nq[mi * S + j][seg];
+                    inv[jj] = rsqrtf(tot / (float)nfeat + p.eps);
                 }
             }
-            const float tot = seg ? s1 : s0;
-            const float inv = rsqrtf(tot / (float)nfeat + p.eps);
-            if (active && mi < p.m) {
+        }
 #pragma unroll
-                for (int i = 0; i < 32; ++i) xv[i] = xv[i] * inv * gv[i];
-                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0 && q == 0)
-                    store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
+        for (int jj = 0; jj < JB; ++jj) {
+            const int mi = q + Q * (j0 + jj);
+            if (mi < M) {
+                if constexpr (PRO != PRO_PLAIN) {
+                    if (active && mi < p.m) {
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) xv[jj][i] = xv[jj][i] * inv[jj] * gv[i];
+                        if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0)
+                            store32(p.normed_out + (int64_t)mi * v.K + kk, xv[jj]);
+                    }
+                }
+                float am = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[jj][i]));
+                am = wave_max(am);
+                const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
+                const float x_s = am / kQMax;
+                XFrag f;
+                quantize_group<FMT>(xv[jj], inv_q, x_s, f);
+                unsigned* dst = xq + (mi * S + s) * kXqWords * kWave + lane;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    dst[w * kWave] = (unsigned)f.hi[w];
+                    dst[(8 + w) * kWave] = (unsigned)f.lo[w];
+                }
+                dst[16 * kWave] = __float_as_uint(f.sxd);
+                dst[17 * kWave] = __float_as_uint(f.corr);
+                if (lane == 0) xsq[mi * S + s] = x_s;
             }
         }
-        float am = 0.0f;
+    }
+    __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
-        am = wave_max(am);
-        const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
-        xs[mi] = am / kQMax;
-        quantize_group<FMT>(xv, inv_q, xs[mi], xf[mi]);
+    for (int mi = 0; mi < M; ++mi) {
+        const unsigned* src = xq + (mi * S + s) * kXqWords * kWave + lane;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            xf[mi].hi[w] = (int)src[w * kWave];
+            xf[mi].lo[w] = (int)src[(8 + w) * kWave];
+        }
+        xf[mi].sxd = __uint_as_float(src[16 * kWave]);
+        xf[mi].corr = __uint_as_float(src[17 * kWave]);
+        xs[mi] = xsq[mi * S + s];
     }
 }
 
@@ -210,40 +335,124 @@ __device__ __forceinline__ void compute_tile(const TileFrags<FMT, R, P>& tf, con
         }
 }
 
+// The work units one worker (a wave, or a whole block when S > 1) goes
+// through.  Fixed shares: worker gid of W takes units gid, gid + W, ...  (for
+// a grid of one unit per worker, unit gid).  Balanced (S == 1): the waves of
+// a block share the units blockIdx.x + gridDim.x * k and claim k one at a
+// time from a counter in LDS, so a wave that is served faster takes more
+// units; one claim is kept in flight.
+struct TileSeq {
+    int base, step, NU, i;
+    bool shared;
+    int pend;  // claim in flight (valid in lane 0)
+
+    template <class Claim>
+    __device__ void init(int b, int st, int nu, bool sh, Claim claim) {
+        base = b;
+        step = st;
+        NU = nu;
+        i = 0;
+        shared = sh;
+        if (shared) pend = claim();
+    }
+    template <class Claim>
+    __device__ int next(Claim claim) {
+        int k;
+        if (!shared) {
+            k = i++;
+        } else {
+            k = __builtin_amdgcn_readfirstlane(pend);
+            pend = claim();
+        }
+        const int u = base + step * k;
+        return u < NU ? u : -1;
+    }
+};
+
 template <int FMT, int M, int PRO, int EPI>
-__global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
+__global__ void __launch_bounds__(head_waves(EPI, M) * 64) k_gemv(const GemvParams p) {
     constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int R = gemv_rows(M, P);
     constexpr int V = R * M * P;
-    __shared__ float red[4][kWave * 2];
-    __shared__ float nred[4][2];
+    constexpr int kWaves = head_waves(EPI, M);  // waves per block, at most
+    __shared__ float red[kWaves][kWave * 2];
+    __shared__ float nred[kWaves][2];
+    __shared__ int claim_ctr;
 
     if (p.zero_words && blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
     if (!resolve_view(p, v)) return;
 
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    // the wave index is wave-uniform; saying so lets every row, pointer and
+    // branch derived from it live in scalar registers
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int S = p.S;
     const int Q = (blockDim.x / kWave) / S;
     const int s = wid % S, q = wid / S;
     const int g = s * kWave + lane;
     const int gc = g < v.G ? g : v.G - 1;
-    const int tile_rows = Q * R;
-    const int ntiles = (v.N + tile_rows - 1) / tile_rows;
+    // Work units: with S == 1 every wave is its own row-group and works on
+    // units of R rows; with S > 1 the row-groups of a block hold barriers
+    // together, so the block moves as one over units of Q*R rows (wave q
+    // taking the q-th R rows of each).
+    const int per = S == 1 ? 1 : Q;
+    const int qo = S == 1 ? 0 : q;
+    const int NU = (v.N + per * R - 1) / (per * R);
 
     // the first tiles' weights are requested before the activation setup so
     // their latency overlaps it (two tiles where the loop double-buffers)
     constexpr bool kDouble = (M <= 2 && P == 1);
-    const int stride = gridDim.x;
+    const bool active = g < v.G;
+    const int kk = g * kGroup;
+    const bool balanced = S == 1 && p.balance;
+    auto claim = [&]() {
+        int r = 0;
+        if (lane == 0) r = atomicAdd(&claim_ctr, 1);
+        return r;
+    };
+    if (balanced) {
+        if (threadIdx.x == 0) claim_ctr = 0;
+        __syncthreads();
+    }
+    TileSeq ts;
+    if (balanced)
+        ts.init(blockIdx.x, gridDim.x, NU, true, claim);
+    else if (S == 1)
+        ts.init(blockIdx.x * Q + q, gridDim.x * Q, NU, false, claim);
+    else
+        ts.init(blockIdx.x, gridDim.x, NU, false, claim);
+    auto row0 = [&](int u) { return (u * per + qo) * R; };
     TileFrags<FMT, R, P> tf, tf2;
-    int t = blockIdx.x;
-    if (t < ntiles) load_tile<FMT, R, P>(tf, v, (t * Q + q) * R, gc);
-    if (kDouble && t + stride < ntiles) load_tile<FMT, R, P>(tf2, v, ((t + stride) * Q + q) * R, gc);
+    int wa = ts.next(claim), wb = -1;
+    if (wa >= 0) load_tile<FMT, R, P>(tf, v, row0(wa), gc);
+    if constexpr (kDouble) {
+        if (wa >= 0) wb = ts.next(claim);
+        if (wb >= 0) load_tile<FMT, R, P>(tf2, v, row0(wb), gc);
+    }
 
     XFrag xf[M];
     float xs[M];
-    gemv_setup<FMT, M, PRO>(p, v, wid, lane, S, xf, xs, nred);
+    bool shared_done = false;
+    if constexpr (M == 2 || M == 4) {
+        __shared__ unsigned xq[xq_slots<M>() * kXqWords * kWave];
+        __shared__ float xsq[xq_slots<M>()];
+        __shared__ float nq[xq_slots<M>()][2];
+        if (M * S <= xq_slots<M>()) {
+            shared_rows<FMT, M, PRO>(p, v, lane, S, Q, s, q, kk, active, xq, xsq, nq, xf, xs);
+            shared_done = true;
+        }
+    }
+    if (!shared_done) {
+        float gv[32];  // gamma is the same for every row: loaded with row 0
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+            float xv[32];
+            load_x_row<PRO>(p, v, mi, kk, active, xv, gv, mi == 0);
+            norm_quant_row<FMT, PRO>(p, v, wid, lane, S, mi, kk, active, xv, gv, xf[mi], xs[mi], nred);
+        }
+    }
 
     const int pos = reduce_base<V, P>(lane) / P;  // = r * M + mi of this lane's result
     const int r_l = pos / M, mi_l = pos % M;
@@ -286,7 +495,7 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
                     }
                 } else {
                     if (p.logits && writer) p.logits[o] = v0;
-                    if (v0 > best) {  // rows only grow within a lane: ties keep the lower one
+                    if (v0 > best || (v0 == best && row < best_i)) {  // ties keep the lower row
                         best = v0;
                         best_i = row;
                     }
@@ -298,35 +507,38 @@ __global__ void __launch_bounds__(256) k_gemv(const GemvParams p) {
     if constexpr (kDouble) {
         // double buffering where the registers allow it: a tile's weights are
         // requested two tiles ahead of their dot products
-        for (; t < ntiles; t += 2 * stride) {
-            const int t1 = t + stride;
+        while (wa >= 0) {
             {
                 float acc[V];
                 compute_tile<FMT, M, R, P>(tf, xf, acc);
-                finish(acc, (t * Q + q) * R);
+                finish(acc, row0(wa));
             }
-            if (t1 >= ntiles) break;
-            if (t1 + stride < ntiles) load_tile<FMT, R, P>(tf, v, ((t1 + stride) * Q + q) * R, gc);
+            if (wb < 0) break;
+            wa = ts.next(claim);
+            if (wa >= 0) load_tile<FMT, R, P>(tf, v, row0(wa), gc);
             {
                 float acc[V];
                 compute_tile<FMT, M, R, P>(tf2, xf, acc);
-                finish(acc, (t1 * Q + q) * R);
+                finish(acc, row0(wb));
             }
-            if (t1 + 2 * stride < ntiles) load_tile<FMT, R, P>(tf2, v, ((t1 + 2 * stride) * Q + q) * R, gc);
+            wb = wa >= 0 ? ts.next(claim) : -1;
+            if (wb >= 0) load_tile<FMT, R, P>(tf2, v, row0(wb), gc);
         }
     } else {
-        for (; t < ntiles; t += stride) {
+        while (wa >= 0) {
             float acc[V];
             compute_tile<FMT, M, R, P>(tf, xf, acc);
             // next tile's loads fly while this one is reduced and stored
-            if (t + stride < ntiles) load_tile<FMT, R, P>(tf, v, ((t + stride) * Q + q) * R, gc);
-            finish(acc, (t * Q + q) * R);
+            const int nx = ts.next(claim);
+            if (nx >= 0) load_tile<FMT, R, P>(tf, v, row0(nx), gc);
+            finish(acc, row0(wa));
+            wa = nx;
         }
     }
     if constexpr (EPI == EPI_ARGMAX) {
         // block best per activation row: waves -> LDS -> thread 0
-        __shared__ float bv_s[4][8];
-        __shared__ int bi_s[4][8];
+        __shared__ float bv_s[kWaves][8];
+        __shared__ int bi_s[kWaves][8];
         if (s == 0) {
 #pragma unroll
             for (int mi = 0; mi < M; ++mi) {
@@ -398,7 +610,6 @@ __global__ void __launch_bounds__(256) k_dequant(const QMat w, int n, int K, flo
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
 
 int device_cu_count() {
     static int cached[64] = {0};
@@ -412,11 +623,11 @@ int device_cu_count() {
     return cached[dev];
 }
 
-GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks) {
+GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int waves) {
     (void)fmt;
     const int G = K / kGroup;
     const int S = (G + kWave - 1) / kWave;
-    const int Q = (S == 1) ? 4 : (S == 2 ? 2 : 1);
+    const int Q = waves / S > 1 ? waves / S : 1;
     const int Mi = inst_m(m);
     const int P = (epi == EPI_SWIGLU) ? 2 : 1;
     const int R = gemv_rows(Mi, P);

@@ -56,6 +56,10 @@ struct GemvParams {
     // (the last block to arrive turns the keys into ids[m] and clears them).
     unsigned long long* head_keys;
     unsigned* counter;
+    // Non-zero (S == 1 only): the waves of a block share its units and claim
+    // them at run time from a block-local counter instead of taking a fixed
+    // share each.
+    int balance;
     int* ids;
     // Any epilogue: when set, block (0, 0) first stores zero into zero_n words
     // here (stream-ordered initialisation of state a later kernel uses).
@@ -81,15 +85,19 @@ constexpr int kGemvVals = 32;
 __host__ __device__ constexpr int gemv_rows(int M, int P) {
     return (kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows;
 }
-// lm_head grid: blocks per compute unit (grid-stride over the vocabulary).
-constexpr int kHeadBlocksPerCU = 2;
+// Row count of the kernel instantiation that serves m activation rows.
+__host__ __device__ constexpr int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
+// Waves per block: 4, except the lm_head's persistent blocks for up to four
+// activation rows, which take a whole compute unit each (8 waves).
+constexpr int kMaxWaves = 8;
+__host__ __device__ constexpr int head_waves(int epi, int m) { return epi == EPI_ARGMAX && m <= 4 ? kMaxWaves : 4; }
 
 struct GemvShape {
     int grid, block, Q, R;
 };
 
 // Grid/block choice for a GEMV of N rows, K features (S chunks) at m rows.
-GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks);
+GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int waves = 4);
 hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
                        hipStream_t stream);
 // MoE slot launch: grid.y = max_slots (blocks of unused slots exit at once).

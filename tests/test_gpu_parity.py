@@ -196,6 +196,31 @@ def test_lmhead_argmax_reuses_one_workspace(planted_config2):
     assert int(ws[:256].count_nonzero().item()) == 0
 
 
+@pytest.mark.parametrize("m", [1, 4])
+def test_lmhead_argmax_ties_keep_lowest_row(m, planted_config2):
+    """Exact ties: each target row is copied to a lower and a higher row with
+    the same position inside an 8-row tile (so both sides compute bitwise
+    equal logits for the copies); the first maximum, the lowest copy, must win
+    whatever order the tiles were processed in."""
+    x, gf, planted, targets, normed, logits, dlm = planted_config2
+    codes, scales, biases = planted.codes.copy(), planted.scales.copy(), planted.biases.copy()
+    V = planted.n
+    want = []
+    taken = set(int(t) for t in targets[:m])
+    for t in (int(t) for t in targets[:m]):
+        dst = [d for d in (t % 8 + 8 * 3, t + 8 * 5) if d != t and 0 <= d < V and d not in taken]
+        for d in dst:
+            codes[d], scales[d], biases[d] = codes[t], scales[t], biases[t]
+            taken.add(d)
+        want.append(min([t] + dst))
+    dup = synth.Q4(codes, scales, biases)
+    _say(f"lmhead ties m={m}: targets {targets[:m].tolist()} -> lowest copies {want}")
+    ref = oracle.head(x[:m], gf, 1e-6, dup)[2]
+    assert ref.tolist() == want
+    ids = _np(mtp.mtp_lmhead_argmax(_t(x[:m]), _t(gf), 1e-6, mtp.DeviceQ4(dup)))
+    assert ids.tolist() == want
+
+
 def test_lmhead_argmax_small_vocab_all_rows():
     g = synth.rng(106)
     x, gf = synth.normal(g, (8, 96)), synth.gamma(g, 96)
