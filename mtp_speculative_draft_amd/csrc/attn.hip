@@ -7,12 +7,16 @@
 // to the cache before attention, causal grouped-query attention with scale
 // 1/sqrt(d), query head h reading KV head h / (n_heads / n_kv_heads).
 //
-// Kernel 1 (grid: position chunks x KV heads): each block takes kAttnChunk
-// cache positions of one KV head and every query head of its group for all m
-// rows, so a K/V row is read from HBM once for the whole group.  The block
-// that owns a new position rotates its k, writes k and v into the cache and
-// uses them from LDS.  It emits per (chunk, query row-head) the chunk maximum,
-// the exp-sum and the unnormalised sum of p*V.
+// Kernel 1 (one block per position chunk x KV head x slice of at most
+// kSliceHM query row-heads): each block takes kAttnChunk cache positions of
+// one KV head for up to kSliceHM (query head, row) pairs of its group, so a
+// K/V row is read from HBM once per slice.  The slices of one chunk are given
+// consecutive block slots on one XCD so they share its L2.  Every row-head's
+// arithmetic is the same whatever the slicing, so m rows at once give
+// bitwise the results of m single-row calls.  The block that owns a new
+// position rotates its k and uses it from LDS; the first slice also writes k
+// and v into the cache.  It emits per (chunk, query row-head) the chunk
+// maximum, the exp-sum and the unnormalised sum of p*V.
 // Kernel 2 (grid: KV heads x query row-heads) merges the chunks with the
 // log-sum-exp rule.
 #include <cmath>
@@ -25,7 +29,7 @@ namespace mtp {
 constexpr int kD = 128;           // head_dim handled here
 constexpr int kC = kAttnChunk;    // positions per block
 constexpr int kKStride = kD + 4;  // padded LDS row (floats)
-constexpr int kMaxHM = 64;        // query row-heads per KV head (group * m)
+constexpr int kSliceHM = 16;      // query row-heads per partial block, at most
 constexpr int kSStride = kC + 4;  // score row stride (16-byte aligned)
 
 // cos/sin of pos * inv_freq: the angle and its reduction to [-pi, pi] in
@@ -37,21 +41,39 @@ __device__ __forceinline__ void rotary(double pos, double inv_freq, float& c, fl
     __sincosf((float)red, &s, &c);
 }
 
-// HMT: the row-head count (group * m) rounded up to 8, 16, 32 or 64; the
-// register-blocked loops below are sized by it.
+// Block slot -> (chunk, KV head, slice): slots are dealt to the XCDs in turn
+// (slot % 8), so the Z slices of a (chunk, head) pair take Z consecutive
+// slots of one XCD.  Returns false for the padding slots of the last round.
+__device__ __forceinline__ bool attn_block(const AttnParams& p, int Z, int& c, int& g, int& z) {
+    const int L = blockIdx.x, x = L % 8, r = L / 8;
+    z = r % Z;
+    const int pair = (r / Z) * 8 + x;
+    if (pair >= p.chunks * p.nkv) return false;
+    c = pair / p.nkv;
+    g = pair % p.nkv;
+    return true;
+}
+
+// HMT: the block's row-head count rounded up to 8 or 16; the register-blocked
+// loops below are sized by it.  Local row-head hl of slice z is the group's
+// row-head z * kSliceHM + hl (= mi * GQ + local query head).
 template <int HMT>
 __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
-    __shared__ float qs[kMaxHM][kD];
+    __shared__ float qs[HMT][kD];
     __shared__ float ks[kC][kKStride];
     __shared__ float vs[kC][kD];
-    __shared__ float sc[kMaxHM][kSStride];
+    __shared__ float sc[HMT][kSStride];
     __shared__ float rc[8][kD / 2], rs[8][kD / 2];  // rotary cos/sin per new row
-    __shared__ float stat_m[kMaxHM], stat_l[kMaxHM];
+    __shared__ float stat_m[HMT], stat_l[HMT];
 
-    const int c = blockIdx.x, g = blockIdx.y;
-    const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
     const int GQ = p.nh / p.nkv;
-    const int HM = GQ * p.m;
+    const int HMall = GQ * p.m;
+    const int Z = (HMall + kSliceHM - 1) / kSliceHM;
+    int c, g, z;
+    if (!attn_block(p, Z, c, g, z)) return;
+    const int hm0 = z * kSliceHM;
+    const int HM = HMall - hm0 < kSliceHM ? HMall - hm0 : kSliceHM;  // row-heads of this block
+    const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
     const int ld = (p.nh + 2 * p.nkv) * kD;  // qkv row stride
     const int p0 = c * kC;
     const int64_t cbase = (int64_t)g * p.capacity * kD;
@@ -83,7 +105,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     //    appended to the cache (only by the chunk that owns them)
     for (int idx = t; idx < HM * (kD / 2); idx += blockDim.x) {
         const int hm = idx / (kD / 2), i = idx % (kD / 2);
-        const int mi = hm / GQ, hq = g * GQ + hm % GQ;
+        const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
         const float* q = p.qkv + (int64_t)mi * ld + hq * kD;
         const float a = q[i], b = q[i + kD / 2];
         const float cs = rc[mi][i], sn = rs[mi][i];
@@ -113,6 +135,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
         ks[j][i + kD / 2] = k1;
         vs[j][i] = vn[i];
         vs[j][i + kD / 2] = vn[i + kD / 2];
+        if (z != 0) continue;  // one slice writes the cache
         float* kd = p.k_cache + cbase + (int64_t)pos * kD;
         float* vd = p.v_cache + cbase + (int64_t)pos * kD;
         kd[i] = k0;
@@ -148,15 +171,15 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
 #pragma unroll
         for (int r = 0; r < HMT / 8; ++r) {
             const int hm = hb + 8 * r;
-            if (hm < HM) sc[hm][j] = (pos <= p.cache_len + hm / GQ) ? acc[r] * scale : -INFINITY;
+            if (hm < HM) sc[hm][j] = (pos <= p.cache_len + (hm0 + hm) / GQ) ? acc[r] * scale : -INFINITY;
         }
     }
     __syncthreads();
 
     // 4. chunk softmax statistics: a wave takes two row-heads at a time, one
     //    per 32-lane half, one position per lane
-    for (int hm0 = 2 * wid; hm0 < HM; hm0 += 2 * (int)(blockDim.x / kWave)) {
-        const int hm = hm0 + (lane >> 5);
+    for (int hp = 2 * wid; hp < HM; hp += 2 * (int)(blockDim.x / kWave)) {
+        const int hm = hp + (lane >> 5);
         const bool ok = hm < HM;
         const float sv = ok ? sc[hm][lane & 31] : -INFINITY;
         float mx = sv;
@@ -175,7 +198,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     __syncthreads();
 
     // 5. unnormalised p*V: thread = (dim, half of the row-heads)
-    float* out = p.part + ((int64_t)c * p.nkv + g) * HM * (kD + 2);
+    float* out = p.part + (((int64_t)c * p.nkv + g) * HMall + hm0) * (kD + 2);
     {
         const int dd = t % kD, hh = t / kD;
         float acc[HMT / 2];
@@ -265,15 +288,13 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int hm = (p.nh / p.nkv) * p.m;
-    const dim3 grid(p.chunks, p.nkv), block(256);
+    const int Z = (hm + kSliceHM - 1) / kSliceHM;
+    const int pairs = p.chunks * p.nkv;
+    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
     if (hm <= 8)
         hipLaunchKernelGGL(k_attn_partial<8>, grid, block, 0, st, p);
-    else if (hm <= 16)
-        hipLaunchKernelGGL(k_attn_partial<16>, grid, block, 0, st, p);
-    else if (hm <= 32)
-        hipLaunchKernelGGL(k_attn_partial<32>, grid, block, 0, st, p);
     else
-        hipLaunchKernelGGL(k_attn_partial<kMaxHM>, grid, block, 0, st, p);
+        hipLaunchKernelGGL(k_attn_partial<kSliceHM>, grid, block, 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int HM = (p.nh / p.nkv) * p.m;

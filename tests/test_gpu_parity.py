@@ -261,8 +261,10 @@ def test_attn_decode_small(cache_len, m):
     _close(gv[:, cache_len:cache_len + m], vr[:, cache_len:cache_len + m], "appended v")
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
 def test_attn_decode_config4_shape(m):
+    """8 query heads per KV head: m = 1, 2 fit one block's 16 row-heads, m = 3,
+    4 and 8 (24, 32, 64 row-heads) are split over 2, 2 and 4 blocks."""
     _say(f"attn config4 shape m={m}")
     g = synth.rng(109, m)
     L = synth.dense_layer(g, vocab=64, ffn_inter=64)  # attention weights at full size
