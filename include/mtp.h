@@ -180,7 +180,7 @@ mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const fl
 /* Shared head with a greedy pick ([mtp.rs] `forward_shared_head_greedy`):
  *   yn = rms(hidden; gamma); logits = lm_head yn; ids[r] = argmax_v logits[r][v]
  * (ties to the lowest index).  normed_out [m][H] and logits_out [m][V] are
- * optional (NULL skips them); ids_out int32 [m] is required.  The first 256
+ * optional (NULL skips them); ids_out int32 [m] is required.  The first 1152
  * bytes of ws hold the state of the fused cross-block argmax: they must be
  * zero when the call starts (zero-fill ws before its first use) and every
  * call leaves them at zero again. */

@@ -343,7 +343,7 @@ def mtp_lmhead_argmax(hidden, gamma, eps: float, lm_head: DeviceQ4, normed_out=N
     _f32(hidden, "hidden")
     m = _rows(hidden)
     ids_out = torch.empty(m, dtype=torch.int32, device=hidden.device) if ids_out is None else ids_out
-    if ws is None:  # its leading counter must start at zero
+    if ws is None:  # its leading argmax state must start at zero
         ws = torch.zeros(max(mtp_lmhead_workspace_size(lm_head.n, m), 256), dtype=torch.uint8, device=hidden.device)
     _check(lib().mtp_lmhead_argmax(_ptr(hidden), _ptr(gamma), float(eps), C.byref(lm_head.desc), _ptr(normed_out),
                                    _ptr(logits_out), _ptr(ids_out), m, _ptr(ws), _nbytes(ws), _stream(hidden)),

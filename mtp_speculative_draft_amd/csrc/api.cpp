@@ -35,7 +35,6 @@ mtp_status hip_fail(hipError_t e, const char* what) {
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap
 
 mtp_status check_rows(int32_t m) {
     if (m < 1 || m > MTP_MAX_ROWS) return fail(MTP_ERR_INVALID_ARG, "m=%d outside 1..%d", m, MTP_MAX_ROWS);
@@ -104,19 +103,20 @@ AttnWs carve_attn(Carve& c, const mtp_layer* L, int32_t cache_len, int32_t m) {
     return w;
 }
 
-// State of the fused lm_head argmax: MTP_MAX_ROWS 64-bit keys then the
-// arrival counter, in one 256-byte piece at the start of the call's share of
-// the workspace.  It is zero between calls.
+// State of the fused lm_head argmax at the start of the call's share of the
+// workspace: MTP_MAX_ROWS 64-bit keys on their own 128-byte lines, then the
+// arrival counter on one more line.  It is zero between calls.
 struct HeadWs {
     unsigned long long* keys;
     unsigned* counter;
 };
-constexpr int kHeadStateWords = MTP_MAX_ROWS * 2 + 1;
+static_assert(kHeadRows == MTP_MAX_ROWS, "argmax state sized for the ABI's row limit");
+constexpr int kHeadStateWords = kHeadStateBytes / 4;
 HeadWs carve_head(Carve& c, int32_t m) {
     (void)m;
     HeadWs w;
-    w.keys = c.take<unsigned long long>(MTP_MAX_ROWS + 1);
-    w.counter = reinterpret_cast<unsigned*>(w.keys + MTP_MAX_ROWS);
+    w.keys = c.take<unsigned long long>(kHeadStateBytes / 8);
+    w.counter = reinterpret_cast<unsigned*>(w.keys + kHeadRows * kKeyStride);
     return w;
 }
 

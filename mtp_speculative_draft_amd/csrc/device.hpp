@@ -10,9 +10,9 @@
 //     scale per (chunk, row): x ~= xs * (256*hi + lo).  The integer dot
 //     products with the weight codes then run on v_dot4_i32_i8, exact in
 //     int32; 4-bit codes only need a mask and a shift to become bytes.
-//   * per (weight row, group) a lane returns s*(A + c) + b*sum(x)/xs, A the
-//     exact integer dot and c a correction for the rounding of x (see
-//     quantize_group); a transposed butterfly reduces many rows' partials
+//   * per (weight row, group) a lane returns s*A + b*sum(x^), A the exact
+//     integer dot and x^ the quantized activations (see quantize_group); a
+//     transposed butterfly reduces many rows' partials
 //     across the 64 lanes at once, and the chunk result is xs * sum.
 // Weight formats (hf2q 0.1.1, src/serve/forward_mlx_shared.rs,
 // `MlxAffineExtra` / `MlxQWeight::from_mlx_affine_linear`): 4-bit codes u32
@@ -166,43 +166,41 @@ __device__ __forceinline__ int argmax_key_index(unsigned long long k) {
 struct XFrag {
     int hi[8];
     int lo[8];
-    float sxd;   // (sum of the 32 values) / xs, the bias factor of 4-bit rows
-    float corr;  // 8 * sum of the rounding residuals x/xs - q (4-bit rows)
+    float sxd;  // sum of the group's 32 quantized values (an integer), the bias factor of 4-bit rows
 };
 
 __device__ __forceinline__ int pack_bytes(int a, int b, int c, int d) {
     return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((unsigned)d << 24);
 }
 
-// Returns the rounding residual x*inv - q.
-__device__ __forceinline__ float split16(float x, float inv, int& h, int& l) {
-    const float t = x * inv;
-    const int q = __float2int_rn(t);  // |q| <= 32512
-    h = (q + 128) >> 8;               // round(q / 256), in -127..127
-    l = q - h * 256;                  // in -128..127
-    return t - (float)q;
+// Returns the 16-bit quantized value q = round(x*inv) as hi*256 + lo.
+__device__ __forceinline__ int split16(float x, float inv, int& h, int& l) {
+    const int q = __float2int_rn(x * inv);  // |q| <= 32512
+    h = (q + 128) >> 8;                     // round(q / 256), in -127..127
+    l = q - h * 256;                        // in -128..127
+    return q;
 }
 
 // Quantizes the 32 values word by word (few live registers).
 //
-// 4-bit rows: a row's group term is s*sum(q_k x_k) + b*sum(x_k).  With
-// x_k = xs*(xq_k + r_k) the products the integer dot misses are
-// s*xs*sum(q_k r_k).  Codes scatter around their midpoint 8 (the bias is about
-// -8s), so that sum is mostly 8*sum(r_k), the same for every row: left alone
-// it would be an error shared by all outputs, which a following projection
-// whose rows also share a mean amplifies.  `corr` = 8*sum(r_k) is added to
-// every row's dot, leaving only sum((q_k - 8) r_k).
+// 4-bit rows: with the group's quantized activations x^_k (x ~ xs * x^) a
+// row's group term is computed as s * sum(c_k x^_k) + b * sum(x^_k), both
+// sums exact integers; that is sum((s c_k + b) x^_k), the exact product of the
+// row's weights with the quantized activations.  Its only error is the
+// activation rounding weighted by the weights themselves, which are centred
+// (the bias is about -8 s), so no error is shared by all rows.  (Summing the
+// unrounded x/xs for the bias factor instead would leave the codes' mean 8
+// times the rounding residual as such a shared error.)
 template <int FMT>
 __device__ __forceinline__ void quantize_group(const float (&xv)[32], float inv, float xs, XFrag& f) {
-    float sx = 0.0f, rs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sx += xv[i];
+    (void)xs;
+    int qs = 0;
     if constexpr (FMT == FMT_Q4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             int h[8], l[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) rs += split16(xv[8 * j + i], inv, h[i], l[i]);
+            for (int i = 0; i < 8; ++i) qs += split16(xv[8 * j + i], inv, h[i], l[i]);
             f.hi[2 * j] = pack_bytes(h[0], h[2], h[4], h[6]);
             f.hi[2 * j + 1] = pack_bytes(h[1], h[3], h[5], h[7]);
             f.lo[2 * j] = pack_bytes(l[0], l[2], l[4], l[6]);
@@ -218,8 +216,7 @@ __device__ __forceinline__ void quantize_group(const float (&xv)[32], float inv,
             f.lo[j] = pack_bytes(l[0], l[1], l[2], l[3]);
         }
     }
-    f.sxd = xs > 0.0f ? sx / xs : 0.0f;
-    f.corr = 8.0f * rs;
+    f.sxd = (float)qs;  // exact: |qs| <= 32 * 32512 < 2^24
 }
 
 // ---------------------------------------------------------------------------
@@ -288,7 +285,7 @@ __device__ __forceinline__ float dot_q4(const Nib& n, float s, float b, const XF
         al = sdot4(n.o[j], x.lo[2 * j + 1], al);
     }
     const int a = ah * 256 + al;  // exact: |a| < 2^24
-    return fmaf(s, (float)a + x.corr, b * x.sxd);
+    return fmaf(s, (float)a, b * x.sxd);
 }
 
 // s*A for an 8-bit row against one activation fragment.

@@ -175,7 +175,7 @@ __device__ __forceinline__ void norm_quant_row(const GemvParams& p, const View& 
 // beside the kernel's other state).
 template <int M>
 __host__ __device__ constexpr int xq_slots() { return M == 2 ? 8 : 12; }
-constexpr int kXqWords = 18;  // hi[8], lo[8], sxd, corr
+constexpr int kXqWords = 18;  // hi[8], lo[8], sxd, one spare word
 
 template <int PRO>
 __device__ __forceinline__ const float* gamma_src(const GemvParams& p, int kk) {
@@ -264,7 +264,6 @@ __device__ __forceinline__ void shared_rows(const GemvParams& p, const View& v, 
                     dst[(8 + w) * kWave] = (unsigned)f.lo[w];
                 }
                 dst[16 * kWave] = __float_as_uint(f.sxd);
-                dst[17 * kWave] = __float_as_uint(f.corr);
                 if (lane == 0) xsq[mi * S + s] = x_s;
             }
         }
@@ -279,7 +278,6 @@ __device__ __forceinline__ void shared_rows(const GemvParams& p, const View& v, 
             xf[mi].lo[w] = (int)src[(8 + w) * kWave];
         }
         xf[mi].sxd = __uint_as_float(src[16 * kWave]);
-        xf[mi].corr = __uint_as_float(src[17 * kWave]);
         xs[mi] = xsq[mi * S + s];
     }
 }
@@ -333,6 +331,35 @@ __device__ __forceinline__ void compute_tile(const TileFrags<FMT, R, P>& tf, con
                 for (int mi = 0; mi < M; ++mi) acc[(r * M + mi) * P + pp] = dot_q8(f, xf[mi]);
             }
         }
+}
+
+// Cross-block argmax, run by thread 0 of every block once the block's per-row
+// bests (value, index) of its nw waves are in LDS.  The block's best key per
+// row goes into the row's key with a returning atomicMax (the returns are
+// consumed, so the updates have been performed before the block counts
+// itself), then the block counts itself on the arrival counter; the last
+// block to arrive turns the keys into ids[m] and leaves keys and counter at
+// zero.  Only workgroup-scope fences are used: the device-scope atomics are
+// performed at the memory side, and an agent-scope fence would write back
+// and invalidate the L2 in every block.
+__device__ __forceinline__ void grid_argmax(const GemvParams& p, int nw, const float (*bv_s)[8],
+                                            const int (*bi_s)[8], unsigned long long* sink) {
+    unsigned long long olds = 0;
+    for (int r = 0; r < p.m; ++r) {
+        float bv = bv_s[0][r];
+        int bi = bi_s[0][r];
+        for (int w = 1; w < nw; ++w) argmax_merge(bv, bi, bv_s[w][r], bi_s[w][r]);
+        if (bi != INT_MAX) olds ^= atomicMax(p.head_keys + r * kKeyStride, argmax_key(bv, bi));
+    }
+    *sink = olds;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (atomicAdd(p.counter, 1u) == gridDim.x - 1) {
+        for (int r = 0; r < p.m; ++r) {
+            const unsigned long long k = atomicExch(p.head_keys + r * kKeyStride, 0ull);
+            p.ids[r] = argmax_key_index(k);
+        }
+        atomicExch(p.counter, 0u);
+    }
 }
 
 // The work units one worker (a wave, or a whole block when S > 1) goes
@@ -553,26 +580,291 @@ __global__ void __launch_bounds__(head_waves(EPI, M) * 64) k_gemv(const GemvPara
         }
         __syncthreads();
         __shared__ unsigned long long sink;
-        if (threadIdx.x == 0) {
-            // returning atomics: their results are consumed below, so each
-            // update has been performed before this block is counted
-            unsigned long long olds = 0;
-            for (int mi = 0; mi < p.m; ++mi) {
-                float bv = bv_s[0][mi];
-                int bi = bi_s[0][mi];
-                for (int j = 1; j < Q; ++j) argmax_merge(bv, bi, bv_s[j][mi], bi_s[j][mi]);
-                if (bi != INT_MAX) olds ^= atomicMax(p.head_keys + mi, argmax_key(bv, bi));
-            }
-            sink = olds;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            if (atomicAdd(p.counter, 1u) == gridDim.x - 1) {
-                for (int mi = 0; mi < p.m; ++mi) {
-                    const unsigned long long k = atomicExch(p.head_keys + mi, 0ull);
-                    p.ids[mi] = argmax_key_index(k);
-                }
-                atomicExch(p.counter, 0u);
+        if (threadIdx.x == 0) grid_argmax(p, Q, bv_s, bi_s, &sink);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core GEMV: 4-bit weights, K = 2048, up to four activation rows.
+//
+// Work unit: 16 weight rows, one wave.  Lane l loads row l%16 and, per load
+// t, the 16 bytes of group 4t + l/16, so a load covers 16 rows x 64 bytes.
+// One v_permlane32_swap per word pair turns the lane quarters' groups into
+// the A operands of two v_mfma_i32_16x16x64_i8 per load, each over a group
+// pair: quarters 0 and 2 then hold the pair's first group (words 0-1 and
+// 2-3), quarters 1 and 3 the second.  The B operand (the activations' int8
+// halves, built once per block in LDS) pairs columns 0..7 with the first
+// group and 8..15 with the second and is zero elsewhere; column c of a group
+// is (activation row c/2, hi half if c is even, lo half if odd).  Each
+// group's int32 result is scaled by its row's scale and accumulated in f32;
+// the bias sums (b times the group's sum of quantized activations) are f32
+// MFMAs (16x16x4) fed with the biases as loaded.  Two DPP adds then fold the
+// group halves and the hi/lo columns, and the result is
+// xs * (256 hi + lo + bias sums), the same quantity as in the vector path.
+// ---------------------------------------------------------------------------
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+constexpr int kMmaRows = 16;
+constexpr int kMmaCols = 16;
+constexpr int kStage = 20;  // floats per group in a wave's scale stage (16 rows, 16-byte aligned)
+
+__device__ __forceinline__ void perm32_swap(unsigned& a, unsigned& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+
+template <int PRO>
+__device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, int wid, int nw, int lane,
+                                          u32x4 (*bq)[2][kWave], float (*tx)[kMmaCols], float* xs_lds) {
+    const int g = lane, kk = g * kGroup;
+    for (int mi = wid; mi < 4; mi += nw) {
+        float xv[32], gv[32];
+        load_x_row<PRO>(p, v, mi, kk, true, xv, gv, true);
+        if constexpr (PRO != PRO_PLAIN) {
+            const int seg = (PRO == PRO_CONCAT && kk >= p.H) ? 1 : 0;
+            const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) ss = fmaf(xv[i], xv[i], ss);
+            const float s0 = wave_sum(seg == 0 ? ss : 0.0f);
+            const float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
+            const float inv = rsqrtf((seg ? s1 : s0) / (float)nfeat + p.eps);
+            if (mi < p.m) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xv[i] = xv[i] * inv * gv[i];
+                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0)
+                    store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
             }
         }
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
+        am = wave_max(am);
+        const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
+        const float x_s = am / kQMax;
+        XFrag f;
+        quantize_group<FMT_Q4>(xv, inv_q, x_s, f);
+        const int t = g >> 2, pp = (g >> 1) & 1, par = g & 1;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int wp = 0; wp < 2; ++wp) {
+            const int h = 2 * wp + par;
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const int* X = hl ? f.lo : f.hi;
+                const int ct = 2 * mi + hl;
+                const u32x4 val = {(unsigned)X[4 * wp], (unsigned)X[4 * wp + 1], (unsigned)X[4 * wp + 2],
+                                   (unsigned)X[4 * wp + 3]};
+                bq[t][pp][ct + 8 * par + 16 * h] = val;
+                bq[t][pp][ct + 8 * (1 - par) + 16 * h] = zero;
+            }
+        }
+        tx[g][2 * mi] = f.sxd;
+        tx[g][2 * mi + 1] = 0.0f;
+        tx[g][8 + 2 * mi] = 0.0f;
+        tx[g][9 + 2 * mi] = 0.0f;
+        if (lane == 0) xs_lds[mi] = x_s;
+    }
+    __syncthreads();
+}
+
+template <int PRO, int EPI>
+__global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p) {
+    __shared__ u32x4 bq[16][2][kWave];              // 32 KB: B operands (load t, group pair)
+    __shared__ float tx[64][kMmaCols];              // 4 KB: sum of x^ per (group, column 2*row), else 0
+    __shared__ float stage[kMaxWaves][64 * kStage];  // 40 KB: each wave's scales, [group][row]
+    __shared__ float xs_lds[4];
+    __shared__ int claim_ctr;
+
+    if (p.zero_words && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
+    View v;
+    resolve_view(p, v);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nw = blockDim.x / kWave;
+    const int NU = (v.N + kMmaRows - 1) / kMmaRows;
+
+    auto claim = [&]() {
+        int r = 0;
+        if (lane == 0) r = atomicAdd(&claim_ctr, 1);
+        return r;
+    };
+    if (p.balance) {
+        if (threadIdx.x == 0) claim_ctr = 0;
+        __syncthreads();
+    }
+    TileSeq ts;
+    if (p.balance)
+        ts.init(blockIdx.x, gridDim.x, NU, true, claim);
+    else
+        ts.init(blockIdx.x * nw + wid, gridDim.x * nw, NU, false, claim);
+
+    mma_setup<PRO>(p, v, wid, nw, lane, bq, tx, xs_lds);
+
+    const int j = lane & 15, h = lane >> 4;
+    const int mi_l = (j & 7) >> 1;
+    const bool lo_col = (j & 1) != 0;
+    const float colf = lo_col ? 1.0f : 256.0f;
+    const bool writer = j < 8 && !lo_col && mi_l < p.m;
+    const float xs_l = xs_lds[mi_l];
+    float* st = stage[wid];
+    float best = -INFINITY;
+    int best_i = INT_MAX;
+
+    // this lane's weight row of unit u, picked among up to three matrices
+    auto row_ptrs = [&](int u, const char*& crow, const float*& srow, const float*& brow) {
+        int row = u * kMmaRows + j;
+        row = row < v.N ? row : v.N - 1;
+        const int64_t in1 = row >= v.n0, in2 = row >= v.n0 + v.n1;
+        const int lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
+        crow = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
+        srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 + in2 * v.ds2) +
+               (int64_t)lr * v.G + 4 * h;
+        brow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 + in2 * v.db2) +
+               (int64_t)lr * v.G + 4 * h;
+    };
+    u32x4 cw[16];
+    v4f_t sv[4], bv[4];
+    auto load_codes = [&](const char* crow, int t) {
+        cw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 64 * t));
+    };
+    auto load_sb = [&](const float* srow, const float* brow) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sv[t] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(srow + 16 * t));
+            bv[t] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(brow + 16 * t));
+        }
+    };
+
+    // Software pipeline: the next unit's weights are requested register by
+    // register as soon as the current unit has consumed it.
+    int u = ts.next(claim);
+    if (u >= 0) {
+        const char* crow;
+        const float *srow, *brow;
+        row_ptrs(u, crow, srow, brow);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) load_codes(crow, t);
+        load_sb(srow, brow);
+    }
+    while (u >= 0) {
+        // the next unit's rows; past the last unit the requests still go out,
+        // to unit 0 (one small region every wave shares, so they hit in L2),
+        // which keeps the loads unconditional and the registers simple
+        const int nu = ts.next(claim);
+        const char* ncrow;
+        const float *nsrow, *nbrow;
+        row_ptrs(nu >= 0 ? nu : 0, ncrow, nsrow, nbrow);
+
+        // bias sums on the f32 matrix core (two independent accumulators);
+        // the scales go to this wave's stage
+        v4f_t cb4[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) cb4[e] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gg = 16 * t + 4 * h + e;
+                st[gg * kStage + j] = sv[t][e];
+                const float tv = tx[gg][j];
+                cb4[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[t][e], tv, cb4[e & 1], 0, 0, 0);
+            }
+        }
+        load_sb(nsrow, nbrow);
+        __builtin_amdgcn_wave_barrier();
+
+        // integer products, kTB loads (2 kTB MFMAs) at a time
+        constexpr int kTB = 2;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t0 = 0; t0 < 16; t0 += kTB) {
+            v4i_t A[kTB][2];
+#pragma unroll
+            for (int dt = 0; dt < kTB; ++dt) {
+                const int t = t0 + dt;
+                unsigned w0 = cw[t].x, w1 = cw[t].y, w2 = cw[t].z, w3 = cw[t].w;
+                perm32_swap(w0, w2);
+                perm32_swap(w1, w3);
+                const unsigned M4 = 0x0F0F0F0Fu;
+                A[dt][0] = (v4i_t){(int)(w0 & M4), (int)((w0 >> 4) & M4), (int)(w1 & M4), (int)((w1 >> 4) & M4)};
+                A[dt][1] = (v4i_t){(int)(w2 & M4), (int)((w2 >> 4) & M4), (int)(w3 & M4), (int)((w3 >> 4) & M4)};
+            }
+            v4i_t D[kTB][2];
+#pragma unroll
+            for (int dt = 0; dt < kTB; ++dt)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const u32x4 bb = bq[t0 + dt][pp][lane];
+                    const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
+                    const v4i_t zero = {0, 0, 0, 0};
+                    D[dt][pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[dt][pp], B, zero, 0, 0, 0);
+                }
+#pragma unroll
+            for (int dt = 0; dt < kTB; ++dt)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int gg = 4 * (t0 + dt) + 2 * pp + (j >> 3);
+                    const float4 s4 = *reinterpret_cast<const float4*>(&st[gg * kStage + 4 * h]);
+                    acc[0] = fmaf(s4.x, (float)D[dt][pp][0], acc[0]);
+                    acc[1] = fmaf(s4.y, (float)D[dt][pp][1], acc[1]);
+                    acc[2] = fmaf(s4.z, (float)D[dt][pp][2], acc[2]);
+                    acc[3] = fmaf(s4.w, (float)D[dt][pp][3], acc[3]);
+                }
+            // the registers of loads t0 .. t0+kTB-1 are free: request the
+            // next unit's
+#pragma unroll
+            for (int dt = 0; dt < kTB; ++dt) load_codes(ncrow, t0 + dt);
+        }
+        __builtin_amdgcn_wave_barrier();
+        v4f_t cb = cb4[0] + cb4[1];
+        // fold: group halves (lanes j, j^8), then hi and lo (lanes 2i, 2i+1)
+        float res[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x = fmaf(acc[r], colf, cb[r]);
+            x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+            x += dpp_partner<1>(x);
+            res[r] = x * xs_l;
+        }
+        if (writer) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int orow = u * kMmaRows + 4 * h + r;
+                if (orow < v.N) {
+                    const int64_t o = (int64_t)mi_l * v.N + orow;
+                    if constexpr (EPI == EPI_STORE) {
+                        v.y[o] = p.residual ? res[r] + p.residual[o] : res[r];
+                    } else {
+                        if (p.logits) p.logits[o] = res[r];
+                        if (res[r] > best || (res[r] == best && orow < best_i)) {
+                            best = res[r];
+                            best_i = orow;
+                        }
+                    }
+                }
+            }
+        }
+        u = nu;
+    }
+    if constexpr (EPI == EPI_ARGMAX) {
+        __shared__ float bv_s[kMaxWaves][8];
+        __shared__ int bi_s[kMaxWaves][8];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            float bvv = (writer && mi_l == mi) ? best : -INFINITY;
+            int bii = (writer && mi_l == mi) ? best_i : INT_MAX;
+            wave_argmax(bvv, bii);
+            if (lane == 0) {
+                bv_s[wid][mi] = bvv;
+                bi_s[wid][mi] = bii;
+            }
+        }
+        __syncthreads();
+        __shared__ unsigned long long sink;
+        if (threadIdx.x == 0) grid_argmax(p, nw, bv_s, bi_s, &sink);
     }
 }
 
@@ -653,9 +945,39 @@ static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int 
     return hipGetLastError();
 }
 
+// The matrix-core path serves 4-bit GEMVs over exactly one 2048-feature
+// chunk at three or four activation rows (store and argmax epilogues).
+static bool mma_path(int fmt, int epi, int m, const GemvParams& p) {
+    return fmt == FMT_Q4 && (epi == EPI_STORE || epi == EPI_ARGMAX) && m >= 3 && m <= 4 && p.K == kChunk &&
+           !p.slot_expert;
+}
+
+template <int PRO, int EPI>
+static hipError_t launch_mma(const GemvParams& p, hipStream_t st, int& blocks) {
+    const int units = (p.N + kMmaRows - 1) / kMmaRows;
+    int waves = 4;
+    blocks = (units + waves - 1) / waves;
+    if (p.balance) {  // persistent: one 8-wave block per compute unit
+        waves = kMaxWaves;
+        const int need = (units + waves - 1) / waves, cu = device_cu_count();
+        blocks = need < cu ? need : cu;
+    }
+    hipLaunchKernelGGL((k_gemv_mma<PRO, EPI>), dim3(blocks), dim3(64 * waves), 0, st, p);
+    return hipGetLastError();
+}
+
+
 hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
                        hipStream_t st) {
     if (p.slot_expert) return hipErrorInvalidValue;  // slot launches use launch_gemv_slots
+    if (epi == EPI_ARGMAX && sh.grid > kHeadMaxBlocks) return hipErrorInvalidValue;
+    if (mma_path(fmt, epi, m, p)) {
+        int blocks = 0;
+        if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_mma<PRO_PLAIN, EPI_STORE>(p, st, blocks);
+        if (pro == PRO_RMS && epi == EPI_STORE) return launch_mma<PRO_RMS, EPI_STORE>(p, st, blocks);
+        if (pro == PRO_CONCAT && epi == EPI_STORE) return launch_mma<PRO_CONCAT, EPI_STORE>(p, st, blocks);
+        if (pro == PRO_RMS && epi == EPI_ARGMAX) return launch_mma<PRO_RMS, EPI_ARGMAX>(p, st, blocks);
+    }
     if (fmt == FMT_Q4) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_RMS, EPI_STORE>(m, p, sh, 1, st);

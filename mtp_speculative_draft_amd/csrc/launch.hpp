@@ -31,7 +31,7 @@ enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 //  epilogue: EPI_STORE  y[r][n] = v (+ residual[r][n])
 //            EPI_SWIGLU y[r][n] = silu(a)*b (* rowscale[r] when given)
 //            EPI_ARGMAX logits[r][n] = v when logits; the per-row argmax
-//                       goes to ids[m] (see head_keys/counter)
+//                       goes to ids[m] (see head_keys)
 struct GemvParams {
     QMat w[3];
     int nmat;
@@ -51,20 +51,23 @@ struct GemvParams {
     const float* residual;
     const float* rowscale;
     float* logits;
-    // EPI_ARGMAX: per-row 64-bit (value, index) keys merged with atomicMax and
-    // a block arrival counter; both are zero on entry and zero again on exit
-    // (the last block to arrive turns the keys into ids[m] and clears them).
+    // EPI_ARGMAX: per-row 64-bit (value, index) keys merged with atomicMax,
+    // row r's at head_keys[r * kKeyStride] so that each has a 128-byte line of
+    // its own (atomics on one line are performed one after another), and the
+    // block arrival counter on a line of its own; all zero on entry and zero
+    // again on exit (the last block to arrive turns the keys into ids[m] and
+    // clears them).
     unsigned long long* head_keys;
     unsigned* counter;
+    int* ids;
+    // Any epilogue: when set, block (0, 0) first stores zero into zero_n words
+    // at zero_words (used to clear a later launch's argmax state).
+    unsigned* zero_words;
+    int zero_n;
     // Non-zero (S == 1 only): the waves of a block share its units and claim
     // them at run time from a block-local counter instead of taking a fixed
     // share each.
     int balance;
-    int* ids;
-    // Any epilogue: when set, block (0, 0) first stores zero into zero_n words
-    // here (stream-ordered initialisation of state a later kernel uses).
-    unsigned* zero_words;
-    int zero_n;
     // Expert slots (MoE): when slot_expert is set, blockIdx.y is a slot; slots
     // >= *n_slots exit at once.  Slot j uses expert e = slot_expert[j] of the
     // stacks in w[0..1] (byte stride ex_codes, float stride ex_scales), or the
@@ -87,6 +90,11 @@ __host__ __device__ constexpr int gemv_rows(int M, int P) {
 }
 // Row count of the kernel instantiation that serves m activation rows.
 __host__ __device__ constexpr int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
+// Argmax state: one 128-byte line per row key, then the counter's line.
+constexpr int kKeyStride = 16;        // u64 between row keys
+constexpr int kHeadRows = 8;          // activation rows at most (the C ABI's MTP_MAX_ROWS)
+constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap
+constexpr int kHeadStateBytes = (kHeadRows + 1) * kKeyStride * 8;
 // Waves per block: 4, except the lm_head's persistent blocks for up to four
 // activation rows, which take a whole compute unit each (8 waves).
 constexpr int kMaxWaves = 8;

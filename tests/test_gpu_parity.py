@@ -87,7 +87,10 @@ def test_qgemv_config0_full():
 
 @pytest.mark.parametrize("n,k,m,res", [(1000, 96, 3, True), (333, 4096, 4, False), (517, 6144, 2, True),
                                        (64, 32, 8, False), (300, 8192, 5, False), (2049, 2048, 7, True),
-                                       (4099, 2048, 1, False), (129, 1024, 6, True)])
+                                       (4099, 2048, 1, False), (129, 1024, 6, True),
+                                       # matrix-core path: 2048 features, 3-4 rows, ragged 16-row units
+                                       (1000, 2048, 4, True), (517, 2048, 3, False), (16, 2048, 4, False),
+                                       (15, 2048, 3, True), (4111, 2048, 4, False)])
 def test_qgemv_shapes(n, k, m, res):
     _say(f"qgemv n={n} k={k} m={m} residual={res}")
     g = synth.rng(102, n, k, m)
@@ -185,15 +188,15 @@ def test_lmhead_argmax_config2_planted(m, planted_config2):
 
 
 def test_lmhead_argmax_reuses_one_workspace(planted_config2):
-    """The fused cross-block argmax leaves its keys and counters at zero: five
+    """The fused cross-block argmax leaves its keys and counter at zero: five
     calls of mixed m on one zero-filled workspace all return the planted ids,
-    and the state block at the start of the workspace reads zero afterwards."""
+    and the state at the start of the workspace reads zero afterwards."""
     x, gf, planted, targets, normed, logits, dlm = planted_config2
     ws = torch.zeros(mtp.mtp_lmhead_workspace_size(planted.n, 4), dtype=torch.uint8, device=DEV)
     for m in (1, 4, 2, 4, 1):
         ids = _np(mtp.mtp_lmhead_argmax(_t(x[:m]), _t(gf), 1e-6, dlm, ws=ws))
         assert ids.tolist() == targets[:m].tolist(), m
-    assert int(ws[:256].count_nonzero().item()) == 0
+    assert int(ws[:1152].count_nonzero().item()) == 0
 
 
 @pytest.mark.parametrize("m", [1, 4])
@@ -415,11 +418,13 @@ def _check_step(S, label, ref):
     assert v[0].tolist() == ver[0].tolist(), "verify ids"
     _close(v[1], ver[1], "verify hidden")
     _close(v[2], ver[2], "verify logits")
-    # batched == sequential on the device, bit for bit: a row's arithmetic
-    # (fragments, reduction tree, attention chunks) does not depend on m
+    # batched against sequential on the device: the same ids, and the same
+    # rows up to summation order (GEMVs over one 2048-feature chunk at three or
+    # four rows run on the matrix cores, which sum the groups in another order
+    # than the vector path; everything else gives bitwise equal rows)
     assert v[0][:3].tolist() == chain[0].tolist()
-    assert np.array_equal(v[1][:3].view(np.uint32), chain[1].view(np.uint32)), "verify rows vs chain (gpu)"
-    assert np.array_equal(v[2][:3].view(np.uint32), chain[2].view(np.uint32)), "verify logits vs chain (gpu)"
+    _close(v[1][:3], chain[1].astype(np.float64), "verify rows vs chain (gpu)", tol=1e-4)
+    _close(v[2][:3], chain[2].astype(np.float64), "verify logits vs chain (gpu)", tol=1e-4)
     L0 = S.cache_len
     _close(gk[:, L0:L0 + 4], kv[0][:, L0:L0 + 4], "cache k rows")
     _close(gv[:, L0:L0 + 4], kv[1][:, L0:L0 + 4], "cache v rows")
