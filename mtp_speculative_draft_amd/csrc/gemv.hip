@@ -684,7 +684,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nw = blockDim.x / kWave;
-    const int NU = (v.N + kMmaRows - 1) / kMmaRows;
+    const int NU = (v.N + (EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows) - 1) / (EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows);
 
     auto claim = [&]() {
         int r = 0;
@@ -701,24 +701,34 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     else
         ts.init(blockIdx.x * nw + wid, gridDim.x * nw, NU, false, claim);
 
-    mma_setup<PRO>(p, v, wid, nw, lane, bq, tx, xs_lds);
-
     const int j = lane & 15, h = lane >> 4;
     const int mi_l = (j & 7) >> 1;
     const bool lo_col = (j & 1) != 0;
     const float colf = lo_col ? 1.0f : 256.0f;
     const bool writer = j < 8 && !lo_col && mi_l < p.m;
-    const float xs_l = xs_lds[mi_l];
     float* st = stage[wid];
     float best = -INFINITY;
     int best_i = INT_MAX;
 
-    // this lane's weight row of unit u, picked among up to three matrices
+
+    // Unit u's rows: 16 rows among up to three concatenated matrices, or for
+    // the SwiGLU pair 8 output rows, gate rows in lanes j < 8 and the same
+    // up rows in lanes j >= 8.
+    constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
     auto row_ptrs = [&](int u, const char*& crow, const float*& srow, const float*& brow) {
-        int row = u * kMmaRows + j;
+        int row = u * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
         row = row < v.N ? row : v.N - 1;
-        const int64_t in1 = row >= v.n0, in2 = row >= v.n0 + v.n1;
-        const int lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
+        int64_t in1, in2;
+        int lr;
+        if constexpr (EPI == EPI_SWIGLU) {
+            in1 = j >> 3;  // 0: gate (w[0]), 1: up (w[1])
+            in2 = 0;
+            lr = row;
+        } else {
+            in1 = row >= v.n0;
+            in2 = row >= v.n0 + v.n1;
+            lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
+        }
         crow = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
         srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 + in2 * v.ds2) +
                (int64_t)lr * v.G + 4 * h;
@@ -738,8 +748,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         }
     };
 
-    // Software pipeline: the next unit's weights are requested register by
-    // register as soon as the current unit has consumed it.
+    // Software pipeline: the first unit's weights are requested before the
+    // activation setup, and the next unit's register by register as soon as
+    // the current unit has consumed it.
     int u = ts.next(claim);
     if (u >= 0) {
         const char* crow;
@@ -749,6 +760,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         for (int t = 0; t < 16; ++t) load_codes(crow, t);
         load_sb(srow, brow);
     }
+    mma_setup<PRO>(p, v, wid, nw, lane, bq, tx, xs_lds);
+    const float xs_l = xs_lds[mi_l];
     while (u >= 0) {
         // the next unit's rows; past the last unit the requests still go out,
         // to unit 0 (one small region every wave shares, so they hit in L2),
@@ -829,7 +842,21 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
             x += dpp_partner<1>(x);
             res[r] = x * xs_l;
         }
-        if (writer) {
+        if constexpr (EPI == EPI_SWIGLU) {
+            // lanes of quarters 0-1 hold gate rows 4h + r, quarters 2-3 the
+            // matching up rows: bring the up values over and combine
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float lo, hi;
+                swap_halves<32>(res[r], res[r], lo, hi);
+                const int orow = u * kOutRows + 4 * h + r;
+                if (writer && h < 2 && orow < v.N) {
+                    float z = silu(res[r]) * hi;
+                    if (v.rowscale) z *= v.rowscale[mi_l];
+                    v.y[(int64_t)mi_l * v.N + orow] = z;
+                }
+            }
+        } else if (writer) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int orow = u * kMmaRows + 4 * h + r;
@@ -946,15 +973,15 @@ static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int 
 }
 
 // The matrix-core path serves 4-bit GEMVs over exactly one 2048-feature
-// chunk at three or four activation rows (store and argmax epilogues).
+// chunk at three or four activation rows.
 static bool mma_path(int fmt, int epi, int m, const GemvParams& p) {
-    return fmt == FMT_Q4 && (epi == EPI_STORE || epi == EPI_ARGMAX) && m >= 3 && m <= 4 && p.K == kChunk &&
-           !p.slot_expert;
+    return fmt == FMT_Q4 && m >= 3 && m <= 4 && p.K == kChunk && !p.slot_expert;
 }
 
 template <int PRO, int EPI>
 static hipError_t launch_mma(const GemvParams& p, hipStream_t st, int& blocks) {
-    const int units = (p.N + kMmaRows - 1) / kMmaRows;
+    const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
+    const int units = (p.N + rows - 1) / rows;
     int waves = 4;
     blocks = (units + waves - 1) / waves;
     if (p.balance) {  // persistent: one 8-wave block per compute unit
@@ -977,6 +1004,8 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_mma<PRO_RMS, EPI_STORE>(p, st, blocks);
         if (pro == PRO_CONCAT && epi == EPI_STORE) return launch_mma<PRO_CONCAT, EPI_STORE>(p, st, blocks);
         if (pro == PRO_RMS && epi == EPI_ARGMAX) return launch_mma<PRO_RMS, EPI_ARGMAX>(p, st, blocks);
+        if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_mma<PRO_PLAIN, EPI_SWIGLU>(p, st, blocks);
+        if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_mma<PRO_RMS, EPI_SWIGLU>(p, st, blocks);
     }
     if (fmt == FMT_Q4) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);

@@ -294,7 +294,9 @@ def test_attn_decode_rejects_overflow_without_writing():
 # FFN
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("H,inter,m,norm,res", [(256, 320, 3, True, True), (96, 64, 1, False, False),
-                                                (2048, 6144, 1, True, True), (2048, 6144, 4, True, True)])
+                                                (2048, 6144, 1, True, True), (2048, 6144, 4, True, True),
+                                                # matrix-core gate/up: units of 8 output rows
+                                                (2048, 1056, 3, False, True), (2048, 544, 4, True, False)])
 def test_ffn_dense(H, inter, m, norm, res):
     _say(f"ffn_dense H={H} I={inter} m={m}")
     g = synth.rng(111, H, inter, m)
