@@ -155,7 +155,7 @@ hipError_t run_gemv(int fmt, int pro, int epi, int m, GemvParams& p, int max_blo
     p.m = m;
     p.G = p.K / MTP_GROUP;
     p.S = (p.G + 63) / 64;
-    const GemvShape sh = gemv_shape(fmt, epi, m, p.N, p.K, max_blocks);
+    const GemvShape sh = gemv_shape(fmt, epi, m, p.N, p.K, max_blocks, block_waves(fmt, epi, inst_m(m)));
     return launch_gemv(fmt, pro, epi, m, p, sh, st);
 }
 
@@ -182,7 +182,7 @@ hipError_t run_head(const float* hidden, const float* gamma, float eps, const mt
     // persistent: one block of 8 waves per compute unit (two of 4 for more
     // than four rows), its waves sharing the block's rows at run time
     p.balance = 1;
-    const int waves = head_waves(EPI_ARGMAX, inst_m(m));
+    const int waves = block_waves(FMT_Q4, EPI_ARGMAX, inst_m(m));
     int maxb = device_cu_count() * (kMaxWaves / waves);
     if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
     const GemvShape sh = gemv_shape(FMT_Q4, EPI_ARGMAX, m, p.N, p.K, maxb, waves);

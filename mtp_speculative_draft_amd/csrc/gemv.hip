@@ -187,7 +187,7 @@ template <int FMT, int M, int PRO>
 __device__ __forceinline__ void shared_rows(const GemvParams& p, const View& v, int lane, int S, int Q, int s,
                                             int q, int kk, bool active, unsigned* xq, float* xsq, float (*nq)[2],
                                             XFrag (&xf)[M], float (&xs)[M]) {
-    constexpr int JB = 2;
+    constexpr int JB = M >= 4 ? 4 : 2;  // rows whose loads are in flight together
     const int per = (M + Q - 1) / Q;  // rows per wave, the same in every wave
     float gv[32];
     if constexpr (PRO != PRO_PLAIN) {
@@ -397,11 +397,11 @@ struct TileSeq {
 };
 
 template <int FMT, int M, int PRO, int EPI>
-__global__ void __launch_bounds__(head_waves(EPI, M) * 64) k_gemv(const GemvParams p) {
+__global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const GemvParams p) {
     constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int R = gemv_rows(M, P);
     constexpr int V = R * M * P;
-    constexpr int kWaves = head_waves(EPI, M);  // waves per block, at most
+    constexpr int kWaves = block_waves(FMT, EPI, M);  // waves per block, at most
     __shared__ float red[kWaves][kWave * 2];
     __shared__ float nred[kWaves][2];
     __shared__ int claim_ctr;

@@ -85,8 +85,10 @@ struct GemvParams {
 // (P = 2 for the SwiGLU pair), at most kGemvVals, and at most kGemvRows rows.
 constexpr int kGemvRows = 8;
 constexpr int kGemvVals = 32;
+// One activation row with a single matrix takes 4 rows per wave: for the
+// small projections that doubles the blocks in flight, which shortens them.
 __host__ __device__ constexpr int gemv_rows(int M, int P) {
-    return (kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows;
+    return (M == 1 && P == 1) ? 4 : ((kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows);
 }
 // Row count of the kernel instantiation that serves m activation rows.
 __host__ __device__ constexpr int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
@@ -95,10 +97,14 @@ constexpr int kKeyStride = 16;        // u64 between row keys
 constexpr int kHeadRows = 8;          // activation rows at most (the C ABI's MTP_MAX_ROWS)
 constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap
 constexpr int kHeadStateBytes = (kHeadRows + 1) * kKeyStride * 8;
-// Waves per block: 4, except the lm_head's persistent blocks for up to four
-// activation rows, which take a whole compute unit each (8 waves).
 constexpr int kMaxWaves = 8;
-__host__ __device__ constexpr int head_waves(int epi, int m) { return epi == EPI_ARGMAX && m <= 4 ? kMaxWaves : 4; }
+// Waves per block.  4-bit GEMVs at two or four rows and the lm_head up to
+// four rows use 8: a block's activation setup (one (row, chunk) fragment per
+// wave) then spreads over twice the waves, and the lm_head's persistent
+// blocks take a whole compute unit each.  Everything else uses 4.
+__host__ __device__ constexpr int block_waves(int fmt, int epi, int m) {
+    return (fmt == FMT_Q4 && ((epi == EPI_ARGMAX && m <= 4) || m == 2 || m == 4)) ? kMaxWaves : 4;
+}
 
 struct GemvShape {
     int grid, block, Q, R;
