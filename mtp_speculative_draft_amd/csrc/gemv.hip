@@ -895,6 +895,225 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core GEMV with the K range split over a block's four waves, for the
+// projections that are not persistent: one block per unit (16 weight rows,
+// or 8 output rows of the SwiGLU pair), K = 2048 S with S <= 3.  A block per
+// unit puts several times more compute units to work than a wave per unit,
+// and each wave's share (4S loads, a quarter of the groups) is short.  The
+// activation setup gives wave w activation row w over all S chunks, so the
+// norms need no cross-wave sums; the four waves' partial sums meet in LDS.
+// Operand layout and arithmetic are those of k_gemv_mma; the activation
+// scale of each chunk is applied when a wave's loads cross into the next
+// chunk (and folded into the bias factors in LDS).
+// ---------------------------------------------------------------------------
+template <int PRO, int S>
+__device__ __forceinline__ void mma_sk_setup(const GemvParams& p, const View& v, int wid, int lane,
+                                             u32x4 (*bq)[2][kWave], float (*tx)[kMmaCols], float (*xs_lds)[4]) {
+    const int mi = wid;  // wave w quantizes activation row w
+    float xv[S][32], gv[S][32];
+#pragma unroll
+    for (int c = 0; c < S; ++c) load_x_row<PRO>(p, v, mi, (64 * c + lane) * kGroup, true, xv[c], gv[c], true);
+    if constexpr (PRO != PRO_PLAIN) {
+        float ss0 = 0.0f, ss1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) ss = fmaf(xv[c][i], xv[c][i], ss);
+            if (PRO == PRO_CONCAT && (64 * c + lane) * kGroup >= p.H)
+                ss1 += ss;
+            else
+                ss0 += ss;
+        }
+        const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
+        const float inv0 = rsqrtf(wave_sum(ss0) / (float)nfeat + p.eps);
+        const float inv1 = PRO == PRO_CONCAT ? rsqrtf(wave_sum(ss1) / (float)nfeat + p.eps) : inv0;
+        if (mi < p.m) {
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                const int kk = (64 * c + lane) * kGroup;
+                const float iv = (PRO == PRO_CONCAT && kk >= p.H) ? inv1 : inv0;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xv[c][i] = xv[c][i] * iv * gv[c][i];
+                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0)
+                    store32(p.normed_out + (int64_t)mi * v.K + kk, xv[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        const int g = lane;
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[c][i]));
+        am = wave_max(am);
+        const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
+        const float x_s = am / kQMax;
+        XFrag f;
+        quantize_group<FMT_Q4>(xv[c], inv_q, x_s, f);
+        const int t = 16 * c + (g >> 2), pp = (g >> 1) & 1, par = g & 1;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int wp = 0; wp < 2; ++wp) {
+            const int h = 2 * wp + par;
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const int* X = hl ? f.lo : f.hi;
+                const int ct = 2 * mi + hl;
+                const u32x4 val = {(unsigned)X[4 * wp], (unsigned)X[4 * wp + 1], (unsigned)X[4 * wp + 2],
+                                   (unsigned)X[4 * wp + 3]};
+                bq[t][pp][ct + 8 * par + 16 * h] = val;
+                bq[t][pp][ct + 8 * (1 - par) + 16 * h] = zero;
+            }
+        }
+        const int G = 64 * c + g;
+        tx[G][2 * mi] = f.sxd * x_s;  // the bias factor already carries the chunk's activation scale
+        tx[G][2 * mi + 1] = 0.0f;
+        tx[G][8 + 2 * mi] = 0.0f;
+        tx[G][9 + 2 * mi] = 0.0f;
+        if (lane == 0) xs_lds[c][mi] = x_s;
+    }
+    __syncthreads();
+}
+
+template <int PRO, int EPI, int S>
+__global__ void __launch_bounds__(256) k_gemv_mma_sk(const GemvParams p) {
+    constexpr int T = 16 * S;   // loads (4 groups x 16 rows each) over K
+    constexpr int TW = T / 4;   // loads per wave
+    constexpr int GW = 4 * TW;  // groups per wave
+    __shared__ u32x4 bq[T][2][kWave];           // B operands, 32 KB per chunk
+    __shared__ float tx[64 * S][kMmaCols];      // bias factors x xs, 4 KB per chunk
+    __shared__ float stage[4][GW * kStage];     // each wave's scales, [group][row]
+    __shared__ float xs_lds[S][4];
+    __shared__ float red[4][4][kWave];          // the waves' partial sums
+
+    if (p.zero_words && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
+    View v;
+    resolve_view(p, v);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int j = lane & 15, h = lane >> 4;
+    const int mi_l = (j & 7) >> 1;
+    const bool lo_col = (j & 1) != 0;
+    const float colf = lo_col ? 1.0f : 256.0f;
+    constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
+    const int u = blockIdx.x;
+
+    // this lane's weight row (among up to three matrices, or gate/up)
+    int row = u * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
+    row = row < v.N ? row : v.N - 1;
+    int64_t in1, in2;
+    int lr;
+    if constexpr (EPI == EPI_SWIGLU) {
+        in1 = j >> 3;
+        in2 = 0;
+        lr = row;
+    } else {
+        in1 = row >= v.n0;
+        in2 = row >= v.n0 + v.n1;
+        lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
+    }
+    const int t0 = wid * TW, g0 = wid * GW;
+    const char* crow = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
+    const float* srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 +
+                                                       in2 * v.ds2) + (int64_t)lr * v.G + g0 + 4 * h;
+    const float* brow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 +
+                                                       in2 * v.db2) + (int64_t)lr * v.G + g0 + 4 * h;
+    // this wave's weights are requested before the activation setup
+    u32x4 cw[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i)));
+    v4f_t sv[S], bv[S];
+#pragma unroll
+    for (int L = 0; L < S; ++L) {
+        sv[L] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(srow + 16 * L));
+        bv[L] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(brow + 16 * L));
+    }
+    mma_sk_setup<PRO, S>(p, v, wid, lane, bq, tx, xs_lds);
+
+    float* st = stage[wid];
+    v4f_t cb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int L = 0; L < S; ++L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int gl = 16 * L + 4 * h + e;  // group within the wave's share
+            st[gl * kStage + j] = sv[L][e];
+            cb = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[L][e], tx[g0 + gl][j], cb, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int t = t0 + i;
+        unsigned w0 = cw[i].x, w1 = cw[i].y, w2 = cw[i].z, w3 = cw[i].w;
+        perm32_swap(w0, w2);
+        perm32_swap(w1, w3);
+        const unsigned M4 = 0x0F0F0F0Fu;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const unsigned a = pp ? w2 : w0, b = pp ? w3 : w1;
+            const v4i_t A = {(int)(a & M4), (int)((a >> 4) & M4), (int)(b & M4), (int)((b >> 4) & M4)};
+            const u32x4 bb = bq[t][pp][lane];
+            const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
+            const v4i_t zero = {0, 0, 0, 0};
+            const v4i_t D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+            const float4 s4 = *reinterpret_cast<const float4*>(&st[(4 * i + 2 * pp + (j >> 3)) * kStage + 4 * h]);
+            acc[0] = fmaf(s4.x, (float)D[0], acc[0]);
+            acc[1] = fmaf(s4.y, (float)D[1], acc[1]);
+            acc[2] = fmaf(s4.z, (float)D[2], acc[2]);
+            acc[3] = fmaf(s4.w, (float)D[3], acc[3]);
+        }
+        if (((t + 1) & 15) == 0 || i == TW - 1) {  // end of a chunk or of the share: apply its scale
+            const float xs_c = xs_lds[t >> 4][mi_l];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                tot[r] = fmaf(acc[r], xs_c, tot[r]);
+                acc[r] = 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wid][r][lane] = fmaf(tot[r], colf, cb[r]);
+    __syncthreads();
+    if (wid != 0) return;
+    float res[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
+        x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+        x += dpp_partner<1>(x);
+        res[r] = x;
+    }
+    const bool writer = j < 8 && !lo_col && mi_l < p.m;
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float lo, hi;
+            swap_halves<32>(res[r], res[r], lo, hi);
+            const int orow = u * kOutRows + 4 * h + r;
+            if (writer && h < 2 && orow < v.N) {
+                float z = silu(res[r]) * hi;
+                if (v.rowscale) z *= v.rowscale[mi_l];
+                v.y[(int64_t)mi_l * v.N + orow] = z;
+            }
+        }
+    } else if (writer) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int orow = u * kMmaRows + 4 * h + r;
+            if (orow < v.N) {
+                const int64_t o = (int64_t)mi_l * v.N + orow;
+                v.y[o] = p.residual ? res[r] + p.residual[o] : res[r];
+            }
+        }
+    }
+}
+
 // Dequantize through the GEMV fragment path (load_frag + nibble unpack): one
 // thread per (row, group).
 template <int FMT>
@@ -978,6 +1197,25 @@ static bool mma_path(int fmt, int epi, int m, const GemvParams& p) {
     return fmt == FMT_Q4 && m >= 3 && m <= 4 && p.K == kChunk && !p.slot_expert;
 }
 
+// Store and SwiGLU GEMVs at three or four rows over 1-3 chunks that are not
+// persistent take the split-K matrix-core kernel, a block per unit.
+static bool mma_sk_path(int fmt, int epi, int m, const GemvParams& p) {
+    return fmt == FMT_Q4 && (epi == EPI_STORE || epi == EPI_SWIGLU) && m >= 3 && m <= 4 && !p.balance &&
+           !p.slot_expert && p.nmat <= 3 && (p.K == kChunk || p.K == 2 * kChunk || p.K == 3 * kChunk);
+}
+
+template <int PRO, int EPI>
+static hipError_t launch_mma_sk(const GemvParams& p, hipStream_t st) {
+    const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
+    const dim3 grid((p.N + rows - 1) / rows), block(4 * kWave);
+    switch (p.K / kChunk) {
+        case 1: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2>), grid, block, 0, st, p); break;
+        default: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 3>), grid, block, 0, st, p); break;
+    }
+    return hipGetLastError();
+}
+
 template <int PRO, int EPI>
 static hipError_t launch_mma(const GemvParams& p, hipStream_t st, int& blocks) {
     const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
@@ -998,6 +1236,13 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
                        hipStream_t st) {
     if (p.slot_expert) return hipErrorInvalidValue;  // slot launches use launch_gemv_slots
     if (epi == EPI_ARGMAX && sh.grid > kHeadMaxBlocks) return hipErrorInvalidValue;
+    if (mma_sk_path(fmt, epi, m, p)) {
+        if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_mma_sk<PRO_PLAIN, EPI_STORE>(p, st);
+        if (pro == PRO_RMS && epi == EPI_STORE) return launch_mma_sk<PRO_RMS, EPI_STORE>(p, st);
+        if (pro == PRO_CONCAT && epi == EPI_STORE) return launch_mma_sk<PRO_CONCAT, EPI_STORE>(p, st);
+        if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_mma_sk<PRO_PLAIN, EPI_SWIGLU>(p, st);
+        if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_mma_sk<PRO_RMS, EPI_SWIGLU>(p, st);
+    }
     if (mma_path(fmt, epi, m, p)) {
         int blocks = 0;
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_mma<PRO_PLAIN, EPI_STORE>(p, st, blocks);

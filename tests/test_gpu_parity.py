@@ -90,7 +90,9 @@ def test_qgemv_config0_full():
                                        (4099, 2048, 1, False), (129, 1024, 6, True),
                                        # matrix-core path: 2048 features, 3-4 rows, ragged 16-row units
                                        (1000, 2048, 4, True), (517, 2048, 3, False), (16, 2048, 4, False),
-                                       (15, 2048, 3, True), (4111, 2048, 4, False)])
+                                       (15, 2048, 3, True), (4111, 2048, 4, False),
+                                       # matrix-core path over 2 and 3 chunks
+                                       (517, 6144, 3, True), (70, 6144, 4, False), (31, 4096, 3, True)])
 def test_qgemv_shapes(n, k, m, res):
     _say(f"qgemv n={n} k={k} m={m} residual={res}")
     g = synth.rng(102, n, k, m)
@@ -149,10 +151,12 @@ def test_norm_concat_proj_small_ragged():
     _close(got, oracle.norm_concat_proj(e, h, ge, gh, 1e-6, w), "u")
 
 
-def test_norm_concat_proj_large_hidden():
-    """H = 3072: the e/h boundary falls inside the second 2048-feature chunk."""
-    g = synth.rng(105)
-    H, m = 3072, 2
+@pytest.mark.parametrize("H,m", [(3072, 2), (3072, 3), (1024, 4)])
+def test_norm_concat_proj_boundary_inside_chunk(H, m):
+    """H = 3072: the e/h boundary falls inside the second 2048-feature chunk;
+    H = 1024: inside the only one."""
+    _say(f"norm_concat_proj H={H} m={m}")
+    g = synth.rng(105, H, m)
     e, h = synth.normal(g, (m, H)), synth.normal(g, (m, H))
     ge, gh = synth.gamma(g, H), synth.gamma(g, H)
     w = synth.q4_weight(g, 257, 2 * H)
@@ -296,7 +300,9 @@ def test_attn_decode_rejects_overflow_without_writing():
 @pytest.mark.parametrize("H,inter,m,norm,res", [(256, 320, 3, True, True), (96, 64, 1, False, False),
                                                 (2048, 6144, 1, True, True), (2048, 6144, 4, True, True),
                                                 # matrix-core gate/up: units of 8 output rows
-                                                (2048, 1056, 3, False, True), (2048, 544, 4, True, False)])
+                                                (2048, 1056, 3, False, True), (2048, 544, 4, True, False),
+                                                # matrix-core gate/up over 2 and 3 chunks
+                                                (4096, 544, 3, True, True), (6144, 96, 4, True, False)])
 def test_ffn_dense(H, inter, m, norm, res):
     _say(f"ffn_dense H={H} I={inter} m={m}")
     g = synth.rng(111, H, inter, m)
