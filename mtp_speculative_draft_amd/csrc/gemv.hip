@@ -333,32 +333,37 @@ __device__ __forceinline__ void compute_tile(const TileFrags<FMT, R, P>& tf, con
         }
 }
 
-// Cross-block argmax, run by thread 0 of every block once the block's per-row
-// bests (value, index) of its nw waves are in LDS.  The block's best key per
-// row goes into the row's key with a returning atomicMax (the returns are
-// consumed, so the updates have been performed before the block counts
-// itself), then the block counts itself on the arrival counter; the last
-// block to arrive turns the keys into ids[m] and leaves keys and counter at
-// zero.  Only workgroup-scope fences are used: the device-scope atomics are
-// performed at the memory side, and an agent-scope fence would write back
-// and invalidate the L2 in every block.
+// Cross-block argmax, run by wave 0 of every block once the block's per-row
+// bests (value, index) of its nw waves are in LDS (rows 0 .. MR-1 filled;
+// MR >= m).  Lane r < MR offers the block's best key of row r to the row's
+// key with a returning atomicMax, all rows in one instruction (rows >= m
+// offer key 0, which changes nothing); the returns are consumed (stored to
+// sink) before lane 0 counts the block on the arrival counter, so the updates
+// have been performed by then.  The last block to arrive turns the keys into
+// ids[m] and leaves keys and counter at zero.  A block thus spends two round
+// trips and the last one three.  Only workgroup-scope fences are used: the
+// device-scope atomics are performed at the memory side, and an agent-scope
+// fence would write back and invalidate the L2 in every block.
+template <int MR>
 __device__ __forceinline__ void grid_argmax(const GemvParams& p, int nw, const float (*bv_s)[8],
-                                            const int (*bi_s)[8], unsigned long long* sink) {
-    unsigned long long olds = 0;
-    for (int r = 0; r < p.m; ++r) {
-        float bv = bv_s[0][r];
-        int bi = bi_s[0][r];
-        for (int w = 1; w < nw; ++w) argmax_merge(bv, bi, bv_s[w][r], bi_s[w][r]);
-        if (bi != INT_MAX) olds ^= atomicMax(p.head_keys + r * kKeyStride, argmax_key(bv, bi));
+                                            const int (*bi_s)[8], unsigned long long* sink, int lane) {
+    static_assert(MR <= kHeadRows, "rows");
+    if (lane < MR) {
+        float bv = bv_s[0][lane];
+        int bi = bi_s[0][lane];
+        for (int w = 1; w < nw; ++w) argmax_merge(bv, bi, bv_s[w][lane], bi_s[w][lane]);
+        const unsigned long long key = (lane < p.m && bi != INT_MAX) ? argmax_key(bv, bi) : 0ull;
+        sink[lane] = atomicMax(p.head_keys + lane * kKeyStride, key);
     }
-    *sink = olds;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (atomicAdd(p.counter, 1u) == gridDim.x - 1) {
-        for (int r = 0; r < p.m; ++r) {
-            const unsigned long long k = atomicExch(p.head_keys + r * kKeyStride, 0ull);
-            p.ids[r] = argmax_key_index(k);
-        }
-        atomicExch(p.counter, 0u);
+    unsigned ticket = 0;
+    if (lane == 0) ticket = atomicAdd(p.counter, 1u);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket == gridDim.x - 1) {
+        unsigned long long k = 0ull;
+        if (lane < MR) k = atomicExch(p.head_keys + lane * kKeyStride, 0ull);
+        if (lane < MR && lane < p.m) p.ids[lane] = argmax_key_index(k);
+        if (lane == 0) atomicExch(p.counter, 0u);
     }
 }
 
@@ -579,8 +584,8 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
             }
         }
         __syncthreads();
-        __shared__ unsigned long long sink;
-        if (threadIdx.x == 0) grid_argmax(p, Q, bv_s, bi_s, &sink);
+        __shared__ unsigned long long sink[kHeadRows];
+        if (wid == 0) grid_argmax<M>(p, Q, bv_s, bi_s, sink, lane);
     }
 }
 
@@ -614,67 +619,220 @@ __device__ __forceinline__ void perm32_swap(unsigned& a, unsigned& b) {
     b = r[1];
 }
 
+// 16-bit activation quantization without a float-to-int conversion: adding
+// 1.5 * 2^23 + 128 to the product x * inv (rounded first, as in split16)
+// leaves q + 128 + 0x400000 in the low mantissa bits, rounded to nearest
+// even exactly as split16 rounds, for |q| < 2^22.  Byte 1 of the result is
+// then hi = (q + 128) >> 8 and byte 0 is lo = q - 256 hi with its sign bit
+// flipped, and the bits of several values sum to sum(q) plus a known
+// multiple of kQBiasBits.
+constexpr float kQBias = 12583040.0f;  // 1.5 * 2^23 + 128
+constexpr unsigned kQBiasBits = 0x4B400080u;
+__device__ __forceinline__ unsigned q_bits(float x, float inv) {
+#pragma clang fp contract(off)
+    const float y = x * inv;
+    return __float_as_uint(y + kQBias);
+}
+
+// Row mi's input for the features of segment seg (PRO_CONCAT: 0 = the
+// embedding row, or the token's table row, 1 = the hidden row; otherwise the
+// one input row) and the matching gamma.
 template <int PRO>
-__device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, int wid, int nw, int lane,
-                                          u32x4 (*bq)[2][kWave], float (*tx)[kMmaCols], float* xs_lds) {
-    const int g = lane, kk = g * kGroup;
-    for (int mi = wid; mi < 4; mi += nw) {
-        float xv[32], gv[32];
-        load_x_row<PRO>(p, v, mi, kk, true, xv, gv, true);
-        if constexpr (PRO != PRO_PLAIN) {
-            const int seg = (PRO == PRO_CONCAT && kk >= p.H) ? 1 : 0;
-            const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
-            float ss = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) ss = fmaf(xv[i], xv[i], ss);
-            const float s0 = wave_sum(seg == 0 ? ss : 0.0f);
-            const float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
-            const float inv = rsqrtf((seg ? s1 : s0) / (float)nfeat + p.eps);
-            if (mi < p.m) {
-#pragma unroll
-                for (int i = 0; i < 32; ++i) xv[i] = xv[i] * inv * gv[i];
-                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0)
-                    store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
+__device__ __forceinline__ const float* x_segment(const GemvParams& p, const View& v, int mi, int seg,
+                                                  const float*& gam) {
+    if constexpr (PRO == PRO_CONCAT) {
+        if (seg) {
+            gam = p.g1;
+            return p.x1 + (int64_t)mi * p.H;
+        }
+        gam = p.g0;
+        if (p.tokens) {
+            int tok = p.tokens[mi];
+            if (tok >= 0 || v.x0 == nullptr) {
+                tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
+                return p.table + (int64_t)tok * p.H;
             }
         }
-        float am = 0.0f;
+        return v.x0 + (int64_t)mi * p.H;
+    } else {
+        gam = p.g0;
+        return v.x0 + (int64_t)mi * v.K;
+    }
+}
+
+// Activation setup of the matrix-core kernels, shared by a block's waves:
+// wave w takes activation row w % 4 and, of each of the S chunks, the 1 KB
+// pieces NI (w / 4) .. NI (w / 4) + NI - 1 (lane l holds features
+// 256 i + 4 l .. +3 of piece i), so that every load instruction reads one
+// contiguous kilobyte.  The loads are issued first (mma_load_x), so that
+// they overlap the weight requests that follow, and consumed by mma_quant_x.
+template <int S, int NI>
+struct XPieces {
+    float4 x[S][NI], g[S][NI];
+};
+
+template <int PRO, int S, int NI>
+__device__ __forceinline__ void mma_load_x(const GemvParams& p, const View& v, int mi, int sub, int lane,
+                                           XPieces<S, NI>& xp) {
+    const float *gam0 = nullptr, *gam1 = nullptr, *src0 = nullptr, *src1 = nullptr;
+    const bool live = mi < p.m;
+    if (live) {
+        src0 = x_segment<PRO>(p, v, mi, 0, gam0);
+        if constexpr (PRO == PRO_CONCAT) src1 = x_segment<PRO>(p, v, mi, 1, gam1);
+    }
 #pragma unroll
-        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
-        am = wave_max(am);
-        const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
-        const float x_s = am / kQMax;
-        XFrag f;
-        quantize_group<FMT_Q4>(xv, inv_q, x_s, f);
-        const int t = g >> 2, pp = (g >> 1) & 1, par = g & 1;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int c = 0; c < S; ++c)
 #pragma unroll
-        for (int wp = 0; wp < 2; ++wp) {
-            const int h = 2 * wp + par;
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                const int* X = hl ? f.lo : f.hi;
-                const int ct = 2 * mi + hl;
-                const u32x4 val = {(unsigned)X[4 * wp], (unsigned)X[4 * wp + 1], (unsigned)X[4 * wp + 2],
-                                   (unsigned)X[4 * wp + 3]};
-                bq[t][pp][ct + 8 * par + 16 * h] = val;
-                bq[t][pp][ct + 8 * (1 - par) + 16 * h] = zero;
+        for (int ii = 0; ii < NI; ++ii) {
+            const int f = kChunk * c + 256 * (sub * NI + ii) + 4 * lane;
+            if (live) {
+                const bool sg = PRO == PRO_CONCAT && f >= p.H;
+                const int kl = sg ? f - p.H : f;
+                xp.x[c][ii] = *reinterpret_cast<const float4*>((sg ? src1 : src0) + kl);
+                if constexpr (PRO != PRO_PLAIN)
+                    xp.g[c][ii] = *reinterpret_cast<const float4*>((sg ? gam1 : gam0) + kl);
+            } else {
+                xp.x[c][ii] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
-        tx[g][2 * mi] = f.sxd;
-        tx[g][2 * mi + 1] = 0.0f;
-        tx[g][8 + 2 * mi] = 0.0f;
-        tx[g][9 + 2 * mi] = 0.0f;
-        if (lane == 0) xs_lds[mi] = x_s;
+}
+
+// The rest of the setup: the norms (PRO_RMS, PRO_CONCAT) and the chunk
+// maxima, each combined over the R waves of a row through part, then the
+// 16-bit quantization into the B operands (bq), the bias factors (tx, which
+// carry the chunk's activation scale) and the scales (xs_lds).  The codes'
+// word of 8 features unpacks to the even features, then the odd ones, and
+// lanes 2k and 2k+1 hold that word's first and last four features, so one
+// quad exchange forms each operand word.  Ends with a block barrier.
+template <int PRO, int S, int R>
+__device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, int mi, int sub, int lane,
+                                            XPieces<S, 8 / R>& xp, u32x4 (*bq)[2][kWave],
+                                            float (*tx)[kMmaCols], float (*xs_lds)[4], float (*part)[4][R]) {
+    constexpr int NI = 8 / R;
+    const bool live = mi < p.m;
+    if constexpr (PRO != PRO_PLAIN) {
+        float ss0 = 0.0f, ss1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < S; ++c)
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) {
+                const float4 x = xp.x[c][ii];
+                const float ss = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, x.w * x.w)));
+                if (PRO == PRO_CONCAT && kChunk * c + 256 * (sub * NI + ii) + 4 * lane >= p.H)
+                    ss1 += ss;
+                else
+                    ss0 += ss;
+            }
+        ss0 = wave_sum(ss0);
+        if constexpr (PRO == PRO_CONCAT) ss1 = wave_sum(ss1);
+        if constexpr (R > 1) {
+            if (lane == 0) {
+                part[S][mi][sub] = ss0;
+                part[S + 1][mi][sub] = ss1;
+            }
+            __syncthreads();
+            ss0 = 0.0f;
+            ss1 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                ss0 += part[S][mi][q];
+                ss1 += part[S + 1][mi][q];
+            }
+        }
+        const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
+        const float inv0 = rsqrtf(ss0 / (float)nfeat + p.eps);
+        const float inv1 = PRO == PRO_CONCAT ? rsqrtf(ss1 / (float)nfeat + p.eps) : inv0;
+        if (live) {
+#pragma unroll
+            for (int c = 0; c < S; ++c)
+#pragma unroll
+                for (int ii = 0; ii < NI; ++ii) {
+                    const int f = kChunk * c + 256 * (sub * NI + ii) + 4 * lane;
+                    const float iv = (PRO == PRO_CONCAT && f >= p.H) ? inv1 : inv0;
+                    float4& x = xp.x[c][ii];
+                    const float4 g = xp.g[c][ii];
+                    x = make_float4(x.x * iv * g.x, x.y * iv * g.y, x.z * iv * g.z, x.w * iv * g.w);
+                    if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0)
+                        *reinterpret_cast<float4*>(p.normed_out + (int64_t)mi * v.K + f) = x;
+                }
+        }
+    }
+    float am[S];
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        float a = 0.0f;
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+            const float4 x = xp.x[c][ii];
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+        }
+        am[c] = wave_max(a);
+        if constexpr (R > 1)
+            if (lane == 0) part[c][mi][sub] = am[c];
+    }
+    if constexpr (R > 1) {
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+            float a = part[c][mi][0];
+#pragma unroll
+            for (int q = 1; q < R; ++q) a = fmaxf(a, part[c][mi][q]);
+            am[c] = a;
+        }
+    }
+    const bool odd = lane & 1;
+    const int wp = (lane >> 2) & 1, word = lane & 3;
+    const unsigned sel_h = odd ? 0x01000504u : 0x05040100u;
+    const unsigned sel_l = odd ? 0x03020706u : 0x07060302u;
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        const float inv_q = am[c] > 0.0f ? kQMax / am[c] : 0.0f;
+        const float x_s = am[c] / kQMax;
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+            const float4 x = xp.x[c][ii];
+            const unsigned b0 = q_bits(x.x, inv_q), b1 = q_bits(x.y, inv_q), b2 = q_bits(x.z, inv_q),
+                           b3 = q_bits(x.w, inv_q);
+            unsigned qsum = (b0 + b1) + (b2 + b3);
+            // bytes (hi of 0, hi of 2, lo of 0, lo of 2) and the same of 1, 3;
+            // the even lane keeps the first and gives the second, the odd the reverse
+            const unsigned p02 = __builtin_amdgcn_perm(b2, b0, 0x04000501u);
+            const unsigned p13 = __builtin_amdgcn_perm(b3, b1, 0x04000501u);
+            const unsigned keep = odd ? p13 : p02;
+            const unsigned got = (unsigned)dpp_partner<1>((int)(odd ? p02 : p13));
+            const unsigned hw = __builtin_amdgcn_perm(got, keep, sel_h);
+            const unsigned lw = __builtin_amdgcn_perm(got, keep, sel_l) ^ 0x80808080u;
+            const int gl = 8 * (sub * NI + ii) + (lane >> 3);  // group within the chunk
+            const int t = 16 * c + (gl >> 2), pp = (gl >> 1) & 1, par = gl & 1, hq = 2 * wp + par;
+            unsigned* slot = reinterpret_cast<unsigned*>(&bq[t][pp][0]) + word;
+            slot[4 * (2 * mi + 8 * par + 16 * hq)] = hw;
+            slot[4 * (2 * mi + 1 + 8 * par + 16 * hq)] = lw;
+            slot[4 * (2 * mi + 8 * (1 - par) + 16 * hq)] = 0u;
+            slot[4 * (2 * mi + 1 + 8 * (1 - par) + 16 * hq)] = 0u;
+            qsum += (unsigned)dpp_partner<1>((int)qsum);
+            qsum += (unsigned)dpp_partner<2>((int)qsum);
+            qsum += (unsigned)dpp_partner<4>((int)qsum);  // the group's eight lanes
+            const int qs = (int)(qsum - 32u * kQBiasBits);
+            const int k8 = lane & 7;
+            if (k8 < 4) {
+                // the bias factor carries the chunk's activation scale (the sum is exact)
+                const int col = k8 == 0 ? 2 * mi : (k8 == 1 ? 2 * mi + 1 : 8 + 2 * mi + (k8 - 2));
+                tx[64 * c + gl][col] = k8 == 0 ? (float)qs * x_s : 0.0f;
+            }
+        }
+        if (sub == 0 && lane == 0) xs_lds[c][mi] = x_s;
     }
     __syncthreads();
 }
 
-template <int PRO, int EPI>
+template <int PRO>
 __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p) {
+    constexpr int R = kMaxWaves / 4;  // waves per activation row in the setup
     __shared__ u32x4 bq[16][2][kWave];              // 32 KB: B operands (load t, group pair)
     __shared__ float tx[64][kMmaCols];              // 4 KB: sum of x^ per (group, column 2*row), else 0
     __shared__ float stage[kMaxWaves][64 * kStage];  // 40 KB: each wave's scales, [group][row]
-    __shared__ float xs_lds[4];
+    __shared__ float part[3][4][R];
+    __shared__ float xs_lds[1][4];
     __shared__ int claim_ctr;
 
     if (p.zero_words && blockIdx.x == 0)
@@ -683,23 +841,17 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     resolve_view(p, v);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nw = blockDim.x / kWave;
-    const int NU = (v.N + (EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows) - 1) / (EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows);
+    const int NU = (v.N + kMmaRows - 1) / kMmaRows;
 
     auto claim = [&]() {
         int r = 0;
         if (lane == 0) r = atomicAdd(&claim_ctr, 1);
         return r;
     };
-    if (p.balance) {
-        if (threadIdx.x == 0) claim_ctr = 0;
-        __syncthreads();
-    }
+    if (threadIdx.x == 0) claim_ctr = 0;
+    __syncthreads();
     TileSeq ts;
-    if (p.balance)
-        ts.init(blockIdx.x, gridDim.x, NU, true, claim);
-    else
-        ts.init(blockIdx.x * nw + wid, gridDim.x * nw, NU, false, claim);
+    ts.init(blockIdx.x, gridDim.x, NU, true, claim);
 
     const int j = lane & 15, h = lane >> 4;
     const int mi_l = (j & 7) >> 1;
@@ -711,29 +863,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     int best_i = INT_MAX;
 
 
-    // Unit u's rows: 16 rows among up to three concatenated matrices, or for
-    // the SwiGLU pair 8 output rows, gate rows in lanes j < 8 and the same
-    // up rows in lanes j >= 8.
-    constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
+    // unit u: rows 16 u .. 16 u + 15 of the one matrix
     auto row_ptrs = [&](int u, const char*& crow, const float*& srow, const float*& brow) {
-        int row = u * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
+        int row = u * kMmaRows + j;
         row = row < v.N ? row : v.N - 1;
-        int64_t in1, in2;
-        int lr;
-        if constexpr (EPI == EPI_SWIGLU) {
-            in1 = j >> 3;  // 0: gate (w[0]), 1: up (w[1])
-            in2 = 0;
-            lr = row;
-        } else {
-            in1 = row >= v.n0;
-            in2 = row >= v.n0 + v.n1;
-            lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
-        }
-        crow = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
-        srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 + in2 * v.ds2) +
-               (int64_t)lr * v.G + 4 * h;
-        brow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 + in2 * v.db2) +
-               (int64_t)lr * v.G + 4 * h;
+        crow = static_cast<const char*>(v.c0) + (int64_t)row * (v.K / 2) + 16 * h;
+        srow = v.s0 + (int64_t)row * v.G + 4 * h;
+        brow = v.b0 + (int64_t)row * v.G + 4 * h;
     };
     u32x4 cw[16];
     v4f_t sv[4], bv[4];
@@ -748,20 +884,25 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         }
     };
 
-    // Software pipeline: the first unit's weights are requested before the
-    // activation setup, and the next unit's register by register as soon as
-    // the current unit has consumed it.
+    // Software pipeline: the activations are requested first, then the first
+    // unit's weights, which arrive during the activation setup; the next
+    // unit's weights go out register by register as soon as the current unit
+    // has consumed them.
+    XPieces<1, 8 / R> xp;
+    mma_load_x<PRO, 1, 8 / R>(p, v, wid & 3, wid >> 2, lane, xp);
     int u = ts.next(claim);
-    if (u >= 0) {
+    {
+        // unconditional (unit 0 stands in for none), so that the setup waits
+        // for the activations only and not for these requests as well
         const char* crow;
         const float *srow, *brow;
-        row_ptrs(u, crow, srow, brow);
+        row_ptrs(u >= 0 ? u : 0, crow, srow, brow);
 #pragma unroll
         for (int t = 0; t < 16; ++t) load_codes(crow, t);
         load_sb(srow, brow);
     }
-    mma_setup<PRO>(p, v, wid, nw, lane, bq, tx, xs_lds);
-    const float xs_l = xs_lds[mi_l];
+    mma_quant_x<PRO, 1, R>(p, v, wid & 3, wid >> 2, lane, xp, bq, tx, xs_lds, part);
+    const float colx = colf * xs_lds[0][mi_l];  // integer sums carry the activation scale here
     while (u >= 0) {
         // the next unit's rows; past the last unit the requests still go out,
         // to unit 0 (one small region every wave shares, so they hit in L2),
@@ -837,46 +978,27 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         float res[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float x = fmaf(acc[r], colf, cb[r]);
+            float x = fmaf(acc[r], colx, cb[r]);
             x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
             x += dpp_partner<1>(x);
-            res[r] = x * xs_l;
+            res[r] = x;
         }
-        if constexpr (EPI == EPI_SWIGLU) {
-            // lanes of quarters 0-1 hold gate rows 4h + r, quarters 2-3 the
-            // matching up rows: bring the up values over and combine
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float lo, hi;
-                swap_halves<32>(res[r], res[r], lo, hi);
-                const int orow = u * kOutRows + 4 * h + r;
-                if (writer && h < 2 && orow < v.N) {
-                    float z = silu(res[r]) * hi;
-                    if (v.rowscale) z *= v.rowscale[mi_l];
-                    v.y[(int64_t)mi_l * v.N + orow] = z;
-                }
-            }
-        } else if (writer) {
+        if (writer) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int orow = u * kMmaRows + 4 * h + r;
                 if (orow < v.N) {
-                    const int64_t o = (int64_t)mi_l * v.N + orow;
-                    if constexpr (EPI == EPI_STORE) {
-                        v.y[o] = p.residual ? res[r] + p.residual[o] : res[r];
-                    } else {
-                        if (p.logits) p.logits[o] = res[r];
-                        if (res[r] > best || (res[r] == best && orow < best_i)) {
-                            best = res[r];
-                            best_i = orow;
-                        }
+                    if (p.logits) p.logits[(int64_t)mi_l * v.N + orow] = res[r];
+                    if (res[r] > best || (res[r] == best && orow < best_i)) {
+                        best = res[r];
+                        best_i = orow;
                     }
                 }
             }
         }
         u = nu;
     }
-    if constexpr (EPI == EPI_ARGMAX) {
+    {
         __shared__ float bv_s[kMaxWaves][8];
         __shared__ int bi_s[kMaxWaves][8];
 #pragma unroll
@@ -890,103 +1012,40 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
             }
         }
         __syncthreads();
-        __shared__ unsigned long long sink;
-        if (threadIdx.x == 0) grid_argmax(p, nw, bv_s, bi_s, &sink);
+        __shared__ unsigned long long sink[kHeadRows];
+        if (wid == 0) grid_argmax<4>(p, kMaxWaves, bv_s, bi_s, sink, lane);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core GEMV with the K range split over a block's four waves, for the
+// Matrix-core GEMV with the K range split over a block's W waves, for the
 // projections that are not persistent: one block per unit (16 weight rows,
 // or 8 output rows of the SwiGLU pair), K = 2048 S with S <= 3.  A block per
-// unit puts several times more compute units to work than a wave per unit,
-// and each wave's share (4S loads, a quarter of the groups) is short.  The
-// activation setup gives wave w activation row w over all S chunks, so the
-// norms need no cross-wave sums; the four waves' partial sums meet in LDS.
+// unit puts many more compute units to work than a wave per unit, and each
+// wave's share (16 S / W loads) is short; with W = 16 every SIMD holds four
+// waves, which hides the latency of both the activation setup and the loop.
+// In the setup, the W / 4 waves of activation row w % 4 split each chunk's
+// features; the norms and chunk maxima meet in LDS.  The waves' partial sums
+// meet in LDS at the end, and wave r < 4 folds and stores register r.
 // Operand layout and arithmetic are those of k_gemv_mma; the activation
 // scale of each chunk is applied when a wave's loads cross into the next
 // chunk (and folded into the bias factors in LDS).
 // ---------------------------------------------------------------------------
-template <int PRO, int S>
-__device__ __forceinline__ void mma_sk_setup(const GemvParams& p, const View& v, int wid, int lane,
-                                             u32x4 (*bq)[2][kWave], float (*tx)[kMmaCols], float (*xs_lds)[4]) {
-    const int mi = wid;  // wave w quantizes activation row w
-    float xv[S][32], gv[S][32];
-#pragma unroll
-    for (int c = 0; c < S; ++c) load_x_row<PRO>(p, v, mi, (64 * c + lane) * kGroup, true, xv[c], gv[c], true);
-    if constexpr (PRO != PRO_PLAIN) {
-        float ss0 = 0.0f, ss1 = 0.0f;
-#pragma unroll
-        for (int c = 0; c < S; ++c) {
-            float ss = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) ss = fmaf(xv[c][i], xv[c][i], ss);
-            if (PRO == PRO_CONCAT && (64 * c + lane) * kGroup >= p.H)
-                ss1 += ss;
-            else
-                ss0 += ss;
-        }
-        const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
-        const float inv0 = rsqrtf(wave_sum(ss0) / (float)nfeat + p.eps);
-        const float inv1 = PRO == PRO_CONCAT ? rsqrtf(wave_sum(ss1) / (float)nfeat + p.eps) : inv0;
-        if (mi < p.m) {
-#pragma unroll
-            for (int c = 0; c < S; ++c) {
-                const int kk = (64 * c + lane) * kGroup;
-                const float iv = (PRO == PRO_CONCAT && kk >= p.H) ? inv1 : inv0;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) xv[c][i] = xv[c][i] * iv * gv[c][i];
-                if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0)
-                    store32(p.normed_out + (int64_t)mi * v.K + kk, xv[c]);
-            }
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < S; ++c) {
-        const int g = lane;
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[c][i]));
-        am = wave_max(am);
-        const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
-        const float x_s = am / kQMax;
-        XFrag f;
-        quantize_group<FMT_Q4>(xv[c], inv_q, x_s, f);
-        const int t = 16 * c + (g >> 2), pp = (g >> 1) & 1, par = g & 1;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int wp = 0; wp < 2; ++wp) {
-            const int h = 2 * wp + par;
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                const int* X = hl ? f.lo : f.hi;
-                const int ct = 2 * mi + hl;
-                const u32x4 val = {(unsigned)X[4 * wp], (unsigned)X[4 * wp + 1], (unsigned)X[4 * wp + 2],
-                                   (unsigned)X[4 * wp + 3]};
-                bq[t][pp][ct + 8 * par + 16 * h] = val;
-                bq[t][pp][ct + 8 * (1 - par) + 16 * h] = zero;
-            }
-        }
-        const int G = 64 * c + g;
-        tx[G][2 * mi] = f.sxd * x_s;  // the bias factor already carries the chunk's activation scale
-        tx[G][2 * mi + 1] = 0.0f;
-        tx[G][8 + 2 * mi] = 0.0f;
-        tx[G][9 + 2 * mi] = 0.0f;
-        if (lane == 0) xs_lds[c][mi] = x_s;
-    }
-    __syncthreads();
-}
-
-template <int PRO, int EPI, int S>
-__global__ void __launch_bounds__(256) k_gemv_mma_sk(const GemvParams p) {
-    constexpr int T = 16 * S;   // loads (4 groups x 16 rows each) over K
-    constexpr int TW = T / 4;   // loads per wave
+template <int PRO, int EPI, int S, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
+    constexpr int R = W / 4;   // waves per activation row in the setup
+    constexpr int NI = 8 / R;  // 1 KB pieces of each chunk per wave in the setup
+    constexpr int T = 16 * S;  // loads (4 groups x 16 rows each) over K
+    constexpr int TW = T / W;  // loads per wave
     constexpr int GW = 4 * TW;  // groups per wave
-    __shared__ u32x4 bq[T][2][kWave];           // B operands, 32 KB per chunk
-    __shared__ float tx[64 * S][kMmaCols];      // bias factors x xs, 4 KB per chunk
-    __shared__ float stage[4][GW * kStage];     // each wave's scales, [group][row]
+    constexpr int NE = GW / 4;  // groups per lane quarter
+    static_assert(T % W == 0 && 8 % R == 0, "wave split");
+    __shared__ u32x4 bq[T][2][kWave];        // B operands, 32 KB per chunk
+    __shared__ float tx[64 * S][kMmaCols];   // bias factors x xs, 4 KB per chunk
+    __shared__ float stage[W][GW * kStage];  // each wave's scales, [group][row]
+    __shared__ float red[W][4][kWave];       // the waves' partial sums
+    __shared__ float part[S + 2][4][R];      // setup partials: chunk maxima, then squares per segment
     __shared__ float xs_lds[S][4];
-    __shared__ float red[4][4][kWave];          // the waves' partial sums
 
     if (p.zero_words && blockIdx.x == 0)
         for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
@@ -994,14 +1053,19 @@ __global__ void __launch_bounds__(256) k_gemv_mma_sk(const GemvParams p) {
     resolve_view(p, v);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int u = blockIdx.x;
+
+    // ---- activations first (they come from L2 and are needed first)
+    const int mi = wid & 3, sub = wid >> 2;
+    XPieces<S, NI> xp;
+    mma_load_x<PRO, S, NI>(p, v, mi, sub, lane, xp);
+
+    // ---- this wave's weights
     const int j = lane & 15, h = lane >> 4;
     const int mi_l = (j & 7) >> 1;
     const bool lo_col = (j & 1) != 0;
     const float colf = lo_col ? 1.0f : 256.0f;
     constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
-    const int u = blockIdx.x;
-
-    // this lane's weight row (among up to three matrices, or gate/up)
     int row = u * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
     row = row < v.N ? row : v.N - 1;
     int64_t in1, in2;
@@ -1018,34 +1082,34 @@ __global__ void __launch_bounds__(256) k_gemv_mma_sk(const GemvParams p) {
     const int t0 = wid * TW, g0 = wid * GW;
     const char* crow = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
     const float* srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 +
-                                                       in2 * v.ds2) + (int64_t)lr * v.G + g0 + 4 * h;
+                                                       in2 * v.ds2) + (int64_t)lr * v.G + g0 + NE * h;
     const float* brow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 +
-                                                       in2 * v.db2) + (int64_t)lr * v.G + g0 + 4 * h;
-    // this wave's weights are requested before the activation setup
+                                                       in2 * v.db2) + (int64_t)lr * v.G + g0 + NE * h;
     u32x4 cw[TW];
 #pragma unroll
     for (int i = 0; i < TW; ++i)
         cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i)));
-    v4f_t sv[S], bv[S];
+    float sv[NE], bv[NE];
 #pragma unroll
-    for (int L = 0; L < S; ++L) {
-        sv[L] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(srow + 16 * L));
-        bv[L] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(brow + 16 * L));
+    for (int e = 0; e < NE; ++e) {
+        sv[e] = __builtin_nontemporal_load(srow + e);
+        bv[e] = __builtin_nontemporal_load(brow + e);
     }
-    mma_sk_setup<PRO, S>(p, v, wid, lane, bq, tx, xs_lds);
 
+    mma_quant_x<PRO, S, R>(p, v, mi, sub, lane, xp, bq, tx, xs_lds, part);
+
+    // ---- bias sums and this wave's scale stage
     float* st = stage[wid];
     v4f_t cb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int L = 0; L < S; ++L) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int gl = 16 * L + 4 * h + e;  // group within the wave's share
-            st[gl * kStage + j] = sv[L][e];
-            cb = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[L][e], tx[g0 + gl][j], cb, 0, 0, 0);
-        }
+    for (int e = 0; e < NE; ++e) {
+        const int gl = NE * h + e;  // group within the wave's share
+        st[gl * kStage + j] = sv[e];
+        cb = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], tx[g0 + gl][j], cb, 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
+
+    // ---- integer products
     float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
@@ -1080,36 +1144,30 @@ __global__ void __launch_bounds__(256) k_gemv_mma_sk(const GemvParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wid][r][lane] = fmaf(tot[r], colf, cb[r]);
     __syncthreads();
-    if (wid != 0) return;
-    float res[4];
+
+    // ---- wave r < 4 sums, folds and stores register r
+    if (wid >= 4) return;
+    const int r = wid;
+    float x = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float x = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
-        x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
-        x += dpp_partner<1>(x);
-        res[r] = x;
-    }
+    for (int q = 0; q < W; ++q) x += red[q][r][lane];
+    x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+    x += dpp_partner<1>(x);
     const bool writer = j < 8 && !lo_col && mi_l < p.m;
     if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float lo, hi;
-            swap_halves<32>(res[r], res[r], lo, hi);
-            const int orow = u * kOutRows + 4 * h + r;
-            if (writer && h < 2 && orow < v.N) {
-                float z = silu(res[r]) * hi;
-                if (v.rowscale) z *= v.rowscale[mi_l];
-                v.y[(int64_t)mi_l * v.N + orow] = z;
-            }
+        float lo, hi;
+        swap_halves<32>(x, x, lo, hi);
+        const int orow = u * kOutRows + 4 * h + r;
+        if (writer && h < 2 && orow < v.N) {
+            float z = silu(x) * hi;
+            if (v.rowscale) z *= v.rowscale[mi_l];
+            v.y[(int64_t)mi_l * v.N + orow] = z;
         }
-    } else if (writer) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int orow = u * kMmaRows + 4 * h + r;
-            if (orow < v.N) {
-                const int64_t o = (int64_t)mi_l * v.N + orow;
-                v.y[o] = p.residual ? res[r] + p.residual[o] : res[r];
-            }
+    } else {
+        const int orow = u * kMmaRows + 4 * h + r;
+        if (writer && orow < v.N) {
+            const int64_t o = (int64_t)mi_l * v.N + orow;
+            v.y[o] = p.residual ? x + p.residual[o] : x;
         }
     }
 }
@@ -1193,8 +1251,11 @@ static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int 
 
 // The matrix-core path serves 4-bit GEMVs over exactly one 2048-feature
 // chunk at three or four activation rows.
-static bool mma_path(int fmt, int epi, int m, const GemvParams& p) {
-    return fmt == FMT_Q4 && m >= 3 && m <= 4 && p.K == kChunk && !p.slot_expert;
+// The lm_head (argmax epilogue) at three or four rows: persistent matrix-core
+// blocks.
+static bool mma_head_path(int fmt, int epi, int m, const GemvParams& p) {
+    return fmt == FMT_Q4 && epi == EPI_ARGMAX && m >= 3 && m <= 4 && p.K == kChunk && p.nmat == 1 &&
+           !p.slot_expert;
 }
 
 // Store and SwiGLU GEMVs at three or four rows over 1-3 chunks that are not
@@ -1204,33 +1265,38 @@ static bool mma_sk_path(int fmt, int epi, int m, const GemvParams& p) {
            !p.slot_expert && p.nmat <= 3 && (p.K == kChunk || p.K == 2 * kChunk || p.K == 3 * kChunk);
 }
 
+// 16 waves per block while the units fit one block per compute unit (every
+// SIMD then holds four of a block's waves), else 8 (three blocks of one
+// chunk fit a compute unit's LDS).
+template <int PRO, int EPI, int W>
+static void launch_mma_sk_w(const GemvParams& p, dim3 grid, hipStream_t st) {
+    const dim3 block(W * kWave);
+    switch (p.K / kChunk) {
+        case 1: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W>), grid, block, 0, st, p); break;
+        default: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 3, W>), grid, block, 0, st, p); break;
+    }
+}
+
 template <int PRO, int EPI>
 static hipError_t launch_mma_sk(const GemvParams& p, hipStream_t st) {
     const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
-    const dim3 grid((p.N + rows - 1) / rows), block(4 * kWave);
-    switch (p.K / kChunk) {
-        case 1: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2>), grid, block, 0, st, p); break;
-        default: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 3>), grid, block, 0, st, p); break;
-    }
-    return hipGetLastError();
-}
-
-template <int PRO, int EPI>
-static hipError_t launch_mma(const GemvParams& p, hipStream_t st, int& blocks) {
-    const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
     const int units = (p.N + rows - 1) / rows;
-    int waves = 4;
-    blocks = (units + waves - 1) / waves;
-    if (p.balance) {  // persistent: one 8-wave block per compute unit
-        waves = kMaxWaves;
-        const int need = (units + waves - 1) / waves, cu = device_cu_count();
-        blocks = need < cu ? need : cu;
-    }
-    hipLaunchKernelGGL((k_gemv_mma<PRO, EPI>), dim3(blocks), dim3(64 * waves), 0, st, p);
+    if (units <= device_cu_count())
+        launch_mma_sk_w<PRO, EPI, 16>(p, dim3(units), st);
+    else
+        launch_mma_sk_w<PRO, EPI, 8>(p, dim3(units), st);
     return hipGetLastError();
 }
 
+// One 8-wave block per compute unit (fewer for a small matrix).
+template <int PRO>
+static hipError_t launch_mma_head(const GemvParams& p, hipStream_t st) {
+    const int units = (p.N + kMmaRows - 1) / kMmaRows;
+    const int need = (units + kMaxWaves - 1) / kMaxWaves, cu = device_cu_count();
+    hipLaunchKernelGGL((k_gemv_mma<PRO>), dim3(need < cu ? need : cu), dim3(64 * kMaxWaves), 0, st, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
                        hipStream_t st) {
@@ -1243,15 +1309,7 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
         if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_mma_sk<PRO_PLAIN, EPI_SWIGLU>(p, st);
         if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_mma_sk<PRO_RMS, EPI_SWIGLU>(p, st);
     }
-    if (mma_path(fmt, epi, m, p)) {
-        int blocks = 0;
-        if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_mma<PRO_PLAIN, EPI_STORE>(p, st, blocks);
-        if (pro == PRO_RMS && epi == EPI_STORE) return launch_mma<PRO_RMS, EPI_STORE>(p, st, blocks);
-        if (pro == PRO_CONCAT && epi == EPI_STORE) return launch_mma<PRO_CONCAT, EPI_STORE>(p, st, blocks);
-        if (pro == PRO_RMS && epi == EPI_ARGMAX) return launch_mma<PRO_RMS, EPI_ARGMAX>(p, st, blocks);
-        if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_mma<PRO_PLAIN, EPI_SWIGLU>(p, st, blocks);
-        if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_mma<PRO_RMS, EPI_SWIGLU>(p, st, blocks);
-    }
+    if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS) return launch_mma_head<PRO_RMS>(p, st);
     if (fmt == FMT_Q4) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_RMS, EPI_STORE>(m, p, sh, 1, st);

@@ -92,7 +92,9 @@ def test_qgemv_config0_full():
                                        (1000, 2048, 4, True), (517, 2048, 3, False), (16, 2048, 4, False),
                                        (15, 2048, 3, True), (4111, 2048, 4, False),
                                        # matrix-core path over 2 and 3 chunks
-                                       (517, 6144, 3, True), (70, 6144, 4, False), (31, 4096, 3, True)])
+                                       (517, 6144, 3, True), (70, 6144, 4, False), (31, 4096, 3, True),
+                                       # more units than compute units: 8-wave blocks
+                                       (4400, 4096, 3, False), (4200, 6144, 4, True)])
 def test_qgemv_shapes(n, k, m, res):
     _say(f"qgemv n={n} k={k} m={m} residual={res}")
     g = synth.rng(102, n, k, m)
