@@ -117,6 +117,47 @@ __device__ __forceinline__ void load_x_row(const GemvParams& p, const View& v, i
     }
 }
 
+// 16-bit activation quantization without a float-to-int conversion: adding
+// 1.5 * 2^23 + 128 to the product x * inv (rounded first, as in split16)
+// leaves q + 128 + 0x400000 in the low mantissa bits, rounded to nearest
+// even exactly as split16 rounds, for |q| < 2^22.  Byte 1 of the result is
+// then hi = (q + 128) >> 8 and byte 0 is lo = q - 256 hi with its sign bit
+// flipped, and the bits of several values sum to sum(q) plus a known
+// multiple of kQBiasBits.
+constexpr float kQBias = 12583040.0f;  // 1.5 * 2^23 + 128
+constexpr unsigned kQBiasBits = 0x4B400080u;
+__device__ __forceinline__ unsigned q_bits(float x, float inv) {
+#pragma clang fp contract(off)
+    const float y = x * inv;
+    return __float_as_uint(y + kQBias);
+}
+
+// Row mi's input for the features of segment seg (PRO_CONCAT: 0 = the
+// embedding row, or the token's table row, 1 = the hidden row; otherwise the
+// one input row) and the matching gamma.
+template <int PRO>
+__device__ __forceinline__ const float* x_segment(const GemvParams& p, const View& v, int mi, int seg,
+                                                  const float*& gam) {
+    if constexpr (PRO == PRO_CONCAT) {
+        if (seg) {
+            gam = p.g1;
+            return p.x1 + (int64_t)mi * p.H;
+        }
+        gam = p.g0;
+        if (p.tokens) {
+            int tok = p.tokens[mi];
+            if (tok >= 0 || v.x0 == nullptr) {
+                tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
+                return p.table + (int64_t)tok * p.H;
+            }
+        }
+        return v.x0 + (int64_t)mi * p.H;
+    } else {
+        gam = p.g0;
+        return v.x0 + (int64_t)mi * v.K;
+    }
+}
+
 // Norm (for PRO_RMS / PRO_CONCAT) and 16-bit split of the lane's features of
 // row mi.  Every thread of the block calls it; it holds block barriers when
 // several waves share one weight row (S > 1).
@@ -282,6 +323,129 @@ __device__ __forceinline__ void shared_rows(const GemvParams& p, const View& v, 
     }
 }
 
+// One activation row, 4-bit weights.  Each wave loads its whole chunk s of
+// the row in 1 KB pieces (lane l holds features 256 i + 4 l .. +3 of piece
+// i), so every load instruction reads a contiguous kilobyte; the loads are
+// requested before the first weight tiles (row1_load), with no branches, so
+// that the setup waits for them alone, and consumed after (row1_finish): the
+// norm (over the block's chunk waves through LDS when S > 1), the chunk
+// maximum, quantization with q_bits, and each group's fragment (hi[8],
+// lo[8], sxd; the layout of quantize_group) passed through a wave-private
+// LDS region to the lane that owns the group.
+struct Row1Pieces {
+    float4 x[8], g[8];
+};
+constexpr int kRow1Chunks = 4;  // K <= 8192
+constexpr int kRow1Words = 17;  // hi[8], lo[8], sxd per group
+
+template <int PRO>
+__device__ __forceinline__ void row1_load(const GemvParams& p, const View& v, int lane, int s, Row1Pieces& rp) {
+    const float *gam0 = nullptr, *gam1 = nullptr;
+    const float* src0 = x_segment<PRO>(p, v, 0, 0, gam0);
+    const float* src1 = PRO == PRO_CONCAT ? x_segment<PRO>(p, v, 0, 1, gam1) : src0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int f = kChunk * s + 256 * i + 4 * lane;
+        f = f < v.K ? f : 0;  // past the end: any valid address, zeroed in row1_finish
+        const bool sg = PRO == PRO_CONCAT && f >= p.H;
+        const int kl = sg ? f - p.H : f;
+        rp.x[i] = *reinterpret_cast<const float4*>((sg ? src1 : src0) + kl);
+        if constexpr (PRO != PRO_PLAIN) rp.g[i] = *reinterpret_cast<const float4*>((sg ? gam1 : gam0) + kl);
+    }
+}
+
+template <int PRO>
+__device__ __forceinline__ void row1_finish(const GemvParams& p, const View& v, int lane, int S, int s, int q,
+                                            Row1Pieces& rp, unsigned* xq, float (*part)[2], XFrag& xf,
+                                            float& xs) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (kChunk * s + 256 * i + 4 * lane >= v.K) rp.x[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if constexpr (PRO != PRO_PLAIN) {
+        float ss0 = 0.0f, ss1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 x = rp.x[i];
+            const float ss = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, x.w * x.w)));
+            if (PRO == PRO_CONCAT && kChunk * s + 256 * i + 4 * lane >= p.H)
+                ss1 += ss;
+            else
+                ss0 += ss;
+        }
+        ss0 = wave_sum(ss0);
+        if constexpr (PRO == PRO_CONCAT) ss1 = wave_sum(ss1);
+        if (S > 1) {  // the other chunks' sums
+            if (lane == 0 && q == 0) {
+                part[s][0] = ss0;
+                part[s][1] = ss1;
+            }
+            __syncthreads();
+            ss0 = 0.0f;
+            ss1 = 0.0f;
+            for (int k = 0; k < S; ++k) {
+                ss0 += part[k][0];
+                ss1 += part[k][1];
+            }
+        }
+        const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
+        const float inv0 = rsqrtf(ss0 / (float)nfeat + p.eps);
+        const float inv1 = PRO == PRO_CONCAT ? rsqrtf(ss1 / (float)nfeat + p.eps) : inv0;
+        const bool store = PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0 && q == 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int f = kChunk * s + 256 * i + 4 * lane;
+            const float iv = (PRO == PRO_CONCAT && f >= p.H) ? inv1 : inv0;
+            float4& x = rp.x[i];
+            const float4 g = rp.g[i];
+            x = make_float4(x.x * iv * g.x, x.y * iv * g.y, x.z * iv * g.z, x.w * iv * g.w);
+            if (store && f < v.K) *reinterpret_cast<float4*>(p.normed_out + f) = x;
+        }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 x = rp.x[i];
+        am = fmaxf(am, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    }
+    am = wave_max(am);
+    const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
+    xs = am / kQMax;
+    // lanes 2k and 2k+1 hold the first and last four features of a code
+    // word, and one quad exchange forms the word's hi and lo operand words
+    // (even features, then odd)
+    const bool odd = lane & 1;
+    const unsigned sel_h = odd ? 0x01000504u : 0x05040100u;
+    const unsigned sel_l = odd ? 0x03020706u : 0x07060302u;
+    const int k8 = lane & 7;  // word of the group
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 x = rp.x[i];
+        const unsigned b0 = q_bits(x.x, inv_q), b1 = q_bits(x.y, inv_q), b2 = q_bits(x.z, inv_q),
+                       b3 = q_bits(x.w, inv_q);
+        unsigned qsum = (b0 + b1) + (b2 + b3);
+        const unsigned p02 = __builtin_amdgcn_perm(b2, b0, 0x04000501u);
+        const unsigned p13 = __builtin_amdgcn_perm(b3, b1, 0x04000501u);
+        const unsigned keep = odd ? p13 : p02;
+        const unsigned got = (unsigned)dpp_partner<1>((int)(odd ? p02 : p13));
+        const int gl = 8 * i + (lane >> 3);  // group within the chunk
+        xq[k8 * kWave + gl] = __builtin_amdgcn_perm(got, keep, sel_h);
+        xq[(8 + k8) * kWave + gl] = __builtin_amdgcn_perm(got, keep, sel_l) ^ 0x80808080u;
+        qsum += (unsigned)dpp_partner<1>((int)qsum);
+        qsum += (unsigned)dpp_partner<2>((int)qsum);
+        qsum += (unsigned)dpp_partner<4>((int)qsum);
+        if (k8 == 0) xq[16 * kWave + gl] = __float_as_uint((float)(int)(qsum - 32u * kQBiasBits));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        xf.hi[k] = (int)xq[k * kWave + lane];
+        xf.lo[k] = (int)xq[(8 + k) * kWave + lane];
+    }
+    xf.sxd = __uint_as_float(xq[16 * kWave + lane]);
+}
+
 // Weight fragments of one tile (R rows x P matrices) for this lane's group.
 template <int FMT, int R, int P>
 struct TileFrags {
@@ -404,7 +568,7 @@ struct TileSeq {
 template <int FMT, int M, int PRO, int EPI>
 __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const GemvParams p) {
     constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
-    constexpr int R = gemv_rows(M, P);
+    constexpr int R = gemv_rows(M, P, EPI);
     constexpr int V = R * M * P;
     constexpr int kWaves = block_waves(FMT, EPI, M);  // waves per block, at most
     __shared__ float red[kWaves][kWave * 2];
@@ -457,16 +621,35 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
         ts.init(blockIdx.x, gridDim.x, NU, false, claim);
     auto row0 = [&](int u) { return (u * per + qo) * R; };
     TileFrags<FMT, R, P> tf, tf2;
-    int wa = ts.next(claim), wb = -1;
-    if (wa >= 0) load_tile<FMT, R, P>(tf, v, row0(wa), gc);
-    if constexpr (kDouble) {
-        if (wa >= 0) wb = ts.next(claim);
-        if (wb >= 0) load_tile<FMT, R, P>(tf2, v, row0(wb), gc);
-    }
-
     XFrag xf[M];
     float xs[M];
     bool shared_done = false;
+    // one 4-bit activation row: its pieces are requested before the first
+    // tiles, which are then requested unconditionally (tile 0 stands in for
+    // none), so that the setup waits for the activations only
+    constexpr bool kRow1 = M == 1 && FMT == FMT_Q4;  // S <= kRow1Chunks (checked at launch)
+    Row1Pieces rp;
+    if constexpr (kRow1) row1_load<PRO>(p, v, lane, s, rp);
+    int wa = ts.next(claim), wb = -1;
+    if constexpr (kRow1) {
+        load_tile<FMT, R, P>(tf, v, row0(wa >= 0 ? wa : 0), gc);
+        if constexpr (kDouble) {
+            if (wa >= 0) wb = ts.next(claim);
+            load_tile<FMT, R, P>(tf2, v, row0(wb >= 0 ? wb : 0), gc);
+        }
+    } else {
+        if (wa >= 0) load_tile<FMT, R, P>(tf, v, row0(wa), gc);
+        if constexpr (kDouble) {
+            if (wa >= 0) wb = ts.next(claim);
+            if (wb >= 0) load_tile<FMT, R, P>(tf2, v, row0(wb), gc);
+        }
+    }
+    if constexpr (kRow1) {
+        __shared__ unsigned xq1[kWaves][kRow1Words * kWave];
+        __shared__ float part1[kRow1Chunks][2];
+        row1_finish<PRO>(p, v, lane, S, s, q, rp, xq1[wid], part1, xf[0], xs[0]);
+        shared_done = true;
+    }
     if constexpr (M == 2 || M == 4) {
         __shared__ unsigned xq[xq_slots<M>() * kXqWords * kWave];
         __shared__ float xsq[xq_slots<M>()];
@@ -617,47 +800,6 @@ __device__ __forceinline__ void perm32_swap(unsigned& a, unsigned& b) {
     const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
     a = r[0];
     b = r[1];
-}
-
-// 16-bit activation quantization without a float-to-int conversion: adding
-// 1.5 * 2^23 + 128 to the product x * inv (rounded first, as in split16)
-// leaves q + 128 + 0x400000 in the low mantissa bits, rounded to nearest
-// even exactly as split16 rounds, for |q| < 2^22.  Byte 1 of the result is
-// then hi = (q + 128) >> 8 and byte 0 is lo = q - 256 hi with its sign bit
-// flipped, and the bits of several values sum to sum(q) plus a known
-// multiple of kQBiasBits.
-constexpr float kQBias = 12583040.0f;  // 1.5 * 2^23 + 128
-constexpr unsigned kQBiasBits = 0x4B400080u;
-__device__ __forceinline__ unsigned q_bits(float x, float inv) {
-#pragma clang fp contract(off)
-    const float y = x * inv;
-    return __float_as_uint(y + kQBias);
-}
-
-// Row mi's input for the features of segment seg (PRO_CONCAT: 0 = the
-// embedding row, or the token's table row, 1 = the hidden row; otherwise the
-// one input row) and the matching gamma.
-template <int PRO>
-__device__ __forceinline__ const float* x_segment(const GemvParams& p, const View& v, int mi, int seg,
-                                                  const float*& gam) {
-    if constexpr (PRO == PRO_CONCAT) {
-        if (seg) {
-            gam = p.g1;
-            return p.x1 + (int64_t)mi * p.H;
-        }
-        gam = p.g0;
-        if (p.tokens) {
-            int tok = p.tokens[mi];
-            if (tok >= 0 || v.x0 == nullptr) {
-                tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
-                return p.table + (int64_t)tok * p.H;
-            }
-        }
-        return v.x0 + (int64_t)mi * p.H;
-    } else {
-        gam = p.g0;
-        return v.x0 + (int64_t)mi * v.K;
-    }
 }
 
 // Activation setup of the matrix-core kernels, shared by a block's waves:
@@ -1226,7 +1368,7 @@ GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int 
     const int Q = waves / S > 1 ? waves / S : 1;
     const int Mi = inst_m(m);
     const int P = (epi == EPI_SWIGLU) ? 2 : 1;
-    const int R = gemv_rows(Mi, P);
+    const int R = gemv_rows(Mi, P, epi);
     const int ntiles = (N + Q * R - 1) / (Q * R);
     GemvShape sh;
     sh.Q = Q;
@@ -1240,6 +1382,7 @@ GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int 
 template <int FMT, int PRO, int EPI>
 static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int slots, hipStream_t st) {
     dim3 grid(sh.grid, slots), block(sh.block);
+    if (FMT == FMT_Q4 && inst_m(m) == 1 && (p.K + kChunk - 1) / kChunk > kRow1Chunks) return hipErrorInvalidValue;
     switch (inst_m(m)) {
         case 1: hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI>), grid, block, 0, st, p); break;
         case 2: hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI>), grid, block, 0, st, p); break;
@@ -1249,8 +1392,6 @@ static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int 
     return hipGetLastError();
 }
 
-// The matrix-core path serves 4-bit GEMVs over exactly one 2048-feature
-// chunk at three or four activation rows.
 // The lm_head (argmax epilogue) at three or four rows: persistent matrix-core
 // blocks.
 static bool mma_head_path(int fmt, int epi, int m, const GemvParams& p) {

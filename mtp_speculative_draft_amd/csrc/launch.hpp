@@ -87,8 +87,12 @@ constexpr int kGemvRows = 8;
 constexpr int kGemvVals = 32;
 // One activation row with a single matrix takes 4 rows per wave: for the
 // small projections that doubles the blocks in flight, which shortens them.
-__host__ __device__ constexpr int gemv_rows(int M, int P) {
-    return (M == 1 && P == 1) ? 4 : ((kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows);
+constexpr int kRowsM1 = 4;    // M = 1, one matrix, store epilogue
+constexpr int kRowsM1P2 = 8;  // M = 1, SwiGLU pair
+__host__ __device__ constexpr int gemv_rows(int M, int P, int epi) {
+    return (M == 1 && P == 1) ? (epi == EPI_ARGMAX ? 4 : kRowsM1)
+                              : ((M == 1 && P == 2) ? kRowsM1P2
+                                                    : ((kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows));
 }
 // Row count of the kernel instantiation that serves m activation rows.
 __host__ __device__ constexpr int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
