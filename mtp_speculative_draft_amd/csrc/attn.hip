@@ -15,8 +15,9 @@
 // arithmetic is the same whatever the slicing, so m rows at once give
 // bitwise the results of m single-row calls.  The block that owns a new
 // position rotates its k and uses it from LDS; the first slice also writes k
-// and v into the cache.  It emits per (chunk, query row-head) the chunk
-// maximum, the exp-sum and the unnormalised sum of p*V.
+// and v into the cache.  The scores and the p*V sums are f32 matrix-core
+// products over 16-row tiles of row-heads.  It emits per (chunk, query
+// row-head) the chunk maximum, the exp-sum and the unnormalised sum of p*V.
 // Kernel 2 (grid: KV heads x query row-heads) merges the chunks with the
 // log-sum-exp rule.
 #include <cmath>
@@ -54,17 +55,16 @@ __device__ __forceinline__ bool attn_block(const AttnParams& p, int Z, int& c, i
     return true;
 }
 
-// HMT: the block's row-head count rounded up to 8 or 16; the register-blocked
-// loops below are sized by it.  Local row-head hl of slice z is the group's
-// row-head z * kSliceHM + hl (= mi * GQ + local query head).
-template <int HMT>
+// Local row-head hl of slice z is the group's row-head z * kSliceHM + hl
+// (= mi * GQ + local query head).
+typedef float v4f_t __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
-    __shared__ float qs[HMT][kD];
+    __shared__ float qs[kSliceHM][kD];
     __shared__ float ks[kC][kKStride];
     __shared__ float vs[kC][kD];
-    __shared__ float sc[HMT][kSStride];
+    __shared__ float sc[kSliceHM][kSStride];
+    __shared__ float spart[2][kSliceHM][kSStride];  // score halves (dims 0-63, 64-127)
     __shared__ float rc[8][kD / 2], rs[8][kD / 2];  // rotary cos/sin per new row
-    __shared__ float stat_m[HMT], stat_l[HMT];
 
     const int GQ = p.nh / p.nkv;
     const int HMall = GQ * p.m;
@@ -79,7 +79,9 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     const int64_t cbase = (int64_t)g * p.capacity * kD;
     constexpr int kQuads = kC * (kD / 4) / 256;  // float4 slots of K (and of V) per thread
 
-    // 1. the chunk's cached K/V rows are requested first ...
+    // 1. every global read of the block is requested up front, so that the
+    //    block waits for memory once: the chunk's cached K/V rows, the query
+    //    pairs (i, i + d/2) of its row-heads and the new k/v rows it owns
     float4 kr[kQuads], vr[kQuads];
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
@@ -90,6 +92,36 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
         if (pos < p.cache_len) {
             kr[u] = reinterpret_cast<const float4*>(p.k_cache + cbase + (int64_t)pos * kD)[w];
             vr[u] = reinterpret_cast<const float4*>(p.v_cache + cbase + (int64_t)pos * kD)[w];
+        }
+    }
+    constexpr int kQPairs = kSliceHM * (kD / 2) / 256;  // query pairs per thread
+    float qa[kQPairs], qb[kQPairs];
+#pragma unroll
+    for (int u = 0; u < kQPairs; ++u) {
+        const int idx = t + 256 * u, hm = idx / (kD / 2), i = idx % (kD / 2);
+        qa[u] = 0.0f;
+        qb[u] = 0.0f;
+        if (hm < HM) {
+            const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
+            const float* q = p.qkv + (int64_t)mi * ld + hq * kD;
+            qa[u] = q[i];
+            qb[u] = q[i + kD / 2];
+        }
+    }
+    constexpr int kNPairs = 8 * (kD / 2) / 256;  // new-row pairs per thread (m <= 8)
+    float ka[kNPairs], kb[kNPairs], va[kNPairs], vb[kNPairs];
+#pragma unroll
+    for (int u = 0; u < kNPairs; ++u) {
+        const int idx = t + 256 * u, mi = idx / (kD / 2), i = idx % (kD / 2);
+        const int pos = p.cache_len + mi;
+        ka[u] = kb[u] = va[u] = vb[u] = 0.0f;
+        if (mi < p.m && pos >= p0 && pos < p0 + kC) {
+            const float* kn = p.qkv + (int64_t)mi * ld + p.nh * kD + g * kD;
+            const float* vn = p.qkv + (int64_t)mi * ld + (p.nh + p.nkv) * kD + g * kD;
+            ka[u] = kn[i];
+            kb[u] = kn[i + kD / 2];
+            va[u] = vn[i];
+            vb[u] = vn[i + kD / 2];
         }
     }
     // ... and the rotary table for positions cache_len + mi is built meanwhile
@@ -103,14 +135,15 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     // 2. rotated queries of this group (hm = mi * GQ + local head), cached
     //    rows into LDS, rows past the new ones zeroed, the new rows rotated and
     //    appended to the cache (only by the chunk that owns them)
-    for (int idx = t; idx < HM * (kD / 2); idx += blockDim.x) {
-        const int hm = idx / (kD / 2), i = idx % (kD / 2);
-        const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
-        const float* q = p.qkv + (int64_t)mi * ld + hq * kD;
-        const float a = q[i], b = q[i + kD / 2];
-        const float cs = rc[mi][i], sn = rs[mi][i];
-        qs[hm][i] = a * cs - b * sn;
-        qs[hm][i + kD / 2] = a * sn + b * cs;
+#pragma unroll
+    for (int u = 0; u < kQPairs; ++u) {
+        const int idx = t + 256 * u, hm = idx / (kD / 2), i = idx % (kD / 2);
+        if (hm < HM) {
+            const int mi = (hm0 + hm) / GQ;
+            const float cs = rc[mi][i], sn = rs[mi][i];
+            qs[hm][i] = qa[u] * cs - qb[u] * sn;
+            qs[hm][i + kD / 2] = qa[u] * sn + qb[u] * cs;
+        }
     }
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
@@ -121,110 +154,106 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
             *reinterpret_cast<float4*>(&vs[j][4 * w]) = vr[u];
         }
     }
-    for (int idx = t; idx < p.m * (kD / 2); idx += blockDim.x) {
-        const int mi = idx / (kD / 2), i = idx % (kD / 2);
+#pragma unroll
+    for (int u = 0; u < kNPairs; ++u) {
+        const int idx = t + 256 * u, mi = idx / (kD / 2), i = idx % (kD / 2);
         const int pos = p.cache_len + mi;
-        if (pos < p0 || pos >= p0 + kC) continue;
-        const int j = pos - p0;
-        const float* kn = p.qkv + (int64_t)mi * ld + p.nh * kD + g * kD;
-        const float* vn = p.qkv + (int64_t)mi * ld + (p.nh + p.nkv) * kD + g * kD;
-        const float a = kn[i], b = kn[i + kD / 2];
-        const float cs = rc[mi][i], sn = rs[mi][i];
-        const float k0 = a * cs - b * sn, k1 = a * sn + b * cs;
-        ks[j][i] = k0;
-        ks[j][i + kD / 2] = k1;
-        vs[j][i] = vn[i];
-        vs[j][i + kD / 2] = vn[i + kD / 2];
-        if (z != 0) continue;  // one slice writes the cache
-        float* kd = p.k_cache + cbase + (int64_t)pos * kD;
-        float* vd = p.v_cache + cbase + (int64_t)pos * kD;
-        kd[i] = k0;
-        kd[i + kD / 2] = k1;
-        vd[i] = vn[i];
-        vd[i + kD / 2] = vn[i + kD / 2];
+        if (mi < p.m && pos >= p0 && pos < p0 + kC) {
+            const int j = pos - p0;
+            const float cs = rc[mi][i], sn = rs[mi][i];
+            const float k0 = ka[u] * cs - kb[u] * sn, k1 = ka[u] * sn + kb[u] * cs;
+            ks[j][i] = k0;
+            ks[j][i + kD / 2] = k1;
+            vs[j][i] = va[u];
+            vs[j][i + kD / 2] = vb[u];
+            if (z == 0) {  // one slice writes the cache
+                float* kd = p.k_cache + cbase + (int64_t)pos * kD;
+                float* vd = p.v_cache + cbase + (int64_t)pos * kD;
+                kd[i] = k0;
+                kd[i + kD / 2] = k1;
+                vd[i] = va[u];
+                vd[i + kD / 2] = vb[u];
+            }
+        }
     }
     __syncthreads();
 
-    // 3. scores: thread = (position j, row-head block hb); one K row read
-    //    serves every row-head hm = hb + 8r of the thread (masked: query row
-    //    mi sees positions <= cache_len + mi)
+    // 3. scores on the matrix cores (16x16x4 f32): a 16 x 16 tile of
+    //    (row-head, position) per wave and half of the dims (wave w: positions
+    //    16 (w & 1) .., dims 64 (w >> 1) ..); row-heads past HM read as zero.
+    //    Lane l supplies row l % 16 of each operand and, over four products,
+    //    the four dims 4 (l / 16) .. of every 16.
+    const int r16 = lane & 15, kq = lane >> 4;
+    const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     {
-        const int j = t % kC, hb = t / kC;  // 8 blocks of row-heads
-        const int pos = p0 + j;
-        const float scale = 1.0f / sqrtf((float)kD);
-        float acc[HMT / 8];
+        const int jt = wid & 1, dh = wid >> 1;
+        v4f_t acc[4];  // four independent product chains
 #pragma unroll
-        for (int r = 0; r < HMT / 8; ++r) acc[r] = 0.0f;
-        const float4* ka = reinterpret_cast<const float4*>(&ks[j][0]);
-#pragma unroll 4
-        for (int u = 0; u < kD / 4; ++u) {
-            const float4 kv = ka[u];
+        for (int e = 0; e < 4; ++e) acc[e] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < HMT / 8; ++r) {
-                const int hm = hb + 8 * r;
-                if (hm < HM) {
-                    const float4 qv = reinterpret_cast<const float4*>(&qs[hm][0])[u];
-                    acc[r] = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, acc[r]))));
-                }
-            }
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int d = 64 * dh + 16 * s2 + 4 * kq;
+            const float4 a = r16 < HM ? *reinterpret_cast<const float4*>(&qs[r16][d]) : zero4;
+            const float4 b = *reinterpret_cast<const float4*>(&ks[16 * jt + r16][d]);
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[1], 0, 0, 0);
+            acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[2], 0, 0, 0);
+            acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[3], 0, 0, 0);
         }
+        const v4f_t sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        // result lane l, register r: row-head 4 (l / 16) + r, position l % 16
 #pragma unroll
-        for (int r = 0; r < HMT / 8; ++r) {
-            const int hm = hb + 8 * r;
-            if (hm < HM) sc[hm][j] = (pos <= p.cache_len + (hm0 + hm) / GQ) ? acc[r] * scale : -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) spart[dh][4 * kq + r][16 * jt + r16] = sum[r];
     }
     __syncthreads();
 
     // 4. chunk softmax statistics: a wave takes two row-heads at a time, one
-    //    per 32-lane half, one position per lane
+    //    per 32-lane half, one position per lane (masked: query row mi sees
+    //    positions <= cache_len + mi)
+    float* out = p.part + (((int64_t)c * p.nkv + g) * HMall + hm0) * (kD + 2);
+    const float scale = 1.0f / sqrtf((float)kD);
     for (int hp = 2 * wid; hp < HM; hp += 2 * (int)(blockDim.x / kWave)) {
-        const int hm = hp + (lane >> 5);
-        const bool ok = hm < HM;
-        const float sv = ok ? sc[hm][lane & 31] : -INFINITY;
+        const int hm = hp + (lane >> 5), j = lane & 31;
+        const bool ok = hm < HM && p0 + j <= p.cache_len + (hm0 + hm) / GQ;
+        const float sv = ok ? (spart[0][hm][j] + spart[1][hm][j]) * scale : -INFINITY;
         float mx = sv;
         mx = half_max(mx);
         const float e = (mx == -INFINITY) ? 0.0f : __expf(sv - mx);
         float l = e;
         l = half_sum(l);
-        if (ok) {
-            sc[hm][lane & 31] = e;
-            if ((lane & 31) == 0) {
-                stat_m[hm] = mx;
-                stat_l[hm] = l;
+        if (hm < HM) {
+            sc[hm][j] = e;
+            if (j == 0) {
+                out[hm * (kD + 2) + kD] = mx;
+                out[hm * (kD + 2) + kD + 1] = l;
             }
         }
     }
     __syncthreads();
 
-    // 5. unnormalised p*V: thread = (dim, half of the row-heads)
-    float* out = p.part + (((int64_t)c * p.nkv + g) * HMall + hm0) * (kD + 2);
-    {
-        const int dd = t % kD, hh = t / kD;
-        float acc[HMT / 2];
+    // 5. unnormalised p*V on the matrix cores: wave w takes the dims
+    //    32 w .. 32 w + 31 as two 16-dim tiles, the positions as the product
+    //    dimension (lane l supplies positions 4 (l / 16) .. of every 16)
 #pragma unroll
-        for (int r = 0; r < HMT / 2; ++r) acc[r] = 0.0f;
-        for (int j0 = 0; j0 < kC; j0 += 4) {
-            const float v0 = vs[j0][dd], v1 = vs[j0 + 1][dd], v2 = vs[j0 + 2][dd], v3 = vs[j0 + 3][dd];
+    for (int t2 = 0; t2 < 2; ++t2) {
+        const int d0 = 16 * (2 * wid + t2);
+        v4f_t acc[2];  // two independent product chains
 #pragma unroll
-            for (int r = 0; r < HMT / 2; ++r) {
-                const int hm = hh + 2 * r;
-                if (hm < HM) {
-                    const float4 pv = *reinterpret_cast<const float4*>(&sc[hm][j0]);
-                    acc[r] = fmaf(pv.x, v0, fmaf(pv.y, v1, fmaf(pv.z, v2, fmaf(pv.w, v3, acc[r]))));
-                }
-            }
+        for (int e = 0; e < 2; ++e) acc[e] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int j = 16 * s2 + 4 * kq;
+            const float4 a = r16 < HM ? *reinterpret_cast<const float4*>(&sc[r16][j]) : zero4;
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, vs[j][d0 + r16], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, vs[j + 1][d0 + r16], acc[1], 0, 0, 0);
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, vs[j + 2][d0 + r16], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, vs[j + 3][d0 + r16], acc[1], 0, 0, 0);
         }
+        const v4f_t sum = acc[0] + acc[1];
 #pragma unroll
-        for (int r = 0; r < HMT / 2; ++r) {
-            const int hm = hh + 2 * r;
-            if (hm < HM) {
-                out[hm * (kD + 2) + dd] = acc[r];
-                if (dd == 0) {
-                    out[hm * (kD + 2) + kD] = stat_m[hm];
-                    out[hm * (kD + 2) + kD + 1] = stat_l[hm];
-                }
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int hm = 4 * kq + r;
+            if (hm < HM) out[hm * (kD + 2) + d0 + r16] = sum[r];
         }
     }
 }
@@ -291,10 +320,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int Z = (hm + kSliceHM - 1) / kSliceHM;
     const int pairs = p.chunks * p.nkv;
     const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
-    if (hm <= 8)
-        hipLaunchKernelGGL(k_attn_partial<8>, grid, block, 0, st, p);
-    else
-        hipLaunchKernelGGL(k_attn_partial<kSliceHM>, grid, block, 0, st, p);
+    hipLaunchKernelGGL(k_attn_partial, grid, block, 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int HM = (p.nh / p.nkv) * p.m;
