@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=3, help="weight/cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ops", action="store_true", help="skip the single-op timings (GEMV, eh_proj, MoE)")
+    ap.add_argument("--ops-only", action="store_true", help="only the single-op timings, for kernel traces")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
     ap.add_argument("--head-only", action="store_true",
                     help="only the lm_head + argmax launches (m=1), for counter runs")
@@ -116,6 +118,9 @@ def main():
         return copy_ref(torch, dev)
     if args.head_only:
         return head_only(torch, mtp, synth, dev, args.steps)
+    if args.ops_only:
+        print(json.dumps({"ops": op_timings(torch, mtp, synth, dev, args.steps, args.warmup)}), flush=True)
+        return
 
     t0 = time.time()
     S = synth.config4_step()
@@ -245,9 +250,103 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
+    if not args.no_ops:
+        del layers, caches, table
+        torch.cuda.empty_cache()
+        result["ops"] = op_timings(torch, mtp, synth, dev, K, W)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(S, step_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def event_us(torch, dev, fn, n, warm):
+    """Mean duration of fn(i) in microseconds, from HIP events recorded on the
+    current stream (the stream every libmtp call of the binding launches on)."""
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warm):
+        fn(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
+def op_timings(torch, mtp, synth, dev, K, W):
+    """The single-op workloads: 4-bit GEMV 1024x1024 (m=1), the e/h norm + concat
+    + eh_proj 2048x4096 (m=1, 4) and the 8-bit MoE FFN (256 experts, top-8 +
+    shared expert, m=1, 4).  Weight copies are rotated so that their total
+    exceeds the 256 MB Infinity Cache; GB/s = algorithmic bytes / event time."""
+    out = {}
+    n = max(K, 20)
+
+    def rotated_q4(w, copies):
+        base = mtp.DeviceQ4(w, dev)
+        reps = [base]
+        for _ in range(copies - 1):
+            c = mtp.DeviceQ4.__new__(mtp.DeviceQ4)
+            c.codes, c.scales, c.biases = base.codes.clone(), base.scales.clone(), base.biases.clone()
+            c.n, c.k = base.n, base.k
+            c.desc = mtp.MtpQ4(c.codes.data_ptr(), c.scales.data_ptr(), c.biases.data_ptr(), c.n, c.k)
+            reps.append(c)
+        return reps
+
+    w0, x0 = synth.config0_gemv()
+    c0 = rotated_q4(w0, 683)
+    x = torch.from_numpy(x0).to(dev)
+    y = torch.empty((1, w0.n), dtype=torch.float32, device=dev)
+    us = event_us(torch, dev, lambda i: mtp.mtp_qgemv(c0[i % len(c0)], x, y=y), n, W)
+    b = c0[0].nbytes + 2 * 1024 * 4
+    out["qgemv_1024x1024_m1"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+    del c0
+    torch.cuda.empty_cache()
+
+    e, h, ge, gh, w1 = synth.config1_proj()
+    c1 = rotated_q4(w1, 86)
+    de, dh = torch.from_numpy(e).to(dev), torch.from_numpy(h).to(dev)
+    dge, dgh = torch.from_numpy(ge).to(dev), torch.from_numpy(gh).to(dev)
+    for m in (1, 4):
+        u = torch.empty((m, w1.n), dtype=torch.float32, device=dev)
+        em, hm = de[:m].contiguous(), dh[:m].contiguous()
+        us = event_us(torch, dev, lambda i: mtp.mtp_norm_concat_proj(em, hm, dge, dgh, 1e-6, c1[i % len(c1)], u=u),
+                      n, W)
+        b = c1[0].nbytes + 2 * 2048 * 4 + m * (2 * 2048 + 2048) * 4
+        out[f"norm_concat_proj_2048x4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+    del c1
+    torch.cuda.empty_cache()
+
+    M = synth.config3_moe(4)
+    copies = []
+    for _ in range(3):  # 3 x 906 MB expert stacks
+        copies.append({k: mtp.DeviceQ8(getattr(M, k), dev)
+                       for k in ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up", "sh_down")})
+    router = torch.from_numpy(M.router).to(dev)
+    xm = torch.from_numpy(M.x).to(dev)
+    ones = torch.ones(2048, device=dev)
+    per_expert = 3 * (512 * 2048 + 512 * 2048 // 32 * 4)
+    for m in (1, 4):
+        xr = xm[:m].contiguous()
+        y = torch.empty((m, 2048), dtype=torch.float32, device=dev)
+        ids = torch.empty((m, M.top_k), dtype=torch.int32, device=dev)
+        gts = torch.empty((m, M.top_k), dtype=torch.float32, device=dev)
+        ws = torch.empty(mtp.mtp_ffn_moe_workspace_size(2048, 256, M.top_k, 512, 512, m), dtype=torch.uint8,
+                         device=dev)
+
+        def call(i, m=m, xr=xr, y=y, ids=ids, gts=gts, ws=ws):
+            c = copies[i % 3]
+            mtp.mtp_ffn_moe_q(xr, None, 1e-6, router, M.top_k, c["gate_exps"], c["up_exps"], c["down_exps"],
+                              c["sh_gate"], c["sh_up"], c["sh_down"], y=y, expert_ids=ids, gates=gts, ws=ws)
+
+        us = event_us(torch, dev, call, n, W)
+        union = len(set(ids.cpu().numpy().ravel().tolist()))
+        b = router.numel() * 4 + (union + 1) * per_expert + m * 2048 * 8
+        out[f"moe_q8_256x8_m{m}"] = {"us": round(us, 3), "experts_touched": union + 1, "bytes": b,
+                                     "GB/s": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def cpu_baseline(S, step_bytes, budget_s):

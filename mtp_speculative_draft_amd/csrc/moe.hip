@@ -15,6 +15,9 @@
 //                  the slot's row gates.
 //   down           quantized GEMV per slot into a per-slot partial.
 //   k_moe_combine  y = residual + sum over slots in slot order.
+// The two slot GEMVs take k_moe_slot (below) when both feature counts are a
+// power-of-two number of groups up to 64 and the shared expert has the
+// routed experts' size; other shapes take the generic GEMV kernel.
 #include <climits>
 #include <cmath>
 
@@ -92,7 +95,10 @@ __global__ void __launch_bounds__(256) k_moe_router(const MoeParams p) {
     }
 }
 
-// One block of 512 threads; wave mi handles row mi.
+// One block of 512 threads; wave mi handles row mi.  Each lane keeps its
+// share of the row's logits (expert lane + 64 j) in registers, so the top-k
+// selection makes no memory round trip.
+constexpr int kTopkPerLane = kMaxE / kWave;
 __global__ void __launch_bounds__(512) k_moe_topk(const MoeParams p) {
     __shared__ int sel[kMaxE];
     __shared__ float gsel[kMaxE][8];
@@ -105,37 +111,46 @@ __global__ void __launch_bounds__(512) k_moe_topk(const MoeParams p) {
     if (wid < p.m) {
         const int mi = wid;
         const float* l = p.logits + (int64_t)mi * p.E;
+        float lv[kTopkPerLane];
+#pragma unroll
+        for (int j = 0; j < kTopkPerLane; ++j) {
+            const int e = lane + kWave * j;
+            lv[j] = e < p.E ? l[e] : -INFINITY;
+        }
         float mx = -INFINITY;
-        for (int e = lane; e < p.E; e += kWave) mx = fmaxf(mx, l[e]);
+#pragma unroll
+        for (int j = 0; j < kTopkPerLane; ++j) mx = fmaxf(mx, lv[j]);
         mx = wave_max(mx);
         // selection on the logits: softmax is monotonic, so the order of p is
         // the order of the logits; ties go to the lower expert index
-        unsigned long long taken = 0;  // bit j: expert lane + 64*j already chosen
-        float psum = 0.0f;
+        unsigned taken = 0;  // bit j: expert lane + 64*j already chosen
+        float psum = 0.0f, my_pe = 0.0f;
+        int my_id = 0;
         for (int s = 0; s < p.top_k; ++s) {
             float bv = -INFINITY;
             int bi = INT_MAX;
-            for (int j = 0, e = lane; e < p.E; ++j, e += kWave)
-                if (!((taken >> j) & 1ull)) argmax_merge(bv, bi, l[e], e);
+#pragma unroll
+            for (int j = 0; j < kTopkPerLane; ++j)
+                if (lane + kWave * j < p.E && !((taken >> j) & 1u)) argmax_merge(bv, bi, lv[j], lane + kWave * j);
             wave_argmax(bv, bi);
-            if (bi == INT_MAX) bi = 0;  // only for non-finite logits
-            if ((bi & (kWave - 1)) == lane) taken |= 1ull << (bi / kWave);
-            const float pe = __expf(l[bi] - mx);
+            if (bi == INT_MAX) {  // only for non-finite logits
+                bi = 0;
+                bv = __shfl(lv[0], 0);
+            }
+            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+            const float pe = __expf(bv - mx);
             psum += pe;
-            if (lane == 0) {
-                p.expert_ids[mi * p.top_k + s] = bi;
-                gsel[bi][mi] = pe;
-                sel[bi] = 1;
+            if (lane == s) {
+                my_id = bi;
+                my_pe = pe;
             }
         }
-        __syncwarp();
-        if (lane == 0) {
-            for (int s = 0; s < p.top_k; ++s) {
-                const int e = p.expert_ids[mi * p.top_k + s];
-                const float gate = gsel[e][mi] / psum;
-                gsel[e][mi] = gate;
-                p.gates[mi * p.top_k + s] = gate;
-            }
+        if (lane < p.top_k) {  // top_k <= 64: lane s holds selection s
+            const float gate = my_pe / psum;
+            p.expert_ids[mi * p.top_k + lane] = my_id;
+            p.gates[mi * p.top_k + lane] = gate;
+            gsel[my_id][mi] = gate;
+            sel[my_id] = 1;
         }
     }
     __syncthreads();
@@ -162,13 +177,241 @@ __global__ void __launch_bounds__(512) k_moe_topk(const MoeParams p) {
     }
 }
 
-__global__ void __launch_bounds__(256) k_moe_combine(const MoeParams p) {
+// y = residual + the slots' partials added one after another in slot order;
+// the partials are requested eight at a time.
+__global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)p.m * p.H) return;
     const int ns = *p.n_slots;
+    const int64_t step = (int64_t)p.m * p.H;
+    const float* src = p.ypart + idx;
     float acc = p.residual ? p.residual[idx] : 0.0f;
-    for (int s = 0; s < ns; ++s) acc += p.ypart[(int64_t)s * p.m * p.H + idx];
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = src[(s + i) * step];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += t[i];
+    }
+    for (; s < ns; ++s) acc += src[s * step];
     p.y[idx] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// k_moe_slot: one 8-bit expert GEMV per slot (grid.y = slot), for K = 32*G
+// features with G a power of two up to 64.
+//
+// Lane mapping: a row's G groups take LG = G consecutive lanes, so one wave
+// load covers RPL = 64/LG rows (lane = rs*LG + g reads 32 code bytes and one
+// scale of row rs, group g); at K = 512 that is four rows of 512 bytes per
+// load instead of one row on a quarter of the lanes.  A "load-set" is those
+// RPL rows (for SwiGLU, the same RPL rows of gate and of up).
+//
+// Activations: the block quantizes its slot's m activation rows once, per
+// group of 32: x ~ xs*(256*hi + lo) with xs = max|x|/32512 of the group, so
+// no lane exchange is needed; the fragments pass through LDS to the lanes of
+// their group.  A row's group term is then (s*xs) * A with A the exact
+// integer dot of the codes with the quantized activations (v_dot4).
+//
+// Work: wave w of block b takes load-sets [(b*W + w)*uw, +uw) of its slot,
+// UB at a time; the next batch's codes are requested before the current one
+// is reduced (a transposed butterfly over the LG lanes of each row) and
+// stored.  The first batch is requested before the activation setup.
+// ---------------------------------------------------------------------------
+struct SlotGemv {
+    const int8_t* codes[2];    // expert stacks [E][N][K] (codes[1]: up, SwiGLU only)
+    const float* scales[2];    // [E][N][K/32]
+    const int8_t* sh_codes[2]; // shared expert [N][K] (NULL when absent)
+    const float* sh_scales[2];
+    int64_t ex_codes, ex_scales;  // per-expert strides: bytes, floats
+    int N, K, m;
+    const float* act;     // [slot][m][K] activations (slot stride act_slot; 0 = shared by all slots)
+    int64_t act_slot;
+    float* out;           // [slot][m][N]
+    int64_t out_slot;
+    const float* slot_gate;  // [slot][m]: SwiGLU output scale (the row's gate of that expert)
+    const int* slot_expert;
+    const int* n_slots;
+    int uw;               // load-sets per wave (a multiple of the batch size)
+};
+
+constexpr int kFragWords = 20;  // hi[8], lo[8], xs, pad (16-byte multiple)
+
+template <int LG>
+__host__ __device__ constexpr int seg_step0() {
+    return LG >= 64 ? 0 : (LG == 32 ? 1 : (LG == 16 ? 2 : (LG == 8 ? 3 : (LG == 4 ? 4 : (LG == 2 ? 5 : 6)))));
+}
+
+// Position of this lane's first value after Butterfly<V, FIN, seg_step0<LG>>.
+template <int V, int FIN, int LG>
+__device__ __forceinline__ int seg_base(int lane) {
+    int base = 0, cur = V;
+#pragma unroll
+    for (int d = LG / 2; d >= 1; d >>= 1) {
+        if (cur > FIN) {
+            cur >>= 1;
+            if (lane & d) base += cur;
+        }
+    }
+    return base;
+}
+
+template <int M>
+__host__ __device__ constexpr int slot_batch() { return M >= 8 ? 2 : 4; }
+
+template <int M, int EPI, int LG, int W>
+__global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
+    constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int RPL = kWave / LG;
+    constexpr int UB = slot_batch<M>();
+    constexpr int V = UB * M * P;
+    constexpr int FIN = (V / LG > P) ? V / LG : P;  // values a lane holds after the reduction
+    constexpr int DUP = LG * FIN / V;               // lanes holding each of them
+    __shared__ __align__(16) unsigned frag[M * LG * kFragWords];
+
+    const int slot = blockIdx.y;
+    if (slot >= *p.n_slots) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int e = p.slot_expert[slot];
+    const int G = LG;  // groups per row
+    const int8_t* cw[2];
+    const float* sw[2];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        cw[i] = e >= 0 ? p.codes[i] + (int64_t)e * p.ex_codes : p.sh_codes[i];
+        sw[i] = e >= 0 ? p.scales[i] + (int64_t)e * p.ex_scales : p.sh_scales[i];
+    }
+    const int g = lane % LG, rs = lane / LG;
+    const int L = (p.N + RPL - 1) / RPL;  // load-sets of the slot
+    const int j_begin = (blockIdx.x * W + wid) * p.uw;
+    const int j_end = min(L, j_begin + p.uw);
+
+    WFrag<FMT_Q8> wf[UB][P];
+    auto load_batch = [&](int j0) {
+#pragma unroll
+        for (int b = 0; b < UB; ++b) {
+            int n = (j0 + b) * RPL + rs;
+            n = n < p.N ? n : p.N - 1;
+#pragma unroll
+            for (int i = 0; i < P; ++i) load_frag(wf[b][i], cw[i], sw[i], nullptr, n, G, g);
+        }
+    };
+    if (j_begin < j_end) load_batch(j_begin);
+
+    // activation setup: (row, group) pairs over the block's threads
+    const float* act = p.act + (int64_t)slot * p.act_slot;
+    for (int q = threadIdx.x; q < M * G; q += W * kWave) {
+        const int mi = q / G, gg = q % G;
+        float xv[32];
+        unsigned* f = frag + (mi * LG + gg) * kFragWords;
+        if (mi < p.m) {
+            load32(xv, act + (int64_t)mi * p.K + gg * kGroup);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(xv[i]));
+        const float inv = mx > 0.0f ? kQMax / mx : 0.0f;
+        XFrag xf;
+        quantize_group<FMT_Q8>(xv, inv, 0.0f, xf);
+        uint4* f4 = reinterpret_cast<uint4*>(f);
+        f4[0] = make_uint4(xf.hi[0], xf.hi[1], xf.hi[2], xf.hi[3]);
+        f4[1] = make_uint4(xf.hi[4], xf.hi[5], xf.hi[6], xf.hi[7]);
+        f4[2] = make_uint4(xf.lo[0], xf.lo[1], xf.lo[2], xf.lo[3]);
+        f4[3] = make_uint4(xf.lo[4], xf.lo[5], xf.lo[6], xf.lo[7]);
+        f4[4] = make_uint4(__float_as_uint(mx / kQMax), 0u, 0u, 0u);
+    }
+    __syncthreads();
+    if (j_begin >= j_end) return;
+    XFrag xf[M];
+    float xs[M];
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+        const uint4* f4 = reinterpret_cast<const uint4*>(frag + (mi * LG + g) * kFragWords);
+        const uint4 a = f4[0], b = f4[1], c = f4[2], d = f4[3], x = f4[4];
+        xf[mi].hi[0] = a.x; xf[mi].hi[1] = a.y; xf[mi].hi[2] = a.z; xf[mi].hi[3] = a.w;
+        xf[mi].hi[4] = b.x; xf[mi].hi[5] = b.y; xf[mi].hi[6] = b.z; xf[mi].hi[7] = b.w;
+        xf[mi].lo[0] = c.x; xf[mi].lo[1] = c.y; xf[mi].lo[2] = c.z; xf[mi].lo[3] = c.w;
+        xf[mi].lo[4] = d.x; xf[mi].lo[5] = d.y; xf[mi].lo[6] = d.z; xf[mi].lo[7] = d.w;
+        xs[mi] = __uint_as_float(x.x);
+    }
+
+    const int base = seg_base<V, FIN, LG>(lane);
+    const bool writer = (lane & (DUP - 1)) == 0;
+    float* out = p.out + (int64_t)slot * p.out_slot;
+    for (int j0 = j_begin; j0 < j_end; j0 += UB) {
+        float v[V];
+#pragma unroll
+        for (int b = 0; b < UB; ++b)
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+#pragma unroll
+                for (int mi = 0; mi < M; ++mi)
+                    v[(b * M + mi) * P + i] = dot_q8(wf[b][i], xf[mi]) * xs[mi];
+        if (j0 + UB < j_end) load_batch(j0 + UB);  // in flight while this batch is reduced
+        Butterfly<V, FIN, seg_step0<LG>()>::run(v, lane);
+        if (writer) {
+#pragma unroll
+            for (int f = 0; f < FIN; f += P) {
+                const int pos = (base + f) / P;  // = b*M + mi
+                const int b = pos / M, mi = pos % M;
+                const int j = j0 + b;
+                const int n = j * RPL + rs;
+                if (j < j_end && n < p.N && mi < p.m) {
+                    const int64_t o = (int64_t)mi * p.N + n;
+                    if constexpr (EPI == EPI_SWIGLU)
+                        out[o] = silu(v[f]) * v[f + 1] * p.slot_gate[(int64_t)slot * p.m + mi];
+                    else
+                        out[o] = v[f];
+                }
+            }
+        }
+    }
+}
+
+// Kernel of one (rows, epilogue, groups per row) case.
+template <int M, int EPI>
+static hipError_t launch_slot_m(const SlotGemv& p, int G, dim3 grid, hipStream_t st) {
+    constexpr int W = 4;
+    const dim3 block(W * kWave);
+    switch (G) {
+        case 64: hipLaunchKernelGGL((k_moe_slot<M, EPI, 64, W>), grid, block, 0, st, p); break;
+        case 16: hipLaunchKernelGGL((k_moe_slot<M, EPI, 16, W>), grid, block, 0, st, p); break;
+        case 8: hipLaunchKernelGGL((k_moe_slot<M, EPI, 8, W>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((k_moe_slot<M, EPI, 2, W>), grid, block, 0, st, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+static bool slot_groups_ok(int K) {
+    const int G = K / kGroup;
+    return K % kGroup == 0 && (G == 64 || G == 16 || G == 8 || G == 2);
+}
+
+// Load-sets per wave: the smallest multiple of the batch that still leaves
+// about two blocks per compute unit over the launch's slots.
+static hipError_t launch_slot(int epi, SlotGemv p, int max_slots, hipStream_t st) {
+    constexpr int W = 4;
+    const int G = p.K / kGroup, rpl = kWave / G;
+    const int L = (p.N + rpl - 1) / rpl;
+    const int mi = inst_m(p.m);
+    const int ub = mi >= 8 ? slot_batch<8>() : slot_batch<4>();
+    const int target = 2 * device_cu_count();
+    int uw = ub;
+    while (uw < 64 && (int64_t)max_slots * ((L + W * 2 * uw - 1) / (W * 2 * uw)) >= target) uw *= 2;
+    p.uw = uw;
+    const dim3 grid((unsigned)((L + W * uw - 1) / (W * uw)), (unsigned)max_slots);
+    switch (mi) {
+        case 1: return epi == EPI_SWIGLU ? launch_slot_m<1, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<1, EPI_STORE>(p, G, grid, st);
+        case 2: return epi == EPI_SWIGLU ? launch_slot_m<2, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<2, EPI_STORE>(p, G, grid, st);
+        case 4: return epi == EPI_SWIGLU ? launch_slot_m<4, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<4, EPI_STORE>(p, G, grid, st);
+        default: return epi == EPI_SWIGLU ? launch_slot_m<8, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<8, EPI_STORE>(p, G, grid, st);
+    }
 }
 
 hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
@@ -184,6 +427,52 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
     const int64_t ex_sc_gu = (int64_t)p.inter * (p.H / kGroup);
     const int64_t ex_codes_d = (int64_t)p.H * p.inter;
     const int64_t ex_sc_d = (int64_t)p.H * (p.inter / kGroup);
+
+    if (slot_groups_ok(p.H) && slot_groups_ok(p.inter) && (!p.sg.codes || p.sh_inter == p.inter)) {
+        SlotGemv g{};
+        g.codes[0] = static_cast<const int8_t*>(p.ge.codes);
+        g.codes[1] = static_cast<const int8_t*>(p.ue.codes);
+        g.scales[0] = p.ge.scales;
+        g.scales[1] = p.ue.scales;
+        g.sh_codes[0] = static_cast<const int8_t*>(p.sg.codes);
+        g.sh_codes[1] = static_cast<const int8_t*>(p.su.codes);
+        g.sh_scales[0] = p.sg.scales;
+        g.sh_scales[1] = p.su.scales;
+        g.ex_codes = ex_codes_gu;
+        g.ex_scales = ex_sc_gu;
+        g.N = p.inter;
+        g.K = p.H;
+        g.m = p.m;
+        g.act = fin;
+        g.act_slot = 0;
+        g.out = p.z;
+        g.out_slot = (int64_t)p.m * imax;
+        g.slot_gate = p.slot_gate;
+        g.slot_expert = p.slot_expert;
+        g.n_slots = p.n_slots;
+        if ((e = launch_slot(EPI_SWIGLU, g, p.max_slots, st)) != hipSuccess) return e;
+
+        SlotGemv d{};
+        d.codes[0] = static_cast<const int8_t*>(p.de.codes);
+        d.scales[0] = p.de.scales;
+        d.sh_codes[0] = static_cast<const int8_t*>(p.sd.codes);
+        d.sh_scales[0] = p.sd.scales;
+        d.ex_codes = ex_codes_d;
+        d.ex_scales = ex_sc_d;
+        d.N = p.H;
+        d.K = p.inter;
+        d.m = p.m;
+        d.act = p.z;
+        d.act_slot = (int64_t)p.m * imax;
+        d.out = p.ypart;
+        d.out_slot = (int64_t)p.m * p.H;
+        d.slot_expert = p.slot_expert;
+        d.n_slots = p.n_slots;
+        if ((e = launch_slot(EPI_STORE, d, p.max_slots, st)) != hipSuccess) return e;
+        const int64_t n = (int64_t)p.m * p.H;
+        hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
+        return hipGetLastError();
+    }
 
     GemvParams g{};
     g.w[0] = p.ge;
@@ -234,7 +523,7 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
     if ((e = launch_gemv_slots(FMT_Q8, EPI_STORE, p.m, d, shd, p.max_slots, st)) != hipSuccess) return e;
 
     const int64_t n = (int64_t)p.m * p.H;
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 
