@@ -95,10 +95,104 @@ __global__ void __launch_bounds__(256) k_moe_router(const MoeParams p) {
     }
 }
 
-// One block of 512 threads; wave mi handles row mi.  Each lane keeps its
-// share of the row's logits (expert lane + 64 j) in registers, so the top-k
-// selection makes no memory round trip.
+// Top-k of one row of router logits by one wave.  Each lane keeps its share
+// of the row (experts lane + 64 j, j < NJ) in registers as 64-bit keys
+// (order-preserving value bits above the complemented index), so a step of
+// the selection is a branch-free key maximum: per lane, then across the wave.
+// Selection runs on the logits (softmax is monotonic, so the order of p is
+// the order of the logits); equal logits go to the lower expert index (-0 is
+// taken as +0) and NaN is never selected.  Lane s < top_k returns selection
+// s: its expert and its renormalised gate p_e / sum of the selected p.
+__device__ __forceinline__ unsigned long long key_max(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+// One all-reduce step of the key maximum at lane class D.  The permlane
+// swaps leave a lane's own key in one result and its partner's in the other
+// (which one depends on the lane), so both are compared.
+template <int D>
+__device__ __forceinline__ unsigned long long key_step(unsigned long long k) {
+    const unsigned hi = (unsigned)(k >> 32), lo = (unsigned)k;
+    if constexpr (D >= 16) {
+        float h0, h1, l0, l1;
+        swap_halves<D>(__uint_as_float(hi), __uint_as_float(hi), h0, h1);
+        swap_halves<D>(__uint_as_float(lo), __uint_as_float(lo), l0, l1);
+        const unsigned long long k0 = ((unsigned long long)__float_as_uint(h0) << 32) | __float_as_uint(l0);
+        const unsigned long long k1 = ((unsigned long long)__float_as_uint(h1) << 32) | __float_as_uint(l1);
+        return key_max(k0, k1);
+    } else {
+        const unsigned ph = (unsigned)dpp_partner<D>((int)hi), pl = (unsigned)dpp_partner<D>((int)lo);
+        return key_max(k, ((unsigned long long)ph << 32) | pl);
+    }
+}
+
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+    k = key_step<32>(k);
+    k = key_step<16>(k);
+    k = key_step<8>(k);
+    k = key_step<4>(k);
+    k = key_step<2>(k);
+    return key_step<1>(k);
+}
+
+// The logit a key was made from (inverse of argmax_key's value bits).
+__device__ __forceinline__ float key_value(unsigned long long k) {
+    const unsigned hi = (unsigned)(k >> 32);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
 constexpr int kTopkPerLane = kMaxE / kWave;
+template <int NJ>
+__device__ __forceinline__ void row_topk_n(const float* l, int E, int top_k, int lane, int& my_id, float& my_gate) {
+    float lv[NJ];
+    unsigned long long key[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + kWave * j;
+        lv[j] = e < E ? l[e] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + kWave * j;
+        mx = fmaxf(mx, lv[j]);
+        const float v = lv[j] + 0.0f;  // -0 -> +0
+        key[j] = (e < E && v == v) ? argmax_key(v, e) : 0ull;
+    }
+    mx = wave_max(mx);
+    float psum = 0.0f, my_pe = 0.0f;
+    my_id = 0;
+    for (int s = 0; s < top_k; ++s) {
+        unsigned long long b = key[0];
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) b = key_max(b, key[j]);
+        b = wave_max_key(b);
+        int bi;
+        float bv;
+        if (b == 0ull) {  // only NaN logits left
+            bi = 0;
+            bv = __shfl(lv[0], 0);
+        } else {
+            bi = argmax_key_index(b);
+            bv = key_value(b);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) key[j] = (lane + kWave * j == bi) ? 0ull : key[j];
+        const float pe = __expf(bv - mx);
+        psum += pe;
+        my_id = (lane == s) ? bi : my_id;
+        my_pe = (lane == s) ? pe : my_pe;
+    }
+    my_gate = my_pe / psum;
+}
+
+__device__ __forceinline__ void row_topk(const float* l, int E, int top_k, int lane, int& my_id, float& my_gate) {
+    if (E <= 4 * kWave)
+        row_topk_n<4>(l, E, top_k, lane, my_id, my_gate);
+    else
+        row_topk_n<kTopkPerLane>(l, E, top_k, lane, my_id, my_gate);
+}
+
+// One block of 512 threads; wave mi handles row mi (top_k <= 64: lane s
+// holds selection s).
 __global__ void __launch_bounds__(512) k_moe_topk(const MoeParams p) {
     __shared__ int sel[kMaxE];
     __shared__ float gsel[kMaxE][8];
@@ -110,43 +204,10 @@ __global__ void __launch_bounds__(512) k_moe_topk(const MoeParams p) {
     __syncthreads();
     if (wid < p.m) {
         const int mi = wid;
-        const float* l = p.logits + (int64_t)mi * p.E;
-        float lv[kTopkPerLane];
-#pragma unroll
-        for (int j = 0; j < kTopkPerLane; ++j) {
-            const int e = lane + kWave * j;
-            lv[j] = e < p.E ? l[e] : -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kTopkPerLane; ++j) mx = fmaxf(mx, lv[j]);
-        mx = wave_max(mx);
-        // selection on the logits: softmax is monotonic, so the order of p is
-        // the order of the logits; ties go to the lower expert index
-        unsigned taken = 0;  // bit j: expert lane + 64*j already chosen
-        float psum = 0.0f, my_pe = 0.0f;
-        int my_id = 0;
-        for (int s = 0; s < p.top_k; ++s) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int j = 0; j < kTopkPerLane; ++j)
-                if (lane + kWave * j < p.E && !((taken >> j) & 1u)) argmax_merge(bv, bi, lv[j], lane + kWave * j);
-            wave_argmax(bv, bi);
-            if (bi == INT_MAX) {  // only for non-finite logits
-                bi = 0;
-                bv = __shfl(lv[0], 0);
-            }
-            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-            const float pe = __expf(bv - mx);
-            psum += pe;
-            if (lane == s) {
-                my_id = bi;
-                my_pe = pe;
-            }
-        }
-        if (lane < p.top_k) {  // top_k <= 64: lane s holds selection s
-            const float gate = my_pe / psum;
+        int my_id;
+        float gate;
+        row_topk(p.logits + (int64_t)mi * p.E, p.E, p.top_k, lane, my_id, gate);
+        if (lane < p.top_k) {
             p.expert_ids[mi * p.top_k + lane] = my_id;
             p.gates[mi * p.top_k + lane] = gate;
             gsel[my_id][mi] = gate;
@@ -234,6 +295,18 @@ struct SlotGemv {
     const int* slot_expert;
     const int* n_slots;
     int uw;               // load-sets per wave (a multiple of the batch size)
+    // Routing in the gate/up launch: when logits ([m][E] router logits) is
+    // set, every block selects the experts itself, so no launch sits between
+    // the router and the experts.  Slot j < n_routed is the j-th selected
+    // expert in ascending order, slot n_routed the shared expert when
+    // has_shared.  Block (0, 0) publishes the slot table and count (read by
+    // the down and combine launches) and the per-row selections.
+    const float* logits;
+    int E, top_k, has_shared;
+    int* slot_expert_out;
+    int* n_slots_out;
+    int* expert_ids_out;
+    float* gates_out;
 };
 
 constexpr int kFragWords = 20;  // hi[8], lo[8], xs, pad (16-byte multiple)
@@ -257,8 +330,100 @@ __device__ __forceinline__ int seg_base(int lane) {
     return base;
 }
 
+// The block's routing (see SlotGemv): returns in *s_e the slot's expert (-1
+// the shared expert, -2 no such slot) and in s_gate[mi] row mi's gate for it.
+template <int W>
+__device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane, int wid,
+                                           unsigned long long* selmask, int (*rid)[kWave], float (*rgate)[kWave],
+                                           int* s_e, float* s_gate) {
+    const int words = (p.E + kWave - 1) / kWave;
+    const bool publish = blockIdx.x == 0 && slot == 0;
+    if ((int)threadIdx.x < words) selmask[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int mi = wid; mi < p.m; mi += W) {
+        int id;
+        float gate;
+        row_topk(p.logits + (int64_t)mi * p.E, p.E, p.top_k, lane, id, gate);
+        if (lane < p.top_k) {
+            rid[mi][lane] = id;
+            rgate[mi][lane] = gate;
+            atomicOr(&selmask[id / kWave], 1ull << (id % kWave));
+            if (publish) {
+                p.expert_ids_out[mi * p.top_k + lane] = id;
+                p.gates_out[mi * p.top_k + lane] = gate;
+            }
+        }
+    }
+    __syncthreads();
+    if (wid != 0) return;
+    // lane w < words owns mask word w; its experts take the slots after those
+    // of the words before it
+    const unsigned long long mw = lane < words ? selmask[lane] : 0ull;
+    const int c = __popcll(mw);
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    const int excl = incl - c;
+    const int n_routed = __shfl(incl, kWave - 1);
+    const int n_slots = n_routed + p.has_shared;
+    if (publish) {
+        int idx = excl;
+        for (unsigned long long b = mw; b; b &= b - 1ull) p.slot_expert_out[idx++] = lane * kWave + __ffsll((long long)b) - 1;
+        if (lane == 0) {
+            if (p.has_shared) p.slot_expert_out[n_routed] = -1;
+            *p.n_slots_out = n_slots;
+        }
+    }
+    int e;
+    if (slot < n_routed) {
+        const bool mine = lane < words && slot >= excl && slot < incl;
+        int cand = 0;
+        if (mine) {
+            unsigned long long b = mw;
+            for (int k = slot - excl; k > 0; --k) b &= b - 1ull;
+            cand = lane * kWave + __ffsll((long long)b) - 1;
+        }
+        const unsigned long long who = __ballot(mine);
+        e = __shfl(cand, __ffsll((long long)who) - 1);
+    } else {
+        e = slot < n_slots ? -1 : -2;
+    }
+    for (int mi = 0; mi < p.m; ++mi) {
+        float gate = 1.0f;
+        if (e >= 0) {
+            const bool hit = lane < p.top_k && rid[mi][lane] == e;
+            const unsigned long long hm = __ballot(hit);
+            const float g = lane < p.top_k ? rgate[mi][lane] : 0.0f;
+            gate = hm ? __shfl(g, __ffsll((long long)hm) - 1) : 0.0f;
+        }
+        if (lane == 0) s_gate[mi] = gate;
+    }
+    if (lane == 0) *s_e = e;
+}
+
+// Load-sets per batch; two batches are in flight per wave.
 template <int M>
-__host__ __device__ constexpr int slot_batch() { return M >= 8 ? 2 : 4; }
+__host__ __device__ constexpr int slot_batch() { return M >= 8 ? 1 : 2; }
+
+// One (row, group) activation fragment of the block's slot: 32 values
+// quantized with their own scale, written to LDS as hi[8], lo[8], xs.
+__device__ __forceinline__ void store_frag(unsigned* f, const float (&xv)[32]) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(xv[i]));
+    const float inv = mx > 0.0f ? kQMax / mx : 0.0f;
+    XFrag xf;
+    quantize_group<FMT_Q8>(xv, inv, 0.0f, xf);
+    uint4* f4 = reinterpret_cast<uint4*>(f);
+    f4[0] = make_uint4(xf.hi[0], xf.hi[1], xf.hi[2], xf.hi[3]);
+    f4[1] = make_uint4(xf.hi[4], xf.hi[5], xf.hi[6], xf.hi[7]);
+    f4[2] = make_uint4(xf.lo[0], xf.lo[1], xf.lo[2], xf.lo[3]);
+    f4[3] = make_uint4(xf.lo[4], xf.lo[5], xf.lo[6], xf.lo[7]);
+    f4[4] = make_uint4(__float_as_uint(mx / kQMax), 0u, 0u, 0u);
+}
 
 template <int M, int EPI, int LG, int W>
 __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
@@ -268,14 +433,43 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     constexpr int V = UB * M * P;
     constexpr int FIN = (V / LG > P) ? V / LG : P;  // values a lane holds after the reduction
     constexpr int DUP = LG * FIN / V;               // lanes holding each of them
+    constexpr int RT = (EPI == EPI_SWIGLU) ? 8 : 1;  // routing state rows (gate/up launch only)
     __shared__ __align__(16) unsigned frag[M * LG * kFragWords];
+    __shared__ unsigned long long selmask[kMaxE / kWave];
+    __shared__ int rid[RT][kWave];
+    __shared__ float rgate[RT][kWave];
+    __shared__ int s_e;
+    __shared__ float s_gate[8];
 
     const int slot = blockIdx.y;
-    if (slot >= *p.n_slots) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int e = p.slot_expert[slot];
+    const bool route = EPI == EPI_SWIGLU && p.logits != nullptr;
     const int G = LG;  // groups per row
+
+    // the first activation pair of this thread is requested before the
+    // routing / slot lookup, whose memory latency it then shares
+    const float* act = p.act + (int64_t)slot * p.act_slot;
+    const int q0 = threadIdx.x;
+    const bool has_q0 = q0 < M * G && q0 / G < p.m;
+    float xv0[32];
+    if (has_q0) {
+        load32(xv0, act + (int64_t)(q0 / G) * p.K + (q0 % G) * kGroup);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xv0[i] = 0.0f;
+    }
+
+    int e;
+    if (route) {
+        if constexpr (EPI == EPI_SWIGLU) route_slot<W>(p, slot, lane, wid, selmask, rid, rgate, &s_e, s_gate);
+        __syncthreads();
+        e = s_e;
+        if (e == -2) return;
+    } else {
+        if (slot >= *p.n_slots) return;
+        e = p.slot_expert[slot];
+    }
     const int8_t* cw[2];
     const float* sw[2];
 #pragma unroll
@@ -288,8 +482,8 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     const int j_begin = (blockIdx.x * W + wid) * p.uw;
     const int j_end = min(L, j_begin + p.uw);
 
-    WFrag<FMT_Q8> wf[UB][P];
-    auto load_batch = [&](int j0) {
+    WFrag<FMT_Q8> wa[UB][P], wb[UB][P];
+    auto load_batch = [&](WFrag<FMT_Q8> (&wf)[UB][P], int j0) {
 #pragma unroll
         for (int b = 0; b < UB; ++b) {
             int n = (j0 + b) * RPL + rs;
@@ -298,32 +492,22 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
             for (int i = 0; i < P; ++i) load_frag(wf[b][i], cw[i], sw[i], nullptr, n, G, g);
         }
     };
-    if (j_begin < j_end) load_batch(j_begin);
+    // two batches in flight from the start
+    if (j_begin < j_end) load_batch(wa, j_begin);
+    if (j_begin + UB < j_end) load_batch(wb, j_begin + UB);
 
     // activation setup: (row, group) pairs over the block's threads
-    const float* act = p.act + (int64_t)slot * p.act_slot;
-    for (int q = threadIdx.x; q < M * G; q += W * kWave) {
+    if (q0 < M * G) store_frag(frag + ((q0 / G) * LG + q0 % G) * kFragWords, xv0);
+    for (int q = q0 + W * kWave; q < M * G; q += W * kWave) {
         const int mi = q / G, gg = q % G;
         float xv[32];
-        unsigned* f = frag + (mi * LG + gg) * kFragWords;
         if (mi < p.m) {
             load32(xv, act + (int64_t)mi * p.K + gg * kGroup);
         } else {
 #pragma unroll
             for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
         }
-        float mx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(xv[i]));
-        const float inv = mx > 0.0f ? kQMax / mx : 0.0f;
-        XFrag xf;
-        quantize_group<FMT_Q8>(xv, inv, 0.0f, xf);
-        uint4* f4 = reinterpret_cast<uint4*>(f);
-        f4[0] = make_uint4(xf.hi[0], xf.hi[1], xf.hi[2], xf.hi[3]);
-        f4[1] = make_uint4(xf.hi[4], xf.hi[5], xf.hi[6], xf.hi[7]);
-        f4[2] = make_uint4(xf.lo[0], xf.lo[1], xf.lo[2], xf.lo[3]);
-        f4[3] = make_uint4(xf.lo[4], xf.lo[5], xf.lo[6], xf.lo[7]);
-        f4[4] = make_uint4(__float_as_uint(mx / kQMax), 0u, 0u, 0u);
+        store_frag(frag + (mi * LG + gg) * kFragWords, xv);
     }
     __syncthreads();
     if (j_begin >= j_end) return;
@@ -343,16 +527,17 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     const int base = seg_base<V, FIN, LG>(lane);
     const bool writer = (lane & (DUP - 1)) == 0;
     float* out = p.out + (int64_t)slot * p.out_slot;
-    for (int j0 = j_begin; j0 < j_end; j0 += UB) {
-        float v[V];
+    // dot products of one batch, then (after the caller's next request) the
+    // reduction over the row's lanes and the epilogue
+    auto dots = [&](const WFrag<FMT_Q8> (&wf)[UB][P], float (&v)[V]) {
 #pragma unroll
         for (int b = 0; b < UB; ++b)
 #pragma unroll
             for (int i = 0; i < P; ++i)
 #pragma unroll
-                for (int mi = 0; mi < M; ++mi)
-                    v[(b * M + mi) * P + i] = dot_q8(wf[b][i], xf[mi]) * xs[mi];
-        if (j0 + UB < j_end) load_batch(j0 + UB);  // in flight while this batch is reduced
+                for (int mi = 0; mi < M; ++mi) v[(b * M + mi) * P + i] = dot_q8(wf[b][i], xf[mi]) * xs[mi];
+    };
+    auto finish = [&](float (&v)[V], int j0) {
         Butterfly<V, FIN, seg_step0<LG>()>::run(v, lane);
         if (writer) {
 #pragma unroll
@@ -364,28 +549,71 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
                 if (j < j_end && n < p.N && mi < p.m) {
                     const int64_t o = (int64_t)mi * p.N + n;
                     if constexpr (EPI == EPI_SWIGLU)
-                        out[o] = silu(v[f]) * v[f + 1] * p.slot_gate[(int64_t)slot * p.m + mi];
+                        out[o] = silu(v[f]) * v[f + 1] * (route ? s_gate[mi] : p.slot_gate[(int64_t)slot * p.m + mi]);
                     else
                         out[o] = v[f];
                 }
             }
         }
+    };
+    for (int j0 = j_begin; j0 < j_end; j0 += 2 * UB) {
+        {
+            float v[V];
+            dots(wa, v);
+            if (j0 + 2 * UB < j_end) load_batch(wa, j0 + 2 * UB);
+            finish(v, j0);
+        }
+        if (j0 + UB >= j_end) break;
+        {
+            float v[V];
+            dots(wb, v);
+            if (j0 + 3 * UB < j_end) load_batch(wb, j0 + 3 * UB);
+            finish(v, j0 + UB);
+        }
     }
 }
 
-// Kernel of one (rows, epilogue, groups per row) case.
-template <int M, int EPI>
-static hipError_t launch_slot_m(const SlotGemv& p, int G, dim3 grid, hipStream_t st) {
+// Resident blocks per compute unit of one kernel (from its registers and
+// LDS), asked once.
+template <int M, int EPI, int LG, int W>
+static int slot_blocks_per_cu() {
+    static int cached = 0;
+    if (!cached) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_moe_slot<M, EPI, LG, W>, W * kWave, 0) != hipSuccess || n < 1)
+            n = 1;
+        cached = n;
+    }
+    return cached;
+}
+
+// Load-sets per wave: the smallest multiple of the batch for which the grid
+// (max_slots rows of blocks) is resident at once, so that no block waits for
+// a second round.
+template <int M, int EPI, int LG>
+static hipError_t launch_slot_g(SlotGemv p, int max_slots, hipStream_t st) {
     constexpr int W = 4;
-    const dim3 block(W * kWave);
-    switch (G) {
-        case 64: hipLaunchKernelGGL((k_moe_slot<M, EPI, 64, W>), grid, block, 0, st, p); break;
-        case 16: hipLaunchKernelGGL((k_moe_slot<M, EPI, 16, W>), grid, block, 0, st, p); break;
-        case 8: hipLaunchKernelGGL((k_moe_slot<M, EPI, 8, W>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((k_moe_slot<M, EPI, 2, W>), grid, block, 0, st, p); break;
+    constexpr int RPL = kWave / LG;
+    constexpr int UB = slot_batch<M>();
+    const int L = (p.N + RPL - 1) / RPL;
+    const int64_t cap = (int64_t)device_cu_count() * slot_blocks_per_cu<M, EPI, LG, W>();
+    int uw = UB;
+    while ((int64_t)max_slots * ((L + W * uw - 1) / (W * uw)) > cap && W * uw < L) uw += UB;
+    p.uw = uw;
+    const dim3 grid((unsigned)((L + W * uw - 1) / (W * uw)), (unsigned)max_slots);
+    hipLaunchKernelGGL((k_moe_slot<M, EPI, LG, W>), grid, dim3(W * kWave), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int M, int EPI>
+static hipError_t launch_slot_m(const SlotGemv& p, int max_slots, hipStream_t st) {
+    switch (p.K / kGroup) {
+        case 64: return launch_slot_g<M, EPI, 64>(p, max_slots, st);
+        case 16: return launch_slot_g<M, EPI, 16>(p, max_slots, st);
+        case 8: return launch_slot_g<M, EPI, 8>(p, max_slots, st);
+        case 2: return launch_slot_g<M, EPI, 2>(p, max_slots, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 static bool slot_groups_ok(int K) {
@@ -393,24 +621,12 @@ static bool slot_groups_ok(int K) {
     return K % kGroup == 0 && (G == 64 || G == 16 || G == 8 || G == 2);
 }
 
-// Load-sets per wave: the smallest multiple of the batch that still leaves
-// about two blocks per compute unit over the launch's slots.
-static hipError_t launch_slot(int epi, SlotGemv p, int max_slots, hipStream_t st) {
-    constexpr int W = 4;
-    const int G = p.K / kGroup, rpl = kWave / G;
-    const int L = (p.N + rpl - 1) / rpl;
-    const int mi = inst_m(p.m);
-    const int ub = mi >= 8 ? slot_batch<8>() : slot_batch<4>();
-    const int target = 2 * device_cu_count();
-    int uw = ub;
-    while (uw < 64 && (int64_t)max_slots * ((L + W * 2 * uw - 1) / (W * 2 * uw)) >= target) uw *= 2;
-    p.uw = uw;
-    const dim3 grid((unsigned)((L + W * uw - 1) / (W * uw)), (unsigned)max_slots);
-    switch (mi) {
-        case 1: return epi == EPI_SWIGLU ? launch_slot_m<1, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<1, EPI_STORE>(p, G, grid, st);
-        case 2: return epi == EPI_SWIGLU ? launch_slot_m<2, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<2, EPI_STORE>(p, G, grid, st);
-        case 4: return epi == EPI_SWIGLU ? launch_slot_m<4, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<4, EPI_STORE>(p, G, grid, st);
-        default: return epi == EPI_SWIGLU ? launch_slot_m<8, EPI_SWIGLU>(p, G, grid, st) : launch_slot_m<8, EPI_STORE>(p, G, grid, st);
+static hipError_t launch_slot(int epi, const SlotGemv& p, int max_slots, hipStream_t st) {
+    switch (inst_m(p.m)) {
+        case 1: return epi == EPI_SWIGLU ? launch_slot_m<1, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<1, EPI_STORE>(p, max_slots, st);
+        case 2: return epi == EPI_SWIGLU ? launch_slot_m<2, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<2, EPI_STORE>(p, max_slots, st);
+        case 4: return epi == EPI_SWIGLU ? launch_slot_m<4, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<4, EPI_STORE>(p, max_slots, st);
+        default: return epi == EPI_SWIGLU ? launch_slot_m<8, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<8, EPI_STORE>(p, max_slots, st);
     }
 }
 
@@ -418,8 +634,11 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
     hipLaunchKernelGGL(k_moe_router, dim3(p.E), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_moe_topk, dim3(1), dim3(512), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const bool slot_path = slot_groups_ok(p.H) && slot_groups_ok(p.inter) && (!p.sg.codes || p.sh_inter == p.inter);
+    if (!slot_path) {
+        hipLaunchKernelGGL(k_moe_topk, dim3(1), dim3(512), 0, st, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     const float* fin = p.gamma ? p.f : p.x;
     const int imax = p.inter > p.sh_inter ? p.inter : p.sh_inter;
@@ -428,7 +647,7 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
     const int64_t ex_codes_d = (int64_t)p.H * p.inter;
     const int64_t ex_sc_d = (int64_t)p.H * (p.inter / kGroup);
 
-    if (slot_groups_ok(p.H) && slot_groups_ok(p.inter) && (!p.sg.codes || p.sh_inter == p.inter)) {
+    if (slot_path) {
         SlotGemv g{};
         g.codes[0] = static_cast<const int8_t*>(p.ge.codes);
         g.codes[1] = static_cast<const int8_t*>(p.ue.codes);
@@ -447,9 +666,14 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
         g.act_slot = 0;
         g.out = p.z;
         g.out_slot = (int64_t)p.m * imax;
-        g.slot_gate = p.slot_gate;
-        g.slot_expert = p.slot_expert;
-        g.n_slots = p.n_slots;
+        g.logits = p.logits;
+        g.E = p.E;
+        g.top_k = p.top_k;
+        g.has_shared = p.sg.codes ? 1 : 0;
+        g.slot_expert_out = p.slot_expert;
+        g.n_slots_out = p.n_slots;
+        g.expert_ids_out = p.expert_ids;
+        g.gates_out = p.gates;
         if ((e = launch_slot(EPI_SWIGLU, g, p.max_slots, st)) != hipSuccess) return e;
 
         SlotGemv d{};
