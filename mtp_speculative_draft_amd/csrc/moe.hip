@@ -275,10 +275,11 @@ __global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
 // their group.  A row's group term is then (s*xs) * A with A the exact
 // integer dot of the codes with the quantized activations (v_dot4).
 //
-// Work: wave w of block b takes load-sets [(b*W + w)*uw, +uw) of its slot,
-// UB at a time; the next batch's codes are requested before the current one
-// is reduced (a transposed butterfly over the LG lanes of each row) and
-// stored.  The first batch is requested before the activation setup.
+// Work: a slot's load-sets, UB at a time (a batch), are spread evenly over
+// the waves of its gridDim.x blocks; two batches are in flight per wave, the
+// next one requested before the current one is reduced (a transposed
+// butterfly over the LG lanes of each row) and stored.  The first two are
+// requested before the activation setup.
 // ---------------------------------------------------------------------------
 struct SlotGemv {
     const int8_t* codes[2];    // expert stacks [E][N][K] (codes[1]: up, SwiGLU only)
@@ -294,7 +295,6 @@ struct SlotGemv {
     const float* slot_gate;  // [slot][m]: SwiGLU output scale (the row's gate of that expert)
     const int* slot_expert;
     const int* n_slots;
-    int uw;               // load-sets per wave (a multiple of the batch size)
     // Routing in the gate/up launch: when logits ([m][E] router logits) is
     // set, every block selects the experts itself, so no launch sits between
     // the router and the experts.  Slot j < n_routed is the j-th selected
@@ -479,8 +479,10 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     }
     const int g = lane % LG, rs = lane / LG;
     const int L = (p.N + RPL - 1) / RPL;  // load-sets of the slot
-    const int j_begin = (blockIdx.x * W + wid) * p.uw;
-    const int j_end = min(L, j_begin + p.uw);
+    // the slot's batches are spread evenly over its gridDim.x * W waves
+    const int U = (L + UB - 1) / UB, NW = gridDim.x * W, wv = blockIdx.x * W + wid;
+    const int j_begin = UB * (int)((int64_t)wv * U / NW);
+    const int j_end = min(L, UB * (int)((int64_t)(wv + 1) * U / NW));
 
     WFrag<FMT_Q8> wa[UB][P], wb[UB][P];
     auto load_batch = [&](WFrag<FMT_Q8> (&wf)[UB][P], int j0) {
@@ -587,20 +589,22 @@ static int slot_blocks_per_cu() {
     return cached;
 }
 
-// Load-sets per wave: the smallest multiple of the batch for which the grid
-// (max_slots rows of blocks) is resident at once, so that no block waits for
-// a second round.
+// Blocks per slot: as many as fill the resident capacity over the launch's
+// slots (so no block waits for a second round and compute units carry equal
+// shares), at most one per wave's batch.
 template <int M, int EPI, int LG>
-static hipError_t launch_slot_g(SlotGemv p, int max_slots, hipStream_t st) {
+static hipError_t launch_slot_g(const SlotGemv& p, int max_slots, hipStream_t st) {
     constexpr int W = 4;
     constexpr int RPL = kWave / LG;
     constexpr int UB = slot_batch<M>();
     const int L = (p.N + RPL - 1) / RPL;
-    const int64_t cap = (int64_t)device_cu_count() * slot_blocks_per_cu<M, EPI, LG, W>();
-    int uw = UB;
-    while ((int64_t)max_slots * ((L + W * uw - 1) / (W * uw)) > cap && W * uw < L) uw += UB;
-    p.uw = uw;
-    const dim3 grid((unsigned)((L + W * uw - 1) / (W * uw)), (unsigned)max_slots);
+    const int U = (L + UB - 1) / UB;
+    const int cap = device_cu_count() * slot_blocks_per_cu<M, EPI, LG, W>();
+    int per_slot = cap / max_slots;
+    per_slot = per_slot < 1 ? 1 : per_slot;
+    const int most = (U + W - 1) / W;
+    per_slot = per_slot > most ? most : per_slot;
+    const dim3 grid((unsigned)per_slot, (unsigned)max_slots);
     hipLaunchKernelGGL((k_moe_slot<M, EPI, LG, W>), grid, dim3(W * kWave), 0, st, p);
     return hipGetLastError();
 }
