@@ -100,6 +100,13 @@ class DenseLayer:
     up: Q4
     down: Q4
     lm_head: Q4
+    # attention variant ([mtp.rs] `forward_full_attention`): per-head q/k
+    # RMSNorm weights [head_dim], a gated q projection (per head: q rows then
+    # gate rows) and a partial rotary dimension (0 = head_dim)
+    gamma_q_head: Optional[np.ndarray] = None
+    gamma_k_head: Optional[np.ndarray] = None
+    q_gated: bool = False
+    rotary_dim: int = 0
 
     def q4_weights(self):
         return [self.eh_proj, self.wq, self.wk, self.wv, self.wo, self.gate, self.up, self.down, self.lm_head]
@@ -168,12 +175,14 @@ def gamma(g: np.random.Generator, h: int) -> np.ndarray:
 
 def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n_kv_heads: int = 2,
                 head_dim: int = 128, vocab: int = 151936, ffn_inter: int = 6144,
-                rope_theta: float = 1.0e6, eps: float = 1e-6) -> DenseLayer:
-    """Dense MTP draft layer with 4-bit weights (draw order fixed)."""
+                rope_theta: float = 1.0e6, eps: float = 1e-6, q_gated: bool = False, qk_norm: bool = False,
+                rotary_dim: int = 0) -> DenseLayer:
+    """Dense MTP draft layer with 4-bit weights (draw order fixed; the
+    attention variant's head norm weights are drawn last)."""
     H = hidden
     gam = [gamma(g, H) for _ in range(5)]
     eh = q4_weight(g, H, 2 * H)
-    wq = q4_weight(g, n_heads * head_dim, H)
+    wq = q4_weight(g, (2 if q_gated else 1) * n_heads * head_dim, H)
     wk = q4_weight(g, n_kv_heads * head_dim, H)
     wv = q4_weight(g, n_kv_heads * head_dim, H)
     wo = q4_weight(g, H, n_heads * head_dim)
@@ -181,8 +190,11 @@ def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n
     up = q4_weight(g, ffn_inter, H)
     down = q4_weight(g, H, ffn_inter)
     lm = q4_weight(g, vocab, H)
+    gq = gamma(g, head_dim) if qk_norm else None
+    gk = gamma(g, head_dim) if qk_norm else None
     return DenseLayer(H, n_heads, n_kv_heads, head_dim, vocab, ffn_inter, float(rope_theta), float(eps),
-                      gam[0], gam[1], gam[2], gam[3], gam[4], eh, wq, wk, wv, wo, gate, up, down, lm)
+                      gam[0], gam[1], gam[2], gam[3], gam[4], eh, wq, wk, wv, wo, gate, up, down, lm,
+                      gq, gk, bool(q_gated), int(rotary_dim))
 
 
 def kv_cache(g: np.random.Generator, n_kv_heads: int, filled: int, capacity: int, head_dim: int):

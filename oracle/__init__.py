@@ -51,7 +51,9 @@ class _Layer(C.Structure):
                 ("gamma_e", C.c_void_p), ("gamma_h", C.c_void_p), ("gamma_attn", C.c_void_p),
                 ("gamma_post", C.c_void_p), ("gamma_final", C.c_void_p),
                 ("eh_proj", _Q4), ("wq", _Q4), ("wk", _Q4), ("wv", _Q4), ("wo", _Q4),
-                ("gate", _Q4), ("up", _Q4), ("down", _Q4), ("lm_head", _Q4)]
+                ("gate", _Q4), ("up", _Q4), ("down", _Q4), ("lm_head", _Q4),
+                ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
+                ("q_gated", C.c_int32), ("rotary_dim", C.c_int32)]
 
 
 def lib():
@@ -69,6 +71,7 @@ def lib():
             "orc_gemv_f32": (None, [P, I, I, P, I, P]),
             "orc_rmsnorm": (None, [P, P, I, I, C.c_float, P]),
             "orc_rope": (None, [P, I, I, I, I, C.c_double]),
+            "orc_rope_partial": (None, [P, I, I, I, I, I, C.c_double]),
             "orc_sdpa": (None, [P, P, P, I, I, I, I, I, I, P]),
             "orc_argmax": (I, [P, I]),
             "orc_norm_concat_proj": (None, [P, P, P, P, C.c_float, P, I, P]),
@@ -129,11 +132,14 @@ def _q8_list(w, keep: _Keep):
 
 def _layer(L, keep: _Keep) -> _Layer:
     f = lambda a: keep.arr(a, np.float32).ctypes.data  # noqa: E731
+    opt = lambda a: None if a is None else f(a)  # noqa: E731
     return _Layer(L.hidden, L.n_heads, L.n_kv_heads, L.head_dim, L.vocab, L.ffn_inter,
                   float(L.rope_theta), float(L.eps),
                   f(L.gamma_e), f(L.gamma_h), f(L.gamma_attn), f(L.gamma_post), f(L.gamma_final),
                   _q4(L.eh_proj, keep), _q4(L.wq, keep), _q4(L.wk, keep), _q4(L.wv, keep), _q4(L.wo, keep),
-                  _q4(L.gate, keep), _q4(L.up, keep), _q4(L.down, keep), _q4(L.lm_head, keep))
+                  _q4(L.gate, keep), _q4(L.up, keep), _q4(L.down, keep), _q4(L.lm_head, keep),
+                  opt(getattr(L, "gamma_q_head", None)), opt(getattr(L, "gamma_k_head", None)),
+                  int(bool(getattr(L, "q_gated", False))), int(getattr(L, "rotary_dim", 0) or 0))
 
 
 # --------------------------------------------------------------------------
@@ -197,9 +203,12 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     return y
 
 
-def rope(x: np.ndarray, n_heads: int, head_dim: int, pos0: int, theta: float) -> np.ndarray:
+def rope(x: np.ndarray, n_heads: int, head_dim: int, pos0: int, theta: float, rotary_dim: int = 0) -> np.ndarray:
     y = np.array(np.atleast_2d(x), dtype=np.float32, copy=True, order="C")
-    lib().orc_rope(_p(y), y.shape[0], n_heads, head_dim, pos0, float(theta))
+    if rotary_dim and rotary_dim != head_dim:
+        lib().orc_rope_partial(_p(y), y.shape[0], n_heads, head_dim, int(rotary_dim), pos0, float(theta))
+    else:
+        lib().orc_rope(_p(y), y.shape[0], n_heads, head_dim, pos0, float(theta))
     return y
 
 

@@ -133,18 +133,22 @@ void orc_rmsnorm(const float* x, const float* gamma, int32_t m, int32_t h, float
     }
 }
 
-/* Rotary embedding over the full head dimension with half-split pairs
- * (i, i + d/2) and inverse frequency theta^(-2i/d); row r sits at position
- * pos0 + r.  [mtp.rs] `forward_full_attention` applies it to q and k after
- * the projections; with text-only positions all rope sections share one id. */
-void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t pos0, double theta) {
-    const int32_t half = head_dim / 2;
+/* Rotary embedding of the first rotary_dim dims of every head with
+ * half-split pairs (i, i + rotary_dim/2) and inverse frequency
+ * theta^(-2i/rotary_dim); the dims from rotary_dim on pass unchanged; row r
+ * sits at position pos0 + r.  [mtp.rs] `forward_full_attention` applies it
+ * (`apply_imrope`, with `rotary_dim`) to q and k after the projections; with
+ * text-only positions all rope sections share one id, so the sections do not
+ * change the angles. */
+void orc_rope_partial(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t rotary_dim, int32_t pos0,
+                      double theta) {
+    const int32_t half = rotary_dim / 2;
     for (int32_t r = 0; r < m; ++r) {
         double pos = (double)(pos0 + r);
         for (int32_t hh = 0; hh < n_heads; ++hh) {
             float* v = x + ((size_t)r * n_heads + hh) * head_dim;
             for (int32_t i = 0; i < half; ++i) {
-                double inv_freq = pow(theta, -2.0 * (double)i / (double)head_dim);
+                double inv_freq = pow(theta, -2.0 * (double)i / (double)rotary_dim);
                 double ang = pos * inv_freq;
                 double c = cos(ang), s = sin(ang);
                 double a = v[i], b = v[i + half];
@@ -153,6 +157,11 @@ void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t po
             }
         }
     }
+}
+
+/* The same over the full head dimension. */
+void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t pos0, double theta) {
+    orc_rope_partial(x, m, n_heads, head_dim, head_dim, pos0, theta);
 }
 
 /* Causal grouped-query attention over the cache ([mtp.rs]
@@ -238,22 +247,38 @@ void orc_norm_concat_proj(const float* e, const float* h, const float* gamma_e, 
  * xa = rms(u; gamma_attn).  The m new K/V rows are written into the caches
  * at rows cache_len .. cache_len+m-1 before the attention reads them
  * ([mtp.rs] `forward_full_attention`; the residual add is the first half of
- * `forward_ffn_residual`'s fused residual norm). */
+ * `forward_ffn_residual`'s fused residual norm).  The optional variant steps
+ * (see orc_layer) follow that function's order: q (and gate) projection, k
+ * and v projections, per-head q and k norms, rotary step, attention, sigmoid
+ * gate, wo. */
 void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_cache,
                    int32_t cache_len, int32_t capacity, int32_t m, float* r1) {
     const int32_t H = L->hidden, d = L->head_dim, nh = L->n_heads, nkv = L->n_kv_heads;
+    const int32_t qrows = (L->q_gated ? 2 : 1) * nh * d;
+    const int32_t rot = L->rotary_dim > 0 ? L->rotary_dim : d;
     float* xa = (float*)xmalloc(sizeof(float) * (size_t)m * H);
+    float* qg = (float*)xmalloc(sizeof(float) * (size_t)m * qrows);
     float* q = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
+    float* gate = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
     float* k = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
     float* v = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
     float* o = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
     float* a = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     orc_rmsnorm(u, L->gamma_attn, m, H, L->eps, xa);
-    orc_gemv4(&L->wq, xa, m, q);
+    orc_gemv4(&L->wq, xa, m, qg);
+    for (int32_t r = 0; r < m; ++r)
+        for (int32_t hh = 0; hh < nh; ++hh) {
+            const float* src = qg + (size_t)r * qrows + (size_t)hh * (L->q_gated ? 2 * d : d);
+            memcpy(q + ((size_t)r * nh + hh) * d, src, sizeof(float) * (size_t)d);
+            if (L->q_gated) memcpy(gate + ((size_t)r * nh + hh) * d, src + d, sizeof(float) * (size_t)d);
+        }
     orc_gemv4(&L->wk, xa, m, k);
     orc_gemv4(&L->wv, xa, m, v);
-    orc_rope(q, m, nh, d, cache_len, L->rope_theta);
-    orc_rope(k, m, nkv, d, cache_len, L->rope_theta);
+    /* per-head norms: every head of every row is one RMSNorm row of head_dim */
+    if (L->gamma_q_head) orc_rmsnorm(q, L->gamma_q_head, m * nh, d, L->eps, q);
+    if (L->gamma_k_head) orc_rmsnorm(k, L->gamma_k_head, m * nkv, d, L->eps, k);
+    orc_rope_partial(q, m, nh, d, rot, cache_len, L->rope_theta);
+    orc_rope_partial(k, m, nkv, d, rot, cache_len, L->rope_theta);
     for (int32_t r = 0; r < m; ++r)
         for (int32_t g = 0; g < nkv; ++g) {
             size_t dst = ((size_t)g * capacity + (size_t)(cache_len + r)) * d;
@@ -261,10 +286,15 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
             memcpy(v_cache + dst, v + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
         }
     orc_sdpa(q, k_cache, v_cache, m, nh, nkv, d, cache_len, capacity, o);
+    if (L->q_gated)
+        for (size_t i = 0; i < (size_t)m * nh * d; ++i)
+            o[i] = (float)((double)o[i] / (1.0 + exp(-(double)gate[i])));
     orc_gemv4(&L->wo, o, m, a);
     for (size_t i = 0; i < (size_t)m * H; ++i) r1[i] = (float)((double)u[i] + (double)a[i]);
     free(xa);
+    free(qg);
     free(q);
+    free(gate);
     free(k);
     free(v);
     free(o);

@@ -49,13 +49,24 @@ typedef struct {
 } orc_q8;
 
 /* One dense MTP draft layer ([mimo.rs] module doc "The draft forward";
- * [mtp.rs] `MtpWeights`). */
+ * [mtp.rs] `MtpWeights`).  Attention variant of [mtp.rs]
+ * `forward_full_attention` (all optional):
+ *   q_gated       wq holds 2*n_heads*head_dim rows, per head h the head's q
+ *                 rows then its gate rows (rows 2hd..2hd+d-1, 2hd+d..2hd+2d-1);
+ *                 the attention output is multiplied by sigmoid(gate) before wo
+ *                 (`MtpQGateWeightsGpu::Gated`, `apply_sigmoid_gate_multiply`);
+ *   gamma_q_head, gamma_k_head  f32 [head_dim]: per-head RMSNorm of q and k
+ *                 before the rotary step (`apply_q_or_k_per_head_rms_norm`);
+ *   rotary_dim    0 or head_dim: rotary over all dims; else only the first
+ *                 rotary_dim dims rotate (`apply_imrope`'s rotary_dim). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab, ffn_inter;
     double rope_theta;
     float eps;
     const float *gamma_e, *gamma_h, *gamma_attn, *gamma_post, *gamma_final;
     orc_q4 eh_proj, wq, wk, wv, wo, gate, up, down, lm_head;
+    const float *gamma_q_head, *gamma_k_head;
+    int32_t q_gated, rotary_dim;
 } orc_layer;
 
 /* ---- weight formats ---- */
@@ -69,6 +80,8 @@ void orc_gemv8(const orc_q8* w, const float* x, int32_t m, float* y);
 void orc_gemv_f32(const float* w, int32_t n, int32_t k, const float* x, int32_t m, float* y);
 void orc_rmsnorm(const float* x, const float* gamma, int32_t m, int32_t h, float eps, float* y);
 void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t pos0, double theta);
+void orc_rope_partial(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t rotary_dim, int32_t pos0,
+                      double theta);
 void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_t m,
               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t cache_len,
               int32_t capacity, float* out);

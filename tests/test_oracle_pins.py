@@ -437,3 +437,147 @@ def test_attention_on_empty_cache_reduces_to_the_value_row():
     o = np.concatenate([v[hh // (L.n_heads // L.n_kv_heads)] for hh in range(L.n_heads)])[None]
     want = (u.astype(np.float64) + oracle.gemv4(L.wo, o).astype(np.float64)).astype(np.float32)
     assert np.array_equal(r1, want)
+
+
+# --------------------------------------------------------------------------
+# attention variant ([mtp.rs] `forward_full_attention`): gated q, per-head
+# q/k norms, partial rotary
+# --------------------------------------------------------------------------
+def test_rope_partial_closed_form_and_pass_through():
+    theta = 1.0e6
+    x = np.array([[0.3, -1.2, 0.7, 2.0, -0.4, 0.9, 1.5, -2.2]], np.float32)  # one head of 8, rotary 4
+    p = 7
+    y = oracle.rope(x, 1, 8, p, theta, rotary_dim=4)[0]
+    xd = [float(v) for v in x[0]]
+    f0, f1 = 1.0, theta ** -0.5  # pairs (0, 2) and (1, 3); frequencies over the rotary dims
+    exp = [xd[0] * math.cos(p * f0) - xd[2] * math.sin(p * f0),
+           xd[1] * math.cos(p * f1) - xd[3] * math.sin(p * f1),
+           xd[0] * math.sin(p * f0) + xd[2] * math.cos(p * f0),
+           xd[1] * math.sin(p * f1) + xd[3] * math.cos(p * f1)] + xd[4:]
+    assert np.allclose(y, np.array(exp, np.float32), rtol=0, atol=2e-7)
+    assert (y[4:] == x[0, 4:]).all()
+
+
+def test_rope_partial_relative_position():
+    g = np.random.default_rng(71)
+    q, k = synth.normal(g, (1, 128)), synth.normal(g, (1, 128))
+    for rot in (32, 64):
+        d1 = float(oracle.rope(q, 1, 128, 100, 1e6, rot)[0].astype(np.float64) @ oracle.rope(k, 1, 128, 90, 1e6, rot)[0])
+        d2 = float(oracle.rope(q, 1, 128, 2010, 1e6, rot)[0].astype(np.float64) @ oracle.rope(k, 1, 128, 2000, 1e6, rot)[0])
+        assert abs(d1 - d2) < 1e-4 * (1 + abs(d1))
+
+
+def _gated_from(L, gate_scale, gate_bias, gate_codes=None):
+    """The layer with a gated q projection whose per-head q rows are L's wq rows
+    and whose gate rows have the given constants (codes of L's q rows unless
+    given)."""
+    import dataclasses
+    nh, d = L.n_heads, L.head_dim
+    G = L.wq.scales.shape[1]
+    qc = L.wq.codes.reshape(nh, d, -1)
+    qs, qb = L.wq.scales.reshape(nh, d, G), L.wq.biases.reshape(nh, d, G)
+    gc = qc if gate_codes is None else gate_codes.reshape(nh, d, -1)
+    codes = np.concatenate([qc, gc], axis=1).reshape(2 * nh * d, -1)
+    def per_head(v):
+        v = np.asarray(v, np.float32)
+        return v.reshape(nh, d, G) if v.ndim == 2 else np.broadcast_to(v, qs.shape)
+
+    scales = np.concatenate([qs, per_head(gate_scale)], axis=1)
+    biases = np.concatenate([qb, per_head(gate_bias)], axis=1)
+    wq = synth.Q4(np.ascontiguousarray(codes), np.ascontiguousarray(scales.reshape(2 * nh * d, G)),
+                  np.ascontiguousarray(biases.reshape(2 * nh * d, G)))
+    return dataclasses.replace(L, wq=wq, q_gated=True)
+
+
+def _attn_delta(L, seed=58, m=2, cache_len=5):
+    g = np.random.default_rng(seed)
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, cache_len, cache_len + m + 1, L.head_dim)
+    u = synth.normal(g, (m, L.hidden))
+    r1 = oracle.attention(L, u, kc, vc, cache_len)
+    return r1.astype(np.float64) - u.astype(np.float64)
+
+
+def test_gate_zero_halves_and_opposite_gates_add_to_the_ungated_output():
+    """sigmoid(0) = 1/2 and sigmoid(g) + sigmoid(-g) = 1; the gate rows follow
+    each head's q rows."""
+    L = _small_layer(seed=23)
+    plain = _attn_delta(L)
+    half = _attn_delta(_gated_from(L, 0.0, 0.0))
+    assert np.allclose(half, 0.5 * plain, rtol=1e-5, atol=1e-6)
+    rng = np.random.default_rng(5)
+    s = rng.uniform(0.005, 0.02, size=L.wq.scales.shape).astype(np.float32)
+    b = (-8.0 * s + rng.normal(0, 1e-3, size=s.shape)).astype(np.float32)
+    pos = _attn_delta(_gated_from(L, s, b))
+    neg = _attn_delta(_gated_from(L, -s, -b))
+    assert not np.allclose(pos, 0.5 * plain, rtol=1e-3, atol=1e-5)
+    assert np.allclose(pos + neg, plain, rtol=1e-5, atol=2e-6)
+
+
+def test_qk_head_norm_is_per_head_and_scale_invariant():
+    """With per-head norms (eps 0), doubling one q head's projection rows or
+    one k head's leaves the attention unchanged; without them it does not."""
+    import dataclasses
+    L = _small_layer(seed=24)
+    g = np.random.default_rng(9)
+    L = dataclasses.replace(L, eps=0.0, gamma_q_head=synth.gamma(g, L.head_dim), gamma_k_head=synth.gamma(g, L.head_dim))
+    base = _attn_delta(L)
+    d = L.head_dim
+
+    def scaled(w, rows):
+        s, b = w.scales.copy(), w.biases.copy()
+        s[rows] *= 2.0
+        b[rows] *= 2.0
+        return synth.Q4(w.codes, s, b)
+
+    one_q = dataclasses.replace(L, wq=scaled(L.wq, slice(d, 2 * d)))  # q head 1 only
+    one_k = dataclasses.replace(L, wk=scaled(L.wk, slice(0, d)))      # k head 0 only
+    assert np.allclose(_attn_delta(one_q), base, rtol=1e-5, atol=2e-6)
+    assert np.allclose(_attn_delta(one_k), base, rtol=1e-5, atol=2e-6)
+    plain = dataclasses.replace(L, gamma_q_head=None, gamma_k_head=None)
+    plain_q = dataclasses.replace(plain, wq=scaled(plain.wq, slice(d, 2 * d)))
+    assert not np.allclose(_attn_delta(plain_q), _attn_delta(plain), rtol=1e-3, atol=1e-5)
+
+
+def test_head_norm_closed_form_inside_attention():
+    """One query head, one cached position: the output is that position's V
+    row whatever q is, and the new k written to the cache is
+    rope(rms(k; gamma_k) per head) at the row's position."""
+    import dataclasses
+    L = _small_layer(seed=25, nh=2, nkv=2, d=16)
+    g = np.random.default_rng(10)
+    gk = synth.gamma(g, L.head_dim)
+    L = dataclasses.replace(L, gamma_q_head=synth.gamma(g, L.head_dim), gamma_k_head=gk, rotary_dim=8)
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, 3, 5, L.head_dim)
+    u = synth.normal(g, (1, L.hidden))
+    oracle.attention(L, u, kc, vc, 3)
+    xa = oracle.rmsnorm(u, L.gamma_attn, L.eps)
+    k = oracle.gemv4(L.wk, xa)[0].reshape(L.n_kv_heads, L.head_dim).astype(np.float64)
+    for h in range(L.n_kv_heads):
+        kn = (k[h] / math.sqrt(float(np.mean(k[h] ** 2)) + L.eps) * gk).astype(np.float32)
+        want = oracle.rope(kn[None], 1, L.head_dim, 3, L.rope_theta, 8)[0]
+        assert np.allclose(kc[h, 3], want, rtol=1e-6, atol=1e-6)
+
+
+def test_large_positive_gate_passes_the_attention_through_and_negative_closes_it():
+    """Gate rows w_k = +1 where xa_k > 0 and -1 elsewhere give gate = sum |xa| >> 0,
+    so sigmoid(gate) = 1 and the output is the ungated one; the negated rows
+    close the gate (output u)."""
+    L = _small_layer(seed=26)
+    g = np.random.default_rng(59)
+    cache_len, m = 4, 1
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, cache_len, cache_len + 2, L.head_dim)
+    u = synth.normal(g, (m, L.hidden))
+    xa = oracle.rmsnorm(u, L.gamma_attn, L.eps)[0]
+    nh, d, H = L.n_heads, L.head_dim, L.hidden
+    bits = (xa > 0).astype(np.uint8) * 15
+    codes = synth.pack_q4(np.broadcast_to(bits, (nh * d, H)))
+
+    def run(layer):
+        kk, vv = kc.copy(), vc.copy()
+        return oracle.attention(layer, u, kk, vv, cache_len).astype(np.float64)
+
+    plain = run(L)
+    opened = run(_gated_from(L, 2.0 / 15.0, -1.0, gate_codes=codes))
+    closed = run(_gated_from(L, -2.0 / 15.0, 1.0, gate_codes=codes))
+    assert np.allclose(opened, plain, rtol=0, atol=1e-6)
+    assert np.allclose(closed, u.astype(np.float64), rtol=0, atol=1e-6)
