@@ -85,7 +85,18 @@ typedef struct {
  * MoE FFN: router f32 [n_experts][hidden], gate_exps/up_exps
  * [n_experts][inter][hidden], down_exps [n_experts][hidden][inter], optional
  * shared expert sh_* (n_experts = 1); lm_head [vocab][hidden].
- * gamma_* are f32 [hidden] norm weights applied as x/rms(x)*gamma. */
+ * gamma_* are f32 [hidden] norm weights applied as x/rms(x)*gamma.
+ * Attention variant ([mtp.rs] `forward_full_attention`, `MtpQGateWeightsGpu`;
+ * zero / NULL fields give the plain attention):
+ *   q_gated       wq is [2*n_heads*head_dim][hidden]: for head h its q rows
+ *                 (2h*d .. 2h*d+d-1) then its gate rows (2h*d+d .. 2h*d+2d-1);
+ *                 the attention output is multiplied by sigmoid(gate) before wo.
+ *   gamma_q_head, gamma_k_head  f32 [head_dim] (both NULL or both set):
+ *                 per-head RMSNorm of q and of k (eps = eps) before the rotary
+ *                 step.
+ *   rotary_dim    0 = head_dim; else a power of two <= head_dim: only the
+ *                 first rotary_dim dims rotate, as pairs (i, i + rotary_dim/2)
+ *                 with inverse frequency rope_theta^(-2i/rotary_dim). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab;
     int32_t ffn_kind; /* MTP_FFN_DENSE_Q4 or MTP_FFN_MOE_Q8 */
@@ -97,6 +108,8 @@ typedef struct {
     mtp_q4 eh_proj, wq, wk, wv, wo, gate, up, down, lm_head;
     const float* router;
     mtp_q8 gate_exps, up_exps, down_exps, sh_gate, sh_up, sh_down;
+    const float *gamma_q_head, *gamma_k_head;
+    int32_t q_gated, rotary_dim;
 } mtp_layer;
 
 const char* mtp_status_string(mtp_status s);

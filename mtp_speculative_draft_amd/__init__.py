@@ -49,7 +49,9 @@ class MtpLayer(C.Structure):
                 ("gate", MtpQ4), ("up", MtpQ4), ("down", MtpQ4), ("lm_head", MtpQ4),
                 ("router", C.c_void_p),
                 ("gate_exps", MtpQ8), ("up_exps", MtpQ8), ("down_exps", MtpQ8),
-                ("sh_gate", MtpQ8), ("sh_up", MtpQ8), ("sh_down", MtpQ8)]
+                ("sh_gate", MtpQ8), ("sh_up", MtpQ8), ("sh_down", MtpQ8),
+                ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
+                ("q_gated", C.c_int32), ("rotary_dim", C.c_int32)]
 
 
 _lib = None
@@ -170,13 +172,19 @@ class DeviceLayer:
                 q8[k] = v.desc
             router, top_k, kind = self.router.data_ptr(), moe.top_k, MTP_FFN_MOE_Q8
         g = [t.data_ptr() for t in self.gammas]
+        # attention variant: per-head q/k norm weights, gated q, partial rotary
+        gq, gk = getattr(dense, "gamma_q_head", None), getattr(dense, "gamma_k_head", None)
+        self.head_gammas = None if gq is None else (f(gq), f(gk))
+        hq = self.head_gammas[0].data_ptr() if self.head_gammas else None
+        hk = self.head_gammas[1].data_ptr() if self.head_gammas else None
         q = self.q4
         self.desc = MtpLayer(dense.hidden, dense.n_heads, dense.n_kv_heads, dense.head_dim, dense.vocab, kind,
                              dense.ffn_inter, top_k, float(dense.rope_theta), float(dense.eps), *g,
                              q["eh_proj"].desc, q["wq"].desc, q["wk"].desc, q["wv"].desc, q["wo"].desc,
                              q["gate"].desc, q["up"].desc, q["down"].desc, q["lm_head"].desc, router,
                              q8["gate_exps"], q8["up_exps"], q8["down_exps"], q8["sh_gate"], q8["sh_up"],
-                             q8["sh_down"])
+                             q8["sh_down"], hq, hk, int(bool(getattr(dense, "q_gated", False))),
+                             int(getattr(dense, "rotary_dim", 0) or 0))
 
     @property
     def weight_nbytes(self) -> int:

@@ -97,7 +97,7 @@ struct AttnWs {
 AttnWs carve_attn(Carve& c, const mtp_layer* L, int32_t cache_len, int32_t m) {
     AttnWs w;
     const int d = L->head_dim, nh = L->n_heads, nkv = L->n_kv_heads;
-    w.qkv = c.take<float>((size_t)m * (nh + 2 * nkv) * d);
+    w.qkv = c.take<float>((size_t)m * ((L->q_gated ? 2 : 1) * nh + 2 * nkv) * d);
     w.part = c.take<float>((size_t)chunks_for(cache_len, m) * nkv * (nh / (nkv ? nkv : 1)) * m * (d + 2));
     w.o = c.take<float>((size_t)m * nh * d);
     return w;
@@ -218,6 +218,11 @@ hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* v
     a.part = w.part;
     a.o = w.o;
     a.chunks = chunks_for(cache_len, m);
+    a.qg = L->q_gated ? 2 : 1;
+    a.gq = L->gamma_q_head;
+    a.gk = L->gamma_k_head;
+    a.eps = L->eps;
+    a.rot = L->rotary_dim > 0 ? L->rotary_dim : L->head_dim;
     if ((e = launch_attention(a, st)) != hipSuccess) return e;
     GemvParams o{};
     o.w[0] = qmat(L->wo);
@@ -308,9 +313,17 @@ mtp_status check_layer_attn(const mtp_layer* L) {
         (s = check_q4(&L->wo, "wo")))
         return s;
     const int qn = L->n_heads * L->head_dim, kvn = L->n_kv_heads * L->head_dim;
-    if (L->wq.n != qn || L->wq.k != H || L->wk.n != kvn || L->wk.k != H || L->wv.n != kvn || L->wv.k != H ||
-        L->wo.n != H || L->wo.k != qn)
+    if (L->q_gated != 0 && L->q_gated != 1) return fail(MTP_ERR_INVALID_ARG, "q_gated=%d (0 or 1)", L->q_gated);
+    if (L->wq.n != (L->q_gated ? 2 : 1) * qn || L->wq.k != H || L->wk.n != kvn || L->wk.k != H || L->wv.n != kvn ||
+        L->wv.k != H || L->wo.n != H || L->wo.k != qn)
         return fail(MTP_ERR_INVALID_ARG, "attention weight shapes do not match hidden/heads/head_dim");
+    if ((L->gamma_q_head == nullptr) != (L->gamma_k_head == nullptr))
+        return fail(MTP_ERR_INVALID_ARG, "gamma_q_head and gamma_k_head: give both or neither");
+    if (L->gamma_q_head && (!a16(L->gamma_q_head) || !a16(L->gamma_k_head)))
+        return fail(MTP_ERR_INVALID_ARG, "gamma_q_head/gamma_k_head must be 16-byte aligned");
+    const int rot = L->rotary_dim;
+    if (rot != 0 && (rot < 2 || rot > L->head_dim || (rot & (rot - 1)) != 0))
+        return fail(MTP_ERR_UNSUPPORTED, "rotary_dim=%d (0 or a power of two <= head_dim)", rot);
     if (qn > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "n_heads*head_dim=%d above %d", qn, MTP_MAX_K);
     return MTP_OK;
 }

@@ -20,6 +20,10 @@
 // row-head) the chunk maximum, the exp-sum and the unnormalised sum of p*V.
 // Kernel 2 (grid: KV heads x query row-heads) merges the chunks with the
 // log-sum-exp rule.
+// Variant steps of the same function (when set): per-head RMSNorm of q and
+// of the new k before the rotary step, a rotary step over the first rot
+// dims only, and the output multiplied by sigmoid(gate) in kernel 2, the
+// gate values of a head following its q values in the projection output.
 #include <cmath>
 
 #include "device.hpp"
@@ -74,7 +78,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     const int hm0 = z * kSliceHM;
     const int HM = HMall - hm0 < kSliceHM ? HMall - hm0 : kSliceHM;  // row-heads of this block
     const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
-    const int ld = (p.nh + 2 * p.nkv) * kD;  // qkv row stride
+    const int ld = (p.qg * p.nh + 2 * p.nkv) * kD;  // qkv row stride
     const int p0 = c * kC;
     const int64_t cbase = (int64_t)g * p.capacity * kD;
     constexpr int kQuads = kC * (kD / 4) / 256;  // float4 slots of K (and of V) per thread
@@ -103,7 +107,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
         qb[u] = 0.0f;
         if (hm < HM) {
             const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
-            const float* q = p.qkv + (int64_t)mi * ld + hq * kD;
+            const float* q = p.qkv + (int64_t)mi * ld + hq * p.qg * kD;
             qa[u] = q[i];
             qb[u] = q[i + kD / 2];
         }
@@ -116,21 +120,64 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
         const int pos = p.cache_len + mi;
         ka[u] = kb[u] = va[u] = vb[u] = 0.0f;
         if (mi < p.m && pos >= p0 && pos < p0 + kC) {
-            const float* kn = p.qkv + (int64_t)mi * ld + p.nh * kD + g * kD;
-            const float* vn = p.qkv + (int64_t)mi * ld + (p.nh + p.nkv) * kD + g * kD;
+            const float* kn = p.qkv + (int64_t)mi * ld + p.qg * p.nh * kD + g * kD;
+            const float* vn = p.qkv + (int64_t)mi * ld + (p.qg * p.nh + p.nkv) * kD + g * kD;
             ka[u] = kn[i];
             kb[u] = kn[i + kD / 2];
             va[u] = vn[i];
             vb[u] = vn[i + kD / 2];
         }
     }
+    // per-head norm weights of this lane's pair (i, i + d/2), i = lane
+    float gqa = 1.0f, gqb = 1.0f, gka = 1.0f, gkb = 1.0f;
+    if (p.gq) {
+        gqa = p.gq[lane];
+        gqb = p.gq[lane + kD / 2];
+        gka = p.gk[lane];
+        gkb = p.gk[lane + kD / 2];
+    }
     // ... and the rotary table for positions cache_len + mi is built meanwhile
-    for (int idx = t; idx < p.m * (kD / 2); idx += blockDim.x) {
-        const int mi = idx / (kD / 2), i = idx % (kD / 2);
-        const double inv_freq = exp2(-(2.0 * (double)i / (double)kD) * p.log2_theta);
+    const int rh = p.rot / 2;  // rotated pairs (i, i + rot/2), i < rh
+    for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
+        const int mi = idx / rh, i = idx % rh;
+        const double inv_freq = exp2(-(2.0 * (double)i / (double)p.rot) * p.log2_theta);
         rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
     }
     __syncthreads();
+
+    // per-head RMSNorm of q and of the new k: a wave holds one row-head (or
+    // one new k row) per load slot, lane i its dims i and i + d/2
+    if (p.gq) {
+#pragma unroll
+        for (int u = 0; u < kQPairs; ++u) {
+            const float inv = rsqrtf(wave_sum(qa[u] * qa[u] + qb[u] * qb[u]) * (1.0f / kD) + p.eps);
+            qa[u] = qa[u] * inv * gqa;
+            qb[u] = qb[u] * inv * gqb;
+        }
+#pragma unroll
+        for (int u = 0; u < kNPairs; ++u) {
+            const float inv = rsqrtf(wave_sum(ka[u] * ka[u] + kb[u] * kb[u]) * (1.0f / kD) + p.eps);
+            ka[u] = ka[u] * inv * gka;
+            kb[u] = kb[u] * inv * gkb;
+        }
+    }
+    // Rotation of a pair-loaded row (lane i holds dims i and i + d/2): over
+    // all dims the pair is the lane's own; over rot < d dims, dim i < rot
+    // pairs with dim i ^ (rot/2) in the neighbouring lane, and dims from rot
+    // on pass unchanged.
+    auto rotate = [&](float a, float b, int mi, float& ra, float& rb) {
+        if (p.rot == kD) {
+            const float cs = rc[mi][lane], sn = rs[mi][lane];
+            ra = a * cs - b * sn;
+            rb = a * sn + b * cs;
+        } else {
+            const float o = __shfl_xor(a, rh);
+            const int j = lane & (rh - 1);
+            const float cs = rc[mi][j], sn = rs[mi][j];
+            ra = lane >= p.rot ? a : (lane < rh ? a * cs - o * sn : o * sn + a * cs);
+            rb = b;
+        }
+    };
 
     // 2. rotated queries of this group (hm = mi * GQ + local head), cached
     //    rows into LDS, rows past the new ones zeroed, the new rows rotated and
@@ -138,11 +185,12 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
 #pragma unroll
     for (int u = 0; u < kQPairs; ++u) {
         const int idx = t + 256 * u, hm = idx / (kD / 2), i = idx % (kD / 2);
+        const int mi = hm < HM ? (hm0 + hm) / GQ : 0;
+        float ra, rb;
+        rotate(qa[u], qb[u], mi, ra, rb);
         if (hm < HM) {
-            const int mi = (hm0 + hm) / GQ;
-            const float cs = rc[mi][i], sn = rs[mi][i];
-            qs[hm][i] = qa[u] * cs - qb[u] * sn;
-            qs[hm][i + kD / 2] = qa[u] * sn + qb[u] * cs;
+            qs[hm][i] = ra;
+            qs[hm][i + kD / 2] = rb;
         }
     }
 #pragma unroll
@@ -158,10 +206,10 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     for (int u = 0; u < kNPairs; ++u) {
         const int idx = t + 256 * u, mi = idx / (kD / 2), i = idx % (kD / 2);
         const int pos = p.cache_len + mi;
+        float k0, k1;
+        rotate(ka[u], kb[u], mi < p.m ? mi : 0, k0, k1);
         if (mi < p.m && pos >= p0 && pos < p0 + kC) {
             const int j = pos - p0;
-            const float cs = rc[mi][i], sn = rs[mi][i];
-            const float k0 = ka[u] * cs - kb[u] * sn, k1 = ka[u] * sn + kb[u] * cs;
             ks[j][i] = k0;
             ks[j][i + kD / 2] = k1;
             vs[j][i] = va[u];
@@ -311,7 +359,12 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     __syncthreads();
     if (cs == 0) {
         for (int j = 1; j < kCombLanes; ++j) lse_merge(M, L, A, sm[j][dl], sl[j][dl], sa[j][dl]);
-        p.o[(int64_t)mi * p.nh * kD + hq * kD + dd] = L > 0.0f ? A / L : 0.0f;
+        float o = L > 0.0f ? A / L : 0.0f;
+        if (p.qg == 2) {  // sigmoid gate: the head's gate values follow its q values
+            const float gv = p.qkv[(int64_t)mi * (2 * p.nh + 2 * p.nkv) * kD + (2 * hq + 1) * kD + dd];
+            o = o / (1.0f + __expf(-gv));
+        }
+        p.o[(int64_t)mi * p.nh * kD + hq * kD + dd] = o;
     }
 }
 

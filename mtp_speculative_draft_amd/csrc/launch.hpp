@@ -127,7 +127,7 @@ int device_cu_count();
 // Attention (head_dim 128): RoPE + append + chunked partial softmax, then the
 // log-sum-exp combine.
 struct AttnParams {
-    const float* qkv;  // [m][(nh + 2 nkv) * d] pre-RoPE q, k and v
+    const float* qkv;  // [m][(qg * nh + 2 nkv) * d] pre-RoPE q (with gate rows when qg = 2), k and v
     float* k_cache;
     float* v_cache;
     int cache_len, capacity, m, nh, nkv, d;
@@ -135,6 +135,11 @@ struct AttnParams {
     float* part;  // [chunks][nkv][group*m][d + 2]: p*V sums, chunk max, exp-sum
     float* o;     // [m][nh * d]
     int chunks;
+    int qg;               // 1: q heads are d apart in qkv; 2: each q head is followed by its d gate values
+    const float* gq;      // per-head RMSNorm weights [d] of q and k (NULL: none)
+    const float* gk;
+    float eps;
+    int rot;              // rotary dims (a power of two <= d)
 };
 constexpr int kAttnChunk = 32;
 hipError_t launch_attention(const AttnParams& p, hipStream_t stream);

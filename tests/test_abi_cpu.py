@@ -2,6 +2,7 @@
 include/mtp.h declares, and rejects bad arguments on the host before anything
 is enqueued (so these calls never reach the HIP runtime)."""
 import ctypes as C
+import os
 import re
 
 import pytest
@@ -128,3 +129,39 @@ def test_lmhead_requires_ids_and_workspace():
                                  None) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_lmhead_argmax(FAKE, FAKE, 1e-6, C.byref(w), None, None, FAKE * 2, 1, FAKE * 3, 16,
                                  None) == mtp.MTP_ERR_WORKSPACE
+
+
+def test_layer_struct_layout_matches_the_header(tmp_path):
+    """The binding's mtp_layer mirrors include/mtp.h field for field."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "mtp.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(mtp_layer), '
+                   'offsetof(mtp_layer, sh_down), offsetof(mtp_layer, gamma_q_head), '
+                   'offsetof(mtp_layer, q_gated), offsetof(mtp_layer, rotary_dim)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(mtp.HEADER), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    L = mtp.MtpLayer
+    assert got == [C.sizeof(L), L.sh_down.offset, L.gamma_q_head.offset, L.q_gated.offset, L.rotary_dim.offset]
+
+
+def test_attention_variant_fields_are_validated():
+    lib = mtp.lib()
+
+    def status(L):
+        return lib.mtp_attn_decode(C.byref(L), FAKE, FAKE * 2, FAKE * 3, 0, 16, 1, FAKE * 4, FAKE * 5, 1 << 30, None)
+
+    L = _layer()
+    L.rotary_dim = 48  # not a power of two
+    assert status(L) == mtp.MTP_ERR_UNSUPPORTED
+    L = _layer()
+    L.rotary_dim = 256  # above head_dim
+    assert status(L) == mtp.MTP_ERR_UNSUPPORTED
+    L = _layer()
+    L.q_gated = 1  # wq still has n_heads * head_dim rows
+    assert status(L) == mtp.MTP_ERR_INVALID_ARG
+    L = _layer()
+    L.gamma_q_head = FAKE  # without gamma_k_head
+    assert status(L) == mtp.MTP_ERR_INVALID_ARG
+    assert b"gamma_k_head" in lib.mtp_last_error()

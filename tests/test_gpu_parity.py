@@ -286,6 +286,51 @@ def test_attn_decode_config4_shape(m):
     _close(_np(dk)[:, 4096:4096 + m], kc[:, 4096:4096 + m], "appended k")
 
 
+_VARIANTS = {
+    "gated": dict(q_gated=True),
+    "qknorm": dict(qk_norm=True),
+    "rot64": dict(rotary_dim=64),
+    "all_rot32": dict(q_gated=True, qk_norm=True, rotary_dim=32),
+    "all_rot2": dict(q_gated=True, qk_norm=True, rotary_dim=2),
+}
+
+
+@pytest.mark.parametrize("variant,cache_len,m", [("gated", 100, 1), ("qknorm", 31, 3), ("rot64", 64, 2),
+                                                 ("all_rot32", 100, 4), ("all_rot32", 0, 1), ("all_rot2", 40, 8)])
+def test_attn_decode_variant_small(variant, cache_len, m):
+    """[mtp.rs] forward_full_attention's gated q, per-head q/k norms and
+    partial rotary dims against the oracle."""
+    _say(f"attn variant {variant} cache_len={cache_len} m={m}")
+    L = synth.dense_layer(synth.rng(112, cache_len, m), hidden=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                          vocab=1000, ffn_inter=320, **_VARIANTS[variant])
+    g = synth.rng(113, cache_len, m)
+    cap = cache_len + m + 3
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, cache_len, cap, 128)
+    u = synth.normal(g, (m, L.hidden))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(u), dk, dv, cache_len))
+    kr, vr = kc.copy(), vc.copy()
+    ref = oracle.attention(L, u, kr, vr, cache_len)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, cache_len:cache_len + m], kr[:, cache_len:cache_len + m], "appended k")
+    _close(_np(dv)[:, cache_len:cache_len + m], vr[:, cache_len:cache_len + m], "appended v")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_attn_decode_variant_config4_shape(m):
+    """All variant steps at the full attention size (16/2 heads x 128, cache 4096)."""
+    _say(f"attn variant config4 shape m={m}")
+    g = synth.rng(114, m)
+    L = synth.dense_layer(g, vocab=64, ffn_inter=64, q_gated=True, qk_norm=True, rotary_dim=64)
+    kc, vc = synth.kv_cache(g, 2, 4096, 4104, 128)
+    u = synth.normal(g, (m, 2048))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(u), dk, dv, 4096))
+    ref = oracle.attention(L, u, kc, vc, 4096)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, 4096:4096 + m], kc[:, 4096:4096 + m], "appended k")
+
+
 def test_attn_decode_rejects_overflow_without_writing():
     L = _small_layer(2)
     g = synth.rng(110)
@@ -451,6 +496,19 @@ def test_draft_step_small_chain_and_verify():
         if min(margins) >= 1e-2:
             break
     _check_step(S, f"small seed {extra}", ref)
+
+
+def test_draft_step_variant_chain_and_verify():
+    """The whole layer with the gated, head-normed, partially rotated attention."""
+    for extra in range(1, 30):
+        S = synth.config4_step(seed_extra=1500 + extra, cache_len=100, capacity=110, hidden=256, n_heads=4,
+                               n_kv_heads=2, head_dim=128, vocab=1000, ffn_inter=320, q_gated=True, qk_norm=True,
+                               rotary_dim=64)
+        ref = _chain_and_verify_oracle(S)
+        margins = [planting.head_margin(o[2]) for o in ref[0]] + [planting.head_margin(r) for r in ref[1][2]]
+        if min(margins) >= 1e-2:
+            break
+    _check_step(S, f"variant seed {extra}", ref)
 
 
 def test_draft_step_config4():
