@@ -62,6 +62,9 @@ __device__ __forceinline__ bool attn_block(const AttnParams& p, int Z, int& c, i
 // Local row-head hl of slice z is the group's row-head z * kSliceHM + hl
 // (= mi * GQ + local query head).
 typedef float v4f_t __attribute__((ext_vector_type(4)));
+// VAR: the per-head norm and partial rotary steps are compiled in (the
+// plain attention runs without them).
+template <bool VAR>
 __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     __shared__ float qs[kSliceHM][kD];
     __shared__ float ks[kC][kKStride];
@@ -130,24 +133,25 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     }
     // per-head norm weights of this lane's pair (i, i + d/2), i = lane
     float gqa = 1.0f, gqb = 1.0f, gka = 1.0f, gkb = 1.0f;
-    if (p.gq) {
+    if (VAR && p.gq) {
         gqa = p.gq[lane];
         gqb = p.gq[lane + kD / 2];
         gka = p.gk[lane];
         gkb = p.gk[lane + kD / 2];
     }
     // ... and the rotary table for positions cache_len + mi is built meanwhile
-    const int rh = p.rot / 2;  // rotated pairs (i, i + rot/2), i < rh
+    const int rot = VAR ? p.rot : kD;
+    const int rh = rot / 2;  // rotated pairs (i, i + rot/2), i < rh
     for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
         const int mi = idx / rh, i = idx % rh;
-        const double inv_freq = exp2(-(2.0 * (double)i / (double)p.rot) * p.log2_theta);
+        const double inv_freq = exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta);
         rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
     }
     __syncthreads();
 
     // per-head RMSNorm of q and of the new k: a wave holds one row-head (or
     // one new k row) per load slot, lane i its dims i and i + d/2
-    if (p.gq) {
+    if (VAR && p.gq) {
 #pragma unroll
         for (int u = 0; u < kQPairs; ++u) {
             const float inv = rsqrtf(wave_sum(qa[u] * qa[u] + qb[u] * qb[u]) * (1.0f / kD) + p.eps);
@@ -166,7 +170,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     // pairs with dim i ^ (rot/2) in the neighbouring lane, and dims from rot
     // on pass unchanged.
     auto rotate = [&](float a, float b, int mi, float& ra, float& rb) {
-        if (p.rot == kD) {
+        if (rot == kD) {
             const float cs = rc[mi][lane], sn = rs[mi][lane];
             ra = a * cs - b * sn;
             rb = a * sn + b * cs;
@@ -174,7 +178,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
             const float o = __shfl_xor(a, rh);
             const int j = lane & (rh - 1);
             const float cs = rc[mi][j], sn = rs[mi][j];
-            ra = lane >= p.rot ? a : (lane < rh ? a * cs - o * sn : o * sn + a * cs);
+            ra = lane >= rot ? a : (lane < rh ? a * cs - o * sn : o * sn + a * cs);
             rb = b;
         }
     };
@@ -373,7 +377,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int Z = (hm + kSliceHM - 1) / kSliceHM;
     const int pairs = p.chunks * p.nkv;
     const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
-    hipLaunchKernelGGL(k_attn_partial, grid, block, 0, st, p);
+    if (p.gq || p.rot != kD)
+        hipLaunchKernelGGL(k_attn_partial<true>, grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL(k_attn_partial<false>, grid, block, 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int HM = (p.nh / p.nkv) * p.m;
