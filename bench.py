@@ -12,7 +12,8 @@ weights and of the KV caches are rotated (step i uses copy i % R).
 
 Printed: one JSON line with the weight-stream GB/s of the whole step
 (algorithmic bytes / time), draft steps/s and verify rows/s, the roofline of
-the dominant call (lm_head + argmax, timed with HIP events on its stream) and
+the dominant call (lm_head + argmax, timed with HIP events on its stream over the
+K launches of its timed region) and
 the oracle's CPU baseline.
 """
 from __future__ import annotations
@@ -192,19 +193,21 @@ def main():
     hws = torch.zeros(mtp.mtp_lmhead_workspace_size(V, 4), dtype=torch.uint8, device=dev)
     ids1 = torch.empty(4, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # one event pair around the K back-to-back launches of the timed region
+    # (rotated weight copies); the average launch duration is the region / K
     head_ms = {}
     for m in (1, 4):
         xm = torch.randn((m, H), device=dev)
         for i in range(W):
             mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m], ws=hws)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        ev0.record(stream)
         for i in range(K):
-            evs[i][0].record(stream)
             mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m], ws=hws)
-            evs[i][1].record(stream)
+        ev1.record(stream)
         torch.cuda.synchronize()
-        head_ms[m] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        head_ms[m] = float(ev0.elapsed_time(ev1)) / K
     lm_bytes = lm_copies[0].nbytes + 8 + H * 4  # weights + ids + gamma
     head_bytes_m1 = lm_bytes + 1 * H * 4
     achieved = head_bytes_m1 / (head_ms[1] * 1e-3) / 1e9

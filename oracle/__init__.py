@@ -80,6 +80,7 @@ def lib():
             "orc_moe": (I, [P, P, I, I, P, P, P, P, P, P, P, I, P, P, P, P]),
             "orc_head": (None, [P, P, C.c_float, P, I, P, P, P]),
             "orc_draft_step": (I, [P, P, P, P, P, P, P, I, I, I, P, P, P]),
+            "orc_append_kv": (None, [P, P, P, P, P, P, P, P, I, I, I]),
         }
         for name, (res, args) in sig.items():
             f = getattr(_lib, name)
@@ -321,6 +322,24 @@ def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_lo
     if rc != 0:
         raise ValueError("orc_draft_step rejected its arguments")
     return ids, hid, logits
+
+
+def append_kv(L, e, tokens, table, pending_h, target_h, k_cache, v_cache, cache_len: int) -> None:
+    """Cache catch-up after a target batch: writes K/V rows cache_len .. cache_len+m-1
+    in place (row r's hidden is target_h row r-1, row 0's pending_h or zero)."""
+    assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
+    assert v_cache.flags.c_contiguous and v_cache.dtype == np.float32
+    keep = _Keep()
+    d = _layer(L, keep)
+    tgt = keep.arr(np.atleast_2d(target_h), np.float32)
+    m = tgt.shape[0]
+    e = None if e is None else keep.arr(np.atleast_2d(e), np.float32)
+    tok = None if tokens is None else keep.arr(np.asarray(tokens).reshape(-1), np.int32)
+    tab = None if table is None else (table if (table.flags.c_contiguous and table.dtype == np.float32)
+                                      else keep.arr(table, np.float32))
+    pend = None if pending_h is None else keep.arr(np.asarray(pending_h).reshape(-1), np.float32)
+    lib().orc_append_kv(C.byref(d), _p(e), _p(tok), _p(tab), _p(pend), _p(tgt), _p(k_cache), _p(v_cache),
+                        cache_len, k_cache.shape[1], m)
 
 
 def cosine(a: np.ndarray, b: np.ndarray) -> float:

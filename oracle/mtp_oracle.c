@@ -301,6 +301,58 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
     free(a);
 }
 
+/* Catch-up of the draft layer's cache after a target batch ([mtp.rs]
+ * `process_target_batch` and `append_attention_kv`): row r's hidden is the
+ * target's post-norm hidden shifted one row right (row 0 = pending_h, or zero
+ * when there is none; row r > 0 = target_h row r-1); u = eh_proj [rms(e_r);
+ * rms(shifted_r)]; then only the attention's K/V side runs: xa = rms(u;
+ * gamma_attn), k = Wk xa, v = Wv xa, the per-head k norm when present, the
+ * rotary step at position cache_len + r, and the rows are written at
+ * cache_len + r.  Nothing else is computed (the FFN and the logits hold no
+ * state). */
+void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                   const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                   int32_t cache_len, int32_t capacity, int32_t m) {
+    const int32_t H = L->hidden, d = L->head_dim, nkv = L->n_kv_heads;
+    const int32_t rot = L->rotary_dim > 0 ? L->rotary_dim : d;
+    float* er = (float*)xmalloc(sizeof(float) * (size_t)m * H);
+    float* sh = (float*)xmalloc(sizeof(float) * (size_t)m * H);
+    float* u = (float*)xmalloc(sizeof(float) * (size_t)m * H);
+    float* xa = (float*)xmalloc(sizeof(float) * (size_t)m * H);
+    float* k = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
+    float* v = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
+    for (int32_t r = 0; r < m; ++r) {
+        const float* src = (tokens && tokens[r] >= 0) ? embed_table + (size_t)tokens[r] * H : e + (size_t)r * H;
+        memcpy(er + (size_t)r * H, src, sizeof(float) * (size_t)H);
+        if (r == 0) {
+            if (pending_h)
+                memcpy(sh, pending_h, sizeof(float) * (size_t)H);
+            else
+                memset(sh, 0, sizeof(float) * (size_t)H);
+        } else {
+            memcpy(sh + (size_t)r * H, target_h + (size_t)(r - 1) * H, sizeof(float) * (size_t)H);
+        }
+    }
+    orc_norm_concat_proj(er, sh, L->gamma_e, L->gamma_h, L->eps, &L->eh_proj, m, u);
+    orc_rmsnorm(u, L->gamma_attn, m, H, L->eps, xa);
+    orc_gemv4(&L->wk, xa, m, k);
+    orc_gemv4(&L->wv, xa, m, v);
+    if (L->gamma_k_head) orc_rmsnorm(k, L->gamma_k_head, m * nkv, d, L->eps, k);
+    orc_rope_partial(k, m, nkv, d, rot, cache_len, L->rope_theta);
+    for (int32_t r = 0; r < m; ++r)
+        for (int32_t g = 0; g < nkv; ++g) {
+            size_t dst = ((size_t)g * capacity + (size_t)(cache_len + r)) * d;
+            memcpy(k_cache + dst, k + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
+            memcpy(v_cache + dst, v + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
+        }
+    free(er);
+    free(sh);
+    free(u);
+    free(xa);
+    free(k);
+    free(v);
+}
+
 static double silu(double a) { return a / (1.0 + exp(-a)); }
 
 /* y = [residual +] down * (silu(gate * x) . (up * x)) with 4-bit weights

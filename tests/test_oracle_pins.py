@@ -581,3 +581,47 @@ def test_large_positive_gate_passes_the_attention_through_and_negative_closes_it
     closed = run(_gated_from(L, -2.0 / 15.0, 1.0, gate_codes=codes))
     assert np.allclose(opened, plain, rtol=0, atol=1e-6)
     assert np.allclose(closed, u.astype(np.float64), rtol=0, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# cache catch-up after a target batch ([mtp.rs] `process_target_batch`)
+# --------------------------------------------------------------------------
+def _catchup_case(seed=27, m=5, cache_len=6, **variant):
+    L = synth.dense_layer(np.random.default_rng(seed), hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, vocab=300,
+                          ffn_inter=96, **variant)
+    g = np.random.default_rng(seed + 100)
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, cache_len, cache_len + m + 2, L.head_dim)
+    e = synth.normal(g, (m, L.hidden))
+    target = synth.normal(g, (m, L.hidden))
+    pending = synth.normal(g, (1, L.hidden))[0]
+    return L, kc, vc, e, target, pending
+
+
+def test_catchup_writes_the_draft_steps_rows_for_the_shifted_hidden():
+    """Catch-up rows equal the K/V rows the full draft forward writes when its
+    hidden rows are the shifted target rows (pending, t_0, ..., t_{m-2})."""
+    for variant in ({}, dict(q_gated=True, qk_norm=True, rotary_dim=8)):
+        L, kc, vc, e, target, pending = _catchup_case(**variant)
+        k1, v1 = kc.copy(), vc.copy()
+        oracle.append_kv(L, e, None, None, pending, target, k1, v1, 6)
+        k2, v2 = kc.copy(), vc.copy()
+        shifted = np.concatenate([pending[None], target[:-1]])
+        oracle.draft_step(L, e, None, None, shifted, k2, v2, 6, want_logits=False)
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_catchup_split_equals_whole_and_cold_prompt_uses_a_zero_hidden():
+    L, kc, vc, e, target, pending = _catchup_case(seed=28, m=6)
+    k1, v1 = kc.copy(), vc.copy()
+    oracle.append_kv(L, e, None, None, pending, target, k1, v1, 6)
+    k2, v2 = kc.copy(), vc.copy()
+    oracle.append_kv(L, e[:2], None, None, pending, target[:2], k2, v2, 6)
+    oracle.append_kv(L, e[2:], None, None, target[1], target[2:], k2, v2, 8)  # the next call's pending is t_1
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    k3, v3 = kc.copy(), vc.copy()
+    oracle.append_kv(L, e, None, None, None, target, k3, v3, 6)
+    k4, v4 = kc.copy(), vc.copy()
+    oracle.append_kv(L, e, None, None, np.zeros(L.hidden, np.float32), target, k4, v4, 6)
+    assert np.array_equal(k3, k4) and np.array_equal(v3, v4)
+    assert not np.array_equal(k3, k1)
+    assert np.array_equal(k1[:, :6], kc[:, :6]) and np.array_equal(k1[:, 12:], kc[:, 12:])  # other rows untouched
