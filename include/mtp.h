@@ -221,6 +221,24 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
                           int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,
                           float* logits_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Cache catch-up after a target batch ([mtp.rs] `process_target_batch` and
+ * `append_attention_kv`): for rows r = 0 .. m-1 at positions cache_len + r,
+ *   shifted_r = pending_h (zero when NULL) for r = 0, target_h row r-1 after;
+ *   u_r = eh_proj [rms(e_r; gamma_e) ; rms(shifted_r; gamma_h)]
+ * (e_r as in mtp_draft_step: embed_table[tokens[r]] or row r of e), and only
+ * the attention's K/V side runs on u_r: rms(u_r; gamma_attn), the wk and wv
+ * projections, the per-head k norm when set, the rotary step; the K and V
+ * rows are written at cache_len + r.  No attention, FFN or logits.
+ * target_h [m][H] is the target model's post-output-norm hidden of the same
+ * m tokens; pending_h [H] the one left over from the previous batch.  m may
+ * exceed MTP_MAX_ROWS (the call works in pieces of MTP_MAX_ROWS rows, so a
+ * whole prompt can be caught up in one call); cache_len + m <= capacity.
+ * ws needs mtp_append_kv_workspace_size(L) bytes. */
+size_t mtp_append_kv_workspace_size(const mtp_layer* L);
+mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                         const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                         int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

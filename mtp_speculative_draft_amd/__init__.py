@@ -76,6 +76,8 @@ _SIGS = {
     "mtp_ffn_moe_q": (_I, [_P, _P, _F, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_lmhead_argmax": (_I, [_P, _P, _F, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_draft_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "mtp_append_kv_workspace_size": (_Z, [_P]),
+    "mtp_append_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]),
 }
 
 
@@ -373,3 +375,14 @@ def mtp_draft_step(layer: DeviceLayer, e, tokens, embed_table, h, k_cache, v_cac
                                 _ptr(ids_out), _ptr(hidden_out), _ptr(logits_out), _ptr(ws), _nbytes(ws),
                                 _stream(h)), "mtp_draft_step")
     return ids_out, hidden_out
+
+
+def mtp_append_kv(layer: DeviceLayer, e, tokens, embed_table, pending_h, target_h, k_cache, v_cache, cache_len: int,
+                  ws=None):
+    """Cache catch-up after a target batch: writes K/V rows cache_len .. cache_len+m-1."""
+    _f32(target_h, "target_h")
+    m = _rows(target_h)
+    ws = _ws(int(lib().mtp_append_kv_workspace_size(C.byref(layer.desc))), target_h, ws)
+    _check(lib().mtp_append_kv(C.byref(layer.desc), _ptr(e), _ptr(tokens), _ptr(embed_table), _ptr(pending_h),
+                               _ptr(target_h), _ptr(k_cache), _ptr(v_cache), int(cache_len), int(k_cache.shape[1]),
+                               m, _ptr(ws), _nbytes(ws), _stream(target_h)), "mtp_append_kv")

@@ -429,6 +429,97 @@ size_t mtp_draft_step_workspace_size(const mtp_layer* L, int32_t cache_len, int3
     return c.off;
 }
 
+size_t mtp_append_kv_workspace_size(const mtp_layer* L) {
+    if (!L || L->hidden < 1 || L->n_kv_heads < 1 || L->head_dim < 1) return 0;
+    Carve c{nullptr};
+    c.take<float>((size_t)MTP_MAX_ROWS * L->hidden);                           // shifted hidden
+    c.take<float>((size_t)MTP_MAX_ROWS * L->hidden);                           // u
+    c.take<float>((size_t)MTP_MAX_ROWS * 2 * L->n_kv_heads * L->head_dim);     // k, v
+    return c.off;
+}
+
+mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                         const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                         int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if (m < 1) return fail(MTP_ERR_INVALID_ARG, "m=%d (at least 1)", m);
+    if ((s = check_layer_attn(L))) return s;
+    const int H = L->hidden;
+    if (!k_cache || !v_cache) return fail(MTP_ERR_INVALID_ARG, "k_cache/v_cache is NULL");
+    if (!a16(k_cache) || !a16(v_cache)) return fail(MTP_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+    if (k_cache == v_cache) return fail(MTP_ERR_INVALID_ARG, "k_cache and v_cache alias");
+    if (cache_len < 0 || capacity < 1) return fail(MTP_ERR_INVALID_ARG, "cache_len=%d capacity=%d", cache_len, capacity);
+    if ((int64_t)cache_len + m > capacity)
+        return fail(MTP_ERR_INVALID_ARG, "cache overflow: cache_len %d + m %d > capacity %d", cache_len, m, capacity);
+    if ((s = check_vec(target_h, "target_h")) || (s = check_vec(L->gamma_e, "gamma_e")) ||
+        (s = check_vec(L->gamma_h, "gamma_h")) || (s = check_q4(&L->eh_proj, "eh_proj")))
+        return s;
+    if (pending_h && (s = check_vec(pending_h, "pending_h"))) return s;
+    if (L->eh_proj.n != H || L->eh_proj.k != 2 * H) return fail(MTP_ERR_INVALID_ARG, "eh_proj must be [hidden][2*hidden]");
+    if (!tokens && !e) return fail(MTP_ERR_INVALID_ARG, "give e or tokens");
+    if (e && (s = check_vec(e, "e"))) return s;
+    if (tokens && (!a4(tokens) || !embed_table)) return fail(MTP_ERR_INVALID_ARG, "tokens needs an aligned pointer and embed_table");
+    if (embed_table && !a16(embed_table)) return fail(MTP_ERR_INVALID_ARG, "embed_table misaligned");
+    if ((s = check_ws(ws, ws_bytes, mtp_append_kv_workspace_size(L)))) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    Carve c{static_cast<char*>(ws)};
+    float* shifted = c.take<float>((size_t)MTP_MAX_ROWS * H);
+    float* u = c.take<float>((size_t)MTP_MAX_ROWS * H);
+    const int kvn = L->n_kv_heads * L->head_dim;
+    float* kv = c.take<float>((size_t)MTP_MAX_ROWS * 2 * kvn);
+    AttnParams a{};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.capacity = capacity;
+    a.nkv = L->n_kv_heads;
+    a.d = L->head_dim;
+    a.log2_theta = log2(L->rope_theta);
+    a.gk = L->gamma_k_head;
+    a.eps = L->eps;
+    a.rot = L->rotary_dim > 0 ? L->rotary_dim : L->head_dim;
+    hipError_t err = hipSuccess;
+    // pieces of MTP_MAX_ROWS rows; after the first piece the shifted hidden
+    // of row c0 + r is the target's row c0 + r - 1, a contiguous run
+    for (int c0 = 0; c0 < m && err == hipSuccess; c0 += MTP_MAX_ROWS) {
+        const int mc = m - c0 < MTP_MAX_ROWS ? m - c0 : MTP_MAX_ROWS;
+        const float* hrows = target_h + (int64_t)(c0 - 1) * H;
+        if (c0 == 0) {
+            if ((err = launch_shift_rows(pending_h, target_h, shifted, mc, H, st)) != hipSuccess) break;
+            hrows = shifted;
+        }
+        GemvParams p{};
+        p.w[0] = qmat(L->eh_proj);
+        p.nmat = 1;
+        p.N = H;
+        p.K = 2 * H;
+        p.H = H;
+        p.x0 = e ? e + (int64_t)c0 * H : nullptr;
+        p.x1 = hrows;
+        p.tokens = tokens ? tokens + c0 : nullptr;
+        p.table = embed_table;
+        p.vocab = L->vocab;
+        p.g0 = L->gamma_e;
+        p.g1 = L->gamma_h;
+        p.eps = L->eps;
+        p.y = u;
+        if ((err = run_gemv(FMT_Q4, PRO_CONCAT, EPI_STORE, mc, p, default_blocks(), st)) != hipSuccess) break;
+        GemvParams q{};
+        q.w[0] = qmat(L->wk);
+        q.w[1] = qmat(L->wv);
+        q.nmat = 2;
+        q.N = 2 * kvn;
+        q.K = H;
+        q.x0 = u;
+        q.g0 = L->gamma_attn;
+        q.eps = L->eps;
+        q.y = kv;
+        if ((err = run_gemv(FMT_Q4, PRO_RMS, EPI_STORE, mc, q, default_blocks(), st)) != hipSuccess) break;
+        err = launch_append_kv(a, kv, mc, cache_len + c0, st);
+    }
+    return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_append_kv");
+}
+
 mtp_status mtp_dequant_q4(const mtp_q4* w, float* out, void* stream) {
     mtp_status s = check_q4(w, "w");
     if (s) return s;

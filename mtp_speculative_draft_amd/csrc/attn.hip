@@ -372,6 +372,75 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     }
 }
 
+// ---------------------------------------------------------------------------
+// Cache catch-up after a target batch ([mtp.rs] `process_target_batch`,
+// `append_attention_kv`): the K/V side of the attention alone.
+// ---------------------------------------------------------------------------
+// The hidden rows of a batch's first piece, shifted one row right: row 0 is
+// the pending hidden (zero when there is none), row r the target's row r-1.
+__global__ void __launch_bounds__(256) k_shift_rows(const float* pending, const float* target, float* out, int m,
+                                                    int H) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)m * H) return;
+    const int r = (int)(idx / H), c = (int)(idx % H);
+    out[idx] = r == 0 ? (pending ? pending[c] : 0.0f) : target[(int64_t)(r - 1) * H + c];
+}
+
+// One wave per (row, KV head): lane i holds dims i and i + d/2 of the row's k
+// (kv [m][2 nkv d]: k heads, then v heads), applies the per-head norm and the
+// rotary step at position pos0 + row exactly as k_attn_partial does for a new
+// row, and writes k and v into the cache.
+template <bool VAR>
+__global__ void __launch_bounds__(64) k_append_kv(const AttnParams p, const float* kv, int pos0) {
+    const int r = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+    const float* kr = kv + (int64_t)r * 2 * p.nkv * kD + g * kD;
+    const float* vr = kr + p.nkv * kD;
+    float a = kr[lane], b = kr[lane + kD / 2];
+    const float va = vr[lane], vb = vr[lane + kD / 2];
+    if (VAR && p.gk) {
+        const float inv = rsqrtf(wave_sum(a * a + b * b) * (1.0f / kD) + p.eps);
+        a = a * inv * p.gk[lane];
+        b = b * inv * p.gk[lane + kD / 2];
+    }
+    const int pos = pos0 + r;
+    const int rot = VAR ? p.rot : kD, rh = rot / 2;
+    float ra, rb;
+    if (rot == kD) {
+        float cs, sn;
+        rotary((double)pos, exp2(-(2.0 * (double)lane / (double)kD) * p.log2_theta), cs, sn);
+        ra = a * cs - b * sn;
+        rb = a * sn + b * cs;
+    } else {
+        const float o = __shfl_xor(a, rh);
+        const int j = lane & (rh - 1);
+        float cs, sn;
+        rotary((double)pos, exp2(-(2.0 * (double)j / (double)rot) * p.log2_theta), cs, sn);
+        ra = lane >= rot ? a : (lane < rh ? a * cs - o * sn : o * sn + a * cs);
+        rb = b;
+    }
+    float* kd = p.k_cache + ((int64_t)g * p.capacity + pos) * kD;
+    float* vd = p.v_cache + ((int64_t)g * p.capacity + pos) * kD;
+    kd[lane] = ra;
+    kd[lane + kD / 2] = rb;
+    vd[lane] = va;
+    vd[lane + kD / 2] = vb;
+}
+
+hipError_t launch_shift_rows(const float* pending, const float* target, float* out, int m, int H, hipStream_t st) {
+    const int64_t n = (int64_t)m * H;
+    hipLaunchKernelGGL(k_shift_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pending, target, out, m, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_kv(const AttnParams& p, const float* kv, int m, int pos0, hipStream_t st) {
+    const dim3 grid((unsigned)m, (unsigned)p.nkv), block(kWave);
+    if (p.gk || p.rot != kD)
+        hipLaunchKernelGGL(k_append_kv<true>, grid, block, 0, st, p, kv, pos0);
+    else
+        hipLaunchKernelGGL(k_append_kv<false>, grid, block, 0, st, p, kv, pos0);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int hm = (p.nh / p.nkv) * p.m;
     const int Z = (hm + kSliceHM - 1) / kSliceHM;

@@ -143,6 +143,13 @@ struct AttnParams {
 };
 constexpr int kAttnChunk = 32;
 hipError_t launch_attention(const AttnParams& p, hipStream_t stream);
+// Cache catch-up: out [m][H] = (pending or 0, target rows 0 .. m-2); and the
+// K/V side of the attention for m rows of kv [m][2 nkv d] at positions
+// pos0 .. pos0+m-1 (fields used: k_cache, v_cache, capacity, nkv, log2_theta,
+// gk, eps, rot).
+hipError_t launch_shift_rows(const float* pending, const float* target, float* out, int m, int H,
+                             hipStream_t stream);
+hipError_t launch_append_kv(const AttnParams& p, const float* kv, int m, int pos0, hipStream_t stream);
 
 // MoE (8-bit experts).
 struct MoeParams {

@@ -165,3 +165,16 @@ def test_attention_variant_fields_are_validated():
     L.gamma_q_head = FAKE  # without gamma_k_head
     assert status(L) == mtp.MTP_ERR_INVALID_ARG
     assert b"gamma_k_head" in lib.mtp_last_error()
+
+
+def test_append_kv_rejects_overflow_and_empty_batches():
+    lib = mtp.lib()
+    L = _layer()
+    need = lib.mtp_append_kv_workspace_size(C.byref(L))
+    assert need > 0
+    args = lambda cache_len, cap, m, ws_bytes: (C.byref(L), FAKE, None, None, None, FAKE * 2, FAKE * 3, FAKE * 4,  # noqa: E731
+                                                cache_len, cap, m, FAKE * 5, ws_bytes, None)
+    assert lib.mtp_append_kv(*args(10, 13, 4, need)) == mtp.MTP_ERR_INVALID_ARG
+    assert b"overflow" in lib.mtp_last_error()
+    assert lib.mtp_append_kv(*args(10, 14, 0, need)) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_append_kv(*args(10, 14, 4, need - 1)) == mtp.MTP_ERR_WORKSPACE

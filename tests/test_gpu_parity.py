@@ -577,3 +577,60 @@ def test_draft_step_moe_chain_and_verify(H, E, inter, top_k, vocab):
     assert v_ids.tolist() == ver[0].tolist()
     _close(v_hid, ver[1], "verify hidden")
     _close(v_log, ver[2], "verify logits")
+
+
+# --------------------------------------------------------------------------
+# cache catch-up after a target batch ([mtp.rs] `process_target_batch`)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("m,pending,variant,use_tokens", [(1, True, None, False), (4, False, None, True),
+                                                          (8, True, "all_rot32", False), (13, True, None, True),
+                                                          (40, False, "qknorm", False), (3, True, "rot64", True)])
+def test_append_kv_small(m, pending, variant, use_tokens):
+    _say(f"append_kv m={m} pending={pending} variant={variant} tokens={use_tokens}")
+    extra = _VARIANTS[variant] if variant else {}
+    S = synth.config4_step(seed_extra=3000 + m, cache_len=20, capacity=20 + m + 3, hidden=256, n_heads=4,
+                           n_kv_heads=2, head_dim=128, vocab=500, ffn_inter=64, **extra)
+    L = S.layer
+    g = synth.rng(115, m)
+    target = synth.normal(g, (m, L.hidden))
+    pend = synth.normal(g, (L.hidden,)) if pending else None
+    tokens = g.integers(0, L.vocab, size=m).astype(np.int32) if use_tokens else None
+    e = None if use_tokens else synth.normal(g, (m, L.hidden))
+    kr, vr = S.k_cache.copy(), S.v_cache.copy()
+    oracle.append_kv(L, e, tokens, S.table if use_tokens else None, pend, target, kr, vr, S.cache_len)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    mtp.mtp_append_kv(mtp.DeviceLayer(L), None if e is None else _t(e), None if tokens is None else _t(tokens),
+                      _t(S.table) if use_tokens else None, None if pend is None else _t(pend), _t(target), dk, dv,
+                      S.cache_len)
+    gk, gv = _np(dk), _np(dv)
+    L0 = S.cache_len
+    _close(gk[:, L0:L0 + m], kr[:, L0:L0 + m], "k rows")
+    _close(gv[:, L0:L0 + m], vr[:, L0:L0 + m], "v rows")
+    assert np.array_equal(gk[:, :L0], S.k_cache[:, :L0]) and np.array_equal(gk[:, L0 + m:], S.k_cache[:, L0 + m:])
+    assert np.array_equal(gv[:, :L0], S.v_cache[:, :L0]) and np.array_equal(gv[:, L0 + m:], S.v_cache[:, L0 + m:])
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_append_kv_config4_shape_equals_draft_step_rows(m):
+    """At the full layer size the catch-up writes the rows the full draft forward
+    writes for the shifted hidden (pending, t_0, .., t_{m-2})."""
+    _say(f"append_kv config4 m={m}")
+    S = synth.config4_step(seed_extra=4000 + m)
+    L = S.layer
+    g = synth.rng(116, m)
+    target, pend = synth.normal(g, (m, L.hidden)), synth.normal(g, (L.hidden,))
+    e = synth.normal(g, (m, L.hidden))
+    dl = mtp.DeviceLayer(L)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    mtp.mtp_append_kv(dl, _t(e), None, None, _t(pend), _t(target), dk, dv, S.cache_len)
+    sk, sv = _t(S.k_cache), _t(S.v_cache)
+    shifted = np.concatenate([pend[None], target[:-1]])
+    mtp.mtp_draft_step(dl, _t(e), None, None, _t(shifted), sk, sv, S.cache_len)
+    L0 = S.cache_len
+    a, b = _np(dk)[:, L0:L0 + m], _np(sk)[:, L0:L0 + m]
+    _say(f"  catch-up vs draft-step k rows: max |diff| {float(np.abs(a - b).max()):.3g}")
+    _close(a, b.astype(np.float64), "k rows vs draft step", tol=1e-5)
+    _close(_np(dv)[:, L0:L0 + m], _np(sv)[:, L0:L0 + m].astype(np.float64), "v rows vs draft step", tol=1e-5)
+    kr, vr = S.k_cache.copy(), S.v_cache.copy()
+    oracle.append_kv(L, e, None, None, pend, target, kr, vr, L0)
+    _close(a, kr[:, L0:L0 + m], "k rows vs oracle")
