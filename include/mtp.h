@@ -239,6 +239,27 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
                          const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
                          int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Speculative round bookkeeping (host only; [mimo.rs] `mimo_spec_round`)  */
+/* ---------------------------------------------------------------------- */
+#define MTP_MAX_DRAFT 16
+typedef struct {
+    uint64_t rounds, drafted, accepted;
+    uint64_t accept_hist[MTP_MAX_DRAFT + 1];  /* rounds that accepted exactly a drafts */
+    uint64_t depth_drafted[MTP_MAX_DRAFT];    /* rounds that drafted at depth d */
+    uint64_t depth_accepted[MTP_MAX_DRAFT];   /* rounds whose draft at depth d was accepted */
+} mtp_stats;
+
+/* The verify step's greedy acceptance: drafts[0..k-1] are the round's drafts,
+ * target_ids[0..k] the target's greedy tokens after [pending, drafts[0..i-1]]
+ * (host int32 arrays).  Returns a, the number of leading drafts equal to the
+ * target's tokens (0..k); target_ids[a] is the round's bonus token, the
+ * target's KV keeps a + 1 new rows and the draft layer's cache is caught up
+ * over them with mtp_append_kv.  When stats is not NULL the round is added
+ * to it.  Returns -1 (and records nothing) for k outside 1..MTP_MAX_DRAFT
+ * or a NULL array. */
+int32_t mtp_accept(const int32_t* drafts, const int32_t* target_ids, int32_t k, mtp_stats* stats);
+
 #ifdef __cplusplus
 }
 #endif

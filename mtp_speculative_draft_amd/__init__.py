@@ -39,6 +39,16 @@ class MtpQ8(C.Structure):
                 ("n_experts", C.c_int32)]
 
 
+MTP_MAX_DRAFT = 16
+
+
+class MtpStats(C.Structure):
+    """Speculative round statistics (mtp_stats)."""
+    _fields_ = [("rounds", C.c_uint64), ("drafted", C.c_uint64), ("accepted", C.c_uint64),
+                ("accept_hist", C.c_uint64 * (MTP_MAX_DRAFT + 1)), ("depth_drafted", C.c_uint64 * MTP_MAX_DRAFT),
+                ("depth_accepted", C.c_uint64 * MTP_MAX_DRAFT)]
+
+
 class MtpLayer(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("vocab", C.c_int32), ("ffn_kind", C.c_int32),
@@ -78,6 +88,7 @@ _SIGS = {
     "mtp_draft_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "mtp_append_kv_workspace_size": (_Z, [_P]),
     "mtp_append_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]),
+    "mtp_accept": (_I, [_P, _P, _I, _P]),
 }
 
 
@@ -386,3 +397,16 @@ def mtp_append_kv(layer: DeviceLayer, e, tokens, embed_table, pending_h, target_
     _check(lib().mtp_append_kv(C.byref(layer.desc), _ptr(e), _ptr(tokens), _ptr(embed_table), _ptr(pending_h),
                                _ptr(target_h), _ptr(k_cache), _ptr(v_cache), int(cache_len), int(k_cache.shape[1]),
                                m, _ptr(ws), _nbytes(ws), _stream(target_h)), "mtp_append_kv")
+
+
+def mtp_accept(drafts, target_ids, stats: Optional[MtpStats] = None) -> int:
+    """Greedy acceptance of one round (host int32 sequences); returns a."""
+    d = np.ascontiguousarray(np.asarray(drafts, dtype=np.int32).reshape(-1))
+    t = np.ascontiguousarray(np.asarray(target_ids, dtype=np.int32).reshape(-1))
+    k = d.size
+    if t.size != k + 1:
+        raise ValueError("target_ids needs k + 1 entries")
+    a = lib().mtp_accept(d.ctypes.data, t.ctypes.data, k, None if stats is None else C.byref(stats))
+    if a < 0:
+        raise MtpError(MTP_ERR_INVALID_ARG, "mtp_accept", lib().mtp_last_error().decode())
+    return int(a)

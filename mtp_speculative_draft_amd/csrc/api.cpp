@@ -520,6 +520,26 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
     return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_append_kv");
 }
 
+int32_t mtp_accept(const int32_t* drafts, const int32_t* target_ids, int32_t k, mtp_stats* stats) {
+    if (!drafts || !target_ids || k < 1 || k > MTP_MAX_DRAFT) {
+        fail(MTP_ERR_INVALID_ARG, "mtp_accept: k=%d (1..%d) and both arrays are required", k, MTP_MAX_DRAFT);
+        return -1;
+    }
+    int32_t a = 0;
+    while (a < k && drafts[a] == target_ids[a]) ++a;
+    if (stats) {
+        stats->rounds += 1;
+        stats->drafted += (uint64_t)k;
+        stats->accepted += (uint64_t)a;
+        stats->accept_hist[a] += 1;
+        for (int32_t d = 0; d < k; ++d) {
+            stats->depth_drafted[d] += 1;
+            if (d < a) stats->depth_accepted[d] += 1;
+        }
+    }
+    return a;
+}
+
 mtp_status mtp_dequant_q4(const mtp_q4* w, float* out, void* stream) {
     mtp_status s = check_q4(w, "w");
     if (s) return s;

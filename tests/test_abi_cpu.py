@@ -178,3 +178,33 @@ def test_append_kv_rejects_overflow_and_empty_batches():
     assert b"overflow" in lib.mtp_last_error()
     assert lib.mtp_append_kv(*args(10, 14, 0, need)) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_append_kv(*args(10, 14, 4, need - 1)) == mtp.MTP_ERR_WORKSPACE
+
+
+def test_accept_is_the_longest_matching_prefix_and_records_the_round():
+    st = mtp.MtpStats()
+    assert mtp.mtp_accept([5, 7, 9], [5, 7, 9, 11], st) == 3  # all drafts accepted, 11 is the bonus token
+    assert mtp.mtp_accept([5, 7, 9], [5, 8, 9, 11], st) == 1  # a later match after a miss does not count
+    assert mtp.mtp_accept([5, 7, 9], [4, 7, 9, 11], st) == 0
+    assert mtp.mtp_accept([1], [1, 2], st) == 1
+    assert (st.rounds, st.drafted, st.accepted) == (4, 10, 5)
+    assert list(st.accept_hist)[:4] == [1, 2, 0, 1]
+    assert list(st.depth_drafted)[:3] == [4, 3, 3] and list(st.depth_accepted)[:3] == [3, 1, 1]
+    lib = mtp.lib()
+    arr = (C.c_int32 * 20)()
+    assert lib.mtp_accept(arr, arr, 0, None) == -1
+    assert lib.mtp_accept(arr, arr, mtp.MTP_MAX_DRAFT + 1, None) == -1
+    assert lib.mtp_accept(None, arr, 2, None) == -1
+    assert mtp.mtp_accept([3, 3], [3, 3, 0]) == 2  # stats are optional
+
+
+def test_stats_struct_layout_matches_the_header(tmp_path):
+    import subprocess
+    src = tmp_path / "stats.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "mtp.h"\n'
+                   'int main(void) { printf("%zu %zu %zu\\n", sizeof(mtp_stats), offsetof(mtp_stats, accept_hist), '
+                   'offsetof(mtp_stats, depth_accepted)); return 0; }\n')
+    exe = tmp_path / "stats"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(mtp.HEADER), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    S = mtp.MtpStats
+    assert got == [C.sizeof(S), S.accept_hist.offset, S.depth_accepted.offset]

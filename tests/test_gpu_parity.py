@@ -634,3 +634,65 @@ def test_append_kv_config4_shape_equals_draft_step_rows(m):
     kr, vr = S.k_cache.copy(), S.v_cache.copy()
     oracle.append_kv(L, e, None, None, pend, target, kr, vr, L0)
     _close(a, kr[:, L0:L0 + m], "k rows vs oracle")
+
+
+def _round_oracle(S, pending_tok, pending_h, target_h_rows):
+    """The oracle's round: 3 chained drafts, acceptance of 2 (the target's third
+    token differs), catch-up over [pending, d1, d2], the next round's first draft."""
+    L, L0 = S.layer, S.cache_len
+    kr, vr = S.k_cache.copy(), S.v_cache.copy()
+    toks, hs, margins = [pending_tok], [pending_h], []
+    for k in range(3):
+        ids, hid, lg = oracle.draft_step(L, None, np.array([toks[-1]], np.int32), S.table, hs[-1][None], kr, vr, L0 + k)
+        toks.append(int(ids[0]))
+        hs.append(hid[0])
+        margins.append(planting.head_margin(lg[0]))
+    drafts = toks[1:]
+    target_ids = [drafts[0], drafts[1], (drafts[2] + 1) % L.vocab, 5]
+    a = 2
+    cat_toks = np.array([pending_tok] + drafts[:a], np.int32)
+    oracle.append_kv(L, None, cat_toks, S.table, pending_h, target_h_rows, kr, vr, L0)
+    rid, _, lg = oracle.draft_step(L, None, np.array([target_ids[a]], np.int32), S.table, target_h_rows[a][None], kr,
+                                   vr, L0 + a + 1)
+    margins.append(planting.head_margin(lg[0]))
+    return drafts, target_ids, cat_toks, (kr, vr), int(rid[0]), min(margins)
+
+
+def test_speculative_round_accept_rollback_and_catch_up():
+    """One round on the device: K=3 drafts, a target that agrees with the first
+    two (its third token differs: a forced partial acceptance), the draft
+    layer's cache caught up over [pending, d1, d2] with the target's hidden
+    rows, then the next round's first draft from the bonus token; every cache
+    row and id against the oracle doing the same steps."""
+    for extra in range(30):
+        S = synth.config4_step(seed_extra=5001 + extra, cache_len=50, capacity=64, hidden=256, n_heads=4,
+                               n_kv_heads=2, head_dim=128, vocab=1000, ffn_inter=320)
+        g = synth.rng(117, extra)
+        pending_tok, pending_h = 17, synth.normal(g, (S.layer.hidden,))
+        target_h = synth.normal(g, (3, S.layer.hidden))
+        drafts_ref, target_ids, cat_toks, (kr, vr), next_ref, margin = _round_oracle(S, pending_tok, pending_h, target_h)
+        if margin >= 1e-2:
+            break
+    _say(f"round seed {extra}: drafts {drafts_ref} next {next_ref} margin {margin:.4f}")
+    L, L0, H = S.layer, S.cache_len, S.layer.hidden
+    dl, dtab = mtp.DeviceLayer(L), _t(S.table)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    tok = torch.tensor([pending_tok, -1, -1, -1], dtype=torch.int32, device=DEV)
+    hb = torch.empty((4, H), dtype=torch.float32, device=DEV)
+    hb[0].copy_(_t(pending_h))
+    for k in range(3):
+        mtp.mtp_draft_step(dl, None, tok[k:k + 1], dtab, hb[k:k + 1], dk, dv, L0 + k, ids_out=tok[k + 1:k + 2],
+                           hidden_out=hb[k + 1:k + 2])
+    drafts = _np(tok)[1:].tolist()
+    assert drafts == drafts_ref
+    st = mtp.MtpStats()
+    a = mtp.mtp_accept(drafts, target_ids, st)
+    assert a == 2 and st.accept_hist[2] == 1 and st.depth_accepted[1] == 1 and st.depth_accepted[2] == 0
+    mtp.mtp_append_kv(dl, None, _t(cat_toks), dtab, _t(pending_h), _t(target_h), dk, dv, L0)
+    gk, gv = _np(dk), _np(dv)
+    _close(gk[:, L0:L0 + a + 1], kr[:, L0:L0 + a + 1], "caught-up k rows")
+    _close(gv[:, L0:L0 + a + 1], vr[:, L0:L0 + a + 1], "caught-up v rows")
+    bonus, L1 = target_ids[a], L0 + a + 1
+    nid = torch.empty(1, dtype=torch.int32, device=DEV)
+    mtp.mtp_draft_step(dl, None, _t(np.array([bonus], np.int32)), dtab, _t(target_h[a][None]), dk, dv, L1, ids_out=nid)
+    assert int(_np(nid)[0]) == next_ref
