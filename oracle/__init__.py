@@ -79,6 +79,7 @@ def lib():
             "orc_ffn_dense": (None, [P, P, P, P, P, I, P]),
             "orc_moe": (I, [P, P, I, I, P, P, P, P, P, P, P, I, P, P, P, P]),
             "orc_head": (None, [P, P, C.c_float, P, I, P, P, P]),
+            "orc_head8": (None, [P, P, C.c_float, P, I, P, P, P]),
             "orc_draft_step": (I, [P, P, P, P, P, P, P, I, I, I, P, P, P]),
             "orc_append_kv": (None, [P, P, P, P, P, P, P, P, I, I, I]),
         }
@@ -297,6 +298,20 @@ def head(hidden, gamma, eps, lm):
     logits = np.empty((m, lm.n), dtype=np.float32)
     ids = np.empty(m, dtype=np.int32)
     lib().orc_head(_p(x), _p(g), float(eps), C.byref(d), m, _p(normed), _p(logits), _p(ids))
+    return normed, logits, ids
+
+
+def head8(hidden, gamma, eps, lm):
+    """8-bit lm_head (a Q8 of one matrix): returns (normed [m, H], logits [m, V], ids [m])."""
+    keep = _Keep()
+    arr = _q8_list(lm, keep)
+    x = keep.arr(np.atleast_2d(hidden), np.float32)
+    g = keep.arr(gamma, np.float32)
+    m = x.shape[0]
+    normed = np.empty((m, lm.k), dtype=np.float32)
+    logits = np.empty((m, lm.n), dtype=np.float32)
+    ids = np.empty(m, dtype=np.int32)
+    lib().orc_head8(_p(x), _p(g), float(eps), C.byref(arr[0]), m, _p(normed), _p(logits), _p(ids))
     return normed, logits, ids
 
 

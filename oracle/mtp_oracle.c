@@ -472,6 +472,21 @@ void orc_head(const float* hidden, const float* gamma, float eps, const orc_q4* 
     if (!logits_out) free(lg);
 }
 
+/* The same head over an 8-bit block lm_head ([mimo.rs]
+ * `mimo_verify_head_rows`: the verify rows' final norm, then one head panel
+ * over the q8 lm_head; the greedy pick of each row as in the 4-bit head). */
+void orc_head8(const float* hidden, const float* gamma, float eps, const orc_q8* lm_head, int32_t m,
+               float* normed_out, float* logits_out, int32_t* ids_out) {
+    const int32_t H = lm_head->k, V = lm_head->n;
+    float* yn = normed_out ? normed_out : (float*)xmalloc(sizeof(float) * (size_t)m * H);
+    float* lg = logits_out ? logits_out : (float*)xmalloc(sizeof(float) * (size_t)m * V);
+    orc_rmsnorm(hidden, gamma, m, H, eps, yn);
+    orc_gemv8(lm_head, yn, m, lg);
+    for (int32_t r = 0; r < m; ++r) ids_out[r] = orc_argmax(lg + (size_t)r * V, V);
+    if (!normed_out) free(yn);
+    if (!logits_out) free(lg);
+}
+
 /* One draft-layer forward over m rows at positions cache_len .. cache_len+m-1
  * ([mimo.rs] module doc "The draft forward" and `mimo_mtp_block_with_probe`;
  * [mtp.rs] `forward_draft_body` then `forward_shared_head_greedy`):

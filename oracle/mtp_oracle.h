@@ -101,6 +101,8 @@ int32_t orc_moe(const float* x, const float* router, int32_t n_experts, int32_t 
                 float* router_logits);
 void orc_head(const float* hidden, const float* gamma, float eps, const orc_q4* lm_head, int32_t m,
               float* normed_out, float* logits_out, int32_t* ids_out);
+void orc_head8(const float* hidden, const float* gamma, float eps, const orc_q8* lm_head, int32_t m,
+               float* normed_out, float* logits_out, int32_t* ids_out);
 void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
                    const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
                    int32_t cache_len, int32_t capacity, int32_t m);

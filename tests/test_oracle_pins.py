@@ -625,3 +625,23 @@ def test_catchup_split_equals_whole_and_cold_prompt_uses_a_zero_hidden():
     assert np.array_equal(k3, k4) and np.array_equal(v3, v4)
     assert not np.array_equal(k3, k1)
     assert np.array_equal(k1[:, :6], kc[:, :6]) and np.array_equal(k1[:, 12:], kc[:, 12:])  # other rows untouched
+
+
+def test_head8_diagonal_weight_picks_the_largest_normed_entry():
+    """An 8-bit lm_head whose row v is code 1 at column v (scale 1) gives logits
+    equal to the normed hidden, so the ids are the rows' argmax of x * gamma
+    (the norm's positive factor does not move it); a scale of 2 on one row
+    doubles that logit exactly."""
+    g = np.random.default_rng(31)
+    H = 64
+    codes = np.zeros((1, H, H), np.int8)
+    codes[0, np.arange(H), np.arange(H)] = 1
+    scales = np.ones((1, H, H // 32), np.float32)
+    x, gam = synth.normal(g, (3, H)), synth.gamma(g, H)
+    normed, logits, ids = oracle.head8(x, gam, 1e-6, synth.Q8(codes, scales))
+    assert np.array_equal(logits, normed)
+    assert ids.tolist() == np.argmax(x.astype(np.float64) * gam, axis=1).tolist()
+    scales2 = scales.copy()
+    scales2[0, 5, :] = 2.0
+    _, logits2, _ = oracle.head8(x, gam, 1e-6, synth.Q8(codes, scales2))
+    assert np.array_equal(logits2[:, 5], 2.0 * normed[:, 5])
