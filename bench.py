@@ -322,6 +322,25 @@ def op_timings(torch, mtp, synth, dev, K, W):
     del c1
     torch.cuda.empty_cache()
 
+    # 8-bit lm_head (vocab 151936 x 2048, int8 + one f32 scale per 32) with the
+    # fused final norm and greedy pick, m = 1 and 4, two rotated copies (700 MB)
+    g8 = synth.rng(8)
+    lm8 = synth.q8_weight(g8, 1, 151936, 2048)
+    c8 = [mtp.DeviceQ8(lm8, dev) for _ in range(2)]
+    del lm8
+    gam8 = torch.ones(2048, device=dev)
+    ws8 = torch.zeros(mtp.mtp_lmhead_workspace_size(151936, 4), dtype=torch.uint8, device=dev)
+    ids8 = torch.empty(4, dtype=torch.int32, device=dev)
+    b8 = 151936 * 2048 + 151936 * 64 * 4
+    for m in (1, 4):
+        xm = torch.randn((m, 2048), device=dev)
+        us = event_us(torch, dev, lambda i: mtp.mtp_lmhead_argmax_q8(xm, gam8, 1e-6, c8[i % 2], ids_out=ids8[:m],
+                                                                      ws=ws8), n, W)
+        out[f"lmhead_q8_151936x2048_m{m}"] = {"us": round(us, 3), "bytes": b8, "GB/s": round(b8 / us / 1e3, 1),
+                                              "frac": round(b8 / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del c8
+    torch.cuda.empty_cache()
+
     M = synth.config3_moe(4)
     copies = []
     for _ in range(3):  # 3 x 906 MB expert stacks

@@ -201,6 +201,15 @@ mtp_status mtp_lmhead_argmax(const float* hidden, const float* gamma, float eps,
                              float* normed_out, float* logits_out, int32_t* ids_out, int32_t m, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* The same over an 8-bit block lm_head (one matrix, n_experts = 1):
+ * [mimo.rs] `mimo_verify_head_rows`, the verify rows' final norm and one head
+ * panel over the q8 lm_head, here with the greedy pick fused.  Same
+ * arguments, workspace (mtp_lmhead_workspace_size) and argmax-state rule as
+ * mtp_lmhead_argmax. */
+mtp_status mtp_lmhead_argmax_q8(const float* hidden, const float* gamma, float eps, const mtp_q8* lm_head,
+                                float* normed_out, float* logits_out, int32_t* ids_out, int32_t m, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* One draft-layer forward over m rows at positions cache_len .. cache_len+m-1
  * ([mimo.rs] "The draft forward" and `mimo_mtp_block_with_probe`; [mtp.rs]
  * `forward_draft_body` and `forward_shared_head_greedy`):

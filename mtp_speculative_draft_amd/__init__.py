@@ -89,6 +89,7 @@ _SIGS = {
     "mtp_append_kv_workspace_size": (_Z, [_P]),
     "mtp_append_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]),
     "mtp_accept": (_I, [_P, _P, _I, _P]),
+    "mtp_lmhead_argmax_q8": (_I, [_P, _P, _F, _P, _P, _P, _P, _I, _P, _Z, _P]),
 }
 
 
@@ -410,3 +411,18 @@ def mtp_accept(drafts, target_ids, stats: Optional[MtpStats] = None) -> int:
     if a < 0:
         raise MtpError(MTP_ERR_INVALID_ARG, "mtp_accept", lib().mtp_last_error().decode())
     return int(a)
+
+
+def mtp_lmhead_argmax_q8(hidden, gamma, eps: float, lm_head: DeviceQ8, normed_out=None, logits_out=None,
+                         ids_out=None, ws=None):
+    """Fused final norm + 8-bit lm_head + greedy pick; returns ids_out."""
+    torch = _torch()
+    _f32(hidden, "hidden")
+    m = _rows(hidden)
+    ids_out = torch.empty(m, dtype=torch.int32, device=hidden.device) if ids_out is None else ids_out
+    if ws is None:  # its leading argmax state must start at zero
+        ws = torch.zeros(max(mtp_lmhead_workspace_size(lm_head.n, m), 256), dtype=torch.uint8, device=hidden.device)
+    _check(lib().mtp_lmhead_argmax_q8(_ptr(hidden), _ptr(gamma), float(eps), C.byref(lm_head.desc),
+                                      _ptr(normed_out), _ptr(logits_out), _ptr(ids_out), m, _ptr(ws), _nbytes(ws),
+                                      _stream(hidden)), "mtp_lmhead_argmax_q8")
+    return ids_out

@@ -161,13 +161,13 @@ hipError_t run_gemv(int fmt, int pro, int epi, int m, GemvParams& p, int max_blo
 
 int default_blocks() { return 4 * device_cu_count(); }
 
-hipError_t run_head(const float* hidden, const float* gamma, float eps, const mtp_q4& lm, float* normed_out,
-                    float* logits_out, int* ids, int m, const HeadWs& w, hipStream_t st) {
+hipError_t run_head_fmt(int fmt, const QMat& lm, int k, const float* hidden, const float* gamma, float eps,
+                        float* normed_out, float* logits_out, int* ids, int m, const HeadWs& w, hipStream_t st) {
     GemvParams p{};
-    p.w[0] = qmat(lm);
+    p.w[0] = lm;
     p.nmat = 1;
     p.N = lm.n;
-    p.K = lm.k;
+    p.K = k;
     p.x0 = hidden;
     p.g0 = gamma;
     p.eps = eps;
@@ -182,11 +182,16 @@ hipError_t run_head(const float* hidden, const float* gamma, float eps, const mt
     // persistent: one block of 8 waves per compute unit (two of 4 for more
     // than four rows), its waves sharing the block's rows at run time
     p.balance = 1;
-    const int waves = block_waves(FMT_Q4, EPI_ARGMAX, inst_m(m));
+    const int waves = block_waves(fmt, EPI_ARGMAX, inst_m(m));
     int maxb = device_cu_count() * (kMaxWaves / waves);
     if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
-    const GemvShape sh = gemv_shape(FMT_Q4, EPI_ARGMAX, m, p.N, p.K, maxb, waves);
-    return launch_gemv(FMT_Q4, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
+    const GemvShape sh = gemv_shape(fmt, EPI_ARGMAX, m, p.N, p.K, maxb, waves);
+    return launch_gemv(fmt, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
+}
+
+hipError_t run_head(const float* hidden, const float* gamma, float eps, const mtp_q4& lm, float* normed_out,
+                    float* logits_out, int* ids, int m, const HeadWs& w, hipStream_t st) {
+    return run_head_fmt(FMT_Q4, qmat(lm), lm.k, hidden, gamma, eps, normed_out, logits_out, ids, m, w, st);
 }
 
 hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* vc, int cache_len, int capacity,
@@ -702,6 +707,29 @@ mtp_status mtp_lmhead_argmax(const float* hidden, const float* gamma, float eps,
     const HeadWs w = carve_head(c, m);
     hipError_t e = run_head(hidden, gamma, eps, *lm_head, normed_out, logits_out, ids_out, m, w, (hipStream_t)stream);
     return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_lmhead_argmax");
+}
+
+mtp_status mtp_lmhead_argmax_q8(const float* hidden, const float* gamma, float eps, const mtp_q8* lm_head,
+                                float* normed_out, float* logits_out, int32_t* ids_out, int32_t m, void* ws,
+                                size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_rows(m)) || (s = check_vec(hidden, "hidden")) || (s = check_vec(gamma, "gamma")) ||
+        (s = check_q8(lm_head, "lm_head")))
+        return s;
+    if (lm_head->n_experts != 1) return fail(MTP_ERR_INVALID_ARG, "lm_head: one matrix (n_experts = 1) expected");
+    if (lm_head->k > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "lm_head k=%d above %d", lm_head->k, MTP_MAX_K);
+    if (!ids_out || !a4(ids_out)) return fail(MTP_ERR_INVALID_ARG, "ids_out is NULL or misaligned");
+    if (normed_out && !a16(normed_out)) return fail(MTP_ERR_INVALID_ARG, "normed_out misaligned");
+    if (logits_out && !a4(logits_out)) return fail(MTP_ERR_INVALID_ARG, "logits_out misaligned");
+    if (normed_out == hidden && normed_out) return fail(MTP_ERR_INVALID_ARG, "normed_out aliases hidden");
+    if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
+    const size_t need = mtp_lmhead_workspace_size(lm_head->n, m);
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    Carve c{static_cast<char*>(ws)};
+    const HeadWs w = carve_head(c, m);
+    hipError_t e = run_head_fmt(FMT_Q8, qmat8(*lm_head, 0), lm_head->k, hidden, gamma, eps, normed_out, logits_out,
+                                ids_out, m, w, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_lmhead_argmax_q8");
 }
 
 mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,

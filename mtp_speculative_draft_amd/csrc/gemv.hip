@@ -1461,6 +1461,7 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
     } else {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
         if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, 1, st);
+        if (pro == PRO_RMS && epi == EPI_ARGMAX) return launch_m<FMT_Q8, PRO_RMS, EPI_ARGMAX>(m, p, sh, 1, st);
     }
     return hipErrorInvalidValue;
 }

@@ -696,3 +696,35 @@ def test_speculative_round_accept_rollback_and_catch_up():
     nid = torch.empty(1, dtype=torch.int32, device=DEV)
     mtp.mtp_draft_step(dl, None, _t(np.array([bonus], np.int32)), dtab, _t(target_h[a][None]), dk, dv, L1, ids_out=nid)
     assert int(_np(nid)[0]) == next_ref
+
+
+# --------------------------------------------------------------------------
+# 8-bit lm_head verify head ([mimo.rs] `mimo_verify_head_rows`)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_lmhead_argmax_q8_full_vocab(m):
+    _say(f"lmhead q8 vocab 151936 m={m}")
+    g = synth.rng(118)
+    lm = synth.q8_weight(g, 1, 151936, 2048)
+    x, gf = synth.normal(g, (m, 2048)), synth.gamma(g, 2048)
+    normed, logits, ids = oracle.head8(x, gf, 1e-6, lm)
+    margin = min(planting.head_margin(r) for r in logits)
+    _say(f"  oracle ids {ids.tolist()} min margin {margin:.4f}")
+    assert margin >= 1e-2
+    dl = mtp.DeviceQ8(lm)
+    nout = torch.empty((m, 2048), dtype=torch.float32, device=DEV)
+    got = _np(mtp.mtp_lmhead_argmax_q8(_t(x), _t(gf), 1e-6, dl, normed_out=nout))
+    assert got.tolist() == ids.tolist()
+    _close(_np(nout), normed, "normed")
+
+
+def test_lmhead_argmax_q8_small_vocab_eight_rows_with_logits():
+    g = synth.rng(119)
+    lm = synth.q8_weight(g, 1, 1001, 256)
+    x, gf = synth.normal(g, (8, 256)), synth.gamma(g, 256)
+    _, logits, ids = oracle.head8(x, gf, 1e-6, lm)
+    assert min(planting.head_margin(r) for r in logits) >= 1e-3
+    lo = torch.empty((8, 1001), dtype=torch.float32, device=DEV)
+    got = _np(mtp.mtp_lmhead_argmax_q8(_t(x), _t(gf), 1e-6, mtp.DeviceQ8(lm), logits_out=lo))
+    assert got.tolist() == ids.tolist()
+    _close(_np(lo), logits, "logits")
