@@ -249,6 +249,36 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
                          int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* Multi-layer draft stack ([mimo.rs] module doc "How the three layers     */
+/* chain"; `mimo_mtp_draft`)                                               */
+/* ---------------------------------------------------------------------- */
+/* One layer of the stack: its weights, its own K/V cache (row j holds
+ * position j) and the first row this round recomputes (rows before it are
+ * final from earlier rounds). */
+typedef struct {
+    const mtp_layer* layer;
+    float* k_cache;
+    float* v_cache;
+    int32_t capacity;
+    int32_t start;
+} mtp_stack_layer;
+
+/* Drafts n_layers tokens for the round that starts after the target
+ * processed position t (token x_{t+1} pending).  Layer k drafts the token for
+ * position t + k + 2: its rows j = start .. t pair the token x_{j+k+1} with
+ * the target's hidden h_j (every layer reads the target's rows, never another
+ * layer's output) at position j of its own cache, and its draft is the greedy
+ * pick of row t.  Tokens past x_{t+1} are this round's earlier drafts.
+ * tokens: device int32 [t + 2 + n_layers]: x_0 .. x_{t+1} on entry; the call
+ * writes draft k at tokens[t + 2 + k].  target_h: device f32 [t + 1][H],
+ * h_0 .. h_t.  Rows start .. t-1 go through the cache catch-up path (no
+ * logits), row t through mtp_draft_step.  All layers share hidden and vocab.
+ * ws needs mtp_stack_draft_workspace_size(layers, n_layers, t) bytes. */
+size_t mtp_stack_draft_workspace_size(const mtp_stack_layer* layers, int32_t n_layers, int32_t t);
+mtp_status mtp_stack_draft(const mtp_stack_layer* layers, int32_t n_layers, int32_t* tokens, const float* embed_table,
+                           const float* target_h, int32_t t, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* Speculative round bookkeeping (host only; [mimo.rs] `mimo_spec_round`)  */
 /* ---------------------------------------------------------------------- */
 #define MTP_MAX_DRAFT 16

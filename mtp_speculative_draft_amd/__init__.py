@@ -42,6 +42,11 @@ class MtpQ8(C.Structure):
 MTP_MAX_DRAFT = 16
 
 
+class MtpStackLayer(C.Structure):
+    _fields_ = [("layer", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("capacity", C.c_int32),
+                ("start", C.c_int32)]
+
+
 class MtpStats(C.Structure):
     """Speculative round statistics (mtp_stats)."""
     _fields_ = [("rounds", C.c_uint64), ("drafted", C.c_uint64), ("accepted", C.c_uint64),
@@ -90,6 +95,8 @@ _SIGS = {
     "mtp_append_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]),
     "mtp_accept": (_I, [_P, _P, _I, _P]),
     "mtp_lmhead_argmax_q8": (_I, [_P, _P, _F, _P, _P, _P, _P, _I, _P, _Z, _P]),
+    "mtp_stack_draft_workspace_size": (_Z, [_P, _I, _I]),
+    "mtp_stack_draft": (_I, [_P, _I, _P, _P, _P, _I, _P, _Z, _P]),
 }
 
 
@@ -426,3 +433,18 @@ def mtp_lmhead_argmax_q8(hidden, gamma, eps: float, lm_head: DeviceQ8, normed_ou
                                       _ptr(normed_out), _ptr(logits_out), _ptr(ids_out), m, _ptr(ws), _nbytes(ws),
                                       _stream(hidden)), "mtp_lmhead_argmax_q8")
     return ids_out
+
+
+def mtp_stack_draft(layers, caches, starts, tokens, embed_table, target_h, t: int, ws=None):
+    """Multi-layer draft: layers (DeviceLayer list), caches [(k, v)], starts
+    (first recomputed row per layer); tokens device int32 [t + 2 + len(layers)]
+    gets draft k at t + 2 + k.  Returns tokens."""
+    n = len(layers)
+    arr = (MtpStackLayer * n)()
+    for i, (dl, (kc, vc), st) in enumerate(zip(layers, caches, starts)):
+        arr[i] = MtpStackLayer(C.addressof(dl.desc), _ptr(kc), _ptr(vc), int(kc.shape[1]), int(st))
+    need = int(lib().mtp_stack_draft_workspace_size(arr, n, int(t)))
+    ws = _ws(need, target_h, ws)
+    _check(lib().mtp_stack_draft(arr, n, _ptr(tokens), _ptr(embed_table), _ptr(target_h), int(t), _ptr(ws),
+                                 _nbytes(ws), _stream(target_h)), "mtp_stack_draft")
+    return tokens

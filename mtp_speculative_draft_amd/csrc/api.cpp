@@ -525,6 +525,61 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
     return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_append_kv");
 }
 
+size_t mtp_stack_draft_workspace_size(const mtp_stack_layer* layers, int32_t n_layers, int32_t t) {
+    if (!layers || n_layers < 1 || t < 0) return 0;
+    size_t need = 0;
+    for (int32_t k = 0; k < n_layers; ++k) {
+        const mtp_layer* L = layers[k].layer;
+        if (!L) return 0;
+        Carve c{nullptr};
+        c.take<float>((size_t)L->hidden);  // the draft row's normed hidden (unused after the call)
+        const size_t a = mtp_draft_step_workspace_size(L, t, 1), b = mtp_append_kv_workspace_size(L);
+        c.off += a > b ? a : b;
+        need = c.off > need ? c.off : need;
+    }
+    return need;
+}
+
+mtp_status mtp_stack_draft(const mtp_stack_layer* layers, int32_t n_layers, int32_t* tokens, const float* embed_table,
+                           const float* target_h, int32_t t, void* ws, size_t ws_bytes, void* stream) {
+    if (!layers || n_layers < 1 || n_layers > MTP_MAX_DRAFT)
+        return fail(MTP_ERR_INVALID_ARG, "n_layers=%d (1..%d)", n_layers, MTP_MAX_DRAFT);
+    if (!tokens || !a4(tokens) || !embed_table || !target_h || t < 0)
+        return fail(MTP_ERR_INVALID_ARG, "tokens, embed_table and target_h are required; t=%d", t);
+    for (int32_t k = 0; k < n_layers; ++k) {
+        const mtp_stack_layer& S = layers[k];
+        if (!S.layer) return fail(MTP_ERR_INVALID_ARG, "layer %d is NULL", k);
+        if (S.layer->hidden != layers[0].layer->hidden || S.layer->vocab != layers[0].layer->vocab)
+            return fail(MTP_ERR_INVALID_ARG, "layer %d: hidden/vocab differ from layer 0", k);
+        if (S.start < 0 || S.start > t) return fail(MTP_ERR_INVALID_ARG, "layer %d: start=%d outside 0..t=%d", k, S.start, t);
+        if (t >= S.capacity) return fail(MTP_ERR_INVALID_ARG, "layer %d: row t=%d beyond capacity %d", k, t, S.capacity);
+    }
+    const size_t need = mtp_stack_draft_workspace_size(layers, n_layers, t);
+    mtp_status s;
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    const int H = layers[0].layer->hidden;
+    Carve c{static_cast<char*>(ws)};
+    float* hid = c.take<float>((size_t)H);
+    void* rest = static_cast<char*>(ws) + c.off;
+    const size_t rest_bytes = ws_bytes - c.off;
+    for (int32_t k = 0; k < n_layers; ++k) {
+        const mtp_stack_layer& S = layers[k];
+        const int n = t - S.start;  // catch-up rows start .. t-1
+        if (n > 0) {
+            // row start + r pairs x_{start+r+k+1} with h_{start+r}: the catch-up's
+            // pending hidden is h_start and its target rows h_{start+1} ..
+            if ((s = mtp_append_kv(S.layer, nullptr, tokens + S.start + k + 1, embed_table, target_h + (int64_t)S.start * H,
+                                   target_h + (int64_t)(S.start + 1) * H, S.k_cache, S.v_cache, S.start, S.capacity, n,
+                                   rest, rest_bytes, stream)))
+                return s;
+        }
+        if ((s = mtp_draft_step(S.layer, nullptr, tokens + t + k + 1, embed_table, target_h + (int64_t)t * H, S.k_cache,
+                                S.v_cache, t, S.capacity, 1, tokens + t + k + 2, hid, nullptr, rest, rest_bytes, stream)))
+            return s;
+    }
+    return MTP_OK;
+}
+
 int32_t mtp_accept(const int32_t* drafts, const int32_t* target_ids, int32_t k, mtp_stats* stats) {
     if (!drafts || !target_ids || k < 1 || k > MTP_MAX_DRAFT) {
         fail(MTP_ERR_INVALID_ARG, "mtp_accept: k=%d (1..%d) and both arrays are required", k, MTP_MAX_DRAFT);

@@ -357,6 +357,26 @@ def append_kv(L, e, tokens, table, pending_h, target_h, k_cache, v_cache, cache_
                         cache_len, k_cache.shape[1], m)
 
 
+def stack_draft(layers, caches, starts, tokens, table, target_h, t: int):
+    """Multi-layer draft ([mimo.rs] module doc "How the three layers chain",
+    `mimo_mtp_draft`): layer k's rows j = start_k .. t pair the token x_{j+k+1}
+    with the target hidden h_j at position j of its own cache; its draft is the
+    greedy pick of row t and becomes x_{t+k+2} for the next layer.  Rows before
+    t take the cache catch-up (K/V only), row t the full forward.  caches are
+    updated in place; returns the drafts."""
+    x = [int(v) for v in np.asarray(tokens).reshape(-1)[:t + 2]]
+    hs = np.atleast_2d(np.asarray(target_h, np.float32))
+    drafts = []
+    for k, (L, (kc, vc), st) in enumerate(zip(layers, caches, starts)):
+        if st < t:
+            append_kv(L, None, np.array(x[st + k + 1:t + k + 1], np.int32), table, hs[st], hs[st + 1:t + 1], kc, vc, st)
+        ids, _, _ = draft_step(L, None, np.array([x[t + k + 1]], np.int32), table, hs[t][None], kc, vc, t,
+                               want_logits=False)
+        x.append(int(ids[0]))
+        drafts.append(int(ids[0]))
+    return drafts
+
+
 def cosine(a: np.ndarray, b: np.ndarray) -> float:
     """Cosine similarity with double accumulation; NaN when a norm is zero
     (hf2q 0.1.1 forward_mlx_shared.rs, `cosine_pairwise_f32`)."""

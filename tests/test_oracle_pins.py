@@ -645,3 +645,31 @@ def test_head8_diagonal_weight_picks_the_largest_normed_entry():
     scales2[0, 5, :] = 2.0
     _, logits2, _ = oracle.head8(x, gam, 1e-6, synth.Q8(codes, scales2))
     assert np.array_equal(logits2[:, 5], 2.0 * normed[:, 5])
+
+
+# --------------------------------------------------------------------------
+# multi-layer draft stack ([mimo.rs] "How the three layers chain")
+# --------------------------------------------------------------------------
+def test_stack_draft_equals_each_layer_run_over_all_its_rows():
+    """The page's per-layer step runs the layer over rows start..t (tokens
+    x_{j+k+1}, target hidden h_j) and picks row t; the oracle's stack takes the
+    catch-up path for rows before t.  Drafts and caches agree."""
+    g = np.random.default_rng(33)
+    H, V, t = 64, 300, 9
+    layers = [synth.dense_layer(np.random.default_rng(40 + k), hidden=H, n_heads=4, n_kv_heads=2, head_dim=16,
+                                vocab=V, ffn_inter=96) for k in range(3)]
+    table = synth.normal(g, (V, H))
+    hist = synth.normal(g, (t + 1, H))
+    x = g.integers(0, V, size=t + 2).astype(np.int32)
+    starts = [6, 5, 7]
+    base = [synth.kv_cache(np.random.default_rng(50 + k), 2, starts[k], t + 4, 16) for k in range(3)]
+    caches = [(kc.copy(), vc.copy()) for kc, vc in base]
+    drafts = oracle.stack_draft(layers, caches, starts, x, table, hist, t)
+    toks = list(x)
+    for k, L in enumerate(layers):
+        kc, vc = base[k][0].copy(), base[k][1].copy()
+        rows = np.array(toks[starts[k] + k + 1:t + k + 2], np.int32)
+        ids, _, _ = oracle.draft_step(L, None, rows, table, hist[starts[k]:t + 1], kc, vc, starts[k])
+        assert int(ids[-1]) == drafts[k]
+        toks.append(int(ids[-1]))
+        assert np.array_equal(kc, caches[k][0]) and np.array_equal(vc, caches[k][1])
