@@ -208,3 +208,18 @@ def test_stats_struct_layout_matches_the_header(tmp_path):
     got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     S = mtp.MtpStats
     assert got == [C.sizeof(S), S.accept_hist.offset, S.depth_accepted.offset]
+
+
+def test_stack_draft_rejects_bad_layers():
+    lib = mtp.lib()
+    L = _layer()
+    arr = (mtp.MtpStackLayer * 2)()
+    arr[0] = mtp.MtpStackLayer(C.addressof(L), FAKE, FAKE * 2, 64, 5)
+    arr[1] = mtp.MtpStackLayer(C.addressof(L), FAKE * 3, FAKE * 4, 64, 11)  # start past t
+    ws = lib.mtp_stack_draft_workspace_size(arr, 2, 10)
+    assert ws > 0
+    assert lib.mtp_stack_draft(arr, 2, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws, None) == mtp.MTP_ERR_INVALID_ARG
+    arr[1].start = 3
+    arr[1].capacity = 10  # row t = 10 beyond capacity
+    assert lib.mtp_stack_draft(arr, 2, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_stack_draft(arr, 0, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws, None) == mtp.MTP_ERR_INVALID_ARG

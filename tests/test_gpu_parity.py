@@ -728,3 +728,47 @@ def test_lmhead_argmax_q8_small_vocab_eight_rows_with_logits():
     got = _np(mtp.mtp_lmhead_argmax_q8(_t(x), _t(gf), 1e-6, mtp.DeviceQ8(lm), logits_out=lo))
     assert got.tolist() == ids.tolist()
     _close(_np(lo), logits, "logits")
+
+
+# --------------------------------------------------------------------------
+# multi-layer draft stack ([mimo.rs] "How the three layers chain")
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("t,starts", [(9, (6, 5, 7)), (30, (10, 29, 30))])
+def test_stack_draft_three_layers(t, starts):
+    _say(f"stack draft t={t} starts={starts}")
+    H, V = 256, 1000
+    for extra in range(30):
+        g = synth.rng(120, t, extra)
+        layers = [synth.dense_layer(synth.rng(121, k, extra), hidden=H, n_heads=4, n_kv_heads=2, head_dim=128,
+                                    vocab=V, ffn_inter=320, **({"q_gated": True, "qk_norm": True} if k == 1 else {}))
+                  for k in range(3)]
+        table = synth.normal(g, (V, H))
+        hist = synth.normal(g, (t + 1, H))
+        x = g.integers(0, V, size=t + 2).astype(np.int32)
+        base = [synth.kv_cache(synth.rng(122, k, extra), 2, starts[k], t + 4, 128) for k in range(3)]
+        caches = [(kc.copy(), vc.copy()) for kc, vc in base]
+        drafts = oracle.stack_draft(layers, caches, starts, x, table, hist, t)
+        # margin gate: each layer's row-t logits from a full step on a copy of its cache
+        toks, margins = list(x), []
+        for k, L in enumerate(layers):
+            kc, vc = base[k][0].copy(), base[k][1].copy()
+            rows = np.array(toks[starts[k] + k + 1:t + k + 2], np.int32)
+            ids, _, lg = oracle.draft_step(L, None, rows, table, hist[starts[k]:t + 1], kc, vc, starts[k])
+            toks.append(int(ids[-1]))
+            margins.append(planting.head_margin(lg[-1]))
+        if min(margins) >= 1e-2:
+            break
+    _say(f"  seed {extra}: drafts {drafts} min margin {min(margins):.4f}")
+    dls = [mtp.DeviceLayer(L) for L in layers]
+    dc = [(_t(kc), _t(vc)) for kc, vc in base]
+    tok = torch.full((t + 2 + 3,), -1, dtype=torch.int32, device=DEV)
+    tok[:t + 2].copy_(_t(x))
+    mtp.mtp_stack_draft(dls, dc, starts, tok, _t(table), _t(hist), t)
+    got = _np(tok)
+    assert got[:t + 2].tolist() == x.tolist()
+    assert got[t + 2:].tolist() == drafts
+    for k in range(3):
+        gk, gv = _np(dc[k][0]), _np(dc[k][1])
+        _close(gk[:, starts[k]:t + 1], caches[k][0][:, starts[k]:t + 1], f"layer {k} k rows")
+        _close(gv[:, starts[k]:t + 1], caches[k][1][:, starts[k]:t + 1], f"layer {k} v rows")
+        assert np.array_equal(gk[:, :starts[k]], base[k][0][:, :starts[k]])
