@@ -275,8 +275,9 @@ __global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
 // their group.  A row's group term is then (s*xs) * A with A the exact
 // integer dot of the codes with the quantized activations (v_dot4).
 //
-// Work: a slot's load-sets, UB at a time (a batch), are spread evenly over
-// the waves of its gridDim.x blocks; two batches are in flight per wave, the
+// Work: a slot's load-sets are spread evenly over the waves of its
+// gridDim.x blocks and taken UB at a time (a batch); two batches are in
+// flight per wave, the
 // next one requested before the current one is reduced (a transposed
 // butterfly over the LG lanes of each row) and stored.  The first two are
 // requested before the activation setup.
@@ -479,15 +480,25 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     }
     const int g = lane % LG, rs = lane / LG;
     const int L = (p.N + RPL - 1) / RPL;  // load-sets of the slot
-    // the slot's batches are spread evenly over its gridDim.x * W waves
-    const int U = (L + UB - 1) / UB, NW = gridDim.x * W, wv = blockIdx.x * W + wid;
-    const int j_begin = UB * (int)((int64_t)wv * U / NW);
-    const int j_end = min(L, UB * (int)((int64_t)(wv + 1) * U / NW));
+    // the slot's load-sets are spread evenly over its gridDim.x * W waves (a
+    // wave's last batch may be partly past its range: those loads are skipped)
+    const int NW = gridDim.x * W, wv = blockIdx.x * W + wid;
+    const int j_begin = (int)((int64_t)wv * L / NW);
+    const int j_end = (int)((int64_t)(wv + 1) * L / NW);
 
     WFrag<FMT_Q8> wa[UB][P], wb[UB][P];
     auto load_batch = [&](WFrag<FMT_Q8> (&wf)[UB][P], int j0) {
 #pragma unroll
         for (int b = 0; b < UB; ++b) {
+            if (j0 + b >= j_end) {  // wave-uniform: past the range, a zero fragment
+#pragma unroll
+                for (int i = 0; i < P; ++i) {
+                    wf[b][i].c0 = (u32x4){0u, 0u, 0u, 0u};
+                    wf[b][i].c1 = (u32x4){0u, 0u, 0u, 0u};
+                    wf[b][i].s = 0.0f;
+                }
+                continue;
+            }
             int n = (j0 + b) * RPL + rs;
             n = n < p.N ? n : p.N - 1;
 #pragma unroll

@@ -394,7 +394,7 @@ def test_moe_small(m, shared):
     _close(y, ry, "y")
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 3, 4])
 def test_moe_config3(m):
     _say(f"moe config3 m={m}")
     for extra in range(20):
@@ -404,6 +404,22 @@ def test_moe_config3(m):
     _say(f"  seed extra {extra}")
     y, ids, gates = _run_moe(inp)
     ry, rids, rgates, _ = oracle.moe(inp)
+    assert ids.tolist() == rids.tolist()
+    _close(gates, rgates, "gates", tol=1e-5)
+    _close(y, ry, "y")
+
+
+@pytest.mark.parametrize("H,inter,m,E,top_k,shared", [(512, 2048, 3, 16, 4, 2048), (2048, 512, 4, 32, 8, None),
+                                                      (512, 512, 4, 12, 8, 512)])
+def test_moe_matrix_core_shapes(H, inter, m, E, top_k, shared):
+    """Three and four rows at K = 512 / 2048 take the matrix-core slot kernel
+    (gate/up and down with the other K), with and without a shared expert, and
+    a case where most experts are selected."""
+    _say(f"moe mma H={H} I={inter} m={m} E={E} k={top_k} shared={shared}")
+    inp, extra = _moe_case(123, m, hidden=H, n_experts=E, inter=inter, top_k=top_k, shared_inter=shared)
+    res = synth.normal(synth.rng(124, m), (m, H))
+    y, ids, gates = _run_moe(inp, residual=res)
+    ry, rids, rgates, _ = oracle.moe(inp, residual=res)
     assert ids.tolist() == rids.tolist()
     _close(gates, rgates, "gates", tol=1e-5)
     _close(y, ry, "y")
