@@ -104,7 +104,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the draft layer runs on a single MI355X; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the draft layer runs on a single MI355X; collectives and sharding are not part of it)", file=sys.stderr)
         sys.exit(2)
 
     import torch
