@@ -96,54 +96,21 @@ __global__ void __launch_bounds__(256) k_moe_router(const MoeParams p) {
 }
 
 // Top-k of one row of router logits by one wave.  Each lane keeps its share
-// of the row (experts lane + 64 j, j < NJ) in registers as 64-bit keys
-// (order-preserving value bits above the complemented index), so a step of
-// the selection is a branch-free key maximum: per lane, then across the wave.
-// Selection runs on the logits (softmax is monotonic, so the order of p is
-// the order of the logits); equal logits go to the lower expert index (-0 is
-// taken as +0) and NaN is never selected.  Lane s < top_k returns selection
-// s: its expert and its renormalised gate p_e / sum of the selected p.
-__device__ __forceinline__ unsigned long long key_max(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
-
-// One all-reduce step of the key maximum at lane class D.  The permlane
-// swaps leave a lane's own key in one result and its partner's in the other
-// (which one depends on the lane), so both are compared.
-template <int D>
-__device__ __forceinline__ unsigned long long key_step(unsigned long long k) {
-    const unsigned hi = (unsigned)(k >> 32), lo = (unsigned)k;
-    if constexpr (D >= 16) {
-        float h0, h1, l0, l1;
-        swap_halves<D>(__uint_as_float(hi), __uint_as_float(hi), h0, h1);
-        swap_halves<D>(__uint_as_float(lo), __uint_as_float(lo), l0, l1);
-        const unsigned long long k0 = ((unsigned long long)__float_as_uint(h0) << 32) | __float_as_uint(l0);
-        const unsigned long long k1 = ((unsigned long long)__float_as_uint(h1) << 32) | __float_as_uint(l1);
-        return key_max(k0, k1);
-    } else {
-        const unsigned ph = (unsigned)dpp_partner<D>((int)hi), pl = (unsigned)dpp_partner<D>((int)lo);
-        return key_max(k, ((unsigned long long)ph << 32) | pl);
-    }
-}
-
-__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
-    k = key_step<32>(k);
-    k = key_step<16>(k);
-    k = key_step<8>(k);
-    k = key_step<4>(k);
-    k = key_step<2>(k);
-    return key_step<1>(k);
-}
-
-// The logit a key was made from (inverse of argmax_key's value bits).
-__device__ __forceinline__ float key_value(unsigned long long k) {
-    const unsigned hi = (unsigned)(k >> 32);
-    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
-}
-
+// of the row (experts lane + 64 j, j < NJ) in registers, so the selection
+// makes no memory round trip.  Selection runs on the logits (softmax is
+// monotonic, so the order of p is the order of the logits).  Lane s < top_k
+// returns selection s: its expert and its renormalised gate p_e / sum of the
+// selected p; row_mask (when given) receives the row's selected experts as
+// NJ 64-bit words.
 constexpr int kTopkPerLane = kMaxE / kWave;
+// A step finds the largest remaining logit with a 32-bit wave maximum, then
+// the lowest expert index holding it with one ballot per register (index
+// lane + 64 j grows with j first).  Equal values (and -0, +0) go to the lower
+// index; NaN is never selected.  Lane s < top_k returns selection s.
 template <int NJ>
-__device__ __forceinline__ void row_topk_n(const float* l, int E, int top_k, int lane, int& my_id, float& my_gate) {
+__device__ __forceinline__ void row_topk_n(const float* l, int E, int top_k, int lane, int& my_id, float& my_gate,
+                                           unsigned long long* row_mask) {
     float lv[NJ];
-    unsigned long long key[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int e = lane + kWave * j;
@@ -151,44 +118,51 @@ __device__ __forceinline__ void row_topk_n(const float* l, int E, int top_k, int
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = lane + kWave * j;
-        mx = fmaxf(mx, lv[j]);
-        const float v = lv[j] + 0.0f;  // -0 -> +0
-        key[j] = (e < E && v == v) ? argmax_key(v, e) : 0ull;
-    }
+    for (int j = 0; j < NJ; ++j) mx = fmaxf(mx, lv[j]);
     mx = wave_max(mx);
+    unsigned taken = 0;  // bit j: expert lane + 64 j chosen
     float psum = 0.0f, my_pe = 0.0f;
     my_id = 0;
     for (int s = 0; s < top_k; ++s) {
-        unsigned long long b = key[0];
+        float lm = -INFINITY;
 #pragma unroll
-        for (int j = 1; j < NJ; ++j) b = key_max(b, key[j]);
-        b = wave_max_key(b);
-        int bi;
-        float bv;
-        if (b == 0ull) {  // only NaN logits left
+        for (int j = 0; j < NJ; ++j)
+            if (!((taken >> j) & 1u) && lane + kWave * j < E) lm = fmaxf(lm, lv[j]);
+        const float vmax = wave_max(lm);
+        int bi = -1;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const unsigned long long hit =
+                __ballot(!((taken >> j) & 1u) && lane + kWave * j < E && lv[j] == vmax);
+            if (bi < 0 && hit) bi = kWave * j + __ffsll((long long)hit) - 1;
+        }
+        float bv = vmax;
+        if (bi < 0) {  // only NaN logits left
             bi = 0;
             bv = __shfl(lv[0], 0);
-        } else {
-            bi = argmax_key_index(b);
-            bv = key_value(b);
         }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) key[j] = (lane + kWave * j == bi) ? 0ull : key[j];
+        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
         const float pe = __expf(bv - mx);
         psum += pe;
         my_id = (lane == s) ? bi : my_id;
         my_pe = (lane == s) ? pe : my_pe;
     }
     my_gate = my_pe / psum;
+    if (row_mask) {  // word j: experts 64 j .. 64 j + 63
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const unsigned long long w = __ballot((taken >> j) & 1u);
+            if (lane == 0) row_mask[j] = w;
+        }
+    }
 }
 
-__device__ __forceinline__ void row_topk(const float* l, int E, int top_k, int lane, int& my_id, float& my_gate) {
+__device__ __forceinline__ void row_topk(const float* l, int E, int top_k, int lane, int& my_id, float& my_gate,
+                                         unsigned long long* row_mask = nullptr) {
     if (E <= 4 * kWave)
-        row_topk_n<4>(l, E, top_k, lane, my_id, my_gate);
+        row_topk_n<4>(l, E, top_k, lane, my_id, my_gate, row_mask);
     else
-        row_topk_n<kTopkPerLane>(l, E, top_k, lane, my_id, my_gate);
+        row_topk_n<kTopkPerLane>(l, E, top_k, lane, my_id, my_gate, row_mask);
 }
 
 // One block of 512 threads; wave mi handles row mi (top_k <= 64: lane s
@@ -335,20 +309,17 @@ __device__ __forceinline__ int seg_base(int lane) {
 // the shared expert, -2 no such slot) and in s_gate[mi] row mi's gate for it.
 template <int W>
 __device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane, int wid,
-                                           unsigned long long* selmask, int (*rid)[kWave], float (*rgate)[kWave],
-                                           int* s_e, float* s_gate) {
+                                           unsigned long long (*rmask)[kMaxE / kWave], int (*rid)[kWave],
+                                           float (*rgate)[kWave], int* s_e, float* s_gate) {
     const int words = (p.E + kWave - 1) / kWave;
     const bool publish = blockIdx.x == 0 && slot == 0;
-    if ((int)threadIdx.x < words) selmask[threadIdx.x] = 0ull;
-    __syncthreads();
     for (int mi = wid; mi < p.m; mi += W) {
         int id;
         float gate;
-        row_topk(p.logits + (int64_t)mi * p.E, p.E, p.top_k, lane, id, gate);
+        row_topk(p.logits + (int64_t)mi * p.E, p.E, p.top_k, lane, id, gate, rmask[mi]);
         if (lane < p.top_k) {
             rid[mi][lane] = id;
             rgate[mi][lane] = gate;
-            atomicOr(&selmask[id / kWave], 1ull << (id % kWave));
             if (publish) {
                 p.expert_ids_out[mi * p.top_k + lane] = id;
                 p.gates_out[mi * p.top_k + lane] = gate;
@@ -359,7 +330,9 @@ __device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane
     if (wid != 0) return;
     // lane w < words owns mask word w; its experts take the slots after those
     // of the words before it
-    const unsigned long long mw = lane < words ? selmask[lane] : 0ull;
+    unsigned long long mw = 0ull;  // the union of the rows' masks
+    if (lane < words)
+        for (int mi = 0; mi < p.m; ++mi) mw |= rmask[mi][lane];
     const int c = __popcll(mw);
     int incl = c;
 #pragma unroll
@@ -436,7 +409,7 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     constexpr int DUP = LG * FIN / V;               // lanes holding each of them
     constexpr int RT = (EPI == EPI_SWIGLU) ? 8 : 1;  // routing state rows (gate/up launch only)
     __shared__ __align__(16) unsigned frag[M * LG * kFragWords];
-    __shared__ unsigned long long selmask[kMaxE / kWave];
+    __shared__ unsigned long long rmask[RT][kMaxE / kWave];
     __shared__ int rid[RT][kWave];
     __shared__ float rgate[RT][kWave];
     __shared__ int s_e;
@@ -463,7 +436,7 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
 
     int e;
     if (route) {
-        if constexpr (EPI == EPI_SWIGLU) route_slot<W>(p, slot, lane, wid, selmask, rid, rgate, &s_e, s_gate);
+        if constexpr (EPI == EPI_SWIGLU) route_slot<W>(p, slot, lane, wid, rmask, rid, rgate, &s_e, s_gate);
         __syncthreads();
         e = s_e;
         if (e == -2) return;
