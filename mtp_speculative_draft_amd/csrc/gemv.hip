@@ -789,6 +789,15 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
 // MFMAs (16x16x4) fed with the biases as loaded.  Two DPP adds then fold the
 // group halves and the hi/lo columns, and the result is
 // xs * (256 hi + lo + bias sums), the same quantity as in the vector path.
+//
+// 8-bit weights (int8 codes, one scale per group, no bias) use the same unit,
+// B columns and scaling.  A row is 2048 bytes, so a unit is 32 loads, and
+// load t of lane l is row l%16's bytes 64 t + 16 (l/16) .. +15, which is
+// already the A operand of one MFMA over the group pair 2t, 2t + 1 (quarters
+// 0-1 hold the first group, 2-3 the second).  The B operand holds the
+// activations in natural order: feature f is byte f%16 of quarter (f/16)%4 of
+// MFMA f/64, in the columns of group parity (f/32)%2.  With no bias there is
+// no f32 MFMA, and the result is xs * (256 hi + lo).
 // ---------------------------------------------------------------------------
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
@@ -846,11 +855,12 @@ __device__ __forceinline__ void mma_load_x(const GemvParams& p, const View& v, i
 // word of 8 features unpacks to the even features, then the odd ones, and
 // lanes 2k and 2k+1 hold that word's first and last four features, so one
 // quad exchange forms each operand word.  Ends with a block barrier.
-template <int PRO, int S, int R>
+template <int PRO, int S, int R, int FMT = FMT_Q4>
 __device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, int mi, int sub, int lane,
                                             XPieces<S, 8 / R>& xp, u32x4 (*bq)[2][kWave],
                                             float (*tx)[kMmaCols], float (*xs_lds)[4], float (*part)[4][R]) {
     constexpr int NI = 8 / R;
+    static_assert(FMT == FMT_Q4 || S == 1, "8-bit operands cover one chunk");
     const bool live = mi < p.m;
     if constexpr (PRO != PRO_PLAIN) {
         float ss0 = 0.0f, ss1 = 0.0f;
@@ -935,6 +945,22 @@ __device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, 
             const float4 x = xp.x[c][ii];
             const unsigned b0 = q_bits(x.x, inv_q), b1 = q_bits(x.y, inv_q), b2 = q_bits(x.z, inv_q),
                            b3 = q_bits(x.w, inv_q);
+            if constexpr (FMT == FMT_Q8) {
+                // (hi 0, hi 1, lo 0, lo 1) and the same of 2, 3, then the hi
+                // word and the lo word of the lane's four features
+                const unsigned p01 = __builtin_amdgcn_perm(b1, b0, 0x04000501u);
+                const unsigned p23 = __builtin_amdgcn_perm(b3, b2, 0x04000501u);
+                const unsigned hw = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+                const unsigned lw = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;
+                const int tq = 4 * (sub * NI + ii) + (lane >> 4);  // MFMA of features 256 i + 4 lane ..
+                const int hq = (lane >> 2) & 3, par = hq >> 1;     // quarter, group parity
+                unsigned* slot = reinterpret_cast<unsigned*>(&bq[tq >> 1][tq & 1][0]) + (lane & 3);
+                slot[4 * (2 * mi + 8 * par + 16 * hq)] = hw;
+                slot[4 * (2 * mi + 1 + 8 * par + 16 * hq)] = lw;
+                slot[4 * (2 * mi + 8 * (1 - par) + 16 * hq)] = 0u;
+                slot[4 * (2 * mi + 1 + 8 * (1 - par) + 16 * hq)] = 0u;
+                continue;
+            }
             unsigned qsum = (b0 + b1) + (b2 + b3);
             // bytes (hi of 0, hi of 2, lo of 0, lo of 2) and the same of 1, 3;
             // the even lane keeps the first and gives the second, the odd the reverse
@@ -967,9 +993,10 @@ __device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, 
     __syncthreads();
 }
 
-template <int PRO>
+template <int FMT, int PRO>
 __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p) {
     constexpr int R = kMaxWaves / 4;  // waves per activation row in the setup
+    constexpr int NT = FMT == FMT_Q4 ? 16 : 32;  // 16-byte code loads per lane and unit
     __shared__ u32x4 bq[16][2][kWave];              // 32 KB: B operands (load t, group pair)
     __shared__ float tx[64][kMmaCols];              // 4 KB: sum of x^ per (group, column 2*row), else 0
     __shared__ float stage[kMaxWaves][64 * kStage];  // 40 KB: each wave's scales, [group][row]
@@ -1009,20 +1036,24 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     auto row_ptrs = [&](int u, const char*& crow, const float*& srow, const float*& brow) {
         int row = u * kMmaRows + j;
         row = row < v.N ? row : v.N - 1;
-        crow = static_cast<const char*>(v.c0) + (int64_t)row * (v.K / 2) + 16 * h;
+        crow = static_cast<const char*>(v.c0) + (int64_t)row * (FMT == FMT_Q4 ? v.K / 2 : v.K) + 16 * h;
         srow = v.s0 + (int64_t)row * v.G + 4 * h;
-        brow = v.b0 + (int64_t)row * v.G + 4 * h;
+        brow = FMT == FMT_Q4 ? v.b0 + (int64_t)row * v.G + 4 * h : nullptr;
     };
-    u32x4 cw[16];
+    u32x4 cw[NT];
     v4f_t sv[4], bv[4];
+    // Plain loads: a load reads one half of a 128-byte line of each of 16
+    // rows and the next load the other half, so the line is better kept in
+    // L2 than streamed past it (nontemporal loads measured 5-9% slower here).
     auto load_codes = [&](const char* crow, int t) {
-        cw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 64 * t));
+        cw[t] = *reinterpret_cast<const u32x4*>(crow + 64 * t);
     };
     auto load_sb = [&](const float* srow, const float* brow) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             sv[t] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(srow + 16 * t));
-            bv[t] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(brow + 16 * t));
+            if constexpr (FMT == FMT_Q4)
+                bv[t] = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(brow + 16 * t));
         }
     };
 
@@ -1040,10 +1071,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         const float *srow, *brow;
         row_ptrs(u >= 0 ? u : 0, crow, srow, brow);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) load_codes(crow, t);
+        for (int t = 0; t < NT; ++t) load_codes(crow, t);
         load_sb(srow, brow);
     }
-    mma_quant_x<PRO, 1, R>(p, v, wid & 3, wid >> 2, lane, xp, bq, tx, xs_lds, part);
+    mma_quant_x<PRO, 1, R, FMT>(p, v, wid & 3, wid >> 2, lane, xp, bq, tx, xs_lds, part);
     const float colx = colf * xs_lds[0][mi_l];  // integer sums carry the activation scale here
     while (u >= 0) {
         // the next unit's rows; past the last unit the requests still go out,
@@ -1065,54 +1096,85 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
             for (int e = 0; e < 4; ++e) {
                 const int gg = 16 * t + 4 * h + e;
                 st[gg * kStage + j] = sv[t][e];
-                const float tv = tx[gg][j];
-                cb4[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[t][e], tv, cb4[e & 1], 0, 0, 0);
+                if constexpr (FMT == FMT_Q4) {
+                    const float tv = tx[gg][j];
+                    cb4[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[t][e], tv, cb4[e & 1], 0, 0, 0);
+                }
             }
         }
         load_sb(nsrow, nbrow);
         __builtin_amdgcn_wave_barrier();
 
-        // integer products, kTB loads (2 kTB MFMAs) at a time
-        constexpr int kTB = 2;
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (FMT == FMT_Q8) {
+            // one MFMA per load, kTB8 at a time
+            constexpr int kTB8 = 4;
 #pragma unroll
-        for (int t0 = 0; t0 < 16; t0 += kTB) {
-            v4i_t A[kTB][2];
+            for (int t0 = 0; t0 < NT; t0 += kTB8) {
+                v4i_t D[kTB8];
 #pragma unroll
-            for (int dt = 0; dt < kTB; ++dt) {
-                const int t = t0 + dt;
-                unsigned w0 = cw[t].x, w1 = cw[t].y, w2 = cw[t].z, w3 = cw[t].w;
-                perm32_swap(w0, w2);
-                perm32_swap(w1, w3);
-                const unsigned M4 = 0x0F0F0F0Fu;
-                A[dt][0] = (v4i_t){(int)(w0 & M4), (int)((w0 >> 4) & M4), (int)(w1 & M4), (int)((w1 >> 4) & M4)};
-                A[dt][1] = (v4i_t){(int)(w2 & M4), (int)((w2 >> 4) & M4), (int)(w3 & M4), (int)((w3 >> 4) & M4)};
-            }
-            v4i_t D[kTB][2];
-#pragma unroll
-            for (int dt = 0; dt < kTB; ++dt)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const u32x4 bb = bq[t0 + dt][pp][lane];
+                for (int dt = 0; dt < kTB8; ++dt) {
+                    const int t = t0 + dt;
+                    const u32x4 bb = bq[t >> 1][t & 1][lane];
+                    const v4i_t A = {(int)cw[t].x, (int)cw[t].y, (int)cw[t].z, (int)cw[t].w};
                     const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
                     const v4i_t zero = {0, 0, 0, 0};
-                    D[dt][pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[dt][pp], B, zero, 0, 0, 0);
+                    D[dt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
                 }
 #pragma unroll
-            for (int dt = 0; dt < kTB; ++dt)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const int gg = 4 * (t0 + dt) + 2 * pp + (j >> 3);
+                for (int dt = 0; dt < kTB8; ++dt) {
+                    const int gg = 2 * (t0 + dt) + (j >> 3);
                     const float4 s4 = *reinterpret_cast<const float4*>(&st[gg * kStage + 4 * h]);
-                    acc[0] = fmaf(s4.x, (float)D[dt][pp][0], acc[0]);
-                    acc[1] = fmaf(s4.y, (float)D[dt][pp][1], acc[1]);
-                    acc[2] = fmaf(s4.z, (float)D[dt][pp][2], acc[2]);
-                    acc[3] = fmaf(s4.w, (float)D[dt][pp][3], acc[3]);
+                    acc[0] = fmaf(s4.x, (float)D[dt][0], acc[0]);
+                    acc[1] = fmaf(s4.y, (float)D[dt][1], acc[1]);
+                    acc[2] = fmaf(s4.z, (float)D[dt][2], acc[2]);
+                    acc[3] = fmaf(s4.w, (float)D[dt][3], acc[3]);
                 }
-            // the registers of loads t0 .. t0+kTB-1 are free: request the
-            // next unit's
 #pragma unroll
-            for (int dt = 0; dt < kTB; ++dt) load_codes(ncrow, t0 + dt);
+                for (int dt = 0; dt < kTB8; ++dt) load_codes(ncrow, t0 + dt);
+            }
+        } else {
+            // integer products, kTB loads (2 kTB MFMAs) at a time
+            constexpr int kTB = 2;
+#pragma unroll
+            for (int t0 = 0; t0 < 16; t0 += kTB) {
+                v4i_t A[kTB][2];
+#pragma unroll
+                for (int dt = 0; dt < kTB; ++dt) {
+                    const int t = t0 + dt;
+                    unsigned w0 = cw[t].x, w1 = cw[t].y, w2 = cw[t].z, w3 = cw[t].w;
+                    perm32_swap(w0, w2);
+                    perm32_swap(w1, w3);
+                    const unsigned M4 = 0x0F0F0F0Fu;
+                    A[dt][0] = (v4i_t){(int)(w0 & M4), (int)((w0 >> 4) & M4), (int)(w1 & M4), (int)((w1 >> 4) & M4)};
+                    A[dt][1] = (v4i_t){(int)(w2 & M4), (int)((w2 >> 4) & M4), (int)(w3 & M4), (int)((w3 >> 4) & M4)};
+                }
+                v4i_t D[kTB][2];
+#pragma unroll
+                for (int dt = 0; dt < kTB; ++dt)
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const u32x4 bb = bq[t0 + dt][pp][lane];
+                        const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
+                        const v4i_t zero = {0, 0, 0, 0};
+                        D[dt][pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[dt][pp], B, zero, 0, 0, 0);
+                    }
+#pragma unroll
+                for (int dt = 0; dt < kTB; ++dt)
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int gg = 4 * (t0 + dt) + 2 * pp + (j >> 3);
+                        const float4 s4 = *reinterpret_cast<const float4*>(&st[gg * kStage + 4 * h]);
+                        acc[0] = fmaf(s4.x, (float)D[dt][pp][0], acc[0]);
+                        acc[1] = fmaf(s4.y, (float)D[dt][pp][1], acc[1]);
+                        acc[2] = fmaf(s4.z, (float)D[dt][pp][2], acc[2]);
+                        acc[3] = fmaf(s4.w, (float)D[dt][pp][3], acc[3]);
+                    }
+                // the registers of loads t0 .. t0+kTB-1 are free: request the
+                // next unit's
+#pragma unroll
+                for (int dt = 0; dt < kTB; ++dt) load_codes(ncrow, t0 + dt);
+            }
         }
         __builtin_amdgcn_wave_barrier();
         v4f_t cb = cb4[0] + cb4[1];
@@ -1230,7 +1292,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     u32x4 cw[TW];
 #pragma unroll
     for (int i = 0; i < TW; ++i)
-        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i)));
+        cw[i] = *reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i));  // plain, as in k_gemv_mma
     float sv[NE], bv[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -1395,7 +1457,7 @@ static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int 
 // The lm_head (argmax epilogue) at three or four rows: persistent matrix-core
 // blocks.
 static bool mma_head_path(int fmt, int epi, int m, const GemvParams& p) {
-    return fmt == FMT_Q4 && epi == EPI_ARGMAX && m >= 3 && m <= 4 && p.K == kChunk && p.nmat == 1 &&
+    return epi == EPI_ARGMAX && m >= 3 && m <= 4 && p.K == kChunk && p.nmat == 1 &&
            !p.slot_expert;
 }
 
@@ -1431,11 +1493,11 @@ static hipError_t launch_mma_sk(const GemvParams& p, hipStream_t st) {
 }
 
 // One 8-wave block per compute unit (fewer for a small matrix).
-template <int PRO>
+template <int FMT, int PRO>
 static hipError_t launch_mma_head(const GemvParams& p, hipStream_t st) {
     const int units = (p.N + kMmaRows - 1) / kMmaRows;
     const int need = (units + kMaxWaves - 1) / kMaxWaves, cu = device_cu_count();
-    hipLaunchKernelGGL((k_gemv_mma<PRO>), dim3(need < cu ? need : cu), dim3(64 * kMaxWaves), 0, st, p);
+    hipLaunchKernelGGL((k_gemv_mma<FMT, PRO>), dim3(need < cu ? need : cu), dim3(64 * kMaxWaves), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1450,7 +1512,8 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
         if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_mma_sk<PRO_PLAIN, EPI_SWIGLU>(p, st);
         if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_mma_sk<PRO_RMS, EPI_SWIGLU>(p, st);
     }
-    if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS) return launch_mma_head<PRO_RMS>(p, st);
+    if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS)
+        return fmt == FMT_Q4 ? launch_mma_head<FMT_Q4, PRO_RMS>(p, st) : launch_mma_head<FMT_Q8, PRO_RMS>(p, st);
     if (fmt == FMT_Q4) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_RMS, EPI_STORE>(m, p, sh, 1, st);

@@ -746,6 +746,54 @@ def test_lmhead_argmax_q8_small_vocab_eight_rows_with_logits():
     _close(_np(lo), logits, "logits")
 
 
+@pytest.mark.parametrize("m", [3, 4])
+def test_lmhead_argmax_q8_matrix_core_ragged_vocab_with_logits(m):
+    """Three or four rows at hidden 2048 take the matrix-core head; a vocab of
+    4099 leaves a last 16-row unit of three rows."""
+    _say(f"lmhead q8 matrix core vocab 4099 m={m}")
+    g = synth.rng(123, m)
+    lm = synth.q8_weight(g, 1, 4099, 2048)
+    x, gf = synth.normal(g, (m, 2048)), synth.gamma(g, 2048)
+    _, logits, ids = oracle.head8(x, gf, 1e-6, lm)
+    margin = min(planting.head_margin(r) for r in logits)
+    _say(f"  oracle ids {ids.tolist()} min margin {margin:.4f}")
+    assert margin >= 1e-3
+    lo = torch.empty((m, 4099), dtype=torch.float32, device=DEV)
+    got = _np(mtp.mtp_lmhead_argmax_q8(_t(x), _t(gf), 1e-6, mtp.DeviceQ8(lm), logits_out=lo))
+    assert got.tolist() == ids.tolist()
+    _close(_np(lo), logits, "logits")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_lmhead_argmax_q8_ties_keep_lowest_row(m):
+    """Each row's maximum is copied to a lower and a higher row at the same
+    position inside a 16-row unit, so both sides compute equal logits for the
+    copies; the lowest copy must win on both."""
+    g = synth.rng(124, m)
+    V = 4099
+    lm = synth.q8_weight(g, 1, V, 2048)
+    x, gf = synth.normal(g, (m, 2048)), synth.gamma(g, 2048)
+    targets = oracle.head8(x, gf, 1e-6, lm)[2].tolist()
+    codes, scales = lm.codes.copy(), lm.scales.copy()
+    taken, copies = set(targets), {}
+    for t in dict.fromkeys(targets):
+        dst = [d for d in (t % 16 + 16 * 3, t + 16 * 5) if d != t and d < V and d not in taken]
+        for d in dst:
+            codes[0, d], scales[0, d] = codes[0, t], scales[0, t]
+            taken.add(d)
+        copies[t] = [t] + dst
+    dup = synth.Q8(codes, scales)
+    _, logits, ref = oracle.head8(x, gf, 1e-6, dup)
+    want = [min(copies[t]) for t in targets]
+    _say(f"lmhead q8 ties m={m}: targets {targets} -> lowest copies {want}")
+    assert ref.tolist() == want
+    for r, t in zip(logits, targets):  # the rest stays clear of the tie
+        rest = np.delete(r, copies[t])
+        assert r[t] - rest.max() >= 1e-3
+    ids = _np(mtp.mtp_lmhead_argmax_q8(_t(x), _t(gf), 1e-6, mtp.DeviceQ8(dup)))
+    assert ids.tolist() == want
+
+
 # --------------------------------------------------------------------------
 # multi-layer draft stack ([mimo.rs] "How the three layers chain")
 # --------------------------------------------------------------------------
