@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=3, help="weight/cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ops", action="store_true", help="skip the single-op timings (GEMV, eh_proj, MoE)")
+    ap.add_argument("--no-ops", action="store_true", help="skip the single-op timings (GEMV, eh_proj, attention, catch-up, stack, 8-bit head, MoE)")
     ap.add_argument("--ops-only", action="store_true", help="only the single-op timings, for kernel traces")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
     ap.add_argument("--head-only", action="store_true",
@@ -279,6 +279,87 @@ def event_us(torch, dev, fn, n, warm):
     return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
 
 
+def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
+    """Attention block (cache 4096, 16 q / 2 kv heads x 128; plain and with gated
+    q, per-head q/k norms and rotary over 64 of 128 dims) at m = 1 and 4, the
+    cache catch-up of a 4-row target batch, and the three-layer draft stack
+    (each layer catches up 4 rows, then drafts row t).  The attention and
+    catch-up loops rotate over 24 layer/cache copies (about 18 MB read each) so that
+    the 256 MB Infinity Cache cannot serve repeats; the stack's three layers
+    stream 825 MB per call."""
+    out = {}
+    H, D, NKV, L0, CAP = 2048, 128, 2, 4096, 4112
+    kvrow = NKV * D * 4 * 2  # K and V bytes of one position
+
+    def q4_bytes(dl, names):
+        return sum(dl.q4[k].nbytes for k in names)
+
+    for name, kw in (("attn", {}), ("attn_variant", {"q_gated": True, "qk_norm": True, "rotary_dim": 64})):
+        g = synth.rng(40)
+        Lh = synth.dense_layer(g, vocab=64, **kw)
+        kc, vc = synth.kv_cache(g, NKV, L0, CAP, D)
+        reps = [(mtp.DeviceLayer(Lh, dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev))
+                for _ in range(24)]
+        wb = q4_bytes(reps[0][0], ("wq", "wk", "wv", "wo"))
+        for m in (1, 4):
+            u = torch.randn((m, H), device=dev)
+            o = torch.empty_like(u)
+            ws = torch.empty(mtp.mtp_attn_decode_workspace_size(reps[0][0], L0, m), dtype=torch.uint8, device=dev)
+
+            def call(i, u=u, o=o, ws=ws):
+                dl, dk, dv = reps[i % len(reps)]
+                mtp.mtp_attn_decode(dl, u, dk, dv, L0, out=o, ws=ws)
+
+            us = event_us(torch, dev, call, n, W)
+            b = wb + kvrow * (L0 + m) + kvrow * m + m * H * 4 * 2
+            out[f"{name}_cache4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+        if name == "attn":
+            # cache catch-up: shifted target hidden -> eh_proj -> K/V rows of 4 positions
+            m = 4
+            tab = torch.randn((64, H), device=dev)
+            toks = torch.arange(m, dtype=torch.int32, device=dev)
+            pend = torch.randn((1, H), device=dev)
+            tgt = torch.randn((m, H), device=dev)
+            ws = torch.empty(mtp.mtp_append_kv_workspace_size(reps[0][0]), dtype=torch.uint8, device=dev)
+
+            def catch_up(i):
+                dl, dk, dv = reps[i % len(reps)]
+                mtp.mtp_append_kv(dl, None, toks, tab, pend, tgt, dk, dv, L0, ws=ws)
+
+            us = event_us(torch, dev, catch_up, n, W)
+            b = q4_bytes(reps[0][0], ("eh_proj", "wk", "wv")) + m * H * 4 * 2 + H * 4 + kvrow * m
+            out["append_kv_4rows_cache4096"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+        del reps
+        torch.cuda.empty_cache()
+
+    # three-layer draft stack, full vocabulary: t = L0 + 3, each layer
+    # recomputes rows t - 4 .. t - 1 (catch-up) and drafts row t
+    layers = [mtp.DeviceLayer(synth.dense_layer(synth.rng(41, k)), dev) for k in range(3)]
+    V = layers[0].vocab
+    t = L0 + 3
+    caches = []
+    for k in range(3):
+        kc, vc = synth.kv_cache(synth.rng(42, k), NKV, t - 4, CAP, D)
+        caches.append((torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)))
+    table = torch.randn((V, H), device=dev)
+    target_h = torch.randn((t + 1, H), device=dev)
+    tokens = torch.randint(0, V, (t + 2 + 3,), dtype=torch.int32, device=dev)
+    starts = [t - 4] * 3
+    ws = torch.empty(mtp.mtp_stack_draft_workspace_size(layers, caches, starts, t), dtype=torch.uint8, device=dev)
+
+    def stack(i):
+        mtp.mtp_stack_draft(layers, caches, starts, tokens, table, target_h, t, ws=ws)
+
+    us = event_us(torch, dev, stack, n, W)
+    per_layer = (layers[0].weight_nbytes + kvrow * (t + 1) + kvrow * 4
+                 + q4_bytes(layers[0], ("eh_proj", "wk", "wv")))
+    b = 3 * per_layer
+    out["stack_draft_3layers_t4099"] = {"us": round(us, 3), "us_per_layer": round(us / 3, 3), "bytes": b,
+                                        "GB/s": round(b / us / 1e3, 1)}
+    del layers, caches, table, target_h
+    return out
+
+
 def op_timings(torch, mtp, synth, dev, K, W):
     """The single-op workloads: 4-bit GEMV 1024x1024 (m=1), the e/h norm + concat
     + eh_proj 2048x4096 (m=1, 4) and the 8-bit MoE FFN (256 experts, top-8 +
@@ -320,6 +401,8 @@ def op_timings(torch, mtp, synth, dev, K, W):
         b = c1[0].nbytes + 2 * 2048 * 4 + m * (2 * 2048 + 2048) * 4
         out[f"norm_concat_proj_2048x4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
     del c1
+    torch.cuda.empty_cache()
+    out.update(attn_catchup_stack_timings(torch, mtp, synth, dev, n, W))
     torch.cuda.empty_cache()
 
     # 8-bit lm_head (vocab 151936 x 2048, int8 + one f32 scale per 32) with the

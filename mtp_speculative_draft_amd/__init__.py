@@ -273,6 +273,22 @@ def mtp_draft_step_workspace_size(layer: DeviceLayer, cache_len: int, m: int) ->
     return int(lib().mtp_draft_step_workspace_size(C.byref(layer.desc), cache_len, m))
 
 
+def mtp_append_kv_workspace_size(layer: DeviceLayer) -> int:
+    return int(lib().mtp_append_kv_workspace_size(C.byref(layer.desc)))
+
+
+def _stack_array(layers, caches, starts):
+    n = len(layers)
+    arr = (MtpStackLayer * n)()
+    for i, (dl, (kc, vc), st) in enumerate(zip(layers, caches, starts)):
+        arr[i] = MtpStackLayer(C.addressof(dl.desc), _ptr(kc), _ptr(vc), int(kc.shape[1]), int(st))
+    return arr
+
+
+def mtp_stack_draft_workspace_size(layers, caches, starts, t: int) -> int:
+    return int(lib().mtp_stack_draft_workspace_size(_stack_array(layers, caches, starts), len(layers), int(t)))
+
+
 # --------------------------------------------------------------------------
 # calls
 # --------------------------------------------------------------------------
@@ -401,7 +417,7 @@ def mtp_append_kv(layer: DeviceLayer, e, tokens, embed_table, pending_h, target_
     """Cache catch-up after a target batch: writes K/V rows cache_len .. cache_len+m-1."""
     _f32(target_h, "target_h")
     m = _rows(target_h)
-    ws = _ws(int(lib().mtp_append_kv_workspace_size(C.byref(layer.desc))), target_h, ws)
+    ws = _ws(mtp_append_kv_workspace_size(layer), target_h, ws)
     _check(lib().mtp_append_kv(C.byref(layer.desc), _ptr(e), _ptr(tokens), _ptr(embed_table), _ptr(pending_h),
                                _ptr(target_h), _ptr(k_cache), _ptr(v_cache), int(cache_len), int(k_cache.shape[1]),
                                m, _ptr(ws), _nbytes(ws), _stream(target_h)), "mtp_append_kv")
@@ -440,9 +456,7 @@ def mtp_stack_draft(layers, caches, starts, tokens, embed_table, target_h, t: in
     (first recomputed row per layer); tokens device int32 [t + 2 + len(layers)]
     gets draft k at t + 2 + k.  Returns tokens."""
     n = len(layers)
-    arr = (MtpStackLayer * n)()
-    for i, (dl, (kc, vc), st) in enumerate(zip(layers, caches, starts)):
-        arr[i] = MtpStackLayer(C.addressof(dl.desc), _ptr(kc), _ptr(vc), int(kc.shape[1]), int(st))
+    arr = _stack_array(layers, caches, starts)
     need = int(lib().mtp_stack_draft_workspace_size(arr, n, int(t)))
     ws = _ws(need, target_h, ws)
     _check(lib().mtp_stack_draft(arr, n, _ptr(tokens), _ptr(embed_table), _ptr(target_h), int(t), _ptr(ws),
