@@ -173,33 +173,47 @@ void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t po
 void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_t m,
               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t cache_len,
               int32_t capacity, float* out) {
+    orc_sdpa_window(q, k_cache, v_cache, m, n_heads, n_kv_heads, head_dim, cache_len, capacity, 0, NULL, out);
+}
+
+/* The same with the sliding window and the sinks of the MiMo draft attention
+ * ([mimo.rs] module doc "The draft forward": "window 128, sinks"): row r at
+ * position p = cache_len + r scores positions max(0, p-W+1) .. p when W > 0
+ * (all of 0 .. p when W = 0), and with sinks the softmax of head hh runs over
+ * those scores and the extra logit sinks[hh], whose value row is zero:
+ *   o = sum_j e^(s_j - M) v_j / (sum_j e^(s_j - M) + e^(sink - M)),
+ *   M = max(sink, max_j s_j). */
+void orc_sdpa_window(const float* q, const float* k_cache, const float* v_cache, int32_t m, int32_t n_heads,
+                     int32_t n_kv_heads, int32_t head_dim, int32_t cache_len, int32_t capacity, int32_t window,
+                     const float* sinks, float* out) {
     const int32_t group = n_heads / n_kv_heads;
     const double scale = 1.0 / sqrt((double)head_dim);
     const int32_t max_len = cache_len + m;
     double* p = (double*)xmalloc(sizeof(double) * (size_t)max_len);
     double* o = (double*)xmalloc(sizeof(double) * (size_t)head_dim);
     for (int32_t r = 0; r < m; ++r) {
-        const int32_t len = cache_len + r + 1;
+        const int32_t pos = cache_len + r;
+        const int32_t lo = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
         for (int32_t hh = 0; hh < n_heads; ++hh) {
             const int32_t g = hh / group;
             const float* qv = q + ((size_t)r * n_heads + hh) * head_dim;
             const float* K = k_cache + (size_t)g * capacity * head_dim;
             const float* V = v_cache + (size_t)g * capacity * head_dim;
-            double mx = -INFINITY;
-            for (int32_t j = 0; j < len; ++j) {
+            double mx = sinks ? (double)sinks[hh] : -INFINITY;
+            for (int32_t j = lo; j <= pos; ++j) {
                 double s = 0.0;
                 for (int32_t t = 0; t < head_dim; ++t)
                     s += (double)qv[t] * (double)K[(size_t)j * head_dim + t];
                 p[j] = s * scale;
                 if (p[j] > mx) mx = p[j];
             }
-            double z = 0.0;
-            for (int32_t j = 0; j < len; ++j) {
+            double z = sinks ? exp((double)sinks[hh] - mx) : 0.0;
+            for (int32_t j = lo; j <= pos; ++j) {
                 p[j] = exp(p[j] - mx);
                 z += p[j];
             }
             for (int32_t t = 0; t < head_dim; ++t) o[t] = 0.0;
-            for (int32_t j = 0; j < len; ++j)
+            for (int32_t j = lo; j <= pos; ++j)
                 for (int32_t t = 0; t < head_dim; ++t) o[t] += p[j] * (double)V[(size_t)j * head_dim + t];
             float* dst = out + ((size_t)r * n_heads + hh) * head_dim;
             for (int32_t t = 0; t < head_dim; ++t) dst[t] = (float)(o[t] / z);
@@ -285,7 +299,7 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
             memcpy(k_cache + dst, k + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
             memcpy(v_cache + dst, v + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
         }
-    orc_sdpa(q, k_cache, v_cache, m, nh, nkv, d, cache_len, capacity, o);
+    orc_sdpa_window(q, k_cache, v_cache, m, nh, nkv, d, cache_len, capacity, L->window, L->sinks, o);
     if (L->q_gated)
         for (size_t i = 0; i < (size_t)m * nh * d; ++i)
             o[i] = (float)((double)o[i] / (1.0 + exp(-(double)gate[i])));

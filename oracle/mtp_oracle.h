@@ -58,7 +58,13 @@ typedef struct {
  *   gamma_q_head, gamma_k_head  f32 [head_dim]: per-head RMSNorm of q and k
  *                 before the rotary step (`apply_q_or_k_per_head_rms_norm`);
  *   rotary_dim    0 or head_dim: rotary over all dims; else only the first
- *                 rotary_dim dims rotate (`apply_imrope`'s rotary_dim). */
+ *                 rotary_dim dims rotate (`apply_imrope`'s rotary_dim).
+ * Sliding-window attention of the MiMo draft layer ([mimo.rs] module doc "The
+ * draft forward": window 128, sinks), both optional:
+ *   window        0: causal over the whole cache; W > 0: the row at position
+ *                 p sees positions p-W+1 .. p only (W rows, itself included);
+ *   sinks         f32 [n_heads] or NULL: one logit per query head that joins
+ *                 the softmax denominator with no value row. */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab, ffn_inter;
     double rope_theta;
@@ -67,6 +73,8 @@ typedef struct {
     orc_q4 eh_proj, wq, wk, wv, wo, gate, up, down, lm_head;
     const float *gamma_q_head, *gamma_k_head;
     int32_t q_gated, rotary_dim;
+    const float* sinks;
+    int32_t window;
 } orc_layer;
 
 /* ---- weight formats ---- */
@@ -85,6 +93,9 @@ void orc_rope_partial(float* x, int32_t m, int32_t n_heads, int32_t head_dim, in
 void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_t m,
               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t cache_len,
               int32_t capacity, float* out);
+void orc_sdpa_window(const float* q, const float* k_cache, const float* v_cache, int32_t m, int32_t n_heads,
+                     int32_t n_kv_heads, int32_t head_dim, int32_t cache_len, int32_t capacity, int32_t window,
+                     const float* sinks, float* out);
 int32_t orc_argmax(const float* v, int32_t n);
 
 /* ---- layer steps ---- */

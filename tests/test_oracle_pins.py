@@ -283,6 +283,90 @@ def test_sdpa_dominant_score_and_causal_rows():
 
 
 # --------------------------------------------------------------------------
+# sliding window and sinks ([mimo.rs] module doc "The draft forward": the
+# draft attention has a 128-row window and per-head sinks)
+# --------------------------------------------------------------------------
+def test_sdpa_window_one_returns_each_rows_own_value():
+    """A window of one row leaves every query its own position only."""
+    g = np.random.default_rng(60)
+    kc, vc = _caches(g, 2, 12, 16)
+    q = synth.normal(g, (3, 4 * 16))
+    o = oracle.sdpa(q, kc, vc, 4, 7, window=1)
+    for r in range(3):
+        for hh in range(4):
+            assert (o[r, hh * 16:(hh + 1) * 16] == vc[hh // 2, 7 + r]).all()
+
+
+def test_sdpa_window_one_with_a_sink_is_a_sigmoid_gate():
+    """One visible key with score s and a sink logit c: the softmax over {s, c}
+    gives the value row weight e^s / (e^s + e^c) = sigmoid(s - c)."""
+    g = np.random.default_rng(61)
+    d = 16
+    kc, vc = _caches(g, 2, 10, d)
+    q = synth.normal(g, (2, 4 * d))
+    sinks = np.array([-1.5, 0.0, 0.75, 2.5], np.float32)
+    o = oracle.sdpa(q, kc, vc, 4, 5, window=1, sinks=sinks)
+    for r in range(2):
+        for hh in range(4):
+            qv = q[r, hh * d:(hh + 1) * d].astype(np.float64)
+            s = float(qv @ kc[hh // 2, 5 + r].astype(np.float64)) / math.sqrt(d)
+            w = 1.0 / (1.0 + math.exp(-(s - float(sinks[hh]))))
+            want = w * vc[hh // 2, 5 + r].astype(np.float64)
+            assert np.allclose(o[r, hh * d:(hh + 1) * d], want, rtol=1e-6, atol=1e-7)
+
+
+def test_sdpa_window_sees_exactly_the_last_w_positions():
+    """Window 3 at cache length 10: row 0 (position 10) sees 8..10, row 1
+    (position 11) sees 9..11; changing a row outside a query's window leaves
+    that query's output bitwise equal, changing one inside does not."""
+    g = np.random.default_rng(62)
+    kc, vc = _caches(g, 1, 14, 8)
+    q = synth.normal(g, (2, 8))
+    base = oracle.sdpa(q, kc, vc, 1, 10, window=3)
+    for pos, same0, same1 in ((7, True, True), (8, False, True), (9, False, False)):
+        k2, v2 = kc.copy(), vc.copy()
+        k2[0, pos] += 1.0
+        v2[0, pos] += 1.0
+        o = oracle.sdpa(q, k2, v2, 1, 10, window=3)
+        assert (o[0] == base[0]).all() == same0, pos
+        assert (o[1] == base[1]).all() == same1, pos
+
+
+def test_sdpa_window_covering_the_cache_is_plain_causal_attention():
+    g = np.random.default_rng(63)
+    kc, vc = _caches(g, 2, 20, 16)
+    q = synth.normal(g, (4, 4 * 16))
+    plain = oracle.sdpa(q, kc, vc, 4, 13)
+    assert (oracle.sdpa(q, kc, vc, 4, 13, window=17) == plain).all()  # row 3 (position 16) sees 0..16
+    assert not (oracle.sdpa(q, kc, vc, 4, 13, window=16) == plain).all()
+
+
+def test_sdpa_equal_keys_with_a_sink_closed_form():
+    """n visible keys of equal score s and a sink c: o = mean(v) * n e^s / (n e^s + e^c)."""
+    g = np.random.default_rng(64)
+    nkv, cap, d, L = 2, 9, 8, 6
+    kc = np.zeros((nkv, cap, d), np.float32)
+    kc[:] = synth.normal(g, (1, 1, d))
+    vc = synth.normal(g, (nkv, cap, d))
+    q = synth.normal(g, (1, 4 * d))
+    sinks = np.array([0.3, -2.0, 1.7, 4.0], np.float32)
+    o = oracle.sdpa(q, kc, vc, 4, L - 1, sinks=sinks)
+    for hh in range(4):
+        s = float(q[0, hh * d:(hh + 1) * d].astype(np.float64) @ kc[0, 0].astype(np.float64)) / math.sqrt(d)
+        w = L * math.exp(s) / (L * math.exp(s) + math.exp(float(sinks[hh])))
+        want = w * vc[hh // 2, :L].astype(np.float64).mean(axis=0)
+        assert np.allclose(o[0, hh * d:(hh + 1) * d], want, rtol=1e-6, atol=1e-7)
+
+
+def test_sdpa_very_negative_sinks_change_nothing():
+    g = np.random.default_rng(65)
+    kc, vc = _caches(g, 2, 20, 16)
+    q = synth.normal(g, (2, 4 * 16))
+    plain = oracle.sdpa(q, kc, vc, 4, 11)
+    assert (oracle.sdpa(q, kc, vc, 4, 11, sinks=np.full(4, -1e4, np.float32)) == plain).all()
+
+
+# --------------------------------------------------------------------------
 # layer steps
 # --------------------------------------------------------------------------
 def _small_layer(seed=21, H=64, nh=4, nkv=2, d=16, inter=96, vocab=300):
