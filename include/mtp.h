@@ -96,7 +96,17 @@ typedef struct {
  *                 step.
  *   rotary_dim    0 = head_dim; else a power of two <= head_dim: only the
  *                 first rotary_dim dims rotate, as pairs (i, i + rotary_dim/2)
- *                 with inverse frequency rope_theta^(-2i/rotary_dim). */
+ *                 with inverse frequency rope_theta^(-2i/rotary_dim).
+ * Sliding-window attention of the MiMo draft layer ([mimo.rs] module doc "The
+ * draft forward": "window 128, sinks"; zero / NULL give the plain causal
+ * attention):
+ *   window        0, or W > 0: the row at position p attends to positions
+ *                 max(0, p-W+1) .. p only (W positions, itself included).
+ *   sinks         f32 [n_heads] (4-byte aligned, finite) or NULL: per query
+ *                 head h a logit sinks[h] that joins the softmax denominator
+ *                 with no value row: o = sum_j e^(s_j-M) v_j /
+ *                 (sum_j e^(s_j-M) + e^(sinks[h]-M)), M = max(sinks[h], max s_j),
+ *                 s_j the scaled scores. */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab;
     int32_t ffn_kind; /* MTP_FFN_DENSE_Q4 or MTP_FFN_MOE_Q8 */
@@ -110,6 +120,8 @@ typedef struct {
     mtp_q8 gate_exps, up_exps, down_exps, sh_gate, sh_up, sh_down;
     const float *gamma_q_head, *gamma_k_head;
     int32_t q_gated, rotary_dim;
+    const float* sinks;
+    int32_t window;
 } mtp_layer;
 
 const char* mtp_status_string(mtp_status s);

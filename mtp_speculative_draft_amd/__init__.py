@@ -66,7 +66,8 @@ class MtpLayer(C.Structure):
                 ("gate_exps", MtpQ8), ("up_exps", MtpQ8), ("down_exps", MtpQ8),
                 ("sh_gate", MtpQ8), ("sh_up", MtpQ8), ("sh_down", MtpQ8),
                 ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
-                ("q_gated", C.c_int32), ("rotary_dim", C.c_int32)]
+                ("q_gated", C.c_int32), ("rotary_dim", C.c_int32),
+                ("sinks", C.c_void_p), ("window", C.c_int32)]
 
 
 _lib = None
@@ -198,6 +199,9 @@ class DeviceLayer:
         self.head_gammas = None if gq is None else (f(gq), f(gk))
         hq = self.head_gammas[0].data_ptr() if self.head_gammas else None
         hk = self.head_gammas[1].data_ptr() if self.head_gammas else None
+        # sliding window and per-head sinks
+        sk = getattr(dense, "sinks", None)
+        self.sinks = None if sk is None else f(sk)
         q = self.q4
         self.desc = MtpLayer(dense.hidden, dense.n_heads, dense.n_kv_heads, dense.head_dim, dense.vocab, kind,
                              dense.ffn_inter, top_k, float(dense.rope_theta), float(dense.eps), *g,
@@ -205,7 +209,9 @@ class DeviceLayer:
                              q["gate"].desc, q["up"].desc, q["down"].desc, q["lm_head"].desc, router,
                              q8["gate_exps"], q8["up_exps"], q8["down_exps"], q8["sh_gate"], q8["sh_up"],
                              q8["sh_down"], hq, hk, int(bool(getattr(dense, "q_gated", False))),
-                             int(getattr(dense, "rotary_dim", 0) or 0))
+                             int(getattr(dense, "rotary_dim", 0) or 0),
+                             None if self.sinks is None else self.sinks.data_ptr(),
+                             int(getattr(dense, "window", 0) or 0))
 
     @property
     def weight_nbytes(self) -> int:

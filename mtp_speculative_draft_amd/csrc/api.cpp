@@ -228,6 +228,10 @@ hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* v
     a.gk = L->gamma_k_head;
     a.eps = L->eps;
     a.rot = L->rotary_dim > 0 ? L->rotary_dim : L->head_dim;
+    a.window = L->window;
+    a.sinks = L->sinks;
+    // the first row (position cache_len) sees nothing before cache_len - W + 1
+    a.c0 = (L->window > 0 && cache_len - L->window + 1 > 0) ? (cache_len - L->window + 1) / kAttnChunk : 0;
     if ((e = launch_attention(a, st)) != hipSuccess) return e;
     GemvParams o{};
     o.w[0] = qmat(L->wo);
@@ -330,6 +334,9 @@ mtp_status check_layer_attn(const mtp_layer* L) {
     if (rot != 0 && (rot < 2 || rot > L->head_dim || (rot & (rot - 1)) != 0))
         return fail(MTP_ERR_UNSUPPORTED, "rotary_dim=%d (0 or a power of two <= head_dim)", rot);
     if (qn > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "n_heads*head_dim=%d above %d", qn, MTP_MAX_K);
+    if (L->window < 0) return fail(MTP_ERR_INVALID_ARG, "window=%d (0 or positive)", L->window);
+    if (L->sinks && !a4(L->sinks))
+        return fail(MTP_ERR_INVALID_ARG, "sinks must be 4-byte aligned");
     return MTP_OK;
 }
 

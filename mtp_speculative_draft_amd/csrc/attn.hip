@@ -24,6 +24,14 @@
 // of the new k before the rotary step, a rotary step over the first rot
 // dims only, and the output multiplied by sigmoid(gate) in kernel 2, the
 // gate values of a head following its q values in the projection output.
+// Sliding window and sinks (cortiq-engine mimo_mtp.rs, module doc "The draft
+// forward": window 128, sinks): with a window W the row at position p sees
+// positions p-W+1 .. p (a score mask in kernel 1, and the chunks before the
+// first row's window are not launched: partials are stored from chunk c0
+// on); a head's sink logit starts kernel 2's merge as a (max = sink,
+// exp-sum = 1, p*V = 0) term.  With a window the m-row call and m single-row
+// calls may merge the same chunk terms in another order (c0 follows the
+// first row), so they agree to rounding rather than bitwise.
 #include <cmath>
 
 #include "device.hpp"
@@ -53,8 +61,8 @@ __device__ __forceinline__ bool attn_block(const AttnParams& p, int Z, int& c, i
     const int L = blockIdx.x, x = L % 8, r = L / 8;
     z = r % Z;
     const int pair = (r / Z) * 8 + x;
-    if (pair >= p.chunks * p.nkv) return false;
-    c = pair / p.nkv;
+    if (pair >= (p.chunks - p.c0) * p.nkv) return false;
+    c = p.c0 + pair / p.nkv;
     g = pair % p.nkv;
     return true;
 }
@@ -262,11 +270,12 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     // 4. chunk softmax statistics: a wave takes two row-heads at a time, one
     //    per 32-lane half, one position per lane (masked: query row mi sees
     //    positions <= cache_len + mi)
-    float* out = p.part + (((int64_t)c * p.nkv + g) * HMall + hm0) * (kD + 2);
+    float* out = p.part + (((int64_t)(c - p.c0) * p.nkv + g) * HMall + hm0) * (kD + 2);
     const float scale = 1.0f / sqrtf((float)kD);
     for (int hp = 2 * wid; hp < HM; hp += 2 * (int)(blockDim.x / kWave)) {
         const int hm = hp + (lane >> 5), j = lane & 31;
-        const bool ok = hm < HM && p0 + j <= p.cache_len + (hm0 + hm) / GQ;
+        const int qpos = p.cache_len + (hm0 + hm) / GQ;  // the row's position
+        const bool ok = hm < HM && p0 + j <= qpos && (p.window == 0 || p0 + j > qpos - p.window);
         const float sv = ok ? (spart[0][hm][j] + spart[1][hm][j]) * scale : -INFINITY;
         float mx = sv;
         mx = half_max(mx);
@@ -342,17 +351,23 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     const int64_t stride = (int64_t)p.nkv * HM * (kD + 2);  // between chunks
     const float* base = p.part + ((int64_t)g * HM + hm) * (kD + 2);
 
+    // the head's sink is a logit with no value row: lane 0 starts from it
     float M = -INFINITY, L = 0.0f, A = 0.0f;
-    for (int c0 = cs; c0 < p.chunks; c0 += kCombLanes * kCombBatch) {
+    if (p.sinks && cs == 0) {
+        M = p.sinks[hq];
+        L = 1.0f;
+    }
+    const int nch = p.chunks - p.c0;  // partials stored from chunk c0 on
+    for (int c0 = cs; c0 < nch; c0 += kCombLanes * kCombBatch) {
         float lv[kCombBatch], mv[kCombBatch], av[kCombBatch];
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) {
             const int c = c0 + u * kCombLanes;
-            const float* pr = base + (int64_t)(c < p.chunks ? c : 0) * stride;
+            const float* pr = base + (int64_t)(c < nch ? c : 0) * stride;
             lv[u] = pr[kD + 1];
             mv[u] = pr[kD];
             av[u] = pr[dd];
-            if (c >= p.chunks) lv[u] = 0.0f;
+            if (c >= nch) lv[u] = 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) lse_merge(M, L, A, mv[u], lv[u], av[u]);
@@ -444,7 +459,7 @@ hipError_t launch_append_kv(const AttnParams& p, const float* kv, int m, int pos
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int hm = (p.nh / p.nkv) * p.m;
     const int Z = (hm + kSliceHM - 1) / kSliceHM;
-    const int pairs = p.chunks * p.nkv;
+    const int pairs = (p.chunks - p.c0) * p.nkv;
     const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
     if (p.gq || p.rot != kD)
         hipLaunchKernelGGL(k_attn_partial<true>, grid, block, 0, st, p);

@@ -140,6 +140,9 @@ struct AttnParams {
     const float* gk;
     float eps;
     int rot;              // rotary dims (a power of two <= d)
+    int window;           // 0, or W: row at position p sees positions p-W+1 .. p
+    const float* sinks;   // per query head softmax sink logits [nh] (NULL: none)
+    int c0;               // first chunk any row sees; partials are stored from it
 };
 constexpr int kAttnChunk = 32;
 hipError_t launch_attention(const AttnParams& p, hipStream_t stream);

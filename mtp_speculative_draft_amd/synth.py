@@ -107,6 +107,10 @@ class DenseLayer:
     gamma_k_head: Optional[np.ndarray] = None
     q_gated: bool = False
     rotary_dim: int = 0
+    # sliding-window attention ([mimo.rs] "window 128, sinks"): per-query-head
+    # sink logits [n_heads] and the window (0 = none)
+    sinks: Optional[np.ndarray] = None
+    window: int = 0
 
     def q4_weights(self):
         return [self.eh_proj, self.wq, self.wk, self.wv, self.wo, self.gate, self.up, self.down, self.lm_head]
@@ -176,9 +180,10 @@ def gamma(g: np.random.Generator, h: int) -> np.ndarray:
 def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n_kv_heads: int = 2,
                 head_dim: int = 128, vocab: int = 151936, ffn_inter: int = 6144,
                 rope_theta: float = 1.0e6, eps: float = 1e-6, q_gated: bool = False, qk_norm: bool = False,
-                rotary_dim: int = 0) -> DenseLayer:
+                rotary_dim: int = 0, window: int = 0, sinks: bool = False) -> DenseLayer:
     """Dense MTP draft layer with 4-bit weights (draw order fixed; the
-    attention variant's head norm weights are drawn last)."""
+    attention variant's head norm weights are drawn last, then the sinks,
+    U(-1, 3) per query head)."""
     H = hidden
     gam = [gamma(g, H) for _ in range(5)]
     eh = q4_weight(g, H, 2 * H)
@@ -192,9 +197,10 @@ def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n
     lm = q4_weight(g, vocab, H)
     gq = gamma(g, head_dim) if qk_norm else None
     gk = gamma(g, head_dim) if qk_norm else None
+    sk = g.uniform(-1.0, 3.0, size=n_heads).astype(np.float32) if sinks else None
     return DenseLayer(H, n_heads, n_kv_heads, head_dim, vocab, ffn_inter, float(rope_theta), float(eps),
                       gam[0], gam[1], gam[2], gam[3], gam[4], eh, wq, wk, wv, wo, gate, up, down, lm,
-                      gq, gk, bool(q_gated), int(rotary_dim))
+                      gq, gk, bool(q_gated), int(rotary_dim), sk, int(window))
 
 
 def kv_cache(g: np.random.Generator, n_kv_heads: int, filled: int, capacity: int, head_dim: int):

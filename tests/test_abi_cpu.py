@@ -136,14 +136,16 @@ def test_layer_struct_layout_matches_the_header(tmp_path):
     import subprocess
     src = tmp_path / "layout.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "mtp.h"\n'
-                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(mtp_layer), '
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(mtp_layer), '
                    'offsetof(mtp_layer, sh_down), offsetof(mtp_layer, gamma_q_head), '
-                   'offsetof(mtp_layer, q_gated), offsetof(mtp_layer, rotary_dim)); return 0; }\n')
+                   'offsetof(mtp_layer, q_gated), offsetof(mtp_layer, rotary_dim), '
+                   'offsetof(mtp_layer, sinks), offsetof(mtp_layer, window)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(mtp.HEADER), str(src), "-o", str(exe)])
     got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     L = mtp.MtpLayer
-    assert got == [C.sizeof(L), L.sh_down.offset, L.gamma_q_head.offset, L.q_gated.offset, L.rotary_dim.offset]
+    assert got == [C.sizeof(L), L.sh_down.offset, L.gamma_q_head.offset, L.q_gated.offset, L.rotary_dim.offset,
+                   L.sinks.offset, L.window.offset]
 
 
 def test_attention_variant_fields_are_validated():
@@ -165,6 +167,14 @@ def test_attention_variant_fields_are_validated():
     L.gamma_q_head = FAKE  # without gamma_k_head
     assert status(L) == mtp.MTP_ERR_INVALID_ARG
     assert b"gamma_k_head" in lib.mtp_last_error()
+    L = _layer()
+    L.window = -1
+    assert status(L) == mtp.MTP_ERR_INVALID_ARG
+    assert b"window" in lib.mtp_last_error()
+    L = _layer()
+    L.sinks = FAKE + 2  # not 4-byte aligned
+    assert status(L) == mtp.MTP_ERR_INVALID_ARG
+    assert b"sinks" in lib.mtp_last_error()
 
 
 def test_append_kv_rejects_overflow_and_empty_batches():

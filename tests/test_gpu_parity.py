@@ -8,6 +8,7 @@ tile, K not a multiple of 2048), the pages' closed-form fixtures, and the full
 configurations (4-bit GEMV 1024x1024; eh_proj 2048x4096; lm_head
 151936x2048; MoE 256 experts; the dense draft step with a 4096-row cache).
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -292,11 +293,21 @@ _VARIANTS = {
     "rot64": dict(rotary_dim=64),
     "all_rot32": dict(q_gated=True, qk_norm=True, rotary_dim=32),
     "all_rot2": dict(q_gated=True, qk_norm=True, rotary_dim=2),
+    # sliding window and sinks ([mimo.rs] "window 128, sinks")
+    "win40": dict(window=40),
+    "sinks": dict(sinks=True),
+    "swa33": dict(window=33, sinks=True),
+    "swa1": dict(window=1, sinks=True),
+    "win500": dict(window=500),
+    "all_swa64": dict(q_gated=True, qk_norm=True, rotary_dim=32, window=64, sinks=True),
 }
 
 
 @pytest.mark.parametrize("variant,cache_len,m", [("gated", 100, 1), ("qknorm", 31, 3), ("rot64", 64, 2),
-                                                 ("all_rot32", 100, 4), ("all_rot32", 0, 1), ("all_rot2", 40, 8)])
+                                                 ("all_rot32", 100, 4), ("all_rot32", 0, 1), ("all_rot2", 40, 8),
+                                                 ("win40", 100, 4), ("sinks", 31, 3), ("swa33", 100, 8),
+                                                 ("swa1", 100, 2), ("win500", 40, 3), ("swa33", 0, 2),
+                                                 ("all_swa64", 200, 4), ("swa33", 64, 1)])
 def test_attn_decode_variant_small(variant, cache_len, m):
     """[mtp.rs] forward_full_attention's gated q, per-head q/k norms and
     partial rotary dims against the oracle."""
@@ -314,6 +325,11 @@ def test_attn_decode_variant_small(variant, cache_len, m):
     _close(got, ref, "out")
     _close(_np(dk)[:, cache_len:cache_len + m], kr[:, cache_len:cache_len + m], "appended k")
     _close(_np(dv)[:, cache_len:cache_len + m], vr[:, cache_len:cache_len + m], "appended v")
+    if (L.window and L.window < cache_len) or L.sinks is not None:
+        # the window / sinks change this case's output (so ignoring them fails)
+        plain = dataclasses.replace(L, window=0, sinks=None)
+        ref0 = oracle.attention(plain, u, kc.copy(), vc.copy(), cache_len)
+        assert oracle.rel_l2(ref0, ref) > 1e-3
 
 
 @pytest.mark.parametrize("m", [1, 4])
@@ -322,6 +338,22 @@ def test_attn_decode_variant_config4_shape(m):
     _say(f"attn variant config4 shape m={m}")
     g = synth.rng(114, m)
     L = synth.dense_layer(g, vocab=64, ffn_inter=64, q_gated=True, qk_norm=True, rotary_dim=64)
+    kc, vc = synth.kv_cache(g, 2, 4096, 4104, 128)
+    u = synth.normal(g, (m, 2048))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(u), dk, dv, 4096))
+    ref = oracle.attention(L, u, kc, vc, 4096)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, 4096:4096 + m], kc[:, 4096:4096 + m], "appended k")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_attn_decode_sliding_window_config4_shape(m):
+    """The MiMo draft attention's window of 128 and per-head sinks at the full
+    attention size (16/2 heads x 128, cache 4096: 5 of 129 chunks launched)."""
+    _say(f"attn window 128 + sinks config4 shape m={m}")
+    g = synth.rng(125, m)
+    L = synth.dense_layer(g, vocab=64, ffn_inter=64, window=128, sinks=True)
     kc, vc = synth.kv_cache(g, 2, 4096, 4104, 128)
     u = synth.normal(g, (m, 2048))
     dk, dv = _t(kc), _t(vc)
@@ -525,6 +557,19 @@ def test_draft_step_variant_chain_and_verify():
         if min(margins) >= 1e-2:
             break
     _check_step(S, f"variant seed {extra}", ref)
+
+
+def test_draft_step_sliding_window_chain_and_verify():
+    """The whole layer with the window-64, sink-carrying attention (the chain
+    crosses no chunk boundary of the window start; the verify rows do)."""
+    for extra in range(1, 30):
+        S = synth.config4_step(seed_extra=1600 + extra, cache_len=100, capacity=110, hidden=256, n_heads=4,
+                               n_kv_heads=2, head_dim=128, vocab=1000, ffn_inter=320, window=64, sinks=True)
+        ref = _chain_and_verify_oracle(S)
+        margins = [planting.head_margin(o[2]) for o in ref[0]] + [planting.head_margin(r) for r in ref[1][2]]
+        if min(margins) >= 1e-2:
+            break
+    _check_step(S, f"window seed {extra}", ref)
 
 
 def test_draft_step_config4():
