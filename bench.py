@@ -280,8 +280,9 @@ def event_us(torch, dev, fn, n, warm):
 
 
 def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
-    """Attention block (cache 4096, 16 q / 2 kv heads x 128; plain and with gated
-    q, per-head q/k norms and rotary over 64 of 128 dims) at m = 1 and 4, the
+    """Attention block (cache 4096, 16 q / 2 kv heads x 128; plain, with gated
+    q, per-head q/k norms and rotary over 64 of 128 dims, and with a 128-row
+    sliding window and per-head sinks) at m = 1 and 4, the
     cache catch-up of a 4-row target batch, and the three-layer draft stack
     (each layer catches up 4 rows, then drafts row t).  The attention and
     catch-up loops rotate over 24 layer/cache copies (about 18 MB read each) so that
@@ -294,7 +295,8 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
     def q4_bytes(dl, names):
         return sum(dl.q4[k].nbytes for k in names)
 
-    for name, kw in (("attn", {}), ("attn_variant", {"q_gated": True, "qk_norm": True, "rotary_dim": 64})):
+    for name, kw in (("attn", {}), ("attn_variant", {"q_gated": True, "qk_norm": True, "rotary_dim": 64}),
+                     ("attn_window128_sinks", {"window": 128, "sinks": True})):
         g = synth.rng(40)
         Lh = synth.dense_layer(g, vocab=64, **kw)
         kc, vc = synth.kv_cache(g, NKV, L0, CAP, D)
@@ -311,7 +313,8 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
                 mtp.mtp_attn_decode(dl, u, dk, dv, L0, out=o, ws=ws)
 
             us = event_us(torch, dev, call, n, W)
-            b = wb + kvrow * (L0 + m) + kvrow * m + m * H * 4 * 2
+            seen = L0 + m if not kw.get("window") else min(L0 + m, kw["window"] + m - 1)  # K/V rows read
+            b = wb + kvrow * seen + kvrow * m + m * H * 4 * 2
             out[f"{name}_cache4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
         if name == "attn":
             # cache catch-up: shifted target hidden -> eh_proj -> K/V rows of 4 positions
