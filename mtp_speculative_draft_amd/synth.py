@@ -111,6 +111,8 @@ class DenseLayer:
     # sink logits [n_heads] and the window (0 = none)
     sinks: Optional[np.ndarray] = None
     window: int = 0
+    # MiMo draft geometry (head 192 / V 128): the V heads' width (0 = head_dim)
+    v_head_dim: int = 0
 
     def q4_weights(self):
         return [self.eh_proj, self.wq, self.wk, self.wv, self.wo, self.gate, self.up, self.down, self.lm_head]
@@ -180,17 +182,18 @@ def gamma(g: np.random.Generator, h: int) -> np.ndarray:
 def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n_kv_heads: int = 2,
                 head_dim: int = 128, vocab: int = 151936, ffn_inter: int = 6144,
                 rope_theta: float = 1.0e6, eps: float = 1e-6, q_gated: bool = False, qk_norm: bool = False,
-                rotary_dim: int = 0, window: int = 0, sinks: bool = False) -> DenseLayer:
+                rotary_dim: int = 0, window: int = 0, sinks: bool = False, v_head_dim: int = 0) -> DenseLayer:
     """Dense MTP draft layer with 4-bit weights (draw order fixed; the
     attention variant's head norm weights are drawn last, then the sinks,
     U(-1, 3) per query head)."""
     H = hidden
     gam = [gamma(g, H) for _ in range(5)]
     eh = q4_weight(g, H, 2 * H)
-    wq = q4_weight(g, (2 if q_gated else 1) * n_heads * head_dim, H)
+    dv = v_head_dim if v_head_dim > 0 else head_dim
+    wq = q4_weight(g, n_heads * (head_dim + dv if q_gated else head_dim), H)
     wk = q4_weight(g, n_kv_heads * head_dim, H)
-    wv = q4_weight(g, n_kv_heads * head_dim, H)
-    wo = q4_weight(g, H, n_heads * head_dim)
+    wv = q4_weight(g, n_kv_heads * dv, H)
+    wo = q4_weight(g, H, n_heads * dv)
     gate = q4_weight(g, ffn_inter, H)
     up = q4_weight(g, ffn_inter, H)
     down = q4_weight(g, H, ffn_inter)
@@ -200,15 +203,18 @@ def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n
     sk = g.uniform(-1.0, 3.0, size=n_heads).astype(np.float32) if sinks else None
     return DenseLayer(H, n_heads, n_kv_heads, head_dim, vocab, ffn_inter, float(rope_theta), float(eps),
                       gam[0], gam[1], gam[2], gam[3], gam[4], eh, wq, wk, wv, wo, gate, up, down, lm,
-                      gq, gk, bool(q_gated), int(rotary_dim), sk, int(window))
+                      gq, gk, bool(q_gated), int(rotary_dim), sk, int(window), int(v_head_dim))
 
 
-def kv_cache(g: np.random.Generator, n_kv_heads: int, filled: int, capacity: int, head_dim: int):
-    """K and V caches [n_kv, capacity, head_dim]: rows < filled ~ N(0,1), the rest zero."""
+def kv_cache(g: np.random.Generator, n_kv_heads: int, filled: int, capacity: int, head_dim: int,
+             v_dim: int = 0):
+    """K cache [n_kv, capacity, head_dim] and V cache [n_kv, capacity, v_dim or
+    head_dim]: rows < filled ~ N(0,1), the rest zero."""
+    dv = v_dim if v_dim > 0 else head_dim
     k = np.zeros((n_kv_heads, capacity, head_dim), dtype=np.float32)
-    v = np.zeros((n_kv_heads, capacity, head_dim), dtype=np.float32)
+    v = np.zeros((n_kv_heads, capacity, dv), dtype=np.float32)
     k[:, :filled] = normal(g, (n_kv_heads, filled, head_dim))
-    v[:, :filled] = normal(g, (n_kv_heads, filled, head_dim))
+    v[:, :filled] = normal(g, (n_kv_heads, filled, dv))
     return k, v
 
 

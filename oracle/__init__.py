@@ -54,7 +54,7 @@ class _Layer(C.Structure):
                 ("gate", _Q4), ("up", _Q4), ("down", _Q4), ("lm_head", _Q4),
                 ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
                 ("q_gated", C.c_int32), ("rotary_dim", C.c_int32),
-                ("sinks", C.c_void_p), ("window", C.c_int32)]
+                ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32)]
 
 
 def lib():
@@ -75,6 +75,7 @@ def lib():
             "orc_rope_partial": (None, [P, I, I, I, I, I, C.c_double]),
             "orc_sdpa": (None, [P, P, P, I, I, I, I, I, I, P]),
             "orc_sdpa_window": (None, [P, P, P, I, I, I, I, I, I, I, P, P]),
+            "orc_sdpa_kv": (None, [P, P, P, I, I, I, I, I, I, I, I, P, P]),
             "orc_argmax": (I, [P, I]),
             "orc_norm_concat_proj": (None, [P, P, P, P, C.c_float, P, I, P]),
             "orc_attention": (None, [P, P, P, P, I, I, I, P]),
@@ -144,7 +145,8 @@ def _layer(L, keep: _Keep) -> _Layer:
                   _q4(L.gate, keep), _q4(L.up, keep), _q4(L.down, keep), _q4(L.lm_head, keep),
                   opt(getattr(L, "gamma_q_head", None)), opt(getattr(L, "gamma_k_head", None)),
                   int(bool(getattr(L, "q_gated", False))), int(getattr(L, "rotary_dim", 0) or 0),
-                  opt(getattr(L, "sinks", None)), int(getattr(L, "window", 0) or 0))
+                  opt(getattr(L, "sinks", None)), int(getattr(L, "window", 0) or 0),
+                  int(getattr(L, "v_head_dim", 0) or 0))
 
 
 # --------------------------------------------------------------------------
@@ -220,15 +222,18 @@ def rope(x: np.ndarray, n_heads: int, head_dim: int, pos0: int, theta: float, ro
 def sdpa(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, n_heads: int, cache_len: int,
          window: int = 0, sinks: Optional[np.ndarray] = None) -> np.ndarray:
     """Causal GQA attention of q [m, n_heads*d] over the caches; window > 0
-    keeps the last `window` positions per row, sinks [n_heads] join the softmax."""
+    keeps the last `window` positions per row, sinks [n_heads] join the softmax.
+    The V cache may have its own row width dv (outputs [m, n_heads*dv])."""
     q = _c(np.atleast_2d(q), np.float32)
     kc = _c(k_cache, np.float32)
     vc = _c(v_cache, np.float32)
     nkv, cap, d = kc.shape
-    out = np.empty((q.shape[0], n_heads * d), dtype=np.float32)
+    dv = vc.shape[2]
+    assert vc.shape[:2] == (nkv, cap)
+    out = np.empty((q.shape[0], n_heads * dv), dtype=np.float32)
     sk = None if sinks is None else _c(sinks, np.float32)
-    lib().orc_sdpa_window(_p(q), _p(kc), _p(vc), q.shape[0], n_heads, nkv, d, cache_len, cap, int(window), _p(sk),
-                          _p(out))
+    lib().orc_sdpa_kv(_p(q), _p(kc), _p(vc), q.shape[0], n_heads, nkv, d, dv, cache_len, cap, int(window), _p(sk),
+                      _p(out))
     return out
 
 

@@ -186,11 +186,21 @@ void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_
 void orc_sdpa_window(const float* q, const float* k_cache, const float* v_cache, int32_t m, int32_t n_heads,
                      int32_t n_kv_heads, int32_t head_dim, int32_t cache_len, int32_t capacity, int32_t window,
                      const float* sinks, float* out) {
+    orc_sdpa_kv(q, k_cache, v_cache, m, n_heads, n_kv_heads, head_dim, head_dim, cache_len, capacity, window, sinks,
+                out);
+}
+
+/* The same with V heads of their own width v_dim (MiMo's head 192 / V 128):
+ * scores over head_dim, scale 1/sqrt(head_dim), outputs and V cache rows of
+ * v_dim floats ([n_kv_heads][capacity][v_dim]). */
+void orc_sdpa_kv(const float* q, const float* k_cache, const float* v_cache, int32_t m, int32_t n_heads,
+                 int32_t n_kv_heads, int32_t head_dim, int32_t v_dim, int32_t cache_len, int32_t capacity,
+                 int32_t window, const float* sinks, float* out) {
     const int32_t group = n_heads / n_kv_heads;
     const double scale = 1.0 / sqrt((double)head_dim);
     const int32_t max_len = cache_len + m;
     double* p = (double*)xmalloc(sizeof(double) * (size_t)max_len);
-    double* o = (double*)xmalloc(sizeof(double) * (size_t)head_dim);
+    double* o = (double*)xmalloc(sizeof(double) * (size_t)v_dim);
     for (int32_t r = 0; r < m; ++r) {
         const int32_t pos = cache_len + r;
         const int32_t lo = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
@@ -198,7 +208,7 @@ void orc_sdpa_window(const float* q, const float* k_cache, const float* v_cache,
             const int32_t g = hh / group;
             const float* qv = q + ((size_t)r * n_heads + hh) * head_dim;
             const float* K = k_cache + (size_t)g * capacity * head_dim;
-            const float* V = v_cache + (size_t)g * capacity * head_dim;
+            const float* V = v_cache + (size_t)g * capacity * v_dim;
             double mx = sinks ? (double)sinks[hh] : -INFINITY;
             for (int32_t j = lo; j <= pos; ++j) {
                 double s = 0.0;
@@ -212,11 +222,11 @@ void orc_sdpa_window(const float* q, const float* k_cache, const float* v_cache,
                 p[j] = exp(p[j] - mx);
                 z += p[j];
             }
-            for (int32_t t = 0; t < head_dim; ++t) o[t] = 0.0;
+            for (int32_t t = 0; t < v_dim; ++t) o[t] = 0.0;
             for (int32_t j = lo; j <= pos; ++j)
-                for (int32_t t = 0; t < head_dim; ++t) o[t] += p[j] * (double)V[(size_t)j * head_dim + t];
-            float* dst = out + ((size_t)r * n_heads + hh) * head_dim;
-            for (int32_t t = 0; t < head_dim; ++t) dst[t] = (float)(o[t] / z);
+                for (int32_t t = 0; t < v_dim; ++t) o[t] += p[j] * (double)V[(size_t)j * v_dim + t];
+            float* dst = out + ((size_t)r * n_heads + hh) * v_dim;
+            for (int32_t t = 0; t < v_dim; ++t) dst[t] = (float)(o[t] / z);
         }
     }
     free(p);
@@ -268,23 +278,24 @@ void orc_norm_concat_proj(const float* e, const float* h, const float* gamma_e, 
 void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_cache,
                    int32_t cache_len, int32_t capacity, int32_t m, float* r1) {
     const int32_t H = L->hidden, d = L->head_dim, nh = L->n_heads, nkv = L->n_kv_heads;
-    const int32_t qrows = (L->q_gated ? 2 : 1) * nh * d;
+    const int32_t dv = L->v_head_dim > 0 ? L->v_head_dim : d;
+    const int32_t qrows = nh * (L->q_gated ? d + dv : d);
     const int32_t rot = L->rotary_dim > 0 ? L->rotary_dim : d;
     float* xa = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* qg = (float*)xmalloc(sizeof(float) * (size_t)m * qrows);
     float* q = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
-    float* gate = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
+    float* gate = (float*)xmalloc(sizeof(float) * (size_t)m * nh * dv);
     float* k = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
-    float* v = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
-    float* o = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
+    float* v = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * dv);
+    float* o = (float*)xmalloc(sizeof(float) * (size_t)m * nh * dv);
     float* a = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     orc_rmsnorm(u, L->gamma_attn, m, H, L->eps, xa);
     orc_gemv4(&L->wq, xa, m, qg);
     for (int32_t r = 0; r < m; ++r)
         for (int32_t hh = 0; hh < nh; ++hh) {
-            const float* src = qg + (size_t)r * qrows + (size_t)hh * (L->q_gated ? 2 * d : d);
+            const float* src = qg + (size_t)r * qrows + (size_t)hh * (L->q_gated ? d + dv : d);
             memcpy(q + ((size_t)r * nh + hh) * d, src, sizeof(float) * (size_t)d);
-            if (L->q_gated) memcpy(gate + ((size_t)r * nh + hh) * d, src + d, sizeof(float) * (size_t)d);
+            if (L->q_gated) memcpy(gate + ((size_t)r * nh + hh) * dv, src + d, sizeof(float) * (size_t)dv);
         }
     orc_gemv4(&L->wk, xa, m, k);
     orc_gemv4(&L->wv, xa, m, v);
@@ -295,13 +306,13 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
     orc_rope_partial(k, m, nkv, d, rot, cache_len, L->rope_theta);
     for (int32_t r = 0; r < m; ++r)
         for (int32_t g = 0; g < nkv; ++g) {
-            size_t dst = ((size_t)g * capacity + (size_t)(cache_len + r)) * d;
-            memcpy(k_cache + dst, k + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
-            memcpy(v_cache + dst, v + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
+            const size_t row = (size_t)g * capacity + (size_t)(cache_len + r);
+            memcpy(k_cache + row * d, k + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
+            memcpy(v_cache + row * dv, v + ((size_t)r * nkv + g) * dv, sizeof(float) * (size_t)dv);
         }
-    orc_sdpa_window(q, k_cache, v_cache, m, nh, nkv, d, cache_len, capacity, L->window, L->sinks, o);
+    orc_sdpa_kv(q, k_cache, v_cache, m, nh, nkv, d, dv, cache_len, capacity, L->window, L->sinks, o);
     if (L->q_gated)
-        for (size_t i = 0; i < (size_t)m * nh * d; ++i)
+        for (size_t i = 0; i < (size_t)m * nh * dv; ++i)
             o[i] = (float)((double)o[i] / (1.0 + exp(-(double)gate[i])));
     orc_gemv4(&L->wo, o, m, a);
     for (size_t i = 0; i < (size_t)m * H; ++i) r1[i] = (float)((double)u[i] + (double)a[i]);
@@ -328,13 +339,14 @@ void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, co
                    const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
                    int32_t cache_len, int32_t capacity, int32_t m) {
     const int32_t H = L->hidden, d = L->head_dim, nkv = L->n_kv_heads;
+    const int32_t dv = L->v_head_dim > 0 ? L->v_head_dim : d;
     const int32_t rot = L->rotary_dim > 0 ? L->rotary_dim : d;
     float* er = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* sh = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* u = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* xa = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* k = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
-    float* v = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * d);
+    float* v = (float*)xmalloc(sizeof(float) * (size_t)m * nkv * dv);
     for (int32_t r = 0; r < m; ++r) {
         const float* src = (tokens && tokens[r] >= 0) ? embed_table + (size_t)tokens[r] * H : e + (size_t)r * H;
         memcpy(er + (size_t)r * H, src, sizeof(float) * (size_t)H);
@@ -355,9 +367,9 @@ void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, co
     orc_rope_partial(k, m, nkv, d, rot, cache_len, L->rope_theta);
     for (int32_t r = 0; r < m; ++r)
         for (int32_t g = 0; g < nkv; ++g) {
-            size_t dst = ((size_t)g * capacity + (size_t)(cache_len + r)) * d;
-            memcpy(k_cache + dst, k + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
-            memcpy(v_cache + dst, v + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
+            const size_t row = (size_t)g * capacity + (size_t)(cache_len + r);
+            memcpy(k_cache + row * d, k + ((size_t)r * nkv + g) * d, sizeof(float) * (size_t)d);
+            memcpy(v_cache + row * dv, v + ((size_t)r * nkv + g) * dv, sizeof(float) * (size_t)dv);
         }
     free(er);
     free(sh);

@@ -64,7 +64,14 @@ typedef struct {
  *   window        0: causal over the whole cache; W > 0: the row at position
  *                 p sees positions p-W+1 .. p only (W rows, itself included);
  *   sinks         f32 [n_heads] or NULL: one logit per query head that joins
- *                 the softmax denominator with no value row. */
+ *                 the softmax denominator with no value row.
+ * MiMo draft geometry ([mimo.rs] module doc "The draft forward": head 192 /
+ * V 128):
+ *   v_head_dim    0 = head_dim; else the width dv of the V heads (and of the
+ *                 attention output per head): wv has n_kv_heads*dv rows, wo
+ *                 n_heads*dv columns, the V cache rows are dv wide, and with
+ *                 q_gated a head's gate rows (dv of them) follow its head_dim
+ *                 q rows. */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab, ffn_inter;
     double rope_theta;
@@ -75,6 +82,7 @@ typedef struct {
     int32_t q_gated, rotary_dim;
     const float* sinks;
     int32_t window;
+    int32_t v_head_dim;
 } orc_layer;
 
 /* ---- weight formats ---- */
@@ -96,6 +104,9 @@ void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_
 void orc_sdpa_window(const float* q, const float* k_cache, const float* v_cache, int32_t m, int32_t n_heads,
                      int32_t n_kv_heads, int32_t head_dim, int32_t cache_len, int32_t capacity, int32_t window,
                      const float* sinks, float* out);
+void orc_sdpa_kv(const float* q, const float* k_cache, const float* v_cache, int32_t m, int32_t n_heads,
+                 int32_t n_kv_heads, int32_t head_dim, int32_t v_dim, int32_t cache_len, int32_t capacity,
+                 int32_t window, const float* sinks, float* out);
 int32_t orc_argmax(const float* v, int32_t n);
 
 /* ---- layer steps ---- */

@@ -7,6 +7,7 @@ group index, dropped bias, transposed weight, wrong RoPE pairing or
 frequency, an off-by-one causal mask, a missing gate renormalisation, the
 concat order) fails at least one test here.
 """
+import dataclasses
 import json
 import math
 import os
@@ -364,6 +365,83 @@ def test_sdpa_very_negative_sinks_change_nothing():
     q = synth.normal(g, (2, 4 * 16))
     plain = oracle.sdpa(q, kc, vc, 4, 11)
     assert (oracle.sdpa(q, kc, vc, 4, 11, sinks=np.full(4, -1e4, np.float32)) == plain).all()
+
+
+# --------------------------------------------------------------------------
+# V heads of their own width ([mimo.rs] module doc "The draft forward": head
+# 192 / V 128)
+# --------------------------------------------------------------------------
+def test_sdpa_narrow_v_length_one_cache_returns_the_v_row():
+    g = np.random.default_rng(70)
+    kc, _ = _caches(g, 2, 4, 24)
+    vc = synth.normal(g, (2, 4, 16))
+    q = synth.normal(g, (1, 4 * 24))
+    o = oracle.sdpa(q, kc, vc, 4, 0)
+    assert o.shape == (1, 4 * 16)
+    for hh in range(4):
+        assert (o[0, hh * 16:(hh + 1) * 16] == vc[hh // 2, 0]).all()
+
+
+def test_sdpa_narrow_v_equals_the_leading_columns_of_a_head_wide_v():
+    """The weights come from q and K only: V rows of width 16 give the first 16
+    columns of what V rows of the head's width 24 (same leading columns) give,
+    and each column block of V gives its block of the output."""
+    g = np.random.default_rng(71)
+    kc, vwide = _caches(g, 2, 20, 24)
+    q = synth.normal(g, (3, 4 * 24))
+    sinks = np.array([0.5, -1.0, 2.0, 0.0], np.float32)
+    wide = oracle.sdpa(q, kc, vwide, 4, 12, window=6, sinks=sinks).reshape(3, 4, 24)
+    narrow = oracle.sdpa(q, kc, np.ascontiguousarray(vwide[:, :, :16]), 4, 12, window=6,
+                         sinks=sinks).reshape(3, 4, 16)
+    assert np.allclose(narrow, wide[:, :, :16], rtol=1e-6, atol=1e-7)
+    tail = oracle.sdpa(q, kc, np.ascontiguousarray(vwide[:, :, 16:]), 4, 12, window=6, sinks=sinks).reshape(3, 4, 8)
+    assert np.allclose(tail, wide[:, :, 16:], rtol=1e-6, atol=1e-7)
+
+
+def test_sdpa_narrow_v_equal_keys_average_v():
+    g = np.random.default_rng(72)
+    nkv, cap, d, dv, L = 2, 9, 24, 8, 6
+    kc = np.zeros((nkv, cap, d), np.float32)
+    kc[:] = synth.normal(g, (1, 1, d))
+    vc = synth.normal(g, (nkv, cap, dv))
+    q = synth.normal(g, (1, 4 * d))
+    o = oracle.sdpa(q, kc, vc, 4, L - 1)
+    for hh in range(4):
+        want = vc[hh // 2, :L].astype(np.float64).mean(axis=0)
+        assert np.allclose(o[0, hh * dv:(hh + 1) * dv], want, rtol=0, atol=1e-6)
+
+
+def test_attention_v_width_equal_to_the_head_is_the_plain_attention():
+    L = synth.dense_layer(np.random.default_rng(73), hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, vocab=50,
+                          ffn_inter=32)
+    g = np.random.default_rng(74)
+    u = synth.normal(g, (3, 64))
+    kc, vc = synth.kv_cache(g, 2, 7, 12, 16)
+    ref = oracle.attention(L, u, kc.copy(), vc.copy(), 7)
+    same = oracle.attention(dataclasses.replace(L, v_head_dim=16), u, kc.copy(), vc.copy(), 7)
+    assert (ref == same).all()
+
+
+def test_attention_narrow_v_appends_v_rows_and_reads_them():
+    """Head 24 with V 16 (and a gated q, whose gate rows are V-wide): the new V
+    rows are Wv rms(u) in 16-wide cache rows, and a window of one row makes the
+    attention output the own row's V times sigmoid(gate), so
+    r1 = u + Wo (v * sigmoid(gate)) per head."""
+    L = synth.dense_layer(np.random.default_rng(75), hidden=64, n_heads=4, n_kv_heads=2, head_dim=24, vocab=50,
+                          ffn_inter=32, v_head_dim=16, q_gated=True, window=1)
+    g = np.random.default_rng(76)
+    m, cl = 2, 5
+    u = synth.normal(g, (m, 64))
+    kc, vc = synth.kv_cache(g, 2, cl, 9, 24, v_dim=16)
+    r1 = oracle.attention(L, u, kc, vc, cl)
+    xa = oracle.rmsnorm(u, L.gamma_attn, L.eps)
+    v = oracle.gemv4(L.wv, xa).reshape(m, 2, 16)
+    assert np.allclose(vc[:, cl:cl + m].transpose(1, 0, 2), v, rtol=0, atol=0)
+    qg = oracle.gemv4(L.wq, xa).reshape(m, 4, 24 + 16)
+    gate = qg[:, :, 24:].astype(np.float64)
+    o = v[:, [0, 0, 1, 1], :].astype(np.float64) / (1.0 + np.exp(-gate))
+    want = u.astype(np.float64) + oracle.gemv4(L.wo, o.reshape(m, 64).astype(np.float32)).astype(np.float64)
+    assert np.allclose(r1, want, rtol=1e-5, atol=1e-5)
 
 
 # --------------------------------------------------------------------------
