@@ -106,7 +106,15 @@ typedef struct {
  *                 head h a logit sinks[h] that joins the softmax denominator
  *                 with no value row: o = sum_j e^(s_j-M) v_j /
  *                 (sum_j e^(s_j-M) + e^(sinks[h]-M)), M = max(sinks[h], max s_j),
- *                 s_j the scaled scores. */
+ *                 s_j the scaled scores.
+ * MiMo draft geometry ([mimo.rs] module doc "The draft forward": "head 192 /
+ * V 128"):
+ *   v_head_dim    0 = head_dim; else the V heads' width dv: wv is
+ *                 [n_kv_heads*dv][hidden], wo [hidden][n_heads*dv], and the V
+ *                 cache is [n_kv_heads][capacity][dv] (the K cache keeps
+ *                 head_dim).  Built: head_dim 128 with V 128, and head_dim 192
+ *                 with V 128 (no gated q or per-head norms there; rotary over
+ *                 all 192 dims by default, pairs (i, i + 96)). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab;
     int32_t ffn_kind; /* MTP_FFN_DENSE_Q4 or MTP_FFN_MOE_Q8 */
@@ -122,6 +130,7 @@ typedef struct {
     int32_t q_gated, rotary_dim;
     const float* sinks;
     int32_t window;
+    int32_t v_head_dim;
 } mtp_layer;
 
 const char* mtp_status_string(mtp_status s);

@@ -67,7 +67,7 @@ class MtpLayer(C.Structure):
                 ("sh_gate", MtpQ8), ("sh_up", MtpQ8), ("sh_down", MtpQ8),
                 ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
                 ("q_gated", C.c_int32), ("rotary_dim", C.c_int32),
-                ("sinks", C.c_void_p), ("window", C.c_int32)]
+                ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32)]
 
 
 _lib = None
@@ -211,7 +211,7 @@ class DeviceLayer:
                              q8["sh_down"], hq, hk, int(bool(getattr(dense, "q_gated", False))),
                              int(getattr(dense, "rotary_dim", 0) or 0),
                              None if self.sinks is None else self.sinks.data_ptr(),
-                             int(getattr(dense, "window", 0) or 0))
+                             int(getattr(dense, "window", 0) or 0), int(getattr(dense, "v_head_dim", 0) or 0))
 
     @property
     def weight_nbytes(self) -> int:

@@ -94,12 +94,14 @@ int chunks_for(int32_t cache_len, int32_t m) { return (cache_len + m + kAttnChun
 struct AttnWs {
     float *qkv, *part, *o;
 };
+int v_dim(const mtp_layer* L) { return L->v_head_dim > 0 ? L->v_head_dim : L->head_dim; }
+
 AttnWs carve_attn(Carve& c, const mtp_layer* L, int32_t cache_len, int32_t m) {
     AttnWs w;
-    const int d = L->head_dim, nh = L->n_heads, nkv = L->n_kv_heads;
-    w.qkv = c.take<float>((size_t)m * ((L->q_gated ? 2 : 1) * nh + 2 * nkv) * d);
-    w.part = c.take<float>((size_t)chunks_for(cache_len, m) * nkv * (nh / (nkv ? nkv : 1)) * m * (d + 2));
-    w.o = c.take<float>((size_t)m * nh * d);
+    const int d = L->head_dim, dv = v_dim(L), nh = L->n_heads, nkv = L->n_kv_heads;
+    w.qkv = c.take<float>((size_t)m * (nh * (L->q_gated ? d + dv : d) + nkv * (d + dv)));
+    w.part = c.take<float>((size_t)chunks_for(cache_len, m) * nkv * (nh / (nkv ? nkv : 1)) * m * (dv + 2));
+    w.o = c.take<float>((size_t)m * nh * dv);
     return w;
 }
 
@@ -219,6 +221,7 @@ hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* v
     a.nh = L->n_heads;
     a.nkv = L->n_kv_heads;
     a.d = L->head_dim;
+    a.vd = v_dim(L);
     a.log2_theta = log2(L->rope_theta);
     a.part = w.part;
     a.o = w.o;
@@ -311,7 +314,14 @@ mtp_status check_layer_attn(const mtp_layer* L) {
     if (!L) return fail(MTP_ERR_INVALID_ARG, "layer is NULL");
     const int H = L->hidden;
     if (H < MTP_GROUP || H % MTP_GROUP || H > MTP_MAX_K) return fail(MTP_ERR_INVALID_ARG, "hidden=%d", H);
-    if (L->head_dim != 128) return fail(MTP_ERR_UNSUPPORTED, "head_dim=%d (only 128 is built)", L->head_dim);
+    if (L->head_dim != 128 && L->head_dim != 192)
+        return fail(MTP_ERR_UNSUPPORTED, "head_dim=%d (128, or 192 with v_head_dim 128)", L->head_dim);
+    if (L->v_head_dim < 0) return fail(MTP_ERR_INVALID_ARG, "v_head_dim=%d", L->v_head_dim);
+    const int dv = v_dim(L);
+    if (dv != 128)
+        return fail(MTP_ERR_UNSUPPORTED, "v_head_dim=%d (V heads of 128 are built)", L->v_head_dim);
+    if (L->head_dim != 128 && (L->q_gated || L->gamma_q_head || L->gamma_k_head))
+        return fail(MTP_ERR_UNSUPPORTED, "head_dim=%d: no gated q or per-head norms", L->head_dim);
     if (L->n_heads < 1 || L->n_kv_heads < 1 || L->n_heads % L->n_kv_heads)
         return fail(MTP_ERR_INVALID_ARG, "n_heads=%d n_kv_heads=%d", L->n_heads, L->n_kv_heads);
     if (!(L->eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
@@ -322,9 +332,10 @@ mtp_status check_layer_attn(const mtp_layer* L) {
         (s = check_q4(&L->wo, "wo")))
         return s;
     const int qn = L->n_heads * L->head_dim, kvn = L->n_kv_heads * L->head_dim;
+    const int on = L->n_heads * dv, vn = L->n_kv_heads * dv;
     if (L->q_gated != 0 && L->q_gated != 1) return fail(MTP_ERR_INVALID_ARG, "q_gated=%d (0 or 1)", L->q_gated);
-    if (L->wq.n != (L->q_gated ? 2 : 1) * qn || L->wq.k != H || L->wk.n != kvn || L->wk.k != H || L->wv.n != kvn ||
-        L->wv.k != H || L->wo.n != H || L->wo.k != qn)
+    if (L->wq.n != qn + (L->q_gated ? on : 0) || L->wq.k != H || L->wk.n != kvn || L->wk.k != H || L->wv.n != vn ||
+        L->wv.k != H || L->wo.n != H || L->wo.k != on)
         return fail(MTP_ERR_INVALID_ARG, "attention weight shapes do not match hidden/heads/head_dim");
     if ((L->gamma_q_head == nullptr) != (L->gamma_k_head == nullptr))
         return fail(MTP_ERR_INVALID_ARG, "gamma_q_head and gamma_k_head: give both or neither");
@@ -333,7 +344,7 @@ mtp_status check_layer_attn(const mtp_layer* L) {
     const int rot = L->rotary_dim;
     if (rot != 0 && (rot < 2 || rot > L->head_dim || (rot & (rot - 1)) != 0))
         return fail(MTP_ERR_UNSUPPORTED, "rotary_dim=%d (0 or a power of two <= head_dim)", rot);
-    if (qn > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "n_heads*head_dim=%d above %d", qn, MTP_MAX_K);
+    if (on > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "n_heads*v_head_dim=%d above %d", on, MTP_MAX_K);
     if (L->window < 0) return fail(MTP_ERR_INVALID_ARG, "window=%d (0 or positive)", L->window);
     if (L->sinks && !a4(L->sinks))
         return fail(MTP_ERR_INVALID_ARG, "sinks must be 4-byte aligned");
@@ -446,7 +457,7 @@ size_t mtp_append_kv_workspace_size(const mtp_layer* L) {
     Carve c{nullptr};
     c.take<float>((size_t)MTP_MAX_ROWS * L->hidden);                           // shifted hidden
     c.take<float>((size_t)MTP_MAX_ROWS * L->hidden);                           // u
-    c.take<float>((size_t)MTP_MAX_ROWS * 2 * L->n_kv_heads * L->head_dim);     // k, v
+    c.take<float>((size_t)MTP_MAX_ROWS * L->n_kv_heads * (L->head_dim + v_dim(L)));  // k, v
     return c.off;
 }
 
@@ -478,14 +489,14 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
     Carve c{static_cast<char*>(ws)};
     float* shifted = c.take<float>((size_t)MTP_MAX_ROWS * H);
     float* u = c.take<float>((size_t)MTP_MAX_ROWS * H);
-    const int kvn = L->n_kv_heads * L->head_dim;
-    float* kv = c.take<float>((size_t)MTP_MAX_ROWS * 2 * kvn);
+    float* kv = c.take<float>((size_t)MTP_MAX_ROWS * L->n_kv_heads * (L->head_dim + v_dim(L)));
     AttnParams a{};
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.capacity = capacity;
     a.nkv = L->n_kv_heads;
     a.d = L->head_dim;
+    a.vd = v_dim(L);
     a.log2_theta = log2(L->rope_theta);
     a.gk = L->gamma_k_head;
     a.eps = L->eps;
@@ -520,7 +531,7 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
         q.w[0] = qmat(L->wk);
         q.w[1] = qmat(L->wv);
         q.nmat = 2;
-        q.N = 2 * kvn;
+        q.N = L->wk.n + L->wv.n;
         q.K = H;
         q.x0 = u;
         q.g0 = L->gamma_attn;

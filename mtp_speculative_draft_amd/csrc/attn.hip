@@ -441,6 +441,152 @@ __global__ void __launch_bounds__(64) k_append_kv(const AttnParams p, const floa
     vd[lane + kD / 2] = vb;
 }
 
+// ---------------------------------------------------------------------------
+// Wide geometry (cortiq-engine mimo_mtp.rs, module doc "The draft forward":
+// q/k heads of 192 with V heads of 128): q/k rows of p.d floats, V rows of
+// p.vd.  Plain f32 arithmetic, one block per (chunk, KV head, slice of up to
+// kSliceHM row-heads) as in k_attn_partial, emitting the same records (p*V
+// sums over the V dims, then the chunk maximum and exp-sum), so the same
+// combine merges them.  Rotary pairs (i, i + rot/2) over the first rot dims;
+// window and sinks as in k_attn_partial; no per-head norms or gate (the caller
+// rejects them for this geometry).
+// ---------------------------------------------------------------------------
+constexpr int kWideKD = 192;  // q/k head dims at most
+constexpr int kWideVD = 128;  // V head dims at most
+
+// Element d of a rotated row x (pairs (i, i + rot/2), dims >= rot unchanged).
+__device__ __forceinline__ float rot_elem(const float* x, int d, int rot, int rh, const float* cs, const float* sn) {
+    if (d >= rot) return x[d];
+    if (d < rh) return x[d] * cs[d] - x[d + rh] * sn[d];
+    const int i = d - rh;
+    return x[i] * sn[i] + x[d] * cs[i];
+}
+
+__global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
+    __shared__ float qs[kSliceHM][kWideKD];
+    __shared__ float ks[kC][kWideKD + 1];
+    __shared__ float vs[kC][kWideVD];
+    __shared__ float sc[kSliceHM][kC + 1];
+    __shared__ float rc[8][kWideKD / 2], rs[8][kWideKD / 2];
+
+    const int KD = p.d, VD = p.vd;
+    const int GQ = p.nh / p.nkv;
+    const int HMall = GQ * p.m;
+    const int Z = (HMall + kSliceHM - 1) / kSliceHM;
+    int c, g, z;
+    if (!attn_block(p, Z, c, g, z)) return;
+    const int hm0 = z * kSliceHM;
+    const int HM = HMall - hm0 < kSliceHM ? HMall - hm0 : kSliceHM;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
+    const int ld = (p.nh + p.nkv) * KD + p.nkv * VD;  // qkv row stride
+    const int p0 = c * kC;
+    const int rot = p.rot, rh = rot / 2;
+
+    // the rotary table of the new rows' positions, and the chunk's cached
+    // K/V rows (rows at or past cache_len are filled below)
+    for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
+        const int mi = idx / rh, i = idx % rh;
+        const double inv_freq = exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta);
+        rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
+    }
+    for (int idx = t; idx < kC * KD; idx += blockDim.x) {
+        const int j = idx / KD, d = idx % KD, pos = p0 + j;
+        ks[j][d] = pos < p.cache_len ? p.k_cache[((int64_t)g * p.capacity + pos) * KD + d] : 0.0f;
+    }
+    for (int idx = t; idx < kC * VD; idx += blockDim.x) {
+        const int j = idx / VD, d = idx % VD, pos = p0 + j;
+        vs[j][d] = pos < p.cache_len ? p.v_cache[((int64_t)g * p.capacity + pos) * VD + d] : 0.0f;
+    }
+    __syncthreads();
+
+    // rotated queries; the new rows this chunk owns (slice 0 writes the cache)
+    for (int idx = t; idx < HM * KD; idx += blockDim.x) {
+        const int hm = idx / KD, d = idx % KD;
+        const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
+        qs[hm][d] = rot_elem(p.qkv + (int64_t)mi * ld + hq * KD, d, rot, rh, rc[mi], rs[mi]);
+    }
+    for (int idx = t; idx < p.m * KD; idx += blockDim.x) {
+        const int mi = idx / KD, d = idx % KD, pos = p.cache_len + mi;
+        if (pos >= p0 && pos < p0 + kC) {
+            const float kval = rot_elem(p.qkv + (int64_t)mi * ld + p.nh * KD + g * KD, d, rot, rh, rc[mi], rs[mi]);
+            ks[pos - p0][d] = kval;
+            if (z == 0) p.k_cache[((int64_t)g * p.capacity + pos) * KD + d] = kval;
+        }
+    }
+    for (int idx = t; idx < p.m * VD; idx += blockDim.x) {
+        const int mi = idx / VD, d = idx % VD, pos = p.cache_len + mi;
+        if (pos >= p0 && pos < p0 + kC) {
+            const float vval = p.qkv[(int64_t)mi * ld + (p.nh + p.nkv) * KD + g * VD + d];
+            vs[pos - p0][d] = vval;
+            if (z == 0) p.v_cache[((int64_t)g * p.capacity + pos) * VD + d] = vval;
+        }
+    }
+    __syncthreads();
+
+    // scores
+    const float scale = 1.0f / sqrtf((float)KD);
+    for (int idx = t; idx < HM * kC; idx += blockDim.x) {
+        const int hm = idx / kC, j = idx % kC;
+        float sv = 0.0f;
+        for (int d = 0; d < KD; ++d) sv = fmaf(qs[hm][d], ks[j][d], sv);
+        sc[hm][j] = sv * scale;
+    }
+    __syncthreads();
+
+    // chunk softmax statistics (causal, window), as in k_attn_partial
+    float* out = p.part + (((int64_t)(c - p.c0) * p.nkv + g) * HMall + hm0) * (VD + 2);
+    for (int hp = 2 * wid; hp < HM; hp += 2 * (int)(blockDim.x / kWave)) {
+        const int hm = hp + (lane >> 5), j = lane & 31;
+        const int qpos = p.cache_len + (hm0 + hm) / GQ;
+        const bool ok = hm < HM && p0 + j <= qpos && (p.window == 0 || p0 + j > qpos - p.window);
+        const float sv = ok ? sc[hm][j] : -INFINITY;
+        float mx = sv;
+        mx = half_max(mx);
+        const float e = (mx == -INFINITY) ? 0.0f : __expf(sv - mx);
+        float l = e;
+        l = half_sum(l);
+        if (hm < HM) {
+            sc[hm][j] = e;
+            if (j == 0) {
+                out[hm * (VD + 2) + VD] = mx;
+                out[hm * (VD + 2) + VD + 1] = l;
+            }
+        }
+    }
+    __syncthreads();
+
+    // unnormalised p*V
+    for (int idx = t; idx < HM * VD; idx += blockDim.x) {
+        const int hm = idx / VD, d = idx % VD;
+        float acc = 0.0f;
+        for (int j = 0; j < kC; ++j) acc = fmaf(sc[hm][j], vs[j][d], acc);
+        out[hm * (VD + 2) + d] = acc;
+    }
+}
+
+// Catch-up of the wide geometry: one wave per (row, KV head); kv rows are
+// [m][n_kv*d k values | n_kv*vd v values].
+__global__ void __launch_bounds__(64) k_append_kv_wide(const AttnParams p, const float* kv, int pos0) {
+    const int r = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+    const int KD = p.d, VD = p.vd, rot = p.rot, rh = rot / 2;
+    const float* kr = kv + (int64_t)r * p.nkv * (KD + VD) + g * KD;
+    const float* vr = kv + (int64_t)r * p.nkv * (KD + VD) + p.nkv * KD + g * VD;
+    const int pos = pos0 + r;
+    float* kd = p.k_cache + ((int64_t)g * p.capacity + pos) * KD;
+    float* vd = p.v_cache + ((int64_t)g * p.capacity + pos) * VD;
+    for (int d = lane; d < KD; d += kWave) {
+        float val = kr[d];
+        if (d < rot) {
+            const int i = d < rh ? d : d - rh;
+            float cs, sn;
+            rotary((double)pos, exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta), cs, sn);
+            val = d < rh ? kr[d] * cs - kr[d + rh] * sn : kr[i] * sn + kr[d] * cs;
+        }
+        kd[d] = val;
+    }
+    for (int d = lane; d < VD; d += kWave) vd[d] = vr[d];
+}
+
 hipError_t launch_shift_rows(const float* pending, const float* target, float* out, int m, int H, hipStream_t st) {
     const int64_t n = (int64_t)m * H;
     hipLaunchKernelGGL(k_shift_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pending, target, out, m, H);
@@ -449,6 +595,11 @@ hipError_t launch_shift_rows(const float* pending, const float* target, float* o
 
 hipError_t launch_append_kv(const AttnParams& p, const float* kv, int m, int pos0, hipStream_t st) {
     const dim3 grid((unsigned)m, (unsigned)p.nkv), block(kWave);
+    if (p.d != kD || p.vd != kD) {
+        if (p.d > kWideKD || p.vd > kWideVD || p.rot > p.d || p.gk) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_append_kv_wide, grid, block, 0, st, p, kv, pos0);
+        return hipGetLastError();
+    }
     if (p.gk || p.rot != kD)
         hipLaunchKernelGGL(k_append_kv<true>, grid, block, 0, st, p, kv, pos0);
     else
@@ -461,7 +612,12 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int Z = (hm + kSliceHM - 1) / kSliceHM;
     const int pairs = (p.chunks - p.c0) * p.nkv;
     const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
-    if (p.gq || p.rot != kD)
+    if (p.d != kD || p.vd != kD) {
+        // the combine below reads records of kD + 2 floats: V heads of kD
+        if (p.d > kWideKD || p.vd != kD || p.rot > p.d || p.gq || p.qg != 1 || p.m > 8)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_attn_partial_wide, grid, block, 0, st, p);
+    } else if (p.gq || p.rot != kD)
         hipLaunchKernelGGL(k_attn_partial<true>, grid, block, 0, st, p);
     else
         hipLaunchKernelGGL(k_attn_partial<false>, grid, block, 0, st, p);

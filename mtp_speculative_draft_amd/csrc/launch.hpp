@@ -131,6 +131,7 @@ struct AttnParams {
     float* k_cache;
     float* v_cache;
     int cache_len, capacity, m, nh, nkv, d;
+    int vd;               // V head dims (d, or the wide geometry's narrower V heads)
     double log2_theta;  // inverse frequency i is 2^(-(2i/d) * log2_theta) = theta^(-2i/d)
     float* part;  // [chunks][nkv][group*m][d + 2]: p*V sums, chunk max, exp-sum
     float* o;     // [m][nh * d]

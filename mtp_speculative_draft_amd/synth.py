@@ -304,6 +304,6 @@ def config4_step(seed_extra: int = 0, cache_len: int = 4096, capacity: int = 410
     layer = dense_layer(g, **shape)
     e0 = normal(g, (1, layer.hidden))
     h0 = normal(g, (1, layer.hidden))
-    kc, vc = kv_cache(g, layer.n_kv_heads, cache_len, capacity, layer.head_dim)
+    kc, vc = kv_cache(g, layer.n_kv_heads, cache_len, capacity, layer.head_dim, layer.v_head_dim)
     table = normal(g, (layer.vocab, layer.hidden))
     return StepInputs(layer, e0, h0, kc, vc, cache_len, capacity, table)

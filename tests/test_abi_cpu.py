@@ -140,12 +140,14 @@ def test_layer_struct_layout_matches_the_header(tmp_path):
                    'offsetof(mtp_layer, sh_down), offsetof(mtp_layer, gamma_q_head), '
                    'offsetof(mtp_layer, q_gated), offsetof(mtp_layer, rotary_dim), '
                    'offsetof(mtp_layer, sinks), offsetof(mtp_layer, window)); return 0; }\n')
+    # (v_head_dim follows window; its offset is checked below)
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(mtp.HEADER), str(src), "-o", str(exe)])
     got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     L = mtp.MtpLayer
     assert got == [C.sizeof(L), L.sh_down.offset, L.gamma_q_head.offset, L.q_gated.offset, L.rotary_dim.offset,
                    L.sinks.offset, L.window.offset]
+    assert L.v_head_dim.offset == L.window.offset + 4 and C.sizeof(L) >= L.v_head_dim.offset + 4
 
 
 def test_attention_variant_fields_are_validated():
@@ -175,6 +177,15 @@ def test_attention_variant_fields_are_validated():
     L.sinks = FAKE + 2  # not 4-byte aligned
     assert status(L) == mtp.MTP_ERR_INVALID_ARG
     assert b"sinks" in lib.mtp_last_error()
+    L = _layer()
+    L.head_dim = 192  # V heads of 192 are not built
+    assert status(L) == mtp.MTP_ERR_UNSUPPORTED
+    L = _layer()
+    L.v_head_dim = 64
+    assert status(L) == mtp.MTP_ERR_UNSUPPORTED
+    L = _layer()
+    L.v_head_dim = -1
+    assert status(L) == mtp.MTP_ERR_INVALID_ARG
 
 
 def test_append_kv_rejects_overflow_and_empty_batches():

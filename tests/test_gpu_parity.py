@@ -363,6 +363,84 @@ def test_attn_decode_sliding_window_config4_shape(m):
     _close(_np(dk)[:, 4096:4096 + m], kc[:, 4096:4096 + m], "appended k")
 
 
+# MiMo draft geometry ([mimo.rs] "head 192 / V 128"): q/k heads of 192, V heads of 128
+_WIDE = {
+    "wide": dict(),
+    "wide_swa": dict(window=33, sinks=True),
+    "wide_rot64": dict(rotary_dim=64, window=40),
+}
+
+
+@pytest.mark.parametrize("variant,cache_len,m", [("wide", 100, 1), ("wide", 0, 3), ("wide_swa", 100, 8),
+                                                 ("wide_rot64", 64, 4), ("wide_swa", 31, 2)])
+def test_attn_decode_wide_heads_small(variant, cache_len, m):
+    _say(f"attn wide heads {variant} cache_len={cache_len} m={m}")
+    L = synth.dense_layer(synth.rng(126, cache_len, m), hidden=256, n_heads=4, n_kv_heads=2, head_dim=192,
+                          vocab=1000, ffn_inter=320, v_head_dim=128, **_WIDE[variant])
+    g = synth.rng(127, cache_len, m)
+    cap = cache_len + m + 3
+    kc, vc = synth.kv_cache(g, 2, cache_len, cap, 192, v_dim=128)
+    u = synth.normal(g, (m, 256))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(u), dk, dv, cache_len))
+    kr, vr = kc.copy(), vc.copy()
+    ref = oracle.attention(L, u, kr, vr, cache_len)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, cache_len:cache_len + m], kr[:, cache_len:cache_len + m], "appended k")
+    _close(_np(dv)[:, cache_len:cache_len + m], vr[:, cache_len:cache_len + m], "appended v")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_attn_decode_wide_heads_mimo_shape(m):
+    """16 query / 8 KV heads of 192 with V 128, window 128 and sinks, hidden
+    2048, cache 4096."""
+    _say(f"attn wide heads MiMo shape m={m}")
+    g = synth.rng(128, m)
+    L = synth.dense_layer(g, n_heads=16, n_kv_heads=8, head_dim=192, vocab=64, ffn_inter=64, v_head_dim=128,
+                          window=128, sinks=True)
+    kc, vc = synth.kv_cache(g, 8, 4096, 4104, 192, v_dim=128)
+    u = synth.normal(g, (m, 2048))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(mtp.DeviceLayer(L), _t(u), dk, dv, 4096))
+    ref = oracle.attention(L, u, kc, vc, 4096)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, 4096:4096 + m], kc[:, 4096:4096 + m], "appended k")
+    _close(_np(dv)[:, 4096:4096 + m], vc[:, 4096:4096 + m], "appended v")
+
+
+@pytest.mark.parametrize("m", [3, 11])
+def test_append_kv_wide_heads(m):
+    """Cache catch-up with K rows of 192 and V rows of 128 (11 rows: two pieces)."""
+    S = synth.config4_step(seed_extra=3100 + m, cache_len=20, capacity=20 + m + 3, hidden=256, n_heads=4,
+                           n_kv_heads=2, head_dim=192, vocab=500, ffn_inter=64, v_head_dim=128, window=16,
+                           sinks=True)
+    L = S.layer
+    g = synth.rng(129, m)
+    target = synth.normal(g, (m, L.hidden))
+    pend = synth.normal(g, (L.hidden,))
+    e = synth.normal(g, (m, L.hidden))
+    kr, vr = S.k_cache.copy(), S.v_cache.copy()
+    oracle.append_kv(L, e, None, None, pend, target, kr, vr, S.cache_len)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    mtp.mtp_append_kv(mtp.DeviceLayer(L), _t(e), None, None, _t(pend), _t(target), dk, dv, S.cache_len)
+    L0 = S.cache_len
+    _close(_np(dk)[:, L0:L0 + m], kr[:, L0:L0 + m], "k rows")
+    _close(_np(dv)[:, L0:L0 + m], vr[:, L0:L0 + m], "v rows")
+
+
+def test_draft_step_wide_heads_chain_and_verify():
+    """The whole layer with MiMo's attention geometry (192 / 128, window 64, sinks)."""
+    for extra in range(1, 30):
+        S = synth.config4_step(seed_extra=1700 + extra, cache_len=100, capacity=110, hidden=256, n_heads=4,
+                               n_kv_heads=2, head_dim=192, vocab=1000, ffn_inter=320, v_head_dim=128, window=64,
+                               sinks=True)
+        ref = _chain_and_verify_oracle(S)
+        margins = [planting.head_margin(o[2]) for o in ref[0]] + [planting.head_margin(r) for r in ref[1][2]]
+        if min(margins) >= 1e-2:
+            break
+    _check_step(S, f"wide seed {extra}", ref)
+
+
 def test_attn_decode_rejects_overflow_without_writing():
     L = _small_layer(2)
     g = synth.rng(110)
