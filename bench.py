@@ -281,8 +281,9 @@ def event_us(torch, dev, fn, n, warm):
 
 def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
     """Attention block (cache 4096, 16 q / 2 kv heads x 128; plain, with gated
-    q, per-head q/k norms and rotary over 64 of 128 dims, and with a 128-row
-    sliding window and per-head sinks) at m = 1 and 4, the
+    q, per-head q/k norms and rotary over 64 of 128 dims, with a 128-row
+    sliding window and per-head sinks, and in MiMo's geometry: 16 query / 8 KV
+    heads of 192 with V heads of 128, window 128, sinks) at m = 1 and 4, the
     cache catch-up of a 4-row target batch, and the three-layer draft stack
     (each layer catches up 4 rows, then drafts row t).  The attention and
     catch-up loops rotate over 24 layer/cache copies (about 18 MB read each) so that
@@ -296,10 +297,15 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
         return sum(dl.q4[k].nbytes for k in names)
 
     for name, kw in (("attn", {}), ("attn_variant", {"q_gated": True, "qk_norm": True, "rotary_dim": 64}),
-                     ("attn_window128_sinks", {"window": 128, "sinks": True})):
+                     ("attn_window128_sinks", {"window": 128, "sinks": True}),
+                     ("attn_mimo_16x8_192v128_window128_sinks",
+                      {"n_heads": 16, "n_kv_heads": 8, "head_dim": 192, "v_head_dim": 128, "window": 128,
+                       "sinks": True})):
         g = synth.rng(40)
         Lh = synth.dense_layer(g, vocab=64, **kw)
-        kc, vc = synth.kv_cache(g, NKV, L0, CAP, D)
+        nkv, kd, vd = Lh.n_kv_heads, Lh.head_dim, Lh.v_head_dim or Lh.head_dim
+        kc, vc = synth.kv_cache(g, nkv, L0, CAP, kd, v_dim=vd)
+        row = nkv * (kd + vd) * 4  # K and V bytes of one position
         reps = [(mtp.DeviceLayer(Lh, dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev))
                 for _ in range(24)]
         wb = q4_bytes(reps[0][0], ("wq", "wk", "wv", "wo"))
@@ -314,7 +320,7 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
 
             us = event_us(torch, dev, call, n, W)
             seen = L0 + m if not kw.get("window") else min(L0 + m, kw["window"] + m - 1)  # K/V rows read
-            b = wb + kvrow * seen + kvrow * m + m * H * 4 * 2
+            b = wb + row * seen + row * m + m * H * 4 * 2
             out[f"{name}_cache4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
         if name == "attn":
             # cache catch-up: shifted target hidden -> eh_proj -> K/V rows of 4 positions

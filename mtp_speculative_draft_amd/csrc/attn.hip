@@ -454,18 +454,10 @@ __global__ void __launch_bounds__(64) k_append_kv(const AttnParams p, const floa
 constexpr int kWideKD = 192;  // q/k head dims at most
 constexpr int kWideVD = 128;  // V head dims at most
 
-// Element d of a rotated row x (pairs (i, i + rot/2), dims >= rot unchanged).
-__device__ __forceinline__ float rot_elem(const float* x, int d, int rot, int rh, const float* cs, const float* sn) {
-    if (d >= rot) return x[d];
-    if (d < rh) return x[d] * cs[d] - x[d + rh] * sn[d];
-    const int i = d - rh;
-    return x[i] * sn[i] + x[d] * cs[i];
-}
-
 __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
-    __shared__ float qs[kSliceHM][kWideKD];
-    __shared__ float ks[kC][kWideKD + 1];
-    __shared__ float vs[kC][kWideVD];
+    __shared__ __align__(16) float qs[kSliceHM][kWideKD];
+    __shared__ float ks[kC][kWideKD + 1];  // odd row stride: the score loop reads a column per lane
+    __shared__ __align__(16) float vs[kC][kWideVD];
     __shared__ float sc[kSliceHM][kC + 1];
     __shared__ float rc[8][kWideKD / 2], rs[8][kWideKD / 2];
 
@@ -482,36 +474,71 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
     const int p0 = c * kC;
     const int rot = p.rot, rh = rot / 2;
 
-    // the rotary table of the new rows' positions, and the chunk's cached
-    // K/V rows (rows at or past cache_len are filled below)
+    // 1. every global read of the block is requested up front (the chunk's
+    //    cached K/V rows and the raw query rows, as float4), so the block
+    //    waits for memory once; rows at or past cache_len are filled below
+    constexpr int kKQ = kC * kWideKD / 4 / 256;  // float4 of K per thread at most
+    constexpr int kVQ = kC * kWideVD / 4 / 256;
+    constexpr int kQQ = kSliceHM * kWideKD / 4 / 256;
+    const int KD4 = KD / 4, VD4 = VD / 4;
+    const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 kq[kKQ], vq[kVQ], qq[kQQ];
+#pragma unroll
+    for (int u = 0; u < kKQ; ++u) {
+        const int idx = t + 256 * u, j = idx / KD4, w = idx % KD4, pos = p0 + j;
+        kq[u] = zero4;
+        if (idx < kC * KD4 && pos < p.cache_len)
+            kq[u] = reinterpret_cast<const float4*>(p.k_cache + ((int64_t)g * p.capacity + pos) * KD)[w];
+    }
+#pragma unroll
+    for (int u = 0; u < kVQ; ++u) {
+        const int idx = t + 256 * u, j = idx / VD4, w = idx % VD4, pos = p0 + j;
+        vq[u] = zero4;
+        if (idx < kC * VD4 && pos < p.cache_len)
+            vq[u] = reinterpret_cast<const float4*>(p.v_cache + ((int64_t)g * p.capacity + pos) * VD)[w];
+    }
+#pragma unroll
+    for (int u = 0; u < kQQ; ++u) {
+        const int idx = t + 256 * u, hm = idx / KD4, w = idx % KD4;
+        qq[u] = zero4;
+        if (hm < HM) {
+            const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
+            qq[u] = reinterpret_cast<const float4*>(p.qkv + (int64_t)mi * ld + hq * KD)[w];
+        }
+    }
+    // ... the rotary table of the new rows' positions meanwhile
     for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
         const int mi = idx / rh, i = idx % rh;
         const double inv_freq = exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta);
         rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
     }
-    for (int idx = t; idx < kC * KD; idx += blockDim.x) {
-        const int j = idx / KD, d = idx % KD, pos = p0 + j;
-        ks[j][d] = pos < p.cache_len ? p.k_cache[((int64_t)g * p.capacity + pos) * KD + d] : 0.0f;
+    // 2. raw rows into LDS (the new rows this chunk owns from the projection
+    //    output), then the rotation of q and the new k rows in place, pair by
+    //    pair; slice 0 writes the new rows to the cache
+#pragma unroll
+    for (int u = 0; u < kKQ; ++u) {
+        const int idx = t + 256 * u, j = idx / KD4, w = idx % KD4;
+        if (idx < kC * KD4) {
+            ks[j][4 * w] = kq[u].x;
+            ks[j][4 * w + 1] = kq[u].y;
+            ks[j][4 * w + 2] = kq[u].z;
+            ks[j][4 * w + 3] = kq[u].w;
+        }
     }
-    for (int idx = t; idx < kC * VD; idx += blockDim.x) {
-        const int j = idx / VD, d = idx % VD, pos = p0 + j;
-        vs[j][d] = pos < p.cache_len ? p.v_cache[((int64_t)g * p.capacity + pos) * VD + d] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kVQ; ++u) {
+        const int idx = t + 256 * u, j = idx / VD4, w = idx % VD4;
+        if (idx < kC * VD4) *reinterpret_cast<float4*>(&vs[j][4 * w]) = vq[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kQQ; ++u) {
+        const int idx = t + 256 * u, hm = idx / KD4, w = idx % KD4;
+        if (hm < HM) *reinterpret_cast<float4*>(&qs[hm][4 * w]) = qq[u];
     }
     __syncthreads();
-
-    // rotated queries; the new rows this chunk owns (slice 0 writes the cache)
-    for (int idx = t; idx < HM * KD; idx += blockDim.x) {
-        const int hm = idx / KD, d = idx % KD;
-        const int mi = (hm0 + hm) / GQ, hq = g * GQ + (hm0 + hm) % GQ;
-        qs[hm][d] = rot_elem(p.qkv + (int64_t)mi * ld + hq * KD, d, rot, rh, rc[mi], rs[mi]);
-    }
     for (int idx = t; idx < p.m * KD; idx += blockDim.x) {
         const int mi = idx / KD, d = idx % KD, pos = p.cache_len + mi;
-        if (pos >= p0 && pos < p0 + kC) {
-            const float kval = rot_elem(p.qkv + (int64_t)mi * ld + p.nh * KD + g * KD, d, rot, rh, rc[mi], rs[mi]);
-            ks[pos - p0][d] = kval;
-            if (z == 0) p.k_cache[((int64_t)g * p.capacity + pos) * KD + d] = kval;
-        }
+        if (pos >= p0 && pos < p0 + kC) ks[pos - p0][d] = p.qkv[(int64_t)mi * ld + p.nh * KD + g * KD + d];
     }
     for (int idx = t; idx < p.m * VD; idx += blockDim.x) {
         const int mi = idx / VD, d = idx % VD, pos = p.cache_len + mi;
@@ -522,6 +549,25 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
         }
     }
     __syncthreads();
+    auto rotate_pair = [&](float* x, int i, int mi) {  // dims i and i + rh, i < rh
+        const float a = x[i], b = x[i + rh], cs = rc[mi][i], sn = rs[mi][i];
+        x[i] = a * cs - b * sn;
+        x[i + rh] = a * sn + b * cs;
+    };
+    for (int idx = t; idx < HM * rh; idx += blockDim.x) {
+        const int hm = idx / rh, i = idx % rh;
+        rotate_pair(qs[hm], i, (hm0 + hm) / GQ);
+    }
+    for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
+        const int mi = idx / rh, i = idx % rh, pos = p.cache_len + mi;
+        if (pos >= p0 && pos < p0 + kC) rotate_pair(ks[pos - p0], i, mi);
+    }
+    __syncthreads();
+    if (z == 0)
+        for (int idx = t; idx < p.m * KD; idx += blockDim.x) {
+            const int mi = idx / KD, d = idx % KD, pos = p.cache_len + mi;
+            if (pos >= p0 && pos < p0 + kC) p.k_cache[((int64_t)g * p.capacity + pos) * KD + d] = ks[pos - p0][d];
+        }
 
     // scores
     const float scale = 1.0f / sqrtf((float)KD);
