@@ -920,19 +920,29 @@ def test_lmhead_argmax_q8_ties_keep_lowest_row(m):
 # --------------------------------------------------------------------------
 # multi-layer draft stack ([mimo.rs] "How the three layers chain")
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("t,starts", [(9, (6, 5, 7)), (30, (10, 29, 30))])
-def test_stack_draft_three_layers(t, starts):
-    _say(f"stack draft t={t} starts={starts}")
+@pytest.mark.parametrize("t,starts,mimo", [(9, (6, 5, 7), False), (30, (10, 29, 30), False),
+                                           (30, (25, 27, 30), True)])
+def test_stack_draft_three_layers(t, starts, mimo):
+    """Three layers (the second with the gated, head-normed attention), or three
+    layers of MiMo's geometry (heads of 192 with V 128, window 8, sinks)."""
+    _say(f"stack draft t={t} starts={starts} mimo={mimo}")
     H, V = 256, 1000
+    D = 192 if mimo else 128
+
+    def attn_kw(k):
+        if mimo:
+            return {"head_dim": 192, "v_head_dim": 128, "window": 8, "sinks": True}
+        return {"head_dim": 128, **({"q_gated": True, "qk_norm": True} if k == 1 else {})}
+
     for extra in range(30):
         g = synth.rng(120, t, extra)
-        layers = [synth.dense_layer(synth.rng(121, k, extra), hidden=H, n_heads=4, n_kv_heads=2, head_dim=128,
-                                    vocab=V, ffn_inter=320, **({"q_gated": True, "qk_norm": True} if k == 1 else {}))
+        layers = [synth.dense_layer(synth.rng(121, k, extra), hidden=H, n_heads=4, n_kv_heads=2, vocab=V,
+                                    ffn_inter=320, **attn_kw(k))
                   for k in range(3)]
         table = synth.normal(g, (V, H))
         hist = synth.normal(g, (t + 1, H))
         x = g.integers(0, V, size=t + 2).astype(np.int32)
-        base = [synth.kv_cache(synth.rng(122, k, extra), 2, starts[k], t + 4, 128) for k in range(3)]
+        base = [synth.kv_cache(synth.rng(122, k, extra), 2, starts[k], t + 4, D, v_dim=128) for k in range(3)]
         caches = [(kc.copy(), vc.copy()) for kc, vc in base]
         drafts = oracle.stack_draft(layers, caches, starts, x, table, hist, t)
         # margin gate: each layer's row-t logits from a full step on a copy of its cache
