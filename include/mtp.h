@@ -80,7 +80,8 @@ typedef struct {
 /* One MTP draft layer ([mimo.rs] module doc "The draft forward"; [mtp.rs]
  * `MtpWeights`, `MtpFullAttnWeightsGpu`, `MtpFfnWeightsGpu`).
  * Shapes: eh_proj [hidden][2*hidden]; wq [n_heads*head_dim][hidden];
- * wk, wv [n_kv_heads*head_dim][hidden]; wo [hidden][n_heads*head_dim];
+ * wk [n_kv_heads*head_dim][hidden], wv [n_kv_heads*dv][hidden]; wo [hidden][n_heads*dv]
+ * (dv = v_head_dim, or head_dim when it is 0);
  * dense FFN: gate, up [ffn_inter][hidden], down [hidden][ffn_inter];
  * MoE FFN: router f32 [n_experts][hidden], gate_exps/up_exps
  * [n_experts][inter][hidden], down_exps [n_experts][hidden][inter], optional
@@ -184,8 +185,9 @@ mtp_status mtp_norm_concat_proj(const float* e, const float* h, const float* gam
  *   rows cache_len .. cache_len+m-1; causal GQA attention (query head h reads
  *   KV head h / (n_heads/n_kv_heads), scale 1/sqrt(head_dim)) over rows
  *   0 .. cache_len + r; out = u + Wo * attn.
- * k_cache, v_cache f32 [n_kv_heads][capacity][head_dim].  Requires
- * cache_len + m <= capacity and head_dim == 128. Uses only L's attention
+ * k_cache f32 [n_kv_heads][capacity][head_dim], v_cache f32
+ * [n_kv_heads][capacity][dv].  Requires cache_len + m <= capacity, and head_dim
+ * 128 (dv 128) or 192 (dv 128). Uses only L's attention
  * fields. out [m][hidden] must not alias u. */
 mtp_status mtp_attn_decode(const mtp_layer* L, const float* u, float* k_cache, float* v_cache,
                            int32_t cache_len, int32_t capacity, int32_t m, float* out, void* ws,
