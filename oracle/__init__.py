@@ -57,6 +57,12 @@ class _Layer(C.Structure):
                 ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32)]
 
 
+class _MoeFfn(C.Structure):
+    _fields_ = [("router", C.c_void_p), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("gate_exps", C.c_void_p), ("up_exps", C.c_void_p), ("down_exps", C.c_void_p),
+                ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -84,6 +90,7 @@ def lib():
             "orc_head": (None, [P, P, C.c_float, P, I, P, P, P]),
             "orc_head8": (None, [P, P, C.c_float, P, I, P, P, P]),
             "orc_draft_step": (I, [P, P, P, P, P, P, P, I, I, I, P, P, P]),
+            "orc_draft_step_moe": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P]),
             "orc_append_kv": (None, [P, P, P, P, P, P, P, P, I, I, I]),
         }
         for name, (res, args) in sig.items():
@@ -328,8 +335,20 @@ def head8(hidden, gamma, eps, lm):
     return normed, logits, ids
 
 
-def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_logits: bool = True):
-    """One draft-layer forward over m rows; appends K/V rows in place.
+def _moe_ffn(inp, keep: _Keep) -> _MoeFfn:
+    router = keep.arr(inp.router, np.float32)
+    ge, ue, de = _q8_list(inp.gate_exps, keep), _q8_list(inp.up_exps, keep), _q8_list(inp.down_exps, keep)
+    addr = C.addressof
+    sh = [None, None, None]
+    if inp.sh_gate is not None:
+        sh = [addr(_q8_list(w, keep)) for w in (inp.sh_gate, inp.sh_up, inp.sh_down)]
+    return _MoeFfn(router.ctypes.data, int(inp.n_experts), int(inp.top_k), addr(ge), addr(ue), addr(de), *sh)
+
+
+def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_logits: bool = True, moe=None):
+    """One draft-layer forward over m rows; appends K/V rows in place.  With
+    moe (a MoE input set of ``synth.moe_inputs``) the FFN is the routed 8-bit
+    mixture of those weights instead of the layer's dense SwiGLU.
 
     Returns (ids [m], hidden_out [m, H] (post-final-norm), logits [m, V] or None)."""
     assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
@@ -345,8 +364,13 @@ def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_lo
     ids = np.empty(m, dtype=np.int32)
     hid = np.empty((m, L.hidden), dtype=np.float32)
     logits = np.empty((m, L.vocab), dtype=np.float32) if want_logits else None
-    rc = lib().orc_draft_step(C.byref(d), _p(e), _p(tok), _p(tab), _p(h), _p(k_cache), _p(v_cache),
-                              cache_len, k_cache.shape[1], m, _p(ids), _p(hid), _p(logits))
+    if moe is None:
+        rc = lib().orc_draft_step(C.byref(d), _p(e), _p(tok), _p(tab), _p(h), _p(k_cache), _p(v_cache),
+                                  cache_len, k_cache.shape[1], m, _p(ids), _p(hid), _p(logits))
+    else:
+        mf = _moe_ffn(moe, keep)
+        rc = lib().orc_draft_step_moe(C.byref(d), C.byref(mf), _p(e), _p(tok), _p(tab), _p(h), _p(k_cache),
+                                      _p(v_cache), cache_len, k_cache.shape[1], m, _p(ids), _p(hid), _p(logits))
     if rc != 0:
         raise ValueError("orc_draft_step rejected its arguments")
     return ids, hid, logits

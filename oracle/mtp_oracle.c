@@ -513,22 +513,37 @@ void orc_head8(const float* hidden, const float* gamma, float eps, const orc_q8*
     if (!logits_out) free(lg);
 }
 
+/* The layer's two FFN forms behind one wiring: the dense 4-bit SwiGLU of the
+ * layer, or the routed 8-bit mixture when moe is given. */
+static int32_t ffn_residual(const orc_layer* L, const orc_moe_ffn* moe, const float* f, const float* r1, int32_t m,
+                            float* r2) {
+    if (!moe) {
+        orc_ffn_dense(f, &L->gate, &L->up, &L->down, r1, m, r2);
+        return 0;
+    }
+    return orc_moe(f, moe->router, moe->n_experts, moe->top_k, moe->gate_exps, moe->up_exps, moe->down_exps,
+                   moe->sh_gate, moe->sh_up, moe->sh_down, r1, m, r2, NULL, NULL, NULL);
+}
+
 /* One draft-layer forward over m rows at positions cache_len .. cache_len+m-1
  * ([mimo.rs] module doc "The draft forward" and `mimo_mtp_block_with_probe`;
- * [mtp.rs] `forward_draft_body` then `forward_shared_head_greedy`):
+ * [mtp.rs] `forward_draft_body`, whose FFN step `forward_ffn_residual` adds
+ * the FFN output to its own input's residual, then `forward_shared_head_greedy`):
  *   u  = eh_proj [rms(e); rms(h)]
  *   r1 = u + attention(rms(u))            (appends K/V rows)
- *   r2 = r1 + ffn(rms(r1))
+ *   r2 = r1 + ffn(rms(r1; gamma_post))    (dense SwiGLU, or the MoE of
+ *                                          `MtpFfnWeightsGpu::Moe`)
  *   yn = rms(r2; gamma_final), logits = LM yn, id = argmax.
  * Row r's embedding is embed_table[tokens[r]] when tokens is given and
  * tokens[r] >= 0, else e[r].  hidden_out receives yn.  Returns 0, or -1 on a
  * bad argument (nothing is written then). */
-int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens,
-                       const float* embed_table, const float* h, float* k_cache, float* v_cache,
-                       int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
-                       float* hidden_out, float* logits_out) {
+static int32_t draft_step(const orc_layer* L, const orc_moe_ffn* moe, const float* e, const int32_t* tokens,
+                          const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                          int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,
+                          float* logits_out) {
     const int32_t H = L->hidden;
     if (m < 1 || cache_len < 0 || cache_len + m > capacity) return -1;
+    if (moe && (moe->top_k < 1 || moe->top_k > moe->n_experts || moe->gate_exps[0].k != H)) return -1;
     for (int32_t r = 0; r < m; ++r) {
         int use_table = tokens && tokens[r] >= 0;
         if (use_table && (!embed_table || tokens[r] >= L->vocab)) return -1;
@@ -546,7 +561,7 @@ int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens
     orc_norm_concat_proj(ee, h, L->gamma_e, L->gamma_h, L->eps, &L->eh_proj, m, u);
     orc_attention(L, u, k_cache, v_cache, cache_len, capacity, m, r1);
     orc_rmsnorm(r1, L->gamma_post, m, H, L->eps, f);
-    orc_ffn_dense(f, &L->gate, &L->up, &L->down, r1, m, r2);
+    ffn_residual(L, moe, f, r1, m, r2);
     orc_head(r2, L->gamma_final, L->eps, &L->lm_head, m, hidden_out, logits_out, ids_out);
     free(ee);
     free(u);
@@ -554,4 +569,21 @@ int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens
     free(f);
     free(r2);
     return 0;
+}
+
+int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens,
+                       const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                       int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
+                       float* hidden_out, float* logits_out) {
+    return draft_step(L, NULL, e, tokens, embed_table, h, k_cache, v_cache, cache_len, capacity, m, ids_out,
+                      hidden_out, logits_out);
+}
+
+int32_t orc_draft_step_moe(const orc_layer* L, const orc_moe_ffn* moe, const float* e, const int32_t* tokens,
+                           const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                           int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,
+                           float* logits_out) {
+    if (!moe) return -1;
+    return draft_step(L, moe, e, tokens, embed_table, h, k_cache, v_cache, cache_len, capacity, m, ids_out,
+                      hidden_out, logits_out);
 }

@@ -85,6 +85,17 @@ typedef struct {
     int32_t v_head_dim;
 } orc_layer;
 
+/* The routed 8-bit FFN of the MoE draft layer ([mtp.rs]
+ * `MtpFfnWeightsGpu::Moe`): f32 router [n_experts][hidden], per-expert 8-bit
+ * gate/up [inter][hidden] and down [hidden][inter] (arrays of n_experts
+ * matrices), and an optional shared expert (sh_gate NULL: none). */
+typedef struct {
+    const float* router;
+    int32_t n_experts, top_k;
+    const orc_q8 *gate_exps, *up_exps, *down_exps;
+    const orc_q8 *sh_gate, *sh_up, *sh_down;
+} orc_moe_ffn;
+
 /* ---- weight formats ---- */
 void orc_unpack4(const uint32_t* codes, int32_t n, int32_t k, uint8_t* out);
 void orc_deq4(const orc_q4* w, float* out);
@@ -132,6 +143,12 @@ int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens
                        const float* embed_table, const float* h, float* k_cache, float* v_cache,
                        int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
                        float* hidden_out, float* logits_out);
+/* The same forward with the routed 8-bit FFN in place of the dense one (the
+ * layer's gate/up/down are not read). */
+int32_t orc_draft_step_moe(const orc_layer* L, const orc_moe_ffn* moe, const float* e, const int32_t* tokens,
+                           const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                           int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,
+                           float* logits_out);
 
 #ifdef __cplusplus
 }

@@ -665,13 +665,12 @@ def test_draft_step_config4():
 # MoE draft layer end to end (the FFN is the routed 8-bit mixture)
 # --------------------------------------------------------------------------
 def _oracle_moe_step(L, moe_inp, e_rows, h, kc, vc, cache_len):
-    """The draft forward composed from the oracle's own steps with the MoE FFN
-    (returns ids, post-final-norm rows, logits, router logits of rms(r1))."""
+    """The oracle's MoE draft forward (ids, post-final-norm rows, logits) and,
+    for the routing-margin gate only, the router logits of rms(r1)."""
     u = oracle.norm_concat_proj(e_rows, h, L.gamma_e, L.gamma_h, L.eps, L.eh_proj)
-    r1 = oracle.attention(L, u, kc, vc, cache_len)
-    f = oracle.rmsnorm(r1, L.gamma_post, L.eps)
-    r2, _, _, rl = oracle.moe(moe_inp, x=f, residual=r1)
-    normed, logits, ids = oracle.head(r2, L.gamma_final, L.eps, L.lm_head)
+    r1 = oracle.attention(L, u, kc.copy(), vc.copy(), cache_len)
+    rl = oracle.gemv_f32(moe_inp.router, oracle.rmsnorm(r1, L.gamma_post, L.eps))
+    ids, normed, logits = oracle.draft_step(L, e_rows, None, None, h, kc, vc, cache_len, moe=moe_inp)
     return ids, normed, logits, rl
 
 

@@ -835,3 +835,176 @@ def test_stack_draft_equals_each_layer_run_over_all_its_rows():
         assert int(ids[-1]) == drafts[k]
         toks.append(int(ids[-1]))
         assert np.array_equal(kc, caches[k][0]) and np.array_equal(vc, caches[k][1])
+
+
+# --------------------------------------------------------------------------
+# FFN bodies and the layer's wiring, against closed forms written in numpy
+# (f64, exact dequantized values) with no oracle call in the expected side
+# --------------------------------------------------------------------------
+def _exact_q4(w) -> np.ndarray:
+    """Exact 4-bit values s*q + b in f64, from the raw codes (low nibble = lowest k)."""
+    c = np.asarray(w.codes, np.uint64)
+    q = np.stack([(c >> np.uint64(4 * i)) & np.uint64(15) for i in range(8)], axis=-1).reshape(c.shape[0], -1)
+    return q.astype(np.float64) * np.repeat(w.scales.astype(np.float64), 32, 1) + np.repeat(
+        w.biases.astype(np.float64), 32, 1)
+
+
+def _exact_q8(w, e: int) -> np.ndarray:
+    """Exact 8-bit values s*q in f64 of expert e of a stack."""
+    return w.codes[e].astype(np.float64) * np.repeat(w.scales[e].astype(np.float64), 32, 1)
+
+
+def _rms64(x, gam, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * np.asarray(gam, np.float64)
+
+
+def _silu64(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def _swiglu64(wg, wu, wd, x):
+    return (_silu64(x @ wg.T) * (x @ wu.T)) @ wd.T
+
+
+def _moe64(inp, x):
+    """Routed mixture in f64: softmax over all experts, top-k by p (index on
+    ties), gates renormalised over the selection, plus the shared expert."""
+    x = np.atleast_2d(np.asarray(x, np.float64))
+    logits = x @ inp.router.astype(np.float64).T
+    out = np.zeros((x.shape[0], inp.gate_exps.k))
+    for r in range(x.shape[0]):
+        p = np.exp(logits[r] - logits[r].max())
+        p /= p.sum()
+        sel = sorted(range(p.size), key=lambda e: (-p[e], e))[: inp.top_k]
+        g = p[sel] / p[sel].sum()
+        for ge, e in zip(g, sel):
+            out[r] += ge * _swiglu64(_exact_q8(inp.gate_exps, e), _exact_q8(inp.up_exps, e),
+                                     _exact_q8(inp.down_exps, e), x[r])
+        if inp.sh_gate is not None:
+            out[r] += _swiglu64(_exact_q8(inp.sh_gate, 0), _exact_q8(inp.sh_up, 0), _exact_q8(inp.sh_down, 0), x[r])
+    return out
+
+
+def test_moe_expert_body_one_hot_closed_form():
+    """One expert, top-1, no shared expert: with x = e_j the expert's gate and
+    up rows are single weights, so y = Wd (silu(Wg[:, j]) * Wu[:, j])."""
+    inp = _moe_small(34, E=1, k=1, shared=0, m=2)
+    js = [5, 50]
+    x = np.zeros((2, 64), np.float32)
+    x[0, js[0]] = 1.0
+    x[1, js[1]] = 1.0
+    y, ids, gates, _ = oracle.moe(inp, x=x)
+    assert (ids == 0).all() and (gates == 1.0).all()
+    wg, wu, wd = _exact_q8(inp.gate_exps, 0), _exact_q8(inp.up_exps, 0), _exact_q8(inp.down_exps, 0)
+    for r, j in enumerate(js):
+        a = wg[:, j].astype(np.float32).astype(np.float64)  # f32 activations between the steps
+        b = wu[:, j].astype(np.float32).astype(np.float64)
+        z = (_silu64(a) * b).astype(np.float32).astype(np.float64)
+        want = wd @ z
+        assert np.allclose(y[r], want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
+
+
+def test_moe_top2_with_shared_matches_the_f64_mixture():
+    """E = 3 experts, top-2 with renormalised gates, plus the shared expert,
+    on random rows: every term written out in numpy."""
+    inp = _moe_small(35, E=3, k=2, m=3)
+    y, ids, gates, _ = oracle.moe(inp)
+    want = _moe64(inp, inp.x)
+    scale = np.abs(want).max()
+    assert np.allclose(y, want, rtol=0, atol=2e-6 * scale)
+
+
+def _zeroed(w):
+    return synth.Q4(w.codes, np.zeros_like(w.scales), np.zeros_like(w.biases))
+
+
+def _zeroed8(w):
+    return synth.Q8(w.codes, np.zeros_like(w.scales))
+
+
+def _wiring_case(seed=57):
+    L = _small_layer(seed)
+    g = np.random.default_rng(seed + 100)
+    cap, L0 = 20, 12
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, L0, cap, L.head_dim)
+    e, h = synth.normal(g, (2, L.hidden)), synth.normal(g, (2, L.hidden))
+    u = oracle.norm_concat_proj(e, h, L.gamma_e, L.gamma_h, L.eps, L.eh_proj)
+    return L, kc, vc, L0, e, h, u
+
+
+def test_draft_step_wiring_dense():
+    """The layer's wiring after the attention ([mtp.rs] `forward_ffn_residual`:
+    FFN input rms(r1; gamma_post), FFN residual r1; head input r2 with
+    gamma_final):
+      wo = 0 and gate = 0      -> hidden_out == rms(u; gamma_final) bitwise
+      gate = 0                 -> hidden_out == rms(r1; gamma_final) bitwise
+      wo = 0                   -> hidden_out ~ rms(u + ffn(rms(u; gamma_post)); gamma_final) in f64."""
+    L, kc, vc, L0, e, h, u = _wiring_case()
+    both = dataclasses.replace(L, wo=_zeroed(L.wo), gate=_zeroed(L.gate))
+    _, hid, _ = oracle.draft_step(both, e, None, None, h, kc.copy(), vc.copy(), L0)
+    assert np.array_equal(hid, oracle.rmsnorm(u, L.gamma_final, L.eps))
+
+    no_ffn = dataclasses.replace(L, gate=_zeroed(L.gate))
+    _, hid, _ = oracle.draft_step(no_ffn, e, None, None, h, kc.copy(), vc.copy(), L0)
+    r1 = oracle.attention(L, u, kc.copy(), vc.copy(), L0)
+    assert not np.array_equal(r1, u)
+    assert np.array_equal(hid, oracle.rmsnorm(r1, L.gamma_final, L.eps))
+
+    no_attn = dataclasses.replace(L, wo=_zeroed(L.wo))
+    _, hid, _ = oracle.draft_step(no_attn, e, None, None, h, kc.copy(), vc.copy(), L0)
+    u64 = u.astype(np.float64)
+    f = _rms64(u64, L.gamma_post, L.eps)
+    r2 = u64 + _swiglu64(_exact_q4(L.gate), _exact_q4(L.up), _exact_q4(L.down), f)
+    want = _rms64(r2, L.gamma_final, L.eps)
+    assert np.allclose(hid, want, rtol=0, atol=2e-5 * np.abs(want).max())
+
+
+def test_draft_step_wiring_moe():
+    """The same wiring with the routed 8-bit FFN (experts zeroed through
+    their gate matrices, the shared expert's included)."""
+    L, kc, vc, L0, e, h, u = _wiring_case(58)
+    inp = synth.moe_inputs(np.random.default_rng(59), 2, hidden=L.hidden, n_experts=6, inter=32, top_k=2,
+                           shared_inter=32)
+    quiet = dataclasses.replace(inp, gate_exps=_zeroed8(inp.gate_exps), sh_gate=_zeroed8(inp.sh_gate))
+    L_wo0 = dataclasses.replace(L, wo=_zeroed(L.wo))
+    _, hid, _ = oracle.draft_step(L_wo0, e, None, None, h, kc.copy(), vc.copy(), L0, moe=quiet)
+    assert np.array_equal(hid, oracle.rmsnorm(u, L.gamma_final, L.eps))
+
+    _, hid, _ = oracle.draft_step(L, e, None, None, h, kc.copy(), vc.copy(), L0, moe=quiet)
+    r1 = oracle.attention(L, u, kc.copy(), vc.copy(), L0)
+    assert np.array_equal(hid, oracle.rmsnorm(r1, L.gamma_final, L.eps))
+
+    _, hid, _ = oracle.draft_step(L_wo0, e, None, None, h, kc.copy(), vc.copy(), L0, moe=inp)
+    u64 = u.astype(np.float64)
+    r2 = u64 + _moe64(inp, _rms64(u64, L.gamma_post, L.eps))
+    want = _rms64(r2, L.gamma_final, L.eps)
+    assert np.allclose(hid, want, rtol=0, atol=2e-5 * np.abs(want).max())
+    # the dense FFN weights of the layer are not read on the MoE path
+    dense_off = dataclasses.replace(L_wo0, gate=_zeroed(L.gate), up=_zeroed(L.up), down=_zeroed(L.down))
+    _, hid2, _ = oracle.draft_step(dense_off, e, None, None, h, kc.copy(), vc.copy(), L0, moe=inp)
+    assert np.array_equal(hid, hid2)
+
+
+def test_draft_step_moe_batched_verify_equals_the_sequential_chain():
+    L = _small_layer(60)
+    inp = synth.moe_inputs(np.random.default_rng(61), 1, hidden=L.hidden, n_experts=8, inter=32, top_k=2,
+                           shared_inter=32)
+    g = np.random.default_rng(62)
+    cap, L0 = 40, 30
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, L0, cap, L.head_dim)
+    table = synth.normal(g, (L.vocab, L.hidden))
+    e0, h0 = synth.normal(g, (1, L.hidden)), synth.normal(g, (1, L.hidden))
+    k1, v1 = kc.copy(), vc.copy()
+    toks, hs, chain = [-1], [h0[0]], []
+    for step in range(3):
+        ids, hid, lg = oracle.draft_step(L, e0, np.array([toks[-1]], np.int32), table, hs[-1][None], k1, v1,
+                                         L0 + step, moe=inp)
+        toks.append(int(ids[0]))
+        hs.append(hid[0])
+        chain.append((int(ids[0]), hid[0], lg[0]))
+    ids_v, hid_v, log_v = oracle.draft_step(L, np.repeat(e0, 4, 0), np.array(toks, np.int32), table, np.stack(hs),
+                                            kc.copy(), vc.copy(), L0, moe=inp)
+    assert ids_v[:3].tolist() == [c[0] for c in chain]
+    assert np.array_equal(hid_v[:3], np.stack([c[1] for c in chain]))
+    assert np.array_equal(log_v[:3], np.stack([c[2] for c in chain]))
