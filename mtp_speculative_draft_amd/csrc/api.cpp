@@ -157,8 +157,7 @@ hipError_t run_gemv(int fmt, int pro, int epi, int m, GemvParams& p, int max_blo
     p.m = m;
     p.G = p.K / MTP_GROUP;
     p.S = (p.G + 63) / 64;
-    const GemvShape sh = gemv_shape(fmt, epi, m, p.N, p.K, max_blocks, block_waves(fmt, epi, inst_m(m)));
-    return launch_gemv(fmt, pro, epi, m, p, sh, st);
+    return launch_gemv(fmt, pro, epi, m, p, max_blocks, st);
 }
 
 int default_blocks() { return 4 * device_cu_count(); }
@@ -181,14 +180,10 @@ hipError_t run_head_fmt(int fmt, const QMat& lm, int k, const float* hidden, con
     p.m = m;
     p.G = p.K / MTP_GROUP;
     p.S = (p.G + 63) / 64;
-    // persistent: one block of 8 waves per compute unit (two of 4 for more
-    // than four rows), its waves sharing the block's rows at run time
+    // persistent: a compute unit's worth of waves per block, its waves sharing
+    // the block's rows at run time
     p.balance = 1;
-    const int waves = block_waves(fmt, EPI_ARGMAX, inst_m(m));
-    int maxb = device_cu_count() * (kMaxWaves / waves);
-    if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
-    const GemvShape sh = gemv_shape(fmt, EPI_ARGMAX, m, p.N, p.K, maxb, waves);
-    return launch_gemv(fmt, PRO_RMS, EPI_ARGMAX, m, p, sh, st);
+    return launch_gemv(fmt, PRO_RMS, EPI_ARGMAX, m, p, 0, st);
 }
 
 hipError_t run_head(const float* hidden, const float* gamma, float eps, const mtp_q4& lm, float* normed_out,

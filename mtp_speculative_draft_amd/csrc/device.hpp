@@ -1,19 +1,22 @@
 // device.hpp -- shared device building blocks of libmtp's gfx950 kernels.
 //
-// Quantized GEMV scheme (all m <= 8 row kernels):
-//   * one wave64 covers 64 consecutive groups of 32 input features (2048
-//     features, a "chunk"); lane l owns group l of the chunk.  A weight row's
-//     codes for a chunk are one contiguous 1 KB (4-bit) or 2 KB (8-bit) span,
-//     so every load instruction of a wave reads whole 128-byte lines.
-//   * the activation group held by a lane is quantized once per kernel to a
-//     16-bit fixed-point value split into two int8 halves (hi, lo) with one
-//     scale per (chunk, row): x ~= xs * (256*hi + lo).  The integer dot
-//     products with the weight codes then run on v_dot4_i32_i8, exact in
-//     int32; 4-bit codes only need a mask and a shift to become bytes.
-//   * per (weight row, group) a lane returns s*A + b*sum(x^), A the exact
-//     integer dot and x^ the quantized activations (see quantize_group); a
-//     transposed butterfly reduces many rows' partials
-//     across the 64 lanes at once, and the chunk result is xs * sum.
+// Quantized GEMV arithmetic (every kernel, vector and matrix core):
+//   * activations stay f32.  Weight codes become exact f16 operands without
+//     any float conversion: a masked 4-bit code c (or 16c) in the low bits of
+//     a 16-bit half is the f16 subnormal c * 2^-24 (16c * 2^-24), and an
+//     8-bit code offset to c + 128 is the subnormal (c + 128) * 2^-24.  The
+//     f32 FMA with an f16 operand (v_fma_mix_f32) and the f16 matrix cores
+//     take these subnormals exactly (the kernels run with f16 subnormals
+//     kept), so every product c * x is exact and only the f32 accumulation
+//     rounds.
+//   * per (weight row, group of 32) a 4-bit row contributes
+//     (s * 2^24) * sum(c x 2^-24) + b * sum(x), which is sum((s c + b) x);
+//     an 8-bit row s * (2^24 * sum((c + 128) x 2^-24) - 128 sum(x)).
+//   * one wave64 covers 64 consecutive groups (2048 features, a "chunk");
+//     lane l owns group l, so a weight row's codes for a chunk are one
+//     contiguous 1 KB (4-bit) or 2 KB (8-bit) span and every load
+//     instruction of a wave reads whole 128-byte lines.  A transposed
+//     butterfly reduces many rows' partials across the 64 lanes at once.
 // Weight formats (hf2q 0.1.1, src/serve/forward_mlx_shared.rs,
 // `MlxAffineExtra` / `MlxQWeight::from_mlx_affine_linear`): 4-bit codes u32
 // [n][k/8], element k in nibble k%8 of word k/8; f32 scale and bias per group
@@ -30,7 +33,7 @@ namespace mtp {
 constexpr int kWave = 64;
 constexpr int kGroup = 32;
 constexpr int kChunk = kWave * kGroup;  // input features covered by one wave
-constexpr float kQMax = 32512.0f;       // |q| bound so that hi = round(q/256) fits int8
+constexpr float kTwo24 = 16777216.0f;   // 2^24: undoes the code subnormal scale
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -156,67 +159,75 @@ __device__ __forceinline__ int argmax_key_index(unsigned long long k) {
     return k == 0ull ? 0 : (int)(0xFFFFFFFFu - (unsigned)(k & 0xFFFFFFFFull));
 }
 
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
 // ---------------------------------------------------------------------------
-// Activation fragment: one row of x restricted to this lane's group of 32.
-// Q4 layout: word j of the group holds nibbles k = 8j..8j+7; the even
-// nibbles (mask 0x0F0F0F0F) pair with hi[2j]/lo[2j] = x[8j+0,2,4,6], the odd
-// nibbles (shift by 4, mask) with hi[2j+1]/lo[2j+1] = x[8j+1,3,5,7].
-// Q8 layout: word j holds k = 4j..4j+3 in byte order, hi[j]/lo[j] likewise.
+// Code words as f16 subnormal pairs.
+// 4-bit word (codes c0..c7 of features 8j..8j+7, c_i in nibble i): four
+// halves pairs, in feature order 0, 4 | 1, 5 | 2, 6 | 3, 7, where the pairs
+// of features 1, 5 and 3, 7 hold 16 c (the nibble stays in bits 4-7), so
+// their activations carry a factor 1/16.  Five integer ops, no conversion.
 // ---------------------------------------------------------------------------
-struct XFrag {
-    int hi[8];
-    int lo[8];
-    float sxd;  // sum of the group's 32 quantized values (an integer), the bias factor of 4-bit rows
+struct Q4Halves {
+    unsigned r[4];
 };
 
-__device__ __forceinline__ int pack_bytes(int a, int b, int c, int d) {
-    return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((unsigned)d << 24);
+__device__ __forceinline__ Q4Halves q4_halves(unsigned w) {
+    const unsigned w8 = w >> 8;
+    return Q4Halves{{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u}};
 }
 
-// Returns the 16-bit quantized value q = round(x*inv) as hi*256 + lo.
-__device__ __forceinline__ int split16(float x, float inv, int& h, int& l) {
-    const int q = __float2int_rn(x * inv);  // |q| <= 32512
-    h = (q + 128) >> 8;                     // round(q / 256), in -127..127
-    l = q - h * 256;                        // in -128..127
-    return q;
+// 8-bit word (codes of features 4j..4j+3 in byte order): (c + 128) of
+// features 0, 2 | 1, 3 as two halves pairs.
+struct Q8Halves {
+    unsigned r[2];
+};
+
+__device__ __forceinline__ Q8Halves q8_halves(unsigned w) {
+    const unsigned u = w ^ 0x80808080u;  // c + 128 in every byte
+    return Q8Halves{{__builtin_amdgcn_perm(u, u, 0x0C020C00u), __builtin_amdgcn_perm(u, u, 0x0C030C01u)}};
 }
 
-// Quantizes the 32 values word by word (few live registers).
-//
-// 4-bit rows: with the group's quantized activations x^_k (x ~ xs * x^) a
-// row's group term is computed as s * sum(c_k x^_k) + b * sum(x^_k), both
-// sums exact integers; that is sum((s c_k + b) x^_k), the exact product of the
-// row's weights with the quantized activations.  Its only error is the
-// activation rounding weighted by the weights themselves, which are centred
-// (the bias is about -8 s), so no error is shared by all rows.  (Summing the
-// unrounded x/xs for the bias factor instead would leave the codes' mean 8
-// times the rounding residual as such a shared error.)
+__device__ __forceinline__ h2_t as_h2(unsigned r) { return __builtin_bit_cast(h2_t, r); }
+
+// Position of feature f (0..7) of a 4-bit word in the halves order, and the
+// activation factor that goes with it.
+__host__ __device__ constexpr int q4_slot(int f) { return (f & 3) * 2 + (f >> 2); }
+__host__ __device__ constexpr float q4_factor(int f) { return (f & 1) ? 0.0625f : 1.0f; }
+// The same for feature f (0..3) of an 8-bit word.
+__host__ __device__ constexpr int q8_slot(int f) { return (f & 1) * 2 + (f >> 1); }
+
+// ---------------------------------------------------------------------------
+// Activation fragment: one row of x restricted to this lane's group of 32,
+// in the halves order of the group's code words (4-bit: word j's slots
+// 8j + q4_slot(f) with the factor q4_factor(f); 8-bit: 4j + q8_slot(f)),
+// and the group's sum (4-bit: sum x, the bias factor; 8-bit: -128 sum x).
+// ---------------------------------------------------------------------------
+struct XFrag {
+    float v[32];
+    float sum;
+};
+
+// xv: the group's 32 features in natural order.
 template <int FMT>
-__device__ __forceinline__ void quantize_group(const float (&xv)[32], float inv, float xs, XFrag& f) {
-    (void)xs;
-    int qs = 0;
+__device__ __forceinline__ void make_frag(const float (&xv)[32], XFrag& f) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += xv[i];
     if constexpr (FMT == FMT_Q4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int h[8], l[8];
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qs += split16(xv[8 * j + i], inv, h[i], l[i]);
-            f.hi[2 * j] = pack_bytes(h[0], h[2], h[4], h[6]);
-            f.hi[2 * j + 1] = pack_bytes(h[1], h[3], h[5], h[7]);
-            f.lo[2 * j] = pack_bytes(l[0], l[2], l[4], l[6]);
-            f.lo[2 * j + 1] = pack_bytes(l[1], l[3], l[5], l[7]);
-        }
+            for (int q = 0; q < 8; ++q) f.v[8 * j + q4_slot(q)] = xv[8 * j + q] * q4_factor(q);
+        f.sum = s;
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            int h[4], l[4];
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) split16(xv[4 * j + i], inv, h[i], l[i]);
-            f.hi[j] = pack_bytes(h[0], h[1], h[2], h[3]);
-            f.lo[j] = pack_bytes(l[0], l[1], l[2], l[3]);
-        }
+            for (int q = 0; q < 4; ++q) f.v[4 * j + q8_slot(q)] = xv[4 * j + q];
+        f.sum = -128.0f * s;
     }
-    f.sxd = (float)qs;  // exact: |qs| <= 32 * 32512 < 2^24
 }
 
 // ---------------------------------------------------------------------------
@@ -256,50 +267,39 @@ __device__ __forceinline__ void load_frag(WFrag<FMT_Q8>& w, const void* codes, c
     w.s = __builtin_nontemporal_load(scales + gi);
 }
 
-// Nibbles of a 4-bit fragment as bytes: e[j] = even nibbles, o[j] = odd.
-struct Nib {
-    int e[4], o[4];
-};
-
-__device__ __forceinline__ Nib unpack_nibbles(const u32x4& c) {
-    Nib n;
+// (s c + b) . x over the group for a 4-bit row: 8 exact products per word
+// accumulated in f32 (two chains), then the scale and the bias term.
+__device__ __forceinline__ float dot_q4(const u32x4& c, float s, float b, const XFrag& x) {
     const unsigned w[4] = {c.x, c.y, c.z, c.w};
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        n.e[j] = (int)(w[j] & 0x0F0F0F0Fu);
-        n.o[j] = (int)((w[j] >> 4) & 0x0F0F0F0Fu);
-    }
-    return n;
-}
-
-__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
-
-// s*A + b*sxd for a 4-bit row against one activation fragment.
-__device__ __forceinline__ float dot_q4(const Nib& n, float s, float b, const XFrag& x) {
-    int ah = 0, al = 0;
+        const Q4Halves q = q4_halves(w[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ah = sdot4(n.e[j], x.hi[2 * j], ah);
-        ah = sdot4(n.o[j], x.hi[2 * j + 1], ah);
-        al = sdot4(n.e[j], x.lo[2 * j], al);
-        al = sdot4(n.o[j], x.lo[2 * j + 1], al);
+        for (int i = 0; i < 4; ++i) {
+            const h2_t h = as_h2(q.r[i]);
+            float& a = (i & 1) ? a1 : a0;
+            a = fmaf((float)h.x, x.v[8 * j + 2 * i], a);
+            a = fmaf((float)h.y, x.v[8 * j + 2 * i + 1], a);
+        }
     }
-    const int a = ah * 256 + al;  // exact: |a| < 2^24
-    return fmaf(s, (float)a, b * x.sxd);
+    return fmaf(s * kTwo24, a0 + a1, b * x.sum);
 }
 
-// s*A for an 8-bit row against one activation fragment.
+// (s c) . x over the group for an 8-bit row.
 __device__ __forceinline__ float dot_q8(const WFrag<FMT_Q8>& w, const XFrag& x) {
-    const int c[8] = {(int)w.c0.x, (int)w.c0.y, (int)w.c0.z, (int)w.c0.w,
-                      (int)w.c1.x, (int)w.c1.y, (int)w.c1.z, (int)w.c1.w};
-    int ah = 0, al = 0;
+    const unsigned c[8] = {w.c0.x, w.c0.y, w.c0.z, w.c0.w, w.c1.x, w.c1.y, w.c1.z, w.c1.w};
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        ah = sdot4(c[j], x.hi[j], ah);
-        al = sdot4(c[j], x.lo[j], al);
+        const Q8Halves q = q8_halves(c[j]);
+        const h2_t h0 = as_h2(q.r[0]), h1 = as_h2(q.r[1]);
+        a0 = fmaf((float)h0.x, x.v[4 * j], a0);
+        a1 = fmaf((float)h0.y, x.v[4 * j + 1], a1);
+        a0 = fmaf((float)h1.x, x.v[4 * j + 2], a0);
+        a1 = fmaf((float)h1.y, x.v[4 * j + 3], a1);
     }
-    const int a = ah * 256 + al;  // |a| < 2^28
-    return w.s * (float)a;
+    return w.s * fmaf(a0 + a1, kTwo24, x.sum);
 }
 
 // ---------------------------------------------------------------------------

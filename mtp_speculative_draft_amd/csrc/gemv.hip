@@ -117,21 +117,6 @@ __device__ __forceinline__ void load_x_row(const GemvParams& p, const View& v, i
     }
 }
 
-// 16-bit activation quantization without a float-to-int conversion: adding
-// 1.5 * 2^23 + 128 to the product x * inv (rounded first, as in split16)
-// leaves q + 128 + 0x400000 in the low mantissa bits, rounded to nearest
-// even exactly as split16 rounds, for |q| < 2^22.  Byte 1 of the result is
-// then hi = (q + 128) >> 8 and byte 0 is lo = q - 256 hi with its sign bit
-// flipped, and the bits of several values sum to sum(q) plus a known
-// multiple of kQBiasBits.
-constexpr float kQBias = 12583040.0f;  // 1.5 * 2^23 + 128
-constexpr unsigned kQBiasBits = 0x4B400080u;
-__device__ __forceinline__ unsigned q_bits(float x, float inv) {
-#pragma clang fp contract(off)
-    const float y = x * inv;
-    return __float_as_uint(y + kQBias);
-}
-
 // Row mi's input for the features of segment seg (PRO_CONCAT: 0 = the
 // embedding row, or the token's table row, 1 = the hidden row; otherwise the
 // one input row) and the matching gamma.
@@ -158,13 +143,13 @@ __device__ __forceinline__ const float* x_segment(const GemvParams& p, const Vie
     }
 }
 
-// Norm (for PRO_RMS / PRO_CONCAT) and 16-bit split of the lane's features of
-// row mi.  Every thread of the block calls it; it holds block barriers when
+// Norm (for PRO_RMS / PRO_CONCAT) of the lane's features of row mi, then its
+// fragment.  Every thread of the block calls it; it holds block barriers when
 // several waves share one weight row (S > 1).
 template <int FMT, int PRO>
-__device__ __forceinline__ void norm_quant_row(const GemvParams& p, const View& v, int wid, int lane, int S, int mi,
-                                               int kk, bool active, float (&xv)[32], const float (&gv)[32],
-                                               XFrag& xf, float& xs, float (*nred)[2]) {
+__device__ __forceinline__ void norm_row(const GemvParams& p, const View& v, int wid, int lane, int S, int mi,
+                                         int kk, bool active, float (&xv)[32], const float (&gv)[32], XFrag& xf,
+                                         float (*nred)[2]) {
     const int q = wid / S;
     if constexpr (PRO != PRO_PLAIN) {
         const int seg = (PRO == PRO_CONCAT && kk >= p.H) ? 1 : 0;
@@ -197,146 +182,23 @@ __device__ __forceinline__ void norm_quant_row(const GemvParams& p, const View& 
                 store32(p.normed_out + (int64_t)mi * v.K + kk, xv);
         }
     }
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[i]));
-    am = wave_max(am);
-    const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
-    xs = am / kQMax;
-    quantize_group<FMT>(xv, inv_q, xs, xf);
+    make_frag<FMT>(xv, xf);
 }
 
-// Block-shared setup for two or more activation rows.  The (row, chunk)
-// fragments are computed once per block instead of once per wave: wave
-// (s, q) takes rows q, q + Q, ... of its chunk s (two rows' loads in flight
-// at a time), norms combine the chunks' sums of squares through LDS, and
-// each fragment goes to LDS, from where every wave of chunk s reads all M.
-// Rows are independent work, so M rows cost about one row's latency when
-// Q >= M.  Used for two and four rows (eight would not fit the registers
-// beside the kernel's other state).
-template <int M>
-__host__ __device__ constexpr int xq_slots() { return M == 2 ? 8 : 12; }
-constexpr int kXqWords = 18;  // hi[8], lo[8], sxd, one spare word
-
-template <int PRO>
-__device__ __forceinline__ const float* gamma_src(const GemvParams& p, int kk) {
-    if constexpr (PRO == PRO_CONCAT) return kk >= p.H ? p.g1 + (kk - p.H) : p.g0 + kk;
-    return p.g0 + kk;
-}
-
-template <int FMT, int M, int PRO>
-__device__ __forceinline__ void shared_rows(const GemvParams& p, const View& v, int lane, int S, int Q, int s,
-                                            int q, int kk, bool active, unsigned* xq, float* xsq, float (*nq)[2],
-                                            XFrag (&xf)[M], float (&xs)[M]) {
-    constexpr int JB = M >= 4 ? 4 : 2;  // rows whose loads are in flight together
-    const int per = (M + Q - 1) / Q;  // rows per wave, the same in every wave
-    float gv[32];
-    if constexpr (PRO != PRO_PLAIN) {
-        if (active) {
-            load32(gv, gamma_src<PRO>(p, kk));
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) gv[i] = 0.0f;
-        }
-    }
-    const int seg = (PRO == PRO_CONCAT && kk >= p.H) ? 1 : 0;
-    for (int j0 = 0; j0 < per; j0 += JB) {
-        float xv[JB][32];
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-            const int mi = q + Q * (j0 + jj);
-            if (mi < M) load_x_row<PRO>(p, v, mi, kk, active, xv[jj], gv, false);
-        }
-        float inv[JB];
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) inv[jj] = 1.0f;
-        if constexpr (PRO != PRO_PLAIN) {
-#pragma unroll
-            for (int jj = 0; jj < JB; ++jj) {
-                const int mi = q + Q * (j0 + jj);
-                if (mi < M) {
-                    float ss = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) ss = fmaf(xv[jj][i], xv[jj][i], ss);
-                    const float s0 = wave_sum(seg == 0 ? ss : 0.0f);
-                    const float s1 = (PRO == PRO_CONCAT) ? wave_sum(seg == 1 ? ss : 0.0f) : 0.0f;
-                    if (lane == 0) {
-                        nq[mi * S + s][0] = s0;
-                        nq[mi * S + s][1] = s1;
-                    }
-                }
-            }
-            __syncthreads();
-            const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
-#pragma unroll
-            for (int jj = 0; jj < JB; ++jj) {
-                const int mi = q + Q * (j0 + jj);
-                if (mi < M) {
-                    float tot = 0.0f;
-                    for (int j = 0; j < S; ++j) tot += nq[mi * S + j][seg];
-                    inv[jj] = rsqrtf(tot / (float)nfeat + p.eps);
-                }
-            }
-        }
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-            const int mi = q + Q * (j0 + jj);
-            if (mi < M) {
-                if constexpr (PRO != PRO_PLAIN) {
-                    if (active && mi < p.m) {
-#pragma unroll
-                        for (int i = 0; i < 32; ++i) xv[jj][i] = xv[jj][i] * inv[jj] * gv[i];
-                        if (PRO == PRO_RMS && p.normed_out && blockIdx.x == 0 && blockIdx.y == 0)
-                            store32(p.normed_out + (int64_t)mi * v.K + kk, xv[jj]);
-                    }
-                }
-                float am = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(xv[jj][i]));
-                am = wave_max(am);
-                const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
-                const float x_s = am / kQMax;
-                XFrag f;
-                quantize_group<FMT>(xv[jj], inv_q, x_s, f);
-                unsigned* dst = xq + (mi * S + s) * kXqWords * kWave + lane;
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    dst[w * kWave] = (unsigned)f.hi[w];
-                    dst[(8 + w) * kWave] = (unsigned)f.lo[w];
-                }
-                dst[16 * kWave] = __float_as_uint(f.sxd);
-                if (lane == 0) xsq[mi * S + s] = x_s;
-            }
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-        const unsigned* src = xq + (mi * S + s) * kXqWords * kWave + lane;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            xf[mi].hi[w] = (int)src[w * kWave];
-            xf[mi].lo[w] = (int)src[(8 + w) * kWave];
-        }
-        xf[mi].sxd = __uint_as_float(src[16 * kWave]);
-        xs[mi] = xsq[mi * S + s];
-    }
-}
-
-// One activation row, 4-bit weights.  Each wave loads its whole chunk s of
-// the row in 1 KB pieces (lane l holds features 256 i + 4 l .. +3 of piece
-// i), so every load instruction reads a contiguous kilobyte; the loads are
-// requested before the first weight tiles (row1_load), with no branches, so
-// that the setup waits for them alone, and consumed after (row1_finish): the
-// norm (over the block's chunk waves through LDS when S > 1), the chunk
-// maximum, quantization with q_bits, and each group's fragment (hi[8],
-// lo[8], sxd; the layout of quantize_group) passed through a wave-private
-// LDS region to the lane that owns the group.
+// One activation row.  Each wave loads its whole chunk s of the row in 1 KB
+// pieces (lane l holds features 256 i + 4 l .. +3 of piece i), so every load
+// instruction reads a contiguous kilobyte; the loads are requested before the
+// first weight tiles (row1_load), with no branches, so that the setup waits
+// for them alone, and consumed after (row1_finish): the norm (over the
+// block's chunk waves through LDS when S > 1), then the pieces pass through a
+// wave-private LDS region (groups 36 floats apart, so that both the writes
+// and the group reads spread over all banks) to the lane that owns the group.
 struct Row1Pieces {
     float4 x[8], g[8];
 };
 constexpr int kRow1Chunks = 4;  // K <= 8192
-constexpr int kRow1Words = 17;  // hi[8], lo[8], sxd per group
+constexpr int kGroupStride = 36;  // floats between groups in the LDS transposes
+constexpr int kRow1Floats = kWave * kGroupStride;
 
 template <int PRO>
 __device__ __forceinline__ void row1_load(const GemvParams& p, const View& v, int lane, int s, Row1Pieces& rp) {
@@ -354,10 +216,9 @@ __device__ __forceinline__ void row1_load(const GemvParams& p, const View& v, in
     }
 }
 
-template <int PRO>
+template <int FMT, int PRO>
 __device__ __forceinline__ void row1_finish(const GemvParams& p, const View& v, int lane, int S, int s, int q,
-                                            Row1Pieces& rp, unsigned* xq, float (*part)[2], XFrag& xf,
-                                            float& xs) {
+                                            Row1Pieces& rp, float* xq, float (*part)[2], XFrag& xf) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         if (kChunk * s + 256 * i + 4 * lane >= v.K) rp.x[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -401,49 +262,23 @@ __device__ __forceinline__ void row1_finish(const GemvParams& p, const View& v, 
             if (store && f < v.K) *reinterpret_cast<float4*>(p.normed_out + f) = x;
         }
     }
-    float am = 0.0f;
+    // piece i, lane l -> group 8 i + l / 8, features 4 (l % 8) ..
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float4 x = rp.x[i];
-        am = fmaxf(am, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
-    }
-    am = wave_max(am);
-    const float inv_q = am > 0.0f ? kQMax / am : 0.0f;
-    xs = am / kQMax;
-    // lanes 2k and 2k+1 hold the first and last four features of a code
-    // word, and one quad exchange forms the word's hi and lo operand words
-    // (even features, then odd)
-    const bool odd = lane & 1;
-    const unsigned sel_h = odd ? 0x01000504u : 0x05040100u;
-    const unsigned sel_l = odd ? 0x03020706u : 0x07060302u;
-    const int k8 = lane & 7;  // word of the group
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float4 x = rp.x[i];
-        const unsigned b0 = q_bits(x.x, inv_q), b1 = q_bits(x.y, inv_q), b2 = q_bits(x.z, inv_q),
-                       b3 = q_bits(x.w, inv_q);
-        unsigned qsum = (b0 + b1) + (b2 + b3);
-        const unsigned p02 = __builtin_amdgcn_perm(b2, b0, 0x04000501u);
-        const unsigned p13 = __builtin_amdgcn_perm(b3, b1, 0x04000501u);
-        const unsigned keep = odd ? p13 : p02;
-        const unsigned got = (unsigned)dpp_partner<1>((int)(odd ? p02 : p13));
-        const int gl = 8 * i + (lane >> 3);  // group within the chunk
-        xq[k8 * kWave + gl] = __builtin_amdgcn_perm(got, keep, sel_h);
-        xq[(8 + k8) * kWave + gl] = __builtin_amdgcn_perm(got, keep, sel_l) ^ 0x80808080u;
-        qsum += (unsigned)dpp_partner<1>((int)qsum);
-        qsum += (unsigned)dpp_partner<2>((int)qsum);
-        qsum += (unsigned)dpp_partner<4>((int)qsum);
-        if (k8 == 0) xq[16 * kWave + gl] = __float_as_uint((float)(int)(qsum - 32u * kQBiasBits));
-    }
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<float4*>(xq + (8 * i + (lane >> 3)) * kGroupStride + 4 * (lane & 7)) = rp.x[i];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float xv[32];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        xf.hi[k] = (int)xq[k * kWave + lane];
-        xf.lo[k] = (int)xq[(8 + k) * kWave + lane];
+        const float4 t = *reinterpret_cast<const float4*>(xq + lane * kGroupStride + 4 * k);
+        xv[4 * k] = t.x;
+        xv[4 * k + 1] = t.y;
+        xv[4 * k + 2] = t.z;
+        xv[4 * k + 3] = t.w;
     }
-    xf.sxd = __uint_as_float(xq[16 * kWave + lane]);
+    make_frag<FMT>(xv, xf);
 }
 
 // Weight fragments of one tile (R rows x P matrices) for this lane's group.
@@ -487,9 +322,8 @@ __device__ __forceinline__ void compute_tile(const TileFrags<FMT, R, P>& tf, con
         for (int pp = 0; pp < P; ++pp) {
             const WFrag<FMT>& f = tf.f[r][pp];
             if constexpr (FMT == FMT_Q4) {
-                const Nib n = unpack_nibbles(f.c);
 #pragma unroll
-                for (int mi = 0; mi < M; ++mi) acc[(r * M + mi) * P + pp] = dot_q4(n, f.s, f.b, xf[mi]);
+                for (int mi = 0; mi < M; ++mi) acc[(r * M + mi) * P + pp] = dot_q4(f.c, f.s, f.b, xf[mi]);
             } else {
 #pragma unroll
                 for (int mi = 0; mi < M; ++mi) acc[(r * M + mi) * P + pp] = dot_q8(f, xf[mi]);
@@ -622,57 +456,37 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
     auto row0 = [&](int u) { return (u * per + qo) * R; };
     TileFrags<FMT, R, P> tf, tf2;
     XFrag xf[M];
-    float xs[M];
-    bool shared_done = false;
-    // one 4-bit activation row: its pieces are requested before the first
-    // tiles, which are then requested unconditionally (tile 0 stands in for
-    // none), so that the setup waits for the activations only
-    constexpr bool kRow1 = M == 1 && FMT == FMT_Q4;  // S <= kRow1Chunks (checked at launch)
+    // the activations are requested before the first tiles, which are then
+    // requested unconditionally (tile 0 stands in for none), so that the
+    // setup waits for the activations only: one row in contiguous 1 KB
+    // pieces, two rows as each lane's own group
+    constexpr bool kRow1 = M == 1;  // S <= kRow1Chunks (checked at launch)
     Row1Pieces rp;
-    if constexpr (kRow1) row1_load<PRO>(p, v, lane, s, rp);
-    int wa = ts.next(claim), wb = -1;
+    float xv2[M][32], gv2[32];
     if constexpr (kRow1) {
-        load_tile<FMT, R, P>(tf, v, row0(wa >= 0 ? wa : 0), gc);
-        if constexpr (kDouble) {
-            if (wa >= 0) wb = ts.next(claim);
-            load_tile<FMT, R, P>(tf2, v, row0(wb >= 0 ? wb : 0), gc);
-        }
+        row1_load<PRO>(p, v, lane, s, rp);
     } else {
-        if (wa >= 0) load_tile<FMT, R, P>(tf, v, row0(wa), gc);
-        if constexpr (kDouble) {
-            if (wa >= 0) wb = ts.next(claim);
-            if (wb >= 0) load_tile<FMT, R, P>(tf2, v, row0(wb), gc);
-        }
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) load_x_row<PRO>(p, v, mi, kk, active, xv2[mi], gv2, mi == 0);
+    }
+    int wa = ts.next(claim), wb = -1;
+    load_tile<FMT, R, P>(tf, v, row0(wa >= 0 ? wa : 0), gc);
+    if constexpr (kDouble) {
+        if (wa >= 0) wb = ts.next(claim);
+        load_tile<FMT, R, P>(tf2, v, row0(wb >= 0 ? wb : 0), gc);
     }
     if constexpr (kRow1) {
-        __shared__ unsigned xq1[kWaves][kRow1Words * kWave];
+        __shared__ float xq1[kWaves][kRow1Floats];
         __shared__ float part1[kRow1Chunks][2];
-        row1_finish<PRO>(p, v, lane, S, s, q, rp, xq1[wid], part1, xf[0], xs[0]);
-        shared_done = true;
-    }
-    if constexpr (M == 2 || M == 4) {
-        __shared__ unsigned xq[xq_slots<M>() * kXqWords * kWave];
-        __shared__ float xsq[xq_slots<M>()];
-        __shared__ float nq[xq_slots<M>()][2];
-        if (M * S <= xq_slots<M>()) {
-            shared_rows<FMT, M, PRO>(p, v, lane, S, Q, s, q, kk, active, xq, xsq, nq, xf, xs);
-            shared_done = true;
-        }
-    }
-    if (!shared_done) {
-        float gv[32];  // gamma is the same for every row: loaded with row 0
+        row1_finish<FMT, PRO>(p, v, lane, S, s, q, rp, xq1[wid], part1, xf[0]);
+    } else {
 #pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-            float xv[32];
-            load_x_row<PRO>(p, v, mi, kk, active, xv, gv, mi == 0);
-            norm_quant_row<FMT, PRO>(p, v, wid, lane, S, mi, kk, active, xv, gv, xf[mi], xs[mi], nred);
-        }
+        for (int mi = 0; mi < M; ++mi) norm_row<FMT, PRO>(p, v, wid, lane, S, mi, kk, active, xv2[mi], gv2, xf[mi], nred);
     }
 
     const int pos = reduce_base<V, P>(lane) / P;  // = r * M + mi of this lane's result
     const int r_l = pos / M, mi_l = pos % M;
     const bool writer = reduce_writer<V, P>(lane);
-    const float xs_l = select_m<M>(xs, mi_l);
     float best = -INFINITY;
     int best_i = INT_MAX;
 
@@ -680,8 +494,8 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
     // apply the epilogue
     auto finish = [&](float (&acc)[V], int row0) {
         reduce_transpose<V, P>(acc, lane);
-        float v0 = acc[0] * xs_l;
-        float v1 = (P == 2) ? acc[P - 1] * xs_l : 0.0f;
+        float v0 = acc[0];
+        float v1 = (P == 2) ? acc[P - 1] : 0.0f;
         if (S > 1) {
             red[wid][2 * lane] = v0;
             red[wid][2 * lane + 1] = v1;
@@ -773,37 +587,38 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core GEMV: 4-bit weights, K = 2048, up to four activation rows.
+// Matrix-core GEMVs for three and four activation rows (f16 MFMA 16x16x32,
+// one group of 32 features per MFMA).
 //
-// Work unit: 16 weight rows, one wave.  Lane l loads row l%16 and, per load
-// t, the 16 bytes of group 4t + l/16, so a load covers 16 rows x 64 bytes.
-// One v_permlane32_swap per word pair turns the lane quarters' groups into
-// the A operands of two v_mfma_i32_16x16x64_i8 per load, each over a group
-// pair: quarters 0 and 2 then hold the pair's first group (words 0-1 and
-// 2-3), quarters 1 and 3 the second.  The B operand (the activations' int8
-// halves, built once per block in LDS) pairs columns 0..7 with the first
-// group and 8..15 with the second and is zero elsewhere; column c of a group
-// is (activation row c/2, hi half if c is even, lo half if odd).  Each
-// group's int32 result is scaled by its row's scale and accumulated in f32;
-// the bias sums (b times the group's sum of quantized activations) are f32
-// MFMAs (16x16x4) fed with the biases as loaded.  Two DPP adds then fold the
-// group halves and the hi/lo columns, and the result is
-// xs * (256 hi + lo + bias sums), the same quantity as in the vector path.
-//
-// 8-bit weights (int8 codes, one scale per group, no bias) use the same unit,
-// B columns and scaling.  A row is 2048 bytes, so a unit is 32 loads, and
-// load t of lane l is row l%16's bytes 64 t + 16 (l/16) .. +15, which is
-// already the A operand of one MFMA over the group pair 2t, 2t + 1 (quarters
-// 0-1 hold the first group, 2-3 the second).  The B operand holds the
-// activations in natural order: feature f is byte f%16 of quarter (f/16)%4 of
-// MFMA f/64, in the columns of group parity (f/32)%2.  With no bias there is
-// no f32 MFMA, and the result is xs * (256 hi + lo).
+// A (weights): 16 weight rows.  Lane (h = l/16, j = l%16) holds row j's
+// k-slot h of the group as 8 f16 halves: the code subnormals of q4_halves
+// (4-bit: word h of the group) or q8_halves (8-bit: words 2 rho(h), 2 rho(h)+1
+// with rho = 0, 2, 1, 3), with no conversion.
+// B (activations): the same k-slots in 12 columns; column 3 mi + t is term t
+// of activation row mi, where v = x 2^(15-e) = hi + mid + lo in three f16
+// values (2^e bounds the row's largest |x|, and features on 16c halves carry
+// 1/16).  hi is v rounded to a fixed grid (16, or 1 for the 1/16 features),
+// so all hi products of a group are multiples of one unit and their sum fits
+// f32's 24 bits: the matrix core adds them exactly whatever its alignment
+// and rounding.  mid and lo are the f16 remainder (|mid| <= 8), so x is
+// represented down to 2^-34 of the row's largest value.  Every product is
+// exact; the MFMA accumulates in f32.  Columns 12..15 read copies of
+// other columns and their results are never used (each D column depends on
+// its own B column only).
+// The codes enter centred (4-bit c - 8, 8-bit c; see q4_operand).
+// D: lane (h, c) holds rows 4h..4h+3 of column c.  Each group's D is scaled
+// by its rows' group scales (staged per wave in LDS) into an f32 accumulator;
+// the 4-bit bias, (b + 8 s) sum(x), is an f32 MFMA (16x16x4) over the group
+// sums.  At the end every column is scaled back by 2^(9+e) (2^24 for the code
+// subnormals times 2^(e-15)), and the three term columns of a row are added
+// (DPP).
 // ---------------------------------------------------------------------------
-typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int kMmaRows = 16;
 constexpr int kMmaCols = 16;
-constexpr int kStage = 20;  // floats per group in a wave's scale stage (16 rows, 16-byte aligned)
+constexpr int kBCols = 12;           // term columns: 4 rows x 3 terms
+constexpr int kBGroup = 4 * kBCols;  // B operands (u32x4) per group: 4 k-slots x 12 columns
+constexpr int kStage = 20;           // floats per group in a wave's scale stage (16 rows, 16-byte aligned)
 
 __device__ __forceinline__ void perm32_swap(unsigned& a, unsigned& b) {
     const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
@@ -811,12 +626,36 @@ __device__ __forceinline__ void perm32_swap(unsigned& a, unsigned& b) {
     b = r[1];
 }
 
+__device__ __forceinline__ void perm16_swap(unsigned& a, unsigned& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+
+// 4 x 4 transpose across the lane quarters: quarter q's word i becomes the
+// word q that quarter i held.
+__device__ __forceinline__ void quarter_transpose(unsigned& w0, unsigned& w1, unsigned& w2, unsigned& w3) {
+    perm32_swap(w0, w2);
+    perm32_swap(w1, w3);
+    perm16_swap(w0, w1);
+    perm16_swap(w2, w3);
+}
+
+__device__ __forceinline__ h8_t as_h8(unsigned a, unsigned b, unsigned c, unsigned d) {
+    const u32x4 t = {a, b, c, d};
+    return __builtin_bit_cast(h8_t, t);
+}
+
+__device__ __forceinline__ unsigned half_bits(float x) {
+    return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)x);
+}
+
 // Activation setup of the matrix-core kernels, shared by a block's waves:
 // wave w takes activation row w % 4 and, of each of the S chunks, the 1 KB
 // pieces NI (w / 4) .. NI (w / 4) + NI - 1 (lane l holds features
 // 256 i + 4 l .. +3 of piece i), so that every load instruction reads one
 // contiguous kilobyte.  The loads are issued first (mma_load_x), so that
-// they overlap the weight requests that follow, and consumed by mma_quant_x.
+// they overlap the weight requests that follow, and consumed by mma_setup.
 template <int S, int NI>
 struct XPieces {
     float4 x[S][NI], g[S][NI];
@@ -848,17 +687,14 @@ __device__ __forceinline__ void mma_load_x(const GemvParams& p, const View& v, i
         }
 }
 
-// The rest of the setup: the norms (PRO_RMS, PRO_CONCAT) and the chunk
-// maxima, each combined over the R waves of a row through part, then the
-// 16-bit quantization into the B operands (bq), the bias factors (tx, which
-// carry the chunk's activation scale) and the scales (xs_lds).  The codes'
-// word of 8 features unpacks to the even features, then the odd ones, and
-// lanes 2k and 2k+1 hold that word's first and last four features, so one
-// quad exchange forms each operand word.  Ends with a block barrier.
-template <int PRO, int S, int R, int FMT = FMT_Q4>
-__device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, int mi, int sub, int lane,
-                                            XPieces<S, 8 / R>& xp, u32x4 (*bq)[2][kWave],
-                                            float (*tx)[kMmaCols], float (*xs_lds)[4], float (*part)[4][R]) {
+// The rest of the setup: the norms (PRO_RMS, PRO_CONCAT) and the row maximum,
+// each combined over the R waves of a row through part, then the B operands
+// (bq), the group sums (tx, column 3 mi of each group) and the scale-back
+// factors (unsc).  Ends with a block barrier.
+template <int FMT, int PRO, int S, int R>
+__device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, int mi, int sub, int lane,
+                                          XPieces<S, 8 / R>& xp, u32x4* bq, float (*tx)[kMmaCols], float* unsc,
+                                          float (*part)[4][R]) {
     constexpr int NI = 8 / R;
     static_assert(FMT == FMT_Q4 || S == 1, "8-bit operands cover one chunk");
     const bool live = mi < p.m;
@@ -879,16 +715,16 @@ __device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, 
         if constexpr (PRO == PRO_CONCAT) ss1 = wave_sum(ss1);
         if constexpr (R > 1) {
             if (lane == 0) {
-                part[S][mi][sub] = ss0;
-                part[S + 1][mi][sub] = ss1;
+                part[0][mi][sub] = ss0;
+                part[1][mi][sub] = ss1;
             }
             __syncthreads();
             ss0 = 0.0f;
             ss1 = 0.0f;
 #pragma unroll
             for (int q = 0; q < R; ++q) {
-                ss0 += part[S][mi][q];
-                ss1 += part[S + 1][mi][q];
+                ss0 += part[0][mi][q];
+                ss1 += part[1][mi][q];
             }
         }
         const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
@@ -909,99 +745,135 @@ __device__ __forceinline__ void mma_quant_x(const GemvParams& p, const View& v, 
                 }
         }
     }
-    float am[S];
+    float am = 0.0f;
 #pragma unroll
-    for (int c = 0; c < S; ++c) {
-        float a = 0.0f;
+    for (int c = 0; c < S; ++c)
 #pragma unroll
         for (int ii = 0; ii < NI; ++ii) {
             const float4 x = xp.x[c][ii];
-            a = fmaxf(a, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+            am = fmaxf(am, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
         }
-        am[c] = wave_max(a);
-        if constexpr (R > 1)
-            if (lane == 0) part[c][mi][sub] = am[c];
-    }
+    am = wave_max(am);
     if constexpr (R > 1) {
+        if (lane == 0) part[2][mi][sub] = am;
         __syncthreads();
+        am = part[2][mi][0];
 #pragma unroll
-        for (int c = 0; c < S; ++c) {
-            float a = part[c][mi][0];
-#pragma unroll
-            for (int q = 1; q < R; ++q) a = fmaxf(a, part[c][mi][q]);
-            am[c] = a;
-        }
+        for (int q = 1; q < R; ++q) am = fmaxf(am, part[2][mi][q]);
     }
+    int e = 0;
+    (void)frexpf(am, &e);  // am = m 2^e with m in [0.5, 1); e = 0 for am = 0
+    const float sc = ldexpf(1.0f, 15 - e);
+    if (sub == 0 && lane == 0) unsc[mi] = ldexpf(1.0f, 9 + e);
     const bool odd = lane & 1;
-    const int wp = (lane >> 2) & 1, word = lane & 3;
-    const unsigned sel_h = odd ? 0x01000504u : 0x05040100u;
-    const unsigned sel_l = odd ? 0x03020706u : 0x07060302u;
 #pragma unroll
-    for (int c = 0; c < S; ++c) {
-        const float inv_q = am[c] > 0.0f ? kQMax / am[c] : 0.0f;
-        const float x_s = am[c] / kQMax;
+    for (int c = 0; c < S; ++c)
 #pragma unroll
         for (int ii = 0; ii < NI; ++ii) {
-            const float4 x = xp.x[c][ii];
-            const unsigned b0 = q_bits(x.x, inv_q), b1 = q_bits(x.y, inv_q), b2 = q_bits(x.z, inv_q),
-                           b3 = q_bits(x.w, inv_q);
-            if constexpr (FMT == FMT_Q8) {
-                // (hi 0, hi 1, lo 0, lo 1) and the same of 2, 3, then the hi
-                // word and the lo word of the lane's four features
-                const unsigned p01 = __builtin_amdgcn_perm(b1, b0, 0x04000501u);
-                const unsigned p23 = __builtin_amdgcn_perm(b3, b2, 0x04000501u);
-                const unsigned hw = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-                const unsigned lw = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;
-                const int tq = 4 * (sub * NI + ii) + (lane >> 4);  // MFMA of features 256 i + 4 lane ..
-                const int hq = (lane >> 2) & 3, par = hq >> 1;     // quarter, group parity
-                unsigned* slot = reinterpret_cast<unsigned*>(&bq[tq >> 1][tq & 1][0]) + (lane & 3);
-                slot[4 * (2 * mi + 8 * par + 16 * hq)] = hw;
-                slot[4 * (2 * mi + 1 + 8 * par + 16 * hq)] = lw;
-                slot[4 * (2 * mi + 8 * (1 - par) + 16 * hq)] = 0u;
-                slot[4 * (2 * mi + 1 + 8 * (1 - par) + 16 * hq)] = 0u;
-                continue;
-            }
-            unsigned qsum = (b0 + b1) + (b2 + b3);
-            // bytes (hi of 0, hi of 2, lo of 0, lo of 2) and the same of 1, 3;
-            // the even lane keeps the first and gives the second, the odd the reverse
-            const unsigned p02 = __builtin_amdgcn_perm(b2, b0, 0x04000501u);
-            const unsigned p13 = __builtin_amdgcn_perm(b3, b1, 0x04000501u);
-            const unsigned keep = odd ? p13 : p02;
-            const unsigned got = (unsigned)dpp_partner<1>((int)(odd ? p02 : p13));
-            const unsigned hw = __builtin_amdgcn_perm(got, keep, sel_h);
-            const unsigned lw = __builtin_amdgcn_perm(got, keep, sel_l) ^ 0x80808080u;
-            const int gl = 8 * (sub * NI + ii) + (lane >> 3);  // group within the chunk
-            const int t = 16 * c + (gl >> 2), pp = (gl >> 1) & 1, par = gl & 1, hq = 2 * wp + par;
-            unsigned* slot = reinterpret_cast<unsigned*>(&bq[t][pp][0]) + word;
-            slot[4 * (2 * mi + 8 * par + 16 * hq)] = hw;
-            slot[4 * (2 * mi + 1 + 8 * par + 16 * hq)] = lw;
-            slot[4 * (2 * mi + 8 * (1 - par) + 16 * hq)] = 0u;
-            slot[4 * (2 * mi + 1 + 8 * (1 - par) + 16 * hq)] = 0u;
-            qsum += (unsigned)dpp_partner<1>((int)qsum);
-            qsum += (unsigned)dpp_partner<2>((int)qsum);
-            qsum += (unsigned)dpp_partner<4>((int)qsum);  // the group's eight lanes
-            const int qs = (int)(qsum - 32u * kQBiasBits);
-            const int k8 = lane & 7;
-            if (k8 < 4) {
-                // the bias factor carries the chunk's activation scale (the sum is exact)
-                const int col = k8 == 0 ? 2 * mi : (k8 == 1 ? 2 * mi + 1 : 8 + 2 * mi + (k8 - 2));
-                tx[64 * c + gl][col] = k8 == 0 ? (float)qs * x_s : 0.0f;
+            const float4 x4 = xp.x[c][ii];
+            const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+            const int gg = 64 * c + 8 * (sub * NI + ii) + (lane >> 3);  // group (all chunks)
+            // the group's sum over its eight lanes
+            float gs = (xv[0] + xv[1]) + (xv[2] + xv[3]);
+            gs += dpp_partner<1>(gs);
+            gs += dpp_partner<2>(gs);
+            gs += dpp_partner<4>(gs);
+            if ((lane & 7) < 3) tx[gg][3 * mi + (lane & 7)] = (lane & 7) == 0 ? gs : 0.0f;
+            u32x4* grp = bq + gg * kBGroup;
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                unsigned hb[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // term t of v = x 2^(15-e) (4-bit: features on 16c halves
+                    // carry 1/16): hi is v on the grid 16 (1 for the 1/16
+                    // features), so every hi product lies on one grid and the
+                    // MFMA sums them exactly; mid and lo are the f16 remainder
+                    const bool sixteenth = FMT == FMT_Q4 && (q & 1);
+                    const float v = xv[q] * sc * (sixteenth ? 0.0625f : 1.0f);
+                    const float step = sixteenth ? 1.0f : 16.0f;
+                    const float hi = rintf(v * (1.0f / step)) * step;  // |hi / step| <= 2^11: exact in f16
+                    const float r1 = v - hi;
+                    const _Float16 h1 = (_Float16)r1;
+                    const float r2 = r1 - (float)h1;
+                    hb[q] = half_bits(t == 0 ? hi : (t == 1 ? (float)h1 : r2));
+                }
+                const int colt = 3 * mi + t;
+                if constexpr (FMT == FMT_Q4) {
+                    // word (lane % 8) / 2 of the group, features 4 (lane % 2) ..;
+                    // halves pair i of the word is (feature i, feature 4 + i): the
+                    // even lane builds pairs 0, 1 and the odd lane pairs 2, 3
+                    const unsigned send = odd ? (hb[0] | (hb[1] << 16)) : (hb[2] | (hb[3] << 16));
+                    const unsigned got = (unsigned)dpp_partner<1>((int)send);
+                    unsigned r0, r1;
+                    if (odd) {
+                        r0 = (got & 0xFFFFu) | (hb[2] << 16);
+                        r1 = (got >> 16) | (hb[3] << 16);
+                    } else {
+                        r0 = hb[0] | (got << 16);
+                        r1 = hb[1] | (got & 0xFFFF0000u);
+                    }
+                    unsigned* dst = reinterpret_cast<unsigned*>(grp + ((lane & 7) >> 1) * kBCols + colt) + 2 * odd;
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(r0, r1);
+                } else {
+                    // 8-bit word lane % 8 of the group sits in k-slot rho(word / 2),
+                    // halves 4 (word % 2) ..: pairs (feature 0, 2) and (1, 3)
+                    const int wd = lane & 7, hq = ((wd >> 1) & 1) * 2 + (wd >> 2);
+                    unsigned* dst = reinterpret_cast<unsigned*>(grp + hq * kBCols + colt) + 2 * (wd & 1);
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0] | (hb[2] << 16), hb[1] | (hb[3] << 16));
+                }
             }
         }
-        if (sub == 0 && lane == 0) xs_lds[c][mi] = x_s;
-    }
     __syncthreads();
 }
 
+// A operands with centred codes: the f16 subnormal pairs shifted by an
+// exact packed f16 subtraction, 4-bit c - 8 (16 (c - 8) on the 16c halves)
+// and 8-bit c.  Centred, a group's product has no common part that the bias
+// would cancel later, so the matrix core's accumulation error stays at the
+// size of the result instead of the size of 8 sum(x) (4-bit) or 128 sum(x)
+// (8-bit).
+__device__ __forceinline__ unsigned sub_h2(unsigned r, unsigned k) {
+    return __builtin_bit_cast(unsigned, as_h2(r) - as_h2(k));
+}
+constexpr unsigned kHalves8 = 0x00080008u;    // (8, 8) x 2^-24
+constexpr unsigned kHalves128 = 0x00800080u;  // (128, 128) x 2^-24
+
+__device__ __forceinline__ h8_t q8_operand(unsigned wa, unsigned wb) {
+    const Q8Halves a = q8_halves(wa), b = q8_halves(wb);
+    return as_h8(sub_h2(a.r[0], kHalves128), sub_h2(a.r[1], kHalves128), sub_h2(b.r[0], kHalves128),
+                 sub_h2(b.r[1], kHalves128));
+}
+
+__device__ __forceinline__ h8_t q4_operand(unsigned w) {
+    const Q4Halves q = q4_halves(w);
+    return as_h8(sub_h2(q.r[0], kHalves8), sub_h2(q.r[1], kHalves128), sub_h2(q.r[2], kHalves8),
+                 sub_h2(q.r[3], kHalves128));
+}
+
+// Sum of a lane's column and the next two (the three terms of an activation
+// row land in the writer lane 3 mi).
+__device__ __forceinline__ float add_terms(float x) {
+    const float a = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x101, 0xF, 0xF, false));
+    const float b = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x102, 0xF, 0xF, false));
+    return x + a + b;
+}
+
+// The lm_head (argmax epilogue) at three or four rows, K = 2048: persistent,
+// one 8-wave block per compute unit; a wave takes 16-row units claimed from
+// its block's LDS counter.  The next unit's codes are requested register by
+// register as the current unit consumes them (past the last unit, and for
+// the first request, they go to unit 0, one small region that hits in L2,
+// which keeps the loads unconditional).
 template <int FMT, int PRO>
 __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p) {
     constexpr int R = kMaxWaves / 4;  // waves per activation row in the setup
     constexpr int NT = FMT == FMT_Q4 ? 16 : 32;  // 16-byte code loads per lane and unit
-    __shared__ u32x4 bq[16][2][kWave];              // 32 KB: B operands (load t, group pair)
-    __shared__ float tx[64][kMmaCols];              // 4 KB: sum of x^ per (group, column 2*row), else 0
+    __shared__ u32x4 bq[64 * kBGroup];               // 48 KB: B operands
+    __shared__ float tx[64][kMmaCols];               // 4 KB: group sums in column 3 mi (4-bit bias)
     __shared__ float stage[kMaxWaves][64 * kStage];  // 40 KB: each wave's scales, [group][row]
     __shared__ float part[3][4][R];
-    __shared__ float xs_lds[1][4];
+    __shared__ float unsc[4];
     __shared__ int claim_ctr;
 
     if (p.zero_words && blockIdx.x == 0)
@@ -1023,14 +895,12 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     ts.init(blockIdx.x, gridDim.x, NU, true, claim);
 
     const int j = lane & 15, h = lane >> 4;
-    const int mi_l = (j & 7) >> 1;
-    const bool lo_col = (j & 1) != 0;
-    const float colf = lo_col ? 1.0f : 256.0f;
-    const bool writer = j < 8 && !lo_col && mi_l < p.m;
+    const int mi_l = j / 3;
+    const bool writer = j < kBCols && j % 3 == 0 && mi_l < p.m;
+    const u32x4* bsrc = bq + h * kBCols + (j < kBCols ? j : j - 4);
     float* st = stage[wid];
     float best = -INFINITY;
     int best_i = INT_MAX;
-
 
     // unit u: rows 16 u .. 16 u + 15 of the one matrix
     auto row_ptrs = [&](int u, const char*& crow, const float*& srow, const float*& brow) {
@@ -1042,9 +912,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
     };
     u32x4 cw[NT];
     v4f_t sv[4], bv[4];
-    // Plain loads: a load reads one half of a 128-byte line of each of 16
-    // rows and the next load the other half, so the line is better kept in
-    // L2 than streamed past it (nontemporal loads measured 5-9% slower here).
+    // Plain loads: a 4-bit load reads one half of a 128-byte line of each of
+    // 16 rows and the next load the other half, so the line is better kept in
+    // L2 than streamed past it.
     auto load_codes = [&](const char* crow, int t) {
         cw[t] = *reinterpret_cast<const u32x4*>(crow + 64 * t);
     };
@@ -1057,16 +927,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         }
     };
 
-    // Software pipeline: the activations are requested first, then the first
-    // unit's weights, which arrive during the activation setup; the next
-    // unit's weights go out register by register as soon as the current unit
-    // has consumed them.
     XPieces<1, 8 / R> xp;
     mma_load_x<PRO, 1, 8 / R>(p, v, wid & 3, wid >> 2, lane, xp);
     int u = ts.next(claim);
     {
-        // unconditional (unit 0 stands in for none), so that the setup waits
-        // for the activations only and not for these requests as well
         const char* crow;
         const float *srow, *brow;
         row_ptrs(u >= 0 ? u : 0, crow, srow, brow);
@@ -1074,12 +938,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         for (int t = 0; t < NT; ++t) load_codes(crow, t);
         load_sb(srow, brow);
     }
-    mma_quant_x<PRO, 1, R, FMT>(p, v, wid & 3, wid >> 2, lane, xp, bq, tx, xs_lds, part);
-    const float colx = colf * xs_lds[0][mi_l];  // integer sums carry the activation scale here
+    mma_setup<FMT, PRO, 1, R>(p, v, wid & 3, wid >> 2, lane, xp, bq, tx, unsc, part);
+    const float cf = j < kBCols ? unsc[mi_l] : 0.0f;
     while (u >= 0) {
-        // the next unit's rows; past the last unit the requests still go out,
-        // to unit 0 (one small region every wave shares, so they hit in L2),
-        // which keeps the loads unconditional and the registers simple
         const int nu = ts.next(claim);
         const char* ncrow;
         const float *nsrow, *nbrow;
@@ -1096,97 +957,57 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
             for (int e = 0; e < 4; ++e) {
                 const int gg = 16 * t + 4 * h + e;
                 st[gg * kStage + j] = sv[t][e];
-                if constexpr (FMT == FMT_Q4) {
-                    const float tv = tx[gg][j];
-                    cb4[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[t][e], tv, cb4[e & 1], 0, 0, 0);
-                }
+                if constexpr (FMT == FMT_Q4)
+                    cb4[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(fmaf(8.0f, sv[t][e], bv[t][e]), tx[gg][j],
+                                                                      cb4[e & 1], 0, 0, 0);
             }
         }
         load_sb(nsrow, nbrow);
         __builtin_amdgcn_wave_barrier();
 
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (FMT == FMT_Q8) {
-            // one MFMA per load, kTB8 at a time
-            constexpr int kTB8 = 4;
+        const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        auto group = [&](const h8_t& A, int gg) {
+            const h8_t B = __builtin_bit_cast(h8_t, bsrc[gg * kBGroup]);
+            const v4f_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zero, 0, 0, 0);
+            const float4 s4 = *reinterpret_cast<const float4*>(&st[gg * kStage + 4 * h]);
+            acc[0] = fmaf(s4.x, D[0], acc[0]);
+            acc[1] = fmaf(s4.y, D[1], acc[1]);
+            acc[2] = fmaf(s4.z, D[2], acc[2]);
+            acc[3] = fmaf(s4.w, D[3], acc[3]);
+        };
+        if constexpr (FMT == FMT_Q4) {
+            // load t: lane quarter h holds group 4 t + h; after the transpose
+            // word i is word h of group 4 t + i
 #pragma unroll
-            for (int t0 = 0; t0 < NT; t0 += kTB8) {
-                v4i_t D[kTB8];
-#pragma unroll
-                for (int dt = 0; dt < kTB8; ++dt) {
-                    const int t = t0 + dt;
-                    const u32x4 bb = bq[t >> 1][t & 1][lane];
-                    const v4i_t A = {(int)cw[t].x, (int)cw[t].y, (int)cw[t].z, (int)cw[t].w};
-                    const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
-                    const v4i_t zero = {0, 0, 0, 0};
-                    D[dt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
-                }
-#pragma unroll
-                for (int dt = 0; dt < kTB8; ++dt) {
-                    const int gg = 2 * (t0 + dt) + (j >> 3);
-                    const float4 s4 = *reinterpret_cast<const float4*>(&st[gg * kStage + 4 * h]);
-                    acc[0] = fmaf(s4.x, (float)D[dt][0], acc[0]);
-                    acc[1] = fmaf(s4.y, (float)D[dt][1], acc[1]);
-                    acc[2] = fmaf(s4.z, (float)D[dt][2], acc[2]);
-                    acc[3] = fmaf(s4.w, (float)D[dt][3], acc[3]);
-                }
-#pragma unroll
-                for (int dt = 0; dt < kTB8; ++dt) load_codes(ncrow, t0 + dt);
+            for (int t = 0; t < NT; ++t) {
+                unsigned w0 = cw[t].x, w1 = cw[t].y, w2 = cw[t].z, w3 = cw[t].w;
+                quarter_transpose(w0, w1, w2, w3);
+                load_codes(ncrow, t);  // the registers are free: the next unit's request
+                group(q4_operand(w0), 4 * t);
+                group(q4_operand(w1), 4 * t + 1);
+                group(q4_operand(w2), 4 * t + 2);
+                group(q4_operand(w3), 4 * t + 3);
             }
         } else {
-            // integer products, kTB loads (2 kTB MFMAs) at a time
-            constexpr int kTB = 2;
+            // load t: lane quarter h holds bytes 16 h .. of the group pair
+            // 2 t, 2 t + 1 (quarters 0, 1 the first group); one swap gives each
+            // quarter two words of both
 #pragma unroll
-            for (int t0 = 0; t0 < 16; t0 += kTB) {
-                v4i_t A[kTB][2];
-#pragma unroll
-                for (int dt = 0; dt < kTB; ++dt) {
-                    const int t = t0 + dt;
-                    unsigned w0 = cw[t].x, w1 = cw[t].y, w2 = cw[t].z, w3 = cw[t].w;
-                    perm32_swap(w0, w2);
-                    perm32_swap(w1, w3);
-                    const unsigned M4 = 0x0F0F0F0Fu;
-                    A[dt][0] = (v4i_t){(int)(w0 & M4), (int)((w0 >> 4) & M4), (int)(w1 & M4), (int)((w1 >> 4) & M4)};
-                    A[dt][1] = (v4i_t){(int)(w2 & M4), (int)((w2 >> 4) & M4), (int)(w3 & M4), (int)((w3 >> 4) & M4)};
-                }
-                v4i_t D[kTB][2];
-#pragma unroll
-                for (int dt = 0; dt < kTB; ++dt)
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const u32x4 bb = bq[t0 + dt][pp][lane];
-                        const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
-                        const v4i_t zero = {0, 0, 0, 0};
-                        D[dt][pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[dt][pp], B, zero, 0, 0, 0);
-                    }
-#pragma unroll
-                for (int dt = 0; dt < kTB; ++dt)
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const int gg = 4 * (t0 + dt) + 2 * pp + (j >> 3);
-                        const float4 s4 = *reinterpret_cast<const float4*>(&st[gg * kStage + 4 * h]);
-                        acc[0] = fmaf(s4.x, (float)D[dt][pp][0], acc[0]);
-                        acc[1] = fmaf(s4.y, (float)D[dt][pp][1], acc[1]);
-                        acc[2] = fmaf(s4.z, (float)D[dt][pp][2], acc[2]);
-                        acc[3] = fmaf(s4.w, (float)D[dt][pp][3], acc[3]);
-                    }
-                // the registers of loads t0 .. t0+kTB-1 are free: request the
-                // next unit's
-#pragma unroll
-                for (int dt = 0; dt < kTB; ++dt) load_codes(ncrow, t0 + dt);
+            for (int t = 0; t < NT; ++t) {
+                unsigned w0 = cw[t].x, w1 = cw[t].y, w2 = cw[t].z, w3 = cw[t].w;
+                perm32_swap(w0, w2);
+                perm32_swap(w1, w3);
+                load_codes(ncrow, t);
+                group(q8_operand(w0, w1), 2 * t);
+                group(q8_operand(w2, w3), 2 * t + 1);
             }
         }
         __builtin_amdgcn_wave_barrier();
-        v4f_t cb = cb4[0] + cb4[1];
-        // fold: group halves (lanes j, j^8), then hi and lo (lanes 2i, 2i+1)
+        const v4f_t cb = cb4[0] + cb4[1];
         float res[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x = fmaf(acc[r], colx, cb[r]);
-            x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
-            x += dpp_partner<1>(x);
-            res[r] = x;
-        }
+        for (int r = 0; r < 4; ++r) res[r] = add_terms(fmaf(acc[r], cf, cb[r]));
         if (writer) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1223,33 +1044,30 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
 
 // ---------------------------------------------------------------------------
 // Matrix-core GEMV with the K range split over a block's W waves, for the
-// projections that are not persistent: one block per unit (16 weight rows,
-// or 8 output rows of the SwiGLU pair), K = 2048 S with S <= 3.  A block per
-// unit puts many more compute units to work than a wave per unit, and each
-// wave's share (16 S / W loads) is short; with W = 16 every SIMD holds four
-// waves, which hides the latency of both the activation setup and the loop.
-// In the setup, the W / 4 waves of activation row w % 4 split each chunk's
-// features; the norms and chunk maxima meet in LDS.  The waves' partial sums
-// meet in LDS at the end, and wave r < 4 folds and stores register r.
-// Operand layout and arithmetic are those of k_gemv_mma; the activation
-// scale of each chunk is applied when a wave's loads cross into the next
-// chunk (and folded into the bias factors in LDS).
+// 4-bit projections that are not persistent: one block per unit (16 weight
+// rows, or 8 output rows of the SwiGLU pair), K = 2048 S with S <= 2.  A
+// block per unit puts many more compute units to work than a wave per unit,
+// and each wave's share (16 S / W loads of four groups) is short; with W = 16
+// every SIMD holds four waves, which hides the latency of both the
+// activation setup and the loop.  The waves' partial sums meet in LDS at the
+// end, and wave r < 4 folds and stores register r.  Operands and arithmetic
+// are those of k_gemv_mma.
 // ---------------------------------------------------------------------------
 template <int PRO, int EPI, int S, int W>
 __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
-    constexpr int R = W / 4;   // waves per activation row in the setup
-    constexpr int NI = 8 / R;  // 1 KB pieces of each chunk per wave in the setup
-    constexpr int T = 16 * S;  // loads (4 groups x 16 rows each) over K
-    constexpr int TW = T / W;  // loads per wave
+    constexpr int R = W / 4;    // waves per activation row in the setup
+    constexpr int NI = 8 / R;   // 1 KB pieces of each chunk per wave in the setup
+    constexpr int T = 16 * S;   // loads (4 groups x 16 rows each) over K
+    constexpr int TW = T / W;   // loads per wave
     constexpr int GW = 4 * TW;  // groups per wave
     constexpr int NE = GW / 4;  // groups per lane quarter
     static_assert(T % W == 0 && 8 % R == 0, "wave split");
-    __shared__ u32x4 bq[T][2][kWave];        // B operands, 32 KB per chunk
-    __shared__ float tx[64 * S][kMmaCols];   // bias factors x xs, 4 KB per chunk
-    __shared__ float stage[W][GW * kStage];  // each wave's scales, [group][row]
-    __shared__ float red[W][4][kWave];       // the waves' partial sums
-    __shared__ float part[S + 2][4][R];      // setup partials: chunk maxima, then squares per segment
-    __shared__ float xs_lds[S][4];
+    __shared__ u32x4 bq[64 * S * kBGroup];    // B operands, 48 KB per chunk
+    __shared__ float tx[64 * S][kMmaCols];    // group sums, 4 KB per chunk
+    __shared__ float stage[W][GW * kStage];   // each wave's scales, [group][row]
+    __shared__ float red[W][4][kWave];        // the waves' partial sums
+    __shared__ float part[3][4][R];
+    __shared__ float unsc[4];
 
     if (p.zero_words && blockIdx.x == 0)
         for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
@@ -1266,9 +1084,6 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
 
     // ---- this wave's weights
     const int j = lane & 15, h = lane >> 4;
-    const int mi_l = (j & 7) >> 1;
-    const bool lo_col = (j & 1) != 0;
-    const float colf = lo_col ? 1.0f : 256.0f;
     constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
     int row = u * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
     row = row < v.N ? row : v.N - 1;
@@ -1291,8 +1106,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
                                                        in2 * v.db2) + (int64_t)lr * v.G + g0 + NE * h;
     u32x4 cw[TW];
 #pragma unroll
-    for (int i = 0; i < TW; ++i)
-        cw[i] = *reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i));  // plain, as in k_gemv_mma
+    for (int i = 0; i < TW; ++i) cw[i] = *reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i));
     float sv[NE], bv[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -1300,64 +1114,54 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
         bv[e] = __builtin_nontemporal_load(brow + e);
     }
 
-    mma_quant_x<PRO, S, R>(p, v, mi, sub, lane, xp, bq, tx, xs_lds, part);
+    mma_setup<FMT_Q4, PRO, S, R>(p, v, mi, sub, lane, xp, bq, tx, unsc, part);
 
-    // ---- bias sums and this wave's scale stage
+    // ---- bias sums and this wave's scale stage (lane quarter h holds the
+    // scales of groups g0 + NE h .. of its row)
     float* st = stage[wid];
     v4f_t cb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         const int gl = NE * h + e;  // group within the wave's share
         st[gl * kStage + j] = sv[e];
-        cb = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], tx[g0 + gl][j], cb, 0, 0, 0);
+        cb = __builtin_amdgcn_mfma_f32_16x16x4f32(fmaf(8.0f, sv[e], bv[e]), tx[g0 + gl][j], cb, 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- integer products
-    float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- products
+    const u32x4* bsrc = bq + h * kBCols + (j < kBCols ? j : j - 4);
+    const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
         const int t = t0 + i;
-        unsigned w0 = cw[i].x, w1 = cw[i].y, w2 = cw[i].z, w3 = cw[i].w;
-        perm32_swap(w0, w2);
-        perm32_swap(w1, w3);
-        const unsigned M4 = 0x0F0F0F0Fu;
+        unsigned w[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+        quarter_transpose(w[0], w[1], w[2], w[3]);
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            const unsigned a = pp ? w2 : w0, b = pp ? w3 : w1;
-            const v4i_t A = {(int)(a & M4), (int)((a >> 4) & M4), (int)(b & M4), (int)((b >> 4) & M4)};
-            const u32x4 bb = bq[t][pp][lane];
-            const v4i_t B = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
-            const v4i_t zero = {0, 0, 0, 0};
-            const v4i_t D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
-            const float4 s4 = *reinterpret_cast<const float4*>(&st[(4 * i + 2 * pp + (j >> 3)) * kStage + 4 * h]);
-            acc[0] = fmaf(s4.x, (float)D[0], acc[0]);
-            acc[1] = fmaf(s4.y, (float)D[1], acc[1]);
-            acc[2] = fmaf(s4.z, (float)D[2], acc[2]);
-            acc[3] = fmaf(s4.w, (float)D[3], acc[3]);
-        }
-        if (((t + 1) & 15) == 0 || i == TW - 1) {  // end of a chunk or of the share: apply its scale
-            const float xs_c = xs_lds[t >> 4][mi_l];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                tot[r] = fmaf(acc[r], xs_c, tot[r]);
-                acc[r] = 0.0f;
-            }
+        for (int q = 0; q < 4; ++q) {
+            const h8_t B = __builtin_bit_cast(h8_t, bsrc[(4 * t + q) * kBGroup]);
+            const v4f_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_operand(w[q]), B, zero, 0, 0, 0);
+            const float4 s4 = *reinterpret_cast<const float4*>(&st[(4 * i + q) * kStage + 4 * h]);
+            acc[0] = fmaf(s4.x, D[0], acc[0]);
+            acc[1] = fmaf(s4.y, D[1], acc[1]);
+            acc[2] = fmaf(s4.z, D[2], acc[2]);
+            acc[3] = fmaf(s4.w, D[3], acc[3]);
         }
     }
+    const float cf = j < kBCols ? unsc[j / 3] : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wid][r][lane] = fmaf(tot[r], colf, cb[r]);
+    for (int r = 0; r < 4; ++r) red[wid][r][lane] = fmaf(acc[r], cf, cb[r]);
     __syncthreads();
 
-    // ---- wave r < 4 sums, folds and stores register r
+    // ---- wave r < 4 sums, adds the terms and stores register r
     if (wid >= 4) return;
     const int r = wid;
     float x = 0.0f;
 #pragma unroll
     for (int q = 0; q < W; ++q) x += red[q][r][lane];
-    x += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
-    x += dpp_partner<1>(x);
-    const bool writer = j < 8 && !lo_col && mi_l < p.m;
+    x = add_terms(x);
+    const int mi_l = j / 3;
+    const bool writer = j < kBCols && j % 3 == 0 && mi_l < p.m;
     if constexpr (EPI == EPI_SWIGLU) {
         float lo, hi;
         swap_halves<32>(x, x, lo, hi);
@@ -1376,8 +1180,10 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     }
 }
 
-// Dequantize through the GEMV fragment path (load_frag + nibble unpack): one
-// thread per (row, group).
+// Dequantize through the GEMV code path (load_frag + the code subnormals):
+// one thread per (row, group).  The value is fmaf(s, c, b) (4-bit) or s c
+// (8-bit), rounded once, computed as fmaf(s 2^24, c 2^-24, b) and
+// fmaf(s 2^24, (c + 128) 2^-24, -128 s).
 template <int FMT>
 __global__ void __launch_bounds__(256) k_dequant(const QMat w, int n, int K, float* out) {
     const int G = K / kGroup;
@@ -1389,21 +1195,32 @@ __global__ void __launch_bounds__(256) k_dequant(const QMat w, int n, int K, flo
     WFrag<FMT> f;
     load_frag(f, w.codes, w.scales, w.biases, row, G, g);
     if constexpr (FMT == FMT_Q4) {
-        const Nib nb = unpack_nibbles(f.c);
+        const unsigned c[4] = {f.c.x, f.c.y, f.c.z, f.c.w};
+        const float s24 = f.s * kTwo24;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            const Q4Halves q = q4_halves(c[j]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                dst[8 * j + 2 * t] = fmaf(f.s, (float)((nb.e[j] >> (8 * t)) & 0xFF), f.b);
-                dst[8 * j + 2 * t + 1] = fmaf(f.s, (float)((nb.o[j] >> (8 * t)) & 0xFF), f.b);
+            for (int k = 0; k < 8; ++k) {
+                const int slot = q4_slot(k);
+                const h2_t hh = as_h2(q.r[slot >> 1]);
+                const float cv = (float)((slot & 1) ? hh.y : hh.x) * q4_factor(k);
+                dst[8 * j + k] = fmaf(s24, cv, f.b);
             }
+        }
     } else {
-        const int c[8] = {(int)f.c0.x, (int)f.c0.y, (int)f.c0.z, (int)f.c0.w,
-                          (int)f.c1.x, (int)f.c1.y, (int)f.c1.z, (int)f.c1.w};
+        const unsigned c[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
+        const float s24 = f.s * kTwo24, off = -128.0f * f.s;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j) {
+            const Q8Halves q = q8_halves(c[j]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) dst[4 * j + t] = f.s * (float)(signed char)((c[j] >> (8 * t)) & 0xFF);
+            for (int k = 0; k < 4; ++k) {
+                const int slot = q8_slot(k);
+                const h2_t hh = as_h2(q.r[slot >> 1]);
+                dst[4 * j + k] = fmaf(s24, (float)((slot & 1) ? hh.y : hh.x), off);
+            }
+        }
     }
 }
 
@@ -1441,44 +1258,43 @@ GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int 
     return sh;
 }
 
+// The vector kernel for one or two rows.
 template <int FMT, int PRO, int EPI>
 static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int slots, hipStream_t st) {
     dim3 grid(sh.grid, slots), block(sh.block);
-    if (FMT == FMT_Q4 && inst_m(m) == 1 && (p.K + kChunk - 1) / kChunk > kRow1Chunks) return hipErrorInvalidValue;
-    switch (inst_m(m)) {
-        case 1: hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI>), grid, block, 0, st, p); break;
-        case 4: hipLaunchKernelGGL((k_gemv<FMT, 4, PRO, EPI>), grid, block, 0, st, p); break;
-        default: hipLaunchKernelGGL((k_gemv<FMT, 8, PRO, EPI>), grid, block, 0, st, p); break;
-    }
+    if (m < 1 || m > 2) return hipErrorInvalidValue;
+    if (m == 1 && (p.K + kChunk - 1) / kChunk > kRow1Chunks) return hipErrorInvalidValue;
+    if (m == 1)
+        hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
 // The lm_head (argmax epilogue) at three or four rows: persistent matrix-core
 // blocks.
 static bool mma_head_path(int fmt, int epi, int m, const GemvParams& p) {
-    return epi == EPI_ARGMAX && m >= 3 && m <= 4 && p.K == kChunk && p.nmat == 1 &&
-           !p.slot_expert;
+    (void)fmt;
+    return epi == EPI_ARGMAX && m >= 3 && m <= 4 && p.K == kChunk && p.nmat == 1 && !p.slot_expert;
 }
 
-// Store and SwiGLU GEMVs at three or four rows over 1-3 chunks that are not
-// persistent take the split-K matrix-core kernel, a block per unit.
+// 4-bit store and SwiGLU GEMVs at three or four rows over one or two chunks
+// that are not persistent take the split-K matrix-core kernel, a block per
+// unit (three chunks of B operands would not fit the LDS).
 static bool mma_sk_path(int fmt, int epi, int m, const GemvParams& p) {
     return fmt == FMT_Q4 && (epi == EPI_STORE || epi == EPI_SWIGLU) && m >= 3 && m <= 4 && !p.balance &&
-           !p.slot_expert && p.nmat <= 3 && (p.K == kChunk || p.K == 2 * kChunk || p.K == 3 * kChunk);
+           !p.slot_expert && p.nmat <= 3 && (p.K == kChunk || p.K == 2 * kChunk);
 }
 
 // 16 waves per block while the units fit one block per compute unit (every
-// SIMD then holds four of a block's waves), else 8 (three blocks of one
-// chunk fit a compute unit's LDS).
+// SIMD then holds four of a block's waves), else 8.
 template <int PRO, int EPI, int W>
 static void launch_mma_sk_w(const GemvParams& p, dim3 grid, hipStream_t st) {
     const dim3 block(W * kWave);
-    switch (p.K / kChunk) {
-        case 1: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W>), grid, block, 0, st, p); break;
-        default: hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 3, W>), grid, block, 0, st, p); break;
-    }
+    if (p.K == kChunk)
+        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W>), grid, block, 0, st, p);
 }
 
 template <int PRO, int EPI>
@@ -1501,10 +1317,30 @@ static hipError_t launch_mma_head(const GemvParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
-                       hipStream_t st) {
-    if (p.slot_expert) return hipErrorInvalidValue;  // slot launches use launch_gemv_slots
-    if (epi == EPI_ARGMAX && sh.grid > kHeadMaxBlocks) return hipErrorInvalidValue;
+// The parameters of a pass over activation rows r0 .. r0 + pm - 1 (rows are
+// independent in every prologue and epilogue, so a pass is the same GEMV on
+// offset row pointers; the argmax state is left at zero by every pass).
+static GemvParams row_pass(const GemvParams& p, int pro, int r0, int pm) {
+    GemvParams q = p;
+    q.m = pm;
+    if (r0 == 0) return q;
+    const int64_t xk = pro == PRO_CONCAT ? p.H : p.K;
+    if (q.x0) q.x0 += r0 * xk;
+    if (q.x1) q.x1 += (int64_t)r0 * p.H;
+    if (q.tokens) q.tokens += r0;
+    if (q.normed_out) q.normed_out += (int64_t)r0 * p.K;
+    if (q.y) q.y += (int64_t)r0 * p.N;
+    if (q.residual) q.residual += (int64_t)r0 * p.N;
+    if (q.rowscale) q.rowscale += r0;
+    if (q.logits) q.logits += (int64_t)r0 * p.N;
+    if (q.ids) q.ids += r0;
+    q.zero_words = nullptr;  // cleared by the first pass
+    q.zero_n = 0;
+    return q;
+}
+
+static hipError_t launch_pass(int fmt, int pro, int epi, int m, const GemvParams& p, int max_blocks,
+                              hipStream_t st) {
     if (mma_sk_path(fmt, epi, m, p)) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_mma_sk<PRO_PLAIN, EPI_STORE>(p, st);
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_mma_sk<PRO_RMS, EPI_STORE>(p, st);
@@ -1514,6 +1350,15 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
     }
     if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS)
         return fmt == FMT_Q4 ? launch_mma_head<FMT_Q4, PRO_RMS>(p, st) : launch_mma_head<FMT_Q8, PRO_RMS>(p, st);
+    if (m > 2) return hipErrorInvalidValue;
+    const int waves = block_waves(fmt, epi, m);
+    int maxb = max_blocks;
+    if (epi == EPI_ARGMAX) {
+        // persistent: one block of 8 waves per compute unit (two of 4 otherwise)
+        maxb = device_cu_count() * (kMaxWaves / waves);
+        if (maxb > kHeadMaxBlocks) maxb = kHeadMaxBlocks;
+    }
+    const GemvShape sh = gemv_shape(fmt, epi, m, p.N, p.K, maxb, waves);
     if (fmt == FMT_Q4) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_PLAIN, EPI_STORE>(m, p, sh, 1, st);
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_m<FMT_Q4, PRO_RMS, EPI_STORE>(m, p, sh, 1, st);
@@ -1529,9 +1374,33 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, co
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, const GemvShape& sh, int max_slots,
+// Rows in passes: up to four on the matrix-core kernels, else up to two on
+// the vector kernel.
+hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, int max_blocks, hipStream_t st) {
+    if (p.slot_expert) return hipErrorInvalidValue;  // slot launches use launch_gemv_slots
+    for (int r0 = 0; r0 < m;) {
+        const int left = m - r0;
+        const int four = left < 4 ? left : 4;
+        GemvParams q = row_pass(p, pro, r0, four);
+        int pm = four;
+        if (!(four >= 3 && (mma_sk_path(fmt, epi, four, q) || mma_head_path(fmt, epi, four, q)))) {
+            pm = left < 2 ? left : 2;
+            q = row_pass(p, pro, r0, pm);
+        }
+        const hipError_t e = launch_pass(fmt, pro, epi, pm, q, max_blocks, st);
+        if (e != hipSuccess) return e;
+        r0 += pm;
+    }
+    return hipSuccess;
+}
+
+// MoE slots on the vector kernel (m <= 2; the MoE launcher runs larger row
+// sets in passes).
+hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, int max_blocks, int max_slots,
                              hipStream_t st) {
-    if (fmt != FMT_Q8 || !p.slot_expert) return hipErrorInvalidValue;
+    if (fmt != FMT_Q8 || !p.slot_expert || m < 1 || m > 2) return hipErrorInvalidValue;
+    const int N = p.N > p.N_sh ? p.N : p.N_sh, K = p.K > p.K_sh ? p.K : p.K_sh;
+    const GemvShape sh = gemv_shape(fmt, epi, m, N, K, max_blocks, block_waves(fmt, epi, m));
     if (epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, max_slots, st);
     if (epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE>(m, p, sh, max_slots, st);
     return hipErrorInvalidValue;

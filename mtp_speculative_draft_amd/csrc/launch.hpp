@@ -81,18 +81,14 @@ struct GemvParams {
     int64_t x_slot, y_slot, rs_slot;
 };
 
-// Weight rows a wave handles per loop iteration: R*M*P partial sums per lane
-// (P = 2 for the SwiGLU pair), at most kGemvVals, and at most kGemvRows rows.
-constexpr int kGemvRows = 8;
-constexpr int kGemvVals = 32;
-// One activation row with a single matrix takes 4 rows per wave: for the
-// small projections that doubles the blocks in flight, which shortens them.
-constexpr int kRowsM1 = 4;    // M = 1, one matrix, store epilogue
-constexpr int kRowsM1P2 = 8;  // M = 1, SwiGLU pair
+// Weight rows a wave handles per loop iteration (the vector kernel, one or
+// two activation rows): one row of a single matrix takes 4 rows per wave
+// (for the small projections that doubles the blocks in flight, which
+// shortens them), the SwiGLU pair 8; two rows keep 8 partial sums per lane.
+constexpr int kRowsM1 = 4;    // M = 1, one matrix
+constexpr int kRowsM1P2 = 4;  // M = 1, SwiGLU pair
 __host__ __device__ constexpr int gemv_rows(int M, int P, int epi) {
-    return (M == 1 && P == 1) ? (epi == EPI_ARGMAX ? 4 : kRowsM1)
-                              : ((M == 1 && P == 2) ? kRowsM1P2
-                                                    : ((kGemvVals / (M * P)) < kGemvRows ? (kGemvVals / (M * P)) : kGemvRows));
+    return (void)epi, (M == 1 ? (P == 1 ? kRowsM1 : kRowsM1P2) : (8 / (M * P) > 0 ? 8 / (M * P) : 1));
 }
 // Row count of the kernel instantiation that serves m activation rows.
 __host__ __device__ constexpr int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
@@ -102,12 +98,10 @@ constexpr int kHeadRows = 8;          // activation rows at most (the C ABI's MT
 constexpr int kHeadMaxBlocks = 1024;  // lm_head grid cap
 constexpr int kHeadStateBytes = (kHeadRows + 1) * kKeyStride * 8;
 constexpr int kMaxWaves = 8;
-// Waves per block.  4-bit GEMVs at two or four rows and the lm_head up to
-// four rows use 8: a block's activation setup (one (row, chunk) fragment per
-// wave) then spreads over twice the waves, and the lm_head's persistent
-// blocks take a whole compute unit each.  Everything else uses 4.
+// Waves per block of the vector kernel.  The 4-bit lm_head uses 8 (its
+// persistent blocks take a whole compute unit each); everything else 4.
 __host__ __device__ constexpr int block_waves(int fmt, int epi, int m) {
-    return (fmt == FMT_Q4 && ((epi == EPI_ARGMAX && m <= 4) || m == 2 || m == 4)) ? kMaxWaves : 4;
+    return (fmt == FMT_Q4 && epi == EPI_ARGMAX && m <= 4) ? kMaxWaves : 4;
 }
 
 struct GemvShape {
@@ -116,10 +110,13 @@ struct GemvShape {
 
 // Grid/block choice for a GEMV of N rows, K features (S chunks) at m rows.
 GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int waves = 4);
-hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, const GemvShape& sh,
+// Any m <= 8: the rows run in passes (up to four rows on the matrix-core
+// kernels, up to two on the vector kernel).  max_blocks caps the grid of the
+// non-persistent vector launches; the argmax epilogue is persistent.
+hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, int max_blocks,
                        hipStream_t stream);
-// MoE slot launch: grid.y = max_slots (blocks of unused slots exit at once).
-hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, const GemvShape& sh, int max_slots,
+// MoE slot launch (m <= 2): grid.y = max_slots (blocks of unused slots exit at once).
+hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, int max_blocks, int max_slots,
                              hipStream_t stream);
 hipError_t launch_dequant(int fmt, const QMat& w, int k, float* out, hipStream_t stream);
 int device_cu_count();

@@ -243,11 +243,11 @@ __global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
 // load instead of one row on a quarter of the lanes.  A "load-set" is those
 // RPL rows (for SwiGLU, the same RPL rows of gate and of up).
 //
-// Activations: the block quantizes its slot's m activation rows once, per
-// group of 32: x ~ xs*(256*hi + lo) with xs = max|x|/32512 of the group, so
-// no lane exchange is needed; the fragments pass through LDS to the lanes of
-// their group.  A row's group term is then (s*xs) * A with A the exact
-// integer dot of the codes with the quantized activations (v_dot4).
+// Activations: the block stages its slot's m activation rows once in LDS,
+// per (row, group of 32) the 32 f32 values and their sum; each lane reads the
+// fragments of its group into registers.  A row's group term is
+// s * (2^24 sum((c + 128) 2^-24 x) - 128 sum(x)) with the exact code
+// subnormals of q8_halves (see device.hpp).
 //
 // Work: a slot's load-sets are spread evenly over the waves of its
 // gridDim.x blocks and taken UB at a time (a batch); two batches are in
@@ -284,7 +284,7 @@ struct SlotGemv {
     float* gates_out;
 };
 
-constexpr int kFragWords = 20;  // hi[8], lo[8], xs, pad (16-byte multiple)
+constexpr int kFragWords = 36;  // 32 values, their sum, pad (16-byte multiple)
 
 template <int LG>
 __host__ __device__ constexpr int seg_step0() {
@@ -380,23 +380,31 @@ __device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane
 
 // Load-sets per batch; two batches are in flight per wave.
 template <int M>
-__host__ __device__ constexpr int slot_batch() { return M >= 8 ? 1 : 2; }
+__host__ __device__ constexpr int slot_batch() { return M >= 4 ? 1 : 2; }
 
-// One (row, group) activation fragment of the block's slot: 32 values
-// quantized with their own scale, written to LDS as hi[8], lo[8], xs.
+// One (row, group) activation fragment of the block's slot: the 32 values
+// and their sum, written to LDS.
 __device__ __forceinline__ void store_frag(unsigned* f, const float (&xv)[32]) {
-    float mx = 0.0f;
+    float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(xv[i]));
-    const float inv = mx > 0.0f ? kQMax / mx : 0.0f;
-    XFrag xf;
-    quantize_group<FMT_Q8>(xv, inv, 0.0f, xf);
-    uint4* f4 = reinterpret_cast<uint4*>(f);
-    f4[0] = make_uint4(xf.hi[0], xf.hi[1], xf.hi[2], xf.hi[3]);
-    f4[1] = make_uint4(xf.hi[4], xf.hi[5], xf.hi[6], xf.hi[7]);
-    f4[2] = make_uint4(xf.lo[0], xf.lo[1], xf.lo[2], xf.lo[3]);
-    f4[3] = make_uint4(xf.lo[4], xf.lo[5], xf.lo[6], xf.lo[7]);
-    f4[4] = make_uint4(__float_as_uint(mx / kQMax), 0u, 0u, 0u);
+    for (int i = 0; i < 32; ++i) sum += xv[i];
+    float4* f4 = reinterpret_cast<float4*>(f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f4[k] = make_float4(xv[4 * k], xv[4 * k + 1], xv[4 * k + 2], xv[4 * k + 3]);
+    f4[8] = make_float4(sum, 0.0f, 0.0f, 0.0f);
+}
+
+// The lane's fragment of an 8-bit row from a stored (row, group) fragment.
+__device__ __forceinline__ void read_frag(const unsigned* f, XFrag& xf) {
+    const float4* f4 = reinterpret_cast<const float4*>(f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float4 t = f4[k];
+        const float xv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xf.v[4 * k + q8_slot(q)] = xv[q];
+    }
+    xf.sum = -128.0f * f4[8].x;
 }
 
 template <int M, int EPI, int LG, int W>
@@ -498,17 +506,8 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     __syncthreads();
     if (j_begin >= j_end) return;
     XFrag xf[M];
-    float xs[M];
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-        const uint4* f4 = reinterpret_cast<const uint4*>(frag + (mi * LG + g) * kFragWords);
-        const uint4 a = f4[0], b = f4[1], c = f4[2], d = f4[3], x = f4[4];
-        xf[mi].hi[0] = a.x; xf[mi].hi[1] = a.y; xf[mi].hi[2] = a.z; xf[mi].hi[3] = a.w;
-        xf[mi].hi[4] = b.x; xf[mi].hi[5] = b.y; xf[mi].hi[6] = b.z; xf[mi].hi[7] = b.w;
-        xf[mi].lo[0] = c.x; xf[mi].lo[1] = c.y; xf[mi].lo[2] = c.z; xf[mi].lo[3] = c.w;
-        xf[mi].lo[4] = d.x; xf[mi].lo[5] = d.y; xf[mi].lo[6] = d.z; xf[mi].lo[7] = d.w;
-        xs[mi] = __uint_as_float(x.x);
-    }
+    for (int mi = 0; mi < M; ++mi) read_frag(frag + (mi * LG + g) * kFragWords, xf[mi]);
 
     const int base = seg_base<V, FIN, LG>(lane);
     const bool writer = (lane & (DUP - 1)) == 0;
@@ -521,7 +520,7 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
 #pragma unroll
             for (int i = 0; i < P; ++i)
 #pragma unroll
-                for (int mi = 0; mi < M; ++mi) v[(b * M + mi) * P + i] = dot_q8(wf[b][i], xf[mi]) * xs[mi];
+                for (int mi = 0; mi < M; ++mi) v[(b * M + mi) * P + i] = dot_q8(wf[b][i], xf[mi]);
     };
     auto finish = [&](float (&v)[V], int j0) {
         Butterfly<V, FIN, seg_step0<LG>()>::run(v, lane);
@@ -614,15 +613,19 @@ static hipError_t launch_slot(int epi, const SlotGemv& p, int max_slots, hipStre
         case 1: return epi == EPI_SWIGLU ? launch_slot_m<1, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<1, EPI_STORE>(p, max_slots, st);
         case 2: return epi == EPI_SWIGLU ? launch_slot_m<2, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<2, EPI_STORE>(p, max_slots, st);
         case 4: return epi == EPI_SWIGLU ? launch_slot_m<4, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<4, EPI_STORE>(p, max_slots, st);
-        default: return epi == EPI_SWIGLU ? launch_slot_m<8, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<8, EPI_STORE>(p, max_slots, st);
+        default: return hipErrorInvalidValue;  // launch_moe runs at most four rows per pass
     }
 }
 
-hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
+static bool moe_slot_path(const MoeParams& p);
+
+// One pass of the MoE over p.m rows (at most four on the slot kernel, two on
+// the generic path).
+static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
     hipLaunchKernelGGL(k_moe_router, dim3(p.E), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const bool slot_path = slot_groups_ok(p.H) && slot_groups_ok(p.inter) && (!p.sg.codes || p.sh_inter == p.inter);
+    const bool slot_path = moe_slot_path(p);
     if (!slot_path) {
         hipLaunchKernelGGL(k_moe_topk, dim3(1), dim3(512), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -709,8 +712,7 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
     g.x_slot = 0;
     g.y_slot = (int64_t)p.m * imax;
     g.rs_slot = p.m;
-    GemvShape sh = gemv_shape(FMT_Q8, EPI_SWIGLU, p.m, imax, p.H, 1 << 20);
-    if ((e = launch_gemv_slots(FMT_Q8, EPI_SWIGLU, p.m, g, sh, p.max_slots, st)) != hipSuccess) return e;
+    if ((e = launch_gemv_slots(FMT_Q8, EPI_SWIGLU, p.m, g, 1 << 20, p.max_slots, st)) != hipSuccess) return e;
 
     GemvParams d{};
     d.w[0] = p.de;
@@ -731,12 +733,36 @@ hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
     d.K_sh = p.sh_inter;
     d.x_slot = (int64_t)p.m * imax;
     d.y_slot = (int64_t)p.m * p.H;
-    GemvShape shd = gemv_shape(FMT_Q8, EPI_STORE, p.m, p.H, imax, 1 << 20);
-    if ((e = launch_gemv_slots(FMT_Q8, EPI_STORE, p.m, d, shd, p.max_slots, st)) != hipSuccess) return e;
+    if ((e = launch_gemv_slots(FMT_Q8, EPI_STORE, p.m, d, 1 << 20, p.max_slots, st)) != hipSuccess) return e;
 
     const int64_t n = (int64_t)p.m * p.H;
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
     return hipGetLastError();
+}
+
+static bool moe_slot_path(const MoeParams& p) {
+    return slot_groups_ok(p.H) && slot_groups_ok(p.inter) && (!p.sg.codes || p.sh_inter == p.inter);
+}
+
+// Rows in passes (each a whole MoE over its rows, sharing the workspace's
+// slot tables, which every pass rebuilds): four rows per pass on the slot
+// kernel, two on the generic path.
+hipError_t launch_moe(const MoeParams& p, hipStream_t st) {
+    const int per = moe_slot_path(p) ? 4 : 2;
+    for (int r0 = 0; r0 < p.m; r0 += per) {
+        MoeParams q = p;
+        q.m = p.m - r0 < per ? p.m - r0 : per;
+        q.x += (int64_t)r0 * p.H;
+        q.f += (int64_t)r0 * p.H;
+        q.logits += (int64_t)r0 * p.E;
+        q.expert_ids += (int64_t)r0 * p.top_k;
+        q.gates += (int64_t)r0 * p.top_k;
+        if (q.residual) q.residual += (int64_t)r0 * p.H;
+        q.y += (int64_t)r0 * p.H;
+        const hipError_t e = moe_pass(q, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace mtp
