@@ -11,16 +11,21 @@ Infinity Cache from serving repeated weight reads, R copies of the layer
 weights and of the KV caches are rotated (step i uses copy i % R).
 
 Printed: one JSON line with the weight-stream GB/s of the whole step
-(algorithmic bytes / time), draft steps/s and verify rows/s, the roofline of
-the dominant call (lm_head + argmax, timed with HIP events on its stream over the
-K launches of its timed region) and
-the oracle's CPU baseline.
+(algorithmic bytes / time of K steps launched back to back), per-step median
+and p10/p90, draft steps/s (3 / time of the K=3 chain captured in a HIP graph
+and replayed) and verify rows/s (4 / time of the captured m=4 pass), the same
+for the MoE draft layer, the roofline of the dominant kernel (lm_head + argmax
+at m=1: HIP events on its stream around K back-to-back launches), the measured
+read-stream ceiling of the box, single-op GPU times (calls captured in graphs),
+and the oracle's CPU baseline on one core and on all host cores.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes as C
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -67,16 +72,108 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=3, help="weight/cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ops", action="store_true", help="skip the single-op timings (GEMV, eh_proj, attention, catch-up, stack, 8-bit head, MoE)")
+    ap.add_argument("--no-ops", action="store_true", help="skip the single-op timings")
+    ap.add_argument("--no-moe", action="store_true", help="skip the MoE draft layer")
     ap.add_argument("--ops-only", action="store_true", help="only the single-op timings, for kernel traces")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline samples")
     ap.add_argument("--head-only", action="store_true",
-                    help="only the lm_head + argmax launches (m=1), for counter runs")
+                    help="only the lm_head + argmax launches, for counter runs")
+    ap.add_argument("--head-m", type=int, default=1, help="rows of the --head-only launches")
+    ap.add_argument("--head-q8", action="store_true", help="--head-only over the 8-bit lm_head")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only a plain device copy of 256 MiB, the reference for scaling byte counters")
     return ap.parse_args()
 
 
+# --------------------------------------------------------------------------
+# timing helpers
+# --------------------------------------------------------------------------
+def capture(torch, fn):
+    """A HIP graph of fn() (every libmtp call launches on torch's current
+    stream, which is the capture stream inside the context)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def replay_stats(torch, graphs, K, W, per_replay_units=1):
+    """Replays graphs round robin: W untimed, then K timed between two
+    synchronizations (the mean), then K with an event pair each (median,
+    p10, p90).  Times are ms per replay / per_replay_units."""
+    stream = torch.cuda.current_stream()
+    for i in range(W):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(K):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    mean = (time.perf_counter() - t) * 1e3 / K
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        evs[i][0].record(stream)
+        graphs[i % len(graphs)].replay()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs], dtype=np.float64)
+    u = float(per_replay_units)
+    return {"mean": mean / u, "median": float(np.median(ms)) / u, "p10": float(np.percentile(ms, 10)) / u,
+            "p90": float(np.percentile(ms, 90)) / u}
+
+
+def eager_region_us(torch, calls, n, W=3):
+    """Average launch duration of a call that is one kernel: n back-to-back
+    calls (fn(i)) on the stream between one event pair, / n.  (This is what
+    the roofline quotes: it agrees with the kernel trace's average duration;
+    the same launches replayed from a HIP graph measured several us longer
+    per launch for the persistent lm_head.)"""
+    for i in range(W):
+        calls(i)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(n):
+        calls(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return float(a.elapsed_time(b)) * 1e3 / n
+
+
+def graph_region_us(torch, calls, n, W=2):
+    """GPU time per call: n calls (fn(i), i = 0..n-1) captured in one graph,
+    replayed W times untimed, then once between an event pair on the stream;
+    the region / n (no host work between the launches)."""
+    for i in range(min(n, 4)):  # eager warm-up (lazy one-time setup, caches)
+        calls(i)
+    torch.cuda.synchronize()
+    g = capture(torch, lambda: [calls(i) for i in range(n)])
+    for _ in range(W):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = float(a.elapsed_time(b)) * 1e3 / n
+    del g
+    return us
+
+
+def r3(x):
+    return round(float(x), 3)
+
+
+def stats_ms(st):
+    return {k: round(v, 5) for k, v in st.items()}
+
+
+# --------------------------------------------------------------------------
+# small modes (counter runs)
+# --------------------------------------------------------------------------
 def copy_ref(torch, dev, reps=4):
     """torch's device copy of a 256 MiB f32 tensor: reads and writes 268,435,456 bytes per launch."""
     src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -87,19 +184,169 @@ def copy_ref(torch, dev, reps=4):
     print(json.dumps({"copy_ref_bytes_per_launch": src.numel() * 4, "launches": reps}), flush=True)
 
 
-def head_only(torch, mtp, synth, dev, reps):
-    """lm_head + argmax at m=1 over 3 rotated copies of a 151936 x 2048 4-bit weight."""
-    lm = synth.config2_head()[2]
-    copies = [mtp.DeviceQ4(lm, dev) for _ in range(3)]
+def head_only(torch, mtp, synth, dev, reps, m, q8):
+    """lm_head + argmax over 3 rotated copies of a 151936 x 2048 weight
+    (4-bit, or 8-bit with --head-q8), eager launches."""
+    if q8:
+        lm = synth.q8_weight(synth.rng(8), 1, 151936, 2048)
+        copies = [mtp.DeviceQ8(lm, dev) for _ in range(3)]
+        call = mtp.mtp_lmhead_argmax_q8
+        nbytes = 151936 * 2048 + 151936 * 64 * 4
+    else:
+        lm = synth.config2_head()[2]
+        copies = [mtp.DeviceQ4(lm, dev) for _ in range(3)]
+        call = mtp.mtp_lmhead_argmax
+        nbytes = copies[0].nbytes
     gam = torch.ones(lm.k, device=dev)
-    ws = torch.zeros(mtp.mtp_lmhead_workspace_size(lm.n, 1), dtype=torch.uint8, device=dev)
-    x = torch.randn((1, lm.k), device=dev)
+    ws = torch.zeros(mtp.mtp_lmhead_workspace_size(lm.n, m), dtype=torch.uint8, device=dev)
+    ids = torch.empty(m, dtype=torch.int32, device=dev)
+    x = torch.randn((m, lm.k), device=dev)
     for i in range(reps):
-        mtp.mtp_lmhead_argmax(x, gam, 1e-6, copies[i % 3], ws=ws)
+        call(x, gam, 1e-6, copies[i % 3], ids_out=ids, ws=ws)
     torch.cuda.synchronize()
-    print(json.dumps({"head_launches": reps, "bytes_per_launch": copies[0].nbytes}), flush=True)
+    print(json.dumps({"head_launches": reps, "rows": m, "bits": 8 if q8 else 4, "bytes_per_launch": nbytes}),
+          flush=True)
 
 
+# --------------------------------------------------------------------------
+# the measured read ceiling (plain read stream, libmtp_bench.so)
+# --------------------------------------------------------------------------
+def read_ceiling(torch, dev, nbytes, K):
+    """GB/s of a plain nontemporal read stream over nbytes, three rotated
+    buffers (past the Infinity Cache), K captured launches."""
+    path = os.path.join(ROOT, "mtp_speculative_draft_amd", "libmtp_bench.so")
+    if not os.path.exists(path):
+        return None
+    lib = C.CDLL(path)
+    lib.mtp_bench_read_stream.restype = C.c_int
+    lib.mtp_bench_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    nb = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(nb // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+    blocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(blocks, dtype=torch.float32, device=dev)
+
+    def call(i):
+        rc = lib.mtp_bench_read_stream(C.c_void_p(bufs[i % 3].data_ptr()), nb, C.c_void_p(out.data_ptr()), blocks,
+                                       C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"read stream launch failed: {rc}")
+
+    us = eager_region_us(torch, call, K)
+    del bufs
+    return {"GB/s": round(nb / us / 1e3, 1), "bytes": nb, "us": r3(us),
+            "kernel": "plain nontemporal float4 read stream (libmtp_bench.so), 3 rotated buffers, back-to-back "
+                      "launches between one event pair"}
+
+
+# --------------------------------------------------------------------------
+# draft steps (dense and MoE)
+# --------------------------------------------------------------------------
+def step_runner(torch, mtp, S, layers, caches, dev):
+    """Callables for the K=3 chain at m=1 and the m=4 verify over copy c."""
+    L = S.layer
+    H, L0 = L.hidden, S.cache_len
+    table = torch.from_numpy(S.table).to(dev)
+    e0 = torch.from_numpy(S.e0).to(dev)
+    e4 = e0.repeat(4, 1).contiguous()
+    hbuf = torch.empty((4, H), dtype=torch.float32, device=dev)
+    hbuf[0].copy_(torch.from_numpy(S.h0[0]).to(dev))
+    tok = torch.full((4,), -1, dtype=torch.int32, device=dev)
+    ids_v = torch.empty(4, dtype=torch.int32, device=dev)
+    hid_v = torch.empty((4, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(mtp.mtp_draft_step_workspace_size(layers[0], L0 + 3, 1),
+                         mtp.mtp_draft_step_workspace_size(layers[0], L0, 4)), dtype=torch.uint8, device=dev)
+    R = len(layers)
+
+    def chain(c):
+        dl = layers[c % R]
+        kc, vc = caches[c % R]
+        for k in range(3):
+            mtp.mtp_draft_step(dl, e0, tok[k:k + 1], table, hbuf[k:k + 1], kc, vc, L0 + k,
+                               ids_out=tok[k + 1:k + 2], hidden_out=hbuf[k + 1:k + 2], ws=ws)
+
+    def verify(c):
+        dl = layers[c % R]
+        kc, vc = caches[c % R]
+        mtp.mtp_draft_step(dl, e4, tok, table, hbuf, kc, vc, L0, ids_out=ids_v, hidden_out=hid_v, ws=ws)
+
+    def outputs():
+        torch.cuda.synchronize()
+        return tok.cpu().numpy().copy(), ids_v.cpu().numpy().copy(), hid_v.cpu().numpy().copy()
+
+    return chain, verify, outputs, table
+
+
+def eager_stats(torch, fn, K, W):
+    """fn(i) launched from the host: W untimed, K between two synchronizations
+    (the mean), then K with an event pair each on the stream (median, p10,
+    p90; the queue stays full, so these are device times)."""
+    for i in range(W):
+        fn(i)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(K):
+        fn(i)
+    torch.cuda.synchronize()
+    mean = (time.perf_counter() - t) * 1e3 / K
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs], dtype=np.float64)
+    return {"mean": mean, "median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+            "p90": float(np.percentile(ms, 90))}
+
+
+def time_steps(torch, chain, verify, outputs, R, K, W):
+    """Eager (host-launched) step timings, and graph-captured timings of the
+    chain, the verify and the whole step; the graph replays must reproduce
+    the eager outputs bit for bit."""
+    eager = eager_stats(torch, lambda i: (chain(i), verify(i)), K, W)
+    chain(0)
+    verify(0)
+    ref = outputs()
+    g_chain = [capture(torch, lambda c=c: chain(c)) for c in range(R)]
+    g_verify = [capture(torch, lambda c=c: verify(c)) for c in range(R)]
+    g_step = [capture(torch, lambda c=c: (chain(c), verify(c))) for c in range(R)]
+    g_step[0].replay()
+    got = outputs()
+    same = all(np.array_equal(a, b) for a, b in zip(ref, got))
+    st_step = replay_stats(torch, g_step, K, W)
+    st_chain = replay_stats(torch, g_chain, K, W)
+    st_verify = replay_stats(torch, g_verify, K, W)
+    del g_chain, g_verify, g_step
+    return eager, st_step, st_chain, st_verify, same, ref
+
+
+def moe_layer_bench(torch, mtp, synth, dev, K, W):
+    """The MoE draft layer at full size: the dense layer's attention, eh_proj
+    and lm_head (vocab 151936) with the routed 8-bit FFN (256 experts, top-8,
+    shared expert, intermediate 512) in place of the SwiGLU; K=3 chain at m=1
+    and verify at m=4 over a 4096-row cache, two rotated copies."""
+    S = synth.config4_step()
+    moe = synth.moe_inputs(synth.rng(30, 0), 1, hidden=2048, n_experts=256, inter=512, top_k=8, shared_inter=512)
+    R = 2
+    layers = [mtp.DeviceLayer(S.layer, dev, moe=moe) for _ in range(R)]
+    caches = [(torch.from_numpy(S.k_cache).to(dev), torch.from_numpy(S.v_cache).to(dev)) for _ in range(R)]
+    chain, verify, outputs, _ = step_runner(torch, mtp, S, layers, caches, dev)
+    eager, st_step, st_chain, st_verify, same, _ = time_steps(torch, chain, verify, outputs, R, K, W)
+    out = {"workload": "MoE draft layer: config-4 attention/eh_proj/lm_head, routed 8-bit FFN 256 experts top-8 "
+                       "+ shared (inter 512); K=3 chain at m=1 + verify at m=4, cache 4096",
+           "graph_replay_equals_eager": bool(same),
+           "draft_steps_per_s": round(3.0 / (st_chain["mean"] * 1e-3), 1),
+           "verify_rows_per_s": round(4.0 / (st_verify["mean"] * 1e-3), 1),
+           "ms_chain3_graph": stats_ms(st_chain), "ms_verify4_graph": stats_ms(st_verify),
+           "ms_step_graph": stats_ms(st_step), "ms_step_eager": stats_ms(eager)}
+    del layers, caches
+    return out
+
+
+# --------------------------------------------------------------------------
+# main
+# --------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
@@ -118,7 +365,7 @@ def main():
     if args.copy_ref:
         return copy_ref(torch, dev)
     if args.head_only:
-        return head_only(torch, mtp, synth, dev, args.steps)
+        return head_only(torch, mtp, synth, dev, args.steps, args.head_m, args.head_q8)
     if args.ops_only:
         print(json.dumps({"ops": op_timings(torch, mtp, synth, dev, args.steps, args.warmup)}), flush=True)
         return
@@ -129,51 +376,14 @@ def main():
     R = max(1, args.copies)
     layers = [mtp.DeviceLayer(L, dev) for _ in range(R)]
     caches = [(torch.from_numpy(S.k_cache).to(dev), torch.from_numpy(S.v_cache).to(dev)) for _ in range(R)]
-    table = torch.from_numpy(S.table).to(dev)
-    e0 = torch.from_numpy(S.e0).to(dev)
-    e4 = e0.repeat(4, 1).contiguous()
-    h0 = torch.from_numpy(S.h0[0]).to(dev)
+    chain, verify, outputs, _ = step_runner(torch, mtp, S, layers, caches, dev)
     H, V, L0 = L.hidden, L.vocab, S.cache_len
-    hbuf = torch.empty((4, H), dtype=torch.float32, device=dev)
-    tok = torch.full((4,), -1, dtype=torch.int32, device=dev)
-    ids_v = torch.empty(4, dtype=torch.int32, device=dev)
-    hid_v = torch.empty((4, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(mtp.mtp_draft_step_workspace_size(layers[0], L0 + 3, 1),
-                         mtp.mtp_draft_step_workspace_size(layers[0], L0, 4)), dtype=torch.uint8, device=dev)
-    hbuf[0].copy_(h0)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    def chain(i):
-        dl = layers[i % R]
-        kc, vc = caches[i % R]
-        for k in range(3):
-            mtp.mtp_draft_step(dl, e0, tok[k:k + 1], table, hbuf[k:k + 1], kc, vc, L0 + k,
-                               ids_out=tok[k + 1:k + 2], hidden_out=hbuf[k + 1:k + 2], ws=ws)
-
-    def verify(i):
-        dl = layers[i % R]
-        kc, vc = caches[i % R]
-        mtp.mtp_draft_step(dl, e4, tok, table, hbuf, kc, vc, L0, ids_out=ids_v, hidden_out=hid_v, ws=ws)
-
-    def step(i):
-        chain(i)
-        verify(i)
-
-    def timed(fn, n, warm):
-        for i in range(warm):
-            fn(i)
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for i in range(n):
-            fn(i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t) / n
-
     K, W = args.steps, args.warmup
-    sec_step = timed(step, K, W)
-    sec_chain = timed(chain, K, W)
-    sec_verify = timed(verify, K, W)
+    eager, st_step, st_chain, st_verify, same, ref = time_steps(torch, chain, verify, outputs, R, K, W)
+    sec_step = eager["mean"] * 1e-3
 
     # algorithmic bytes: every weight byte once per call, the K/V rows read
     # (positions 0..cache_len+m-1, both heads, K and V) and the new rows written,
@@ -187,30 +397,25 @@ def main():
     step_bytes = sum(call_bytes(L0 + k, 1) for k in range(3)) + call_bytes(L0, 4)
     gbs = step_bytes / sec_step / 1e9
 
-    # dominant call: lm_head + final norm + argmax, events on its own stream
+    # dominant kernel: lm_head + final norm + argmax (one launch per call),
+    # K back-to-back launches over rotated copies between one event pair on
+    # its stream; the average launch duration is region / K
     lm_copies = [dl.q4["lm_head"] for dl in layers]
     gam = layers[0].gammas[4]
     hws = torch.zeros(mtp.mtp_lmhead_workspace_size(V, 4), dtype=torch.uint8, device=dev)
     ids1 = torch.empty(4, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    # one event pair around the K back-to-back launches of the timed region
-    # (rotated weight copies); the average launch duration is the region / K
-    head_ms = {}
+    head_us = {}
     for m in (1, 4):
         xm = torch.randn((m, H), device=dev)
-        for i in range(W):
-            mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m], ws=hws)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(K):
-            mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m], ws=hws)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        head_ms[m] = float(ev0.elapsed_time(ev1)) / K
+        head_us[m] = eager_region_us(
+            torch, lambda i, xm=xm, m=m: mtp.mtp_lmhead_argmax(xm, gam, 1e-6, lm_copies[i % R], ids_out=ids1[:m],
+                                                               ws=hws), K)
     lm_bytes = lm_copies[0].nbytes + 8 + H * 4  # weights + ids + gamma
     head_bytes_m1 = lm_bytes + 1 * H * 4
-    achieved = head_bytes_m1 / (head_ms[1] * 1e-3) / 1e9
+    achieved = head_bytes_m1 / (head_us[1] * 1e-6) / 1e9
+    del layers, caches
+    torch.cuda.empty_cache()
+    ceiling = read_ceiling(torch, dev, head_bytes_m1, K)
 
     result = {
         "metric": METRIC,
@@ -219,26 +424,36 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(sec_step * 1e3, 4),
+        "ms_per_step": round(eager["mean"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8-dot/f32",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": "dense MTP draft step: K=3 chain at m=1 (cache 4096->4099) + verify at m=4; hidden 2048, "
                         "16 q / 2 kv heads x 128, SwiGLU 6144, vocab 151936, 4-bit affine g32 weights, f32 KV",
             "hidden": H, "vocab": V, "cache_len": L0, "verify_rows": 4, "draft_chain": 3,
             "weight_copies_rotated": R,
+            "arithmetic": "f32 activations; codes enter exactly (f16 subnormals), products exact, f32 accumulation",
+            "timing": "steps launched from the host back to back (value, ms_per_step, ms_step_stats); the K=3 "
+                      "chain and the verify also captured in HIP graphs and replayed (draft_steps_per_s, "
+                      "verify_rows_per_s)",
         },
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "draft_steps_per_s": round(3.0 / sec_chain, 1),
-        "verify_rows_per_s": round(4.0 / sec_verify, 1),
-        "ms_chain3": round(sec_chain * 1e3, 4),
-        "ms_verify4": round(sec_verify * 1e3, 4),
+        "ms_step_stats": stats_ms(eager),
+        "ms_step_graph": stats_ms(st_step),
+        "graph_replay_equals_eager": bool(same),
+        "draft_steps_per_s": round(3.0 / (st_chain["mean"] * 1e-3), 1),
+        "verify_rows_per_s": round(4.0 / (st_verify["mean"] * 1e-3), 1),
+        "ms_chain3_graph": stats_ms(st_chain),
+        "ms_verify4_graph": stats_ms(st_verify),
         "step_bytes": int(step_bytes),
+        "chain_ids": ref[0][1:].tolist(),
+        "verify_ids": ref[1].tolist(),
         "roofline": {
-            "kernel": "mtp_lmhead_argmax (fused final RMSNorm + 4-bit lm_head GEMV + argmax), m=1",
+            "kernel": "mtp::k_gemv<0, 1, 1, 2> = mtp_lmhead_argmax (fused final RMSNorm + 4-bit lm_head GEMV + "
+                      "argmax), m=1",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -246,49 +461,42 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(),
             "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, see profiles/)",
-            "ms_per_launch_m1": round(head_ms[1], 5),
-            "ms_per_launch_m4": round(head_ms[4], 5),
+            "us_per_launch_m1": r3(head_us[1]),
+            "us_per_launch_m4": r3(head_us[4]),
             "bytes_per_launch_m1": int(head_bytes_m1),
+            "frac_of_measured_read_ceiling": (round(achieved / ceiling["GB/s"], 4) if ceiling else None),
         },
+        "read_ceiling": ceiling,
         "setup_s": round(setup_s, 1),
     }
-
+    if not args.no_moe:
+        torch.cuda.empty_cache()
+        result["moe_layer"] = moe_layer_bench(torch, mtp, synth, dev, K, W)
     if not args.no_ops:
-        del layers, caches, table
         torch.cuda.empty_cache()
         result["ops"] = op_timings(torch, mtp, synth, dev, K, W)
-
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(S, step_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def event_us(torch, dev, fn, n, warm):
-    """Mean duration of fn(i) in microseconds, from HIP events recorded on the
-    current stream (the stream every libmtp call of the binding launches on)."""
-    stream = torch.cuda.current_stream(dev)
-    for i in range(warm):
-        fn(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    torch.cuda.synchronize()
-    for i in range(n):
-        evs[i][0].record(stream)
-        fn(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+# --------------------------------------------------------------------------
+# single ops (GPU time per call from captured graphs)
+# --------------------------------------------------------------------------
+def op_entry(us, b):
+    return {"us": r3(us), "bytes": int(b), "GB/s": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
-def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
+def attn_catchup_stack_timings(torch, mtp, synth, dev, n):
     """Attention block (cache 4096, 16 q / 2 kv heads x 128; plain, with gated
     q, per-head q/k norms and rotary over 64 of 128 dims, with a 128-row
     sliding window and per-head sinks, and in MiMo's geometry: 16 query / 8 KV
     heads of 192 with V heads of 128, window 128, sinks) at m = 1 and 4, the
     cache catch-up of a 4-row target batch, and the three-layer draft stack
     (each layer catches up 4 rows, then drafts row t).  The attention and
-    catch-up loops rotate over 24 layer/cache copies (about 18 MB read each) so that
-    the 256 MB Infinity Cache cannot serve repeats; the stack's three layers
-    stream 825 MB per call."""
+    catch-up calls rotate over 24 layer/cache copies (about 18 MB read each)
+    so that the 256 MB Infinity Cache cannot serve repeats; the stack's three
+    layers stream 825 MB per call."""
     out = {}
     H, D, NKV, L0, CAP = 2048, 128, 2, 4096, 4112
     kvrow = NKV * D * 4 * 2  # K and V bytes of one position
@@ -312,16 +520,16 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
         for m in (1, 4):
             u = torch.randn((m, H), device=dev)
             o = torch.empty_like(u)
-            ws = torch.empty(mtp.mtp_attn_decode_workspace_size(reps[0][0], L0, m), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(mtp.mtp_attn_decode_workspace_size(reps[0][0], L0, m), dtype=torch.uint8, device=dev)
 
             def call(i, u=u, o=o, ws=ws):
                 dl, dk, dv = reps[i % len(reps)]
                 mtp.mtp_attn_decode(dl, u, dk, dv, L0, out=o, ws=ws)
 
-            us = event_us(torch, dev, call, n, W)
+            us = graph_region_us(torch, call, n)
             seen = L0 + m if not kw.get("window") else min(L0 + m, kw["window"] + m - 1)  # K/V rows read
             b = wb + row * seen + row * m + m * H * 4 * 2
-            out[f"{name}_cache4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+            out[f"{name}_cache4096_m{m}"] = op_entry(us, b)
         if name == "attn":
             # cache catch-up: shifted target hidden -> eh_proj -> K/V rows of 4 positions
             m = 4
@@ -329,15 +537,15 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
             toks = torch.arange(m, dtype=torch.int32, device=dev)
             pend = torch.randn((1, H), device=dev)
             tgt = torch.randn((m, H), device=dev)
-            ws = torch.empty(mtp.mtp_append_kv_workspace_size(reps[0][0]), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(mtp.mtp_append_kv_workspace_size(reps[0][0]), dtype=torch.uint8, device=dev)
 
             def catch_up(i):
                 dl, dk, dv = reps[i % len(reps)]
                 mtp.mtp_append_kv(dl, None, toks, tab, pend, tgt, dk, dv, L0, ws=ws)
 
-            us = event_us(torch, dev, catch_up, n, W)
+            us = graph_region_us(torch, catch_up, n)
             b = q4_bytes(reps[0][0], ("eh_proj", "wk", "wv")) + m * H * 4 * 2 + H * 4 + kvrow * m
-            out["append_kv_4rows_cache4096"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+            out["append_kv_4rows_cache4096"] = op_entry(us, b)
         del reps
         torch.cuda.empty_cache()
 
@@ -354,27 +562,27 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n, W):
     target_h = torch.randn((t + 1, H), device=dev)
     tokens = torch.randint(0, V, (t + 2 + 3,), dtype=torch.int32, device=dev)
     starts = [t - 4] * 3
-    ws = torch.empty(mtp.mtp_stack_draft_workspace_size(layers, caches, starts, t), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(mtp.mtp_stack_draft_workspace_size(layers, caches, starts, t), dtype=torch.uint8, device=dev)
 
     def stack(i):
         mtp.mtp_stack_draft(layers, caches, starts, tokens, table, target_h, t, ws=ws)
 
-    us = event_us(torch, dev, stack, n, W)
+    us = graph_region_us(torch, stack, max(4, n // 4))
     per_layer = (layers[0].weight_nbytes + kvrow * (t + 1) + kvrow * 4
                  + q4_bytes(layers[0], ("eh_proj", "wk", "wv")))
-    b = 3 * per_layer
-    out["stack_draft_3layers_t4099"] = {"us": round(us, 3), "us_per_layer": round(us / 3, 3), "bytes": b,
-                                        "GB/s": round(b / us / 1e3, 1)}
+    out["stack_draft_3layers_t4099"] = dict(op_entry(us, 3 * per_layer), us_per_layer=r3(us / 3))
     del layers, caches, table, target_h
     return out
 
 
 def op_timings(torch, mtp, synth, dev, K, W):
     """The single-op workloads: 4-bit GEMV 1024x1024 (m=1), the e/h norm + concat
-    + eh_proj 2048x4096 (m=1, 4) and the 8-bit MoE FFN (256 experts, top-8 +
-    shared expert, m=1, 4).  Weight copies are rotated so that their total
-    exceeds the 256 MB Infinity Cache; GB/s = algorithmic bytes / event time."""
-    out = {}
+    + eh_proj 2048x4096 (m=1, 4), the attention block, catch-up and stack
+    (above), the 8-bit lm_head (m=1, 4) and the 8-bit MoE FFN (256 experts,
+    top-8 + shared expert, m=1, 4).  Weight copies are rotated so that their
+    total exceeds the 256 MB Infinity Cache; each entry is GPU time per call
+    (n calls captured in one graph) and GB/s = algorithmic bytes / that time."""
+    out = {"note": "us = GPU time per call: n calls captured in one HIP graph, events around one replay, / n"}
     n = max(K, 20)
 
     def rotated_q4(w, copies):
@@ -392,9 +600,8 @@ def op_timings(torch, mtp, synth, dev, K, W):
     c0 = rotated_q4(w0, 683)
     x = torch.from_numpy(x0).to(dev)
     y = torch.empty((1, w0.n), dtype=torch.float32, device=dev)
-    us = event_us(torch, dev, lambda i: mtp.mtp_qgemv(c0[i % len(c0)], x, y=y), n, W)
-    b = c0[0].nbytes + 2 * 1024 * 4
-    out["qgemv_1024x1024_m1"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+    us = graph_region_us(torch, lambda i: mtp.mtp_qgemv(c0[i % len(c0)], x, y=y), 200)
+    out["qgemv_1024x1024_m1"] = op_entry(us, c0[0].nbytes + 2 * 1024 * 4)
     del c0
     torch.cuda.empty_cache()
 
@@ -405,13 +612,12 @@ def op_timings(torch, mtp, synth, dev, K, W):
     for m in (1, 4):
         u = torch.empty((m, w1.n), dtype=torch.float32, device=dev)
         em, hm = de[:m].contiguous(), dh[:m].contiguous()
-        us = event_us(torch, dev, lambda i: mtp.mtp_norm_concat_proj(em, hm, dge, dgh, 1e-6, c1[i % len(c1)], u=u),
-                      n, W)
-        b = c1[0].nbytes + 2 * 2048 * 4 + m * (2 * 2048 + 2048) * 4
-        out[f"norm_concat_proj_2048x4096_m{m}"] = {"us": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1)}
+        us = graph_region_us(torch, lambda i: mtp.mtp_norm_concat_proj(em, hm, dge, dgh, 1e-6, c1[i % len(c1)], u=u),
+                             86)
+        out[f"norm_concat_proj_2048x4096_m{m}"] = op_entry(us, c1[0].nbytes + 2 * 2048 * 4 + m * (2 * 2048 + 2048) * 4)
     del c1
     torch.cuda.empty_cache()
-    out.update(attn_catchup_stack_timings(torch, mtp, synth, dev, n, W))
+    out.update(attn_catchup_stack_timings(torch, mtp, synth, dev, n))
     torch.cuda.empty_cache()
 
     # 8-bit lm_head (vocab 151936 x 2048, int8 + one f32 scale per 32) with the
@@ -426,10 +632,9 @@ def op_timings(torch, mtp, synth, dev, K, W):
     b8 = 151936 * 2048 + 151936 * 64 * 4
     for m in (1, 4):
         xm = torch.randn((m, 2048), device=dev)
-        us = event_us(torch, dev, lambda i: mtp.mtp_lmhead_argmax_q8(xm, gam8, 1e-6, c8[i % 2], ids_out=ids8[:m],
-                                                                      ws=ws8), n, W)
-        out[f"lmhead_q8_151936x2048_m{m}"] = {"us": round(us, 3), "bytes": b8, "GB/s": round(b8 / us / 1e3, 1),
-                                              "frac": round(b8 / us / 1e3 / HBM_PEAK_GBS, 4)}
+        us = graph_region_us(torch, lambda i, xm=xm, m=m: mtp.mtp_lmhead_argmax_q8(xm, gam8, 1e-6, c8[i % 2],
+                                                                                   ids_out=ids8[:m], ws=ws8), n)
+        out[f"lmhead_q8_151936x2048_m{m}"] = op_entry(us, b8)
     del c8
     torch.cuda.empty_cache()
 
@@ -440,14 +645,13 @@ def op_timings(torch, mtp, synth, dev, K, W):
                        for k in ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up", "sh_down")})
     router = torch.from_numpy(M.router).to(dev)
     xm = torch.from_numpy(M.x).to(dev)
-    ones = torch.ones(2048, device=dev)
     per_expert = 3 * (512 * 2048 + 512 * 2048 // 32 * 4)
     for m in (1, 4):
         xr = xm[:m].contiguous()
         y = torch.empty((m, 2048), dtype=torch.float32, device=dev)
         ids = torch.empty((m, M.top_k), dtype=torch.int32, device=dev)
         gts = torch.empty((m, M.top_k), dtype=torch.float32, device=dev)
-        ws = torch.empty(mtp.mtp_ffn_moe_workspace_size(2048, 256, M.top_k, 512, 512, m), dtype=torch.uint8,
+        ws = torch.zeros(mtp.mtp_ffn_moe_workspace_size(2048, 256, M.top_k, 512, 512, m), dtype=torch.uint8,
                          device=dev)
 
         def call(i, m=m, xr=xr, y=y, ids=ids, gts=gts, ws=ws):
@@ -455,43 +659,84 @@ def op_timings(torch, mtp, synth, dev, K, W):
             mtp.mtp_ffn_moe_q(xr, None, 1e-6, router, M.top_k, c["gate_exps"], c["up_exps"], c["down_exps"],
                               c["sh_gate"], c["sh_up"], c["sh_down"], y=y, expert_ids=ids, gates=gts, ws=ws)
 
-        us = event_us(torch, dev, call, n, W)
+        us = graph_region_us(torch, call, n)
         union = len(set(ids.cpu().numpy().ravel().tolist()))
         b = router.numel() * 4 + (union + 1) * per_expert + m * 2048 * 8
-        out[f"moe_q8_256x8_m{m}"] = {"us": round(us, 3), "experts_touched": union + 1, "bytes": b,
-                                     "GB/s": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        out[f"moe_q8_256x8_m{m}"] = dict(op_entry(us, b), experts_touched=union + 1)
     return out
 
 
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle, timed as written
+# --------------------------------------------------------------------------
+def host_cpu():
+    model = None
+    try:
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:
+        usable = os.cpu_count()
+    return model, usable
+
+
 def cpu_baseline(S, step_bytes, budget_s):
-    """The scalar-C oracle (single thread, as written) on a bounded sample of
-    the same workload: whole steps (chain of 3 + verify of 4) until the budget
-    is spent, at least one."""
+    """The scalar-C oracle on bounded samples of the same workload: the K=3
+    chain (three m=1 drafts) and the m=4 verify, timed apart, repeated until
+    half the budget is spent (at least once): first the plain build (one
+    thread), then its OpenMP twin over all usable host cores (the same
+    per-element sums, so the same bits)."""
     import oracle
 
     L = S.layer
-    n = 0
-    t = time.perf_counter()
-    while True:
-        kc, vc = S.k_cache.copy(), S.v_cache.copy()
-        toks, hs = [-1], [S.h0[0]]
-        for k in range(3):
-            ids, hid, _ = oracle.draft_step(L, S.e0, np.array([toks[-1]], np.int32), S.table, hs[-1][None], kc, vc,
-                                            S.cache_len + k, want_logits=False)
-            toks.append(int(ids[0]))
-            hs.append(hid[0])
-        oracle.draft_step(L, np.repeat(S.e0, 4, 0), np.array(toks, np.int32), S.table, np.stack(hs), kc, vc,
-                          S.cache_len, want_logits=False)
-        n += 1
-        el = time.perf_counter() - t
-        if el >= budget_s or el / n * (n + 1) > 2.5 * budget_s:
-            break
-    sec = el / n
-    return {"value": round(step_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} whole step(s) (3 chained m=1 drafts + one m=4 verify) of the same workload",
-            "ms_per_step": round(sec * 1e3, 1),
-            # the oracle's loops are row-independent, so each of the 7 rows costs about the same
-            "draft_steps_per_s": round(7.0 / sec, 3)}
+    model, usable = host_cpu()
+    threads = int(os.environ.get("OMP_NUM_THREADS") or usable or 1)
+
+    def sample(limit):
+        n, tc, tv = 0, 0.0, 0.0
+        while True:
+            kc, vc = S.k_cache.copy(), S.v_cache.copy()
+            toks, hs = [-1], [S.h0[0]]
+            t = time.perf_counter()
+            for k in range(3):
+                ids, hid, _ = oracle.draft_step(L, S.e0, np.array([toks[-1]], np.int32), S.table, hs[-1][None], kc, vc,
+                                                S.cache_len + k, want_logits=False)
+                toks.append(int(ids[0]))
+                hs.append(hid[0])
+            t1 = time.perf_counter()
+            oracle.draft_step(L, np.repeat(S.e0, 4, 0), np.array(toks, np.int32), S.table, np.stack(hs), kc, vc,
+                              S.cache_len, want_logits=False)
+            tc += t1 - t
+            tv += time.perf_counter() - t1
+            n += 1
+            if tc + tv >= limit or (tc + tv) / n * (n + 1) > 2.0 * limit:
+                break
+        return n, tc / n, tv / n
+
+    out = {}
+    for name, threaded in (("one_core", False), ("all_cores", True)):
+        oracle.set_threaded(threaded)
+        try:
+            n, chain_s, verify_s = sample(budget_s / 2)
+        finally:
+            oracle.set_threaded(False)
+        step_s = chain_s + verify_s
+        out[name] = {"threads": threads if threaded else 1, "steps_sampled": n,
+                     "ms_per_step": round(step_s * 1e3, 1), "GB/s": round(step_bytes / step_s / 1e9, 3),
+                     "draft_steps_per_s": round(3.0 / chain_s, 3), "verify_rows_per_s": round(4.0 / verify_s, 3)}
+    a = out["all_cores"]
+    return {"value": a["GB/s"], "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
+            "sample": f"{a['steps_sampled']} whole step(s) (3 chained m=1 drafts + one m=4 verify, timed apart) of "
+                      f"the same workload on {a['threads']} threads (OpenMP build of the oracle, same bits); "
+                      f"{out['one_core']['steps_sampled']} on one thread (plain build)",
+            "draft_steps_per_s": a["draft_steps_per_s"], "verify_rows_per_s": a["verify_rows_per_s"],
+            "ms_per_step": a["ms_per_step"], "one_core": out["one_core"], "host_cpu_model": model,
+            "host_cpus_usable": usable}
 
 
 if __name__ == "__main__":

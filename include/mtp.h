@@ -28,6 +28,13 @@
  *   cache included).  mtp_last_error() then describes the failure (a
  *   thread-local string).  A failed HIP launch returns MTP_ERR_HIP.
  * - Results are deterministic: the same inputs give bit-identical outputs.
+ * - Workspaces: the first 1152 bytes of every workspace are reserved for the
+ *   state of the lm_head's fused cross-block argmax.  They must be zero before
+ *   a workspace's first use (zero-fill it once when it is allocated); no call
+ *   writes anything else there and every call leaves them zero, so one
+ *   workspace may serve any sequence of calls on one stream.
+ * - Arithmetic: activations stay f32 throughout; weight codes enter the
+ *   products exactly and every sum accumulates in f32.
  */
 #ifndef MTP_H
 #define MTP_H
@@ -216,10 +223,9 @@ mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const fl
 /* Shared head with a greedy pick ([mtp.rs] `forward_shared_head_greedy`):
  *   yn = rms(hidden; gamma); logits = lm_head yn; ids[r] = argmax_v logits[r][v]
  * (ties to the lowest index).  normed_out [m][H] and logits_out [m][V] are
- * optional (NULL skips them); ids_out int32 [m] is required.  The first 1152
- * bytes of ws hold the state of the fused cross-block argmax: they must be
- * zero when the call starts (zero-fill ws before its first use) and every
- * call leaves them at zero again. */
+ * optional (NULL skips them); ids_out int32 [m] is required.  The fused
+ * cross-block argmax keeps its state in the reserved first 1152 bytes of ws
+ * (zero on entry; see the workspace convention above). */
 mtp_status mtp_lmhead_argmax(const float* hidden, const float* gamma, float eps, const mtp_q4* lm_head,
                              float* normed_out, float* logits_out, int32_t* ids_out, int32_t m, void* ws,
                              size_t ws_bytes, void* stream);
@@ -243,8 +249,9 @@ mtp_status mtp_lmhead_argmax_q8(const float* hidden, const float* gamma, float e
  *   ids_out = argmax.
  * Row r's embedding e_r is embed_table[tokens[r]] when tokens is not NULL and
  * tokens[r] >= 0 (device int32 [m]; embed_table f32 [vocab][H]), else row r
- * of e [m][H].  Token ids are read on the device: an id >= vocab is clamped
- * to vocab-1.  hidden_out [m][H] is the post-final-norm row, the input of a
+ * of e [m][H].  Token ids are read on the device, where the host cannot check
+ * them: an id >= vocab is clamped to vocab-1 (the call rejects vocab < 1 when
+ * tokens are given).  hidden_out [m][H] is the post-final-norm row, the input of a
  * chained next step ([mtp.rs] `forward_draft_with_hidden`); logits_out
  * [m][vocab] is optional.  The call never advances any cursor: the caller
  * owns cache_len and rolls back by passing a smaller one. */
@@ -296,6 +303,8 @@ typedef struct {
  * writes draft k at tokens[t + 2 + k].  target_h: device f32 [t + 1][H],
  * h_0 .. h_t.  Rows start .. t-1 go through the cache catch-up path (no
  * logits), row t through mtp_draft_step.  All layers share hidden and vocab.
+ * Every layer's calls are checked before the first launch, so an error in
+ * any layer leaves every cache and the token buffer untouched.
  * ws needs mtp_stack_draft_workspace_size(layers, n_layers, t) bytes. */
 size_t mtp_stack_draft_workspace_size(const mtp_stack_layer* layers, int32_t n_layers, int32_t t);
 mtp_status mtp_stack_draft(const mtp_stack_layer* layers, int32_t n_layers, int32_t* tokens, const float* embed_table,

@@ -249,7 +249,8 @@ def _ws(nbytes: int, like, ws):
     torch = _torch()
     if ws is not None:
         return ws
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=like.device)
+    # zero-filled: the reserved head-state bytes at its start must read zero
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=like.device)
 
 
 def _nbytes(t) -> int:

@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmtp.so")
 SOURCES = ["gemv.hip", "attn.hip", "moe.hip", "api.cpp"]
+# measurement support for bench.py (a plain read stream), a library of its own
+BENCH_LIB_PATH = os.path.join(HERE, "libmtp_bench.so")
+BENCH_SOURCES = ["bench_stream.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
@@ -33,11 +36,17 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    _build_lib(SOURCES, LIB_PATH, verbose)
+    _build_lib(BENCH_SOURCES, BENCH_LIB_PATH, verbose)
+    return LIB_PATH
+
+
+def _build_lib(sources, lib_path: str, verbose: bool) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
         objs.append(obj)
         cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -55,13 +64,13 @@ def build(verbose: bool = False) -> str:
     if failed:
         msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    tmp = lib_path + ".tmp%d" % os.getpid()
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -74,11 +74,16 @@ QMat qmat8(const mtp_q8& w, int expert) {
                 w.scales + (int64_t)expert * w.n * gpr, nullptr, w.n};
 }
 
+constexpr size_t kHeadStateBytesZ = (size_t)kHeadStateBytes;
+
 // Bump allocator over the caller's workspace (256-byte aligned pieces).  With
-// base == nullptr it only measures.
+// base == nullptr it only measures.  The first kHeadStateBytes of every
+// workspace are reserved for the fused argmax state of the lm_head (see
+// carve_head): no other buffer is carved there, so a workspace shared by any
+// sequence of calls keeps those bytes at zero between calls.
 struct Carve {
     char* base;
-    size_t off = 0;
+    size_t off = kHeadStateBytesZ;
     template <class T>
     T* take(size_t count) {
         off = (off + 255) & ~size_t(255);
@@ -105,9 +110,10 @@ AttnWs carve_attn(Carve& c, const mtp_layer* L, int32_t cache_len, int32_t m) {
     return w;
 }
 
-// State of the fused lm_head argmax at the start of the call's share of the
-// workspace: MTP_MAX_ROWS 64-bit keys on their own 128-byte lines, then the
-// arrival counter on one more line.  It is zero between calls.
+// State of the fused lm_head argmax, the reserved start of the workspace:
+// MTP_MAX_ROWS 64-bit keys on their own 128-byte lines, then the arrival
+// counter on one more line.  Every head launch leaves it zero, and the draft
+// step also clears it in its first kernel.
 struct HeadWs {
     unsigned long long* keys;
     unsigned* counter;
@@ -117,7 +123,7 @@ constexpr int kHeadStateWords = kHeadStateBytes / 4;
 HeadWs carve_head(Carve& c, int32_t m) {
     (void)m;
     HeadWs w;
-    w.keys = c.take<unsigned long long>(kHeadStateBytes / 8);
+    w.keys = reinterpret_cast<unsigned long long*>(c.base);
     w.counter = reinterpret_cast<unsigned*>(w.keys + kHeadRows * kKeyStride);
     return w;
 }
@@ -383,6 +389,23 @@ mtp_status check_moe_weights(const float* router, int top_k, const mtp_q8* ge, c
     return MTP_OK;
 }
 
+// Checks and launches of the draft step and the cache catch-up, apart, so
+// that a call made of several of them checks everything before launching.
+mtp_status check_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                            const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                            int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                            size_t ws_bytes);
+mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                              const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                              int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                              void* stream);
+mtp_status check_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                           const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                           int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes);
+mtp_status enqueue_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                             const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                             int32_t cache_len, int32_t capacity, int32_t m, void* ws, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -456,9 +479,14 @@ size_t mtp_append_kv_workspace_size(const mtp_layer* L) {
     return c.off;
 }
 
-mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
-                         const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
-                         int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of mtp_append_kv; launches nothing.
+mtp_status check_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                           const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                           int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes) {
     mtp_status s;
     if (m < 1) return fail(MTP_ERR_INVALID_ARG, "m=%d (at least 1)", m);
     if ((s = check_layer_attn(L))) return s;
@@ -477,9 +505,16 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
     if (!tokens && !e) return fail(MTP_ERR_INVALID_ARG, "give e or tokens");
     if (e && (s = check_vec(e, "e"))) return s;
     if (tokens && (!a4(tokens) || !embed_table)) return fail(MTP_ERR_INVALID_ARG, "tokens needs an aligned pointer and embed_table");
+    if (tokens && L->vocab < 1) return fail(MTP_ERR_INVALID_ARG, "vocab=%d: tokens need a table of at least one row", L->vocab);
     if (embed_table && !a16(embed_table)) return fail(MTP_ERR_INVALID_ARG, "embed_table misaligned");
-    if ((s = check_ws(ws, ws_bytes, mtp_append_kv_workspace_size(L)))) return s;
+    return check_ws(ws, ws_bytes, mtp_append_kv_workspace_size(L));
+}
 
+// The launches of mtp_append_kv (arguments already checked).
+mtp_status enqueue_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                             const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                             int32_t cache_len, int32_t capacity, int32_t m, void* ws, void* stream) {
+    const int H = L->hidden;
     hipStream_t st = (hipStream_t)stream;
     Carve c{static_cast<char*>(ws)};
     float* shifted = c.take<float>((size_t)MTP_MAX_ROWS * H);
@@ -538,6 +573,21 @@ mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* toke
     return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_append_kv");
 }
 
+}  // namespace
+
+extern "C" {
+
+mtp_status mtp_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                         const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
+                         int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_append_kv(L, e, tokens, embed_table, pending_h, target_h, k_cache, v_cache, cache_len, capacity, m,
+                             ws, ws_bytes)))
+        return s;
+    return enqueue_append_kv(L, e, tokens, embed_table, pending_h, target_h, k_cache, v_cache, cache_len, capacity, m,
+                             ws, stream);
+}
+
 size_t mtp_stack_draft_workspace_size(const mtp_stack_layer* layers, int32_t n_layers, int32_t t) {
     if (!layers || n_layers < 1 || t < 0) return 0;
     size_t need = 0;
@@ -546,6 +596,7 @@ size_t mtp_stack_draft_workspace_size(const mtp_stack_layer* layers, int32_t n_l
         if (!L) return 0;
         Carve c{nullptr};
         c.take<float>((size_t)L->hidden);  // the draft row's normed hidden (unused after the call)
+        c.off = (c.off + 255) & ~size_t(255);
         const size_t a = mtp_draft_step_workspace_size(L, t, 1), b = mtp_append_kv_workspace_size(L);
         c.off += a > b ? a : b;
         need = c.off > need ? c.off : need;
@@ -573,22 +624,37 @@ mtp_status mtp_stack_draft(const mtp_stack_layer* layers, int32_t n_layers, int3
     const int H = layers[0].layer->hidden;
     Carve c{static_cast<char*>(ws)};
     float* hid = c.take<float>((size_t)H);
+    c.off = (c.off + 255) & ~size_t(255);
     void* rest = static_cast<char*>(ws) + c.off;
     const size_t rest_bytes = ws_bytes - c.off;
-    for (int32_t k = 0; k < n_layers; ++k) {
-        const mtp_stack_layer& S = layers[k];
-        const int n = t - S.start;  // catch-up rows start .. t-1
-        if (n > 0) {
-            // row start + r pairs x_{start+r+k+1} with h_{start+r}: the catch-up's
-            // pending hidden is h_start and its target rows h_{start+1} ..
-            if ((s = mtp_append_kv(S.layer, nullptr, tokens + S.start + k + 1, embed_table, target_h + (int64_t)S.start * H,
-                                   target_h + (int64_t)(S.start + 1) * H, S.k_cache, S.v_cache, S.start, S.capacity, n,
-                                   rest, rest_bytes, stream)))
-                return s;
+    // row start + r of layer k pairs x_{start+r+k+1} with h_{start+r}: the
+    // catch-up's pending hidden is h_start and its target rows h_{start+1} ..;
+    // every layer's calls are checked before the first launch
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int32_t k = 0; k < n_layers; ++k) {
+            const mtp_stack_layer& S = layers[k];
+            const int n = t - S.start;  // catch-up rows start .. t-1
+            const int32_t* ctok = tokens + S.start + k + 1;
+            const float* pend = target_h + (int64_t)S.start * H;
+            const float* tgt = target_h + (int64_t)(S.start + 1) * H;
+            const int32_t* dtok = tokens + t + k + 1;
+            const float* dh = target_h + (int64_t)t * H;
+            if (pass == 0) {
+                if (n > 0 && (s = check_append_kv(S.layer, nullptr, ctok, embed_table, pend, tgt, S.k_cache, S.v_cache,
+                                                  S.start, S.capacity, n, rest, rest_bytes)))
+                    return fail(s, "layer %d catch-up: %s", k, mtp_last_error());
+                if ((s = check_draft_step(S.layer, nullptr, dtok, embed_table, dh, S.k_cache, S.v_cache, t, S.capacity, 1,
+                                          tokens + t + k + 2, hid, nullptr, rest, rest_bytes)))
+                    return fail(s, "layer %d draft: %s", k, mtp_last_error());
+            } else {
+                if (n > 0 && (s = enqueue_append_kv(S.layer, nullptr, ctok, embed_table, pend, tgt, S.k_cache,
+                                                    S.v_cache, S.start, S.capacity, n, rest, stream)))
+                    return s;
+                if ((s = enqueue_draft_step(S.layer, nullptr, dtok, embed_table, dh, S.k_cache, S.v_cache, t,
+                                            S.capacity, 1, tokens + t + k + 2, hid, nullptr, rest, stream)))
+                    return s;
+            }
         }
-        if ((s = mtp_draft_step(S.layer, nullptr, tokens + t + k + 1, embed_table, target_h + (int64_t)t * H, S.k_cache,
-                                S.v_cache, t, S.capacity, 1, tokens + t + k + 2, hid, nullptr, rest, rest_bytes, stream)))
-            return s;
     }
     return MTP_OK;
 }
@@ -728,8 +794,9 @@ mtp_status mtp_ffn_dense_q(const float* x, const float* gamma, float eps, const 
     if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
     const size_t need = mtp_ffn_dense_workspace_size(gate->n, m);
     if ((s = check_ws(ws, ws_bytes, need))) return s;
-    hipError_t e = run_ffn_dense(x, gamma, eps, *gate, *up, *down, residual, y, m, static_cast<float*>(ws),
-                                 (hipStream_t)stream);
+    Carve c{static_cast<char*>(ws)};
+    float* z = c.take<float>((size_t)m * gate->n);
+    hipError_t e = run_ffn_dense(x, gamma, eps, *gate, *up, *down, residual, y, m, z, (hipStream_t)stream);
     return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_ffn_dense_q");
 }
 
@@ -800,10 +867,15 @@ mtp_status mtp_lmhead_argmax_q8(const float* hidden, const float* gamma, float e
     return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_lmhead_argmax_q8");
 }
 
-mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
-                          const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
-                          int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
-                          size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of mtp_draft_step; launches nothing.
+mtp_status check_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                            const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                            int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                            size_t ws_bytes) {
     mtp_status s;
     if ((s = check_rows(m)) || (s = check_layer_attn(L)) || (s = check_cache(k_cache, v_cache, cache_len, capacity, m, L)))
         return s;
@@ -817,6 +889,7 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
     if (!tokens && !e) return fail(MTP_ERR_INVALID_ARG, "give e or tokens");
     if (e && (s = check_vec(e, "e"))) return s;
     if (tokens && (!a4(tokens) || !embed_table)) return fail(MTP_ERR_INVALID_ARG, "tokens needs an aligned pointer and embed_table");
+    if (tokens && L->vocab < 1) return fail(MTP_ERR_INVALID_ARG, "vocab=%d: tokens need a table of at least one row", L->vocab);
     if (embed_table && !a16(embed_table)) return fail(MTP_ERR_INVALID_ARG, "embed_table misaligned");
     if (!ids_out || !a4(ids_out)) return fail(MTP_ERR_INVALID_ARG, "ids_out is NULL or misaligned");
     if (!hidden_out || !a16(hidden_out)) return fail(MTP_ERR_INVALID_ARG, "hidden_out is NULL or misaligned");
@@ -836,8 +909,15 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
         return fail(MTP_ERR_INVALID_ARG, "ffn_kind=%d", L->ffn_kind);
     }
     const size_t need = mtp_draft_step_workspace_size(L, cache_len, m);
-    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    return check_ws(ws, ws_bytes, need);
+}
 
+// The launches of mtp_draft_step (arguments already checked).
+mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                              const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                              int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                              void* stream) {
+    const int H = L->hidden;
     hipStream_t st = (hipStream_t)stream;
     // carve in the order mtp_draft_step_workspace_size measures
     Carve c{static_cast<char*>(ws)};
@@ -888,6 +968,22 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
     if ((err = run_head(r2, L->gamma_final, L->eps, L->lm_head, hidden_out, logits_out, ids_out, m, hw, st)) != hipSuccess)
         return hip_fail(err, "mtp_draft_step head");
     return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                          const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                          int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    mtp_status s;
+    if ((s = check_draft_step(L, e, tokens, embed_table, h, k_cache, v_cache, cache_len, capacity, m, ids_out,
+                              hidden_out, logits_out, ws, ws_bytes)))
+        return s;
+    return enqueue_draft_step(L, e, tokens, embed_table, h, k_cache, v_cache, cache_len, capacity, m, ids_out,
+                              hidden_out, logits_out, ws, stream);
 }
 
 }  // extern "C"

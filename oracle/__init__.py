@@ -21,18 +21,36 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mtp_oracle.c")
 _HDR = os.path.join(_HERE, "mtp_oracle.h")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
-_lib = None
+# the same source built with OpenMP: the independent output elements of the
+# GEMVs and attention heads are shared out over threads, every element keeping
+# its own ascending double sum, so its results equal the plain build's bit for
+# bit (used only to time the oracle on all host cores)
+LIB_OMP_PATH = os.path.join(_HERE, "liboracle_omp.so")
+_libs = {}
+_threaded = False
+
+
+def _build_one(path: str, extra, force: bool) -> str:
+    stale = (not os.path.exists(path) or
+             os.path.getmtime(path) < max(os.path.getmtime(_SRC), os.path.getmtime(_HDR)))
+    if force or stale:
+        tmp = path + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wno-unknown-pragmas", *extra, "-fPIC", "-shared",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, path)
+    return path
 
 
 def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc -O2 -std=c99 (no fast-math)."""
-    stale = (not os.path.exists(LIB_PATH) or
-             os.path.getmtime(LIB_PATH) < max(os.path.getmtime(_SRC), os.path.getmtime(_HDR)))
-    if force or stale:
-        tmp = LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    """Compile liboracle.so (gcc -O2 -std=c99, no fast-math) and its OpenMP twin."""
+    _build_one(LIB_OMP_PATH, ["-fopenmp"], force)
+    return _build_one(LIB_PATH, [], force)
+
+
+def set_threaded(flag: bool) -> None:
+    """Route every following call to the OpenMP build (True) or the plain one."""
+    global _threaded
+    _threaded = bool(flag)
 
 
 class _Q4(C.Structure):
@@ -64,10 +82,12 @@ class _MoeFfn(C.Structure):
 
 
 def lib():
-    global _lib
+    key = "omp" if _threaded else "plain"
+    _lib = _libs.get(key)
     if _lib is None:
         build()
-        _lib = C.CDLL(LIB_PATH)
+        _lib = C.CDLL(LIB_OMP_PATH if _threaded else LIB_PATH)
+        _libs[key] = _lib
         P, I = C.c_void_p, C.c_int32
         sig = {
             "orc_unpack4": (None, [P, I, I, P]),

@@ -76,42 +76,53 @@ void orc_deq8(const orc_q8* w, float* out) {
  * this is x times W transposed. */
 void orc_gemv4(const orc_q4* w, const float* x, int32_t m, float* y) {
     const int32_t n = w->n, k = w->k, gpr = k / GROUP;
-    double* row = (double*)xmalloc(sizeof(double) * (size_t)k);
-    for (int32_t o = 0; o < n; ++o) {
-        for (int32_t c = 0; c < k; ++c) {
-            size_t gi = (size_t)o * gpr + (size_t)(c / GROUP);
-            row[c] = (double)w->scales[gi] * (double)code4(w->codes, k, o, c) + (double)w->biases[gi];
+    /* output rows are independent: a build with OpenMP shares them out over
+     * threads, each element keeping its own ascending sum (same bits) */
+#pragma omp parallel
+    {
+        double* row = (double*)xmalloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int32_t o = 0; o < n; ++o) {
+            for (int32_t c = 0; c < k; ++c) {
+                size_t gi = (size_t)o * gpr + (size_t)(c / GROUP);
+                row[c] = (double)w->scales[gi] * (double)code4(w->codes, k, o, c) + (double)w->biases[gi];
+            }
+            for (int32_t r = 0; r < m; ++r) {
+                const float* xr = x + (size_t)r * k;
+                double acc = 0.0;
+                for (int32_t c = 0; c < k; ++c) acc += (double)xr[c] * row[c];
+                y[(size_t)r * n + o] = (float)acc;
+            }
         }
-        for (int32_t r = 0; r < m; ++r) {
-            const float* xr = x + (size_t)r * k;
-            double acc = 0.0;
-            for (int32_t c = 0; c < k; ++c) acc += (double)xr[c] * row[c];
-            y[(size_t)r * n + o] = (float)acc;
-        }
+        free(row);
     }
-    free(row);
 }
 
 void orc_gemv8(const orc_q8* w, const float* x, int32_t m, float* y) {
     const int32_t n = w->n, k = w->k, gpr = k / GROUP;
-    double* row = (double*)xmalloc(sizeof(double) * (size_t)k);
-    for (int32_t o = 0; o < n; ++o) {
-        for (int32_t c = 0; c < k; ++c)
-            row[c] = (double)w->scales[(size_t)o * gpr + (size_t)(c / GROUP)] *
-                     (double)w->codes[(size_t)o * k + c];
-        for (int32_t r = 0; r < m; ++r) {
-            const float* xr = x + (size_t)r * k;
-            double acc = 0.0;
-            for (int32_t c = 0; c < k; ++c) acc += (double)xr[c] * row[c];
-            y[(size_t)r * n + o] = (float)acc;
+#pragma omp parallel
+    {
+        double* row = (double*)xmalloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int32_t o = 0; o < n; ++o) {
+            for (int32_t c = 0; c < k; ++c)
+                row[c] = (double)w->scales[(size_t)o * gpr + (size_t)(c / GROUP)] *
+                         (double)w->codes[(size_t)o * k + c];
+            for (int32_t r = 0; r < m; ++r) {
+                const float* xr = x + (size_t)r * k;
+                double acc = 0.0;
+                for (int32_t c = 0; c < k; ++c) acc += (double)xr[c] * row[c];
+                y[(size_t)r * n + o] = (float)acc;
+            }
         }
+        free(row);
     }
-    free(row);
 }
 
 /* Dense f32 projection (the MoE router). */
 void orc_gemv_f32(const float* w, int32_t n, int32_t k, const float* x, int32_t m, float* y) {
     for (int32_t r = 0; r < m; ++r)
+#pragma omp parallel for schedule(static)
         for (int32_t o = 0; o < n; ++o) {
             double acc = 0.0;
             for (int32_t c = 0; c < k; ++c)
@@ -199,12 +210,16 @@ void orc_sdpa_kv(const float* q, const float* k_cache, const float* v_cache, int
     const int32_t group = n_heads / n_kv_heads;
     const double scale = 1.0 / sqrt((double)head_dim);
     const int32_t max_len = cache_len + m;
+    /* (row, head) pairs are independent (threads with OpenMP) */
+#pragma omp parallel
+    {
     double* p = (double*)xmalloc(sizeof(double) * (size_t)max_len);
     double* o = (double*)xmalloc(sizeof(double) * (size_t)v_dim);
+#pragma omp for collapse(2) schedule(static)
     for (int32_t r = 0; r < m; ++r) {
-        const int32_t pos = cache_len + r;
-        const int32_t lo = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
         for (int32_t hh = 0; hh < n_heads; ++hh) {
+            const int32_t pos = cache_len + r;
+            const int32_t lo = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
             const int32_t g = hh / group;
             const float* qv = q + ((size_t)r * n_heads + hh) * head_dim;
             const float* K = k_cache + (size_t)g * capacity * head_dim;
@@ -231,6 +246,7 @@ void orc_sdpa_kv(const float* q, const float* k_cache, const float* v_cache, int
     }
     free(p);
     free(o);
+    }
 }
 
 /* Greedy pick: first index of the largest value (ties go to the lowest index;

@@ -244,3 +244,51 @@ def test_stack_draft_rejects_bad_layers():
     arr[1].capacity = 10  # row t = 10 beyond capacity
     assert lib.mtp_stack_draft(arr, 2, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws, None) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_stack_draft(arr, 0, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws, None) == mtp.MTP_ERR_INVALID_ARG
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0  # counts devices without initialising them
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="passes fake device pointers; a check that failed to reject would launch them")
+def test_stack_draft_checks_every_layer_before_launching():
+    """A valid layer 0 and a layer 1 without a K cache: the call must fail in
+    its checks (MTP_ERR_INVALID_ARG), before layer 0's catch-up or draft is
+    enqueued (with no device here, any launch would surface as MTP_ERR_HIP)."""
+    lib = mtp.lib()
+    L = _layer()
+    arr = (mtp.MtpStackLayer * 2)()
+    arr[0] = mtp.MtpStackLayer(C.addressof(L), FAKE, FAKE * 2, 64, 5)
+    arr[1] = mtp.MtpStackLayer(C.addressof(L), None, FAKE * 4, 64, 5)
+    ws = lib.mtp_stack_draft_workspace_size(arr, 2, 10)
+    assert lib.mtp_stack_draft(arr, 2, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws, None) == mtp.MTP_ERR_INVALID_ARG
+    assert b"layer 1" in lib.mtp_last_error()
+    # a bad workspace size is caught the same way (no partial work for layer 0)
+    arr[1].k_cache = FAKE * 3
+    assert lib.mtp_stack_draft(arr, 2, FAKE * 5, FAKE * 6, FAKE * 7, 10, FAKE * 8, ws - 256, None) in (
+        mtp.MTP_ERR_WORKSPACE, mtp.MTP_ERR_INVALID_ARG)
+
+
+def test_token_rows_need_a_vocabulary():
+    lib = mtp.lib()
+    L = _layer(vocab=0)
+    need = lib.mtp_append_kv_workspace_size(C.byref(L))
+    assert lib.mtp_append_kv(C.byref(L), None, FAKE, FAKE * 2, None, FAKE * 3, FAKE * 4, FAKE * 5, 0, 16, 2,
+                             FAKE * 6, need, None) == mtp.MTP_ERR_INVALID_ARG
+    assert b"vocab" in lib.mtp_last_error()
+
+
+def test_every_workspace_reserves_the_argmax_state():
+    """The first 1152 bytes of every workspace belong to the head's argmax
+    state, so every size covers at least them plus one 256-byte piece."""
+    lib = mtp.lib()
+    L = _layer()
+    assert lib.mtp_lmhead_workspace_size(1000, 1) == 1152
+    for n in (lib.mtp_attn_decode_workspace_size(C.byref(L), 10, 1), lib.mtp_ffn_dense_workspace_size(64, 1),
+              lib.mtp_append_kv_workspace_size(C.byref(L)), lib.mtp_draft_step_workspace_size(C.byref(L), 10, 1),
+              lib.mtp_ffn_moe_workspace_size(256, 16, 4, 64, 64, 1)):
+        assert n >= 1280 + 256

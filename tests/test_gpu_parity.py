@@ -330,6 +330,42 @@ def test_lmhead_argmax_reuses_one_workspace(planted_config2):
     assert int(ws[:1152].count_nonzero().item()) == 0
 
 
+def test_one_workspace_shared_by_every_call_keeps_the_head_state_zero():
+    """One zero-filled workspace serves a draft step, the attention block, the
+    dense and MoE FFNs and a cache catch-up, then the standalone head: none of
+    them writes the reserved argmax state, so the head still returns the
+    oracle's ids, and the state reads zero at the end."""
+    S = synth.config4_step(seed_extra=4242, cache_len=40, capacity=60, hidden=256, n_heads=4, n_kv_heads=2,
+                           head_dim=128, vocab=1000, ffn_inter=320)
+    L = S.layer
+    dl = mtp.DeviceLayer(L)
+    inp = synth.moe_inputs(synth.rng(136), 2, hidden=256, n_experts=16, inter=64, top_k=4, shared_inter=64)
+    need = max(mtp.mtp_draft_step_workspace_size(dl, S.cache_len, 4), mtp.mtp_attn_decode_workspace_size(dl, S.cache_len, 4),
+               mtp.mtp_ffn_dense_workspace_size(L.ffn_inter, 4), mtp.mtp_append_kv_workspace_size(dl),
+               mtp.mtp_ffn_moe_workspace_size(256, 16, 4, 64, 64, 2), mtp.mtp_lmhead_workspace_size(L.vocab, 4))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    g = synth.rng(137)
+    mtp.mtp_draft_step(dl, _t(S.e0), None, None, _t(S.h0), dk, dv, S.cache_len, ws=ws)
+    u = _t(synth.normal(g, (2, 256)))
+    mtp.mtp_attn_decode(dl, u, dk, dv, S.cache_len + 1, ws=ws)
+    mtp.mtp_ffn_dense_q(u, dl.gammas[3], 1e-6, dl.q4["gate"], dl.q4["up"], dl.q4["down"], ws=ws)
+    mtp.mtp_ffn_moe_q(_t(inp.x), None, 1e-6, _t(inp.router), 4, mtp.DeviceQ8(inp.gate_exps), mtp.DeviceQ8(inp.up_exps),
+                      mtp.DeviceQ8(inp.down_exps), mtp.DeviceQ8(inp.sh_gate), mtp.DeviceQ8(inp.sh_up),
+                      mtp.DeviceQ8(inp.sh_down), ws=ws)
+    mtp.mtp_append_kv(dl, _t(synth.normal(g, (3, 256))), None, None, None, _t(synth.normal(g, (3, 256))), dk, dv,
+                      S.cache_len + 3, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:1152].count_nonzero().item()) == 0
+    x = synth.normal(g, (4, 256))
+    for m in (1, 4):
+        _, logits, ids = oracle.head(x[:m], L.gamma_final, L.eps, L.lm_head)
+        assert min(planting.head_margin(r) for r in logits) >= 1e-3
+        got = _np(mtp.mtp_lmhead_argmax(_t(x[:m]), dl.gammas[4], L.eps, dl.q4["lm_head"], ws=ws))
+        assert got.tolist() == ids.tolist()
+    assert int(ws[:1152].count_nonzero().item()) == 0
+
+
 @pytest.mark.parametrize("m", [1, 4])
 def test_lmhead_argmax_ties_keep_lowest_row(m, planted_config2):
     """Exact ties: each target row is copied to a lower and a higher row with
@@ -1104,3 +1140,58 @@ def test_stack_draft_three_layers(t, starts, mimo):
         _close(gk[:, starts[k]:t + 1], caches[k][0][:, starts[k]:t + 1], f"layer {k} k rows")
         _close(gv[:, starts[k]:t + 1], caches[k][1][:, starts[k]:t + 1], f"layer {k} v rows")
         assert np.array_equal(gk[:, :starts[k]], base[k][0][:, :starts[k]])
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture of the chain and the verify (the form a decode loop and
+# bench.py run them in): every replay, with eager work and synchronizations
+# between replays, equals the eager result bit for bit
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("moe", [False, True])
+def test_graph_replays_equal_the_eager_chain_and_verify(moe):
+    S = synth.config4_step(seed_extra=4300, cache_len=70, capacity=80, hidden=256, n_heads=4, n_kv_heads=2,
+                           head_dim=128, vocab=1000, ffn_inter=320)
+    inp = (synth.moe_inputs(synth.rng(138), 1, hidden=256, n_experts=16, inter=64, top_k=4, shared_inter=64)
+           if moe else None)
+    dl = mtp.DeviceLayer(S.layer, moe=inp)
+    H, L0 = S.layer.hidden, S.cache_len
+    dk, dv, tab = _t(S.k_cache), _t(S.v_cache), _t(S.table)
+    e0 = _t(S.e0)
+    e4 = e0.repeat(4, 1).contiguous()
+    tok = torch.full((4,), -1, dtype=torch.int32, device=DEV)
+    hb = torch.empty((4, H), dtype=torch.float32, device=DEV)
+    hb[0].copy_(_t(S.h0[0]))
+    ids_v = torch.empty(4, dtype=torch.int32, device=DEV)
+    hid_v = torch.empty((4, H), dtype=torch.float32, device=DEV)
+    lg_v = torch.empty((4, S.layer.vocab), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(max(mtp.mtp_draft_step_workspace_size(dl, L0 + 3, 1), mtp.mtp_draft_step_workspace_size(dl, L0, 4)),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        for k in range(3):
+            mtp.mtp_draft_step(dl, e0, tok[k:k + 1], tab, hb[k:k + 1], dk, dv, L0 + k, ids_out=tok[k + 1:k + 2],
+                               hidden_out=hb[k + 1:k + 2], ws=ws)
+        mtp.mtp_draft_step(dl, e4, tok, tab, hb, dk, dv, L0, ids_out=ids_v, hidden_out=hid_v, logits_out=lg_v, ws=ws)
+
+    def snap():
+        return [_np(t).copy() for t in (tok, hb, ids_v, hid_v, lg_v, dk, dv)]
+
+    step()
+    ref = snap()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    scratch = _t(synth.normal(synth.rng(139), (2, H)))
+    for rep in range(4):
+        # eager work on the same workspace between replays, then clear outputs
+        mtp.mtp_attn_decode(dl, scratch, dk.clone(), dv.clone(), L0, ws=ws)
+        for t in (hid_v, lg_v):
+            t.zero_()
+        ids_v.fill_(-7)
+        tok[1:].fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        got = snap()
+        for a, b, name in zip(ref, got, ("tokens", "hidden chain", "verify ids", "verify hidden", "verify logits",
+                                         "k cache", "v cache")):
+            assert np.array_equal(a, b), f"replay {rep}: {name}"

@@ -1008,3 +1008,25 @@ def test_draft_step_moe_batched_verify_equals_the_sequential_chain():
     assert ids_v[:3].tolist() == [c[0] for c in chain]
     assert np.array_equal(hid_v[:3], np.stack([c[1] for c in chain]))
     assert np.array_equal(log_v[:3], np.stack([c[2] for c in chain]))
+
+
+def test_threaded_oracle_build_gives_the_same_bits():
+    """The OpenMP build (used only to time the oracle on all cores) shares out
+    independent output elements; every element keeps its ascending sum, so a
+    whole draft step equals the plain build's bit for bit."""
+    L = _small_layer(63)
+    g = np.random.default_rng(64)
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, 12, 20, L.head_dim)
+    e, h = synth.normal(g, (3, L.hidden)), synth.normal(g, (3, L.hidden))
+    outs = []
+    for threaded in (False, True):
+        oracle.set_threaded(threaded)
+        try:
+            k2, v2 = kc.copy(), vc.copy()
+            outs.append((oracle.draft_step(L, e, None, None, h, k2, v2, 12), k2, v2))
+        finally:
+            oracle.set_threaded(False)
+    (a, ka, va), (b, kb, vb) = outs
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert np.array_equal(ka, kb) and np.array_equal(va, vb)
