@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--head-q8", action="store_true", help="--head-only over the 8-bit lm_head")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only a plain device copy of 256 MiB, the reference for scaling byte counters")
+    ap.add_argument("--moe-only", action="store_true", help="only the 8-bit MoE FFN at m=4 (counter runs)")
+    ap.add_argument("--attn-only", action="store_true", help="only the attention block at m=1 (counter runs)")
     return ap.parse_args()
 
 
@@ -206,6 +208,40 @@ def head_only(torch, mtp, synth, dev, reps, m, q8):
     torch.cuda.synchronize()
     print(json.dumps({"head_launches": reps, "rows": m, "bits": 8 if q8 else 4, "bytes_per_launch": nbytes}),
           flush=True)
+
+
+def moe_only(torch, mtp, synth, dev, reps):
+    """The config-3 MoE FFN (256 experts, top-8 + shared) at m=4 over 3 rotated
+    expert-stack copies, eager launches."""
+    M = synth.config3_moe(4)
+    copies = [{k: mtp.DeviceQ8(getattr(M, k), dev) for k in ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up",
+                                                               "sh_down")} for _ in range(3)]
+    router, x = torch.from_numpy(M.router).to(dev), torch.from_numpy(M.x).to(dev)
+    ws = torch.zeros(mtp.mtp_ffn_moe_workspace_size(2048, 256, M.top_k, 512, 512, 4), dtype=torch.uint8, device=dev)
+    y = torch.empty((4, 2048), dtype=torch.float32, device=dev)
+    for i in range(reps):
+        c = copies[i % 3]
+        mtp.mtp_ffn_moe_q(x, None, 1e-6, router, M.top_k, c["gate_exps"], c["up_exps"], c["down_exps"], c["sh_gate"],
+                          c["sh_up"], c["sh_down"], y=y, ws=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"moe_m4_calls": reps}), flush=True)
+
+
+def attn_only(torch, mtp, synth, dev, reps):
+    """The attention block at m=1, cache 4096 (16 q / 2 kv heads x 128), over
+    24 rotated layer/cache copies, eager launches."""
+    g = synth.rng(40)
+    Lh = synth.dense_layer(g, vocab=64)
+    kc, vc = synth.kv_cache(g, Lh.n_kv_heads, 4096, 4112, 128)
+    reps_ = [(mtp.DeviceLayer(Lh, dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)) for _ in range(24)]
+    u = torch.randn((1, 2048), device=dev)
+    o = torch.empty_like(u)
+    ws = torch.zeros(mtp.mtp_attn_decode_workspace_size(reps_[0][0], 4096, 1), dtype=torch.uint8, device=dev)
+    for i in range(reps):
+        dl, dk, dv = reps_[i % 24]
+        mtp.mtp_attn_decode(dl, u, dk, dv, 4096, out=o, ws=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"attn_m1_calls": reps}), flush=True)
 
 
 # --------------------------------------------------------------------------
@@ -366,6 +402,10 @@ def main():
         return copy_ref(torch, dev)
     if args.head_only:
         return head_only(torch, mtp, synth, dev, args.steps, args.head_m, args.head_q8)
+    if args.moe_only:
+        return moe_only(torch, mtp, synth, dev, args.steps)
+    if args.attn_only:
+        return attn_only(torch, mtp, synth, dev, args.steps)
     if args.ops_only:
         print(json.dumps({"ops": op_timings(torch, mtp, synth, dev, args.steps, args.warmup)}), flush=True)
         return
