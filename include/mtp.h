@@ -11,9 +11,10 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every pointer argument is DEVICE memory owned by the caller, unless a
- *   comment says "host".  The library never allocates, frees or keeps device
+ *   comment says "host".  The library never allocates or frees device
  *   memory; scratch space is the caller's `ws` of at least the size the
- *   matching *_workspace_size() call returns.
+ *   matching *_workspace_size() call returns (mtp_draft_step_noalloc alone
+ *   uses a static device array of the library instead).
  * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work and return; outputs are valid once the stream has reached
  *   that point.  Calls that share an output or a workspace must be ordered on
@@ -49,6 +50,10 @@ extern "C" {
 #define MTP_MAX_ROWS 8
 #define MTP_GROUP 32
 #define MTP_MAX_K 8192
+/* Size of the static device scratch array of mtp_draft_step_noalloc (32 MiB
+ * per GPU, held from the library's first use of it on that GPU until the
+ * process ends). */
+#define MTP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum {
     MTP_OK = 0,
@@ -259,6 +264,29 @@ mtp_status mtp_draft_step(const mtp_layer* L, const float* e, const int32_t* tok
                           const float* h, float* k_cache, float* v_cache, int32_t cache_len,
                           int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,
                           float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/* mtp_draft_step without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that keep
+ * their memory fixed, harnesses that forbid hipMalloc).  Arguments and
+ * results are those of mtp_draft_step minus ws / ws_bytes; the step's
+ * scratch space is instead a static device array of the library,
+ * MTP_NOALLOC_SCRATCH_BYTES on each GPU, whose device address is looked up
+ * on the call's first use of a device.  The call allocates and frees
+ * nothing.
+ * - A step that needs more scratch than that
+ *   (mtp_draft_step_workspace_size(L, cache_len, m) > MTP_NOALLOC_SCRATCH_BYTES)
+ *   is rejected with MTP_ERR_WORKSPACE before anything is enqueued.
+ * - The stream must belong to the current device (MTP_ERR_INVALID_ARG
+ *   otherwise).
+ * - Every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents (the step clears what must start at zero itself): calls
+ *   that may overlap on one GPU (on different streams, or from several
+ *   threads without ordering) race and give wrong results.  Order them on one
+ *   stream, or use mtp_draft_step with a workspace per stream. */
+mtp_status mtp_draft_step_noalloc(const mtp_layer* L, const float* e, const int32_t* tokens,
+                                  const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                                  int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
+                                  float* hidden_out, float* logits_out, void* stream);
 
 /* Cache catch-up after a target batch ([mtp.rs] `process_target_batch` and
  * `append_attention_kv`): for rows r = 0 .. m-1 at positions cache_len + r,

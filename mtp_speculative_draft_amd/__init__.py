@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mtp.h")
 
 MTP_OK, MTP_ERR_INVALID_ARG, MTP_ERR_UNSUPPORTED, MTP_ERR_WORKSPACE, MTP_ERR_HIP = range(5)
 MTP_MAX_ROWS = 8
+MTP_NOALLOC_SCRATCH_BYTES = 32 << 20
 MTP_FFN_DENSE_Q4, MTP_FFN_MOE_Q8 = 0, 1
 
 
@@ -92,6 +93,7 @@ _SIGS = {
     "mtp_ffn_moe_q": (_I, [_P, _P, _F, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_lmhead_argmax": (_I, [_P, _P, _F, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_draft_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "mtp_draft_step_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "mtp_append_kv_workspace_size": (_Z, [_P]),
     "mtp_append_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]),
     "mtp_accept": (_I, [_P, _P, _I, _P]),
@@ -416,6 +418,19 @@ def mtp_draft_step(layer: DeviceLayer, e, tokens, embed_table, h, k_cache, v_cac
                                 _ptr(k_cache), _ptr(v_cache), int(cache_len), int(k_cache.shape[1]), m,
                                 _ptr(ids_out), _ptr(hidden_out), _ptr(logits_out), _ptr(ws), _nbytes(ws),
                                 _stream(h)), "mtp_draft_step")
+    return ids_out, hidden_out
+
+
+def mtp_draft_step_noalloc(layer: DeviceLayer, e, tokens, embed_table, h, k_cache, v_cache, cache_len: int, ids_out,
+                           hidden_out, logits_out=None):
+    """mtp_draft_step with the library's static scratch instead of a workspace
+    (the outputs are the caller's: nothing is allocated here either)."""
+    _f32(h, "h")
+    m = _rows(h)
+    _check(lib().mtp_draft_step_noalloc(C.byref(layer.desc), _ptr(e), _ptr(tokens), _ptr(embed_table), _ptr(h),
+                                        _ptr(k_cache), _ptr(v_cache), int(cache_len), int(k_cache.shape[1]), m,
+                                        _ptr(ids_out), _ptr(hidden_out), _ptr(logits_out), _stream(h)),
+           "mtp_draft_step_noalloc")
     return ids_out, hidden_out
 
 

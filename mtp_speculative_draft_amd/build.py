@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmtp.so")
-SOURCES = ["gemv.hip", "attn.hip", "moe.hip", "api.cpp"]
+SOURCES = ["gemv.hip", "attn.hip", "moe.hip", "api.cpp", "noalloc.hip"]
 # measurement support for bench.py (a plain read stream), a library of its own
 BENCH_LIB_PATH = os.path.join(HERE, "libmtp_bench.so")
 BENCH_SOURCES = ["bench_stream.hip"]

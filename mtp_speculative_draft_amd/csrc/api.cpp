@@ -10,13 +10,16 @@
 #include <string>
 
 #include "../../include/mtp.h"
+#include "api_internal.hpp"
 #include "launch.hpp"
 
 using namespace mtp;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
+
+namespace mtp {
 
 mtp_status fail(mtp_status s, const char* fmt, ...) {
     char buf[512];
@@ -31,6 +34,10 @@ mtp_status fail(mtp_status s, const char* fmt, ...) {
 mtp_status hip_fail(hipError_t e, const char* what) {
     return fail(MTP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+}  // namespace mtp
+
+namespace {
 
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -390,15 +397,12 @@ mtp_status check_moe_weights(const float* router, int top_k, const mtp_q8* ge, c
 }
 
 // Checks and launches of the draft step and the cache catch-up, apart, so
-// that a call made of several of them checks everything before launching.
+// that a call made of several of them checks everything before launching
+// (the draft step's pair is declared in api_internal.hpp).
 mtp_status check_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
                             const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
                             int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
                             size_t ws_bytes);
-mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
-                              const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
-                              int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
-                              void* stream);
 mtp_status check_append_kv(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
                            const float* pending_h, const float* target_h, float* k_cache, float* v_cache,
                            int32_t cache_len, int32_t capacity, int32_t m, void* ws, size_t ws_bytes);
@@ -869,13 +873,14 @@ mtp_status mtp_lmhead_argmax_q8(const float* hidden, const float* gamma, float e
 
 }  // extern "C"
 
-namespace {
+namespace mtp {
 
-// Every check of mtp_draft_step; launches nothing.
-mtp_status check_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
-                            const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
-                            int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
-                            size_t ws_bytes) {
+// Every check of mtp_draft_step but the workspace's; launches nothing and
+// makes no HIP call.
+mtp_status check_draft_step_args(const mtp_layer* L, const float* e, const int32_t* tokens,
+                                 const float* embed_table, const float* h, float* k_cache, float* v_cache,
+                                 int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
+                                 float* hidden_out, float* logits_out) {
     mtp_status s;
     if ((s = check_rows(m)) || (s = check_layer_attn(L)) || (s = check_cache(k_cache, v_cache, cache_len, capacity, m, L)))
         return s;
@@ -908,9 +913,27 @@ mtp_status check_draft_step(const mtp_layer* L, const float* e, const int32_t* t
     } else {
         return fail(MTP_ERR_INVALID_ARG, "ffn_kind=%d", L->ffn_kind);
     }
-    const size_t need = mtp_draft_step_workspace_size(L, cache_len, m);
-    return check_ws(ws, ws_bytes, need);
+    return MTP_OK;
 }
+
+}  // namespace mtp
+
+namespace {
+
+// Every check of mtp_draft_step; launches nothing.
+mtp_status check_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
+                            const float* h, float* k_cache, float* v_cache, int32_t cache_len, int32_t capacity,
+                            int32_t m, int32_t* ids_out, float* hidden_out, float* logits_out, void* ws,
+                            size_t ws_bytes) {
+    mtp_status s = check_draft_step_args(L, e, tokens, embed_table, h, k_cache, v_cache, cache_len, capacity, m,
+                                         ids_out, hidden_out, logits_out);
+    if (s) return s;
+    return check_ws(ws, ws_bytes, mtp_draft_step_workspace_size(L, cache_len, m));
+}
+
+}  // namespace
+
+namespace mtp {
 
 // The launches of mtp_draft_step (arguments already checked).
 mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
@@ -970,7 +993,7 @@ mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t*
     return MTP_OK;
 }
 
-}  // namespace
+}  // namespace mtp
 
 extern "C" {
 

@@ -292,3 +292,22 @@ def test_every_workspace_reserves_the_argmax_state():
               lib.mtp_append_kv_workspace_size(C.byref(L)), lib.mtp_draft_step_workspace_size(C.byref(L), 10, 1),
               lib.mtp_ffn_moe_workspace_size(256, 16, 4, 64, 64, 1)):
         assert n >= 1280 + 256
+
+
+def test_noalloc_draft_step_rejects_steps_beyond_its_scratch():
+    """The allocation-free draft step runs every argument check, then rejects a
+    step whose workspace would exceed the static scratch, before any HIP call
+    (no GPU here: reaching the runtime would give MTP_ERR_HIP instead)."""
+    lib = mtp.lib()
+    L = _layer()
+    big = 1 << 22
+    assert lib.mtp_draft_step_workspace_size(C.byref(L), big, 8) > mtp.MTP_NOALLOC_SCRATCH_BYTES
+    args = lambda cache_len, cap, m: (C.byref(L), FAKE, None, None, FAKE, FAKE * 2, FAKE * 3, cache_len,  # noqa: E731
+                                      cap, m, FAKE * 4, FAKE * 5, None, None)
+    assert lib.mtp_draft_step_noalloc(*args(big, big + 8, 8)) == mtp.MTP_ERR_WORKSPACE
+    msg = lib.mtp_last_error()
+    assert b"MTP_NOALLOC_SCRATCH_BYTES" in msg and b"mtp_draft_step with a workspace" in msg
+    # argument errors come first and read as those of mtp_draft_step
+    assert lib.mtp_draft_step_noalloc(*args(big, big + 7, 8)) == mtp.MTP_ERR_INVALID_ARG
+    assert b"overflow" in lib.mtp_last_error()
+    assert lib.mtp_draft_step_noalloc(*args(10, 20, 9)) == mtp.MTP_ERR_INVALID_ARG
