@@ -12,6 +12,10 @@ and `MlxQWeight::from_mlx_affine_linear`):
   biases ``[n, k/32]``; value = scale * code + bias.
 * 8-bit block, block 32: int8 codes ``[..., n, k]`` and f32 scales
   ``[..., n, k/32]``; value = scale * code.
+* 4-bit affine expert stack with bf16 group constants (hf2q 0.1.1,
+  `MlxAffineMoeStack`): u32 codes ``[E, n, k/8]`` in the 4-bit nibble order,
+  bf16 scales and biases ``[E, n, k/32]`` stored as their 16 bits (the upper
+  half of an f32); value = scale * code + bias.
 
 Every generator takes a ``numpy.random.Generator`` so that callers fix the
 draw order; ``rng(config, *extra)`` seeds one from ``SeedSequence`` entropy
@@ -74,6 +78,29 @@ class Q8:
     @property
     def expert_nbytes(self) -> int:
         return int(self.codes[0].nbytes + self.scales[0].nbytes)
+
+
+@dataclasses.dataclass
+class Q4E:
+    codes: np.ndarray  # uint32 [E, n, k/8]
+    scales: np.ndarray  # uint16 (bf16 bits) [E, n, k/32]
+    biases: np.ndarray  # uint16 (bf16 bits) [E, n, k/32]
+
+    @property
+    def n_experts(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[1])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[2]) * 8
+
+    @property
+    def expert_nbytes(self) -> int:
+        return int(self.codes[0].nbytes + self.scales[0].nbytes + self.biases[0].nbytes)
 
 
 @dataclasses.dataclass
@@ -170,6 +197,29 @@ def q8_weight(g: np.random.Generator, n_experts: int, n: int, k: int) -> Q8:
     return Q8(codes, scales)
 
 
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """The bf16 nearest to each finite f32 (ties to even), as its 16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """The f32 that 16 bf16 bits stand for (format only)."""
+    return (np.asarray(bits, dtype=np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def q4e_weight(g: np.random.Generator, n_experts: int, n: int, k: int) -> Q4E:
+    """codes ~ U{0..15}; scale ~ U(0.005, 0.02) and bias = -8*scale + N(0, 1e-3),
+    each rounded to bf16."""
+    if k % GROUP:
+        raise ValueError("k must be a multiple of 32")
+    byte = g.integers(0, 256, size=(n_experts, n, k // 2), dtype=np.uint8)
+    codes = np.ascontiguousarray(byte).view("<u4").reshape(n_experts, n, k // 8).copy()
+    scales = g.uniform(0.005, 0.02, size=(n_experts, n, k // GROUP))
+    biases = -8.0 * scales + g.normal(0.0, 1e-3, size=(n_experts, n, k // GROUP))
+    return Q4E(codes, bf16_bits(scales.astype(np.float32)), bf16_bits(biases.astype(np.float32)))
+
+
 def normal(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return (g.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
 
@@ -220,32 +270,40 @@ def kv_cache(g: np.random.Generator, n_kv_heads: int, filled: int, capacity: int
 
 @dataclasses.dataclass
 class MoeInputs:
+    """Routed FFN weights and input rows; the expert matrices are all Q8
+    (8-bit experts) or all Q4E (4-bit experts with bf16 group constants)."""
     x: np.ndarray
     router: np.ndarray
-    gate_exps: Q8
-    up_exps: Q8
-    down_exps: Q8
-    sh_gate: Optional[Q8]
-    sh_up: Optional[Q8]
-    sh_down: Optional[Q8]
+    gate_exps: "Q8 | Q4E"
+    up_exps: "Q8 | Q4E"
+    down_exps: "Q8 | Q4E"
+    sh_gate: "Optional[Q8 | Q4E]"
+    sh_up: "Optional[Q8 | Q4E]"
+    sh_down: "Optional[Q8 | Q4E]"
     top_k: int
 
     @property
     def n_experts(self) -> int:
         return self.gate_exps.n_experts
 
+    @property
+    def q4(self) -> bool:
+        return isinstance(self.gate_exps, Q4E)
+
 
 def moe_inputs(g: np.random.Generator, m: int, hidden: int = 2048, n_experts: int = 256, inter: int = 512,
-               top_k: int = 8, shared_inter: Optional[int] = 512) -> MoeInputs:
+               top_k: int = 8, shared_inter: Optional[int] = 512, q4: bool = False) -> MoeInputs:
+    """q4: 4-bit experts with bf16 group constants instead of 8-bit ones."""
+    draw = q4e_weight if q4 else q8_weight
     x = normal(g, (m, hidden))
     router = normal(g, (n_experts, hidden), 0.02)
-    ge = q8_weight(g, n_experts, inter, hidden)
-    ue = q8_weight(g, n_experts, inter, hidden)
-    de = q8_weight(g, n_experts, hidden, inter)
+    ge = draw(g, n_experts, inter, hidden)
+    ue = draw(g, n_experts, inter, hidden)
+    de = draw(g, n_experts, hidden, inter)
     if shared_inter:
-        sg = q8_weight(g, 1, shared_inter, hidden)
-        su = q8_weight(g, 1, shared_inter, hidden)
-        sd = q8_weight(g, 1, hidden, shared_inter)
+        sg = draw(g, 1, shared_inter, hidden)
+        su = draw(g, 1, shared_inter, hidden)
+        sd = draw(g, 1, hidden, shared_inter)
     else:
         sg = su = sd = None
     return MoeInputs(x, router, ge, ue, de, sg, su, sd, top_k)

@@ -62,6 +62,11 @@ class _Q8(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
 
 
+class _Q4E(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("n", C.c_int32), ("k", C.c_int32)]
+
+
 class _Layer(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("vocab", C.c_int32), ("ffn_inter", C.c_int32),
@@ -78,7 +83,10 @@ class _Layer(C.Structure):
 class _MoeFfn(C.Structure):
     _fields_ = [("router", C.c_void_p), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("gate_exps", C.c_void_p), ("up_exps", C.c_void_p), ("down_exps", C.c_void_p),
-                ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p)]
+                ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+                ("q4", C.c_int32),
+                ("gate_exps4", C.c_void_p), ("up_exps4", C.c_void_p), ("down_exps4", C.c_void_p),
+                ("sh_gate4", C.c_void_p), ("sh_up4", C.c_void_p), ("sh_down4", C.c_void_p)]
 
 
 def lib():
@@ -93,6 +101,10 @@ def lib():
             "orc_unpack4": (None, [P, I, I, P]),
             "orc_deq4": (None, [P, P]),
             "orc_deq8": (None, [P, P]),
+            "orc_bf16": (C.c_float, [C.c_uint16]),
+            "orc_deq4e": (None, [P, P]),
+            "orc_gemv4e": (None, [P, P, I, P]),
+            "orc_moe4": (I, [P, P, I, I, P, P, P, P, P, P, P, I, P, P, P, P]),
             "orc_gemv4": (None, [P, P, I, P]),
             "orc_gemv8": (None, [P, P, I, P]),
             "orc_gemv_f32": (None, [P, I, I, P, I, P]),
@@ -162,6 +174,25 @@ def _q8_list(w, keep: _Keep):
     return arr
 
 
+def _q4e_list(w, keep: _Keep):
+    """Array of per-expert _Q4E descriptors over an [E, n, k/8] stack."""
+    c = keep.arr(w.codes, np.uint32)
+    s = keep.arr(w.scales, np.uint16)
+    b = keep.arr(w.biases, np.uint16)
+    E, n, kw = c.shape
+    g = kw * 8 // 32
+    arr = (_Q4E * E)()
+    for e in range(E):
+        arr[e] = _Q4E(c.ctypes.data + e * n * kw * 4, s.ctypes.data + e * n * g * 2, b.ctypes.data + e * n * g * 2,
+                      n, kw * 8)
+    keep.refs.append(arr)
+    return arr
+
+
+def _experts(w, keep: _Keep):
+    return _q4e_list(w, keep) if hasattr(w, "biases") and w.codes.ndim == 3 else _q8_list(w, keep)
+
+
 def _layer(L, keep: _Keep) -> _Layer:
     f = lambda a: keep.arr(a, np.float32).ctypes.data  # noqa: E731
     opt = lambda a: None if a is None else f(a)  # noqa: E731
@@ -201,6 +232,29 @@ def deq8(w, expert: int = 0) -> np.ndarray:
     out = np.empty((w.n, w.k), dtype=np.float32)
     lib().orc_deq8(C.byref(arr[expert]), _p(out))
     return out
+
+
+def bf16(bits) -> np.ndarray:
+    """The f32 values of bf16 bit patterns (one C call each)."""
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib().orc_bf16(int(v)) for v in b], dtype=np.float32).reshape(np.shape(bits))
+
+
+def deq4e(w, expert: int = 0) -> np.ndarray:
+    keep = _Keep()
+    arr = _q4e_list(w, keep)
+    out = np.empty((w.n, w.k), dtype=np.float32)
+    lib().orc_deq4e(C.byref(arr[expert]), _p(out))
+    return out
+
+
+def gemv4e(w, x: np.ndarray, expert: int = 0) -> np.ndarray:
+    keep = _Keep()
+    arr = _q4e_list(w, keep)
+    x = keep.arr(np.atleast_2d(x), np.float32)
+    y = np.empty((x.shape[0], w.n), dtype=np.float32)
+    lib().orc_gemv4e(C.byref(arr[expert]), _p(x), x.shape[0], _p(y))
+    return y
 
 
 def gemv4(w, x: np.ndarray) -> np.ndarray:
@@ -309,10 +363,10 @@ def moe(inp, x=None, residual=None):
     x = keep.arr(np.atleast_2d(inp.x if x is None else x), np.float32)
     router = keep.arr(inp.router, np.float32)
     m, E, K = x.shape[0], inp.n_experts, inp.top_k
-    ge, ue, de = _q8_list(inp.gate_exps, keep), _q8_list(inp.up_exps, keep), _q8_list(inp.down_exps, keep)
+    ge, ue, de = _experts(inp.gate_exps, keep), _experts(inp.up_exps, keep), _experts(inp.down_exps, keep)
     if inp.sh_gate is not None:
-        sg, su, sd = (C.byref(_q8_list(inp.sh_gate, keep)[0]), C.byref(_q8_list(inp.sh_up, keep)[0]),
-                      C.byref(_q8_list(inp.sh_down, keep)[0]))
+        sg, su, sd = (C.byref(_experts(inp.sh_gate, keep)[0]), C.byref(_experts(inp.sh_up, keep)[0]),
+                      C.byref(_experts(inp.sh_down, keep)[0]))
     else:
         sg = su = sd = None
     res = None if residual is None else keep.arr(np.atleast_2d(residual), np.float32)
@@ -320,8 +374,8 @@ def moe(inp, x=None, residual=None):
     ids = np.empty((m, K), dtype=np.int32)
     gates = np.empty((m, K), dtype=np.float32)
     logits = np.empty((m, E), dtype=np.float32)
-    rc = lib().orc_moe(_p(x), _p(router), E, K, ge, ue, de, sg, su, sd, _p(res), m, _p(y), _p(ids),
-                       _p(gates), _p(logits))
+    fn = lib().orc_moe4 if inp.q4 else lib().orc_moe
+    rc = fn(_p(x), _p(router), E, K, ge, ue, de, sg, su, sd, _p(res), m, _p(y), _p(ids), _p(gates), _p(logits))
     if rc != 0:
         raise ValueError("orc_moe rejected its arguments")
     return y, ids, gates, logits
@@ -357,18 +411,22 @@ def head8(hidden, gamma, eps, lm):
 
 def _moe_ffn(inp, keep: _Keep) -> _MoeFfn:
     router = keep.arr(inp.router, np.float32)
-    ge, ue, de = _q8_list(inp.gate_exps, keep), _q8_list(inp.up_exps, keep), _q8_list(inp.down_exps, keep)
-    addr = C.addressof
+    ws = [addr for addr in (C.addressof(_experts(w, keep)) for w in (inp.gate_exps, inp.up_exps, inp.down_exps))]
     sh = [None, None, None]
     if inp.sh_gate is not None:
-        sh = [addr(_q8_list(w, keep)) for w in (inp.sh_gate, inp.sh_up, inp.sh_down)]
-    return _MoeFfn(router.ctypes.data, int(inp.n_experts), int(inp.top_k), addr(ge), addr(ue), addr(de), *sh)
+        sh = [C.addressof(_experts(w, keep)) for w in (inp.sh_gate, inp.sh_up, inp.sh_down)]
+    if inp.q4:
+        return _MoeFfn(router.ctypes.data, int(inp.n_experts), int(inp.top_k), None, None, None, None, None, None,
+                       1, *ws, *sh)
+    return _MoeFfn(router.ctypes.data, int(inp.n_experts), int(inp.top_k), *ws, *sh, 0,
+                   None, None, None, None, None, None)
 
 
 def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_logits: bool = True, moe=None):
     """One draft-layer forward over m rows; appends K/V rows in place.  With
-    moe (a MoE input set of ``synth.moe_inputs``) the FFN is the routed 8-bit
-    mixture of those weights instead of the layer's dense SwiGLU.
+    moe (a MoE input set of ``synth.moe_inputs``, 8-bit or 4-bit experts) the
+    FFN is the routed mixture of those weights instead of the layer's dense
+    SwiGLU.
 
     Returns (ids [m], hidden_out [m, H] (post-final-norm), logits [m, V] or None)."""
     assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32

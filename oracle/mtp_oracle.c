@@ -66,6 +66,28 @@ void orc_deq8(const orc_q8* w, float* out) {
         }
 }
 
+/* The f32 a bf16 value stands for: its 16 bits are the upper half of that
+ * f32's bits, the lower half zero (so the widening is exact). */
+float orc_bf16(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* f32 dequantized 4-bit weight with bf16 group constants ([shared.rs]
+ * `MlxAffineMoeStack`): scale*code + bias with scale and bias widened to f32,
+ * the exact value rounded once (fmaf), as orc_deq4. */
+void orc_deq4e(const orc_q4e* w, float* out) {
+    const int32_t gpr = w->k / GROUP;
+    for (int32_t r = 0; r < w->n; ++r)
+        for (int32_t c = 0; c < w->k; ++c) {
+            size_t gi = (size_t)r * gpr + (size_t)(c / GROUP);
+            out[(size_t)r * w->k + c] =
+                fmaf(orc_bf16(w->scales[gi]), (float)code4(w->codes, w->k, r, c), orc_bf16(w->biases[gi]));
+        }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Primitives                                                                */
 /* ------------------------------------------------------------------------ */
@@ -108,6 +130,31 @@ void orc_gemv8(const orc_q8* w, const float* x, int32_t m, float* y) {
             for (int32_t c = 0; c < k; ++c)
                 row[c] = (double)w->scales[(size_t)o * gpr + (size_t)(c / GROUP)] *
                          (double)w->codes[(size_t)o * k + c];
+            for (int32_t r = 0; r < m; ++r) {
+                const float* xr = x + (size_t)r * k;
+                double acc = 0.0;
+                for (int32_t c = 0; c < k; ++c) acc += (double)xr[c] * row[c];
+                y[(size_t)r * n + o] = (float)acc;
+            }
+        }
+        free(row);
+    }
+}
+
+/* The 4-bit GEMV of orc_gemv4 over bf16 group constants: the weight
+ * scale*code + bias exact in double with scale and bias widened. */
+void orc_gemv4e(const orc_q4e* w, const float* x, int32_t m, float* y) {
+    const int32_t n = w->n, k = w->k, gpr = k / GROUP;
+#pragma omp parallel
+    {
+        double* row = (double*)xmalloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int32_t o = 0; o < n; ++o) {
+            for (int32_t c = 0; c < k; ++c) {
+                size_t gi = (size_t)o * gpr + (size_t)(c / GROUP);
+                row[c] = (double)orc_bf16(w->scales[gi]) * (double)code4(w->codes, k, o, c) +
+                         (double)orc_bf16(w->biases[gi]);
+            }
             for (int32_t r = 0; r < m; ++r) {
                 const float* xr = x + (size_t)r * k;
                 double acc = 0.0;
@@ -417,17 +464,109 @@ void orc_ffn_dense(const float* x, const orc_q4* gate, const orc_q4* up, const o
     free(dz);
 }
 
-/* One 8-bit SwiGLU expert applied to one row: out = down*(silu(gate x).(up x)). */
-static void expert8(const orc_q8* g, const orc_q8* u, const orc_q8* d, const float* x, float* out) {
-    const int32_t I = g->n;
+/* One SwiGLU expert applied to one row, out = down*(silu(gate x).(up x)),
+ * over 8-bit (q8 set) or 4-bit bf16-constant matrices. */
+typedef struct {
+    const orc_q8 *g8, *u8, *d8;
+    const orc_q4e *g4, *u4, *d4;
+} expert_w;
+
+static void expert(const expert_w* w, const float* x, float* out) {
+    const int32_t I = w->g8 ? w->g8->n : w->g4->n;
     float* a = (float*)xmalloc(sizeof(float) * (size_t)I);
     float* b = (float*)xmalloc(sizeof(float) * (size_t)I);
-    orc_gemv8(g, x, 1, a);
-    orc_gemv8(u, x, 1, b);
+    if (w->g8) {
+        orc_gemv8(w->g8, x, 1, a);
+        orc_gemv8(w->u8, x, 1, b);
+    } else {
+        orc_gemv4e(w->g4, x, 1, a);
+        orc_gemv4e(w->u4, x, 1, b);
+    }
     for (int32_t i = 0; i < I; ++i) a[i] = (float)(silu((double)a[i]) * (double)b[i]);
-    orc_gemv8(d, a, 1, out);
+    if (w->d8)
+        orc_gemv8(w->d8, a, 1, out);
+    else
+        orc_gemv4e(w->d4, a, 1, out);
     free(a);
     free(b);
+}
+
+/* Routing of one row: p = softmax(l) over all experts, the top_k experts by
+ * (p descending, index ascending) into sel, their gates p_e / (sum of the
+ * selected p) into gsel. */
+static void route_row(const float* l, int32_t n_experts, int32_t top_k, int32_t* sel, double* gsel) {
+    double* p = (double*)xmalloc(sizeof(double) * (size_t)n_experts);
+    char* taken = (char*)xmalloc((size_t)n_experts);
+    double mx = -INFINITY, z = 0.0;
+    for (int32_t e = 0; e < n_experts; ++e)
+        if ((double)l[e] > mx) mx = (double)l[e];
+    for (int32_t e = 0; e < n_experts; ++e) {
+        p[e] = exp((double)l[e] - mx);
+        z += p[e];
+    }
+    for (int32_t e = 0; e < n_experts; ++e) p[e] /= z;
+    memset(taken, 0, (size_t)n_experts);
+    double psum = 0.0;
+    for (int32_t s = 0; s < top_k; ++s) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < n_experts; ++e)
+            if (!taken[e] && (best < 0 || p[e] > p[best])) best = e;
+        taken[best] = 1;
+        sel[s] = best;
+        psum += p[best];
+    }
+    for (int32_t s = 0; s < top_k; ++s) gsel[s] = p[sel[s]] / psum;
+    free(p);
+    free(taken);
+}
+
+/* The mixture over rows; ex(e) gives expert e's matrices, sh the shared
+ * expert's (NULL: none). */
+static int32_t moe_rows(const float* x, const float* router, int32_t n_experts, int32_t top_k, int32_t H,
+                        const orc_q8* ge8, const orc_q8* ue8, const orc_q8* de8, const orc_q4e* ge4,
+                        const orc_q4e* ue4, const orc_q4e* de4, const expert_w* sh, const float* residual,
+                        int32_t m, float* y, int32_t* expert_ids, float* gates, float* router_logits) {
+    if (top_k < 1 || top_k > n_experts) return -1;
+    float* l = (float*)xmalloc(sizeof(float) * (size_t)n_experts);
+    int32_t* sel = (int32_t*)xmalloc(sizeof(int32_t) * (size_t)top_k);
+    double* gsel = (double*)xmalloc(sizeof(double) * (size_t)top_k);
+    float* eo = (float*)xmalloc(sizeof(float) * (size_t)H);
+    double* acc = (double*)xmalloc(sizeof(double) * (size_t)H);
+    for (int32_t r = 0; r < m; ++r) {
+        const float* xr = x + (size_t)r * H;
+        orc_gemv_f32(router, n_experts, H, xr, 1, l);
+        if (router_logits) memcpy(router_logits + (size_t)r * n_experts, l, sizeof(float) * (size_t)n_experts);
+        route_row(l, n_experts, top_k, sel, gsel);
+        for (int32_t i = 0; i < H; ++i) acc[i] = residual ? (double)residual[(size_t)r * H + i] : 0.0;
+        for (int32_t s = 0; s < top_k; ++s) {
+            const int32_t e = sel[s];
+            expert_w w = {NULL, NULL, NULL, NULL, NULL, NULL};
+            if (ge8) {
+                w.g8 = &ge8[e];
+                w.u8 = &ue8[e];
+                w.d8 = &de8[e];
+            } else {
+                w.g4 = &ge4[e];
+                w.u4 = &ue4[e];
+                w.d4 = &de4[e];
+            }
+            expert(&w, xr, eo);
+            for (int32_t i = 0; i < H; ++i) acc[i] += gsel[s] * (double)eo[i];
+            if (expert_ids) expert_ids[(size_t)r * top_k + s] = e;
+            if (gates) gates[(size_t)r * top_k + s] = (float)gsel[s];
+        }
+        if (sh) {
+            expert(sh, xr, eo);
+            for (int32_t i = 0; i < H; ++i) acc[i] += (double)eo[i];
+        }
+        for (int32_t i = 0; i < H; ++i) y[(size_t)r * H + i] = (float)acc[i];
+    }
+    free(l);
+    free(sel);
+    free(gsel);
+    free(eo);
+    free(acc);
+    return 0;
 }
 
 /* Routed mixture of 8-bit SwiGLU experts plus one always-on shared expert
@@ -443,60 +582,21 @@ int32_t orc_moe(const float* x, const float* router, int32_t n_experts, int32_t 
                 const orc_q8* sh_gate, const orc_q8* sh_up, const orc_q8* sh_down,
                 const float* residual, int32_t m, float* y, int32_t* expert_ids, float* gates,
                 float* router_logits) {
-    if (top_k < 1 || top_k > n_experts) return -1;
-    const int32_t H = gate_exps[0].k;
-    float* l = (float*)xmalloc(sizeof(float) * (size_t)n_experts);
-    double* p = (double*)xmalloc(sizeof(double) * (size_t)n_experts);
-    char* taken = (char*)xmalloc((size_t)n_experts);
-    int32_t* sel = (int32_t*)xmalloc(sizeof(int32_t) * (size_t)top_k);
-    double* gsel = (double*)xmalloc(sizeof(double) * (size_t)top_k);
-    float* eo = (float*)xmalloc(sizeof(float) * (size_t)H);
-    double* acc = (double*)xmalloc(sizeof(double) * (size_t)H);
-    for (int32_t r = 0; r < m; ++r) {
-        const float* xr = x + (size_t)r * H;
-        orc_gemv_f32(router, n_experts, H, xr, 1, l);
-        if (router_logits) memcpy(router_logits + (size_t)r * n_experts, l, sizeof(float) * (size_t)n_experts);
-        double mx = -INFINITY, z = 0.0;
-        for (int32_t e = 0; e < n_experts; ++e)
-            if ((double)l[e] > mx) mx = (double)l[e];
-        for (int32_t e = 0; e < n_experts; ++e) {
-            p[e] = exp((double)l[e] - mx);
-            z += p[e];
-        }
-        for (int32_t e = 0; e < n_experts; ++e) p[e] /= z;
-        memset(taken, 0, (size_t)n_experts);
-        double psum = 0.0;
-        for (int32_t s = 0; s < top_k; ++s) {
-            int32_t best = -1;
-            for (int32_t e = 0; e < n_experts; ++e)
-                if (!taken[e] && (best < 0 || p[e] > p[best])) best = e;
-            taken[best] = 1;
-            sel[s] = best;
-            psum += p[best];
-        }
-        for (int32_t s = 0; s < top_k; ++s) gsel[s] = p[sel[s]] / psum;
-        for (int32_t i = 0; i < H; ++i) acc[i] = residual ? (double)residual[(size_t)r * H + i] : 0.0;
-        for (int32_t s = 0; s < top_k; ++s) {
-            const int32_t e = sel[s];
-            expert8(&gate_exps[e], &up_exps[e], &down_exps[e], xr, eo);
-            for (int32_t i = 0; i < H; ++i) acc[i] += gsel[s] * (double)eo[i];
-            if (expert_ids) expert_ids[(size_t)r * top_k + s] = e;
-            if (gates) gates[(size_t)r * top_k + s] = (float)gsel[s];
-        }
-        if (sh_gate) {
-            expert8(sh_gate, sh_up, sh_down, xr, eo);
-            for (int32_t i = 0; i < H; ++i) acc[i] += (double)eo[i];
-        }
-        for (int32_t i = 0; i < H; ++i) y[(size_t)r * H + i] = (float)acc[i];
-    }
-    free(l);
-    free(p);
-    free(taken);
-    free(sel);
-    free(gsel);
-    free(eo);
-    free(acc);
-    return 0;
+    expert_w sh = {sh_gate, sh_up, sh_down, NULL, NULL, NULL};
+    return moe_rows(x, router, n_experts, top_k, gate_exps[0].k, gate_exps, up_exps, down_exps, NULL, NULL, NULL,
+                    sh_gate ? &sh : NULL, residual, m, y, expert_ids, gates, router_logits);
+}
+
+/* The same mixture over 4-bit experts with bf16 group constants ([shared.rs]
+ * `MlxAffineMoeStack`), the shared expert in the same form. */
+int32_t orc_moe4(const float* x, const float* router, int32_t n_experts, int32_t top_k,
+                 const orc_q4e* gate_exps, const orc_q4e* up_exps, const orc_q4e* down_exps,
+                 const orc_q4e* sh_gate, const orc_q4e* sh_up, const orc_q4e* sh_down,
+                 const float* residual, int32_t m, float* y, int32_t* expert_ids, float* gates,
+                 float* router_logits) {
+    expert_w sh = {NULL, NULL, NULL, sh_gate, sh_up, sh_down};
+    return moe_rows(x, router, n_experts, top_k, gate_exps[0].k, NULL, NULL, NULL, gate_exps, up_exps, down_exps,
+                    sh_gate ? &sh : NULL, residual, m, y, expert_ids, gates, router_logits);
 }
 
 /* Shared head with greedy pick: yn = rms(hidden; gamma), logits = LM yn,
@@ -529,14 +629,17 @@ void orc_head8(const float* hidden, const float* gamma, float eps, const orc_q8*
     if (!logits_out) free(lg);
 }
 
-/* The layer's two FFN forms behind one wiring: the dense 4-bit SwiGLU of the
- * layer, or the routed 8-bit mixture when moe is given. */
+/* The layer's FFN forms behind one wiring: the dense 4-bit SwiGLU of the
+ * layer, or the routed mixture (8-bit or 4-bit experts) when moe is given. */
 static int32_t ffn_residual(const orc_layer* L, const orc_moe_ffn* moe, const float* f, const float* r1, int32_t m,
                             float* r2) {
     if (!moe) {
         orc_ffn_dense(f, &L->gate, &L->up, &L->down, r1, m, r2);
         return 0;
     }
+    if (moe->q4)
+        return orc_moe4(f, moe->router, moe->n_experts, moe->top_k, moe->gate_exps4, moe->up_exps4,
+                        moe->down_exps4, moe->sh_gate4, moe->sh_up4, moe->sh_down4, r1, m, r2, NULL, NULL, NULL);
     return orc_moe(f, moe->router, moe->n_experts, moe->top_k, moe->gate_exps, moe->up_exps, moe->down_exps,
                    moe->sh_gate, moe->sh_up, moe->sh_down, r1, m, r2, NULL, NULL, NULL);
 }
@@ -559,7 +662,9 @@ static int32_t draft_step(const orc_layer* L, const orc_moe_ffn* moe, const floa
                           float* logits_out) {
     const int32_t H = L->hidden;
     if (m < 1 || cache_len < 0 || cache_len + m > capacity) return -1;
-    if (moe && (moe->top_k < 1 || moe->top_k > moe->n_experts || moe->gate_exps[0].k != H)) return -1;
+    if (moe && (moe->top_k < 1 || moe->top_k > moe->n_experts ||
+                (moe->q4 ? moe->gate_exps4[0].k : moe->gate_exps[0].k) != H))
+        return -1;
     for (int32_t r = 0; r < m; ++r) {
         int use_table = tokens && tokens[r] >= 0;
         if (use_table && (!embed_table || tokens[r] >= L->vocab)) return -1;

@@ -16,9 +16,10 @@
  *   - the f32 dequantized weight is the exact affine value rounded once
  *     (fmaf), while the products inside a GEMV use the exact value in double.
  *
- * Parity-unpinned parts: absolute values of a whole draft step.  The pages
- * print no outputs for it; it is pinned only through invariants (batched
- * equals sequential, length-1 attention returns V, gates sum to one, ...).
+ * Pins: the pages print values for the 4-bit GEMV only; every other function
+ * is pinned by closed forms written out in numpy (f64, from the raw codes),
+ * special cases that reduce to a textbook routine, brute force on tiny
+ * inputs and invariants (batched equals sequential, gates sum to one, ...).
  */
 #ifndef MTP_ORACLE_H
 #define MTP_ORACLE_H
@@ -47,6 +48,19 @@ typedef struct {
     const float* scales;
     int32_t n, k;
 } orc_q8;
+
+/* 4-bit affine matrix with bf16 group constants, one matrix of an expert
+ * stack ([shared.rs] `MlxAffineMoeStack`: packed-u32 codes [e][n][k/8] in the
+ * nibble order of orc_q4, bf16 scales and biases [e][n][k/32]).  A bf16 value
+ * is stored as its 16 bits, the upper half of the f32 it stands for; the
+ * weight is scale*code + bias with scale and bias widened to f32.  Expert
+ * stacks are passed as arrays of these. */
+typedef struct {
+    const uint32_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    int32_t n, k;
+} orc_q4e;
 
 /* One dense MTP draft layer ([mimo.rs] module doc "The draft forward";
  * [mtp.rs] `MtpWeights`).  Attention variant of [mtp.rs]
@@ -85,25 +99,33 @@ typedef struct {
     int32_t v_head_dim;
 } orc_layer;
 
-/* The routed 8-bit FFN of the MoE draft layer ([mtp.rs]
- * `MtpFfnWeightsGpu::Moe`): f32 router [n_experts][hidden], per-expert 8-bit
- * gate/up [inter][hidden] and down [hidden][inter] (arrays of n_experts
- * matrices), and an optional shared expert (sh_gate NULL: none). */
+/* The routed FFN of the MoE draft layer ([mtp.rs] `MtpFfnWeightsGpu::Moe`):
+ * f32 router [n_experts][hidden], per-expert gate/up [inter][hidden] and down
+ * [hidden][inter] (arrays of n_experts matrices), and an optional shared
+ * expert (its gate NULL: none).  q4 = 0: the 8-bit matrices (gate_exps ...);
+ * q4 != 0: the 4-bit bf16-constant matrices of [shared.rs]
+ * `MlxAffineMoeStack` (gate_exps4 ...), the shared expert in the same form. */
 typedef struct {
     const float* router;
     int32_t n_experts, top_k;
     const orc_q8 *gate_exps, *up_exps, *down_exps;
     const orc_q8 *sh_gate, *sh_up, *sh_down;
+    int32_t q4;
+    const orc_q4e *gate_exps4, *up_exps4, *down_exps4;
+    const orc_q4e *sh_gate4, *sh_up4, *sh_down4;
 } orc_moe_ffn;
 
 /* ---- weight formats ---- */
 void orc_unpack4(const uint32_t* codes, int32_t n, int32_t k, uint8_t* out);
 void orc_deq4(const orc_q4* w, float* out);
 void orc_deq8(const orc_q8* w, float* out);
+float orc_bf16(uint16_t bits);
+void orc_deq4e(const orc_q4e* w, float* out);
 
 /* ---- primitives ---- */
 void orc_gemv4(const orc_q4* w, const float* x, int32_t m, float* y);
 void orc_gemv8(const orc_q8* w, const float* x, int32_t m, float* y);
+void orc_gemv4e(const orc_q4e* w, const float* x, int32_t m, float* y);
 void orc_gemv_f32(const float* w, int32_t n, int32_t k, const float* x, int32_t m, float* y);
 void orc_rmsnorm(const float* x, const float* gamma, int32_t m, int32_t h, float eps, float* y);
 void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t pos0, double theta);
@@ -132,6 +154,11 @@ int32_t orc_moe(const float* x, const float* router, int32_t n_experts, int32_t 
                 const orc_q8* sh_gate, const orc_q8* sh_up, const orc_q8* sh_down,
                 const float* residual, int32_t m, float* y, int32_t* expert_ids, float* gates,
                 float* router_logits);
+int32_t orc_moe4(const float* x, const float* router, int32_t n_experts, int32_t top_k,
+                 const orc_q4e* gate_exps, const orc_q4e* up_exps, const orc_q4e* down_exps,
+                 const orc_q4e* sh_gate, const orc_q4e* sh_up, const orc_q4e* sh_down,
+                 const float* residual, int32_t m, float* y, int32_t* expert_ids, float* gates,
+                 float* router_logits);
 void orc_head(const float* hidden, const float* gamma, float eps, const orc_q4* lm_head, int32_t m,
               float* normed_out, float* logits_out, int32_t* ids_out);
 void orc_head8(const float* hidden, const float* gamma, float eps, const orc_q8* lm_head, int32_t m,
@@ -143,8 +170,8 @@ int32_t orc_draft_step(const orc_layer* L, const float* e, const int32_t* tokens
                        const float* embed_table, const float* h, float* k_cache, float* v_cache,
                        int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out,
                        float* hidden_out, float* logits_out);
-/* The same forward with the routed 8-bit FFN in place of the dense one (the
- * layer's gate/up/down are not read). */
+/* The same forward with the routed FFN (8-bit or 4-bit experts) in place of
+ * the dense one (the layer's gate/up/down are not read). */
 int32_t orc_draft_step_moe(const orc_layer* L, const orc_moe_ffn* moe, const float* e, const int32_t* tokens,
                            const float* embed_table, const float* h, float* k_cache, float* v_cache,
                            int32_t cache_len, int32_t capacity, int32_t m, int32_t* ids_out, float* hidden_out,

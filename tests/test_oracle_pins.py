@@ -490,9 +490,9 @@ def test_ffn_zero_gate_returns_residual_and_closed_form():
     assert abs(dd[0, 0] - np.float32(wd[0, 0])) == 0
 
 
-def _moe_small(seed, E=6, k=2, H=64, inter=32, shared=32, m=3):
+def _moe_small(seed, E=6, k=2, H=64, inter=32, shared=32, m=3, q4=False):
     return synth.moe_inputs(np.random.default_rng(seed), m, hidden=H, n_experts=E, inter=inter, top_k=k,
-                            shared_inter=shared)
+                            shared_inter=shared, q4=q4)
 
 
 def test_moe_gates_sum_to_one_and_selection_is_a_full_sort():
@@ -854,6 +854,30 @@ def _exact_q8(w, e: int) -> np.ndarray:
     return w.codes[e].astype(np.float64) * np.repeat(w.scales[e].astype(np.float64), 32, 1)
 
 
+def _bf16_f64(bits) -> np.ndarray:
+    """bf16 bits as values, from the format's fields (sign, 8-bit biased
+    exponent, 7-bit fraction); finite patterns only."""
+    b = np.asarray(bits, np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    ex = (b >> 7) & 0xFF
+    fr = (b & 0x7F).astype(np.float64)
+    normal = np.ldexp(1.0 + fr / 128.0, (ex - 127).astype(np.int64))
+    sub = np.ldexp(fr / 128.0, -126)
+    return sign * np.where(ex == 0, sub, normal)
+
+
+def _exact_q4e(w, e: int) -> np.ndarray:
+    """Exact values s*q + b in f64 of expert e of a 4-bit stack with bf16
+    constants, from the raw codes (low nibble = lowest k) and the bf16 fields."""
+    c = np.asarray(w.codes[e], np.uint64)
+    q = np.stack([(c >> np.uint64(4 * i)) & np.uint64(15) for i in range(8)], axis=-1).reshape(c.shape[0], -1)
+    return q.astype(np.float64) * np.repeat(_bf16_f64(w.scales[e]), 32, 1) + np.repeat(_bf16_f64(w.biases[e]), 32, 1)
+
+
+def _exact_ex(w, e: int) -> np.ndarray:
+    return _exact_q4e(w, e) if isinstance(w, synth.Q4E) else _exact_q8(w, e)
+
+
 def _rms64(x, gam, eps):
     x = np.asarray(x, np.float64)
     return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * np.asarray(gam, np.float64)
@@ -879,24 +903,25 @@ def _moe64(inp, x):
         sel = sorted(range(p.size), key=lambda e: (-p[e], e))[: inp.top_k]
         g = p[sel] / p[sel].sum()
         for ge, e in zip(g, sel):
-            out[r] += ge * _swiglu64(_exact_q8(inp.gate_exps, e), _exact_q8(inp.up_exps, e),
-                                     _exact_q8(inp.down_exps, e), x[r])
+            out[r] += ge * _swiglu64(_exact_ex(inp.gate_exps, e), _exact_ex(inp.up_exps, e),
+                                     _exact_ex(inp.down_exps, e), x[r])
         if inp.sh_gate is not None:
-            out[r] += _swiglu64(_exact_q8(inp.sh_gate, 0), _exact_q8(inp.sh_up, 0), _exact_q8(inp.sh_down, 0), x[r])
+            out[r] += _swiglu64(_exact_ex(inp.sh_gate, 0), _exact_ex(inp.sh_up, 0), _exact_ex(inp.sh_down, 0), x[r])
     return out
 
 
-def test_moe_expert_body_one_hot_closed_form():
+@pytest.mark.parametrize("q4", [False, True])
+def test_moe_expert_body_one_hot_closed_form(q4):
     """One expert, top-1, no shared expert: with x = e_j the expert's gate and
     up rows are single weights, so y = Wd (silu(Wg[:, j]) * Wu[:, j])."""
-    inp = _moe_small(34, E=1, k=1, shared=0, m=2)
+    inp = _moe_small(34, E=1, k=1, shared=0, m=2, q4=q4)
     js = [5, 50]
     x = np.zeros((2, 64), np.float32)
     x[0, js[0]] = 1.0
     x[1, js[1]] = 1.0
     y, ids, gates, _ = oracle.moe(inp, x=x)
     assert (ids == 0).all() and (gates == 1.0).all()
-    wg, wu, wd = _exact_q8(inp.gate_exps, 0), _exact_q8(inp.up_exps, 0), _exact_q8(inp.down_exps, 0)
+    wg, wu, wd = _exact_ex(inp.gate_exps, 0), _exact_ex(inp.up_exps, 0), _exact_ex(inp.down_exps, 0)
     for r, j in enumerate(js):
         a = wg[:, j].astype(np.float32).astype(np.float64)  # f32 activations between the steps
         b = wu[:, j].astype(np.float32).astype(np.float64)
@@ -905,10 +930,11 @@ def test_moe_expert_body_one_hot_closed_form():
         assert np.allclose(y[r], want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
 
 
-def test_moe_top2_with_shared_matches_the_f64_mixture():
+@pytest.mark.parametrize("q4", [False, True])
+def test_moe_top2_with_shared_matches_the_f64_mixture(q4):
     """E = 3 experts, top-2 with renormalised gates, plus the shared expert,
     on random rows: every term written out in numpy."""
-    inp = _moe_small(35, E=3, k=2, m=3)
+    inp = _moe_small(35, E=3, k=2, m=3, q4=q4)
     y, ids, gates, _ = oracle.moe(inp)
     want = _moe64(inp, inp.x)
     scale = np.abs(want).max()
@@ -920,6 +946,8 @@ def _zeroed(w):
 
 
 def _zeroed8(w):
+    if isinstance(w, synth.Q4E):  # bf16 zero is the bit pattern 0
+        return synth.Q4E(w.codes, np.zeros_like(w.scales), np.zeros_like(w.biases))
     return synth.Q8(w.codes, np.zeros_like(w.scales))
 
 
@@ -960,12 +988,13 @@ def test_draft_step_wiring_dense():
     assert np.allclose(hid, want, rtol=0, atol=2e-5 * np.abs(want).max())
 
 
-def test_draft_step_wiring_moe():
-    """The same wiring with the routed 8-bit FFN (experts zeroed through
-    their gate matrices, the shared expert's included)."""
+@pytest.mark.parametrize("q4", [False, True])
+def test_draft_step_wiring_moe(q4):
+    """The same wiring with the routed FFN, 8-bit or 4-bit experts (experts
+    zeroed through their gate matrices, the shared expert's included)."""
     L, kc, vc, L0, e, h, u = _wiring_case(58)
     inp = synth.moe_inputs(np.random.default_rng(59), 2, hidden=L.hidden, n_experts=6, inter=32, top_k=2,
-                           shared_inter=32)
+                           shared_inter=32, q4=q4)
     quiet = dataclasses.replace(inp, gate_exps=_zeroed8(inp.gate_exps), sh_gate=_zeroed8(inp.sh_gate))
     L_wo0 = dataclasses.replace(L, wo=_zeroed(L.wo))
     _, hid, _ = oracle.draft_step(L_wo0, e, None, None, h, kc.copy(), vc.copy(), L0, moe=quiet)
@@ -986,10 +1015,11 @@ def test_draft_step_wiring_moe():
     assert np.array_equal(hid, hid2)
 
 
-def test_draft_step_moe_batched_verify_equals_the_sequential_chain():
+@pytest.mark.parametrize("q4", [False, True])
+def test_draft_step_moe_batched_verify_equals_the_sequential_chain(q4):
     L = _small_layer(60)
     inp = synth.moe_inputs(np.random.default_rng(61), 1, hidden=L.hidden, n_experts=8, inter=32, top_k=2,
-                           shared_inter=32)
+                           shared_inter=32, q4=q4)
     g = np.random.default_rng(62)
     cap, L0 = 40, 30
     kc, vc = synth.kv_cache(g, L.n_kv_heads, L0, cap, L.head_dim)
@@ -1030,3 +1060,54 @@ def test_threaded_oracle_build_gives_the_same_bits():
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+
+
+# --------------------------------------------------------------------------
+# 4-bit expert matrices with bf16 group constants
+# --------------------------------------------------------------------------
+def test_bf16_widening_follows_the_format_fields():
+    """Every finite bf16 pattern widens to the value its sign, exponent and
+    fraction fields define (subnormals included); infinities and NaN stay."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16(bits).astype(np.float64)
+    ex = (bits.astype(np.int64) >> 7) & 0xFF
+    fin = ex != 0xFF
+    assert np.array_equal(got[fin], _bf16_f64(bits[fin]))
+    inf = ~fin & ((bits & 0x7F) == 0)
+    assert np.all(np.isinf(got[inf])) and np.all(np.isnan(got[~fin & ~inf]))
+    assert got[0x3F80] == 1.0 and got[0xC000] == -2.0 and got[0x0001] == 2.0 ** -133
+
+
+def test_deq4e_hand_case_and_exact_rounding():
+    """scale 0.5 and bias -4 (exact in bf16) give 0.5 c - 4 per element; on
+    random stacks the f32 weight is the exact f64 value s c + b rounded once,
+    and equals the f32-constant 4-bit format's dequantization of the same
+    codes with the widened constants."""
+    codes = np.arange(64, dtype=np.uint8).reshape(2, 32) % 16
+    packed = synth.pack_q4(codes)[None]
+    sc = np.array([[[0x3F00]], [[0x3F00]]], np.uint16).reshape(1, 2, 1)
+    bi = np.array([0xC080, 0xC080], np.uint16).reshape(1, 2, 1)
+    w = synth.Q4E(packed, sc, bi)
+    assert np.array_equal(oracle.deq4e(w), 0.5 * codes.astype(np.float32) - 4.0)
+    st = synth.q4e_weight(np.random.default_rng(71), 3, 40, 96)
+    for e in range(3):
+        got = oracle.deq4e(st, e)
+        assert np.array_equal(got, _exact_q4e(st, e).astype(np.float32))
+        as_q4 = synth.Q4(st.codes[e], _bf16_f64(st.scales[e]).astype(np.float32),
+                         _bf16_f64(st.biases[e]).astype(np.float32))
+        assert np.array_equal(got.view(np.uint32), oracle.deq4(as_q4).view(np.uint32))
+
+
+def test_gemv4e_is_the_4bit_gemv_on_widened_constants():
+    """The bf16-constant GEMV equals the (page-pinned) f32-constant 4-bit GEMV
+    of the same codes with the constants widened, bit for bit, and a one-hot
+    row returns one column of the exact weights."""
+    st = synth.q4e_weight(np.random.default_rng(72), 2, 50, 128)
+    x = synth.normal(np.random.default_rng(73), (3, 128))
+    for e in range(2):
+        as_q4 = synth.Q4(st.codes[e], _bf16_f64(st.scales[e]).astype(np.float32),
+                         _bf16_f64(st.biases[e]).astype(np.float32))
+        assert np.array_equal(oracle.gemv4e(st, x, e), oracle.gemv4(as_q4, x))
+        one = np.zeros((1, 128), np.float32)
+        one[0, 77] = 1.0
+        assert np.array_equal(oracle.gemv4e(st, one, e)[0], _exact_q4e(st, e)[:, 77].astype(np.float32))
