@@ -248,30 +248,36 @@ def attn_only(torch, mtp, synth, dev, reps):
 # the measured read ceiling (plain read stream, libmtp_bench.so)
 # --------------------------------------------------------------------------
 def read_ceiling(torch, dev, nbytes, K):
-    """GB/s of a plain nontemporal read stream over nbytes, three rotated
-    buffers (past the Infinity Cache), K captured launches."""
+    """GB/s of plain nontemporal read streams over nbytes, three rotated
+    buffers (past the Infinity Cache), K back-to-back launches between one
+    event pair: a grid-stride kernel and two with contiguous per-wave shares
+    (4 KB and 8 KB tiles) at a few grid sizes; the fastest is the ceiling."""
     path = os.path.join(ROOT, "mtp_speculative_draft_amd", "libmtp_bench.so")
     if not os.path.exists(path):
         return None
     lib = C.CDLL(path)
     lib.mtp_bench_read_stream.restype = C.c_int
-    lib.mtp_bench_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    lib.mtp_bench_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
     nb = (nbytes + 15) // 16 * 16
     bufs = [torch.ones(nb // 4, dtype=torch.float32, device=dev) for _ in range(3)]
-    blocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
-    out = torch.empty(blocks, dtype=torch.float32, device=dev)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(8 * cu, dtype=torch.float32, device=dev)
+    variants = {}
+    for mode, blocks in ((0, 8 * cu), (1, cu), (1, 2 * cu), (2, cu), (2, 2 * cu)):
+        def call(i, mode=mode, blocks=blocks):
+            rc = lib.mtp_bench_read_stream(C.c_void_p(bufs[i % 3].data_ptr()), nb, C.c_void_p(out.data_ptr()), blocks,
+                                           mode, C.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"read stream launch failed: {rc}")
 
-    def call(i):
-        rc = lib.mtp_bench_read_stream(C.c_void_p(bufs[i % 3].data_ptr()), nb, C.c_void_p(out.data_ptr()), blocks,
-                                       C.c_void_p(torch.cuda.current_stream().cuda_stream))
-        if rc != 0:
-            raise RuntimeError(f"read stream launch failed: {rc}")
-
-    us = eager_region_us(torch, call, K)
+        us = eager_region_us(torch, call, K)
+        variants[f"{('grid_stride', 'chunks_4k', 'chunks_8k')[mode]}_b{blocks}"] = r3(us)
     del bufs
-    return {"GB/s": round(nb / us / 1e3, 1), "bytes": nb, "us": r3(us),
-            "kernel": "plain nontemporal float4 read stream (libmtp_bench.so), 3 rotated buffers, back-to-back "
-                      "launches between one event pair"}
+    best = min(variants, key=variants.get)
+    us = variants[best]
+    return {"GB/s": round(nb / us / 1e3, 1), "bytes": nb, "us": us, "best": best, "us_by_variant": variants,
+            "kernel": "plain nontemporal float4 read streams (libmtp_bench.so), 3 rotated buffers, back-to-back "
+                      "launches between one event pair; the fastest variant"}
 
 
 # --------------------------------------------------------------------------
@@ -357,20 +363,75 @@ def time_steps(torch, chain, verify, outputs, R, K, W):
     return eager, st_step, st_chain, st_verify, same, ref
 
 
-def moe_layer_bench(torch, mtp, synth, dev, K, W):
+def stage_split(torch, mtp, S, layers, caches, dev, n):
+    """One m = 1 draft step of the dense layer split into the stages the
+    pages' draft profile reports (projection, attention, FFN, head), each run
+    through its own libmtp call over the rotated weight copies and timed as
+    graph GPU time per call; their sum is compared with the chain's per-draft
+    time by the reader (each stage call carries its own launch boundary)."""
+    L = S.layer
+    H, V, L0 = L.hidden, L.vocab, S.cache_len
+    R = len(layers)
+    e = torch.from_numpy(S.e0).to(dev)
+    h = torch.from_numpy(S.h0[:1]).to(dev)
+    u = torch.empty((1, H), dtype=torch.float32, device=dev)
+    r1 = torch.empty((1, H), dtype=torch.float32, device=dev)
+    r2 = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ids = torch.empty(1, dtype=torch.int32, device=dev)
+    ws_a = torch.zeros(mtp.mtp_attn_decode_workspace_size(layers[0], L0, 1), dtype=torch.uint8, device=dev)
+    ws_f = torch.zeros(mtp.mtp_ffn_dense_workspace_size(L.ffn_inter, 1), dtype=torch.uint8, device=dev)
+    ws_h = torch.zeros(mtp.mtp_lmhead_workspace_size(V, 1), dtype=torch.uint8, device=dev)
+    mtp.mtp_norm_concat_proj(e, h, layers[0].gammas[0], layers[0].gammas[1], L.eps, layers[0].q4["eh_proj"], u=u)
+    mtp.mtp_attn_decode(layers[0], u, caches[0][0], caches[0][1], L0, out=r1, ws=ws_a)
+    mtp.mtp_ffn_dense_q(r1, layers[0].gammas[3], L.eps, layers[0].q4["gate"], layers[0].q4["up"],
+                        layers[0].q4["down"], residual=r1, y=r2, ws=ws_f)
+
+    def proj(i):
+        dl = layers[i % R]
+        mtp.mtp_norm_concat_proj(e, h, dl.gammas[0], dl.gammas[1], L.eps, dl.q4["eh_proj"], u=u)
+
+    def attn(i):
+        dl, (kc, vc) = layers[i % R], caches[i % R]
+        mtp.mtp_attn_decode(dl, u, kc, vc, L0, out=r1, ws=ws_a)
+
+    def ffn(i):
+        dl = layers[i % R]
+        mtp.mtp_ffn_dense_q(r1, dl.gammas[3], L.eps, dl.q4["gate"], dl.q4["up"], dl.q4["down"], residual=r1, y=r2,
+                            ws=ws_f)
+
+    def head(i):
+        dl = layers[i % R]
+        mtp.mtp_lmhead_argmax(r2, dl.gammas[4], L.eps, dl.q4["lm_head"], ids_out=ids, ws=ws_h)
+
+    out = {"note": "GPU time per call of each stage's libmtp call (graph-captured, weights rotated); "
+                   "proj = e/h norms + eh_proj, attn = attention norm + q/k/v + RoPE/append + SDPA + wo, "
+                   "ffn = post-attention norm + gate/up + SwiGLU + down, head = final norm + lm_head + argmax"}
+    total = 0.0
+    for name, fn in (("proj", proj), ("attn", attn), ("ffn", ffn), ("head", head)):
+        us = graph_region_us(torch, fn, max(n, 3 * R))
+        out[f"{name}_us"] = r3(us)
+        total += us
+    out["sum_us"] = r3(total)
+    return out
+
+
+def moe_layer_bench(torch, mtp, synth, dev, K, W, q4=False):
     """The MoE draft layer at full size: the dense layer's attention, eh_proj
-    and lm_head (vocab 151936) with the routed 8-bit FFN (256 experts, top-8,
-    shared expert, intermediate 512) in place of the SwiGLU; K=3 chain at m=1
-    and verify at m=4 over a 4096-row cache, two rotated copies."""
+    and lm_head (vocab 151936) with the routed FFN (256 experts, top-8, shared
+    expert, intermediate 512; 8-bit experts, or 4-bit with bf16 constants) in
+    place of the SwiGLU; K=3 chain at m=1 and verify at m=4 over a 4096-row
+    cache, two rotated copies."""
     S = synth.config4_step()
-    moe = synth.moe_inputs(synth.rng(30, 0), 1, hidden=2048, n_experts=256, inter=512, top_k=8, shared_inter=512)
+    moe = synth.moe_inputs(synth.rng(30, 0), 1, hidden=2048, n_experts=256, inter=512, top_k=8, shared_inter=512,
+                           q4=q4)
     R = 2
     layers = [mtp.DeviceLayer(S.layer, dev, moe=moe) for _ in range(R)]
     caches = [(torch.from_numpy(S.k_cache).to(dev), torch.from_numpy(S.v_cache).to(dev)) for _ in range(R)]
     chain, verify, outputs, _ = step_runner(torch, mtp, S, layers, caches, dev)
     eager, st_step, st_chain, st_verify, same, _ = time_steps(torch, chain, verify, outputs, R, K, W)
-    out = {"workload": "MoE draft layer: config-4 attention/eh_proj/lm_head, routed 8-bit FFN 256 experts top-8 "
-                       "+ shared (inter 512); K=3 chain at m=1 + verify at m=4, cache 4096",
+    out = {"workload": "MoE draft layer: the dense layer's attention/eh_proj/lm_head, routed "
+                       + ("4-bit (bf16 constants)" if q4 else "8-bit")
+                       + " FFN 256 experts top-8 + shared (inter 512); K=3 chain at m=1 + verify at m=4, cache 4096",
            "graph_replay_equals_eager": bool(same),
            "draft_steps_per_s": round(3.0 / (st_chain["mean"] * 1e-3), 1),
            "verify_rows_per_s": round(4.0 / (st_verify["mean"] * 1e-3), 1),
@@ -453,6 +514,7 @@ def main():
     lm_bytes = lm_copies[0].nbytes + 8 + H * 4  # weights + ids + gamma
     head_bytes_m1 = lm_bytes + 1 * H * 4
     achieved = head_bytes_m1 / (head_us[1] * 1e-6) / 1e9
+    stages = stage_split(torch, mtp, S, layers, caches, dev, K)
     del layers, caches
     torch.cuda.empty_cache()
     ceiling = read_ceiling(torch, dev, head_bytes_m1, K)
@@ -507,11 +569,14 @@ def main():
             "frac_of_measured_read_ceiling": (round(achieved / ceiling["GB/s"], 4) if ceiling else None),
         },
         "read_ceiling": ceiling,
+        "draft_stages_m1": stages,
         "setup_s": round(setup_s, 1),
     }
     if not args.no_moe:
         torch.cuda.empty_cache()
         result["moe_layer"] = moe_layer_bench(torch, mtp, synth, dev, K, W)
+        torch.cuda.empty_cache()
+        result["moe_layer_q4"] = moe_layer_bench(torch, mtp, synth, dev, K, W, q4=True)
     if not args.no_ops:
         torch.cuda.empty_cache()
         result["ops"] = op_timings(torch, mtp, synth, dev, K, W)
@@ -618,8 +683,8 @@ def attn_catchup_stack_timings(torch, mtp, synth, dev, n):
 def op_timings(torch, mtp, synth, dev, K, W):
     """The single-op workloads: 4-bit GEMV 1024x1024 (m=1), the e/h norm + concat
     + eh_proj 2048x4096 (m=1, 4), the attention block, catch-up and stack
-    (above), the 8-bit lm_head (m=1, 4) and the 8-bit MoE FFN (256 experts,
-    top-8 + shared expert, m=1, 4).  Weight copies are rotated so that their
+    (above), the 8-bit lm_head (m=1, 4) and the MoE FFN (256 experts, top-8 +
+    shared expert, m=1, 4) with 8-bit and with 4-bit experts.  Weight copies are rotated so that their
     total exceeds the 256 MB Infinity Cache; each entry is GPU time per call
     (n calls captured in one graph) and GB/s = algorithmic bytes / that time."""
     out = {"note": "us = GPU time per call: n calls captured in one HIP graph, events around one replay, / n"}
@@ -678,14 +743,26 @@ def op_timings(torch, mtp, synth, dev, K, W):
     del c8
     torch.cuda.empty_cache()
 
-    M = synth.config3_moe(4)
-    copies = []
-    for _ in range(3):  # 3 x 906 MB expert stacks
-        copies.append({k: mtp.DeviceQ8(getattr(M, k), dev)
-                       for k in ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up", "sh_down")})
+    out.update(moe_timings(torch, mtp, synth, dev, n, q4=False))
+    torch.cuda.empty_cache()
+    out.update(moe_timings(torch, mtp, synth, dev, n, q4=True))
+    return out
+
+
+def moe_timings(torch, mtp, synth, dev, n, q4):
+    """The MoE FFN of the configuration (hidden 2048, 256 experts of 512,
+    top-8 + shared) at m = 1 and 4: 8-bit experts (three rotated 906 MB
+    stacks) or 4-bit experts with bf16 constants (two 505 MB stacks).  The
+    bytes count the experts the call selected (read back from its ids)."""
+    out = {}
+    M = synth.config3_moe(4) if not q4 else synth.moe_inputs(synth.rng(3, 0), 4, q4=True)
+    names = ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up", "sh_down")
+    R = 2 if q4 else 3
+    copies = [{k: mtp.device_experts(getattr(M, k), dev) for k in names} for _ in range(R)]
     router = torch.from_numpy(M.router).to(dev)
     xm = torch.from_numpy(M.x).to(dev)
-    per_expert = 3 * (512 * 2048 + 512 * 2048 // 32 * 4)
+    per_expert = M.gate_exps.expert_nbytes * 3
+    fn = mtp.mtp_ffn_moe_q4 if q4 else mtp.mtp_ffn_moe_q
     for m in (1, 4):
         xr = xm[:m].contiguous()
         y = torch.empty((m, 2048), dtype=torch.float32, device=dev)
@@ -695,14 +772,14 @@ def op_timings(torch, mtp, synth, dev, K, W):
                          device=dev)
 
         def call(i, m=m, xr=xr, y=y, ids=ids, gts=gts, ws=ws):
-            c = copies[i % 3]
-            mtp.mtp_ffn_moe_q(xr, None, 1e-6, router, M.top_k, c["gate_exps"], c["up_exps"], c["down_exps"],
-                              c["sh_gate"], c["sh_up"], c["sh_down"], y=y, expert_ids=ids, gates=gts, ws=ws)
+            c = copies[i % R]
+            fn(xr, None, 1e-6, router, M.top_k, *(c[k] for k in names), y=y, expert_ids=ids, gates=gts, ws=ws)
 
         us = graph_region_us(torch, call, n)
         union = len(set(ids.cpu().numpy().ravel().tolist()))
         b = router.numel() * 4 + (union + 1) * per_expert + m * 2048 * 8
-        out[f"moe_q8_256x8_m{m}"] = dict(op_entry(us, b), experts_touched=union + 1)
+        out[f"moe_{'q4' if q4 else 'q8'}_256x8_m{m}"] = dict(op_entry(us, b), experts_touched=union + 1)
+    del copies
     return out
 
 

@@ -86,8 +86,23 @@ typedef struct {
     int32_t n, k, n_experts;
 } mtp_q8;
 
+/* 4-bit affine expert stack, group 32, with bf16 group constants
+ * ([shared.rs] `MlxAffineMoeStack`; n_experts = 1 for a single matrix):
+ *   codes  u32 [n_experts][n][k/8], nibble order as in mtp_q4;
+ *   scales, biases bf16 [n_experts][n][k/32], each stored as its 16 bits (the
+ *          upper half of the f32 it stands for);
+ *   value = scale*code + bias with scale and bias widened to f32 (exactly),
+ *   the f32 result rounded once. */
+typedef struct {
+    const uint32_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    int32_t n, k, n_experts;
+} mtp_q4e;
+
 #define MTP_FFN_DENSE_Q4 0
 #define MTP_FFN_MOE_Q8 1
+#define MTP_FFN_MOE_Q4 2
 
 /* One MTP draft layer ([mimo.rs] module doc "The draft forward"; [mtp.rs]
  * `MtpWeights`, `MtpFullAttnWeightsGpu`, `MtpFfnWeightsGpu`).
@@ -97,7 +112,10 @@ typedef struct {
  * dense FFN: gate, up [ffn_inter][hidden], down [hidden][ffn_inter];
  * MoE FFN: router f32 [n_experts][hidden], gate_exps/up_exps
  * [n_experts][inter][hidden], down_exps [n_experts][hidden][inter], optional
- * shared expert sh_* (n_experts = 1); lm_head [vocab][hidden].
+ * shared expert sh_* (n_experts = 1); 8-bit experts in gate_exps ... sh_down
+ * (ffn_kind MTP_FFN_MOE_Q8), 4-bit experts with bf16 constants in
+ * gate_exps4 ... sh_down4 (MTP_FFN_MOE_Q4, the shared expert in the same
+ * form); lm_head [vocab][hidden].
  * gamma_* are f32 [hidden] norm weights applied as x/rms(x)*gamma.
  * Attention variant ([mtp.rs] `forward_full_attention`, `MtpQGateWeightsGpu`;
  * zero / NULL fields give the plain attention):
@@ -130,7 +148,7 @@ typedef struct {
  *                 all 192 dims by default, pairs (i, i + 96)). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab;
-    int32_t ffn_kind; /* MTP_FFN_DENSE_Q4 or MTP_FFN_MOE_Q8 */
+    int32_t ffn_kind; /* MTP_FFN_DENSE_Q4, MTP_FFN_MOE_Q8 or MTP_FFN_MOE_Q4 */
     int32_t ffn_inter;
     int32_t top_k;
     double rope_theta;
@@ -144,6 +162,7 @@ typedef struct {
     const float* sinks;
     int32_t window;
     int32_t v_head_dim;
+    mtp_q4e gate_exps4, up_exps4, down_exps4, sh_gate4, sh_up4, sh_down4;
 } mtp_layer;
 
 const char* mtp_status_string(mtp_status s);
@@ -168,6 +187,9 @@ size_t mtp_draft_step_workspace_size(const mtp_layer* L, int32_t cache_len, int3
 mtp_status mtp_dequant_q4(const mtp_q4* w, float* out, void* stream);
 /* out f32 [n][k] = scale*code of matrix `expert` of the stack. */
 mtp_status mtp_dequant_q8(const mtp_q8* w, int32_t expert, float* out, void* stream);
+/* out f32 [n][k] = scale*code + bias of matrix `expert` of a 4-bit stack with
+ * bf16 constants ([shared.rs] `MlxAffineMoeStack`), rounded once. */
+mtp_status mtp_dequant_q4e(const mtp_q4e* w, int32_t expert, float* out, void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* Hot-path calls                                                          */
@@ -224,6 +246,18 @@ mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const fl
                          const mtp_q8* sh_gate, const mtp_q8* sh_up, const mtp_q8* sh_down,
                          const float* residual, float* y, int32_t* expert_ids, float* gates, int32_t m,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* The same routed mixture over 4-bit experts with bf16 group constants
+ * ([shared.rs] `MlxAffineMoeStack`, consumed by the MoE-id path), the shared
+ * expert in the same form.  Arguments as mtp_ffn_moe_q; the workspace is
+ * mtp_ffn_moe_workspace_size's.  Built shapes (MTP_ERR_UNSUPPORTED
+ * otherwise): hidden/32 and inter/32 each 2, 8, 16 or 64 groups, and a shared
+ * expert of the routed experts' intermediate size. */
+mtp_status mtp_ffn_moe_q4(const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
+                          const mtp_q4e* gate_exps, const mtp_q4e* up_exps, const mtp_q4e* down_exps,
+                          const mtp_q4e* sh_gate, const mtp_q4e* sh_up, const mtp_q4e* sh_down,
+                          const float* residual, float* y, int32_t* expert_ids, float* gates, int32_t m,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Shared head with a greedy pick ([mtp.rs] `forward_shared_head_greedy`):
  *   yn = rms(hidden; gamma); logits = lm_head yn; ids[r] = argmax_v logits[r][v]

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mtp.h")
 MTP_OK, MTP_ERR_INVALID_ARG, MTP_ERR_UNSUPPORTED, MTP_ERR_WORKSPACE, MTP_ERR_HIP = range(5)
 MTP_MAX_ROWS = 8
 MTP_NOALLOC_SCRATCH_BYTES = 32 << 20
-MTP_FFN_DENSE_Q4, MTP_FFN_MOE_Q8 = 0, 1
+MTP_FFN_DENSE_Q4, MTP_FFN_MOE_Q8, MTP_FFN_MOE_Q4 = 0, 1, 2
 
 
 class MtpError(RuntimeError):
@@ -38,6 +38,11 @@ class MtpQ4(C.Structure):
 class MtpQ8(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32),
                 ("n_experts", C.c_int32)]
+
+
+class MtpQ4E(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("n", C.c_int32), ("k", C.c_int32), ("n_experts", C.c_int32)]
 
 
 MTP_MAX_DRAFT = 16
@@ -68,7 +73,9 @@ class MtpLayer(C.Structure):
                 ("sh_gate", MtpQ8), ("sh_up", MtpQ8), ("sh_down", MtpQ8),
                 ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
                 ("q_gated", C.c_int32), ("rotary_dim", C.c_int32),
-                ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32)]
+                ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32),
+                ("gate_exps4", MtpQ4E), ("up_exps4", MtpQ4E), ("down_exps4", MtpQ4E),
+                ("sh_gate4", MtpQ4E), ("sh_up4", MtpQ4E), ("sh_down4", MtpQ4E)]
 
 
 _lib = None
@@ -85,12 +92,14 @@ _SIGS = {
     "mtp_draft_step_workspace_size": (_Z, [_P, _I, _I]),
     "mtp_dequant_q4": (_I, [_P, _P, _P]),
     "mtp_dequant_q8": (_I, [_P, _I, _P, _P]),
+    "mtp_dequant_q4e": (_I, [_P, _I, _P, _P]),
     "mtp_qgemv": (_I, [_P, _P, _P, _P, _I, _P]),
     "mtp_q8gemv": (_I, [_P, _I, _P, _P, _P, _I, _P]),
     "mtp_norm_concat_proj": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _P]),
     "mtp_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _Z, _P]),
     "mtp_ffn_dense_q": (_I, [_P, _P, _F, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_ffn_moe_q": (_I, [_P, _P, _F, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
+    "mtp_ffn_moe_q4": (_I, [_P, _P, _F, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_lmhead_argmax": (_I, [_P, _P, _F, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "mtp_draft_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "mtp_draft_step_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
@@ -136,6 +145,8 @@ def _dev_tensor(a: np.ndarray, device):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint32:
         a = a.view(np.int32)
+    elif a.dtype == np.uint16:  # bf16 bits
+        a = a.view(np.int16)
     return torch.from_numpy(a).to(device)
 
 
@@ -164,15 +175,37 @@ class DeviceQ8:
         self.desc = MtpQ8(self.codes.data_ptr(), self.scales.data_ptr(), self.n, self.k, self.n_experts)
 
 
+class DeviceQ4E:
+    """4-bit expert stack with bf16 group constants [E, n, k/8] resident on the device."""
+
+    def __init__(self, w, device="cuda"):
+        self.codes = _dev_tensor(w.codes, device)
+        self.scales = _dev_tensor(w.scales, device)
+        self.biases = _dev_tensor(w.biases, device)
+        self.n_experts, self.n = (int(s) for s in w.codes.shape[:2])
+        self.k = int(w.codes.shape[2]) * 8
+        self.desc = MtpQ4E(self.codes.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(), self.n, self.k,
+                           self.n_experts)
+
+
 def _empty_q8() -> MtpQ8:
     return MtpQ8(None, None, 0, 0, 0)
+
+
+def _empty_q4e() -> MtpQ4E:
+    return MtpQ4E(None, None, None, 0, 0, 0)
+
+
+def device_experts(w, device="cuda"):
+    """DeviceQ4E for a 4-bit stack with bf16 constants, DeviceQ8 for an 8-bit one."""
+    return DeviceQ4E(w, device) if w.codes.dtype == np.uint32 else DeviceQ8(w, device)
 
 
 class DeviceLayer:
     """A draft layer resident on the device; ``desc`` is the mtp_layer struct.
 
     ``dense`` is a ``synth.DenseLayer``; an optional ``moe`` (``synth.MoeInputs``
-    weights) turns the FFN into the routed 8-bit mixture."""
+    weights, 8-bit or 4-bit experts) turns the FFN into the routed mixture."""
 
     def __init__(self, dense, device="cuda", moe=None):
         torch = _torch()
@@ -183,18 +216,19 @@ class DeviceLayer:
         self.q4 = {name: DeviceQ4(getattr(dense, name), device)
                    for name in ("eh_proj", "wq", "wk", "wv", "wo", "gate", "up", "down", "lm_head")}
         self.moe = None
-        q8 = {k: _empty_q8() for k in ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up", "sh_down")}
+        names = ("gate_exps", "up_exps", "down_exps", "sh_gate", "sh_up", "sh_down")
+        q8 = {k: _empty_q8() for k in names}
+        q4e = {k: _empty_q4e() for k in names}
         router, top_k, kind = None, 0, MTP_FFN_DENSE_Q4
         if moe is not None:
             self.router = f(moe.router)
-            self.moe = {"gate_exps": DeviceQ8(moe.gate_exps, device), "up_exps": DeviceQ8(moe.up_exps, device),
-                        "down_exps": DeviceQ8(moe.down_exps, device)}
+            self.moe = {k: device_experts(getattr(moe, k), device) for k in names[:3]}
             if moe.sh_gate is not None:
-                self.moe.update(sh_gate=DeviceQ8(moe.sh_gate, device), sh_up=DeviceQ8(moe.sh_up, device),
-                                sh_down=DeviceQ8(moe.sh_down, device))
+                self.moe.update({k: device_experts(getattr(moe, k), device) for k in names[3:]})
+            is4 = isinstance(self.moe["gate_exps"], DeviceQ4E)
             for k, v in self.moe.items():
-                q8[k] = v.desc
-            router, top_k, kind = self.router.data_ptr(), moe.top_k, MTP_FFN_MOE_Q8
+                (q4e if is4 else q8)[k] = v.desc
+            router, top_k, kind = self.router.data_ptr(), moe.top_k, (MTP_FFN_MOE_Q4 if is4 else MTP_FFN_MOE_Q8)
         g = [t.data_ptr() for t in self.gammas]
         # attention variant: per-head q/k norm weights, gated q, partial rotary
         gq, gk = getattr(dense, "gamma_q_head", None), getattr(dense, "gamma_k_head", None)
@@ -213,7 +247,8 @@ class DeviceLayer:
                              q8["sh_down"], hq, hk, int(bool(getattr(dense, "q_gated", False))),
                              int(getattr(dense, "rotary_dim", 0) or 0),
                              None if self.sinks is None else self.sinks.data_ptr(),
-                             int(getattr(dense, "window", 0) or 0), int(getattr(dense, "v_head_dim", 0) or 0))
+                             int(getattr(dense, "window", 0) or 0), int(getattr(dense, "v_head_dim", 0) or 0),
+                             *(q4e[k] for k in names))
 
     @property
     def weight_nbytes(self) -> int:
@@ -315,6 +350,13 @@ def mtp_dequant_q8(w: DeviceQ8, expert: int = 0, out=None):
     return out
 
 
+def mtp_dequant_q4e(w: DeviceQ4E, expert: int = 0, out=None):
+    torch = _torch()
+    out = torch.empty((w.n, w.k), dtype=torch.float32, device=w.codes.device) if out is None else out
+    _check(lib().mtp_dequant_q4e(C.byref(w.desc), int(expert), _ptr(out), _stream(out)), "mtp_dequant_q4e")
+    return out
+
+
 def mtp_qgemv(w: DeviceQ4, x, residual=None, y=None):
     torch = _torch()
     _f32(x, "x")
@@ -388,6 +430,27 @@ def mtp_ffn_moe_q(x, gamma, eps: float, router, top_k: int, gate_exps: DeviceQ8,
                                ref(up_exps), ref(down_exps), ref(sh_gate), ref(sh_up), ref(sh_down), _ptr(residual),
                                _ptr(y), _ptr(expert_ids), _ptr(gates), m, _ptr(ws), _nbytes(ws), _stream(x)),
            "mtp_ffn_moe_q")
+    return y, expert_ids, gates
+
+
+def mtp_ffn_moe_q4(x, gamma, eps: float, router, top_k: int, gate_exps: DeviceQ4E, up_exps: DeviceQ4E,
+                   down_exps: DeviceQ4E, sh_gate: Optional[DeviceQ4E] = None, sh_up: Optional[DeviceQ4E] = None,
+                   sh_down: Optional[DeviceQ4E] = None, residual=None, y=None, expert_ids=None, gates=None, ws=None):
+    """The routed mixture over 4-bit experts with bf16 constants; returns
+    (y, expert_ids [m, top_k] int32, gates [m, top_k])."""
+    torch = _torch()
+    _f32(x, "x")
+    m = _rows(x)
+    y = torch.empty((m, gate_exps.k), dtype=torch.float32, device=x.device) if y is None else y
+    expert_ids = torch.empty((m, top_k), dtype=torch.int32, device=x.device) if expert_ids is None else expert_ids
+    gates = torch.empty((m, top_k), dtype=torch.float32, device=x.device) if gates is None else gates
+    sh_n = sh_gate.n if sh_gate is not None else 0
+    ws = _ws(mtp_ffn_moe_workspace_size(gate_exps.k, gate_exps.n_experts, top_k, gate_exps.n, sh_n, m), x, ws)
+    ref = lambda w: None if w is None else C.byref(w.desc)  # noqa: E731
+    _check(lib().mtp_ffn_moe_q4(_ptr(x), _ptr(gamma), float(eps), _ptr(router), int(top_k), ref(gate_exps),
+                                ref(up_exps), ref(down_exps), ref(sh_gate), ref(sh_up), ref(sh_down), _ptr(residual),
+                                _ptr(y), _ptr(expert_ids), _ptr(gates), m, _ptr(ws), _nbytes(ws), _stream(x)),
+           "mtp_ffn_moe_q4")
     return y, expert_ids, gates
 
 

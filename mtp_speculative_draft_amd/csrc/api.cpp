@@ -74,6 +74,31 @@ mtp_status check_vec(const void* p, const char* name) {
     return MTP_OK;
 }
 
+// An expert stack of either format as the MoE code takes it: 8-bit block
+// (f32 scales) or 4-bit with bf16 scales and biases (q4).
+struct ExpMat {
+    const void* codes;
+    const void* scales;
+    const void* biases;
+    int n, k, n_experts, q4;
+};
+ExpMat emat(const mtp_q8& w) { return ExpMat{w.codes, w.scales, nullptr, w.n, w.k, w.n_experts, 0}; }
+ExpMat emat(const mtp_q4e& w) { return ExpMat{w.codes, w.scales, w.biases, w.n, w.k, w.n_experts, 1}; }
+
+bool a2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+mtp_status check_emat(const ExpMat* w, const char* name) {
+    if (!w) return fail(MTP_ERR_INVALID_ARG, "%s: descriptor is NULL", name);
+    if (!w->codes || !w->scales || (w->q4 && !w->biases))
+        return fail(MTP_ERR_INVALID_ARG, "%s: NULL codes/scales%s", name, w->q4 ? "/biases" : "");
+    if (w->n < 1 || w->n_experts < 1) return fail(MTP_ERR_INVALID_ARG, "%s: n=%d n_experts=%d", name, w->n, w->n_experts);
+    if (w->k < MTP_GROUP || w->k % MTP_GROUP) return fail(MTP_ERR_INVALID_ARG, "%s: k=%d must be a positive multiple of 32", name, w->k);
+    if (w->k > MTP_MAX_K) return fail(MTP_ERR_UNSUPPORTED, "%s: k=%d above %d", name, w->k, MTP_MAX_K);
+    if (!a16(w->codes) || !(w->q4 ? a2(w->scales) && a2(w->biases) : a4(w->scales)))
+        return fail(MTP_ERR_INVALID_ARG, "%s: misaligned pointer", name);
+    return MTP_OK;
+}
+
 QMat qmat(const mtp_q4& w) { return QMat{w.codes, w.scales, w.biases, w.n}; }
 QMat qmat8(const mtp_q8& w, int expert) {
     const int64_t gpr = w.k / MTP_GROUP;
@@ -280,8 +305,14 @@ hipError_t run_ffn_dense(const float* x, const float* gamma, float eps, const mt
     return run_gemv(FMT_Q4, PRO_PLAIN, EPI_STORE, m, d, default_blocks(), st);
 }
 
-hipError_t run_moe(const float* x, const float* gamma, float eps, const float* router, int top_k, const mtp_q8& ge,
-                   const mtp_q8& ue, const mtp_q8& de, const mtp_q8* sg, const mtp_q8* su, const mtp_q8* sd,
+// The first matrix of an expert stack as the MoE launch takes it (for 4-bit
+// stacks the QMat's scale and bias fields carry the bf16 arrays).
+QMat qmat_e(const ExpMat& w) {
+    return QMat{w.codes, static_cast<const float*>(w.scales), static_cast<const float*>(w.biases), w.n};
+}
+
+hipError_t run_moe(const float* x, const float* gamma, float eps, const float* router, int top_k, const ExpMat& ge,
+                   const ExpMat& ue, const ExpMat& de, const ExpMat* sg, const ExpMat* su, const ExpMat* sd,
                    const float* residual, float* y, int* ids_out, float* gates_out, int m, const MoeWs& w,
                    hipStream_t st) {
     MoeParams p{};
@@ -301,15 +332,16 @@ hipError_t run_moe(const float* x, const float* gamma, float eps, const float* r
     p.slot_gate = w.slot_gate;
     p.n_slots = w.n_slots;
     p.max_slots = w.max_slots;
-    p.ge = qmat8(ge, 0);
-    p.ue = qmat8(ue, 0);
-    p.de = qmat8(de, 0);
+    p.ge = qmat_e(ge);
+    p.ue = qmat_e(ue);
+    p.de = qmat_e(de);
     if (sg) {
-        p.sg = qmat8(*sg, 0);
-        p.su = qmat8(*su, 0);
-        p.sd = qmat8(*sd, 0);
+        p.sg = qmat_e(*sg);
+        p.su = qmat_e(*su);
+        p.sd = qmat_e(*sd);
         p.sh_inter = sg->n;
     }
+    p.q4 = ge.q4;
     p.inter = ge.n;
     p.z = w.z;
     p.ypart = w.ypart;
@@ -372,10 +404,15 @@ mtp_status check_cache(const float* kc, const float* vc, int32_t cache_len, int3
     return MTP_OK;
 }
 
-mtp_status check_moe_weights(const float* router, int top_k, const mtp_q8* ge, const mtp_q8* ue, const mtp_q8* de,
-                             const mtp_q8* sg, const mtp_q8* su, const mtp_q8* sd, int H) {
+// The slot kernel's feature counts: 2, 8, 16 or 64 groups of 32.
+bool slot_groups(int k) { return k == 64 || k == 256 || k == 512 || k == 2048; }
+
+mtp_status check_moe_weights(const float* router, int top_k, const ExpMat* ge, const ExpMat* ue, const ExpMat* de,
+                             const ExpMat* sg, const ExpMat* su, const ExpMat* sd, int H) {
     mtp_status s;
-    if ((s = check_q8(ge, "gate_exps")) || (s = check_q8(ue, "up_exps")) || (s = check_q8(de, "down_exps"))) return s;
+    if ((s = check_emat(ge, "gate_exps")) || (s = check_emat(ue, "up_exps")) || (s = check_emat(de, "down_exps")))
+        return s;
+    if (ue->q4 != ge->q4 || de->q4 != ge->q4) return fail(MTP_ERR_INVALID_ARG, "expert stacks differ in format");
     if (!router || !a4(router)) return fail(MTP_ERR_INVALID_ARG, "router is NULL or misaligned");
     const int E = ge->n_experts, I = ge->n;
     if (ue->n_experts != E || de->n_experts != E) return fail(MTP_ERR_INVALID_ARG, "expert stacks differ in n_experts");
@@ -386,14 +423,54 @@ mtp_status check_moe_weights(const float* router, int top_k, const mtp_q8* ge, c
     const bool any = sg || su || sd, all = sg && su && sd;
     if (any && !all) return fail(MTP_ERR_INVALID_ARG, "shared expert: give all of sh_gate/sh_up/sh_down or none");
     if (all) {
-        if ((s = check_q8(sg, "sh_gate")) || (s = check_q8(su, "sh_up")) || (s = check_q8(sd, "sh_down"))) return s;
+        if ((s = check_emat(sg, "sh_gate")) || (s = check_emat(su, "sh_up")) || (s = check_emat(sd, "sh_down"))) return s;
+        if (sg->q4 != ge->q4 || su->q4 != ge->q4 || sd->q4 != ge->q4)
+            return fail(MTP_ERR_INVALID_ARG, "the shared expert must have the routed experts' format");
         const int Is = sg->n;
         if (sg->k != H || su->k != H || su->n != Is || sd->n != H || sd->k != Is)
             return fail(MTP_ERR_INVALID_ARG, "shared expert shapes do not match");
         if ((I + 2047) / 2048 != (Is + 2047) / 2048)
             return fail(MTP_ERR_UNSUPPORTED, "expert and shared intermediate sizes need the same 2048-wide chunk count");
+        if (ge->q4 && Is != I)
+            return fail(MTP_ERR_UNSUPPORTED, "4-bit experts: the shared expert needs the routed intermediate size %d (got %d)",
+                        I, Is);
     }
+    if (ge->q4 && (!slot_groups(H) || !slot_groups(I)))
+        return fail(MTP_ERR_UNSUPPORTED, "4-bit experts: hidden %d and intermediate %d must each be 64, 256, 512 or 2048",
+                    H, I);
     return MTP_OK;
+}
+
+// The expert stacks of a MoE layer (ffn_kind MTP_FFN_MOE_Q8 or _Q4); shared
+// ones are left zero (codes NULL) when the layer has none.
+struct LayerExperts {
+    ExpMat ge, ue, de, sg, su, sd;
+    bool shared;
+};
+LayerExperts layer_experts(const mtp_layer* L) {
+    LayerExperts x{};
+    if (L->ffn_kind == MTP_FFN_MOE_Q4) {
+        x.ge = emat(L->gate_exps4);
+        x.ue = emat(L->up_exps4);
+        x.de = emat(L->down_exps4);
+        x.shared = L->sh_gate4.codes != nullptr;
+        if (x.shared) {
+            x.sg = emat(L->sh_gate4);
+            x.su = emat(L->sh_up4);
+            x.sd = emat(L->sh_down4);
+        }
+    } else {
+        x.ge = emat(L->gate_exps);
+        x.ue = emat(L->up_exps);
+        x.de = emat(L->down_exps);
+        x.shared = L->sh_gate.codes != nullptr;
+        if (x.shared) {
+            x.sg = emat(L->sh_gate);
+            x.su = emat(L->sh_up);
+            x.sd = emat(L->sh_down);
+        }
+    }
+    return x;
 }
 
 // Checks and launches of the draft step and the cache catch-up, apart, so
@@ -466,8 +543,10 @@ size_t mtp_draft_step_workspace_size(const mtp_layer* L, int32_t cache_len, int3
     c.take<float>((size_t)m * L->hidden);  // r1
     c.take<float>((size_t)m * L->hidden);  // r2
     carve_attn(c, L, cache_len, m);
-    if (L->ffn_kind == MTP_FFN_MOE_Q8)
-        carve_moe(c, L->hidden, L->gate_exps.n_experts, L->top_k, L->gate_exps.n, L->sh_gate.codes ? L->sh_gate.n : 0, m);
+    if (L->ffn_kind == MTP_FFN_MOE_Q8 || L->ffn_kind == MTP_FFN_MOE_Q4) {
+        const LayerExperts x = layer_experts(L);
+        carve_moe(c, L->hidden, x.ge.n_experts, L->top_k, x.ge.n, x.shared ? x.sg.n : 0, m);
+    }
     else
         c.take<float>((size_t)m * L->ffn_inter);
     carve_head(c, m);
@@ -700,6 +779,20 @@ mtp_status mtp_dequant_q8(const mtp_q8* w, int32_t expert, float* out, void* str
     return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_dequant_q8");
 }
 
+mtp_status mtp_dequant_q4e(const mtp_q4e* w, int32_t expert, float* out, void* stream) {
+    if (!w) return fail(MTP_ERR_INVALID_ARG, "w: descriptor is NULL");
+    const ExpMat e = emat(*w);
+    mtp_status s = check_emat(&e, "w");
+    if (s) return s;
+    if (expert < 0 || expert >= w->n_experts) return fail(MTP_ERR_INVALID_ARG, "expert=%d outside 0..%d", expert, w->n_experts - 1);
+    if (!out || !a4(out)) return fail(MTP_ERR_INVALID_ARG, "out is NULL or misaligned");
+    const int64_t gpe = (int64_t)w->n * (w->k / MTP_GROUP);
+    hipError_t err = launch_dequant_q4e(reinterpret_cast<const char*>(w->codes) + expert * (int64_t)w->n * (w->k / 2),
+                                        w->scales + expert * gpe, w->biases + expert * gpe, w->n, w->k, out,
+                                        (hipStream_t)stream);
+    return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_dequant_q4e");
+}
+
 mtp_status mtp_qgemv(const mtp_q4* w, const float* x, const float* residual, float* y, int32_t m, void* stream) {
     mtp_status s;
     if ((s = check_rows(m)) || (s = check_q4(w, "w")) || (s = check_vec(x, "x"))) return s;
@@ -804,28 +897,68 @@ mtp_status mtp_ffn_dense_q(const float* x, const float* gamma, float eps, const 
     return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_ffn_dense_q");
 }
 
-mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
-                         const mtp_q8* gate_exps, const mtp_q8* up_exps, const mtp_q8* down_exps, const mtp_q8* sh_gate,
-                         const mtp_q8* sh_up, const mtp_q8* sh_down, const float* residual, float* y,
-                         int32_t* expert_ids, float* gates, int32_t m, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// mtp_ffn_moe_q and mtp_ffn_moe_q4 over either expert format.
+mtp_status ffn_moe(const char* what, const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
+                   const ExpMat* ge, const ExpMat* ue, const ExpMat* de, const ExpMat* sg, const ExpMat* su,
+                   const ExpMat* sd, const float* residual, float* y, int32_t* expert_ids, float* gates, int32_t m,
+                   void* ws, size_t ws_bytes, void* stream) {
     mtp_status s;
     if ((s = check_rows(m)) || (s = check_vec(x, "x"))) return s;
-    if (!gate_exps) return fail(MTP_ERR_INVALID_ARG, "gate_exps is NULL");
-    const int H = gate_exps->k;
-    if ((s = check_moe_weights(router, top_k, gate_exps, up_exps, down_exps, sh_gate, sh_up, sh_down, H))) return s;
+    if (!ge) return fail(MTP_ERR_INVALID_ARG, "gate_exps is NULL");
+    const int H = ge->k;
+    if ((s = check_moe_weights(router, top_k, ge, ue, de, sg, su, sd, H))) return s;
     if (gamma && (s = check_vec(gamma, "gamma"))) return s;
     if (!y || !a4(y)) return fail(MTP_ERR_INVALID_ARG, "y is NULL or misaligned");
     if (residual && !a4(residual)) return fail(MTP_ERR_INVALID_ARG, "residual misaligned");
     if ((const float*)y == x) return fail(MTP_ERR_INVALID_ARG, "y aliases x");
     if (!(eps >= 0.0f)) return fail(MTP_ERR_INVALID_ARG, "eps must be >= 0");
-    const int sh_inter = sh_gate ? sh_gate->n : 0;
-    const size_t need = mtp_ffn_moe_workspace_size(H, gate_exps->n_experts, top_k, gate_exps->n, sh_inter, m);
+    const int sh_inter = sg ? sg->n : 0;
+    const size_t need = mtp_ffn_moe_workspace_size(H, ge->n_experts, top_k, ge->n, sh_inter, m);
     if ((s = check_ws(ws, ws_bytes, need))) return s;
     Carve c{static_cast<char*>(ws)};
-    const MoeWs w = carve_moe(c, H, gate_exps->n_experts, top_k, gate_exps->n, sh_inter, m);
-    hipError_t e = run_moe(x, gamma, eps, router, top_k, *gate_exps, *up_exps, *down_exps, sh_gate, sh_up, sh_down,
-                           residual, y, expert_ids, gates, m, w, (hipStream_t)stream);
-    return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_ffn_moe_q");
+    const MoeWs w = carve_moe(c, H, ge->n_experts, top_k, ge->n, sh_inter, m);
+    hipError_t e = run_moe(x, gamma, eps, router, top_k, *ge, *ue, *de, sg, su, sd, residual, y, expert_ids, gates, m,
+                           w, (hipStream_t)stream);
+    return e == hipSuccess ? MTP_OK : hip_fail(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+mtp_status mtp_ffn_moe_q(const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
+                         const mtp_q8* gate_exps, const mtp_q8* up_exps, const mtp_q8* down_exps, const mtp_q8* sh_gate,
+                         const mtp_q8* sh_up, const mtp_q8* sh_down, const float* residual, float* y,
+                         int32_t* expert_ids, float* gates, int32_t m, void* ws, size_t ws_bytes, void* stream) {
+    if (!gate_exps || !up_exps || !down_exps) return fail(MTP_ERR_INVALID_ARG, "expert stack descriptor is NULL");
+    const ExpMat ge = emat(*gate_exps), ue = emat(*up_exps), de = emat(*down_exps);
+    ExpMat sg{}, su{}, sd{};
+    if (sh_gate) sg = emat(*sh_gate);
+    if (sh_up) su = emat(*sh_up);
+    if (sh_down) sd = emat(*sh_down);
+    return ffn_moe("mtp_ffn_moe_q", x, gamma, eps, router, top_k, &ge, &ue, &de, sh_gate ? &sg : nullptr,
+                   sh_up ? &su : nullptr, sh_down ? &sd : nullptr, residual, y, expert_ids, gates, m, ws, ws_bytes,
+                   stream);
+}
+
+mtp_status mtp_ffn_moe_q4(const float* x, const float* gamma, float eps, const float* router, int32_t top_k,
+                          const mtp_q4e* gate_exps, const mtp_q4e* up_exps, const mtp_q4e* down_exps,
+                          const mtp_q4e* sh_gate, const mtp_q4e* sh_up, const mtp_q4e* sh_down,
+                          const float* residual, float* y, int32_t* expert_ids, float* gates, int32_t m, void* ws,
+                          size_t ws_bytes, void* stream) {
+    if (!gate_exps || !up_exps || !down_exps) return fail(MTP_ERR_INVALID_ARG, "expert stack descriptor is NULL");
+    const ExpMat ge = emat(*gate_exps), ue = emat(*up_exps), de = emat(*down_exps);
+    ExpMat sg{}, su{}, sd{};
+    if (sh_gate) sg = emat(*sh_gate);
+    if (sh_up) su = emat(*sh_up);
+    if (sh_down) sd = emat(*sh_down);
+    return ffn_moe("mtp_ffn_moe_q4", x, gamma, eps, router, top_k, &ge, &ue, &de, sh_gate ? &sg : nullptr,
+                   sh_up ? &su : nullptr, sh_down ? &sd : nullptr, residual, y, expert_ids, gates, m, ws, ws_bytes,
+                   stream);
 }
 
 mtp_status mtp_lmhead_argmax(const float* hidden, const float* gamma, float eps, const mtp_q4* lm_head,
@@ -905,10 +1038,10 @@ mtp_status check_draft_step_args(const mtp_layer* L, const float* e, const int32
         if (L->gate.n != L->ffn_inter || L->up.n != L->ffn_inter || L->gate.k != H || L->up.k != H ||
             L->down.n != H || L->down.k != L->ffn_inter)
             return fail(MTP_ERR_INVALID_ARG, "dense FFN shapes do not match hidden/ffn_inter");
-    } else if (L->ffn_kind == MTP_FFN_MOE_Q8) {
-        const bool sh = L->sh_gate.codes != nullptr;
-        if ((s = check_moe_weights(L->router, L->top_k, &L->gate_exps, &L->up_exps, &L->down_exps, sh ? &L->sh_gate : nullptr,
-                                   sh ? &L->sh_up : nullptr, sh ? &L->sh_down : nullptr, H)))
+    } else if (L->ffn_kind == MTP_FFN_MOE_Q8 || L->ffn_kind == MTP_FFN_MOE_Q4) {
+        const LayerExperts x = layer_experts(L);
+        if ((s = check_moe_weights(L->router, L->top_k, &x.ge, &x.ue, &x.de, x.shared ? &x.sg : nullptr,
+                                   x.shared ? &x.su : nullptr, x.shared ? &x.sd : nullptr, H)))
             return s;
     } else {
         return fail(MTP_ERR_INVALID_ARG, "ffn_kind=%d", L->ffn_kind);
@@ -948,12 +1081,13 @@ mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t*
     float* r1 = c.take<float>((size_t)m * H);
     float* r2 = c.take<float>((size_t)m * H);
     const AttnWs aw = carve_attn(c, L, cache_len, m);
-    const bool moe = L->ffn_kind == MTP_FFN_MOE_Q8;
-    const bool sh = L->sh_gate.codes != nullptr;
+    const bool moe = L->ffn_kind == MTP_FFN_MOE_Q8 || L->ffn_kind == MTP_FFN_MOE_Q4;
+    const LayerExperts xe = moe ? layer_experts(L) : LayerExperts{};
+    const bool sh = xe.shared;
     float* z = nullptr;
     MoeWs mw{};
     if (moe)
-        mw = carve_moe(c, H, L->gate_exps.n_experts, L->top_k, L->gate_exps.n, sh ? L->sh_gate.n : 0, m);
+        mw = carve_moe(c, H, xe.ge.n_experts, L->top_k, xe.ge.n, sh ? xe.sg.n : 0, m);
     else
         z = c.take<float>((size_t)m * L->ffn_inter);
     const HeadWs hw = carve_head(c, m);
@@ -983,9 +1117,8 @@ mtp_status enqueue_draft_step(const mtp_layer* L, const float* e, const int32_t*
     if (!moe) {
         err = run_ffn_dense(r1, L->gamma_post, L->eps, L->gate, L->up, L->down, r1, r2, m, z, st);
     } else {
-        err = run_moe(r1, L->gamma_post, L->eps, L->router, L->top_k, L->gate_exps, L->up_exps, L->down_exps,
-                      sh ? &L->sh_gate : nullptr, sh ? &L->sh_up : nullptr, sh ? &L->sh_down : nullptr, r1, r2,
-                      nullptr, nullptr, m, mw, st);
+        err = run_moe(r1, L->gamma_post, L->eps, L->router, L->top_k, xe.ge, xe.ue, xe.de, sh ? &xe.sg : nullptr,
+                      sh ? &xe.su : nullptr, sh ? &xe.sd : nullptr, r1, r2, nullptr, nullptr, m, mw, st);
     }
     if (err != hipSuccess) return hip_fail(err, "mtp_draft_step ffn");
     if ((err = run_head(r2, L->gamma_final, L->eps, L->lm_head, hidden_out, logits_out, ids_out, m, hw, st)) != hipSuccess)

@@ -267,6 +267,38 @@ __device__ __forceinline__ void load_frag(WFrag<FMT_Q8>& w, const void* codes, c
     w.s = __builtin_nontemporal_load(scales + gi);
 }
 
+// 4-bit expert stacks with bf16 group constants (hf2q 0.1.1,
+// `MlxAffineMoeStack`): a bf16 value is the upper half of an f32's bits, so
+// widening it is a shift.
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
+
+__device__ __forceinline__ void load_frag_b16(WFrag<FMT_Q4>& w, const void* codes, const unsigned short* scales,
+                                              const unsigned short* biases, int64_t row, int G, int g) {
+    const int64_t gi = row * G + g;
+    w.c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes) + gi);
+    w.s = bf16_to_f32(__builtin_nontemporal_load(scales + gi));
+    w.b = bf16_to_f32(__builtin_nontemporal_load(biases + gi));
+}
+
+// The 32 f32 weights of a 4-bit group, s c + b rounded once each: the code
+// halves are c 2^-24 exactly (16 c 2^-24 times 1/16 for the upper nibbles of
+// a byte), so fma(s 2^24, c 2^-24, b) is fma(s, c, b).
+__device__ __forceinline__ void dequant_q4_group(const WFrag<FMT_Q4>& f, float* dst) {
+    const unsigned c[4] = {f.c.x, f.c.y, f.c.z, f.c.w};
+    const float s24 = f.s * kTwo24;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const Q4Halves q = q4_halves(c[j]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int slot = q4_slot(k);
+            const h2_t hh = as_h2(q.r[slot >> 1]);
+            const float cv = (float)((slot & 1) ? hh.y : hh.x) * q4_factor(k);
+            dst[8 * j + k] = fmaf(s24, cv, f.b);
+        }
+    }
+}
+
 // (s c + b) . x over the group for a 4-bit row: 8 exact products per word
 // accumulated in f32 (two chains), then the scale and the bias term.
 __device__ __forceinline__ float dot_q4(const u32x4& c, float s, float b, const XFrag& x) {

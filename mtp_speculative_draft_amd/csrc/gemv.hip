@@ -1195,19 +1195,7 @@ __global__ void __launch_bounds__(256) k_dequant(const QMat w, int n, int K, flo
     WFrag<FMT> f;
     load_frag(f, w.codes, w.scales, w.biases, row, G, g);
     if constexpr (FMT == FMT_Q4) {
-        const unsigned c[4] = {f.c.x, f.c.y, f.c.z, f.c.w};
-        const float s24 = f.s * kTwo24;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const Q4Halves q = q4_halves(c[j]);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int slot = q4_slot(k);
-                const h2_t hh = as_h2(q.r[slot >> 1]);
-                const float cv = (float)((slot & 1) ? hh.y : hh.x) * q4_factor(k);
-                dst[8 * j + k] = fmaf(s24, cv, f.b);
-            }
-        }
+        dequant_q4_group(f, dst);
     } else {
         const unsigned c[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
         const float s24 = f.s * kTwo24, off = -128.0f * f.s;

@@ -152,7 +152,9 @@ hipError_t launch_shift_rows(const float* pending, const float* target, float* o
                              hipStream_t stream);
 hipError_t launch_append_kv(const AttnParams& p, const float* kv, int m, int pos0, hipStream_t stream);
 
-// MoE (8-bit experts).
+// MoE (8-bit experts, or 4-bit experts with bf16 group constants when q4:
+// then the QMat scales/biases fields of ge ... sd carry the bf16 arrays'
+// addresses and are read as 16-bit values).
 struct MoeParams {
     const float* x;      // [m][H] input rows
     const float* gamma;  // optional input norm
@@ -174,7 +176,10 @@ struct MoeParams {
     float* ypart;         // [max_slots][m][H]
     const float* residual;
     float* y;
+    int q4;
 };
 hipError_t launch_moe(const MoeParams& p, hipStream_t stream);
+hipError_t launch_dequant_q4e(const void* codes, const unsigned short* scales, const unsigned short* biases, int n,
+                              int k, float* out, hipStream_t stream);
 
 }  // namespace mtp

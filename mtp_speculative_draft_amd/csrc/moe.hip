@@ -1,6 +1,8 @@
-// moe.hip -- routed mixture of 8-bit SwiGLU experts (hf2q 0.1.13,
+// moe.hip -- routed mixture of SwiGLU experts (hf2q 0.1.13,
 // src/inference/models/qwen35/mtp.rs, `MtpFfnWeightsGpu::Moe`: router
-// `ffn_gate_inp`, stacked gate/up/down experts, shared-expert tensors).
+// `ffn_gate_inp`, stacked gate/up/down experts, shared-expert tensors), over
+// 8-bit block experts or 4-bit affine experts with bf16 group constants
+// (hf2q 0.1.1, src/serve/forward_mlx_shared.rs, `MlxAffineMoeStack`).
 //
 // Launch sequence (one stream, no host round trip):
 //   k_moe_router   one block per expert row: optional input RMSNorm, f32
@@ -17,9 +19,11 @@
 //   k_moe_combine  y = residual + sum over slots in slot order.
 // The two slot GEMVs take k_moe_slot (below) when both feature counts are a
 // power-of-two number of groups up to 64 and the shared expert has the
-// routed experts' size; other shapes take the generic GEMV kernel.
+// routed experts' size; other shapes take the generic GEMV kernel (8-bit
+// experts only: the host rejects other shapes for 4-bit experts).
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -234,20 +238,23 @@ __global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// k_moe_slot: one 8-bit expert GEMV per slot (grid.y = slot), for K = 32*G
-// features with G a power of two up to 64.
+// k_moe_slot: one expert GEMV per slot (grid.y = slot), for K = 32*G
+// features with G a power of two up to 64; FMT_Q8 (8-bit block experts) or
+// FMT_Q4 (4-bit experts with bf16 scale and bias per group).
 //
 // Lane mapping: a row's G groups take LG = G consecutive lanes, so one wave
-// load covers RPL = 64/LG rows (lane = rs*LG + g reads 32 code bytes and one
-// scale of row rs, group g); at K = 512 that is four rows of 512 bytes per
-// load instead of one row on a quarter of the lanes.  A "load-set" is those
-// RPL rows (for SwiGLU, the same RPL rows of gate and of up).
+// load covers RPL = 64/LG rows (lane = rs*LG + g reads the codes and group
+// constants of row rs, group g: 32 bytes and a scale for 8-bit, 16 bytes and
+// two bf16 for 4-bit); at K = 512 that is four rows per load instead of one
+// row on a quarter of the lanes.  A "load-set" is those RPL rows (for SwiGLU,
+// the same RPL rows of gate and of up).
 //
 // Activations: the block stages its slot's m activation rows once in LDS,
 // per (row, group of 32) the 32 f32 values and their sum; each lane reads the
-// fragments of its group into registers.  A row's group term is
-// s * (2^24 sum((c + 128) 2^-24 x) - 128 sum(x)) with the exact code
-// subnormals of q8_halves (see device.hpp).
+// fragments of its group into registers, in the order of its format's code
+// halves.  A row's group term is s * (2^24 sum((c + 128) 2^-24 x) - 128 sum(x))
+// for 8-bit codes and (s 2^24) sum(c 2^-24 x) + b sum(x) for 4-bit codes,
+// with the exact code subnormals of q8_halves / q4_halves (see device.hpp).
 //
 // Work: a slot's load-sets are spread evenly over the waves of its
 // gridDim.x blocks and taken UB at a time (a batch); two batches are in
@@ -257,11 +264,13 @@ __global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
 // requested before the activation setup.
 // ---------------------------------------------------------------------------
 struct SlotGemv {
-    const int8_t* codes[2];    // expert stacks [E][N][K] (codes[1]: up, SwiGLU only)
-    const float* scales[2];    // [E][N][K/32]
-    const int8_t* sh_codes[2]; // shared expert [N][K] (NULL when absent)
-    const float* sh_scales[2];
-    int64_t ex_codes, ex_scales;  // per-expert strides: bytes, floats
+    const void* codes[2];      // expert stacks (codes[1]: up, SwiGLU only): int8 [E][N][K] or u32 [E][N][K/8]
+    const void* scales[2];     // [E][N][K/32]: f32 (8-bit) or bf16 bits (4-bit)
+    const void* biases[2];     // [E][N][K/32] bf16 bits (4-bit only)
+    const void* sh_codes[2];   // shared expert, one matrix of the same format (NULL when absent)
+    const void* sh_scales[2];
+    const void* sh_biases[2];
+    int64_t ex_codes, ex_scales;  // per-expert strides: code bytes, group constants
     int N, K, m;
     const float* act;     // [slot][m][K] activations (slot stride act_slot; 0 = shared by all slots)
     int64_t act_slot;
@@ -394,7 +403,9 @@ __device__ __forceinline__ void store_frag(unsigned* f, const float (&xv)[32]) {
     f4[8] = make_float4(sum, 0.0f, 0.0f, 0.0f);
 }
 
-// The lane's fragment of an 8-bit row from a stored (row, group) fragment.
+// The lane's fragment of a row of format FMT from a stored (row, group)
+// fragment (the order of make_frag<FMT>).
+template <int FMT>
 __device__ __forceinline__ void read_frag(const unsigned* f, XFrag& xf) {
     const float4* f4 = reinterpret_cast<const float4*>(f);
 #pragma unroll
@@ -402,12 +413,32 @@ __device__ __forceinline__ void read_frag(const unsigned* f, XFrag& xf) {
         const float4 t = f4[k];
         const float xv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xf.v[4 * k + q8_slot(q)] = xv[q];
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (FMT == FMT_Q4) {
+                const int f8 = 4 * (k & 1) + q;  // feature within the 4-bit word k/2
+                xf.v[8 * (k >> 1) + q4_slot(f8)] = xv[q] * q4_factor(f8);
+            } else {
+                xf.v[4 * k + q8_slot(q)] = xv[q];
+            }
+        }
     }
-    xf.sum = -128.0f * f4[8].x;
+    xf.sum = (FMT == FMT_Q4 ? 1.0f : -128.0f) * f4[8].x;
 }
 
-template <int M, int EPI, int LG, int W>
+__device__ __forceinline__ void zero_frag(WFrag<FMT_Q8>& w) {
+    w.c0 = (u32x4){0u, 0u, 0u, 0u};
+    w.c1 = (u32x4){0u, 0u, 0u, 0u};
+    w.s = 0.0f;
+}
+__device__ __forceinline__ void zero_frag(WFrag<FMT_Q4>& w) {
+    w.c = (u32x4){0u, 0u, 0u, 0u};
+    w.s = 0.0f;
+    w.b = 0.0f;
+}
+__device__ __forceinline__ float dot_frag(const WFrag<FMT_Q8>& w, const XFrag& x) { return dot_q8(w, x); }
+__device__ __forceinline__ float dot_frag(const WFrag<FMT_Q4>& w, const XFrag& x) { return dot_q4(w.c, w.s, w.b, x); }
+
+template <int FMT, int M, int EPI, int LG, int W>
 __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int RPL = kWave / LG;
@@ -452,12 +483,21 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
         if (slot >= *p.n_slots) return;
         e = p.slot_expert[slot];
     }
-    const int8_t* cw[2];
-    const float* sw[2];
+    // this slot's matrices (typed by format; the 4-bit constants are bf16)
+    using SC = typename std::conditional<FMT == FMT_Q4, unsigned short, float>::type;
+    const char* cw[2];
+    const SC* sw[2];
+    const unsigned short* bw[2];
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-        cw[i] = e >= 0 ? p.codes[i] + (int64_t)e * p.ex_codes : p.sh_codes[i];
-        sw[i] = e >= 0 ? p.scales[i] + (int64_t)e * p.ex_scales : p.sh_scales[i];
+        cw[i] = e >= 0 ? static_cast<const char*>(p.codes[i]) + (int64_t)e * p.ex_codes
+                       : static_cast<const char*>(p.sh_codes[i]);
+        sw[i] = e >= 0 ? static_cast<const SC*>(p.scales[i]) + (int64_t)e * p.ex_scales
+                       : static_cast<const SC*>(p.sh_scales[i]);
+        bw[i] = nullptr;
+        if constexpr (FMT == FMT_Q4)
+            bw[i] = e >= 0 ? static_cast<const unsigned short*>(p.biases[i]) + (int64_t)e * p.ex_scales
+                           : static_cast<const unsigned short*>(p.sh_biases[i]);
     }
     const int g = lane % LG, rs = lane / LG;
     const int L = (p.N + RPL - 1) / RPL;  // load-sets of the slot
@@ -467,23 +507,24 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     const int j_begin = (int)((int64_t)wv * L / NW);
     const int j_end = (int)((int64_t)(wv + 1) * L / NW);
 
-    WFrag<FMT_Q8> wa[UB][P], wb[UB][P];
-    auto load_batch = [&](WFrag<FMT_Q8> (&wf)[UB][P], int j0) {
+    WFrag<FMT> wa[UB][P], wb[UB][P];
+    auto load_batch = [&](WFrag<FMT> (&wf)[UB][P], int j0) {
 #pragma unroll
         for (int b = 0; b < UB; ++b) {
             if (j0 + b >= j_end) {  // wave-uniform: past the range, a zero fragment
 #pragma unroll
-                for (int i = 0; i < P; ++i) {
-                    wf[b][i].c0 = (u32x4){0u, 0u, 0u, 0u};
-                    wf[b][i].c1 = (u32x4){0u, 0u, 0u, 0u};
-                    wf[b][i].s = 0.0f;
-                }
+                for (int i = 0; i < P; ++i) zero_frag(wf[b][i]);
                 continue;
             }
             int n = (j0 + b) * RPL + rs;
             n = n < p.N ? n : p.N - 1;
 #pragma unroll
-            for (int i = 0; i < P; ++i) load_frag(wf[b][i], cw[i], sw[i], nullptr, n, G, g);
+            for (int i = 0; i < P; ++i) {
+                if constexpr (FMT == FMT_Q4)
+                    load_frag_b16(wf[b][i], cw[i], sw[i], bw[i], n, G, g);
+                else
+                    load_frag(wf[b][i], cw[i], sw[i], nullptr, n, G, g);
+            }
         }
     };
     // two batches in flight from the start
@@ -507,20 +548,20 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     if (j_begin >= j_end) return;
     XFrag xf[M];
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) read_frag(frag + (mi * LG + g) * kFragWords, xf[mi]);
+    for (int mi = 0; mi < M; ++mi) read_frag<FMT>(frag + (mi * LG + g) * kFragWords, xf[mi]);
 
     const int base = seg_base<V, FIN, LG>(lane);
     const bool writer = (lane & (DUP - 1)) == 0;
     float* out = p.out + (int64_t)slot * p.out_slot;
     // dot products of one batch, then (after the caller's next request) the
     // reduction over the row's lanes and the epilogue
-    auto dots = [&](const WFrag<FMT_Q8> (&wf)[UB][P], float (&v)[V]) {
+    auto dots = [&](const WFrag<FMT> (&wf)[UB][P], float (&v)[V]) {
 #pragma unroll
         for (int b = 0; b < UB; ++b)
 #pragma unroll
             for (int i = 0; i < P; ++i)
 #pragma unroll
-                for (int mi = 0; mi < M; ++mi) v[(b * M + mi) * P + i] = dot_q8(wf[b][i], xf[mi]);
+                for (int mi = 0; mi < M; ++mi) v[(b * M + mi) * P + i] = dot_frag(wf[b][i], xf[mi]);
     };
     auto finish = [&](float (&v)[V], int j0) {
         Butterfly<V, FIN, seg_step0<LG>()>::run(v, lane);
@@ -560,12 +601,13 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
 
 // Resident blocks per compute unit of one kernel (from its registers and
 // LDS), asked once.
-template <int M, int EPI, int LG, int W>
+template <int FMT, int M, int EPI, int LG, int W>
 static int slot_blocks_per_cu() {
     static int cached = 0;
     if (!cached) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_moe_slot<M, EPI, LG, W>, W * kWave, 0) != hipSuccess || n < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_moe_slot<FMT, M, EPI, LG, W>, W * kWave, 0) != hipSuccess ||
+            n < 1)
             n = 1;
         cached = n;
     }
@@ -575,31 +617,44 @@ static int slot_blocks_per_cu() {
 // Blocks per slot: as many as fill the resident capacity over the launch's
 // slots (so no block waits for a second round and compute units carry equal
 // shares), at most one per wave's batch.
-template <int M, int EPI, int LG>
+template <int FMT, int M, int EPI, int LG>
 static hipError_t launch_slot_g(const SlotGemv& p, int max_slots, hipStream_t st) {
     constexpr int W = 4;
     constexpr int RPL = kWave / LG;
     constexpr int UB = slot_batch<M>();
     const int L = (p.N + RPL - 1) / RPL;
     const int U = (L + UB - 1) / UB;
-    const int cap = device_cu_count() * slot_blocks_per_cu<M, EPI, LG, W>();
+    const int cap = device_cu_count() * slot_blocks_per_cu<FMT, M, EPI, LG, W>();
     int per_slot = cap / max_slots;
     per_slot = per_slot < 1 ? 1 : per_slot;
     const int most = (U + W - 1) / W;
     per_slot = per_slot > most ? most : per_slot;
     const dim3 grid((unsigned)per_slot, (unsigned)max_slots);
-    hipLaunchKernelGGL((k_moe_slot<M, EPI, LG, W>), grid, dim3(W * kWave), 0, st, p);
+    hipLaunchKernelGGL((k_moe_slot<FMT, M, EPI, LG, W>), grid, dim3(W * kWave), 0, st, p);
     return hipGetLastError();
 }
 
-template <int M, int EPI>
+template <int FMT, int M, int EPI>
 static hipError_t launch_slot_m(const SlotGemv& p, int max_slots, hipStream_t st) {
     switch (p.K / kGroup) {
-        case 64: return launch_slot_g<M, EPI, 64>(p, max_slots, st);
-        case 16: return launch_slot_g<M, EPI, 16>(p, max_slots, st);
-        case 8: return launch_slot_g<M, EPI, 8>(p, max_slots, st);
-        case 2: return launch_slot_g<M, EPI, 2>(p, max_slots, st);
+        case 64: return launch_slot_g<FMT, M, EPI, 64>(p, max_slots, st);
+        case 16: return launch_slot_g<FMT, M, EPI, 16>(p, max_slots, st);
+        case 8: return launch_slot_g<FMT, M, EPI, 8>(p, max_slots, st);
+        case 2: return launch_slot_g<FMT, M, EPI, 2>(p, max_slots, st);
         default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT>
+static hipError_t launch_slot_f(int epi, const SlotGemv& p, int max_slots, hipStream_t st) {
+    switch (inst_m(p.m)) {
+        case 1: return epi == EPI_SWIGLU ? launch_slot_m<FMT, 1, EPI_SWIGLU>(p, max_slots, st)
+                                         : launch_slot_m<FMT, 1, EPI_STORE>(p, max_slots, st);
+        case 2: return epi == EPI_SWIGLU ? launch_slot_m<FMT, 2, EPI_SWIGLU>(p, max_slots, st)
+                                         : launch_slot_m<FMT, 2, EPI_STORE>(p, max_slots, st);
+        case 4: return epi == EPI_SWIGLU ? launch_slot_m<FMT, 4, EPI_SWIGLU>(p, max_slots, st)
+                                         : launch_slot_m<FMT, 4, EPI_STORE>(p, max_slots, st);
+        default: return hipErrorInvalidValue;  // launch_moe runs at most four rows per pass
     }
 }
 
@@ -608,13 +663,8 @@ static bool slot_groups_ok(int K) {
     return K % kGroup == 0 && (G == 64 || G == 16 || G == 8 || G == 2);
 }
 
-static hipError_t launch_slot(int epi, const SlotGemv& p, int max_slots, hipStream_t st) {
-    switch (inst_m(p.m)) {
-        case 1: return epi == EPI_SWIGLU ? launch_slot_m<1, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<1, EPI_STORE>(p, max_slots, st);
-        case 2: return epi == EPI_SWIGLU ? launch_slot_m<2, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<2, EPI_STORE>(p, max_slots, st);
-        case 4: return epi == EPI_SWIGLU ? launch_slot_m<4, EPI_SWIGLU>(p, max_slots, st) : launch_slot_m<4, EPI_STORE>(p, max_slots, st);
-        default: return hipErrorInvalidValue;  // launch_moe runs at most four rows per pass
-    }
+static hipError_t launch_slot(int fmt, int epi, const SlotGemv& p, int max_slots, hipStream_t st) {
+    return fmt == FMT_Q4 ? launch_slot_f<FMT_Q4>(epi, p, max_slots, st) : launch_slot_f<FMT_Q8>(epi, p, max_slots, st);
 }
 
 static bool moe_slot_path(const MoeParams& p);
@@ -633,21 +683,28 @@ static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
 
     const float* fin = p.gamma ? p.f : p.x;
     const int imax = p.inter > p.sh_inter ? p.inter : p.sh_inter;
-    const int64_t ex_codes_gu = (int64_t)p.inter * p.H;          // int8 bytes per gate/up expert
+    const int fmt = p.q4 ? FMT_Q4 : FMT_Q8;
+    const int64_t cdiv = p.q4 ? 2 : 1;                                   // code bytes per weight: 1/2 or 1
+    const int64_t ex_codes_gu = (int64_t)p.inter * p.H / cdiv;          // code bytes per gate/up expert
     const int64_t ex_sc_gu = (int64_t)p.inter * (p.H / kGroup);
-    const int64_t ex_codes_d = (int64_t)p.H * p.inter;
+    const int64_t ex_codes_d = (int64_t)p.H * p.inter / cdiv;
     const int64_t ex_sc_d = (int64_t)p.H * (p.inter / kGroup);
+    if (p.q4 && !slot_path) return hipErrorInvalidValue;  // the host admits only slot-kernel shapes
 
     if (slot_path) {
         SlotGemv g{};
-        g.codes[0] = static_cast<const int8_t*>(p.ge.codes);
-        g.codes[1] = static_cast<const int8_t*>(p.ue.codes);
+        g.codes[0] = p.ge.codes;
+        g.codes[1] = p.ue.codes;
         g.scales[0] = p.ge.scales;
         g.scales[1] = p.ue.scales;
-        g.sh_codes[0] = static_cast<const int8_t*>(p.sg.codes);
-        g.sh_codes[1] = static_cast<const int8_t*>(p.su.codes);
+        g.biases[0] = p.ge.biases;
+        g.biases[1] = p.ue.biases;
+        g.sh_codes[0] = p.sg.codes;
+        g.sh_codes[1] = p.su.codes;
         g.sh_scales[0] = p.sg.scales;
         g.sh_scales[1] = p.su.scales;
+        g.sh_biases[0] = p.sg.biases;
+        g.sh_biases[1] = p.su.biases;
         g.ex_codes = ex_codes_gu;
         g.ex_scales = ex_sc_gu;
         g.N = p.inter;
@@ -665,13 +722,15 @@ static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
         g.n_slots_out = p.n_slots;
         g.expert_ids_out = p.expert_ids;
         g.gates_out = p.gates;
-        if ((e = launch_slot(EPI_SWIGLU, g, p.max_slots, st)) != hipSuccess) return e;
+        if ((e = launch_slot(fmt, EPI_SWIGLU, g, p.max_slots, st)) != hipSuccess) return e;
 
         SlotGemv d{};
-        d.codes[0] = static_cast<const int8_t*>(p.de.codes);
+        d.codes[0] = p.de.codes;
         d.scales[0] = p.de.scales;
-        d.sh_codes[0] = static_cast<const int8_t*>(p.sd.codes);
+        d.biases[0] = p.de.biases;
+        d.sh_codes[0] = p.sd.codes;
         d.sh_scales[0] = p.sd.scales;
+        d.sh_biases[0] = p.sd.biases;
         d.ex_codes = ex_codes_d;
         d.ex_scales = ex_sc_d;
         d.N = p.H;
@@ -683,7 +742,7 @@ static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
         d.out_slot = (int64_t)p.m * p.H;
         d.slot_expert = p.slot_expert;
         d.n_slots = p.n_slots;
-        if ((e = launch_slot(EPI_STORE, d, p.max_slots, st)) != hipSuccess) return e;
+        if ((e = launch_slot(fmt, EPI_STORE, d, p.max_slots, st)) != hipSuccess) return e;
         const int64_t n = (int64_t)p.m * p.H;
         hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
         return hipGetLastError();
@@ -737,6 +796,28 @@ static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
 
     const int64_t n = (int64_t)p.m * p.H;
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+
+// out [n][K] = the f32 weights of one 4-bit matrix with bf16 constants (the
+// rounding of the 4-bit GEMVs' dequantization, device.hpp).
+__global__ void __launch_bounds__(256) k_dequant_q4e(const void* codes, const unsigned short* scales,
+                                                     const unsigned short* biases, int n, int K, float* out) {
+    const int G = K / kGroup;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)n * G) return;
+    const int64_t row = gid / G;
+    const int g = (int)(gid % G);
+    WFrag<FMT_Q4> f;
+    load_frag_b16(f, codes, scales, biases, row, G, g);
+    dequant_q4_group(f, out + row * K + (int64_t)g * kGroup);
+}
+
+hipError_t launch_dequant_q4e(const void* codes, const unsigned short* scales, const unsigned short* biases, int n,
+                              int k, float* out, hipStream_t st) {
+    const int64_t groups = (int64_t)n * (k / kGroup);
+    const int64_t blocks = (groups + 255) / 256;
+    hipLaunchKernelGGL(k_dequant_q4e, dim3((unsigned)blocks), dim3(256), 0, st, codes, scales, biases, n, k, out);
     return hipGetLastError();
 }
 

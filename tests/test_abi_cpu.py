@@ -135,19 +135,17 @@ def test_layer_struct_layout_matches_the_header(tmp_path):
     """The binding's mtp_layer mirrors include/mtp.h field for field."""
     import subprocess
     src = tmp_path / "layout.c"
+    fields = ("sh_down", "gamma_q_head", "q_gated", "rotary_dim", "sinks", "window", "v_head_dim", "gate_exps4",
+              "sh_down4")
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "mtp.h"\n'
-                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(mtp_layer), '
-                   'offsetof(mtp_layer, sh_down), offsetof(mtp_layer, gamma_q_head), '
-                   'offsetof(mtp_layer, q_gated), offsetof(mtp_layer, rotary_dim), '
-                   'offsetof(mtp_layer, sinks), offsetof(mtp_layer, window)); return 0; }\n')
-    # (v_head_dim follows window; its offset is checked below)
+                   'int main(void) { printf("%zu %zu\\n", sizeof(mtp_layer), sizeof(mtp_q4e));'
+                   + "".join(f' printf("%zu\\n", offsetof(mtp_layer, {f}));' for f in fields)
+                   + ' return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(mtp.HEADER), str(src), "-o", str(exe)])
     got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     L = mtp.MtpLayer
-    assert got == [C.sizeof(L), L.sh_down.offset, L.gamma_q_head.offset, L.q_gated.offset, L.rotary_dim.offset,
-                   L.sinks.offset, L.window.offset]
-    assert L.v_head_dim.offset == L.window.offset + 4 and C.sizeof(L) >= L.v_head_dim.offset + 4
+    assert got == [C.sizeof(L), C.sizeof(mtp.MtpQ4E)] + [getattr(L, f).offset for f in fields]
 
 
 def test_attention_variant_fields_are_validated():
@@ -311,3 +309,46 @@ def test_noalloc_draft_step_rejects_steps_beyond_its_scratch():
     assert lib.mtp_draft_step_noalloc(*args(big, big + 7, 8)) == mtp.MTP_ERR_INVALID_ARG
     assert b"overflow" in lib.mtp_last_error()
     assert lib.mtp_draft_step_noalloc(*args(10, 20, 9)) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_moe_q4_rejects_unbuilt_shapes_and_mixed_formats():
+    """4-bit experts run on the slot kernel only: other feature counts, or a
+    shared expert of another size, are MTP_ERR_UNSUPPORTED; bad descriptors
+    are rejected before anything is enqueued."""
+    lib = mtp.lib()
+    q = lambda n, k, E=4: mtp.MtpQ4E(FAKE, FAKE, FAKE, n, k, E)  # noqa: E731
+    ws_big = 1 << 30
+
+    def call(ge, ue, de, sh=(None, None, None), H=None, top_k=2):
+        return lib.mtp_ffn_moe_q4(FAKE, None, 1e-6, FAKE, top_k, C.byref(ge), C.byref(ue), C.byref(de),
+                                  *(None if w is None else C.byref(w) for w in sh), None, FAKE * 2, None, None, 1,
+                                  FAKE * 3, ws_big, None)
+    assert call(q(96, 2048), q(96, 2048), q(2048, 96)) == mtp.MTP_ERR_UNSUPPORTED  # inter 96: 3 groups
+    assert b"4-bit experts" in lib.mtp_last_error()
+    assert call(q(512, 1024), q(512, 1024), q(1024, 512)) == mtp.MTP_ERR_UNSUPPORTED  # hidden 1024: 32 groups
+    sh = (q(256, 2048, 1), q(256, 2048, 1), q(2048, 256, 1))
+    assert call(q(512, 2048), q(512, 2048), q(2048, 512), sh) == mtp.MTP_ERR_UNSUPPORTED
+    assert b"shared expert" in lib.mtp_last_error()
+    bad = mtp.MtpQ4E(FAKE, FAKE, None, 512, 2048, 4)  # no biases
+    assert call(bad, q(512, 2048), q(2048, 512)) == mtp.MTP_ERR_INVALID_ARG
+    odd = mtp.MtpQ4E(FAKE, FAKE + 1, FAKE, 512, 2048, 4)  # bf16 scales must be 2-byte aligned
+    assert call(odd, q(512, 2048), q(2048, 512)) == mtp.MTP_ERR_INVALID_ARG
+    assert call(q(512, 2048), q(512, 2048), q(2048, 512, 3)) == mtp.MTP_ERR_INVALID_ARG  # expert counts differ
+    assert lib.mtp_dequant_q4e(C.byref(q(512, 2048)), 4, FAKE, None) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_draft_step_takes_the_4bit_expert_layer_fields():
+    """ffn_kind MTP_FFN_MOE_Q4 reads gate_exps4 ... sh_down4: a layer whose
+    4-bit stacks are missing is rejected, and its workspace is sized from them."""
+    lib = mtp.lib()
+    L = _layer(H=2048)
+    L.ffn_kind = mtp.MTP_FFN_MOE_Q4
+    L.top_k = 2
+    L.router = FAKE
+    args = (C.byref(L), FAKE, None, None, FAKE, FAKE * 2, FAKE * 3, 10, 20, 1, FAKE * 4, FAKE * 5, None, FAKE * 6,
+            1 << 30, None)
+    assert lib.mtp_draft_step(*args) == mtp.MTP_ERR_INVALID_ARG
+    assert b"gate_exps" in lib.mtp_last_error()
+    a = lib.mtp_draft_step_workspace_size(C.byref(L), 10, 4)
+    L.gate_exps4 = mtp.MtpQ4E(FAKE, FAKE, FAKE, 512, 2048, 256)
+    assert lib.mtp_draft_step_workspace_size(C.byref(L), 10, 4) > a

@@ -233,6 +233,30 @@ def test_lmhead_outlier_activations(m, fmt):
 
 
 @pytest.mark.parametrize("m", [1, 4])
+def test_moe_q4_outlier_activations(m):
+    for extra in range(20):
+        inp = synth.moe_inputs(synth.rng(136, m, extra), m, hidden=2048, n_experts=32, inter=512, top_k=4, q4=True)
+        xo, c2 = _outlier_rows(synth.rng(137, m, extra), m, 2048)
+        for st in (inp.gate_exps, inp.up_exps, inp.sh_gate, inp.sh_up):
+            # zero weight columns: code 8 with bias -8 * scale (bf16: -8 s is exact)
+            for c in c2:
+                word, nib, grp = c // 8, c % 8, c // 32
+                st.codes[:, :, word] = (st.codes[:, :, word] & ~np.uint32(0xF << (4 * nib))) | np.uint32(8 << (4 * nib))
+                st.biases[:, :, grp] = synth.bf16_bits(-8.0 * synth.bf16_value(st.scales[:, :, grp]))
+        inp = dataclasses.replace(inp, x=xo)
+        ok = planting.router_margin_ok(oracle.gemv_f32(inp.router, inp.x), inp.top_k, 1e-3)
+        if ok:
+            break
+    assert ok, "no seed met the routing margin gate"
+    w0 = oracle.deq4e(inp.gate_exps, 0)
+    assert (w0[:, c2] == 0).all()
+    y, ids, gates = _run_moe(inp)
+    ry, rids, rgates, _ = oracle.moe(inp)
+    assert ids.tolist() == rids.tolist()
+    _close(y, ry, "moe q4 y")
+
+
+@pytest.mark.parametrize("m", [1, 4])
 def test_q8gemv_and_moe_outlier_activations(m):
     g = synth.rng(133, m)
     x, cols = _outlier_rows(g, m, 2048)
@@ -646,10 +670,13 @@ def _moe_case(cfg_seed, m, **shape):
 
 
 def _run_moe(inp, gamma=None, residual=None):
-    dg, du, dd = mtp.DeviceQ8(inp.gate_exps), mtp.DeviceQ8(inp.up_exps), mtp.DeviceQ8(inp.down_exps)
-    sh = [mtp.DeviceQ8(w) for w in (inp.sh_gate, inp.sh_up, inp.sh_down)] if inp.sh_gate is not None else [None] * 3
-    y, ids, gates = mtp.mtp_ffn_moe_q(_t(inp.x), None if gamma is None else _t(gamma), 1e-6, _t(inp.router),
-                                      inp.top_k, dg, du, dd, *sh, residual=None if residual is None else _t(residual))
+    """mtp_ffn_moe_q (8-bit experts) or mtp_ffn_moe_q4 (4-bit, bf16 constants)."""
+    dev = mtp.device_experts
+    dg, du, dd = dev(inp.gate_exps), dev(inp.up_exps), dev(inp.down_exps)
+    sh = [dev(w) for w in (inp.sh_gate, inp.sh_up, inp.sh_down)] if inp.sh_gate is not None else [None] * 3
+    call = mtp.mtp_ffn_moe_q4 if inp.q4 else mtp.mtp_ffn_moe_q
+    y, ids, gates = call(_t(inp.x), None if gamma is None else _t(gamma), 1e-6, _t(inp.router), inp.top_k, dg, du,
+                         dd, *sh, residual=None if residual is None else _t(residual))
     return _np(y), _np(ids), _np(gates)
 
 
@@ -696,6 +723,53 @@ def test_moe_matrix_core_shapes(H, inter, m, E, top_k, shared):
     assert ids.tolist() == rids.tolist()
     _close(gates, rgates, "gates", tol=1e-5)
     _close(y, ry, "y")
+
+
+# 4-bit experts with bf16 group constants (the slot kernel's shapes: hidden
+# and intermediate of 2, 8, 16 or 64 groups)
+@pytest.mark.parametrize("m,shared", [(1, True), (2, False), (3, True), (4, True), (5, False), (8, True)])
+def test_moe_q4_small(m, shared):
+    _say(f"moe q4 small m={m} shared={shared}")
+    inp, extra = _moe_case(140, m, hidden=256, n_experts=16, inter=64, top_k=4, shared_inter=64 if shared else None,
+                           q4=True)
+    res = synth.normal(synth.rng(141, m), (m, 256))
+    y, ids, gates = _run_moe(inp, residual=res)
+    ry, rids, rgates, _ = oracle.moe(inp, residual=res)
+    assert ids.tolist() == rids.tolist()
+    _close(gates, rgates, "gates", tol=1e-5)
+    _close(y, ry, "y")
+
+
+@pytest.mark.parametrize("m", [1, 3, 4, 8])
+def test_moe_q4_config3_shape(m):
+    """The configuration's MoE (hidden 2048, 256 experts of 512, top-8 and a
+    shared expert) with 4-bit experts."""
+    _say(f"moe q4 config3 shape m={m}")
+    inp, extra = _moe_case(142, m, hidden=2048, n_experts=256, inter=512, top_k=8, shared_inter=512, q4=True)
+    _say(f"  seed extra {extra}")
+    y, ids, gates = _run_moe(inp)
+    ry, rids, rgates, _ = oracle.moe(inp)
+    assert ids.tolist() == rids.tolist()
+    _close(gates, rgates, "gates", tol=1e-5)
+    _close(y, ry, "y")
+
+
+@pytest.mark.parametrize("H,inter", [(64, 2048), (2048, 256)])
+def test_moe_q4_other_group_counts(H, inter):
+    _say(f"moe q4 H={H} I={inter}")
+    inp, extra = _moe_case(143, 4, hidden=H, n_experts=8, inter=inter, top_k=2, shared_inter=inter, q4=True)
+    y, ids, gates = _run_moe(inp)
+    ry, rids, rgates, _ = oracle.moe(inp)
+    assert ids.tolist() == rids.tolist()
+    _close(y, ry, "y")
+
+
+def test_dequant_q4e_bit_exact():
+    w = synth.q4e_weight(synth.rng(144), 3, 40, 2048)
+    dw = mtp.DeviceQ4E(w)
+    for e in range(3):
+        got = _np(mtp.mtp_dequant_q4e(dw, e))
+        assert np.array_equal(got.view(np.uint32), oracle.deq4e(w, e).view(np.uint32))
 
 
 def test_moe_with_input_norm():
@@ -841,11 +915,11 @@ def _oracle_moe_step(L, moe_inp, e_rows, h, kc, vc, cache_len):
     return ids, normed, logits, rl
 
 
-def _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cap):
+def _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cap, q4=False):
     S = synth.config4_step(seed_extra=3000 + extra, cache_len=cache_len, capacity=cap, hidden=H, n_heads=H // 128,
                            n_kv_heads=2 if H >= 256 else 1, head_dim=128, vocab=vocab, ffn_inter=64)
-    moe_inp = synth.moe_inputs(synth.rng(30, extra), 1, hidden=H, n_experts=E, inter=inter, top_k=top_k,
-                               shared_inter=inter)
+    moe_inp = synth.moe_inputs(synth.rng(30, extra, int(q4)), 1, hidden=H, n_experts=E, inter=inter, top_k=top_k,
+                               shared_inter=inter, q4=q4)
     L = S.layer
     kc, vc = S.k_cache.copy(), S.v_cache.copy()
     toks, hs, chain, rls = [-1], [S.h0[0]], [], []
@@ -865,12 +939,14 @@ def _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cap):
     return S, moe_inp, toks, chain, ver, ok
 
 
-@pytest.mark.parametrize("H,E,inter,top_k,vocab", [(256, 16, 64, 4, 1000), (2048, 256, 512, 8, 151936)])
-def test_draft_step_moe_chain_and_verify(H, E, inter, top_k, vocab):
-    _say(f"moe draft step H={H} E={E} top_k={top_k}")
+@pytest.mark.parametrize("H,E,inter,top_k,vocab,q4", [(256, 16, 64, 4, 1000, False), (2048, 256, 512, 8, 151936, False),
+                                                      (256, 16, 64, 4, 1000, True), (2048, 256, 512, 8, 151936, True)])
+def test_draft_step_moe_chain_and_verify(H, E, inter, top_k, vocab, q4):
+    _say(f"moe draft step H={H} E={E} top_k={top_k} q4={q4}")
     cache_len = 100 if H == 256 else 4096
     for extra in range(30):
-        S, moe_inp, toks, chain, ver, ok = _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cache_len + 8)
+        S, moe_inp, toks, chain, ver, ok = _moe_step_case(extra, H, E, inter, top_k, vocab, cache_len, cache_len + 8,
+                                                          q4)
         if ok:
             break
     assert ok, "no seed met the argmax and routing margin gates"
