@@ -140,6 +140,10 @@ class DenseLayer:
     window: int = 0
     # MiMo draft geometry (head 192 / V 128): the V heads' width (0 = head_dim)
     v_head_dim: int = 0
+    # multi-section rotary ([mtp.rs] `apply_imrope`, `mrope_section`): the
+    # sizes of the first three position-id sections (with the position ids of
+    # a call's rows given per call)
+    mrope_section: tuple = (0, 0, 0, 0)
 
     def q4_weights(self):
         return [self.eh_proj, self.wq, self.wk, self.wv, self.wo, self.gate, self.up, self.down, self.lm_head]
@@ -232,7 +236,8 @@ def gamma(g: np.random.Generator, h: int) -> np.ndarray:
 def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n_kv_heads: int = 2,
                 head_dim: int = 128, vocab: int = 151936, ffn_inter: int = 6144,
                 rope_theta: float = 1.0e6, eps: float = 1e-6, q_gated: bool = False, qk_norm: bool = False,
-                rotary_dim: int = 0, window: int = 0, sinks: bool = False, v_head_dim: int = 0) -> DenseLayer:
+                rotary_dim: int = 0, window: int = 0, sinks: bool = False, v_head_dim: int = 0,
+                mrope_section=(0, 0, 0, 0)) -> DenseLayer:
     """Dense MTP draft layer with 4-bit weights (draw order fixed; the
     attention variant's head norm weights are drawn last, then the sinks,
     U(-1, 3) per query head)."""
@@ -253,7 +258,8 @@ def dense_layer(g: np.random.Generator, hidden: int = 2048, n_heads: int = 16, n
     sk = g.uniform(-1.0, 3.0, size=n_heads).astype(np.float32) if sinks else None
     return DenseLayer(H, n_heads, n_kv_heads, head_dim, vocab, ffn_inter, float(rope_theta), float(eps),
                       gam[0], gam[1], gam[2], gam[3], gam[4], eh, wq, wk, wv, wo, gate, up, down, lm,
-                      gq, gk, bool(q_gated), int(rotary_dim), sk, int(window), int(v_head_dim))
+                      gq, gk, bool(q_gated), int(rotary_dim), sk, int(window), int(v_head_dim),
+                      tuple(int(v) for v in mrope_section))
 
 
 def kv_cache(g: np.random.Generator, n_kv_heads: int, filled: int, capacity: int, head_dim: int,
@@ -365,3 +371,14 @@ def config4_step(seed_extra: int = 0, cache_len: int = 4096, capacity: int = 410
     kc, vc = kv_cache(g, layer.n_kv_heads, cache_len, capacity, layer.head_dim, layer.v_head_dim)
     table = normal(g, (layer.vocab, layer.hidden))
     return StepInputs(layer, e0, h0, kc, vc, cache_len, capacity, table)
+
+
+def imrope_positions(g: np.random.Generator, m: int, base: int, spread: int = 64) -> np.ndarray:
+    """Four rotary position ids per row (int32 [m, 4]): the row's sequence
+    position base + r for the first id, the others drawn within +-spread of it
+    (the distinct per-section ids of a multimodal token)."""
+    p = np.empty((m, 4), dtype=np.int32)
+    for r in range(m):
+        p[r, 0] = base + r
+        p[r, 1:] = base + r + g.integers(-spread, spread + 1, size=3)
+    return np.maximum(p, 0)

@@ -77,7 +77,8 @@ class _Layer(C.Structure):
                 ("gate", _Q4), ("up", _Q4), ("down", _Q4), ("lm_head", _Q4),
                 ("gamma_q_head", C.c_void_p), ("gamma_k_head", C.c_void_p),
                 ("q_gated", C.c_int32), ("rotary_dim", C.c_int32),
-                ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32)]
+                ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32),
+                ("mrope_section", C.c_int32 * 4), ("positions", C.c_void_p)]
 
 
 class _MoeFfn(C.Structure):
@@ -111,6 +112,8 @@ def lib():
             "orc_rmsnorm": (None, [P, P, I, I, C.c_float, P]),
             "orc_rope": (None, [P, I, I, I, I, C.c_double]),
             "orc_rope_partial": (None, [P, I, I, I, I, I, C.c_double]),
+            "orc_imrope_section": (I, [I, P]),
+            "orc_rope_sections": (None, [P, I, I, I, I, P, P, C.c_double]),
             "orc_sdpa": (None, [P, P, P, I, I, I, I, I, I, P]),
             "orc_sdpa_window": (None, [P, P, P, I, I, I, I, I, I, I, P, P]),
             "orc_sdpa_kv": (None, [P, P, P, I, I, I, I, I, I, I, I, P, P]),
@@ -193,9 +196,13 @@ def _experts(w, keep: _Keep):
     return _q4e_list(w, keep) if hasattr(w, "biases") and w.codes.ndim == 3 else _q8_list(w, keep)
 
 
-def _layer(L, keep: _Keep) -> _Layer:
+def _layer(L, keep: _Keep, positions=None) -> _Layer:
+    """The layer descriptor; positions (int32 [m, 4]) are the call's rotary
+    position ids when given."""
     f = lambda a: keep.arr(a, np.float32).ctypes.data  # noqa: E731
     opt = lambda a: None if a is None else f(a)  # noqa: E731
+    sec = (C.c_int32 * 4)(*[int(v) for v in (getattr(L, "mrope_section", None) or (0, 0, 0, 0))])
+    pos = None if positions is None else keep.arr(np.asarray(positions).reshape(-1, 4), np.int32).ctypes.data
     return _Layer(L.hidden, L.n_heads, L.n_kv_heads, L.head_dim, L.vocab, L.ffn_inter,
                   float(L.rope_theta), float(L.eps),
                   f(L.gamma_e), f(L.gamma_h), f(L.gamma_attn), f(L.gamma_post), f(L.gamma_final),
@@ -204,7 +211,7 @@ def _layer(L, keep: _Keep) -> _Layer:
                   opt(getattr(L, "gamma_q_head", None)), opt(getattr(L, "gamma_k_head", None)),
                   int(bool(getattr(L, "q_gated", False))), int(getattr(L, "rotary_dim", 0) or 0),
                   opt(getattr(L, "sinks", None)), int(getattr(L, "window", 0) or 0),
-                  int(getattr(L, "v_head_dim", 0) or 0))
+                  int(getattr(L, "v_head_dim", 0) or 0), sec, pos)
 
 
 # --------------------------------------------------------------------------
@@ -300,6 +307,21 @@ def rope(x: np.ndarray, n_heads: int, head_dim: int, pos0: int, theta: float, ro
     return y
 
 
+def imrope_section(pair: int, sections) -> int:
+    sec = (C.c_int32 * 4)(*[int(v) for v in sections])
+    return int(lib().orc_imrope_section(int(pair), sec))
+
+
+def rope_sections(x: np.ndarray, n_heads: int, head_dim: int, rotary_dim: int, positions, sections,
+                  theta: float) -> np.ndarray:
+    """Rotary with four position ids per row (positions int32 [m, 4])."""
+    y = np.array(np.atleast_2d(x), dtype=np.float32, copy=True, order="C")
+    pos = _c(np.asarray(positions).reshape(-1, 4), np.int32)
+    sec = _c(np.asarray(sections).reshape(4), np.int32)
+    lib().orc_rope_sections(_p(y), y.shape[0], n_heads, head_dim, int(rotary_dim), _p(pos), _p(sec), float(theta))
+    return y
+
+
 def sdpa(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, n_heads: int, cache_len: int,
          window: int = 0, sinks: Optional[np.ndarray] = None) -> np.ndarray:
     """Causal GQA attention of q [m, n_heads*d] over the caches; window > 0
@@ -334,12 +356,13 @@ def norm_concat_proj(e, h, gamma_e, gamma_h, eps, w) -> np.ndarray:
     return u
 
 
-def attention(L, u, k_cache: np.ndarray, v_cache: np.ndarray, cache_len: int) -> np.ndarray:
-    """Attention block with residual; appends K/V rows into the given caches in place."""
+def attention(L, u, k_cache: np.ndarray, v_cache: np.ndarray, cache_len: int, positions=None) -> np.ndarray:
+    """Attention block with residual; appends K/V rows into the given caches in
+    place.  positions: the rows' four rotary position ids (int32 [m, 4])."""
     assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
     assert v_cache.flags.c_contiguous and v_cache.dtype == np.float32
     keep = _Keep()
-    d = _layer(L, keep)
+    d = _layer(L, keep, positions)
     u = keep.arr(np.atleast_2d(u), np.float32)
     r1 = np.empty_like(u)
     lib().orc_attention(C.byref(d), _p(u), _p(k_cache), _p(v_cache), cache_len, k_cache.shape[1],
@@ -422,17 +445,18 @@ def _moe_ffn(inp, keep: _Keep) -> _MoeFfn:
                    None, None, None, None, None, None)
 
 
-def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_logits: bool = True, moe=None):
+def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_logits: bool = True, moe=None,
+               positions=None):
     """One draft-layer forward over m rows; appends K/V rows in place.  With
     moe (a MoE input set of ``synth.moe_inputs``, 8-bit or 4-bit experts) the
     FFN is the routed mixture of those weights instead of the layer's dense
-    SwiGLU.
+    SwiGLU.  positions: the rows' four rotary position ids (int32 [m, 4]).
 
     Returns (ids [m], hidden_out [m, H] (post-final-norm), logits [m, V] or None)."""
     assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
     assert v_cache.flags.c_contiguous and v_cache.dtype == np.float32
     keep = _Keep()
-    d = _layer(L, keep)
+    d = _layer(L, keep, positions)
     h = keep.arr(np.atleast_2d(h), np.float32)
     m = h.shape[0]
     e = None if e is None else keep.arr(np.atleast_2d(e), np.float32)
@@ -454,13 +478,13 @@ def draft_step(L, e, tokens, table, h, k_cache, v_cache, cache_len: int, want_lo
     return ids, hid, logits
 
 
-def append_kv(L, e, tokens, table, pending_h, target_h, k_cache, v_cache, cache_len: int) -> None:
+def append_kv(L, e, tokens, table, pending_h, target_h, k_cache, v_cache, cache_len: int, positions=None) -> None:
     """Cache catch-up after a target batch: writes K/V rows cache_len .. cache_len+m-1
     in place (row r's hidden is target_h row r-1, row 0's pending_h or zero)."""
     assert k_cache.flags.c_contiguous and k_cache.dtype == np.float32
     assert v_cache.flags.c_contiguous and v_cache.dtype == np.float32
     keep = _Keep()
-    d = _layer(L, keep)
+    d = _layer(L, keep, positions)
     tgt = keep.arr(np.atleast_2d(target_h), np.float32)
     m = tgt.shape[0]
     e = None if e is None else keep.arr(np.atleast_2d(e), np.float32)

@@ -222,6 +222,46 @@ void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t po
     orc_rope_partial(x, m, n_heads, head_dim, head_dim, pos0, theta);
 }
 
+/* Which of a token's four position ids turns rotary pair j under the
+ * interleaved multi-section rotary of [mtp.rs] `apply_imrope` (sections
+ * `mrope_section` = sizes s0, s1, s2 of the first three ids; reading: the
+ * pairs cycle through ids 0, 1, 2 by j mod 3, each id keeping the pairs of
+ * its residue while it has pairs left (id k owns the pairs j = k mod 3 with
+ * j < 3 s_k), and every other pair takes the fourth id). */
+int32_t orc_imrope_section(int32_t pair, const int32_t* sections) {
+    const int32_t k = pair % 3;
+    return pair < 3 * sections[k] ? k : 3;
+}
+
+/* orc_rope_partial with a position per (row, section): pair i of row r turns
+ * by positions[4 r + orc_imrope_section(i)] * theta^(-2i/rotary_dim). */
+void orc_rope_sections(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t rotary_dim,
+                       const int32_t* positions, const int32_t* sections, double theta) {
+    const int32_t half = rotary_dim / 2;
+    for (int32_t r = 0; r < m; ++r)
+        for (int32_t hh = 0; hh < n_heads; ++hh) {
+            float* v = x + ((size_t)r * n_heads + hh) * head_dim;
+            for (int32_t i = 0; i < half; ++i) {
+                double pos = (double)positions[4 * (size_t)r + (size_t)orc_imrope_section(i, sections)];
+                double inv_freq = pow(theta, -2.0 * (double)i / (double)rotary_dim);
+                double ang = pos * inv_freq;
+                double c = cos(ang), s = sin(ang);
+                double a = v[i], b = v[i + half];
+                v[i] = (float)(a * c - b * s);
+                v[i + half] = (float)(a * s + b * c);
+            }
+        }
+}
+
+/* The rotary step of the layer for m rows of a call at cache_len. */
+static void layer_rope(const orc_layer* L, float* x, int32_t m, int32_t n_heads, int32_t cache_len) {
+    const int32_t d = L->head_dim, rot = L->rotary_dim > 0 ? L->rotary_dim : d;
+    if (L->positions)
+        orc_rope_sections(x, m, n_heads, d, rot, L->positions, L->mrope_section, L->rope_theta);
+    else
+        orc_rope_partial(x, m, n_heads, d, rot, cache_len, L->rope_theta);
+}
+
 /* Causal grouped-query attention over the cache ([mtp.rs]
  * `apply_sdpa_with_kv_cache` call in `forward_full_attention`; [mimo.rs]
  * `qwen_attention_batch` call in `mimo_mtp_block_with_probe`).  Query row r
@@ -343,7 +383,6 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
     const int32_t H = L->hidden, d = L->head_dim, nh = L->n_heads, nkv = L->n_kv_heads;
     const int32_t dv = L->v_head_dim > 0 ? L->v_head_dim : d;
     const int32_t qrows = nh * (L->q_gated ? d + dv : d);
-    const int32_t rot = L->rotary_dim > 0 ? L->rotary_dim : d;
     float* xa = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* qg = (float*)xmalloc(sizeof(float) * (size_t)m * qrows);
     float* q = (float*)xmalloc(sizeof(float) * (size_t)m * nh * d);
@@ -365,8 +404,8 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
     /* per-head norms: every head of every row is one RMSNorm row of head_dim */
     if (L->gamma_q_head) orc_rmsnorm(q, L->gamma_q_head, m * nh, d, L->eps, q);
     if (L->gamma_k_head) orc_rmsnorm(k, L->gamma_k_head, m * nkv, d, L->eps, k);
-    orc_rope_partial(q, m, nh, d, rot, cache_len, L->rope_theta);
-    orc_rope_partial(k, m, nkv, d, rot, cache_len, L->rope_theta);
+    layer_rope(L, q, m, nh, cache_len);
+    layer_rope(L, k, m, nkv, cache_len);
     for (int32_t r = 0; r < m; ++r)
         for (int32_t g = 0; g < nkv; ++g) {
             const size_t row = (size_t)g * capacity + (size_t)(cache_len + r);
@@ -395,7 +434,8 @@ void orc_attention(const orc_layer* L, const float* u, float* k_cache, float* v_
  * when there is none; row r > 0 = target_h row r-1); u = eh_proj [rms(e_r);
  * rms(shifted_r)]; then only the attention's K/V side runs: xa = rms(u;
  * gamma_attn), k = Wk xa, v = Wv xa, the per-head k norm when present, the
- * rotary step at position cache_len + r, and the rows are written at
+ * rotary step at position cache_len + r (or at the row's position ids when
+ * the layer carries them), and the rows are written at
  * cache_len + r.  Nothing else is computed (the FFN and the logits hold no
  * state). */
 void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, const float* embed_table,
@@ -403,7 +443,6 @@ void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, co
                    int32_t cache_len, int32_t capacity, int32_t m) {
     const int32_t H = L->hidden, d = L->head_dim, nkv = L->n_kv_heads;
     const int32_t dv = L->v_head_dim > 0 ? L->v_head_dim : d;
-    const int32_t rot = L->rotary_dim > 0 ? L->rotary_dim : d;
     float* er = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* sh = (float*)xmalloc(sizeof(float) * (size_t)m * H);
     float* u = (float*)xmalloc(sizeof(float) * (size_t)m * H);
@@ -427,7 +466,7 @@ void orc_append_kv(const orc_layer* L, const float* e, const int32_t* tokens, co
     orc_gemv4(&L->wk, xa, m, k);
     orc_gemv4(&L->wv, xa, m, v);
     if (L->gamma_k_head) orc_rmsnorm(k, L->gamma_k_head, m * nkv, d, L->eps, k);
-    orc_rope_partial(k, m, nkv, d, rot, cache_len, L->rope_theta);
+    layer_rope(L, k, m, nkv, cache_len);
     for (int32_t r = 0; r < m; ++r)
         for (int32_t g = 0; g < nkv; ++g) {
             const size_t row = (size_t)g * capacity + (size_t)(cache_len + r);

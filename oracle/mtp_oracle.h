@@ -85,7 +85,14 @@ typedef struct {
  *                 attention output per head): wv has n_kv_heads*dv rows, wo
  *                 n_heads*dv columns, the V cache rows are dv wide, and with
  *                 q_gated a head's gate rows (dv of them) follow its head_dim
- *                 q rows. */
+ *                 q rows.
+ * Multi-section rotary positions ([mtp.rs] `apply_imrope` with
+ * `mrope_section` and four position ids per token):
+ *   positions     NULL: row r of a call at cache_len sits at cache_len + r for
+ *                 every rotary pair; else int32 [m][4], the four position ids
+ *                 of each row of the call, and rotary pair j of row r turns by
+ *                 positions[4r + orc_imrope_section(j, mrope_section)];
+ *   mrope_section the four section sizes (see orc_imrope_section). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab, ffn_inter;
     double rope_theta;
@@ -97,6 +104,8 @@ typedef struct {
     const float* sinks;
     int32_t window;
     int32_t v_head_dim;
+    int32_t mrope_section[4];
+    const int32_t* positions;
 } orc_layer;
 
 /* The routed FFN of the MoE draft layer ([mtp.rs] `MtpFfnWeightsGpu::Moe`):
@@ -129,6 +138,9 @@ void orc_gemv4e(const orc_q4e* w, const float* x, int32_t m, float* y);
 void orc_gemv_f32(const float* w, int32_t n, int32_t k, const float* x, int32_t m, float* y);
 void orc_rmsnorm(const float* x, const float* gamma, int32_t m, int32_t h, float eps, float* y);
 void orc_rope(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t pos0, double theta);
+int32_t orc_imrope_section(int32_t pair, const int32_t* sections);
+void orc_rope_sections(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t rotary_dim,
+                       const int32_t* positions, const int32_t* sections, double theta);
 void orc_rope_partial(float* x, int32_t m, int32_t n_heads, int32_t head_dim, int32_t rotary_dim, int32_t pos0,
                       double theta);
 void orc_sdpa(const float* q, const float* k_cache, const float* v_cache, int32_t m,

@@ -1111,3 +1111,93 @@ def test_gemv4e_is_the_4bit_gemv_on_widened_constants():
         one = np.zeros((1, 128), np.float32)
         one[0, 77] = 1.0
         assert np.array_equal(oracle.gemv4e(st, one, e)[0], _exact_q4e(st, e)[:, 77].astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# multi-section rotary positions ([mtp.rs] `apply_imrope`, `mrope_section`)
+# --------------------------------------------------------------------------
+# sections (2, 2, 1) over 8 pairs, worked by hand from the reading: the ids
+# cycle 0, 1, 2 by pair index while each has pairs of its residue left
+# (id k keeps pair j = k mod 3 while j < 3 s_k): pairs 0..4 take 0, 1, 2, 0, 1;
+# pair 5 (residue 2, but id 2's one pair is pair 2) and pairs 6, 7 (ids 0 and
+# 1 have used their two) take the fourth id
+_SEC_221 = [0, 1, 2, 0, 1, 3, 3, 3]
+
+
+def test_imrope_section_map_hand_examples():
+    assert [oracle.imrope_section(j, (2, 2, 1, 0)) for j in range(8)] == _SEC_221
+    # a 64-dim rotary with sections (11, 11, 10): the interleave covers all 32 pairs
+    got = [oracle.imrope_section(j, (11, 11, 10, 0)) for j in range(32)]
+    assert got.count(0) == 11 and got.count(1) == 11 and got.count(2) == 10 and 3 not in got
+    assert got[:6] == [0, 1, 2, 0, 1, 2] and got[29:] == [2, 0, 1]
+    # no sections: every pair takes the fourth id
+    assert [oracle.imrope_section(j, (0, 0, 0, 0)) for j in range(6)] == [3] * 6
+
+
+def test_rope_sections_with_one_position_is_plain_rope():
+    x = synth.normal(np.random.default_rng(80), (3, 2 * 128))
+    pos = np.array([[700 + r] * 4 for r in range(3)], np.int32)
+    got = oracle.rope_sections(x, 2, 128, 64, pos, (11, 11, 10, 0), 1e6)
+    assert np.array_equal(got, oracle.rope(x, 2, 128, 700, 1e6, rotary_dim=64))
+
+
+def test_rope_sections_turn_each_pair_by_its_sections_position():
+    """Unit vectors (1 in every pair's first dim): pair j comes out as
+    (cos a_j, sin a_j) with a_j = pos[section j] * theta^(-2j/16)."""
+    theta = 1e4
+    pos = np.array([[5, 9, 13, 21]], np.int32)
+    x = np.zeros((1, 16), np.float32)
+    x[0, :8] = 1.0
+    got = oracle.rope_sections(x, 1, 16, 16, pos, (2, 2, 1, 0), theta)[0].astype(np.float64)
+    for j in range(8):
+        a = float(pos[0, _SEC_221[j]]) * theta ** (-2.0 * j / 16)
+        assert abs(got[j] - np.cos(a)) < 1e-6 and abs(got[j + 8] - np.sin(a)) < 1e-6, j
+
+
+def _imrope_layer(seed):
+    L = _small_layer(seed)
+    return dataclasses.replace(L, mrope_section=(2, 2, 1, 0))
+
+
+def test_attention_with_section_positions_depends_on_position_differences():
+    """With no cache rows the m rows attend to each other only, so adding one
+    offset to every position id of every row leaves the output unchanged (up
+    to the rounding of the angles); ids equal to the cache rows reproduce the
+    plain layer bit for bit; distinct per-section ids change the output."""
+    L = _imrope_layer(81)
+    g = np.random.default_rng(82)
+    m, cap = 3, 8
+    kc, vc = np.zeros((L.n_kv_heads, cap, L.head_dim), np.float32), np.zeros((L.n_kv_heads, cap, L.head_dim),
+                                                                            np.float32)
+    u = synth.normal(g, (m, L.hidden))
+    P = synth.imrope_positions(g, m, 0, spread=5) + 10
+    ra = oracle.attention(L, u, kc.copy(), vc.copy(), 0, positions=P)
+    rb = oracle.attention(L, u, kc.copy(), vc.copy(), 0, positions=P + 1000)
+    assert np.allclose(ra, rb, rtol=0, atol=2e-5 * np.abs(ra).max())
+    same = np.array([[r] * 4 for r in range(m)], np.int32)
+    assert np.array_equal(oracle.attention(L, u, kc.copy(), vc.copy(), 0, positions=same),
+                          oracle.attention(L, u, kc.copy(), vc.copy(), 0))
+    assert not np.allclose(ra, oracle.attention(L, u, kc.copy(), vc.copy(), 0), rtol=0, atol=1e-4)
+
+
+def test_draft_step_with_section_positions_batched_verify_equals_the_chain():
+    L = _imrope_layer(83)
+    g = np.random.default_rng(84)
+    cap, L0 = 40, 30
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, L0, cap, L.head_dim)
+    table = synth.normal(g, (L.vocab, L.hidden))
+    e0, h0 = synth.normal(g, (1, L.hidden)), synth.normal(g, (1, L.hidden))
+    P = synth.imrope_positions(g, 4, L0)
+    k1, v1 = kc.copy(), vc.copy()
+    toks, hs, chain = [-1], [h0[0]], []
+    for step in range(3):
+        ids, hid, lg = oracle.draft_step(L, e0, np.array([toks[-1]], np.int32), table, hs[-1][None], k1, v1,
+                                         L0 + step, positions=P[step:step + 1])
+        toks.append(int(ids[0]))
+        hs.append(hid[0])
+        chain.append((int(ids[0]), hid[0], lg[0]))
+    ids_v, hid_v, log_v = oracle.draft_step(L, np.repeat(e0, 4, 0), np.array(toks, np.int32), table, np.stack(hs),
+                                            kc.copy(), vc.copy(), L0, positions=P)
+    assert ids_v[:3].tolist() == [c[0] for c in chain]
+    assert np.array_equal(hid_v[:3], np.stack([c[1] for c in chain]))
+    assert np.array_equal(log_v[:3], np.stack([c[2] for c in chain]))
