@@ -145,7 +145,20 @@ typedef struct {
  *                 cache is [n_kv_heads][capacity][dv] (the K cache keeps
  *                 head_dim).  Built: head_dim 128 with V 128, and head_dim 192
  *                 with V 128 (no gated q or per-head norms there; rotary over
- *                 all 192 dims by default, pairs (i, i + 96)). */
+ *                 all 192 dims by default, pairs (i, i + 96)).
+ * Multi-section rotary positions ([mtp.rs] `apply_imrope` with
+ * `mrope_section` and four position ids per token; head_dim 128 only):
+ *   positions     NULL: row r of a call at cache_len turns every rotary pair
+ *                 by position cache_len + r.  Else device int32 [m][4] (4-byte
+ *                 aligned), read by every call that takes this descriptor:
+ *                 the four position ids of each of the call's m rows (for
+ *                 mtp_append_kv, of all its rows), and rotary pair j of row r
+ *                 turns by positions[4r + s(j)], where s(j) = j mod 3 when
+ *                 j < 3 * mrope_section[j mod 3], else 3 (the three sections
+ *                 interleave pair by pair, the fourth id takes the rest).  The
+ *                 cache row of row r stays cache_len + r either way.
+ *   mrope_section the section sizes (entries >= 0; only the first three are
+ *                 read). */
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, vocab;
     int32_t ffn_kind; /* MTP_FFN_DENSE_Q4, MTP_FFN_MOE_Q8 or MTP_FFN_MOE_Q4 */
@@ -163,6 +176,8 @@ typedef struct {
     int32_t window;
     int32_t v_head_dim;
     mtp_q4e gate_exps4, up_exps4, down_exps4, sh_gate4, sh_up4, sh_down4;
+    int32_t mrope_section[4];
+    const int32_t* positions;
 } mtp_layer;
 
 const char* mtp_status_string(mtp_status s);

@@ -75,7 +75,8 @@ class MtpLayer(C.Structure):
                 ("q_gated", C.c_int32), ("rotary_dim", C.c_int32),
                 ("sinks", C.c_void_p), ("window", C.c_int32), ("v_head_dim", C.c_int32),
                 ("gate_exps4", MtpQ4E), ("up_exps4", MtpQ4E), ("down_exps4", MtpQ4E),
-                ("sh_gate4", MtpQ4E), ("sh_up4", MtpQ4E), ("sh_down4", MtpQ4E)]
+                ("sh_gate4", MtpQ4E), ("sh_up4", MtpQ4E), ("sh_down4", MtpQ4E),
+                ("mrope_section", C.c_int32 * 4), ("positions", C.c_void_p)]
 
 
 _lib = None
@@ -248,7 +249,21 @@ class DeviceLayer:
                              int(getattr(dense, "rotary_dim", 0) or 0),
                              None if self.sinks is None else self.sinks.data_ptr(),
                              int(getattr(dense, "window", 0) or 0), int(getattr(dense, "v_head_dim", 0) or 0),
-                             *(q4e[k] for k in names))
+                             *(q4e[k] for k in names),
+                             (C.c_int32 * 4)(*[int(v) for v in (getattr(dense, "mrope_section", None)
+                                                                 or (0, 0, 0, 0))]), None)
+        self.positions = None
+
+    def set_positions(self, positions) -> None:
+        """The rotary position ids (int32 device tensor [rows, 4]) that the
+        following calls read for their rows; None: the rows' cache positions."""
+        if positions is not None:
+            torch = _torch()
+            if positions.dtype != torch.int32 or not positions.is_cuda or positions.dim() != 2 or \
+                    positions.shape[1] != 4 or not positions.is_contiguous():
+                raise ValueError("positions must be a contiguous int32 device tensor [rows, 4]")
+        self.positions = positions
+        self.desc.positions = None if positions is None else positions.data_ptr()
 
     @property
     def weight_nbytes(self) -> int:

@@ -229,6 +229,12 @@ hipError_t run_head(const float* hidden, const float* gamma, float eps, const mt
     return run_head_fmt(FMT_Q4, qmat(lm), lm.k, hidden, gamma, eps, normed_out, logits_out, ids, m, w, st);
 }
 
+// The rotary position ids of rows row0 .. of a call (NULL: the cache rows).
+void set_positions(AttnParams& a, const mtp_layer* L, int row0) {
+    a.positions = L->positions ? L->positions + 4 * (int64_t)row0 : nullptr;
+    for (int k = 0; k < 4; ++k) a.sec[k] = L->mrope_section[k];
+}
+
 hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* vc, int cache_len, int capacity,
                          int m, float* out, const AttnWs& w, hipStream_t st) {
     GemvParams p{};
@@ -268,6 +274,7 @@ hipError_t run_attention(const mtp_layer* L, const float* u, float* kc, float* v
     a.sinks = L->sinks;
     // the first row (position cache_len) sees nothing before cache_len - W + 1
     a.c0 = (L->window > 0 && cache_len - L->window + 1 > 0) ? (cache_len - L->window + 1) / kAttnChunk : 0;
+    set_positions(a, L, 0);
     if ((e = launch_attention(a, st)) != hipSuccess) return e;
     GemvParams o{};
     o.w[0] = qmat(L->wo);
@@ -388,8 +395,17 @@ mtp_status check_layer_attn(const mtp_layer* L) {
     if (L->window < 0) return fail(MTP_ERR_INVALID_ARG, "window=%d (0 or positive)", L->window);
     if (L->sinks && !a4(L->sinks))
         return fail(MTP_ERR_INVALID_ARG, "sinks must be 4-byte aligned");
+    for (int k = 0; k < 4; ++k)
+        if (L->mrope_section[k] < 0) return fail(MTP_ERR_INVALID_ARG, "mrope_section[%d]=%d", k, L->mrope_section[k]);
+    if (L->positions) {
+        if (!a4(L->positions)) return fail(MTP_ERR_INVALID_ARG, "positions must be 4-byte aligned");
+        if (L->head_dim != 128)
+            return fail(MTP_ERR_UNSUPPORTED, "positions (multi-section rotary) with head_dim=%d (128 is built)",
+                        L->head_dim);
+    }
     return MTP_OK;
 }
+
 
 mtp_status check_cache(const float* kc, const float* vc, int32_t cache_len, int32_t capacity, int32_t m,
                        const mtp_layer* L) {
@@ -651,6 +667,7 @@ mtp_status enqueue_append_kv(const mtp_layer* L, const float* e, const int32_t* 
         q.eps = L->eps;
         q.y = kv;
         if ((err = run_gemv(FMT_Q4, PRO_RMS, EPI_STORE, mc, q, default_blocks(), st)) != hipSuccess) break;
+        set_positions(a, L, c0);
         err = launch_append_kv(a, kv, mc, cache_len + c0, st);
     }
     return err == hipSuccess ? MTP_OK : hip_fail(err, "mtp_append_kv");

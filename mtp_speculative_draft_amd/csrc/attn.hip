@@ -153,7 +153,8 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
         const int mi = idx / rh, i = idx % rh;
         const double inv_freq = exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta);
-        rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
+        const int pos = (VAR && p.positions) ? p.positions[4 * mi + imrope_sec(i, p.sec)] : p.cache_len + mi;
+        rotary((double)pos, inv_freq, rc[mi][i], rs[mi][i]);
     }
     __syncthreads();
 
@@ -419,17 +420,19 @@ __global__ void __launch_bounds__(64) k_append_kv(const AttnParams p, const floa
     }
     const int pos = pos0 + r;
     const int rot = VAR ? p.rot : kD, rh = rot / 2;
+    // rotary position of pair j (the row's ids, offset by the piece's first row)
+    auto rpos = [&](int j) { return (VAR && p.positions) ? p.positions[4 * r + imrope_sec(j, p.sec)] : pos; };
     float ra, rb;
     if (rot == kD) {
         float cs, sn;
-        rotary((double)pos, exp2(-(2.0 * (double)lane / (double)kD) * p.log2_theta), cs, sn);
+        rotary((double)rpos(lane), exp2(-(2.0 * (double)lane / (double)kD) * p.log2_theta), cs, sn);
         ra = a * cs - b * sn;
         rb = a * sn + b * cs;
     } else {
         const float o = __shfl_xor(a, rh);
         const int j = lane & (rh - 1);
         float cs, sn;
-        rotary((double)pos, exp2(-(2.0 * (double)j / (double)rot) * p.log2_theta), cs, sn);
+        rotary((double)rpos(j), exp2(-(2.0 * (double)j / (double)rot) * p.log2_theta), cs, sn);
         ra = lane >= rot ? a : (lane < rh ? a * cs - o * sn : o * sn + a * cs);
         rb = b;
     }
@@ -642,11 +645,11 @@ hipError_t launch_shift_rows(const float* pending, const float* target, float* o
 hipError_t launch_append_kv(const AttnParams& p, const float* kv, int m, int pos0, hipStream_t st) {
     const dim3 grid((unsigned)m, (unsigned)p.nkv), block(kWave);
     if (p.d != kD || p.vd != kD) {
-        if (p.d > kWideKD || p.vd > kWideVD || p.rot > p.d || p.gk) return hipErrorInvalidValue;
+        if (p.d > kWideKD || p.vd > kWideVD || p.rot > p.d || p.gk || p.positions) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_append_kv_wide, grid, block, 0, st, p, kv, pos0);
         return hipGetLastError();
     }
-    if (p.gk || p.rot != kD)
+    if (p.gk || p.rot != kD || p.positions)
         hipLaunchKernelGGL(k_append_kv<true>, grid, block, 0, st, p, kv, pos0);
     else
         hipLaunchKernelGGL(k_append_kv<false>, grid, block, 0, st, p, kv, pos0);
@@ -660,10 +663,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
     if (p.d != kD || p.vd != kD) {
         // the combine below reads records of kD + 2 floats: V heads of kD
-        if (p.d > kWideKD || p.vd != kD || p.rot > p.d || p.gq || p.qg != 1 || p.m > 8)
+        if (p.d > kWideKD || p.vd != kD || p.rot > p.d || p.gq || p.qg != 1 || p.m > 8 || p.positions)
             return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_attn_partial_wide, grid, block, 0, st, p);
-    } else if (p.gq || p.rot != kD)
+    } else if (p.gq || p.rot != kD || p.positions)
         hipLaunchKernelGGL(k_attn_partial<true>, grid, block, 0, st, p);
     else
         hipLaunchKernelGGL(k_attn_partial<false>, grid, block, 0, st, p);

@@ -141,7 +141,16 @@ struct AttnParams {
     int window;           // 0, or W: row at position p sees positions p-W+1 .. p
     const float* sinks;   // per query head softmax sink logits [nh] (NULL: none)
     int c0;               // first chunk any row sees; partials are stored from it
+    const int* positions;  // [m][4] rotary position ids of the rows (NULL: row r at cache_len + r)
+    int sec[4];            // their section sizes (rotary pair j takes id imrope_sec(j, sec))
 };
+// Position id of rotary pair j: ids 0, 1, 2 interleave pair by pair while
+// each has pairs left (id k keeps the pairs j = k mod 3 with j < 3 sec[k]);
+// the other pairs take id 3.
+__host__ __device__ inline int imrope_sec(int j, const int (&sec)[4]) {
+    const int k = j % 3;
+    return j < 3 * sec[k] ? k : 3;
+}
 constexpr int kAttnChunk = 32;
 hipError_t launch_attention(const AttnParams& p, hipStream_t stream);
 // Cache catch-up: out [m][H] = (pending or 0, target rows 0 .. m-2); and the

@@ -136,7 +136,7 @@ def test_layer_struct_layout_matches_the_header(tmp_path):
     import subprocess
     src = tmp_path / "layout.c"
     fields = ("sh_down", "gamma_q_head", "q_gated", "rotary_dim", "sinks", "window", "v_head_dim", "gate_exps4",
-              "sh_down4")
+              "sh_down4", "mrope_section", "positions")
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "mtp.h"\n'
                    'int main(void) { printf("%zu %zu\\n", sizeof(mtp_layer), sizeof(mtp_q4e));'
                    + "".join(f' printf("%zu\\n", offsetof(mtp_layer, {f}));' for f in fields)
@@ -352,3 +352,28 @@ def test_draft_step_takes_the_4bit_expert_layer_fields():
     a = lib.mtp_draft_step_workspace_size(C.byref(L), 10, 4)
     L.gate_exps4 = mtp.MtpQ4E(FAKE, FAKE, FAKE, 512, 2048, 256)
     assert lib.mtp_draft_step_workspace_size(C.byref(L), 10, 4) > a
+
+
+def test_rotary_positions_are_validated():
+    """Negative section sizes, misaligned position ids and position ids on the
+    head-192 geometry are rejected on the host."""
+    lib = mtp.lib()
+    need = 1 << 30
+    args = lambda L: (C.byref(L), FAKE, FAKE * 2, FAKE * 3, 10, 20, 1, FAKE * 4, FAKE * 5, need, None)  # noqa: E731
+    L = _layer()
+    L.mrope_section[1] = -1
+    assert lib.mtp_attn_decode(*args(L)) == mtp.MTP_ERR_INVALID_ARG
+    assert b"mrope_section" in lib.mtp_last_error()
+    L = _layer()
+    L.positions = FAKE + 2
+    assert lib.mtp_attn_decode(*args(L)) == mtp.MTP_ERR_INVALID_ARG
+    assert b"positions" in lib.mtp_last_error()
+    L = _layer(d=192)
+    L.v_head_dim = 128
+    L.wq = _q4(2 * 192, 256)
+    L.wk = _q4(192, 256)
+    L.wv = _q4(128, 256)
+    L.wo = _q4(256, 2 * 128)
+    L.positions = FAKE
+    assert lib.mtp_attn_decode(*args(L)) == mtp.MTP_ERR_UNSUPPORTED
+    assert b"positions" in lib.mtp_last_error()

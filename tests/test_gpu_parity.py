@@ -516,6 +516,141 @@ def test_attn_decode_variant_small(variant, cache_len, m):
         assert oracle.rel_l2(ref0, ref) > 1e-3
 
 
+# multi-section rotary positions ([mtp.rs] `apply_imrope`, `mrope_section`):
+# four position ids per row, drawn apart so that the sections turn differently
+_IMROPE = {
+    "full": dict(mrope_section=(22, 21, 21, 0)),                    # 64 pairs over 128 dims
+    "rot64": dict(rotary_dim=64, mrope_section=(11, 11, 10, 0)),    # 32 pairs, the pages' 3 sections
+    "short": dict(rotary_dim=64, mrope_section=(4, 3, 2, 0)),       # pairs past the sections take id 3
+    "qknorm": dict(qk_norm=True, q_gated=True, rotary_dim=32, mrope_section=(6, 5, 5, 0)),
+}
+
+
+@pytest.mark.parametrize("variant,cache_len,m", [("full", 100, 1), ("rot64", 64, 4), ("short", 31, 3),
+                                                 ("qknorm", 100, 8), ("rot64", 0, 2)])
+def test_attn_decode_imrope_small(variant, cache_len, m):
+    _say(f"attn imrope {variant} cache_len={cache_len} m={m}")
+    L = synth.dense_layer(synth.rng(150, cache_len, m), hidden=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                          vocab=1000, ffn_inter=320, **_IMROPE[variant])
+    g = synth.rng(151, cache_len, m)
+    cap = cache_len + m + 3
+    kc, vc = synth.kv_cache(g, L.n_kv_heads, cache_len, cap, 128)
+    u = synth.normal(g, (m, L.hidden))
+    P = synth.imrope_positions(g, m, cache_len, spread=200)
+    dl = mtp.DeviceLayer(L)
+    dl.set_positions(_t(P))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(dl, _t(u), dk, dv, cache_len))
+    kr, vr = kc.copy(), vc.copy()
+    ref = oracle.attention(L, u, kr, vr, cache_len, positions=P)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, cache_len:cache_len + m], kr[:, cache_len:cache_len + m], "appended k")
+    _close(_np(dv)[:, cache_len:cache_len + m], vr[:, cache_len:cache_len + m], "appended v")
+    # the per-section ids change this case's output
+    ref0 = oracle.attention(L, u, kc.copy(), vc.copy(), cache_len)
+    assert oracle.rel_l2(ref0, ref) > 1e-3
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_attn_decode_imrope_config4_shape(m):
+    _say(f"attn imrope config4 shape m={m}")
+    g = synth.rng(152, m)
+    L = synth.dense_layer(g, vocab=64, ffn_inter=64, rotary_dim=64, mrope_section=(11, 11, 10, 0))
+    kc, vc = synth.kv_cache(g, 2, 4096, 4104, 128)
+    u = synth.normal(g, (m, L.hidden))
+    P = synth.imrope_positions(g, m, 4096, spread=500)
+    dl = mtp.DeviceLayer(L)
+    dl.set_positions(_t(P))
+    dk, dv = _t(kc), _t(vc)
+    got = _np(mtp.mtp_attn_decode(dl, _t(u), dk, dv, 4096))
+    kr, vr = kc.copy(), vc.copy()
+    ref = oracle.attention(L, u, kr, vr, 4096, positions=P)
+    _close(got, ref, "out")
+    _close(_np(dk)[:, 4096:4096 + m], kr[:, 4096:4096 + m], "appended k")
+
+
+@pytest.mark.parametrize("m", [3, 13])
+def test_append_kv_imrope(m):
+    """The catch-up's K rows at the rows' own position ids (13 rows: two
+    pieces, the second reading its ids from row 8 on)."""
+    _say(f"append_kv imrope m={m}")
+    S = synth.config4_step(seed_extra=153 + m, cache_len=20, capacity=20 + m + 3, hidden=256, n_heads=4,
+                           n_kv_heads=2, head_dim=128, vocab=500, ffn_inter=64, rotary_dim=64,
+                           mrope_section=(11, 11, 10, 0))
+    L = S.layer
+    g = synth.rng(154, m)
+    target = synth.normal(g, (m, L.hidden))
+    pend = synth.normal(g, (L.hidden,))
+    e = synth.normal(g, (m, L.hidden))
+    P = synth.imrope_positions(g, m, S.cache_len, spread=300)
+    kr, vr = S.k_cache.copy(), S.v_cache.copy()
+    oracle.append_kv(L, e, None, None, pend, target, kr, vr, S.cache_len, positions=P)
+    dl = mtp.DeviceLayer(L)
+    dl.set_positions(_t(P))
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    mtp.mtp_append_kv(dl, _t(e), None, None, _t(pend), _t(target), dk, dv, S.cache_len)
+    L0 = S.cache_len
+    _close(_np(dk)[:, L0:L0 + m], kr[:, L0:L0 + m], "k rows")
+    _close(_np(dv)[:, L0:L0 + m], vr[:, L0:L0 + m], "v rows")
+
+
+@pytest.mark.parametrize("H", [256, 2048])
+def test_draft_step_imrope_chain_and_verify(H):
+    """The K=3 chain and the m=4 verify with per-row position ids (the
+    verify's rows reuse the chain rows' ids)."""
+    _say(f"draft step imrope H={H}")
+    big = H == 2048
+    for extra in range(1, 30):
+        S = synth.config4_step(seed_extra=1700 + extra, cache_len=4096 if big else 100,
+                               capacity=4104 if big else 110, rotary_dim=64, mrope_section=(11, 11, 10, 0),
+                               **({} if big else dict(hidden=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                                                      vocab=1000, ffn_inter=320)))
+        L = S.layer
+        P = synth.imrope_positions(synth.rng(155, extra), 4, S.cache_len, spread=300)
+        kc, vc = S.k_cache.copy(), S.v_cache.copy()
+        toks, hs, out = [-1], [S.h0[0]], []
+        for step in range(3):
+            ids, hid, lg = oracle.draft_step(L, S.e0, np.array([toks[-1]], np.int32), S.table, hs[-1][None], kc, vc,
+                                             S.cache_len + step, positions=P[step:step + 1])
+            toks.append(int(ids[0]))
+            hs.append(hid[0])
+            out.append((int(ids[0]), hid[0], lg[0]))
+        kv = S.k_cache.copy(), S.v_cache.copy()
+        ver = oracle.draft_step(L, S.e0, np.array(toks, np.int32), S.table, np.stack(hs), kv[0], kv[1], S.cache_len,
+                                positions=P)
+        margins = [planting.head_margin(o[2]) for o in out] + [planting.head_margin(r) for r in ver[2]]
+        if min(margins) >= 1e-2:
+            break
+    assert min(margins) >= 1e-2, "no seed met the argmax margin gate"
+    _say(f"  seed {extra}: chain {toks[1:]} verify {ver[0].tolist()}")
+    dl = mtp.DeviceLayer(L)
+    dtable = _t(S.table)
+    dP = _t(P)
+    m_h = torch.empty((4, L.hidden), dtype=torch.float32, device=DEV)
+    m_h[0].copy_(_t(S.h0[0]))
+    tok = torch.full((4,), -1, dtype=torch.int32, device=DEV)
+    e0 = _t(S.e0)
+    dk, dv = _t(S.k_cache), _t(S.v_cache)
+    logits = torch.empty((3, L.vocab), dtype=torch.float32, device=DEV)
+    for step in range(3):
+        dl.set_positions(dP[step:step + 1])
+        mtp.mtp_draft_step(dl, e0, tok[step:step + 1], dtable, m_h[step:step + 1], dk, dv, S.cache_len + step,
+                           ids_out=tok[step + 1:step + 2], hidden_out=m_h[step + 1:step + 2],
+                           logits_out=logits[step:step + 1])
+    assert _np(tok)[1:].tolist() == toks[1:]
+    _close(_np(m_h)[1:], np.stack([o[1] for o in out]), "chain hidden")
+    _close(_np(logits), np.stack([o[2] for o in out]), "chain logits")
+    dl.set_positions(dP)
+    ids_v = torch.empty(4, dtype=torch.int32, device=DEV)
+    hid_v = torch.empty((4, L.hidden), dtype=torch.float32, device=DEV)
+    log_v = torch.empty((4, L.vocab), dtype=torch.float32, device=DEV)
+    mtp.mtp_draft_step(dl, e0.repeat(4, 1).contiguous(), tok, dtable, m_h, dk, dv, S.cache_len, ids_out=ids_v,
+                       hidden_out=hid_v, logits_out=log_v)
+    assert _np(ids_v).tolist() == ver[0].tolist()
+    _close(_np(hid_v), ver[1], "verify hidden")
+    _close(_np(log_v), ver[2], "verify logits")
+
+
 @pytest.mark.parametrize("m", [1, 4])
 def test_attn_decode_variant_config4_shape(m):
     """All variant steps at the full attention size (16/2 heads x 128, cache 4096)."""
