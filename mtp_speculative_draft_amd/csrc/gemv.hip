@@ -865,13 +865,14 @@ __device__ __forceinline__ float add_terms(float x) {
 // register as the current unit consumes them (past the last unit, and for
 // the first request, they go to unit 0, one small region that hits in L2,
 // which keeps the loads unconditional).
-template <int FMT, int PRO>
-__global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p) {
-    constexpr int R = kMaxWaves / 4;  // waves per activation row in the setup
+template <int FMT, int PRO, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
+    static_assert(W >= 4, "waves 0-3 build the B operands");
+    constexpr int R = 1;  // waves per activation row in the setup
     constexpr int NT = FMT == FMT_Q4 ? 16 : 32;  // 16-byte code loads per lane and unit
     __shared__ u32x4 bq[64 * kBGroup];               // 48 KB: B operands
     __shared__ float tx[64][kMmaCols];               // 4 KB: group sums in column 3 mi (4-bit bias)
-    __shared__ float stage[kMaxWaves][64 * kStage];  // 40 KB: each wave's scales, [group][row]
+    __shared__ float stage[W][64 * kStage];  // 5 KB per wave: its scales, [group][row]
     __shared__ float part[3][4][R];
     __shared__ float unsc[4];
     __shared__ int claim_ctr;
@@ -927,18 +928,32 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         }
     };
 
-    XPieces<1, 8 / R> xp;
-    mma_load_x<PRO, 1, 8 / R>(p, v, wid & 3, wid >> 2, lane, xp);
+    // Waves 0-3 build the B operands (activation row w each) while the
+    // other waves request their first unit's weights at once.  A wave issues
+    // its memory requests in order and stalls while the memory queues are
+    // full, so a wave that requested weights first would start its setup only
+    // once the weights drain; the barrier after the activation requests keeps
+    // those ahead of every weight request of the block.
+    XPieces<1, 8> xp;
+    const bool setup_wave = wid < 4;
+    if (setup_wave) mma_load_x<PRO, 1, 8>(p, v, wid, 0, lane, xp);
+    __builtin_amdgcn_s_barrier();
     int u = ts.next(claim);
-    {
+    auto first_loads = [&]() {
         const char* crow;
         const float *srow, *brow;
         row_ptrs(u >= 0 ? u : 0, crow, srow, brow);
 #pragma unroll
         for (int t = 0; t < NT; ++t) load_codes(crow, t);
         load_sb(srow, brow);
+    };
+    if (setup_wave) {
+        mma_setup<FMT, PRO, 1, 1>(p, v, wid, 0, lane, xp, bq, tx, unsc, part);  // ends with a block barrier
+        first_loads();
+    } else {
+        first_loads();
+        __syncthreads();  // the setup's closing barrier
     }
-    mma_setup<FMT, PRO, 1, R>(p, v, wid & 3, wid >> 2, lane, xp, bq, tx, unsc, part);
     const float cf = j < kBCols ? unsc[mi_l] : 0.0f;
     while (u >= 0) {
         const int nu = ts.next(claim);
@@ -1024,8 +1039,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         u = nu;
     }
     {
-        __shared__ float bv_s[kMaxWaves][8];
-        __shared__ int bi_s[kMaxWaves][8];
+        __shared__ float bv_s[W][8];
+        __shared__ int bi_s[W][8];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             float bvv = (writer && mi_l == mi) ? best : -INFINITY;
@@ -1038,7 +1053,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_gemv_mma(const GemvParams p)
         }
         __syncthreads();
         __shared__ unsigned long long sink[kHeadRows];
-        if (wid == 0) grid_argmax<4>(p, kMaxWaves, bv_s, bi_s, sink, lane);
+        if (wid == 0) grid_argmax<4>(p, W, bv_s, bi_s, sink, lane);
     }
 }
 
@@ -1299,9 +1314,10 @@ static hipError_t launch_mma_sk(const GemvParams& p, hipStream_t st) {
 // One 8-wave block per compute unit (fewer for a small matrix).
 template <int FMT, int PRO>
 static hipError_t launch_mma_head(const GemvParams& p, hipStream_t st) {
+    constexpr int W = kMaxWaves;
     const int units = (p.N + kMmaRows - 1) / kMmaRows;
-    const int need = (units + kMaxWaves - 1) / kMaxWaves, cu = device_cu_count();
-    hipLaunchKernelGGL((k_gemv_mma<FMT, PRO>), dim3(need < cu ? need : cu), dim3(64 * kMaxWaves), 0, st, p);
+    const int need = (units + W - 1) / W, cu = device_cu_count();
+    hipLaunchKernelGGL((k_gemv_mma<FMT, PRO, W>), dim3(need < cu ? need : cu), dim3(64 * W), 0, st, p);
     return hipGetLastError();
 }
 
