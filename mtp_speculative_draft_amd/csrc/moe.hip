@@ -6,8 +6,8 @@
 //
 // Launch sequence (one stream, no host round trip):
 //   k_moe_router   one block per expert row: optional input RMSNorm, f32
-//                  router dot products for all m rows (block 0 stores the
-//                  normalised rows for the expert GEMVs).
+//                  router dot products for the m <= 4 rows of a pass (block 0
+//                  stores the normalised rows for the expert GEMVs).
 //   k_moe_topk     one block: per row softmax, top-k by (p desc, index asc),
 //                  renormalised gates; then the union of selected experts over
 //                  the m rows is compacted (ascending expert id) into slots,
@@ -32,70 +32,62 @@ namespace mtp {
 
 constexpr int kMaxE = 1024;
 
+// One block per router row e, m <= 4 rows: every global value the block
+// needs (its router row, the rows' features and the norm weights) is
+// requested in one round, and the rows' sums of squares and their dot
+// products with the row are formed together, so the norm costs no second
+// memory round trip: logit = rsqrt(mean(x^2) + eps) * sum_k w_k x_k gamma_k.
+constexpr int kRouterU = 8;  // features per thread and round (2048 per block round)
 __global__ void __launch_bounds__(256) k_moe_router(const MoeParams p) {
-    __shared__ float red[4][8];
-    __shared__ float inv_s[8];
+    __shared__ float red[4][2][4];  // [wave][sum of squares | dot][row]
+    __shared__ float inv_s[4];
     const int e = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
     const float* w = p.router + (int64_t)e * p.H;
-    float inv[8];
+    const bool norm = p.gamma != nullptr;
+    float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < p.H; k0 += 256 * kRouterU) {
+        float wv[kRouterU], gv[kRouterU], xv[4][kRouterU];
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) inv[mi] = 1.0f;
-    if (p.gamma) {
+        for (int u = 0; u < kRouterU; ++u) {
+            const int k = k0 + t + 256 * u;
+            const bool in = k < p.H;
+            wv[u] = in ? w[k] : 0.0f;
+            gv[u] = (in && norm) ? p.gamma[k] : 1.0f;
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            if (mi < p.m) {
-                float ss = 0.0f;
-                for (int k = t; k < p.H; k += blockDim.x) {
-                    const float v = p.x[(int64_t)mi * p.H + k];
-                    ss = fmaf(v, v, ss);
-                }
-                ss = wave_sum(ss);
-                if (lane == 0) red[wid][mi] = ss;
+            for (int mi = 0; mi < 4; ++mi) xv[mi][u] = (in && mi < p.m) ? p.x[(int64_t)mi * p.H + k] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kRouterU; ++u)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                ss[mi] = fmaf(xv[mi][u], xv[mi][u], ss[mi]);
+                dot[mi] = fmaf(wv[u], xv[mi][u] * gv[u], dot[mi]);
             }
-        }
-        __syncthreads();
-        if (t < p.m) {
-            float ss = 0.0f;
-            for (int j = 0; j < (int)(blockDim.x / kWave); ++j) ss += red[j][t];
-            inv_s[t] = rsqrtf(ss / (float)p.H + p.eps);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) inv[mi] = (mi < p.m) ? inv_s[mi] : 1.0f;
-        if (e == 0) {
-            for (int mi = 0; mi < p.m; ++mi)
-                for (int k = t; k < p.H; k += blockDim.x)
-                    p.f[(int64_t)mi * p.H + k] = p.x[(int64_t)mi * p.H + k] * inv_s[mi] * p.gamma[k];
-        }
-        __syncthreads();
-    }
-    float acc[8];
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi) acc[mi] = 0.0f;
-    for (int k = t; k < p.H; k += blockDim.x) {
-        const float wv = w[k];
-        const float gk = p.gamma ? p.gamma[k] : 1.0f;
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            if (mi < p.m) {
-                float xv = p.x[(int64_t)mi * p.H + k];
-                if (p.gamma) xv = xv * inv[mi] * gk;
-                acc[mi] = fmaf(wv, xv, acc[mi]);
-            }
-        }
     }
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-        if (mi < p.m) {
-            const float s = wave_sum(acc[mi]);
-            if (lane == 0) red[wid][mi] = s;
+    for (int mi = 0; mi < 4; ++mi) {
+        const float a = wave_sum(ss[mi]), d = wave_sum(dot[mi]);
+        if (lane == 0) {
+            red[wid][0][mi] = a;
+            red[wid][1][mi] = d;
         }
     }
     __syncthreads();
     if (t < p.m) {
-        float s = 0.0f;
-        for (int j = 0; j < (int)(blockDim.x / kWave); ++j) s += red[j][t];
-        p.logits[(int64_t)t * p.E + e] = s;
+        float a = 0.0f, d = 0.0f;
+        for (int j = 0; j < 4; ++j) {
+            a += red[j][0][t];
+            d += red[j][1][t];
+        }
+        const float inv = norm ? rsqrtf(a / (float)p.H + p.eps) : 1.0f;
+        inv_s[t] = inv;
+        p.logits[(int64_t)t * p.E + e] = d * inv;
+    }
+    if (norm && e == 0) {  // the normalised rows for the expert GEMVs
+        __syncthreads();
+        for (int mi = 0; mi < p.m; ++mi)
+            for (int k = t; k < p.H; k += blockDim.x)
+                p.f[(int64_t)mi * p.H + k] = p.x[(int64_t)mi * p.H + k] * inv_s[mi] * p.gamma[k];
     }
 }
 
