@@ -273,9 +273,10 @@ struct SlotGemv {
     const int* n_slots;
     // Routing in the gate/up launch: when logits ([m][E] router logits) is
     // set, every block selects the experts itself, so no launch sits between
-    // the router and the experts.  Slot j < n_routed is the j-th selected
-    // expert in ascending order, slot n_routed the shared expert when
-    // has_shared.  Block (0, 0) publishes the slot table and count (read by
+    // the router and the experts.  With a shared expert it takes slot 0 (its
+    // blocks skip the routing and stream at once) and slot 1 + j is the j-th
+    // selected expert in ascending order; without one slot j is.  Block 0 of
+    // the first routed slot publishes the slot table and count (read by
     // the down and combine launches) and the per-row selections.
     const float* logits;
     int E, top_k, has_shared;
@@ -313,7 +314,8 @@ __device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane
                                            unsigned long long (*rmask)[kMaxE / kWave], int (*rid)[kWave],
                                            float (*rgate)[kWave], int* s_e, float* s_gate) {
     const int words = (p.E + kWave - 1) / kWave;
-    const bool publish = blockIdx.x == 0 && slot == 0;
+    const bool publish = blockIdx.x == 0 && slot == p.has_shared;
+    const int rslot = slot - p.has_shared;  // routed slot index (the shared expert holds slot 0)
     for (int mi = wid; mi < p.m; mi += W) {
         int id;
         float gate;
@@ -345,26 +347,26 @@ __device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane
     const int n_routed = __shfl(incl, kWave - 1);
     const int n_slots = n_routed + p.has_shared;
     if (publish) {
-        int idx = excl;
+        int idx = p.has_shared + excl;
         for (unsigned long long b = mw; b; b &= b - 1ull) p.slot_expert_out[idx++] = lane * kWave + __ffsll((long long)b) - 1;
         if (lane == 0) {
-            if (p.has_shared) p.slot_expert_out[n_routed] = -1;
+            if (p.has_shared) p.slot_expert_out[0] = -1;
             *p.n_slots_out = n_slots;
         }
     }
     int e;
-    if (slot < n_routed) {
-        const bool mine = lane < words && slot >= excl && slot < incl;
+    if (rslot < n_routed) {
+        const bool mine = lane < words && rslot >= excl && rslot < incl;
         int cand = 0;
         if (mine) {
             unsigned long long b = mw;
-            for (int k = slot - excl; k > 0; --k) b &= b - 1ull;
+            for (int k = rslot - excl; k > 0; --k) b &= b - 1ull;
             cand = lane * kWave + __ffsll((long long)b) - 1;
         }
         const unsigned long long who = __ballot(mine);
         e = __shfl(cand, __ffsll((long long)who) - 1);
     } else {
-        e = slot < n_slots ? -1 : -2;
+        e = -2;  // past the selected experts: no such slot
     }
     for (int mi = 0; mi < p.m; ++mi) {
         float gate = 1.0f;
@@ -466,7 +468,11 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     }
 
     int e;
-    if (route) {
+    if (route && p.has_shared && slot == 0) {
+        // the shared expert: no routing to wait for, a gate of 1 for every row
+        e = -1;
+        if (threadIdx.x < 8) s_gate[threadIdx.x] = 1.0f;
+    } else if (route) {
         if constexpr (EPI == EPI_SWIGLU) route_slot<W>(p, slot, lane, wid, rmask, rid, rgate, &s_e, s_gate);
         __syncthreads();
         e = s_e;
