@@ -27,6 +27,7 @@ struct View {
     const float* rowscale;
 };
 
+template <bool SLOT>
 __device__ __forceinline__ bool resolve_view(const GemvParams& p, View& v) {
     v.c0 = p.w[0].codes;
     v.s0 = p.w[0].scales;
@@ -51,7 +52,7 @@ __device__ __forceinline__ bool resolve_view(const GemvParams& p, View& v) {
     v.x0 = p.x0;
     v.y = p.y;
     v.rowscale = p.rowscale;
-    if (p.slot_expert) {
+    if constexpr (SLOT) {
         const int slot = blockIdx.y;
         if (slot >= *p.n_slots) return false;
         const int e = p.slot_expert[slot];
@@ -122,7 +123,7 @@ __device__ __forceinline__ void load_x_row(const GemvParams& p, const View& v, i
 // one input row) and the matching gamma.
 template <int PRO>
 __device__ __forceinline__ const float* x_segment(const GemvParams& p, const View& v, int mi, int seg,
-                                                  const float*& gam) {
+                                                  const float*& gam, int tok_in = INT_MIN) {
     if constexpr (PRO == PRO_CONCAT) {
         if (seg) {
             gam = p.g1;
@@ -130,7 +131,7 @@ __device__ __forceinline__ const float* x_segment(const GemvParams& p, const Vie
         }
         gam = p.g0;
         if (p.tokens) {
-            int tok = p.tokens[mi];
+            int tok = tok_in != INT_MIN ? tok_in : p.tokens[mi];  // tok_in: the row's token, already read
             if (tok >= 0 || v.x0 == nullptr) {
                 tok = tok < 0 ? 0 : (tok < p.vocab ? tok : p.vocab - 1);
                 return p.table + (int64_t)tok * p.H;
@@ -201,9 +202,10 @@ constexpr int kGroupStride = 36;  // floats between groups in the LDS transposes
 constexpr int kRow1Floats = kWave * kGroupStride;
 
 template <int PRO>
-__device__ __forceinline__ void row1_load(const GemvParams& p, const View& v, int lane, int s, Row1Pieces& rp) {
+__device__ __forceinline__ void row1_load(const GemvParams& p, const View& v, int lane, int s, int tok0,
+                                          Row1Pieces& rp) {
     const float *gam0 = nullptr, *gam1 = nullptr;
-    const float* src0 = x_segment<PRO>(p, v, 0, 0, gam0);
+    const float* src0 = x_segment<PRO>(p, v, 0, 0, gam0, PRO == PRO_CONCAT ? tok0 : INT_MIN);
     const float* src1 = PRO == PRO_CONCAT ? x_segment<PRO>(p, v, 0, 1, gam1) : src0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -287,7 +289,9 @@ struct TileFrags {
     WFrag<FMT> f[R][P];
 };
 
-template <int FMT, int R, int P>
+// MULTI: up to three matrices concatenated along n (P == 1); otherwise one
+// matrix, or the SwiGLU pair (P == 2).
+template <int FMT, int R, int P, bool MULTI>
 __device__ __forceinline__ void load_tile(TileFrags<FMT, R, P>& tf, const View& v, int row0, int gc) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -296,6 +300,8 @@ __device__ __forceinline__ void load_tile(TileFrags<FMT, R, P>& tf, const View& 
         if constexpr (P == 2) {
             load_frag(tf.f[r][0], v.c0, v.s0, v.b0, row, v.G, gc);
             load_frag(tf.f[r][1], v.c1, v.s1, v.b1, row, v.G, gc);
+        } else if constexpr (!MULTI) {
+            load_frag(tf.f[r][0], v.c0, v.s0, v.b0, row, v.G, gc);
         } else {
             // rows of up to three matrices concatenated along n (row is
             // wave-uniform); the matrix is picked with 0/1 multiples of the
@@ -371,18 +377,32 @@ __device__ __forceinline__ void grid_argmax(const GemvParams& p, int nw, const f
 // a block share the units blockIdx.x + gridDim.x * k and claim k one at a
 // time from a counter in LDS, so a wave that is served faster takes more
 // units; one claim is kept in flight.
+// In the shared mode wave w's first ns units are fixed (k = w, Q + w, ...), so
+// that they can be requested before the block has set its counter up; the
+// counter starts at ns * Q and start_claims() (after the block barrier that
+// follows the counter's initialisation) puts the first claim in flight.
 struct TileSeq {
     int base, step, NU, i;
     bool shared;
+    int wid, Q, ns;
     int pend;  // claim in flight (valid in lane 0)
 
-    template <class Claim>
-    __device__ void init(int b, int st, int nu, bool sh, Claim claim) {
+    __device__ void init(int b, int st, int nu) {
         base = b;
         step = st;
         NU = nu;
         i = 0;
-        shared = sh;
+        shared = false;
+    }
+    __device__ void init_shared(int b, int st, int nu, int w, int q, int nfixed) {
+        init(b, st, nu);
+        shared = true;
+        wid = w;
+        Q = q;
+        ns = nfixed;
+    }
+    template <class Claim>
+    __device__ void start_claims(Claim claim) {
         if (shared) pend = claim();
     }
     template <class Claim>
@@ -390,6 +410,8 @@ struct TileSeq {
         int k;
         if (!shared) {
             k = i++;
+        } else if (i < ns) {
+            k = i++ * Q + wid;
         } else {
             k = __builtin_amdgcn_readfirstlane(pend);
             pend = claim();
@@ -399,27 +421,60 @@ struct TileSeq {
     }
 };
 
-template <int FMT, int M, int PRO, int EPI>
+// The launch parameters that the first requests of k_gemv depend on, named in
+// one empty asm statement as scalar operands: the compiler then issues all
+// their loads back to back and waits for them once, where it would otherwise
+// load each group where it is first used and wait there (a division by S,
+// then the pointers, ...), one round trip after another.
+template <int PRO, int EPI>
+__device__ __forceinline__ void gather_params(const GemvParams& p, unsigned gx, unsigned* zero_words, int zero_n) {
+    if constexpr (PRO == PRO_CONCAT)
+        asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.N), "s"(p.K), "s"(p.G),
+                     "s"(p.S), "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.x1), "s"(p.tokens), "s"(p.table), "s"(p.vocab),
+                     "s"(p.H), "s"(p.g0), "s"(p.g1), "s"(p.eps), "s"(p.residual), "s"(zero_words), "s"(zero_n));
+    else if constexpr (EPI == EPI_ARGMAX)
+        asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.N), "s"(p.K), "s"(p.G),
+                     "s"(p.S), "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.g0), "s"(p.eps), "s"(p.balance));
+    else
+        asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.w[1].codes),
+                     "s"(p.w[1].scales), "s"(p.w[1].biases), "s"(p.w[2].codes), "s"(p.w[2].scales),
+                     "s"(p.w[2].biases), "s"(p.w[0].n), "s"(p.w[1].n), "s"(p.N), "s"(p.K), "s"(p.G), "s"(p.S),
+                     "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.g0), "s"(p.eps), "s"(p.residual));
+}
+
+// SLOT: the MoE slot launch (grid.y = slots, the matrices picked per slot).
+// Nothing that depends on a launch parameter branches before the first
+// requests (a branch waits for the parameter loads it depends on, and the
+// loads after it would wait again), so the block pays one parameter round
+// trip before it asks for its activations, weights and residuals.
+template <int FMT, int M, int PRO, int EPI, bool SLOT>
 __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const GemvParams p) {
     constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int R = gemv_rows(M, P, EPI);
     constexpr int V = R * M * P;
     constexpr int kWaves = block_waves(FMT, EPI, M);  // waves per block, at most
+    // matrices concatenated along n (q/k/v); the lm_head takes the same row
+    // arithmetic (for one matrix it picks matrix 0 at run time), which
+    // measured faster for its loop than the one-matrix form
+    constexpr bool kMulti = (PRO == PRO_RMS && EPI == EPI_STORE) || EPI == EPI_ARGMAX;
     __shared__ float red[kWaves][kWave * 2];
     __shared__ float nred[kWaves][2];
     __shared__ int claim_ctr;
 
-    if (p.zero_words && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
-    if (!resolve_view(p, v)) return;
+    if (!resolve_view<SLOT>(p, v)) return;
+    const unsigned gx = gridDim.x;
+    constexpr bool kClears = PRO == PRO_CONCAT && EPI == EPI_STORE;  // zero_words: the eh_proj only
+    unsigned* const zero_words = kClears ? p.zero_words : nullptr;
+    const int zero_n = kClears ? p.zero_n : 0;
+    if constexpr (!SLOT) gather_params<PRO, EPI>(p, gx, zero_words, zero_n);
 
     // the wave index is wave-uniform; saying so lets every row, pointer and
     // branch derived from it live in scalar registers
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int S = p.S;
-    const int Q = (blockDim.x / kWave) / S;
+    const int Q = S >= kWaves ? 1 : kWaves / S;  // the launch's S * Q waves per block
     const int s = wid % S, q = wid / S;
     const int g = s * kWave + lane;
     const int gc = g < v.G ? g : v.G - 1;
@@ -436,44 +491,66 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
     constexpr bool kDouble = (M <= 2 && P == 1);
     const bool active = g < v.G;
     const int kk = g * kGroup;
-    const bool balanced = S == 1 && p.balance;
+    const bool balanced = EPI == EPI_ARGMAX && S == 1 && p.balance;  // the persistent lm_head only
     auto claim = [&]() {
         int r = 0;
         if (lane == 0) r = atomicAdd(&claim_ctr, 1);
         return r;
     };
+    TileSeq ts;
     if (balanced) {
         if (threadIdx.x == 0) claim_ctr = 0;
-        __syncthreads();
-    }
-    TileSeq ts;
-    if (balanced)
-        ts.init(blockIdx.x, gridDim.x, NU, true, claim);
-    else if (S == 1)
-        ts.init(blockIdx.x * Q + q, gridDim.x * Q, NU, false, claim);
+        __syncthreads();  // the counter is set before any wave claims from it
+        ts.init_shared(blockIdx.x, (int)gx, NU, wid, Q, 0);
+        ts.start_claims(claim);
+    } else if (S == 1)
+        ts.init(blockIdx.x * Q + q, (int)gx * Q, NU);
     else
-        ts.init(blockIdx.x, gridDim.x, NU, false, claim);
+        ts.init(blockIdx.x, (int)gx, NU);
     auto row0 = [&](int u) { return (u * per + qo) * R; };
     TileFrags<FMT, R, P> tf, tf2;
     XFrag xf[M];
     // the activations are requested before the first tiles, which are then
     // requested unconditionally (tile 0 stands in for none), so that the
     // setup waits for the activations only: one row in contiguous 1 KB
-    // pieces, two rows as each lane's own group
+    // pieces, two rows as each lane's own group.  A token row's address
+    // waits for the token id: only the waves whose features reach into the
+    // embedding half request it and wait for it (their row still goes out
+    // before their tiles: requested after the tiles, the row, which is what
+    // these waves wait for longest, would queue behind their traffic).
     constexpr bool kRow1 = M == 1;  // S <= kRow1Chunks (checked at launch)
+    // a wave whose features reach into the embedding half of the concat
+    const bool tok_wave = kRow1 && PRO == PRO_CONCAT && kChunk * s < p.H;
     Row1Pieces rp;
     float xv2[M][32], gv2[32];
+    int tok0 = -1;
+    if (tok_wave) tok0 = p.tokens ? p.tokens[0] : -1;
     if constexpr (kRow1) {
-        row1_load<PRO>(p, v, lane, s, rp);
+        row1_load<PRO>(p, v, lane, s, tok_wave ? tok0 : -1, rp);
     } else {
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) load_x_row<PRO>(p, v, mi, kk, active, xv2[mi], gv2, mi == 0);
     }
+    const int pos = reduce_base<V, P>(lane) / P;  // = r * M + mi of this lane's result
+    const int r_l = pos / M, mi_l = pos % M;
+    const bool writer = reduce_writer<V, P>(lane);
+    // the residual a writer lane adds to its result, requested with the tile
+    auto load_res = [&](int u) {
+        float r = 0.0f;
+        if constexpr (EPI == EPI_STORE) {
+            const int row = row0(u) + r_l;
+            if (p.residual && u >= 0 && writer && s == 0 && row < v.N && mi_l < p.m)
+                r = p.residual[(int64_t)mi_l * v.N + row];
+        }
+        return r;
+    };
     int wa = ts.next(claim), wb = -1;
-    load_tile<FMT, R, P>(tf, v, row0(wa >= 0 ? wa : 0), gc);
+    load_tile<FMT, R, P, kMulti>(tf, v, row0(wa >= 0 ? wa : 0), gc);
+    float res_a = load_res(wa), res_b = 0.0f;
     if constexpr (kDouble) {
         if (wa >= 0) wb = ts.next(claim);
-        load_tile<FMT, R, P>(tf2, v, row0(wb >= 0 ? wb : 0), gc);
+        load_tile<FMT, R, P, kMulti>(tf2, v, row0(wb >= 0 ? wb : 0), gc);
+        res_b = load_res(wb);
     }
     if constexpr (kRow1) {
         __shared__ float xq1[kWaves][kRow1Floats];
@@ -484,15 +561,12 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
         for (int mi = 0; mi < M; ++mi) norm_row<FMT, PRO>(p, v, wid, lane, S, mi, kk, active, xv2[mi], gv2, xf[mi], nred);
     }
 
-    const int pos = reduce_base<V, P>(lane) / P;  // = r * M + mi of this lane's result
-    const int r_l = pos / M, mi_l = pos % M;
-    const bool writer = reduce_writer<V, P>(lane);
     float best = -INFINITY;
     int best_i = INT_MAX;
 
     // reduce one tile's partials across the lanes (and the S chunk waves) and
     // apply the epilogue
-    auto finish = [&](float (&acc)[V], int row0) {
+    auto finish = [&](float (&acc)[V], int row0, float res) {
         reduce_transpose<V, P>(acc, lane);
         float v0 = acc[0];
         float v1 = (P == 2) ? acc[P - 1] : 0.0f;
@@ -515,7 +589,7 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
             if (row < v.N && mi_l < p.m) {
                 const int64_t o = (int64_t)mi_l * v.N + row;
                 if constexpr (EPI == EPI_STORE) {
-                    if (writer) v.y[o] = p.residual ? v0 + p.residual[o] : v0;
+                    if (writer) v.y[o] = p.residual ? v0 + res : v0;
                 } else if constexpr (EPI == EPI_SWIGLU) {
                     if (writer) {
                         float z = silu(v0) * v1;
@@ -540,18 +614,24 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
             {
                 float acc[V];
                 compute_tile<FMT, M, R, P>(tf, xf, acc);
-                finish(acc, row0(wa));
+                finish(acc, row0(wa), res_a);
             }
             if (wb < 0) break;
             wa = ts.next(claim);
-            if (wa >= 0) load_tile<FMT, R, P>(tf, v, row0(wa), gc);
+            if (wa >= 0) {
+                load_tile<FMT, R, P, kMulti>(tf, v, row0(wa), gc);
+                res_a = load_res(wa);
+            }
             {
                 float acc[V];
                 compute_tile<FMT, M, R, P>(tf2, xf, acc);
-                finish(acc, row0(wb));
+                finish(acc, row0(wb), res_b);
             }
             wb = wa >= 0 ? ts.next(claim) : -1;
-            if (wb >= 0) load_tile<FMT, R, P>(tf2, v, row0(wb), gc);
+            if (wb >= 0) {
+                load_tile<FMT, R, P, kMulti>(tf2, v, row0(wb), gc);
+                res_b = load_res(wb);
+            }
         }
     } else {
         while (wa >= 0) {
@@ -559,9 +639,14 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
             compute_tile<FMT, M, R, P>(tf, xf, acc);
             // next tile's loads fly while this one is reduced and stored
             const int nx = ts.next(claim);
-            if (nx >= 0) load_tile<FMT, R, P>(tf, v, row0(nx), gc);
-            finish(acc, row0(wa));
+            float res_n = 0.0f;
+            if (nx >= 0) {
+                load_tile<FMT, R, P, kMulti>(tf, v, row0(nx), gc);
+                res_n = load_res(nx);
+            }
+            finish(acc, row0(wa), res_a);
             wa = nx;
+            res_a = res_n;
         }
     }
     if constexpr (EPI == EPI_ARGMAX) {
@@ -584,6 +669,11 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
         __shared__ unsigned long long sink[kHeadRows];
         if (wid == 0) grid_argmax<M>(p, Q, bv_s, bi_s, sink, lane);
     }
+    // the lm_head's argmax state, cleared by the layer's first launch (the
+    // eh_proj; its readers run later on the same stream)
+    if constexpr (kClears)
+        if (zero_words && blockIdx.x == 0 && blockIdx.y == 0)
+            for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_words[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -880,7 +970,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
     if (p.zero_words && blockIdx.x == 0)
         for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
-    resolve_view(p, v);
+    resolve_view<false>(p, v);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int NU = (v.N + kMmaRows - 1) / kMmaRows;
@@ -893,7 +983,8 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
     if (threadIdx.x == 0) claim_ctr = 0;
     __syncthreads();
     TileSeq ts;
-    ts.init(blockIdx.x, gridDim.x, NU, true, claim);
+    ts.init_shared(blockIdx.x, gridDim.x, NU, wid, W, 0);
+    ts.start_claims(claim);
 
     const int j = lane & 15, h = lane >> 4;
     const int mi_l = j / 3;
@@ -1087,7 +1178,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     if (p.zero_words && blockIdx.x == 0)
         for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
-    resolve_view(p, v);
+    resolve_view<false>(p, v);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int u = blockIdx.x;
@@ -1261,16 +1352,21 @@ GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int 
     return sh;
 }
 
-// The vector kernel for one or two rows.
-template <int FMT, int PRO, int EPI>
+// The vector kernel for one or two rows (SLOT: a MoE slot launch).
+template <int FMT, int PRO, int EPI, bool SLOT = false>
 static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int slots, hipStream_t st) {
     dim3 grid(sh.grid, slots), block(sh.block);
     if (m < 1 || m > 2) return hipErrorInvalidValue;
+    if (SLOT != (p.slot_expert != nullptr)) return hipErrorInvalidValue;
+    if (p.zero_words && !(PRO == PRO_CONCAT && EPI == EPI_STORE)) return hipErrorInvalidValue;  // eh_proj only
+    // matrices concatenated along n: the RMS-prologue store only (q/k/v)
+    if (p.nmat != (EPI == EPI_SWIGLU ? 2 : 1) && !(PRO == PRO_RMS && EPI == EPI_STORE && p.nmat <= 3))
+        return hipErrorInvalidValue;
     if (m == 1 && (p.K + kChunk - 1) / kChunk > kRow1Chunks) return hipErrorInvalidValue;
     if (m == 1)
-        hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI, SLOT>), grid, block, 0, st, p);
     else
-        hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI, SLOT>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
@@ -1405,8 +1501,8 @@ hipError_t launch_gemv_slots(int fmt, int epi, int m, const GemvParams& p, int m
     if (fmt != FMT_Q8 || !p.slot_expert || m < 1 || m > 2) return hipErrorInvalidValue;
     const int N = p.N > p.N_sh ? p.N : p.N_sh, K = p.K > p.K_sh ? p.K : p.K_sh;
     const GemvShape sh = gemv_shape(fmt, epi, m, N, K, max_blocks, block_waves(fmt, epi, m));
-    if (epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU>(m, p, sh, max_slots, st);
-    if (epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE>(m, p, sh, max_slots, st);
+    if (epi == EPI_SWIGLU) return launch_m<FMT_Q8, PRO_PLAIN, EPI_SWIGLU, true>(m, p, sh, max_slots, st);
+    if (epi == EPI_STORE) return launch_m<FMT_Q8, PRO_PLAIN, EPI_STORE, true>(m, p, sh, max_slots, st);
     return hipErrorInvalidValue;
 }
 

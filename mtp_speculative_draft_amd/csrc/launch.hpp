@@ -60,8 +60,9 @@ struct GemvParams {
     unsigned long long* head_keys;
     unsigned* counter;
     int* ids;
-    // Any epilogue: when set, block (0, 0) first stores zero into zero_n words
-    // at zero_words (used to clear a later launch's argmax state).
+    // The e/h concat store (eh_proj) only: when set, block (0, 0) stores zero
+    // into zero_n words at zero_words (used to clear a later launch's argmax
+    // state); other launches reject it.
     unsigned* zero_words;
     int zero_n;
     // Non-zero (S == 1 only): the waves of a block share its units and claim
