@@ -43,6 +43,7 @@ constexpr int kD = 128;           // head_dim handled here
 constexpr int kC = kAttnChunk;    // positions per block
 constexpr int kKStride = kD + 4;  // padded LDS row (floats)
 constexpr int kSliceHM = 16;      // query row-heads per partial block, at most
+constexpr int kAttnThreads = 256;  // threads of a partial block (the launch's block size)
 constexpr int kSStride = kC + 4;  // score row stride (16-byte aligned)
 
 // cos/sin of pos * inv_freq: the angle and its reduction to [-pi, pi] in
@@ -67,13 +68,22 @@ __device__ __forceinline__ bool attn_block(const AttnParams& p, int Z, int& c, i
     return true;
 }
 
+// The launch parameters the first requests of a block depend on, named in one
+// empty asm statement as scalar operands, so that their loads are issued
+// together and waited for once (loaded where first used, the block mapping's
+// fields, then the cache pointers, take one round trip after another).
+__device__ __forceinline__ void gather_attn(const AttnParams& p) {
+    asm volatile("" ::"s"(p.qkv), "s"(p.k_cache), "s"(p.v_cache), "s"(p.cache_len), "s"(p.capacity), "s"(p.m),
+                 "s"(p.nh), "s"(p.nkv), "s"(p.part), "s"(p.o), "s"(p.chunks), "s"(p.qg), "s"(p.sinks), "s"(p.c0));
+}
+
 // Local row-head hl of slice z is the group's row-head z * kSliceHM + hl
 // (= mi * GQ + local query head).
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 // VAR: the per-head norm and partial rotary steps are compiled in (the
 // plain attention runs without them).
 template <bool VAR>
-__global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads) k_attn_partial(const AttnParams p) {
     __shared__ float qs[kSliceHM][kD];
     __shared__ float ks[kC][kKStride];
     __shared__ float vs[kC][kD];
@@ -81,6 +91,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     __shared__ float spart[2][kSliceHM][kSStride];  // score halves (dims 0-63, 64-127)
     __shared__ float rc[8][kD / 2], rs[8][kD / 2];  // rotary cos/sin per new row
 
+    gather_attn(p);
     const int GQ = p.nh / p.nkv;
     const int HMall = GQ * p.m;
     const int Z = (HMall + kSliceHM - 1) / kSliceHM;
@@ -150,7 +161,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     // ... and the rotary table for positions cache_len + mi is built meanwhile
     const int rot = VAR ? p.rot : kD;
     const int rh = rot / 2;  // rotated pairs (i, i + rot/2), i < rh
-    for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
+    for (int idx = t; idx < p.m * rh; idx += kAttnThreads) {
         const int mi = idx / rh, i = idx % rh;
         const double inv_freq = exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta);
         const int pos = (VAR && p.positions) ? p.positions[4 * mi + imrope_sec(i, p.sec)] : p.cache_len + mi;
@@ -273,7 +284,7 @@ __global__ void __launch_bounds__(256) k_attn_partial(const AttnParams p) {
     //    positions <= cache_len + mi)
     float* out = p.part + (((int64_t)(c - p.c0) * p.nkv + g) * HMall + hm0) * (kD + 2);
     const float scale = 1.0f / sqrtf((float)kD);
-    for (int hp = 2 * wid; hp < HM; hp += 2 * (int)(blockDim.x / kWave)) {
+    for (int hp = 2 * wid; hp < HM; hp += 2 * (kAttnThreads / kWave)) {
         const int hm = hp + (lane >> 5), j = lane & 31;
         const int qpos = p.cache_len + (hm0 + hm) / GQ;  // the row's position
         const bool ok = hm < HM && p0 + j <= qpos && (p.window == 0 || p0 + j > qpos - p.window);
@@ -343,6 +354,7 @@ __device__ __forceinline__ void lse_merge(float& M, float& L, float& A, float m2
 
 __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const AttnParams p) {
     __shared__ float sm[kCombLanes][kCombDims], sl[kCombLanes][kCombDims], sa[kCombLanes][kCombDims];
+    gather_attn(p);
     const int g = blockIdx.x, hm = blockIdx.y;
     const int t = threadIdx.x, dl = t % kCombDims, cs = t / kCombDims;
     const int dd = blockIdx.z * kCombDims + dl;
@@ -352,15 +364,12 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     const int64_t stride = (int64_t)p.nkv * HM * (kD + 2);  // between chunks
     const float* base = p.part + ((int64_t)g * HM + hm) * (kD + 2);
 
-    // the head's sink is a logit with no value row: lane 0 starts from it
-    float M = -INFINITY, L = 0.0f, A = 0.0f;
-    if (p.sinks && cs == 0) {
-        M = p.sinks[hq];
-        L = 1.0f;
-    }
+    // the first batch of partials is requested before anything else: the
+    // head's sink and gate values go out behind it (the sink is a scalar
+    // load, and waiting for it would also wait for the parameters)
     const int nch = p.chunks - p.c0;  // partials stored from chunk c0 on
-    for (int c0 = cs; c0 < nch; c0 += kCombLanes * kCombBatch) {
-        float lv[kCombBatch], mv[kCombBatch], av[kCombBatch];
+    float lv[kCombBatch], mv[kCombBatch], av[kCombBatch];
+    auto request = [&](int c0) {
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) {
             const int c = c0 + u * kCombLanes;
@@ -370,8 +379,22 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
             av[u] = pr[dd];
             if (c >= nch) lv[u] = 0.0f;
         }
+    };
+    request(cs);
+    float gv = 0.0f;
+    if (p.qg == 2 && cs == 0) gv = p.qkv[(int64_t)mi * (2 * p.nh + 2 * p.nkv) * kD + (2 * hq + 1) * kD + dd];
+    // the head's sink is a logit with no value row: lane 0 starts from it
+    float M = -INFINITY, L = 0.0f, A = 0.0f;
+    if (p.sinks && cs == 0) {
+        M = p.sinks[hq];
+        L = 1.0f;
+    }
+    for (int c0 = cs;;) {
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) lse_merge(M, L, A, mv[u], lv[u], av[u]);
+        c0 += kCombLanes * kCombBatch;
+        if (c0 >= nch) break;
+        request(c0);
     }
     sm[cs][dl] = M;
     sl[cs][dl] = L;
@@ -380,10 +403,7 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     if (cs == 0) {
         for (int j = 1; j < kCombLanes; ++j) lse_merge(M, L, A, sm[j][dl], sl[j][dl], sa[j][dl]);
         float o = L > 0.0f ? A / L : 0.0f;
-        if (p.qg == 2) {  // sigmoid gate: the head's gate values follow its q values
-            const float gv = p.qkv[(int64_t)mi * (2 * p.nh + 2 * p.nkv) * kD + (2 * hq + 1) * kD + dd];
-            o = o / (1.0f + __expf(-gv));
-        }
+        if (p.qg == 2) o = o / (1.0f + __expf(-gv));  // sigmoid gate (the head's gate values follow its q values)
         p.o[(int64_t)mi * p.nh * kD + hq * kD + dd] = o;
     }
 }
@@ -457,7 +477,7 @@ __global__ void __launch_bounds__(64) k_append_kv(const AttnParams p, const floa
 constexpr int kWideKD = 192;  // q/k head dims at most
 constexpr int kWideVD = 128;  // V head dims at most
 
-__global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads) k_attn_partial_wide(const AttnParams p) {
     __shared__ __align__(16) float qs[kSliceHM][kWideKD];
     __shared__ float ks[kC][kWideKD + 1];  // odd row stride: the score loop reads a column per lane
     __shared__ __align__(16) float vs[kC][kWideVD];
@@ -510,7 +530,7 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
         }
     }
     // ... the rotary table of the new rows' positions meanwhile
-    for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
+    for (int idx = t; idx < p.m * rh; idx += kAttnThreads) {
         const int mi = idx / rh, i = idx % rh;
         const double inv_freq = exp2(-(2.0 * (double)i / (double)rot) * p.log2_theta);
         rotary((double)(p.cache_len + mi), inv_freq, rc[mi][i], rs[mi][i]);
@@ -539,11 +559,11 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
         if (hm < HM) *reinterpret_cast<float4*>(&qs[hm][4 * w]) = qq[u];
     }
     __syncthreads();
-    for (int idx = t; idx < p.m * KD; idx += blockDim.x) {
+    for (int idx = t; idx < p.m * KD; idx += kAttnThreads) {
         const int mi = idx / KD, d = idx % KD, pos = p.cache_len + mi;
         if (pos >= p0 && pos < p0 + kC) ks[pos - p0][d] = p.qkv[(int64_t)mi * ld + p.nh * KD + g * KD + d];
     }
-    for (int idx = t; idx < p.m * VD; idx += blockDim.x) {
+    for (int idx = t; idx < p.m * VD; idx += kAttnThreads) {
         const int mi = idx / VD, d = idx % VD, pos = p.cache_len + mi;
         if (pos >= p0 && pos < p0 + kC) {
             const float vval = p.qkv[(int64_t)mi * ld + (p.nh + p.nkv) * KD + g * VD + d];
@@ -557,24 +577,24 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
         x[i] = a * cs - b * sn;
         x[i + rh] = a * sn + b * cs;
     };
-    for (int idx = t; idx < HM * rh; idx += blockDim.x) {
+    for (int idx = t; idx < HM * rh; idx += kAttnThreads) {
         const int hm = idx / rh, i = idx % rh;
         rotate_pair(qs[hm], i, (hm0 + hm) / GQ);
     }
-    for (int idx = t; idx < p.m * rh; idx += blockDim.x) {
+    for (int idx = t; idx < p.m * rh; idx += kAttnThreads) {
         const int mi = idx / rh, i = idx % rh, pos = p.cache_len + mi;
         if (pos >= p0 && pos < p0 + kC) rotate_pair(ks[pos - p0], i, mi);
     }
     __syncthreads();
     if (z == 0)
-        for (int idx = t; idx < p.m * KD; idx += blockDim.x) {
+        for (int idx = t; idx < p.m * KD; idx += kAttnThreads) {
             const int mi = idx / KD, d = idx % KD, pos = p.cache_len + mi;
             if (pos >= p0 && pos < p0 + kC) p.k_cache[((int64_t)g * p.capacity + pos) * KD + d] = ks[pos - p0][d];
         }
 
     // scores
     const float scale = 1.0f / sqrtf((float)KD);
-    for (int idx = t; idx < HM * kC; idx += blockDim.x) {
+    for (int idx = t; idx < HM * kC; idx += kAttnThreads) {
         const int hm = idx / kC, j = idx % kC;
         float sv = 0.0f;
         for (int d = 0; d < KD; ++d) sv = fmaf(qs[hm][d], ks[j][d], sv);
@@ -584,7 +604,7 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
 
     // chunk softmax statistics (causal, window), as in k_attn_partial
     float* out = p.part + (((int64_t)(c - p.c0) * p.nkv + g) * HMall + hm0) * (VD + 2);
-    for (int hp = 2 * wid; hp < HM; hp += 2 * (int)(blockDim.x / kWave)) {
+    for (int hp = 2 * wid; hp < HM; hp += 2 * (kAttnThreads / kWave)) {
         const int hm = hp + (lane >> 5), j = lane & 31;
         const int qpos = p.cache_len + (hm0 + hm) / GQ;
         const bool ok = hm < HM && p0 + j <= qpos && (p.window == 0 || p0 + j > qpos - p.window);
@@ -605,7 +625,7 @@ __global__ void __launch_bounds__(256) k_attn_partial_wide(const AttnParams p) {
     __syncthreads();
 
     // unnormalised p*V
-    for (int idx = t; idx < HM * VD; idx += blockDim.x) {
+    for (int idx = t; idx < HM * VD; idx += kAttnThreads) {
         const int hm = idx / VD, d = idx % VD;
         float acc = 0.0f;
         for (int j = 0; j < kC; ++j) acc = fmaf(sc[hm][j], vs[j][d], acc);
@@ -660,7 +680,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int hm = (p.nh / p.nkv) * p.m;
     const int Z = (hm + kSliceHM - 1) / kSliceHM;
     const int pairs = (p.chunks - p.c0) * p.nkv;
-    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(256);
+    const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * Z)), block(kAttnThreads);
     if (p.d != kD || p.vd != kD) {
         // the combine below reads records of kD + 2 floats: V heads of kD
         if (p.d > kWideKD || p.vd != kD || p.rot > p.d || p.gq || p.qg != 1 || p.m > 8 || p.positions)

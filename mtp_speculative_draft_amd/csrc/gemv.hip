@@ -426,6 +426,14 @@ struct TileSeq {
 // their loads back to back and waits for them once, where it would otherwise
 // load each group where it is first used and wait there (a division by S,
 // then the pointers, ...), one round trip after another.
+// The lm_head's, its epilogue's pointers included (the argmax state, the
+// normed row and the logits are used by every wave at its end).
+__device__ __forceinline__ void gather_head_params(const GemvParams& p, unsigned gx) {
+    asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.N), "s"(p.K), "s"(p.G),
+                 "s"(p.S), "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.g0), "s"(p.eps), "s"(p.balance), "s"(p.normed_out),
+                 "s"(p.logits), "s"(p.head_keys), "s"(p.counter), "s"(p.ids));
+}
+
 template <int PRO, int EPI>
 __device__ __forceinline__ void gather_params(const GemvParams& p, unsigned gx, unsigned* zero_words, int zero_n) {
     if constexpr (PRO == PRO_CONCAT)
@@ -433,13 +441,26 @@ __device__ __forceinline__ void gather_params(const GemvParams& p, unsigned gx, 
                      "s"(p.S), "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.x1), "s"(p.tokens), "s"(p.table), "s"(p.vocab),
                      "s"(p.H), "s"(p.g0), "s"(p.g1), "s"(p.eps), "s"(p.residual), "s"(zero_words), "s"(zero_n));
     else if constexpr (EPI == EPI_ARGMAX)
-        asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.N), "s"(p.K), "s"(p.G),
-                     "s"(p.S), "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.g0), "s"(p.eps), "s"(p.balance));
+        gather_head_params(p, gx);
     else
         asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.w[1].codes),
                      "s"(p.w[1].scales), "s"(p.w[1].biases), "s"(p.w[2].codes), "s"(p.w[2].scales),
                      "s"(p.w[2].biases), "s"(p.w[0].n), "s"(p.w[1].n), "s"(p.N), "s"(p.K), "s"(p.G), "s"(p.S),
                      "s"(p.m), "s"(gx), "s"(p.x0), "s"(p.g0), "s"(p.eps), "s"(p.residual));
+}
+
+// The same for the split-K matrix-core kernel, by prologue and epilogue.
+template <int PRO, int EPI>
+__device__ __forceinline__ void gather_sk_params(const GemvParams& p) {
+    asm volatile("" ::"s"(p.w[0].codes), "s"(p.w[0].scales), "s"(p.w[0].biases), "s"(p.w[1].codes),
+                 "s"(p.w[1].scales), "s"(p.w[1].biases), "s"(p.N), "s"(p.K), "s"(p.G), "s"(p.m), "s"(p.x0), "s"(p.y));
+    if constexpr (PRO != PRO_PLAIN) asm volatile("" ::"s"(p.g0), "s"(p.eps));
+    if constexpr (PRO == PRO_CONCAT)
+        asm volatile("" ::"s"(p.x1), "s"(p.tokens), "s"(p.table), "s"(p.vocab), "s"(p.H), "s"(p.g1),
+                     "s"(p.zero_words), "s"(p.zero_n));
+    if constexpr (EPI == EPI_STORE)
+        asm volatile("" ::"s"(p.w[2].codes), "s"(p.w[2].scales), "s"(p.w[2].biases), "s"(p.w[0].n), "s"(p.w[1].n),
+                     "s"(p.residual));
 }
 
 // SLOT: the MoE slot launch (grid.y = slots, the matrices picked per slot).
@@ -673,7 +694,7 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
     // eh_proj; its readers run later on the same stream)
     if constexpr (kClears)
         if (zero_words && blockIdx.x == 0 && blockIdx.y == 0)
-            for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_words[i] = 0u;
+            for (int i = threadIdx.x; i < zero_n; i += kWave * S * Q) zero_words[i] = 0u;  // (the block's threads)
 }
 
 // ---------------------------------------------------------------------------
@@ -967,10 +988,9 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
     __shared__ float unsc[4];
     __shared__ int claim_ctr;
 
-    if (p.zero_words && blockIdx.x == 0)
-        for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
     resolve_view<false>(p, v);
+    gather_head_params(p, gridDim.x);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int NU = (v.N + kMmaRows - 1) / kMmaRows;
@@ -1175,10 +1195,9 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     __shared__ float part[3][4][R];
     __shared__ float unsc[4];
 
-    if (p.zero_words && blockIdx.x == 0)
-        for (int i = threadIdx.x; i < p.zero_n; i += blockDim.x) p.zero_words[i] = 0u;
     View v;
     resolve_view<false>(p, v);
+    gather_sk_params<PRO, EPI>(p);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int u = blockIdx.x;
@@ -1219,6 +1238,15 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
         sv[e] = __builtin_nontemporal_load(srow + e);
         bv[e] = __builtin_nontemporal_load(brow + e);
     }
+    // the residual that a storing lane (waves 0-3) adds, requested with the
+    // weights
+    const int mi_l = j / 3;
+    const bool writer = j < kBCols && j % 3 == 0 && mi_l < p.m;
+    float res = 0.0f;
+    if constexpr (EPI == EPI_STORE) {
+        const int orow = u * kMmaRows + 4 * h + wid;
+        if (p.residual && wid < 4 && writer && orow < v.N) res = p.residual[(int64_t)mi_l * v.N + orow];
+    }
 
     mma_setup<FMT_Q4, PRO, S, R>(p, v, mi, sub, lane, xp, bq, tx, unsc, part);
 
@@ -1258,6 +1286,11 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wid][r][lane] = fmaf(acc[r], cf, cb[r]);
     __syncthreads();
+    // the lm_head's argmax state, cleared by the layer's first launch (the
+    // eh_proj; its readers run later on the same stream)
+    if constexpr (PRO == PRO_CONCAT)
+        if (p.zero_words && blockIdx.x == 0)
+            for (int i = threadIdx.x; i < p.zero_n; i += 64 * W) p.zero_words[i] = 0u;  // (64 W threads a block)
 
     // ---- wave r < 4 sums, adds the terms and stores register r
     if (wid >= 4) return;
@@ -1266,8 +1299,6 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
 #pragma unroll
     for (int q = 0; q < W; ++q) x += red[q][r][lane];
     x = add_terms(x);
-    const int mi_l = j / 3;
-    const bool writer = j < kBCols && j % 3 == 0 && mi_l < p.m;
     if constexpr (EPI == EPI_SWIGLU) {
         float lo, hi;
         swap_halves<32>(x, x, lo, hi);
@@ -1281,7 +1312,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
         const int orow = u * kMmaRows + 4 * h + r;
         if (writer && orow < v.N) {
             const int64_t o = (int64_t)mi_l * v.N + orow;
-            v.y[o] = p.residual ? x + p.residual[o] : x;
+            v.y[o] = p.residual ? x + res : x;
         }
     }
 }
@@ -1441,6 +1472,7 @@ static GemvParams row_pass(const GemvParams& p, int pro, int r0, int pm) {
 
 static hipError_t launch_pass(int fmt, int pro, int epi, int m, const GemvParams& p, int max_blocks,
                               hipStream_t st) {
+    if (p.zero_words && !(pro == PRO_CONCAT && epi == EPI_STORE)) return hipErrorInvalidValue;  // eh_proj only
     if (mma_sk_path(fmt, epi, m, p)) {
         if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_mma_sk<PRO_PLAIN, EPI_STORE>(p, st);
         if (pro == PRO_RMS && epi == EPI_STORE) return launch_mma_sk<PRO_RMS, EPI_STORE>(p, st);
@@ -1448,7 +1480,7 @@ static hipError_t launch_pass(int fmt, int pro, int epi, int m, const GemvParams
         if (pro == PRO_PLAIN && epi == EPI_SWIGLU) return launch_mma_sk<PRO_PLAIN, EPI_SWIGLU>(p, st);
         if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_mma_sk<PRO_RMS, EPI_SWIGLU>(p, st);
     }
-    if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS)
+    if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS && !p.zero_words)
         return fmt == FMT_Q4 ? launch_mma_head<FMT_Q4, PRO_RMS>(p, st) : launch_mma_head<FMT_Q8, PRO_RMS>(p, st);
     if (m > 2) return hipErrorInvalidValue;
     const int waves = block_waves(fmt, epi, m);
