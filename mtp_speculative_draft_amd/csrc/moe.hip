@@ -38,9 +38,21 @@ constexpr int kMaxE = 1024;
 // products with the row are formed together, so the norm costs no second
 // memory round trip: logit = rsqrt(mean(x^2) + eps) * sum_k w_k x_k gamma_k.
 constexpr int kRouterU = 8;  // features per thread and round (2048 per block round)
-__global__ void __launch_bounds__(256) k_moe_router(const MoeParams p) {
+constexpr int kCombThreads = 64;  // threads of a combine block
+constexpr int kRouterThreads = 256;  // threads of a router block
+// The launch parameters the first requests of a kernel depend on, named in
+// empty asm statements as scalar operands: the compiler issues their loads
+// together and waits for them once, where it would otherwise load each group
+// where it is first used and wait there, one round trip after another.
+__device__ __forceinline__ void gather_router(const MoeParams& p) {
+    asm volatile("" ::"s"(p.x), "s"(p.gamma), "s"(p.eps), "s"(p.f), "s"(p.router), "s"(p.logits), "s"(p.E), "s"(p.H),
+                 "s"(p.m));
+}
+
+__global__ void __launch_bounds__(kRouterThreads) k_moe_router(const MoeParams p) {
     __shared__ float red[4][2][4];  // [wave][sum of squares | dot][row]
     __shared__ float inv_s[4];
+    gather_router(p);
     const int e = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
     const float* w = p.router + (int64_t)e * p.H;
     const bool norm = p.gamma != nullptr;
@@ -86,7 +98,7 @@ __global__ void __launch_bounds__(256) k_moe_router(const MoeParams p) {
     if (norm && e == 0) {  // the normalised rows for the expert GEMVs
         __syncthreads();
         for (int mi = 0; mi < p.m; ++mi)
-            for (int k = t; k < p.H; k += blockDim.x)
+            for (int k = t; k < p.H; k += kRouterThreads)
                 p.f[(int64_t)mi * p.H + k] = p.x[(int64_t)mi * p.H + k] * inv_s[mi] * p.gamma[k];
     }
 }
@@ -210,22 +222,34 @@ __global__ void __launch_bounds__(512) k_moe_topk(const MoeParams p) {
 
 // y = residual + the slots' partials added one after another in slot order;
 // the partials are requested eight at a time.
-__global__ void __launch_bounds__(64) k_moe_combine(const MoeParams p) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// The first kCombFirst slots' partials (rows of the max_slots the buffer
+// holds) are requested with the residual before the slot count arrives; the
+// sum runs in slot order either way.
+constexpr int kCombFirst = 12;
+
+__global__ void __launch_bounds__(kCombThreads) k_moe_combine(const MoeParams p) {
+    asm volatile("" ::"s"(p.m), "s"(p.H), "s"(p.n_slots), "s"(p.max_slots), "s"(p.ypart), "s"(p.residual),
+                 "s"(p.y));
+    const int64_t idx = (int64_t)blockIdx.x * kCombThreads + threadIdx.x;
     if (idx >= (int64_t)p.m * p.H) return;
-    const int ns = *p.n_slots;
     const int64_t step = (int64_t)p.m * p.H;
     const float* src = p.ypart + idx;
+    float t0[kCombFirst];
+#pragma unroll
+    for (int i = 0; i < kCombFirst; ++i) t0[i] = i < p.max_slots ? src[i * step] : 0.0f;
     float acc = p.residual ? p.residual[idx] : 0.0f;
-    int s = 0;
-    for (; s + 8 <= ns; s += 8) {
+    const int ns = *p.n_slots;
+#pragma unroll
+    for (int i = 0; i < kCombFirst; ++i)
+        if (i < ns) acc += t0[i];
+    for (int s = kCombFirst; s < ns; s += 8) {  // the rest in batches of 8 (one round trip each)
         float t[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = src[(s + i) * step];
+        for (int i = 0; i < 8; ++i) t[i] = s + i < ns ? src[(s + i) * step] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc += t[i];
+        for (int i = 0; i < 8; ++i)
+            if (s + i < ns) acc += t[i];
     }
-    for (; s < ns; ++s) acc += src[s * step];
     p.y[idx] = acc;
 }
 
@@ -448,6 +472,12 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     __shared__ int s_e;
     __shared__ float s_gate[8];
 
+    asm volatile("" ::"s"(p.act), "s"(p.act_slot), "s"(p.K), "s"(p.m), "s"(p.N), "s"(p.logits), "s"(p.E),
+                 "s"(p.top_k), "s"(p.has_shared), "s"(p.n_slots), "s"(p.slot_expert), "s"(p.codes[0]),
+                 "s"(p.codes[1]), "s"(p.scales[0]), "s"(p.scales[1]), "s"(p.sh_codes[0]), "s"(p.sh_codes[1]),
+                 "s"(p.sh_scales[0]), "s"(p.sh_scales[1]), "s"(p.ex_codes), "s"(p.ex_scales));
+    if constexpr (FMT == FMT_Q4)
+        asm volatile("" ::"s"(p.biases[0]), "s"(p.biases[1]), "s"(p.sh_biases[0]), "s"(p.sh_biases[1]));
     const int slot = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -670,7 +700,7 @@ static bool moe_slot_path(const MoeParams& p);
 // One pass of the MoE over p.m rows (at most four on the slot kernel, two on
 // the generic path).
 static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
-    hipLaunchKernelGGL(k_moe_router, dim3(p.E), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_moe_router, dim3(p.E), dim3(kRouterThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool slot_path = moe_slot_path(p);
@@ -742,7 +772,8 @@ static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
         d.n_slots = p.n_slots;
         if ((e = launch_slot(fmt, EPI_STORE, d, p.max_slots, st)) != hipSuccess) return e;
         const int64_t n = (int64_t)p.m * p.H;
-        hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
+        hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + kCombThreads - 1) / kCombThreads)), dim3(kCombThreads), 0, st,
+                           p);
         return hipGetLastError();
     }
 
@@ -793,7 +824,8 @@ static hipError_t moe_pass(const MoeParams& p, hipStream_t st) {
     if ((e = launch_gemv_slots(FMT_Q8, EPI_STORE, p.m, d, 1 << 20, p.max_slots, st)) != hipSuccess) return e;
 
     const int64_t n = (int64_t)p.m * p.H;
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + kCombThreads - 1) / kCombThreads)), dim3(kCombThreads), 0, st,
+                           p);
     return hipGetLastError();
 }
 
