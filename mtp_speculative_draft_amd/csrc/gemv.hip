@@ -1383,11 +1383,13 @@ GemvShape gemv_shape(int fmt, int epi, int m, int N, int K, int max_blocks, int 
     return sh;
 }
 
-// The vector kernel for one or two rows (SLOT: a MoE slot launch).
+// The vector kernel for one or two rows (SLOT: a MoE slot launch), or four
+// on the vec4 path.
 template <int FMT, int PRO, int EPI, bool SLOT = false>
 static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int slots, hipStream_t st) {
     dim3 grid(sh.grid, slots), block(sh.block);
-    if (m < 1 || m > 2) return hipErrorInvalidValue;
+    constexpr bool kFour = FMT == FMT_Q4 && PRO == PRO_PLAIN && EPI == EPI_STORE && !SLOT;
+    if (m < 1 || m > (kFour ? 4 : 2)) return hipErrorInvalidValue;
     if (SLOT != (p.slot_expert != nullptr)) return hipErrorInvalidValue;
     if (p.zero_words && !(PRO == PRO_CONCAT && EPI == EPI_STORE)) return hipErrorInvalidValue;  // eh_proj only
     // matrices concatenated along n: the RMS-prologue store only (q/k/v)
@@ -1396,8 +1398,10 @@ static hipError_t launch_m(int m, const GemvParams& p, const GemvShape& sh, int 
     if (m == 1 && (p.K + kChunk - 1) / kChunk > kRow1Chunks) return hipErrorInvalidValue;
     if (m == 1)
         hipLaunchKernelGGL((k_gemv<FMT, 1, PRO, EPI, SLOT>), grid, block, 0, st, p);
-    else
+    else if (m == 2)
         hipLaunchKernelGGL((k_gemv<FMT, 2, PRO, EPI, SLOT>), grid, block, 0, st, p);
+    else if constexpr (kFour)
+        hipLaunchKernelGGL((k_gemv<FMT, 4, PRO, EPI, SLOT>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
@@ -1414,6 +1418,15 @@ static bool mma_head_path(int fmt, int epi, int m, const GemvParams& p) {
 static bool mma_sk_path(int fmt, int epi, int m, const GemvParams& p) {
     return fmt == FMT_Q4 && (epi == EPI_STORE || epi == EPI_SWIGLU) && m >= 3 && m <= 4 && !p.balance &&
            !p.slot_expert && p.nmat <= 3 && (p.K == kChunk || p.K == 2 * kChunk);
+}
+
+// 4-bit plain stores of three or four rows that neither matrix-core kernel
+// takes (the dense down projection, K over two chunks): one pass of the
+// vector kernel over four rows instead of two passes of two, so the weights
+// are streamed once.
+static bool vec4_path(int fmt, int pro, int epi, int m, const GemvParams& p) {
+    return fmt == FMT_Q4 && pro == PRO_PLAIN && epi == EPI_STORE && m >= 3 && m <= 4 && p.nmat == 1 &&
+           !p.slot_expert && !mma_sk_path(fmt, epi, m, p);
 }
 
 // 16 waves per block while the units fit one block per compute unit (every
@@ -1482,7 +1495,7 @@ static hipError_t launch_pass(int fmt, int pro, int epi, int m, const GemvParams
     }
     if (mma_head_path(fmt, epi, m, p) && pro == PRO_RMS && !p.zero_words)
         return fmt == FMT_Q4 ? launch_mma_head<FMT_Q4, PRO_RMS>(p, st) : launch_mma_head<FMT_Q8, PRO_RMS>(p, st);
-    if (m > 2) return hipErrorInvalidValue;
+    if (m > 2 && !vec4_path(fmt, pro, epi, m, p)) return hipErrorInvalidValue;
     const int waves = block_waves(fmt, epi, m);
     int maxb = max_blocks;
     if (epi == EPI_ARGMAX) {
@@ -1506,8 +1519,8 @@ static hipError_t launch_pass(int fmt, int pro, int epi, int m, const GemvParams
     return hipErrorInvalidValue;
 }
 
-// Rows in passes: up to four on the matrix-core kernels, else up to two on
-// the vector kernel.
+// Rows in passes: up to four on the matrix-core kernels and the vec4 path,
+// else up to two on the vector kernel.
 hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, int max_blocks, hipStream_t st) {
     if (p.slot_expert) return hipErrorInvalidValue;  // slot launches use launch_gemv_slots
     for (int r0 = 0; r0 < m;) {
@@ -1515,7 +1528,8 @@ hipError_t launch_gemv(int fmt, int pro, int epi, int m, const GemvParams& p, in
         const int four = left < 4 ? left : 4;
         GemvParams q = row_pass(p, pro, r0, four);
         int pm = four;
-        if (!(four >= 3 && (mma_sk_path(fmt, epi, four, q) || mma_head_path(fmt, epi, four, q)))) {
+        if (!(four >= 3 && (mma_sk_path(fmt, epi, four, q) || mma_head_path(fmt, epi, four, q) ||
+                            vec4_path(fmt, pro, epi, four, q)))) {
             pm = left < 2 ? left : 2;
             q = row_pass(p, pro, r0, pm);
         }

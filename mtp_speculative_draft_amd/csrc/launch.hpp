@@ -88,8 +88,13 @@ struct GemvParams {
 // shortens them), the SwiGLU pair 8; two rows keep 8 partial sums per lane.
 constexpr int kRowsM1 = 4;    // M = 1, one matrix
 constexpr int kRowsM1P2 = 4;  // M = 1, SwiGLU pair
+// M = 4, one matrix (the vec4 path): as many rows as at two activation rows,
+// so that the grid keeps its wave count (at its register use, about two
+// waves a SIMD fit: twice the waves would run in two rounds)
+constexpr int kRowsM4 = 4;
 __host__ __device__ constexpr int gemv_rows(int M, int P, int epi) {
-    return (void)epi, (M == 1 ? (P == 1 ? kRowsM1 : kRowsM1P2) : (8 / (M * P) > 0 ? 8 / (M * P) : 1));
+    return (void)epi, (M == 1 ? (P == 1 ? kRowsM1 : kRowsM1P2)
+                              : (M == 4 && P == 1 ? kRowsM4 : (8 / (M * P) > 0 ? 8 / (M * P) : 1)));
 }
 // Row count of the kernel instantiation that serves m activation rows.
 __host__ __device__ constexpr int inst_m(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
