@@ -554,7 +554,7 @@ def main():
         "chain_ids": ref[0][1:].tolist(),
         "verify_ids": ref[1].tolist(),
         "roofline": {
-            "kernel": "mtp::k_gemv<0, 1, 1, 2> = mtp_lmhead_argmax (fused final RMSNorm + 4-bit lm_head GEMV + "
+            "kernel": "mtp::k_gemv<0, 1, 1, 2, false> = mtp_lmhead_argmax (fused final RMSNorm + 4-bit lm_head GEMV + "
                       "argmax), m=1",
             "bound": "hbm",
             "achieved": round(achieved, 1),
