@@ -1179,7 +1179,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
 // end, and wave r < 4 folds and stores register r.  Operands and arithmetic
 // are those of k_gemv_mma.
 // ---------------------------------------------------------------------------
-template <int PRO, int EPI, int S, int W>
+template <int PRO, int EPI, int S, int W, bool PERSIST>
 __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     constexpr int R = W / 4;    // waves per activation row in the setup
     constexpr int NI = 8 / R;   // 1 KB pieces of each chunk per wave in the setup
@@ -1191,7 +1191,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     __shared__ u32x4 bq[64 * S * kBGroup];    // B operands, 48 KB per chunk
     __shared__ float tx[64 * S][kMmaCols];    // group sums, 4 KB per chunk
     __shared__ float stage[W][GW * kStage];   // each wave's scales, [group][row]
-    __shared__ float red[W][4][kWave];        // the waves' partial sums
+    __shared__ float red[PERSIST ? 2 : 1][W][4][kWave];  // the waves' partial sums (two areas in the loop)
     __shared__ float part[3][4][R];
     __shared__ float unsc[4];
 
@@ -1200,120 +1200,144 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     gather_sk_params<PRO, EPI>(p);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int u = blockIdx.x;
+    constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
+    const int NU = (v.N + kOutRows - 1) / kOutRows;
+    int u = blockIdx.x;  // this block's units: blockIdx.x + gridDim.x k
 
     // ---- activations first (they come from L2 and are needed first)
     const int mi = wid & 3, sub = wid >> 2;
     XPieces<S, NI> xp;
     mma_load_x<PRO, S, NI>(p, v, mi, sub, lane, xp);
 
-    // ---- this wave's weights
+    // ---- this wave's weights of a unit
     const int j = lane & 15, h = lane >> 4;
-    constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
-    int row = u * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
-    row = row < v.N ? row : v.N - 1;
-    int64_t in1, in2;
-    int lr;
-    if constexpr (EPI == EPI_SWIGLU) {
-        in1 = j >> 3;
-        in2 = 0;
-        lr = row;
-    } else {
-        in1 = row >= v.n0;
-        in2 = row >= v.n0 + v.n1;
-        lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
-    }
     const int t0 = wid * TW, g0 = wid * GW;
-    const char* crow = static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
-    const float* srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 +
-                                                       in2 * v.ds2) + (int64_t)lr * v.G + g0 + NE * h;
-    const float* brow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 +
-                                                       in2 * v.db2) + (int64_t)lr * v.G + g0 + NE * h;
-    u32x4 cw[TW];
-#pragma unroll
-    for (int i = 0; i < TW; ++i) cw[i] = *reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i));
-    float sv[NE], bv[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        sv[e] = __builtin_nontemporal_load(srow + e);
-        bv[e] = __builtin_nontemporal_load(brow + e);
-    }
-    // the residual that a storing lane (waves 0-3) adds, requested with the
-    // weights
     const int mi_l = j / 3;
     const bool writer = j < kBCols && j % 3 == 0 && mi_l < p.m;
-    float res = 0.0f;
-    if constexpr (EPI == EPI_STORE) {
-        const int orow = u * kMmaRows + 4 * h + wid;
-        if (p.residual && wid < 4 && writer && orow < v.N) res = p.residual[(int64_t)mi_l * v.N + orow];
-    }
+    u32x4 cw[TW];
+    float sv[NE], bv[NE];
+    auto load_unit = [&](int uu) {
+        int row = uu * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
+        row = row < v.N ? row : v.N - 1;
+        int64_t in1, in2;
+        int lr;
+        if constexpr (EPI == EPI_SWIGLU) {
+            in1 = j >> 3;
+            in2 = 0;
+            lr = row;
+        } else {
+            in1 = row >= v.n0;
+            in2 = row >= v.n0 + v.n1;
+            lr = row - (int)in1 * v.n0 - (int)in2 * v.n1;
+        }
+        const char* crow =
+            static_cast<const char*>(v.c0) + in1 * v.dc1 + in2 * v.dc2 + (int64_t)lr * (v.K / 2) + 16 * h;
+        const float* srow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s0) + in1 * v.ds1 +
+                                                           in2 * v.ds2) + (int64_t)lr * v.G + g0 + NE * h;
+        const float* brow = reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.b0) + in1 * v.db1 +
+                                                           in2 * v.db2) + (int64_t)lr * v.G + g0 + NE * h;
+#pragma unroll
+        for (int i = 0; i < TW; ++i) cw[i] = *reinterpret_cast<const u32x4*>(crow + 64 * (t0 + i));
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            sv[e] = __builtin_nontemporal_load(srow + e);
+            bv[e] = __builtin_nontemporal_load(brow + e);
+        }
+    };
+    // the residual that a storing lane (waves 0-3) adds, requested with the
+    // weights
+    auto load_res = [&](int uu) {
+        float r = 0.0f;
+        if constexpr (EPI == EPI_STORE) {
+            const int orow = uu * kMmaRows + 4 * h + wid;
+            if (p.residual && wid < 4 && writer && orow < v.N) r = p.residual[(int64_t)mi_l * v.N + orow];
+        }
+        return r;
+    };
+    load_unit(u);
+    float res = load_res(u);
 
     mma_setup<FMT_Q4, PRO, S, R>(p, v, mi, sub, lane, xp, bq, tx, unsc, part);
-
-    // ---- bias sums and this wave's scale stage (lane quarter h holds the
-    // scales of groups g0 + NE h .. of its row)
-    float* st = stage[wid];
-    v4f_t cb = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        const int gl = NE * h + e;  // group within the wave's share
-        st[gl * kStage + j] = sv[e];
-        cb = __builtin_amdgcn_mfma_f32_16x16x4f32(fmaf(8.0f, sv[e], bv[e]), tx[g0 + gl][j], cb, 0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- products
-    const u32x4* bsrc = bq + h * kBCols + (j < kBCols ? j : j - 4);
-    const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < TW; ++i) {
-        const int t = t0 + i;
-        unsigned w[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
-        quarter_transpose(w[0], w[1], w[2], w[3]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const h8_t B = __builtin_bit_cast(h8_t, bsrc[(4 * t + q) * kBGroup]);
-            const v4f_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_operand(w[q]), B, zero, 0, 0, 0);
-            const float4 s4 = *reinterpret_cast<const float4*>(&st[(4 * i + q) * kStage + 4 * h]);
-            acc[0] = fmaf(s4.x, D[0], acc[0]);
-            acc[1] = fmaf(s4.y, D[1], acc[1]);
-            acc[2] = fmaf(s4.z, D[2], acc[2]);
-            acc[3] = fmaf(s4.w, D[3], acc[3]);
-        }
-    }
-    const float cf = j < kBCols ? unsc[j / 3] : 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wid][r][lane] = fmaf(acc[r], cf, cb[r]);
-    __syncthreads();
     // the lm_head's argmax state, cleared by the layer's first launch (the
     // eh_proj; its readers run later on the same stream)
     if constexpr (PRO == PRO_CONCAT)
         if (p.zero_words && blockIdx.x == 0)
             for (int i = threadIdx.x; i < p.zero_n; i += 64 * W) p.zero_words[i] = 0u;  // (64 W threads a block)
 
-    // ---- wave r < 4 sums, adds the terms and stores register r
-    if (wid >= 4) return;
-    const int r = wid;
-    float x = 0.0f;
+    float* st = stage[wid];
+    const u32x4* bsrc = bq + h * kBCols + (j < kBCols ? j : j - 4);
+    const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float cf = j < kBCols ? unsc[j / 3] : 0.0f;
+    for (int it = 0;; ++it) {
+        // ---- bias sums and this wave's scale stage (lane quarter h holds
+        // the scales of groups g0 + NE h .. of its row)
+        v4f_t cb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int q = 0; q < W; ++q) x += red[q][r][lane];
-    x = add_terms(x);
-    if constexpr (EPI == EPI_SWIGLU) {
-        float lo, hi;
-        swap_halves<32>(x, x, lo, hi);
-        const int orow = u * kOutRows + 4 * h + r;
-        if (writer && h < 2 && orow < v.N) {
-            float z = silu(x) * hi;
-            if (v.rowscale) z *= v.rowscale[mi_l];
-            v.y[(int64_t)mi_l * v.N + orow] = z;
+        for (int e = 0; e < NE; ++e) {
+            const int gl = NE * h + e;  // group within the wave's share
+            st[gl * kStage + j] = sv[e];
+            cb = __builtin_amdgcn_mfma_f32_16x16x4f32(fmaf(8.0f, sv[e], bv[e]), tx[g0 + gl][j], cb, 0, 0, 0);
         }
-    } else {
-        const int orow = u * kMmaRows + 4 * h + r;
-        if (writer && orow < v.N) {
-            const int64_t o = (int64_t)mi_l * v.N + orow;
-            v.y[o] = p.residual ? x + res : x;
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- products
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int t = t0 + i;
+            unsigned w[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+            quarter_transpose(w[0], w[1], w[2], w[3]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const h8_t B = __builtin_bit_cast(h8_t, bsrc[(4 * t + q) * kBGroup]);
+                const v4f_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_operand(w[q]), B, zero, 0, 0, 0);
+                const float4 s4 = *reinterpret_cast<const float4*>(&st[(4 * i + q) * kStage + 4 * h]);
+                acc[0] = fmaf(s4.x, D[0], acc[0]);
+                acc[1] = fmaf(s4.y, D[1], acc[1]);
+                acc[2] = fmaf(s4.z, D[2], acc[2]);
+                acc[3] = fmaf(s4.w, D[3], acc[3]);
+            }
         }
+        // the next unit's weights go out now (past the last unit, this one's
+        // again: cache hits, and the requests stay unconditional)
+        const int un = u + (int)gridDim.x;
+        float res_n = 0.0f;
+        if constexpr (PERSIST) {
+            load_unit(un < NU ? un : u);
+            res_n = load_res(un < NU ? un : u);
+        }
+        float (*rb)[4][kWave] = red[PERSIST ? (it & 1) : 0];  // two areas: one barrier a unit
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rb[wid][r][lane] = fmaf(acc[r], cf, cb[r]);
+        __syncthreads();
+
+        // ---- wave r < 4 sums, adds the terms and stores register r
+        if (wid < 4) {
+            const int r = wid;
+            float x = 0.0f;
+#pragma unroll
+            for (int q = 0; q < W; ++q) x += rb[q][r][lane];
+            x = add_terms(x);
+            if constexpr (EPI == EPI_SWIGLU) {
+                float lo, hi;
+                swap_halves<32>(x, x, lo, hi);
+                const int orow = u * kOutRows + 4 * h + r;
+                if (writer && h < 2 && orow < v.N) {
+                    float z = silu(x) * hi;
+                    if (v.rowscale) z *= v.rowscale[mi_l];
+                    v.y[(int64_t)mi_l * v.N + orow] = z;
+                }
+            } else {
+                const int orow = u * kMmaRows + 4 * h + r;
+                if (writer && orow < v.N) {
+                    const int64_t o = (int64_t)mi_l * v.N + orow;
+                    v.y[o] = p.residual ? x + res : x;
+                }
+            }
+        }
+        if (!PERSIST || un >= NU) break;
+        u = un;
+        res = res_n;
     }
 }
 
@@ -1434,20 +1458,28 @@ static bool vec4_path(int fmt, int pro, int epi, int m, const GemvParams& p) {
 template <int PRO, int EPI, int W>
 static void launch_mma_sk_w(const GemvParams& p, dim3 grid, hipStream_t st) {
     const dim3 block(W * kWave);
+    constexpr bool kPersist = W == 8;  // the 8-wave launch runs over more units than blocks
     if (p.K == kChunk)
-        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W, kPersist>), grid, block, 0, st, p);
     else
-        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W, kPersist>), grid, block, 0, st, p);
 }
+
+// Blocks a compute unit of the split-K kernel when there are more units than
+// compute units: one 8-wave block, which builds the activation operands once
+// and then loops over its units (two blocks a unit, each over half as many
+// units, measured slower).
+constexpr int kSkBlocksPerCu = 1;
 
 template <int PRO, int EPI>
 static hipError_t launch_mma_sk(const GemvParams& p, hipStream_t st) {
     const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
     const int units = (p.N + rows - 1) / rows;
-    if (units <= device_cu_count())
+    const int cu = device_cu_count();
+    if (units <= cu)
         launch_mma_sk_w<PRO, EPI, 16>(p, dim3(units), st);
-    else
-        launch_mma_sk_w<PRO, EPI, 8>(p, dim3(units), st);
+    else  // persistent: kSkBlocksPerCu blocks a compute unit, each over several units
+        launch_mma_sk_w<PRO, EPI, 8>(p, dim3(units < kSkBlocksPerCu * cu ? units : kSkBlocksPerCu * cu), st);
     return hipGetLastError();
 }
 
