@@ -1179,7 +1179,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
 // end, and wave r < 4 folds and stores register r.  Operands and arithmetic
 // are those of k_gemv_mma.
 // ---------------------------------------------------------------------------
-template <int PRO, int EPI, int S, int W, bool PERSIST>
+template <int PRO, int EPI, int S, int W, bool PERSIST, bool HALF = false>
 __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     constexpr int R = W / 4;    // waves per activation row in the setup
     constexpr int NI = 8 / R;   // 1 KB pieces of each chunk per wave in the setup
@@ -1200,7 +1200,10 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     gather_sk_params<PRO, EPI>(p);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    constexpr int kOutRows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
+    // HALF (store): 8-row units, lanes j and j + 8 on one row (twice the
+    // blocks for the matrices that give fewer units than compute units)
+    constexpr bool kHalfRows = EPI == EPI_SWIGLU || HALF;
+    constexpr int kOutRows = kHalfRows ? kMmaRows / 2 : kMmaRows;
     const int NU = (v.N + kOutRows - 1) / kOutRows;
     int u = blockIdx.x;  // this block's units: blockIdx.x + gridDim.x k
 
@@ -1217,7 +1220,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     u32x4 cw[TW];
     float sv[NE], bv[NE];
     auto load_unit = [&](int uu) {
-        int row = uu * kOutRows + (EPI == EPI_SWIGLU ? (j & 7) : j);
+        int row = uu * kOutRows + (kHalfRows ? (j & 7) : j);
         row = row < v.N ? row : v.N - 1;
         int64_t in1, in2;
         int lr;
@@ -1249,8 +1252,9 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     auto load_res = [&](int uu) {
         float r = 0.0f;
         if constexpr (EPI == EPI_STORE) {
-            const int orow = uu * kMmaRows + 4 * h + wid;
-            if (p.residual && wid < 4 && writer && orow < v.N) r = p.residual[(int64_t)mi_l * v.N + orow];
+            const int orow = uu * kOutRows + 4 * h + wid;
+            if (p.residual && wid < 4 && writer && (!HALF || h < 2) && orow < v.N)
+                r = p.residual[(int64_t)mi_l * v.N + orow];
         }
         return r;
     };
@@ -1328,8 +1332,8 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
                     v.y[(int64_t)mi_l * v.N + orow] = z;
                 }
             } else {
-                const int orow = u * kMmaRows + 4 * h + r;
-                if (writer && orow < v.N) {
+                const int orow = u * kOutRows + 4 * h + r;
+                if (writer && (!HALF || h < 2) && orow < v.N) {
                     const int64_t o = (int64_t)mi_l * v.N + orow;
                     v.y[o] = p.residual ? x + res : x;
                 }
@@ -1455,14 +1459,14 @@ static bool vec4_path(int fmt, int pro, int epi, int m, const GemvParams& p) {
 
 // 16 waves per block while the units fit one block per compute unit (every
 // SIMD then holds four of a block's waves), else 8.
-template <int PRO, int EPI, int W>
+template <int PRO, int EPI, int W, bool HALF = false>
 static void launch_mma_sk_w(const GemvParams& p, dim3 grid, hipStream_t st) {
     const dim3 block(W * kWave);
     constexpr bool kPersist = W == 8;  // the 8-wave launch runs over more units than blocks
     if (p.K == kChunk)
-        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W, kPersist>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 1, W, kPersist, HALF>), grid, block, 0, st, p);
     else
-        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W, kPersist>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_gemv_mma_sk<PRO, EPI, 2, W, kPersist, HALF>), grid, block, 0, st, p);
 }
 
 // Blocks a compute unit of the split-K kernel when there are more units than
@@ -1476,7 +1480,9 @@ static hipError_t launch_mma_sk(const GemvParams& p, hipStream_t st) {
     const int rows = EPI == EPI_SWIGLU ? kMmaRows / 2 : kMmaRows;
     const int units = (p.N + rows - 1) / rows;
     const int cu = device_cu_count();
-    if (units <= cu)
+    if (EPI == EPI_STORE && 2 * units <= cu)  // 8-row units: twice the blocks, still one a compute unit
+        launch_mma_sk_w<PRO, EPI, 16, true>(p, dim3((p.N + kMmaRows / 2 - 1) / (kMmaRows / 2)), st);
+    else if (units <= cu)
         launch_mma_sk_w<PRO, EPI, 16>(p, dim3(units), st);
     else  // persistent: kSkBlocksPerCu blocks a compute unit, each over several units
         launch_mma_sk_w<PRO, EPI, 8>(p, dim3(units < kSkBlocksPerCu * cu ? units : kSkBlocksPerCu * cu), st);
