@@ -1170,14 +1170,17 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
 
 // ---------------------------------------------------------------------------
 // Matrix-core GEMV with the K range split over a block's W waves, for the
-// 4-bit projections that are not persistent: one block per unit (16 weight
-// rows, or 8 output rows of the SwiGLU pair), K = 2048 S with S <= 2.  A
-// block per unit puts many more compute units to work than a wave per unit,
-// and each wave's share (16 S / W loads of four groups) is short; with W = 16
-// every SIMD holds four waves, which hides the latency of both the
-// activation setup and the loop.  The waves' partial sums meet in LDS at the
-// end, and wave r < 4 folds and stores register r.  Operands and arithmetic
-// are those of k_gemv_mma.
+// 4-bit projections other than the lm_head: a block takes a unit (16 weight
+// rows; 8 output rows of the SwiGLU pair, or 8 rows of a store with few
+// units: HALF) over K = 2048 S with S <= 2.  A block per unit puts many more
+// compute units to work than a wave per unit, and each wave's share (16 S / W
+// loads of four groups) is short; with W = 16 every SIMD holds four waves,
+// which hides the latency of both the activation setup and the loop.  The
+// waves' partial sums meet in LDS, and wave r < 4 folds and stores register
+// r.  PERSIST (more units than compute units): one block per compute unit
+// builds the activation operands once and loops over its units, requesting
+// the next unit's weights before each reduction.  Operands and arithmetic are
+// those of k_gemv_mma.
 // ---------------------------------------------------------------------------
 template <int PRO, int EPI, int S, int W, bool PERSIST, bool HALF = false>
 __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
