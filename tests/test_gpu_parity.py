@@ -779,7 +779,10 @@ def test_attn_decode_rejects_overflow_without_writing():
                                                 # matrix-core gate/up: units of 8 output rows
                                                 (2048, 1056, 3, False, True), (2048, 544, 4, True, False),
                                                 # matrix-core gate/up over 2 and 3 chunks
-                                                (4096, 544, 3, True, True), (6144, 96, 4, True, False)])
+                                                (4096, 544, 3, True, True), (6144, 96, 4, True, False),
+                                                # more 8-row units than compute units (260): persistent
+                                                # blocks, four of them taking a second unit; 1 and 2 chunks
+                                                (2048, 2080, 3, True, True), (4096, 2080, 4, False, True)])
 def test_ffn_dense(H, inter, m, norm, res):
     _say(f"ffn_dense H={H} I={inter} m={m}")
     g = synth.rng(111, H, inter, m)
