@@ -84,6 +84,8 @@ def parse():
                     help="only a plain device copy of 256 MiB, the reference for scaling byte counters")
     ap.add_argument("--moe-only", action="store_true", help="only the 8-bit MoE FFN at m=4 (counter runs)")
     ap.add_argument("--attn-only", action="store_true", help="only the attention block at m=1 (counter runs)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the dense draft step, eager, --steps times (per-kernel counter runs)")
     return ap.parse_args()
 
 
@@ -208,6 +210,36 @@ def head_only(torch, mtp, synth, dev, reps, m, q8):
     torch.cuda.synchronize()
     print(json.dumps({"head_launches": reps, "rows": m, "bits": 8 if q8 else 4, "bytes_per_launch": nbytes}),
           flush=True)
+
+
+def step_only(torch, mtp, synth, dev, reps, copies):
+    """The dense draft step alone (K=3 chain at m=1 + verify at m=4, cache
+    4096) over rotated layer/cache copies, eager launches, for per-kernel
+    counter runs.  Prints the algorithmic bytes of each kernel role: the
+    weights it streams once, the K/V rows read, and the partials."""
+    S = synth.config4_step()
+    L = S.layer
+    R = max(1, copies)
+    layers = [mtp.DeviceLayer(L, dev) for _ in range(R)]
+    caches = [(torch.from_numpy(S.k_cache).to(dev), torch.from_numpy(S.v_cache).to(dev)) for _ in range(R)]
+    chain, verify, _, _ = step_runner(torch, mtp, S, layers, caches, dev)
+    for i in range(reps):
+        chain(i)
+        verify(i)
+    torch.cuda.synchronize()
+    q = layers[0].q4
+    H, L0 = L.hidden, S.cache_len
+    kvrow = L.n_kv_heads * L.head_dim * 4 * 2
+    chunks = lambda m: (L0 + m + 31) // 32  # noqa: E731  (cache positions per partial block: 32)
+    part = lambda m: chunks(m) * L.n_kv_heads * (L.n_heads // L.n_kv_heads) * m * (L.head_dim + 2) * 4  # noqa: E731
+    roles = {}
+    for m in (1, 4):
+        roles[f"m{m}"] = {
+            "eh_proj": q["eh_proj"].nbytes, "qkv": q["wq"].nbytes + q["wk"].nbytes + q["wv"].nbytes,
+            "attn_partial_read": kvrow * L0, "attn_partial_write": part(m) + kvrow * m,
+            "attn_combine_read": part(m), "wo": q["wo"].nbytes, "gate_up": q["gate"].nbytes + q["up"].nbytes,
+            "down": q["down"].nbytes, "lm_head": q["lm_head"].nbytes}
+    print(json.dumps({"step_calls": reps, "algorithmic_bytes": roles}), flush=True)
 
 
 def moe_only(torch, mtp, synth, dev, reps):
@@ -467,6 +499,8 @@ def main():
         return moe_only(torch, mtp, synth, dev, args.steps)
     if args.attn_only:
         return attn_only(torch, mtp, synth, dev, args.steps)
+    if args.step_only:
+        return step_only(torch, mtp, synth, dev, args.steps, args.copies)
     if args.ops_only:
         print(json.dumps({"ops": op_timings(torch, mtp, synth, dev, args.steps, args.warmup)}), flush=True)
         return
