@@ -761,6 +761,13 @@ __device__ __forceinline__ unsigned half_bits(float x) {
     return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)x);
 }
 
+// Two f32 values to an f16 pair (round to nearest even), and its bits.
+typedef float f2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2_t pack_h2(float a, float b) {
+    return __builtin_convertvector((f2_t){a, b}, h2_t);
+}
+__device__ __forceinline__ unsigned h2_bits(h2_t h) { return __builtin_bit_cast(unsigned, h); }
+
 // Activation setup of the matrix-core kernels, shared by a block's waves:
 // wave w takes activation row w % 4 and, of each of the S chunks, the 1 KB
 // pieces NI (w / 4) .. NI (w / 4) + NI - 1 (lane l holds features
@@ -891,46 +898,55 @@ __device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, in
             gs += dpp_partner<4>(gs);
             if ((lane & 7) < 3) tx[gg][3 * mi + (lane & 7)] = (lane & 7) == 0 ? gs : 0.0f;
             u32x4* grp = bq + gg * kBGroup;
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                unsigned hb[4];
+            if constexpr (FMT == FMT_Q4) {
+                // Lanes 2 k and 2 k + 1 hold features 0-3 and 4-7 of word k,
+                // and operand word i of its k-slot pairs features (i, i + 4)
+                // (q4_halves).  The pair swaps two values, so that lane 2 k + s
+                // holds features 2 s, 2 s + 1, 2 s + 4, 2 s + 5 and forms the
+                // words 2 s and 2 s + 1 alone; features 2 s + 1 and 2 s + 5 sit
+                // on the 16c halves.
+                const float r0 = dpp_partner<1>(odd ? xv[0] : xv[2]), r1 = dpp_partner<1>(odd ? xv[1] : xv[3]);
+                const float pv[4] = {odd ? r0 : xv[0], odd ? r1 : xv[1], odd ? xv[2] : r0, odd ? xv[3] : r1};
+                float hi[4], rm[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    // term t of v = x 2^(15-e) (4-bit: features on 16c halves
-                    // carry 1/16): hi is v on the grid 16 (1 for the 1/16
-                    // features), so every hi product lies on one grid and the
-                    // MFMA sums them exactly; mid and lo are the f16 remainder
-                    const bool sixteenth = FMT == FMT_Q4 && (q & 1);
-                    const float v = xv[q] * sc * (sixteenth ? 0.0625f : 1.0f);
+                    // term split of v = x 2^(15-e): hi is v on the grid 16 (1 for
+                    // the 1/16 features), so every hi product lies on one grid
+                    // and the MFMA sums them exactly; mid is the remainder rm
+                    // rounded to f16 and lo the rest, in f16
+                    const bool sixteenth = q & 1;
+                    const float vq = pv[q] * sc * (sixteenth ? 0.0625f : 1.0f);
                     const float step = sixteenth ? 1.0f : 16.0f;
-                    const float hi = rintf(v * (1.0f / step)) * step;  // |hi / step| <= 2^11: exact in f16
-                    const float r1 = v - hi;
-                    const _Float16 h1 = (_Float16)r1;
-                    const float r2 = r1 - (float)h1;
-                    hb[q] = half_bits(t == 0 ? hi : (t == 1 ? (float)h1 : r2));
+                    hi[q] = rintf(vq * (1.0f / step)) * step;  // |hi / step| <= 2^11: exact in f16
+                    rm[q] = vq - hi[q];
                 }
-                const int colt = 3 * mi + t;
-                if constexpr (FMT == FMT_Q4) {
-                    // word (lane % 8) / 2 of the group, features 4 (lane % 2) ..;
-                    // halves pair i of the word is (feature i, feature 4 + i): the
-                    // even lane builds pairs 0, 1 and the odd lane pairs 2, 3
-                    const unsigned send = odd ? (hb[0] | (hb[1] << 16)) : (hb[2] | (hb[3] << 16));
-                    const unsigned got = (unsigned)dpp_partner<1>((int)send);
-                    unsigned r0, r1;
-                    if (odd) {
-                        r0 = (got & 0xFFFFu) | (hb[2] << 16);
-                        r1 = (got >> 16) | (hb[3] << 16);
-                    } else {
-                        r0 = hb[0] | (got << 16);
-                        r1 = hb[1] | (got & 0xFFFF0000u);
+                const h2_t m0 = pack_h2(rm[0], rm[2]), m1 = pack_h2(rm[1], rm[3]);
+                const h2_t l0 = pack_h2(rm[0] - (float)m0.x, rm[2] - (float)m0.y);
+                const h2_t l1 = pack_h2(rm[1] - (float)m1.x, rm[3] - (float)m1.y);
+                // term columns 3 mi .. 3 mi + 2 of k-slot (lane % 8) / 2: words 2 s, 2 s + 1
+                unsigned* dst = reinterpret_cast<unsigned*>(grp + ((lane & 7) >> 1) * kBCols + 3 * mi) + 2 * odd;
+                *reinterpret_cast<uint2*>(dst) = make_uint2(h2_bits(pack_h2(hi[0], hi[2])), h2_bits(pack_h2(hi[1], hi[3])));
+                *reinterpret_cast<uint2*>(dst + 4) = make_uint2(h2_bits(m0), h2_bits(m1));
+                *reinterpret_cast<uint2*>(dst + 8) = make_uint2(h2_bits(l0), h2_bits(l1));
+            } else {
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    unsigned hb[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // term t of v = x 2^(15-e), split as for the 4-bit
+                        // operands with the grid 16 for every feature
+                        const float vq = xv[q] * sc;
+                        const float hi = rintf(vq * (1.0f / 16.0f)) * 16.0f;
+                        const float r1 = vq - hi;
+                        const _Float16 h1 = (_Float16)r1;
+                        const float r2 = r1 - (float)h1;
+                        hb[q] = half_bits(t == 0 ? hi : (t == 1 ? (float)h1 : r2));
                     }
-                    unsigned* dst = reinterpret_cast<unsigned*>(grp + ((lane & 7) >> 1) * kBCols + colt) + 2 * odd;
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(r0, r1);
-                } else {
                     // 8-bit word lane % 8 of the group sits in k-slot rho(word / 2),
                     // halves 4 (word % 2) ..: pairs (feature 0, 2) and (1, 3)
                     const int wd = lane & 7, hq = ((wd >> 1) & 1) * 2 + (wd >> 2);
-                    unsigned* dst = reinterpret_cast<unsigned*>(grp + hq * kBCols + colt) + 2 * (wd & 1);
+                    unsigned* dst = reinterpret_cast<unsigned*>(grp + hq * kBCols + 3 * mi + t) + 2 * (wd & 1);
                     *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0] | (hb[2] << 16), hb[1] | (hb[3] << 16));
                 }
             }
