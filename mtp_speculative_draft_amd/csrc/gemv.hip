@@ -283,6 +283,56 @@ __device__ __forceinline__ void row1_finish(const GemvParams& p, const View& v, 
     make_frag<FMT>(xv, xf);
 }
 
+// Four plain rows (the four-row pass): each wave loads its chunk of every
+// row in 1 KB pieces as row1_load does (a load instruction covers eight whole
+// lines, where each lane's own group would touch 64), rows past m reading row
+// 0 (zeroed later), and passes them one row at a time through its LDS region
+// to the lanes that own the groups.
+__device__ __forceinline__ void rows4_load(const View& v, int lane, int s, int m, Row1Pieces (&rp)[4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const float* src = v.x0 + (int64_t)(mi < m ? mi : 0) * v.K;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int f = kChunk * s + 256 * i + 4 * lane;
+            f = f < v.K ? f : 0;  // past the end: any valid address, zeroed in rows4_finish
+            rp[mi].x[i] = *reinterpret_cast<const float4*>(src + f);
+        }
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void rows4_finish(const View& v, int lane, int s, int m, Row1Pieces (&rp)[4], float* xq,
+                                             XFrag (&xf)[4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        // piece i, lane l -> group 8 i + l / 8, features 4 (l % 8) ..
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool live = mi < m && kChunk * s + 256 * i + 4 * lane < v.K;
+            *reinterpret_cast<float4*>(xq + (8 * i + (lane >> 3)) * kGroupStride + 4 * (lane & 7)) =
+                live ? rp[mi].x[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float xv[32];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float4 t = *reinterpret_cast<const float4*>(xq + lane * kGroupStride + 4 * k);
+            xv[4 * k] = t.x;
+            xv[4 * k + 1] = t.y;
+            xv[4 * k + 2] = t.z;
+            xv[4 * k + 3] = t.w;
+        }
+        // every lane has read the row before the next one overwrites the region
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        make_frag<FMT>(xv, xf[mi]);
+    }
+}
+
 // Weight fragments of one tile (R rows x P matrices) for this lane's group.
 template <int FMT, int R, int P>
 struct TileFrags {
@@ -540,14 +590,18 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
     // before their tiles: requested after the tiles, the row, which is what
     // these waves wait for longest, would queue behind their traffic).
     constexpr bool kRow1 = M == 1;  // S <= kRow1Chunks (checked at launch)
+    constexpr bool kRows4 = M == 4 && PRO == PRO_PLAIN;  // the four-row pass
     // a wave whose features reach into the embedding half of the concat
     const bool tok_wave = kRow1 && PRO == PRO_CONCAT && kChunk * s < p.H;
     Row1Pieces rp;
+    Row1Pieces rp4[kRows4 ? 4 : 1];
     float xv2[M][32], gv2[32];
     int tok0 = -1;
     if (tok_wave) tok0 = p.tokens ? p.tokens[0] : -1;
     if constexpr (kRow1) {
         row1_load<PRO>(p, v, lane, s, tok_wave ? tok0 : -1, rp);
+    } else if constexpr (kRows4) {
+        rows4_load(v, lane, s, p.m, rp4);
     } else {
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) load_x_row<PRO>(p, v, mi, kk, active, xv2[mi], gv2, mi == 0);
@@ -577,6 +631,9 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
         __shared__ float xq1[kWaves][kRow1Floats];
         __shared__ float part1[kRow1Chunks][2];
         row1_finish<FMT, PRO>(p, v, lane, S, s, q, rp, xq1[wid], part1, xf[0]);
+    } else if constexpr (kRows4) {
+        __shared__ float xq4[kWaves][kRow1Floats];
+        rows4_finish<FMT>(v, lane, s, p.m, rp4, xq4[wid], xf);
     } else {
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) norm_row<FMT, PRO>(p, v, wid, lane, S, mi, kk, active, xv2[mi], gv2, xf[mi], nred);
