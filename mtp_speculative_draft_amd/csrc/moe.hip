@@ -409,17 +409,6 @@ __device__ __forceinline__ void route_slot(const SlotGemv& p, int slot, int lane
 template <int M>
 __host__ __device__ constexpr int slot_batch() { return M >= 4 ? 1 : 2; }
 
-// One (row, group) activation fragment of the block's slot: the 32 values
-// and their sum, written to LDS.
-__device__ __forceinline__ void store_frag(unsigned* f, const float (&xv)[32]) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += xv[i];
-    float4* f4 = reinterpret_cast<float4*>(f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) f4[k] = make_float4(xv[4 * k], xv[4 * k + 1], xv[4 * k + 2], xv[4 * k + 3]);
-    f4[8] = make_float4(sum, 0.0f, 0.0f, 0.0f);
-}
 
 // The lane's fragment of a row of format FMT from a stored (row, group)
 // fragment (the order of make_frag<FMT>).
@@ -484,17 +473,21 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     const bool route = EPI == EPI_SWIGLU && p.logits != nullptr;
     const int G = LG;  // groups per row
 
-    // the first activation pair of this thread is requested before the
-    // routing / slot lookup, whose memory latency it then shares
+    // the activations are requested before the routing / slot lookup, whose
+    // memory latency they then share: the m rows (K = 32 G features each,
+    // contiguous) in 16-byte pieces, thread t taking pieces t, t + 64 W, ...,
+    // so that a load instruction reads one contiguous kilobyte (eight lines);
+    // the eight pieces of a group sit in eight consecutive lanes
     const float* act = p.act + (int64_t)slot * p.act_slot;
-    const int q0 = threadIdx.x;
-    const bool has_q0 = q0 < M * G && q0 / G < p.m;
-    float xv0[32];
-    if (has_q0) {
-        load32(xv0, act + (int64_t)(q0 / G) * p.K + (q0 % G) * kGroup);
-    } else {
+    constexpr int kRowF4 = LG * kGroup / 4;  // 16-byte pieces per row (K = 32 LG)
+    constexpr int kActF4 = (M * kRowF4 + W * kWave - 1) / (W * kWave);
+    float4 xa[kActF4];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) xv0[i] = 0.0f;
+    for (int i = 0; i < kActF4; ++i) {
+        const int f4 = threadIdx.x + W * kWave * i;
+        const bool ok = f4 < M * kRowF4 && f4 / kRowF4 < p.m;
+        const float4 x = reinterpret_cast<const float4*>(act)[ok ? f4 : 0];  // rows past m: any valid address
+        xa[i] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 
     int e;
@@ -559,18 +552,22 @@ __global__ void __launch_bounds__(W * 64) k_moe_slot(const SlotGemv p) {
     if (j_begin < j_end) load_batch(wa, j_begin);
     if (j_begin + UB < j_end) load_batch(wb, j_begin + UB);
 
-    // activation setup: (row, group) pairs over the block's threads
-    if (q0 < M * G) store_frag(frag + ((q0 / G) * LG + q0 % G) * kFragWords, xv0);
-    for (int q = q0 + W * kWave; q < M * G; q += W * kWave) {
-        const int mi = q / G, gg = q % G;
-        float xv[32];
-        if (mi < p.m) {
-            load32(xv, act + (int64_t)mi * p.K + gg * kGroup);
-        } else {
+    // activation setup: each (row, group) fragment is the group's 32 values
+    // and their sum, which its eight lanes form together
 #pragma unroll
-            for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
+    for (int i = 0; i < kActF4; ++i) {
+        const int f4 = threadIdx.x + W * kWave * i;
+        const float4 x = xa[i];
+        float sum = (x.x + x.y) + (x.z + x.w);
+        sum += dpp_partner<1>(sum);
+        sum += dpp_partner<2>(sum);
+        sum += dpp_partner<4>(sum);
+        if (f4 < M * kRowF4) {
+            const int mi = f4 / kRowF4, k4 = f4 % kRowF4;
+            float4* fr = reinterpret_cast<float4*>(frag + (mi * LG + k4 / 8) * kFragWords);
+            fr[k4 % 8] = x;
+            if (k4 % 8 == 0) fr[8] = make_float4(sum, 0.0f, 0.0f, 0.0f);
         }
-        store_frag(frag + (mi * LG + gg) * kFragWords, xv);
     }
     __syncthreads();
     if (j_begin >= j_end) return;
