@@ -84,7 +84,7 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 // plain attention runs without them).
 template <bool VAR>
 __global__ void __launch_bounds__(kAttnThreads) k_attn_partial(const AttnParams p) {
-    __shared__ float qs[kSliceHM][kD];
+    __shared__ float qs[kSliceHM][kKStride];  // padded rows: the score reads of 16 rows spread over the banks
     __shared__ float ks[kC][kKStride];
     __shared__ float vs[kC][kD];
     __shared__ float sc[kSliceHM][kSStride];
