@@ -785,7 +785,9 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int kMmaRows = 16;
 constexpr int kMmaCols = 16;
 constexpr int kBCols = 12;           // term columns: 4 rows x 3 terms
-constexpr int kBGroup = 4 * kBCols;  // B operands (u32x4) per group: 4 k-slots x 12 columns
+// B operands (u32x4) per group: 4 k-slots x 12 columns, and one entry of
+// padding, so that the groups a wave writes at once start on different banks
+constexpr int kBGroup = 4 * kBCols + 1;
 constexpr int kStage = 20;           // floats per group in a wave's scale stage (16 rows, 16-byte aligned)
 
 __device__ __forceinline__ void perm32_swap(unsigned& a, unsigned& b) {
@@ -1054,7 +1056,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
     static_assert(W >= 4, "waves 0-3 build the B operands");
     constexpr int R = 1;  // waves per activation row in the setup
     constexpr int NT = FMT == FMT_Q4 ? 16 : 32;  // 16-byte code loads per lane and unit
-    __shared__ u32x4 bq[64 * kBGroup];               // 48 KB: B operands
+    __shared__ u32x4 bq[64 * kBGroup];               // 49 KB: B operands
     __shared__ float tx[64][kMmaCols];               // 4 KB: group sums in column 3 mi (4-bit bias)
     __shared__ float stage[W][64 * kStage];  // 5 KB per wave: its scales, [group][row]
     __shared__ float part[3][4][R];
@@ -1264,7 +1266,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     constexpr int GW = 4 * TW;  // groups per wave
     constexpr int NE = GW / 4;  // groups per lane quarter
     static_assert(T % W == 0 && 8 % R == 0, "wave split");
-    __shared__ u32x4 bq[64 * S * kBGroup];    // B operands, 48 KB per chunk
+    __shared__ u32x4 bq[64 * S * kBGroup];    // B operands, 49 KB per chunk
     __shared__ float tx[64 * S][kMmaCols];    // group sums, 4 KB per chunk
     __shared__ float stage[W][GW * kStage];   // each wave's scales, [group][row]
     __shared__ float red[PERSIST ? 2 : 1][W][4][kWave];  // the waves' partial sums (two areas in the loop)
