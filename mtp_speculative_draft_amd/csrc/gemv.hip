@@ -558,8 +558,11 @@ __global__ void __launch_bounds__(block_waves(FMT, EPI, M) * 64) k_gemv(const Ge
     const int NU = (v.N + per * R - 1) / (per * R);
 
     // the first tiles' weights are requested before the activation setup so
-    // their latency overlaps it (two tiles where the loop double-buffers)
-    constexpr bool kDouble = (M <= 2 && P == 1);
+    // their latency overlaps it (two tiles where the loop double-buffers: the
+    // persistent lm_head, whose waves take many units; the other launches
+    // give each wave one unit, where a second tile would only be requests
+    // that hold up the others)
+    constexpr bool kDouble = EPI == EPI_ARGMAX && M <= 2 && P == 1;
     const bool active = g < v.G;
     const int kk = g * kGroup;
     const bool balanced = EPI == EPI_ARGMAX && S == 1 && p.balance;  // the persistent lm_head only
