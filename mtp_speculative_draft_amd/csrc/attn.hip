@@ -368,16 +368,21 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     // head's sink and gate values go out behind it (the sink is a scalar
     // load, and waiting for it would also wait for the parameters)
     const int nch = p.chunks - p.c0;  // partials stored from chunk c0 on
-    float lv[kCombBatch], mv[kCombBatch], av[kCombBatch];
+    // The 64 lanes of a wave take one dim each of the same chunks, so a
+    // chunk's (max, exp-sum) pair is the same for all of them: lane u of the
+    // wave requests the pair of the batch's chunk u (one load for the batch
+    // instead of two per chunk, each a request of its own), and the merge
+    // reads the pairs back with readlane.
+    static_assert(kCombDims == kWave && kCombBatch <= kWave, "one wave per chunk lane");
+    float2 ml;
+    float av[kCombBatch];
     auto request = [&](int c0) {
+        const int cl = c0 + (dl < kCombBatch ? dl : 0) * kCombLanes;
+        ml = *reinterpret_cast<const float2*>(base + (int64_t)(cl < nch ? cl : 0) * stride + kD);
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) {
             const int c = c0 + u * kCombLanes;
-            const float* pr = base + (int64_t)(c < nch ? c : 0) * stride;
-            lv[u] = pr[kD + 1];
-            mv[u] = pr[kD];
-            av[u] = pr[dd];
-            if (c >= nch) lv[u] = 0.0f;
+            av[u] = base[(int64_t)(c < nch ? c : 0) * stride + dd];
         }
     };
     request(cs);
@@ -391,7 +396,12 @@ __global__ void __launch_bounds__(kCombLanes * kCombDims) k_attn_combine(const A
     }
     for (int c0 = cs;;) {
 #pragma unroll
-        for (int u = 0; u < kCombBatch; ++u) lse_merge(M, L, A, mv[u], lv[u], av[u]);
+        for (int u = 0; u < kCombBatch; ++u) {
+            const float m2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.x), u));
+            float l2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), u));
+            if (c0 + u * kCombLanes >= nch) l2 = 0.0f;
+            lse_merge(M, L, A, m2, l2, av[u]);
+        }
         c0 += kCombLanes * kCombBatch;
         if (c0 >= nch) break;
         request(c0);
