@@ -867,8 +867,9 @@ __device__ __forceinline__ void mma_load_x(const GemvParams& p, const View& v, i
         }
 }
 
-// The rest of the setup: the norms (PRO_RMS, PRO_CONCAT) and the row maximum,
-// each combined over the R waves of a row through part, then the B operands
+// The rest of the setup: the norms (PRO_RMS, PRO_CONCAT) and the row maximum
+// (of a normed row, a bound taken in the norm's pass), combined over the R
+// waves of a row through part in one exchange, then the B operands
 // (bq), the group sums (tx, column 3 mi of each group) and the scale-back
 // factors (unsc).  Ends with a block barrier.
 template <int FMT, int PRO, int S, int R>
@@ -878,25 +879,39 @@ __device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, in
     constexpr int NI = 8 / R;
     static_assert(FMT == FMT_Q4 || S == 1, "8-bit operands cover one chunk");
     const bool live = mi < p.m;
+    float am = 0.0f;  // the row's largest |value|, or a bound just above it
     if constexpr (PRO != PRO_PLAIN) {
-        float ss0 = 0.0f, ss1 = 0.0f;
+        // sum of squares and max |x gamma| of each segment in one pass and one
+        // exchange: the normalised row's maximum is inv max |x gamma|
+        float ss0 = 0.0f, ss1 = 0.0f, gm0 = 0.0f, gm1 = 0.0f;
 #pragma unroll
         for (int c = 0; c < S; ++c)
 #pragma unroll
             for (int ii = 0; ii < NI; ++ii) {
-                const float4 x = xp.x[c][ii];
+                const float4 x = xp.x[c][ii], g = xp.g[c][ii];
                 const float ss = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, x.w * x.w)));
-                if (PRO == PRO_CONCAT && kChunk * c + 256 * (sub * NI + ii) + 4 * lane >= p.H)
+                const float gm = fmaxf(fmaxf(fabsf(x.x * g.x), fabsf(x.y * g.y)),
+                                       fmaxf(fabsf(x.z * g.z), fabsf(x.w * g.w)));
+                if (PRO == PRO_CONCAT && kChunk * c + 256 * (sub * NI + ii) + 4 * lane >= p.H) {
                     ss1 += ss;
-                else
+                    gm1 = fmaxf(gm1, gm);
+                } else {
                     ss0 += ss;
+                    gm0 = fmaxf(gm0, gm);
+                }
             }
         ss0 = wave_sum(ss0);
-        if constexpr (PRO == PRO_CONCAT) ss1 = wave_sum(ss1);
+        gm0 = wave_max(gm0);
+        if constexpr (PRO == PRO_CONCAT) {
+            ss1 = wave_sum(ss1);
+            gm1 = wave_max(gm1);
+        }
         if constexpr (R > 1) {
             if (lane == 0) {
                 part[0][mi][sub] = ss0;
                 part[1][mi][sub] = ss1;
+                part[2][mi][sub] = gm0;
+                part[3][mi][sub] = gm1;
             }
             __syncthreads();
             ss0 = 0.0f;
@@ -905,11 +920,19 @@ __device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, in
             for (int q = 0; q < R; ++q) {
                 ss0 += part[0][mi][q];
                 ss1 += part[1][mi][q];
+                gm0 = fmaxf(gm0, part[2][mi][q]);
+                gm1 = fmaxf(gm1, part[3][mi][q]);
             }
         }
         const int nfeat = PRO == PRO_CONCAT ? p.H : v.K;
         const float inv0 = rsqrtf(ss0 / (float)nfeat + p.eps);
         const float inv1 = PRO == PRO_CONCAT ? rsqrtf(ss1 / (float)nfeat + p.eps) : inv0;
+        // A normalised value (x inv) gamma and the bound inv max |x gamma|
+        // differ by at most four roundings (< 2^-21 relative): the margin
+        // 2^-20 keeps the bound above every |value|, so the term split's hi
+        // parts stay within f16's exact range (a bound that crosses a power of
+        // two costs one bit of the split's range, nothing else).
+        am = fmaxf(inv0 * gm0, inv1 * gm1) * (1.0f + 0x1p-20f);
         if (live) {
 #pragma unroll
             for (int c = 0; c < S; ++c)
@@ -924,22 +947,22 @@ __device__ __forceinline__ void mma_setup(const GemvParams& p, const View& v, in
                         *reinterpret_cast<float4*>(p.normed_out + (int64_t)mi * v.K + f) = x;
                 }
         }
-    }
-    float am = 0.0f;
+    } else {
 #pragma unroll
-    for (int c = 0; c < S; ++c)
+        for (int c = 0; c < S; ++c)
 #pragma unroll
-        for (int ii = 0; ii < NI; ++ii) {
-            const float4 x = xp.x[c][ii];
-            am = fmaxf(am, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+            for (int ii = 0; ii < NI; ++ii) {
+                const float4 x = xp.x[c][ii];
+                am = fmaxf(am, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+            }
+        am = wave_max(am);
+        if constexpr (R > 1) {
+            if (lane == 0) part[2][mi][sub] = am;
+            __syncthreads();
+            am = part[2][mi][0];
+#pragma unroll
+            for (int q = 1; q < R; ++q) am = fmaxf(am, part[2][mi][q]);
         }
-    am = wave_max(am);
-    if constexpr (R > 1) {
-        if (lane == 0) part[2][mi][sub] = am;
-        __syncthreads();
-        am = part[2][mi][0];
-#pragma unroll
-        for (int q = 1; q < R; ++q) am = fmaxf(am, part[2][mi][q]);
     }
     int e = 0;
     (void)frexpf(am, &e);  // am = m 2^e with m in [0.5, 1); e = 0 for am = 0
@@ -1062,7 +1085,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma(const GemvParams p) {
     __shared__ u32x4 bq[64 * kBGroup];               // 49 KB: B operands
     __shared__ float tx[64][kMmaCols];               // 4 KB: group sums in column 3 mi (4-bit bias)
     __shared__ float stage[W][64 * kStage];  // 5 KB per wave: its scales, [group][row]
-    __shared__ float part[3][4][R];
+    __shared__ float part[4][4][R];
     __shared__ float unsc[4];
     __shared__ int claim_ctr;
 
@@ -1273,7 +1296,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_mma_sk(const GemvParams p) {
     __shared__ float tx[64 * S][kMmaCols];    // group sums, 4 KB per chunk
     __shared__ float stage[W][GW * kStage];   // each wave's scales, [group][row]
     __shared__ float red[PERSIST ? 2 : 1][W][4][kWave];  // the waves' partial sums (two areas in the loop)
-    __shared__ float part[3][4][R];
+    __shared__ float part[4][4][R];
     __shared__ float unsc[4];
 
     View v;
