@@ -232,6 +232,60 @@ def test_lmhead_outlier_activations(m, fmt):
             assert int(got[r]) == int(ids[r]), r
 
 
+def _pow2_max_rows(g, m, k):
+    """Rows of +-1, so the RMSNorm's inverse is 1 / sqrt(1 + eps), and gammas
+    in [0.5, 1.9] except one 2 per 2048 features: the largest normalised value
+    of a row is 2 / sqrt(1 + eps), exactly 2 at eps = 0 and just below it
+    otherwise, at the edge of a binade."""
+    x = np.where(g.random((m, k)) < 0.5, -1.0, 1.0).astype(np.float32)
+    gm = np.clip(synth.gamma(g, k), 0.5, 1.9).astype(np.float32)
+    for c0 in range(0, k, 2048):
+        gm[c0 + int(g.integers(0, min(2048, k - c0)))] = np.float32(2.0)
+    return x, gm
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+@pytest.mark.parametrize("m,fmt", [(4, 4), (3, 4), (4, 8)])
+def test_lmhead_normed_maximum_at_a_power_of_two(m, fmt, eps):
+    """Normed rows whose largest value is 2 or just below it (the matrix-core
+    heads take the row maximum as a bound from the norm's pass, which here
+    sits on or just above the power of two): normed rows, logits, and the ids
+    where the oracle's margin allows."""
+    _say(f"lmhead normed max at 2: m={m} {fmt}-bit eps={eps}")
+    g = synth.rng(138, m, fmt)
+    x, gf = _pow2_max_rows(g, m, 2048)
+    V = 4113
+    if fmt == 4:
+        lm = synth.q4_weight(g, V, 2048)
+        normed, logits, ids = oracle.head(x, gf, eps, lm)
+        call, dlm = mtp.mtp_lmhead_argmax, mtp.DeviceQ4(lm)
+    else:
+        lm = synth.q8_weight(g, 1, V, 2048)
+        normed, logits, ids = oracle.head8(x, gf, eps, lm)
+        call, dlm = mtp.mtp_lmhead_argmax_q8, mtp.DeviceQ8(lm)
+    assert np.abs(normed).max() <= 2.0 and np.abs(normed).max() > 2.0 - 1e-5
+    nout = torch.empty((m, 2048), dtype=torch.float32, device=DEV)
+    lout = torch.empty((m, V), dtype=torch.float32, device=DEV)
+    got = _np(call(_t(x), _t(gf), eps, dlm, normed_out=nout, logits_out=lout))
+    _close(_np(nout), normed, "normed")
+    _close(_np(lout), logits, "logits")
+    for r in range(m):
+        if planting.head_margin(logits[r]) >= 1e-3:
+            assert int(got[r]) == int(ids[r]), r
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+def test_norm_concat_proj_normed_maximum_at_a_power_of_two(eps):
+    """eh_proj at four rows (split-K matrix cores) over normed halves whose
+    largest value is 2 or just below it."""
+    g = synth.rng(139)
+    e, ge = _pow2_max_rows(g, 4, 2048)
+    h, gh = _pow2_max_rows(g, 4, 2048)
+    w = synth.q4_weight(g, 2048, 4096)
+    got = _np(mtp.mtp_norm_concat_proj(_t(e), _t(h), _t(ge), _t(gh), eps, mtp.DeviceQ4(w)))
+    _close(got, oracle.norm_concat_proj(e, h, ge, gh, eps, w), "u")
+
+
 @pytest.mark.parametrize("m", [1, 4])
 def test_moe_q4_outlier_activations(m):
     for extra in range(20):
